@@ -1,0 +1,199 @@
+"""CPU oracle of the trainer->sampler weight-delta codec (test infrastructure).
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its binding) never does, and shares no code with it.  The arithmetic lives in
+``oracle.c`` (plain C, built by ``oracle/_build.py``); this module only moves
+numpy arrays in and out.  Parity status per function: see the header of
+``oracle.c``.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import _build
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+CAPACITY = 1
+BADINDEX = 2
+CORRUPT = 4
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        L = ctypes.CDLL(_build.LIB)
+        L.oracle_bf16_rne.argtypes = [ctypes.c_uint32]
+        L.oracle_bf16_rne.restype = ctypes.c_uint16
+        L.oracle_cast_bf16.argtypes = [_P, _P, _I64]
+        L.oracle_cast_diff.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _P, _P, _I64]
+        L.oracle_compact.argtypes = [_P, _P, _P, _P, _I64, _P, _P, _I64]
+        L.oracle_apply_patch.argtypes = [_P, _I64, _P, _P, _I64, _P]
+        L.oracle_xor_apply.argtypes = [_P, _P, _I64]
+        L.oracle_lz4_encode_block.argtypes = [_P, _I64, _P]
+        L.oracle_lz4_encode_block.restype = _I64
+        L.oracle_lz4_encode_blocks.argtypes = [_P, _P, _I64, _I32, _P, _I64, _P, _P, _P, _P]
+        L.oracle_lz4_decode_block.argtypes = [_P, _I64, _P, _I64]
+        L.oracle_lz4_decode_block.restype = ctypes.c_int
+        L.oracle_lz4_decode_blocks.argtypes = [_P, _I64, _P, _P, _I64, _I32, _I64, _P, _I32, _P]
+        L.oracle_e4m3_rne.argtypes = [ctypes.c_float]
+        L.oracle_e4m3_rne.restype = ctypes.c_uint8
+        L.oracle_fp8_block_quant.argtypes = [_P, _P, _I32, _I64, _I64, _P, _P, _P]
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a)
+    assert a.dtype == dtype, (a.dtype, dtype)
+    return a
+
+
+def bf16_rne(bits: int) -> int:
+    return int(lib().oracle_bf16_rne(ctypes.c_uint32(bits)))
+
+
+def cast_bf16(w):
+    w = _c(w, np.float32)
+    out = np.empty(w.shape, np.uint16)
+    lib().oracle_cast_bf16(_ptr(w), _ptr(out), w.size)
+    return out
+
+
+def cast_diff(w_new, b_old=None, cap=None, want_new=True, want_mask=True, want_patch=True):
+    """Returns dict(b_new, mask, idx, val, count, status) for the requested outputs."""
+    w_new = _c(w_new, np.float32).reshape(-1)
+    n = w_new.size
+    b_old = None if b_old is None else _c(b_old, np.uint16).reshape(-1)
+    cap = n if cap is None else int(cap)
+    b_new = np.empty(n, np.uint16) if want_new else None
+    mask = np.empty(n, np.uint16) if (want_mask and b_old is not None) else None
+    idx = np.empty(max(cap, 1), np.int32) if (want_patch and b_old is not None) else None
+    val = np.empty(max(cap, 1), np.uint16) if (want_patch and b_old is not None) else None
+    count = np.zeros(1, np.int64)
+    status = np.zeros(1, np.uint32)
+    lib().oracle_cast_diff(_ptr(w_new), _ptr(b_old), _ptr(b_new), _ptr(mask), _ptr(idx), _ptr(val),
+                           cap, _ptr(count), _ptr(status), n)
+    m = int(count[0])
+    if idx is not None:
+        idx, val = idx[:min(m, cap)], val[:min(m, cap)]
+    return dict(b_new=b_new, mask=mask, idx=idx, val=val,
+                count=m if b_old is not None else None, status=int(status[0]))
+
+
+def compact(b_old, b_new, cap=None):
+    b_old = _c(b_old, np.uint16).reshape(-1)
+    b_new = _c(b_new, np.uint16).reshape(-1)
+    n = b_old.size
+    cap = n if cap is None else int(cap)
+    idx = np.empty(max(cap, 1), np.int32)
+    val = np.empty(max(cap, 1), np.uint16)
+    count = np.zeros(1, np.int64)
+    status = np.zeros(1, np.uint32)
+    lib().oracle_compact(_ptr(b_old), _ptr(b_new), _ptr(idx), _ptr(val), cap, _ptr(count), _ptr(status), n)
+    m = int(count[0])
+    return idx[:min(m, cap)], val[:min(m, cap)], m, int(status[0])
+
+
+def apply_patch(b, idx, val, count=None):
+    """Applies in place to a copy; returns (new array, status)."""
+    b = _c(b, np.uint16).reshape(-1).copy()
+    idx = _c(idx, np.int32)
+    val = _c(val, np.uint16)
+    count = idx.size if count is None else int(count)
+    status = np.zeros(1, np.uint32)
+    lib().oracle_apply_patch(_ptr(b), b.size, _ptr(idx), _ptr(val), count, _ptr(status))
+    return b, int(status[0])
+
+
+def xor_apply(dst, mask):
+    d = np.ascontiguousarray(dst).copy()
+    m = np.ascontiguousarray(mask)
+    assert d.nbytes == m.nbytes
+    lib().oracle_xor_apply(_ptr(d), _ptr(m), d.nbytes)
+    return d
+
+
+def lz4_encode_block(src) -> bytes:
+    s = np.frombuffer(bytes(src), np.uint8) if not isinstance(src, np.ndarray) else _c(src, np.uint8)
+    n = s.size
+    out = np.empty(n + n // 255 + 64, np.uint8)
+    sz = lib().oracle_lz4_encode_block(_ptr(s) if n else None, n, _ptr(out))
+    return out[:sz].tobytes()
+
+
+def lz4_encode_blocks(src, block_bytes=65536, src_xor=None, cap=None):
+    """src, src_xor: any contiguous arrays (viewed as bytes).
+    Returns dict(payload, sizes, offsets, total, status)."""
+    s = np.ascontiguousarray(src).view(np.uint8).reshape(-1)
+    x = None if src_xor is None else np.ascontiguousarray(src_xor).view(np.uint8).reshape(-1)
+    nbytes = s.size
+    nb = (nbytes + block_bytes - 1) // block_bytes
+    worst = nb * (block_bytes + block_bytes // 255 + 16)
+    cap = worst if cap is None else int(cap)
+    payload = np.empty(max(cap, 1), np.uint8)
+    sizes = np.zeros(max(nb, 1), np.uint32)
+    offsets = np.zeros(max(nb, 1), np.uint64)
+    total = np.zeros(1, np.uint64)
+    status = np.zeros(1, np.uint32)
+    lib().oracle_lz4_encode_blocks(_ptr(s), _ptr(x), nbytes, block_bytes, _ptr(payload), cap,
+                                   _ptr(sizes), _ptr(offsets), _ptr(total), _ptr(status))
+    t = int(total[0])
+    return dict(payload=payload[:min(t, cap)], sizes=sizes[:nb], offsets=offsets[:nb], total=t,
+                status=int(status[0]))
+
+
+def lz4_decode_block(comp, out_size):
+    c = np.frombuffer(bytes(comp), np.uint8)
+    out = np.zeros(max(out_size, 1), np.uint8)
+    rc = lib().oracle_lz4_decode_block(_ptr(c) if c.size else None, c.size, _ptr(out), out_size)
+    return (out[:out_size].tobytes() if rc == 0 else None)
+
+
+def lz4_decode_blocks(payload, offsets, sizes, dst, block_bytes=65536, mode=0, payload_bytes=None):
+    """Decodes into a copy of dst (any dtype, viewed as bytes).  Returns (new dst, status)."""
+    p = _c(payload, np.uint8).reshape(-1)
+    offs = _c(offsets, np.uint64)
+    szs = _c(sizes, np.uint32)
+    d = np.ascontiguousarray(dst).copy()
+    db = d.view(np.uint8).reshape(-1)
+    status = np.zeros(1, np.uint32)
+    pb = p.size if payload_bytes is None else int(payload_bytes)
+    lib().oracle_lz4_decode_blocks(_ptr(p), pb, _ptr(offs), _ptr(szs), offs.size, block_bytes,
+                                   db.size, _ptr(db), mode, _ptr(status))
+    return d, int(status[0])
+
+
+def e4m3_rne(q: float) -> int:
+    return int(lib().oracle_e4m3_rne(ctypes.c_float(q)))
+
+
+def fp8_block_quant(srcs, batch=1):
+    """srcs: list of uint16 arrays shaped [batch, rows_i, cols] (or [rows_i, cols] when batch == 1).
+    Returns (codes [batch, R, cols] uint8, scales [batch, ceil(R/128), ceil(cols/128)] float32)."""
+    arrs = [_c(s, np.uint16) for s in srcs]
+    if batch == 1:
+        arrs = [a.reshape((1,) + a.shape[-2:]) for a in arrs]
+    cols = arrs[0].shape[-1]
+    rows = np.array([a.shape[1] for a in arrs], np.int64)
+    strides = np.array([a.shape[1] * cols for a in arrs], np.int64)
+    R = int(rows.sum())
+    codes = np.empty((batch, R, cols), np.uint8)
+    scales = np.empty((batch, (R + 127) // 128, (cols + 127) // 128), np.float32)
+    ptrs = (ctypes.c_void_p * len(arrs))(*[a.ctypes.data for a in arrs])
+    lib().oracle_fp8_block_quant(ctypes.cast(ptrs, ctypes.c_void_p), _ptr(rows), len(arrs), cols,
+                                 batch, _ptr(strides), _ptr(codes), _ptr(scales))
+    return codes, scales

@@ -1,0 +1,28 @@
+"""Build the CPU oracle (test infrastructure) into oracle/liboracle.so.
+
+Plain gcc, -O2, no fast-math, no FP contraction, no intrinsics: the oracle is
+meant to be read against its definitions, not to be fast.
+"""
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB = os.path.join(HERE, "liboracle.so")
+
+
+def build(verbose: bool = False) -> str:
+    cmd = [
+        "gcc", "-std=c11", "-O2", "-fPIC", "-shared",
+        "-fno-fast-math", "-ffp-contract=off", "-fno-strict-aliasing",
+        "-Wall", "-Wextra",
+        os.path.join(HERE, "oracle.c"), "-o", LIB + ".tmp", "-lm",
+    ]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))
