@@ -1,0 +1,232 @@
+/*
+ * pulse.h -- C ABI of the MI355X (gfx950) trainer->sampler weight-delta codec.
+ *
+ * Sender (trainer): cast FP32 master weights to the served BF16 view, compare
+ * it bitwise with the previous served view, and ship either sparse patches of
+ * (index, new absolute value) or an LZ4-block-encoded XOR mask.  Receiver
+ * (sampler): scatter the patches, or decode the mask and XOR it in place,
+ * rebuilding the new BF16 view bit for bit; optionally stack q/k/v or
+ * gate/up and quantise to FP8-E4M3 per 128x128 block for an FP8 sampler.
+ *
+ * Sources cited below:
+ *  [Jiang talk]    "Taking Reinforcement Learning Cross Datacenter -- Nan Jiang,
+ *                  Modal", talk transcript (timecodes mm:ss).
+ *  [PULSE summary] gist.science technical summary of arXiv 2602.03839 (PULSE),
+ *                  section "1. PULSESync" (Processo / Ricostruzione / Compressione).
+ *  [Teleport]      Turkish write-up of the humansand.ai "GPU weight teleportation"
+ *                  post, sections "XOR masks", "Moving the pipeline onto GPUs".
+ *  [Perplexity]    "Weight transfer for RL post-training in under 2 seconds",
+ *                  sections "Potok zadan", "Kontrola uzycia pamieci GPU",
+ *                  "Czysta separacja".
+ *  The LZ4 byte format is the public LZ4 Block Format description; FP8 is OCP
+ *  8-bit floating point E4M3 ("fn": bias 7, max 448, no Inf).
+ *
+ * Conventions (all entry points):
+ *  - Pointers are DEVICE pointers unless marked (host).  Every call only
+ *    enqueues work on `stream` (NULL = the null stream) and returns; results
+ *    written to device memory are valid once the stream has reached them.
+ *  - The caller owns every buffer.  The library never allocates device memory;
+ *    calls that need scratch take a caller-provided workspace (the pages' cap on
+ *    in-flight temporary GPU memory, [Perplexity] "Kontrola uzycia pamieci GPU").
+ *  - Return value: PULSE_OK, or a negative PULSE_E* code for argument errors
+ *    (nothing was enqueued) or a failed launch (PULSE_EHIP).
+ *  - Data-dependent conditions are reported in a device status word: the
+ *    PULSE_DS_* bits are OR-ed into *d_status; no call ever clears it, the
+ *    caller zeroes it before the calls it wants to observe.
+ *  - Dense buffers (weights, views, masks, LZ4 sources/destinations, FP8
+ *    sources) must be 16-byte aligned (PULSE_EALIGN otherwise).
+ *  - Calls that share a workspace must be ordered (same stream, or joined by
+ *    events); concurrent calls on one workspace race.
+ *  - One component per call, each testable in isolation ([Perplexity],
+ *    "Czysta separacja").
+ */
+#ifndef PULSE_H
+#define PULSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes ---------------------------------------------------------- */
+#define PULSE_OK 0
+#define PULSE_EINVAL (-1)     /* NULL required pointer, bad mode/size/shape     */
+#define PULSE_EALIGN (-2)     /* a dense buffer is not 16-byte aligned          */
+#define PULSE_ERANGE (-3)     /* element count beyond int32 indices (2^31 - 1)   */
+#define PULSE_EWORKSPACE (-4) /* workspace NULL or smaller than required        */
+#define PULSE_EHIP (-5)       /* the kernel launch failed                       */
+
+/* ---- device status bits (OR-ed into *d_status) ----------------------------- */
+#define PULSE_DS_CAPACITY 0x1u /* more patch entries / payload bytes than the
+                                  capacity; counts/totals stay exact, entries
+                                  or whole blocks beyond the capacity are not
+                                  written                                    */
+#define PULSE_DS_BADINDEX 0x2u /* apply: entries with index >= n were skipped  */
+#define PULSE_DS_CORRUPT 0x4u  /* lz4 decode: >= 1 malformed block; the dst
+                                  range of such a block is left untouched    */
+
+/* ---- workspaces ------------------------------------------------------------ */
+#define PULSE_OP_CAST_DIFF 1  /* n = element count                               */
+#define PULSE_OP_COMPACT 2    /* n = element count                               */
+#define PULSE_OP_LZ4_ENCODE 3 /* n = source bytes, aux = block_bytes              */
+#define PULSE_OP_LZ4_DECODE 4 /* n = number of blocks, aux = payload bytes         */
+
+/* Bytes of workspace the op needs for the given size (0 if it needs none).
+ * A workspace sized for a larger call serves any smaller call of any op. */
+size_t pulse_workspace_bytes(int op, int64_t n, int64_t aux);
+
+/* Zero a workspace before its first use.  After that each call leaves it
+ * ready for the next one (it carries a per-call epoch so the status words of
+ * earlier calls are never mistaken for the current call's), so it is called
+ * once per allocation, not per call. */
+int pulse_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Human-readable name of a return code (static string). */
+const char *pulse_status_string(int code);
+
+/* Library version, "major.minor.patch" (static string). */
+const char *pulse_version(void);
+
+/* ---- a1 + a2 + a3: cast, diff, compaction ----------------------------------
+ * The served view is the master weight cast to BF16 with round-to-nearest-
+ * even ([Jiang talk] 10:49-10:56; a value only changes once an update crosses
+ * half a BF16 ulp, 07:24-08:07); versions are compared bitwise and the patch
+ * holds the changed positions and their new absolute BF16 bits ([PULSE
+ * summary] "1. PULSESync", Processo/Ricostruzione; [Jiang talk] 12:12-12:44).
+ *
+ *   w_new      [n] float32 master weights (read).
+ *   b_old      [n] previous BF16 view (read), or NULL: pure cast (then xor_mask,
+ *              patch_idx, patch_val, d_count must be NULL).
+ *   b_new      [n] cast result (written), or NULL.  May equal b_old (in-place
+ *              update of the sender's view).
+ *   xor_mask   [n] b_old ^ b_new (written), or NULL.
+ *   patch_idx  [patch_cap] int32 positions of the changed elements in strictly
+ *              ascending order (written), or NULL together with patch_val and
+ *              d_count.
+ *   patch_val  [patch_cap] new BF16 bits at those positions (written).
+ *   patch_cap  capacity of patch_idx/patch_val (>= 0).
+ *   d_count    (device int64) exact number of changed elements (written).
+ *   d_status   (device uint32) PULSE_DS_CAPACITY when count > patch_cap; the
+ *              first patch_cap entries are still written.  May be NULL when no
+ *              patch is requested.
+ *   n          element count; with a patch, n <= 2^31 - 1 (PULSE_ERANGE).
+ *   ws         workspace of pulse_workspace_bytes(PULSE_OP_CAST_DIFF, n, 0)
+ *              bytes when a patch is requested; ignored otherwise.
+ * NaN inputs give a quiet NaN with the input's sign and top payload bits.
+ */
+int pulse_cast_diff(const float *w_new, const uint16_t *b_old, uint16_t *b_new,
+                    uint16_t *xor_mask, int32_t *patch_idx, uint16_t *patch_val,
+                    int64_t patch_cap, int64_t *d_count, uint32_t *d_status, int64_t n,
+                    void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---- a3 on two existing BF16 views ----------------------------------------
+ * Same patch as pulse_cast_diff, with the new view given directly.
+ *   b_old, b_new [n] BF16 views (read).  Other arguments as above. */
+int pulse_compact(const uint16_t *b_old, const uint16_t *b_new, int32_t *patch_idx,
+                  uint16_t *patch_val, int64_t patch_cap, int64_t *d_count,
+                  uint32_t *d_status, int64_t n, void *ws, size_t ws_bytes,
+                  hipStream_t stream);
+
+/* ---- a4: patch scatter-apply ---------------------------------------------
+ * Selective override: b[patch_idx[k]] = patch_val[k] for k < count, bit-level
+ * writes with no floating-point addition ([Jiang talk] 11:08-11:30; [PULSE
+ * summary] "1. PULSESync", Ricostruzione); applied in sequence the patches of
+ * consecutive versions bring a lagging copy up to date (16:52-16:58).
+ *   b          [n] BF16 view, updated in place.
+ *   patch_idx, patch_val  the patch (indices unique, as produced above).
+ *   d_count    (device) number of entries; count = min(*d_count, max_count).
+ *   max_count  (host) bound used to size the launch, e.g. the patch capacity.
+ *   d_status   PULSE_DS_BADINDEX when an index lies outside [0, n) (skipped).
+ * The count is read on the device, so encode -> apply needs no host sync. */
+int pulse_apply_patch(uint16_t *b, int64_t n, const int32_t *patch_idx,
+                      const uint16_t *patch_val, const int64_t *d_count, int64_t max_count,
+                      uint32_t *d_status, hipStream_t stream);
+
+/* ---- a2/a6: dense XOR apply ------------------------------------------------
+ * dst ^= mask over nbytes bytes: the sampler XORs the same-size mask into its
+ * old weights and obtains the new ones, whatever the dtype ([Teleport] "XOR
+ * masks").  dst and mask 16-byte aligned; nbytes any value >= 0. */
+int xor_mask_apply(void *dst, const void *mask, int64_t nbytes, hipStream_t stream);
+
+/* ---- a5: LZ4 block encode of a mask ---------------------------------------
+ * The mask (mostly zero) is cut into independent blocks of block_bytes bytes
+ * (the last one short) and each block is LZ4-encoded with the canonical
+ * "offset-1 run" parse: every maximal run of one byte value [s, e) with
+ * i = s+1, j = min(e, n-5), j-i >= 4 and i <= n-12 becomes one sequence
+ * (literals since the previous such run, then a match of offset 1 and length
+ * j-i); the rest of the block is the final literal run.  LZ4 was chosen on the
+ * pages because it codes long runs in few commands and RL masks are long zero
+ * runs ([Teleport] "Moving the pipeline onto GPUs").  The output is standard
+ * LZ4 block format; any LZ4 block decoder accepts it.
+ *   src          [nbytes] bytes to encode (read).
+ *   src_xor      [nbytes] or NULL; when given the encoded bytes are
+ *                src[i] ^ src_xor[i] (the XOR mask of two views, never
+ *                materialised).
+ *   block_bytes  a multiple of 16384, at most 65536.
+ *   payload      [payload_cap] concatenated encoded blocks (written).
+ *                nblocks * (block_bytes + block_bytes/255 + 16) always suffices.
+ *   comp_sizes   [nblocks] uint32 encoded size per block (written).
+ *   comp_offsets [nblocks] uint64 exclusive prefix sum of comp_sizes (written).
+ *   d_total      (device uint64) total encoded bytes, exact (written).
+ *   d_status     PULSE_DS_CAPACITY when the total exceeds payload_cap; blocks
+ *                that do not fit entirely are not written.
+ *   ws           pulse_workspace_bytes(PULSE_OP_LZ4_ENCODE, nbytes, block_bytes).
+ * nblocks = ceil(nbytes / block_bytes). */
+int lz4_encode_blocks(const void *src, const void *src_xor, int64_t nbytes,
+                      int32_t block_bytes, uint8_t *payload, int64_t payload_cap,
+                      uint32_t *comp_sizes, uint64_t *comp_offsets, uint64_t *d_total,
+                      uint32_t *d_status, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---- a6: LZ4 block decode + in-place apply -------------------------------
+ * Decodes any valid LZ4 block (not only the canonical parse) and either stores
+ * the bytes (mode 0) or XORs them into dst in place (mode 1): the sampler gets
+ * exactly the new weights ([Teleport] "XOR masks"; the decoded mask is applied
+ * in place in HBM, "Moving the pipeline onto GPUs").  Each block is validated
+ * in full before any byte of its dst range is written; a malformed block
+ * (length past its input, offset 0 or beyond the bytes produced, output past
+ * its size, input not ending right after a literal run with the output exactly
+ * full, bytes outside [0, payload_bytes), or a start before the end of any
+ * earlier block in the payload) leaves its dst range untouched and sets
+ * PULSE_DS_CORRUPT.
+ *   payload        [payload_bytes] encoded blocks (read).
+ *   comp_offsets, comp_sizes  [nblocks] block table (read).
+ *   block_bytes    decoded size of every block but the last (<= 65536).
+ *   nbytes         total decoded bytes; nblocks == ceil(nbytes / block_bytes).
+ *   dst            [nbytes], 16-byte aligned.
+ *   ws             pulse_workspace_bytes(PULSE_OP_LZ4_DECODE, nblocks, payload_bytes). */
+int lz4_decode_blocks(const uint8_t *payload, int64_t payload_bytes,
+                      const uint64_t *comp_offsets, const uint32_t *comp_sizes,
+                      int64_t nblocks, int32_t block_bytes, int64_t nbytes, void *dst,
+                      int32_t mode, uint32_t *d_status, void *ws, size_t ws_bytes,
+                      hipStream_t stream);
+
+/* ---- a7: projection fusion + FP8-E4M3 block quantisation -----------------
+ * The sender rebuilds the full weight, fuses projections and quantises BF16
+ * training weights for FP8 inference ([Perplexity] opening paragraph and
+ * "Potok zadan").  The sources are stacked along rows (the output dimension of
+ * an nn.Linear [out, in] weight), e.g. [q; k; v] or per expert [gate; up];
+ * the stacked [R, cols] matrix is cut into 128x128 blocks; per block
+ * amax = max |x|, s = amax / 448 (IEEE float32 division; s = 1 when amax == 0)
+ * and code = E4M3(x / s) (IEEE division, round to nearest even, saturating at
+ * 448).  Dequantisation is E4M3(code) * s.
+ *   srcs        (host) array of nsrc (1..8) device pointers to BF16 [rows_i, cols],
+ *               row-major, 16-byte aligned.
+ *   src_rows    (host) rows of each source.
+ *   cols        columns, a multiple of 8.
+ *   batch       number of stacked matrices (e.g. experts); source i of entry e
+ *               starts at srcs[i] + e * src_batch_stride[i] elements.
+ *   src_batch_stride (host) per-source stride in elements; NULL if batch == 1.
+ *   codes       [batch][R][cols] uint8 (written), R = sum of rows.
+ *   scales      [batch][ceil(R/128)][ceil(cols/128)] float32 (written). */
+int fp8_block_quant(const uint16_t *const *srcs, const int64_t *src_rows, int32_t nsrc,
+                    int64_t cols, int64_t batch, const int64_t *src_batch_stride,
+                    uint8_t *codes, float *scales, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PULSE_H */

@@ -224,7 +224,9 @@ void oracle_lz4_encode_blocks(const uint8_t *src, const uint8_t *src_xor, int64_
 /* so a block that does not decode cleanly must not touch them.  Malformed:   */
 /* a length running past the input, offset 0 or beyond the bytes produced so  */
 /* far, output beyond out_size, or input ending anywhere but after a literal  */
-/* run with exactly out_size bytes produced (our reading).                    */
+/* run with exactly out_size bytes produced; over a payload also a block     */
+/* outside [0, payload_bytes) or starting before the end of an earlier block  */
+/* (our readings).                                                            */
 /* ------------------------------------------------------------------------ */
 static int read_len_ext(const uint8_t *in, int64_t comp_size, int64_t *ip, int64_t *len)
 {
@@ -266,13 +268,19 @@ void oracle_lz4_decode_blocks(const uint8_t *payload, int64_t payload_bytes,
                               uint8_t *dst, int32_t mode, uint32_t *status)
 {
     uint8_t *blk = (uint8_t *)malloc((size_t)block_bytes);
+    uint64_t end_so_far = 0; /* furthest end of any earlier block in the payload */
     for (int64_t bi = 0; bi < nblocks; ++bi) {
         int64_t base = bi * (int64_t)block_bytes;
         if (base >= nbytes) break;
         int64_t n = nbytes - base < block_bytes ? nbytes - base : block_bytes;
         uint64_t off = comp_offsets[bi];
         uint64_t sz = comp_sizes[bi];
-        int bad = off > (uint64_t)payload_bytes || sz > (uint64_t)payload_bytes - off;
+        uint64_t end = off + sz < off ? UINT64_MAX : off + sz;
+        /* blocks lie inside the payload, one after another: a block that starts
+         * before the end of an earlier one is malformed (our reading) */
+        int bad = off > (uint64_t)payload_bytes || sz > (uint64_t)payload_bytes - off ||
+                  (bi > 0 && off < end_so_far);
+        if (end > end_so_far) end_so_far = end;
         if (!bad) bad = oracle_lz4_decode_block(payload + off, (int64_t)sz, blk, n) != 0;
         if (bad) {
             if (status) *status |= ORACLE_CORRUPT;

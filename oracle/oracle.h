@@ -84,7 +84,8 @@ int oracle_lz4_decode_block(const uint8_t *in, int64_t comp_size, uint8_t *out,
 
 /* a6 over a payload: mode 0 stores the decoded bytes into dst, mode 1 XORs them
  * into dst.  A malformed block (including one whose bytes lie outside
- * [0, payload_bytes)) leaves its dst range untouched and sets ORACLE_CORRUPT. */
+ * [0, payload_bytes) or that starts before the end of an earlier block) leaves
+ * its dst range untouched and sets ORACLE_CORRUPT. */
 void oracle_lz4_decode_blocks(const uint8_t *payload, int64_t payload_bytes,
                               const uint64_t *comp_offsets, const uint32_t *comp_sizes,
                               int64_t nblocks, int32_t block_bytes, int64_t nbytes,

@@ -1,0 +1,217 @@
+"""Python binding of libpulse.so, the MI355X weight-delta codec (include/pulse.h).
+
+Argument marshalling only: every function takes torch tensors that already live
+on the GPU, passes their data pointers, sizes and torch's current HIP stream to
+the C entry point of the same name, and raises if that entry point returns an
+error.  Every step of the codec runs in the library's HIP kernels.  There is no
+fallback: if the library is not built, importing this package fails.
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "PULSE_DS_CAPACITY", "PULSE_DS_BADINDEX", "PULSE_DS_CORRUPT",
+    "PULSE_OP_CAST_DIFF", "PULSE_OP_COMPACT", "PULSE_OP_LZ4_ENCODE", "PULSE_OP_LZ4_DECODE",
+    "pulse_version", "pulse_workspace_bytes", "pulse_workspace_init", "workspace",
+    "pulse_cast_diff", "pulse_compact", "pulse_apply_patch", "xor_mask_apply",
+    "lz4_encode_blocks", "lz4_decode_blocks", "fp8_block_quant", "lz4_payload_bound", "lib_path",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libpulse.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(
+        f"{_LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+        "(or python sparse_delta_codec_amd/_build.py) first")
+_lib = ctypes.CDLL(_LIB_PATH)
+
+PULSE_DS_CAPACITY = 0x1
+PULSE_DS_BADINDEX = 0x2
+PULSE_DS_CORRUPT = 0x4
+PULSE_OP_CAST_DIFF = 1
+PULSE_OP_COMPACT = 2
+PULSE_OP_LZ4_ENCODE = 3
+PULSE_OP_LZ4_DECODE = 4
+
+_P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+_lib.pulse_version.restype = ctypes.c_char_p
+_lib.pulse_status_string.restype = ctypes.c_char_p
+_lib.pulse_status_string.argtypes = [ctypes.c_int]
+_lib.pulse_workspace_bytes.restype = _SZ
+_lib.pulse_workspace_bytes.argtypes = [ctypes.c_int, _I64, _I64]
+_lib.pulse_workspace_init.argtypes = [_P, _SZ, _P]
+_lib.pulse_cast_diff.argtypes = [_P, _P, _P, _P, _P, _P, _I64, _P, _P, _I64, _P, _SZ, _P]
+_lib.pulse_compact.argtypes = [_P, _P, _P, _P, _I64, _P, _P, _I64, _P, _SZ, _P]
+_lib.pulse_apply_patch.argtypes = [_P, _I64, _P, _P, _P, _I64, _P, _P]
+_lib.xor_mask_apply.argtypes = [_P, _P, _I64, _P]
+_lib.lz4_encode_blocks.argtypes = [_P, _P, _I64, _I32, _P, _I64, _P, _P, _P, _P, _P, _SZ, _P]
+_lib.lz4_decode_blocks.argtypes = [_P, _I64, _P, _P, _I64, _I32, _I64, _P, _I32, _P, _P, _SZ, _P]
+_lib.fp8_block_quant.argtypes = [_P, _P, _I32, _I64, _I64, _P, _P, _P, _P]
+for _f in ("pulse_workspace_init", "pulse_cast_diff", "pulse_compact", "pulse_apply_patch",
+           "xor_mask_apply", "lz4_encode_blocks", "lz4_decode_blocks", "fp8_block_quant"):
+    getattr(_lib, _f).restype = ctypes.c_int
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def pulse_version() -> str:
+    return _lib.pulse_version().decode()
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise RuntimeError(f"{what}: {_lib.pulse_status_string(rc).decode()} ({rc})")
+
+
+def _dev(t, name, dtype=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return t.data_ptr()
+
+
+def _need(t, nbytes, name):
+    """Host-side size check: the kernels trust the sizes they are given."""
+    if t is not None and t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name} holds {t.numel() * t.element_size()} bytes, needs {nbytes}")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+_U16 = (torch.uint16, torch.int16, torch.bfloat16)
+
+
+def pulse_workspace_bytes(op: int, n: int, aux: int = 0) -> int:
+    return int(_lib.pulse_workspace_bytes(op, n, aux))
+
+
+def pulse_workspace_init(ws: torch.Tensor, stream=None):
+    _check(_lib.pulse_workspace_init(_dev(ws, "ws"), ws.numel() * ws.element_size(), _stream(stream)),
+           "pulse_workspace_init")
+
+
+def workspace(op: int, n: int, aux: int = 0, device="cuda") -> torch.Tensor:
+    """A zeroed workspace of the size the op needs (allocation is the caller's)."""
+    nbytes = max(pulse_workspace_bytes(op, n, aux), 256)
+    return torch.zeros((nbytes + 15) // 16 * 16, dtype=torch.uint8, device=device)
+
+
+def _ws(ws):
+    if ws is None:
+        return None, 0
+    return _dev(ws, "ws"), ws.numel() * ws.element_size()
+
+
+def pulse_cast_diff(w_new, b_old=None, b_new=None, xor_mask=None, patch_idx=None, patch_val=None,
+                    d_count=None, d_status=None, ws=None, n=None, stream=None):
+    n = w_new.numel() if n is None else n
+    cap = 0 if patch_idx is None else patch_idx.numel()
+    _need(w_new, 4 * n, "w_new")
+    for t, nm in ((b_old, "b_old"), (b_new, "b_new"), (xor_mask, "xor_mask")):
+        _need(t, 2 * n, nm)
+    _need(patch_val, 2 * cap, "patch_val")
+    wsp, wsb = _ws(ws)
+    _check(_lib.pulse_cast_diff(
+        _dev(w_new, "w_new", torch.float32), _dev(b_old, "b_old", _U16), _dev(b_new, "b_new", _U16),
+        _dev(xor_mask, "xor_mask", _U16), _dev(patch_idx, "patch_idx", torch.int32),
+        _dev(patch_val, "patch_val", _U16), cap, _dev(d_count, "d_count", torch.int64),
+        _dev(d_status, "d_status", torch.int32), n, wsp, wsb, _stream(stream)), "pulse_cast_diff")
+
+
+def pulse_compact(b_old, b_new, patch_idx, patch_val, d_count, d_status, ws, n=None, stream=None):
+    n = b_old.numel() if n is None else n
+    _need(b_old, 2 * n, "b_old")
+    _need(b_new, 2 * n, "b_new")
+    _need(patch_val, 2 * patch_idx.numel(), "patch_val")
+    wsp, wsb = _ws(ws)
+    _check(_lib.pulse_compact(
+        _dev(b_old, "b_old", _U16), _dev(b_new, "b_new", _U16), _dev(patch_idx, "patch_idx", torch.int32),
+        _dev(patch_val, "patch_val", _U16), patch_idx.numel(), _dev(d_count, "d_count", torch.int64),
+        _dev(d_status, "d_status", torch.int32), n, wsp, wsb, _stream(stream)), "pulse_compact")
+
+
+def pulse_apply_patch(b, patch_idx, patch_val, d_count, d_status, max_count=None, n=None, stream=None):
+    n = b.numel() if n is None else n
+    max_count = patch_idx.numel() if max_count is None else max_count
+    _need(b, 2 * n, "b")
+    _need(patch_idx, 4 * max_count, "patch_idx")
+    _need(patch_val, 2 * max_count, "patch_val")
+    _check(_lib.pulse_apply_patch(
+        _dev(b, "b", _U16), n, _dev(patch_idx, "patch_idx", torch.int32), _dev(patch_val, "patch_val", _U16),
+        _dev(d_count, "d_count", torch.int64), max_count, _dev(d_status, "d_status", torch.int32),
+        _stream(stream)), "pulse_apply_patch")
+
+
+def xor_mask_apply(dst, mask, nbytes=None, stream=None):
+    nbytes = dst.numel() * dst.element_size() if nbytes is None else nbytes
+    _need(dst, nbytes, "dst")
+    _need(mask, nbytes, "mask")
+    _check(_lib.xor_mask_apply(_dev(dst, "dst"), _dev(mask, "mask"), nbytes, _stream(stream)), "xor_mask_apply")
+
+
+def lz4_payload_bound(nbytes: int, block_bytes: int = 65536) -> int:
+    nb = (nbytes + block_bytes - 1) // block_bytes
+    return nb * (block_bytes + block_bytes // 255 + 16)
+
+
+def lz4_encode_blocks(src, payload, comp_sizes, comp_offsets, d_total, d_status, ws, src_xor=None,
+                      block_bytes=65536, nbytes=None, stream=None):
+    nbytes = src.numel() * src.element_size() if nbytes is None else nbytes
+    nb = (nbytes + block_bytes - 1) // block_bytes
+    _need(src, nbytes, "src")
+    _need(src_xor, nbytes, "src_xor")
+    _need(comp_sizes, 4 * nb, "comp_sizes")
+    _need(comp_offsets, 8 * nb, "comp_offsets")
+    wsp, wsb = _ws(ws)
+    _check(_lib.lz4_encode_blocks(
+        _dev(src, "src"), _dev(src_xor, "src_xor"), nbytes, block_bytes, _dev(payload, "payload", torch.uint8),
+        payload.numel(), _dev(comp_sizes, "comp_sizes", torch.int32), _dev(comp_offsets, "comp_offsets", torch.int64),
+        _dev(d_total, "d_total", torch.int64), _dev(d_status, "d_status", torch.int32), wsp, wsb,
+        _stream(stream)), "lz4_encode_blocks")
+
+
+def lz4_decode_blocks(payload, comp_offsets, comp_sizes, dst, d_status, ws, mode=1, block_bytes=65536,
+                      nbytes=None, payload_bytes=None, stream=None):
+    nbytes = dst.numel() * dst.element_size() if nbytes is None else nbytes
+    payload_bytes = payload.numel() if payload_bytes is None else payload_bytes
+    nb = (nbytes + block_bytes - 1) // block_bytes
+    _need(dst, nbytes, "dst")
+    _need(payload, payload_bytes, "payload")
+    _need(comp_sizes, 4 * nb, "comp_sizes")
+    _need(comp_offsets, 8 * nb, "comp_offsets")
+    wsp, wsb = _ws(ws)
+    _check(_lib.lz4_decode_blocks(
+        _dev(payload, "payload", torch.uint8), payload_bytes, _dev(comp_offsets, "comp_offsets", torch.int64),
+        _dev(comp_sizes, "comp_sizes", torch.int32), nb, block_bytes, nbytes, _dev(dst, "dst"), mode,
+        _dev(d_status, "d_status", torch.int32), wsp, wsb, _stream(stream)), "lz4_decode_blocks")
+
+
+def fp8_block_quant(srcs, codes, scales, batch=1, stream=None):
+    """srcs: list of BF16/uint16 GPU tensors [batch, rows_i, cols] (or [rows_i, cols] when batch == 1)."""
+    cols = srcs[0].shape[-1]
+    R = sum(int(t.shape[-2]) for t in srcs)
+    for i, t in enumerate(srcs):
+        if t.shape[-1] != cols or (batch > 1 and (t.dim() != 3 or t.shape[0] != batch)):
+            raise ValueError(f"srcs[{i}] has shape {tuple(t.shape)}")
+    _need(codes, batch * R * cols, "codes")
+    _need(scales, 4 * batch * ((R + 127) // 128) * ((cols + 127) // 128), "scales")
+    ptrs = (ctypes.c_void_p * len(srcs))(*[_dev(s, f"srcs[{i}]", _U16) for i, s in enumerate(srcs)])
+    rows = (ctypes.c_int64 * len(srcs))(*[s.shape[-2] for s in srcs])
+    strides = (ctypes.c_int64 * len(srcs))(*[s.shape[-2] * cols for s in srcs]) if batch > 1 else None
+    _check(_lib.fp8_block_quant(
+        ctypes.cast(ptrs, ctypes.c_void_p), ctypes.cast(rows, ctypes.c_void_p), len(srcs), cols, batch,
+        None if strides is None else ctypes.cast(strides, ctypes.c_void_p),
+        _dev(codes, "codes", torch.uint8), _dev(scales, "scales", torch.float32), _stream(stream)),
+        "fp8_block_quant")

@@ -1,0 +1,94 @@
+// apply.hip -- row a4 (patch scatter-apply) and the dense XOR apply of row a2/a6.
+//
+// Scatter: the receiver overrides the listed positions with the replacement
+// bits; no floating-point addition, so no drift ("Taking Reinforcement Learning
+// Cross Datacenter", Nan Jiang talk, 11:08-11:30; PULSE technical summary,
+// "1. PULSESync", Ricostruzione).  Entries are read coalesced, four per lane
+// (int4 + ushort4 when the arrays allow it); because indices ascend, the 2-byte
+// stores of a wave land in a few neighbouring cache lines.
+//
+// XOR: dst ^= mask with 16-byte loads/stores ("GPU weight teleportation"
+// write-up, "XOR masks").
+#include "device.hpp"
+
+namespace pulse {
+
+__global__ __launch_bounds__(256) void k_apply_patch(uint16_t *__restrict__ b, int64_t n,
+                                                     const int32_t *__restrict__ idx,
+                                                     const uint16_t *__restrict__ val,
+                                                     const int64_t *__restrict__ d_count,
+                                                     int64_t max_count, uint32_t *d_status,
+                                                     bool vec) {
+    int64_t count = *d_count;
+    if (count > max_count) count = max_count;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
+    bool bad = false;
+    for (int64_t k = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; k < count; k += stride) {
+        int32_t ii[4];
+        uint16_t vv[4];
+        if (vec && k + 3 < count) {
+            const int4 i4 = *reinterpret_cast<const int4 *>(idx + k);
+            const ushort4 v4 = *reinterpret_cast<const ushort4 *>(val + k);
+            ii[0] = i4.x; ii[1] = i4.y; ii[2] = i4.z; ii[3] = i4.w;
+            vv[0] = v4.x; vv[1] = v4.y; vv[2] = v4.z; vv[3] = v4.w;
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                ii[q] = (k + q < count) ? idx[k + q] : -1;
+                vv[q] = (k + q < count) ? val[k + q] : 0;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (k + q >= count) break;
+            const int64_t i = ii[q];
+            if (i >= 0 && i < n) b[i] = vv[q];
+            else bad = true;
+        }
+    }
+    if (__ballot(bad) && lane_id() == 0) or_agent32(d_status, 2u /*PULSE_DS_BADINDEX*/);
+}
+
+__global__ __launch_bounds__(256) void k_xor_apply(uint8_t *__restrict__ dst,
+                                                   const uint8_t *__restrict__ mask,
+                                                   int64_t nbytes) {
+    const int64_t nvec = nbytes / 16;
+    uint4 *d4 = reinterpret_cast<uint4 *>(dst);
+    const uint4 *m4 = reinterpret_cast<const uint4 *>(mask);
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec; v += stride) {
+        uint4 d = d4[v];
+        const uint4 m = m4[v];
+        d.x ^= m.x; d.y ^= m.y; d.z ^= m.z; d.w ^= m.w;
+        d4[v] = d;
+    }
+    if (blockIdx.x == 0 && threadIdx.x < (nbytes & 15)) {
+        const int64_t i = nvec * 16 + threadIdx.x;
+        dst[i] ^= mask[i];
+    }
+}
+
+}  // namespace pulse
+
+using namespace pulse;
+
+extern "C" int pulse_launch_apply_patch(uint16_t *b, int64_t n, const int32_t *idx, const uint16_t *val,
+                                        const int64_t *d_count, int64_t max_count, uint32_t *d_status,
+                                        hipStream_t stream) {
+    int64_t blocks = (max_count + 1023) / 1024;
+    if (blocks > 256 * 32) blocks = 256 * 32;
+    if (blocks < 1) blocks = 1;
+    const bool vec = ((uintptr_t)idx % 16 == 0) && ((uintptr_t)val % 8 == 0);
+    k_apply_patch<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(b, n, idx, val, d_count, max_count,
+                                                                   d_status, vec);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+extern "C" int pulse_launch_xor_apply(void *dst, const void *mask, int64_t nbytes, hipStream_t stream) {
+    int64_t blocks = (nbytes / 16 + 255) / 256;
+    if (blocks > 256 * 64) blocks = 256 * 64;
+    if (blocks < 1) blocks = 1;
+    k_xor_apply<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(static_cast<uint8_t *>(dst),
+                                                                 static_cast<const uint8_t *>(mask), nbytes);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}

@@ -1,0 +1,180 @@
+// capi.cpp -- the C ABI of include/pulse.h: argument checks, workspace sizing
+// and dispatch to the kernel launchers.  No device memory is allocated here;
+// nothing is enqueued when a check fails.
+#include "../../include/pulse.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+extern "C" {
+int pulse_launch_cast_diff(const float *, const uint16_t *, const uint16_t *, uint16_t *, uint16_t *,
+                           int32_t *, uint16_t *, int64_t, int64_t *, uint32_t *, int64_t, void *,
+                           hipStream_t);
+size_t pulse_cast_diff_ws_bytes(int64_t n);
+int pulse_launch_apply_patch(uint16_t *, int64_t, const int32_t *, const uint16_t *, const int64_t *,
+                             int64_t, uint32_t *, hipStream_t);
+int pulse_launch_xor_apply(void *, const void *, int64_t, hipStream_t);
+size_t pulse_lz4_encode_ws_bytes(int64_t nbytes, int32_t block_bytes);
+int pulse_launch_lz4_encode(const void *, const void *, int64_t, int32_t, uint8_t *, int64_t, uint32_t *,
+                            uint64_t *, uint64_t *, uint32_t *, void *, hipStream_t);
+size_t pulse_lz4_decode_ws_bytes(int64_t nblocks, int64_t payload_bytes);
+int pulse_launch_lz4_decode(const uint8_t *, int64_t, const uint64_t *, const uint32_t *, int64_t, int32_t,
+                            int64_t, void *, int32_t, uint32_t *, void *, hipStream_t);
+int pulse_launch_fp8_block_quant(const uint16_t *const *, const int64_t *, int32_t, int64_t, int64_t,
+                                 const int64_t *, uint8_t *, float *, hipStream_t);
+int pulse_launch_fill_zero(void *, size_t, hipStream_t);
+int pulse_launch_write_count(int64_t *, int64_t, hipStream_t);
+}
+
+namespace {
+
+constexpr int64_t kMaxIndexed = 2147483647;    // int32 patch indices
+constexpr int64_t kMaxPayload = (1ll << 39) - 2; // look-back value field
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char *pulse_version(void) { return "0.1.0"; }
+
+const char *pulse_status_string(int code) {
+    switch (code) {
+    case PULSE_OK: return "PULSE_OK";
+    case PULSE_EINVAL: return "PULSE_EINVAL: invalid argument";
+    case PULSE_EALIGN: return "PULSE_EALIGN: buffer not 16-byte aligned";
+    case PULSE_ERANGE: return "PULSE_ERANGE: size beyond the supported range";
+    case PULSE_EWORKSPACE: return "PULSE_EWORKSPACE: workspace missing or too small";
+    case PULSE_EHIP: return "PULSE_EHIP: kernel launch failed";
+    default: return "unknown pulse status";
+    }
+}
+
+size_t pulse_workspace_bytes(int op, int64_t n, int64_t aux) {
+    if (n < 0) return 0;
+    switch (op) {
+    case PULSE_OP_CAST_DIFF:
+    case PULSE_OP_COMPACT: return pulse_cast_diff_ws_bytes(n);
+    case PULSE_OP_LZ4_ENCODE:
+        if (aux <= 0) return 0;
+        return pulse_lz4_encode_ws_bytes(n, (int32_t)aux);
+    case PULSE_OP_LZ4_DECODE:
+        if (aux < 0) return 0;
+        return pulse_lz4_decode_ws_bytes(n, aux);
+    default: return 0;
+    }
+}
+
+int pulse_workspace_init(void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (!ws) return PULSE_EINVAL;
+    if (ws_bytes == 0) return PULSE_OK;
+    return pulse_launch_fill_zero(ws, ws_bytes, stream);
+}
+
+int pulse_cast_diff(const float *w_new, const uint16_t *b_old, uint16_t *b_new, uint16_t *xor_mask,
+                    int32_t *patch_idx, uint16_t *patch_val, int64_t patch_cap, int64_t *d_count,
+                    uint32_t *d_status, int64_t n, void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (!w_new || n < 0) return PULSE_EINVAL;
+    const bool patch = patch_idx || patch_val || d_count;
+    if (patch && !(patch_idx && patch_val && d_count && d_status)) return PULSE_EINVAL;
+    if (!b_old && (xor_mask || patch)) return PULSE_EINVAL;
+    if (!b_new && !xor_mask && !patch) return PULSE_EINVAL;  // nothing to produce
+    if (patch_cap < 0) return PULSE_EINVAL;
+    if (!aligned16(w_new) || (b_old && !aligned16(b_old)) || (b_new && !aligned16(b_new)) ||
+        (xor_mask && !aligned16(xor_mask)))
+        return PULSE_EALIGN;
+    if (patch) {
+        if (n > kMaxIndexed) return PULSE_ERANGE;
+        if (!ws || ws_bytes < pulse_cast_diff_ws_bytes(n)) return PULSE_EWORKSPACE;
+        if (n == 0) return pulse_launch_write_count(d_count, 0, stream);
+    }
+    if (n == 0) return PULSE_OK;
+    return pulse_launch_cast_diff(w_new, nullptr, b_old, b_new, xor_mask, patch_idx, patch_val, patch_cap,
+                                  d_count, d_status, n, ws, stream);
+}
+
+int pulse_compact(const uint16_t *b_old, const uint16_t *b_new, int32_t *patch_idx, uint16_t *patch_val,
+                  int64_t patch_cap, int64_t *d_count, uint32_t *d_status, int64_t n, void *ws,
+                  size_t ws_bytes, hipStream_t stream) {
+    if (!b_old || !b_new || !patch_idx || !patch_val || !d_count || !d_status || n < 0 || patch_cap < 0)
+        return PULSE_EINVAL;
+    if (!aligned16(b_old) || !aligned16(b_new)) return PULSE_EALIGN;
+    if (n > kMaxIndexed) return PULSE_ERANGE;
+    if (!ws || ws_bytes < pulse_cast_diff_ws_bytes(n)) return PULSE_EWORKSPACE;
+    if (n == 0) return pulse_launch_write_count(d_count, 0, stream);
+    return pulse_launch_cast_diff(nullptr, b_new, b_old, nullptr, nullptr, patch_idx, patch_val, patch_cap,
+                                  d_count, d_status, n, ws, stream);
+}
+
+int pulse_apply_patch(uint16_t *b, int64_t n, const int32_t *patch_idx, const uint16_t *patch_val,
+                      const int64_t *d_count, int64_t max_count, uint32_t *d_status, hipStream_t stream) {
+    if (!b || !patch_idx || !patch_val || !d_count || !d_status || n < 0 || max_count < 0)
+        return PULSE_EINVAL;
+    if (n > kMaxIndexed + 1) return PULSE_ERANGE;
+    if (max_count == 0) return PULSE_OK;
+    return pulse_launch_apply_patch(b, n, patch_idx, patch_val, d_count, max_count, d_status, stream);
+}
+
+int xor_mask_apply(void *dst, const void *mask, int64_t nbytes, hipStream_t stream) {
+    if (!dst || !mask || nbytes < 0) return PULSE_EINVAL;
+    if (!aligned16(dst) || !aligned16(mask)) return PULSE_EALIGN;
+    if (nbytes == 0) return PULSE_OK;
+    return pulse_launch_xor_apply(dst, mask, nbytes, stream);
+}
+
+int lz4_encode_blocks(const void *src, const void *src_xor, int64_t nbytes, int32_t block_bytes,
+                      uint8_t *payload, int64_t payload_cap, uint32_t *comp_sizes, uint64_t *comp_offsets,
+                      uint64_t *d_total, uint32_t *d_status, void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (!src || !payload || !comp_sizes || !comp_offsets || !d_total || !d_status || nbytes <= 0 ||
+        payload_cap < 0)
+        return PULSE_EINVAL;
+    if (block_bytes <= 0 || block_bytes > 65536 || block_bytes % 16384 != 0) return PULSE_EINVAL;
+    if (!aligned16(src) || (src_xor && !aligned16(src_xor))) return PULSE_EALIGN;
+    const int64_t nb = (nbytes + block_bytes - 1) / block_bytes;
+    if (nb > 0xFFFFFFFFll || nbytes > kMaxPayload / 2) return PULSE_ERANGE;
+    if (!ws || ws_bytes < pulse_lz4_encode_ws_bytes(nbytes, block_bytes)) return PULSE_EWORKSPACE;
+    return pulse_launch_lz4_encode(src, src_xor, nbytes, block_bytes, payload, payload_cap, comp_sizes,
+                                   comp_offsets, d_total, d_status, ws, stream);
+}
+
+int lz4_decode_blocks(const uint8_t *payload, int64_t payload_bytes, const uint64_t *comp_offsets,
+                      const uint32_t *comp_sizes, int64_t nblocks, int32_t block_bytes, int64_t nbytes,
+                      void *dst, int32_t mode, uint32_t *d_status, void *ws, size_t ws_bytes,
+                      hipStream_t stream) {
+    if (!payload || !comp_offsets || !comp_sizes || !dst || !d_status || payload_bytes < 0 || nbytes <= 0 ||
+        nblocks <= 0)
+        return PULSE_EINVAL;
+    if (mode != 0 && mode != 1) return PULSE_EINVAL;
+    if (block_bytes <= 0 || block_bytes > 65536 || block_bytes % 16 != 0) return PULSE_EINVAL;
+    if (nblocks != (nbytes + block_bytes - 1) / block_bytes) return PULSE_EINVAL;
+    if (!aligned16(dst)) return PULSE_EALIGN;
+    if (payload_bytes > kMaxPayload || nblocks > 0x3FFFFFFFll) return PULSE_ERANGE;
+    if (!ws || ws_bytes < pulse_lz4_decode_ws_bytes(nblocks, payload_bytes)) return PULSE_EWORKSPACE;
+    return pulse_launch_lz4_decode(payload, payload_bytes, comp_offsets, comp_sizes, nblocks, block_bytes, nbytes,
+                                   dst, mode, d_status, ws, stream);
+}
+
+int fp8_block_quant(const uint16_t *const *srcs, const int64_t *src_rows, int32_t nsrc, int64_t cols,
+                    int64_t batch, const int64_t *src_batch_stride, uint8_t *codes, float *scales,
+                    hipStream_t stream) {
+    if (!srcs || !src_rows || !codes || !scales || nsrc < 1 || nsrc > 8 || cols <= 0 || batch < 1)
+        return PULSE_EINVAL;
+    if (cols % 8 != 0) return PULSE_EINVAL;
+    if (batch > 1 && !src_batch_stride) return PULSE_EINVAL;
+    int64_t R = 0;
+    for (int i = 0; i < nsrc; ++i) {
+        if (!srcs[i] || src_rows[i] < 0) return PULSE_EINVAL;
+        if (!aligned16(srcs[i])) return PULSE_EALIGN;
+        if (batch > 1 && (src_batch_stride[i] < 0 || src_batch_stride[i] % 8 != 0)) return PULSE_EALIGN;
+        R += src_rows[i];
+    }
+    if (R == 0) return PULSE_EINVAL;
+    if ((R + 127) / 128 > 65535 || batch > 65535 || (cols + 127) / 128 > 0x7FFFFFFF) return PULSE_ERANGE;
+    if (reinterpret_cast<uintptr_t>(codes) % 8 != 0 || reinterpret_cast<uintptr_t>(scales) % 4 != 0)
+        return PULSE_EALIGN;
+    return pulse_launch_fp8_block_quant(srcs, src_rows, nsrc, cols, batch, src_batch_stride, codes, scales, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,249 @@
+// device.hpp -- gfx950 building blocks shared by the codec kernels:
+// wave64 scans/reductions, agent-scope status words and the decoupled
+// look-back prefix (Merrill & Garland, "Single-pass Parallel Prefix Scan with
+// Decoupled Look-back", 2016) used to place per-tile outputs in order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pulse {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+__device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
+
+// ---- wave-level scans and reductions (ds_bpermute based shuffles) ----------
+template <typename T>
+__device__ __forceinline__ T wave_incl_sum(T v) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        T o = __shfl_up(v, d, kWave);
+        if (lane >= d) v += o;
+    }
+    return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_incl_max(T v) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        T o = __shfl_up(v, d, kWave);
+        if (lane >= d) v = o > v ? o : v;
+    }
+    return v;
+}
+
+// inclusive scan from the top lane down: lane l gets min(v[l..63])
+template <typename T>
+__device__ __forceinline__ T wave_incl_min_rev(T v) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        T o = __shfl_down(v, d, kWave);
+        if (lane + d < kWave) v = o < v ? o : v;
+    }
+    return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_reduce_max(T v) {
+#pragma unroll
+    for (int d = kWave / 2; d > 0; d >>= 1) {
+        T o = __shfl_xor(v, d, kWave);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_reduce_sum(T v) {
+#pragma unroll
+    for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
+    return v;
+}
+
+// ---- block-level scans (NW waves); `sh` holds NW entries, one barrier pair ---
+// exclusive sum; returns the thread's exclusive prefix, *total the block sum
+template <int NW, typename T>
+__device__ __forceinline__ T block_excl_sum(T v, T *sh, T *total) {
+    T incl = wave_incl_sum(v);
+    if (lane_id() == kWave - 1) sh[wave_id()] = incl;
+    __syncthreads();
+    T base = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        T x = sh[w];
+        if (w < wave_id()) base += x;
+        tot += x;
+    }
+    __syncthreads();
+    *total = tot;
+    return base + incl - v;
+}
+
+// exclusive max over lower threads (identity `lo`), *total = block max
+template <int NW, typename T>
+__device__ __forceinline__ T block_excl_max(T v, T lo, T *sh, T *total) {
+    T incl = wave_incl_max(v);
+    T excl = __shfl_up(incl, 1, kWave);
+    if (lane_id() == 0) excl = lo;
+    if (lane_id() == kWave - 1) sh[wave_id()] = incl;
+    __syncthreads();
+    T base = lo, tot = lo;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        T x = sh[w];
+        if (w < wave_id()) base = x > base ? x : base;
+        tot = x > tot ? x : tot;
+    }
+    __syncthreads();
+    *total = tot;
+    return excl > base ? excl : base;
+}
+
+// exclusive min over higher threads (identity `hi`)
+template <int NW, typename T>
+__device__ __forceinline__ T block_excl_min_rev(T v, T hi, T *sh) {
+    T incl = wave_incl_min_rev(v);
+    T excl = __shfl_down(incl, 1, kWave);
+    if (lane_id() == kWave - 1) excl = hi;
+    if (lane_id() == 0) sh[wave_id()] = incl;
+    __syncthreads();
+    T base = hi;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        T x = sh[w];
+        if (w > wave_id()) base = x < base ? x : base;
+    }
+    __syncthreads();
+    return excl < base ? excl : base;
+}
+
+// ---- agent-scope (whole-device) atomics --------------------------------------
+// MI355X has one L2 per XCD; agent-scope atomic loads/stores make the status
+// words coherent across the eight XCDs.
+__device__ __forceinline__ uint64_t ld_agent(const uint64_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(uint64_t *p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_agent32(const uint32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent32(uint32_t *p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t add_agent32(uint32_t *p, uint32_t v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void or_agent32(uint32_t *p, uint32_t v) {
+    __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---- workspace layout shared by every single-pass (look-back) kernel --------
+// [0, 256): header; [256, ...): one 64-bit status word per tile.
+// status word: [63:40] epoch tag (never 0), [39] inclusive flag, [38:0] value.
+struct WsHeader {
+    uint32_t epoch;   // calls completed on this workspace, mod kTagMod
+    uint32_t ticket;  // dynamic tile ids handed out in the current call
+    uint32_t done;    // tiles finished in the current call
+    uint32_t aux;     // per-op counter (decode: slow-block count)
+    uint32_t aux2;    // per-op counter (decode: slow-kernel blocks finished)
+    uint32_t pad[59];
+};
+static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
+
+constexpr uint32_t kTagMod = 0xFFFFFFu;
+constexpr uint64_t kValueMask = (1ull << 39) - 1;
+constexpr uint64_t kInclusive = 1ull << 39;
+
+__device__ __forceinline__ uint64_t make_status(uint32_t tag, bool inclusive, uint64_t v) {
+    return ((uint64_t)tag << 40) | (inclusive ? kInclusive : 0ull) | (v & kValueMask);
+}
+
+// Per-call prologue, thread 0 only: the tile id (ticket order == start order,
+// so every tile this one waits on is already resident) and this call's tag.
+__device__ __forceinline__ void ws_begin(WsHeader *h, uint32_t *tile, uint32_t *tag) {
+    *tile = add_agent32(&h->ticket, 1u);
+    *tag = (ld_agent32(&h->epoch) % kTagMod) + 1u;
+}
+
+// Per-call epilogue, thread 0 only, after the tile's last status access: the
+// last tile to finish rearms the header for the next call on this workspace.
+__device__ __forceinline__ void ws_end(WsHeader *h, uint32_t ntiles) {
+    uint32_t d = add_agent32(&h->done, 1u);
+    if (d == ntiles - 1) {
+        st_agent32(&h->ticket, 0u);
+        st_agent32(&h->done, 0u);
+        st_agent32(&h->epoch, (ld_agent32(&h->epoch) + 1u) % kTagMod);
+    }
+}
+
+// Decoupled look-back, executed by one full wave (all 64 lanes) of the tile.
+// Publishes the tile's aggregate, sums predecessors' aggregates until one with
+// an inclusive prefix is found, publishes the tile's inclusive prefix and
+// returns the exclusive prefix (identical in every lane).
+// MAX = true combines with max instead of +.
+template <bool MAX = false>
+__device__ __forceinline__ uint64_t lookback_wave(uint64_t *status, uint32_t tile, uint32_t tag,
+                                                  uint64_t aggregate) {
+    const int lane = lane_id();
+    if (tile == 0) {
+        if (lane == 0) st_agent(&status[0], make_status(tag, true, aggregate));
+        return 0;
+    }
+    if (lane == 0) st_agent(&status[tile], make_status(tag, false, aggregate));
+
+    uint64_t prefix = 0;
+    int64_t j = (int64_t)tile - 1;  // newest predecessor the window starts at
+    while (true) {
+        const int64_t p = j - lane;
+        uint64_t w = 0;
+        bool valid, incl;
+        while (true) {
+            if (p >= 0) w = ld_agent(&status[p]);
+            valid = p < 0 || (uint32_t)(w >> 40) == tag;
+            incl = p >= 0 && valid && (w & kInclusive);
+            const uint64_t vmask = __ballot(valid);
+            const uint64_t imask = __ballot(incl);
+            if (imask) {
+                const int stop = __builtin_ctzll(imask);
+                const uint64_t need = (stop == 63) ? ~0ull : ((2ull << stop) - 1);
+                if ((vmask & need) == need) break;
+            } else if (vmask == ~0ull) {
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        const uint64_t imask = __ballot(incl);
+        uint64_t mine = (p >= 0) ? (w & kValueMask) : 0;
+        const int stop = imask ? __builtin_ctzll(imask) : kWave;
+        if (lane > stop) mine = 0;
+        if constexpr (MAX) {
+            const uint64_t r = wave_reduce_max(mine);
+            prefix = r > prefix ? r : prefix;
+        } else {
+            prefix += wave_reduce_sum(mine);
+        }
+        if (imask) break;
+        j -= kWave;
+    }
+    uint64_t incl_v;
+    if constexpr (MAX) incl_v = aggregate > prefix ? aggregate : prefix;
+    else incl_v = prefix + aggregate;
+    if (lane == 0) st_agent(&status[tile], make_status(tag, true, incl_v));
+    return prefix;
+}
+
+__device__ __forceinline__ uint16_t bf16_rne(uint32_t x) {
+    // nearest BF16, ties to even; NaN -> quiet NaN with sign and top payload
+    if ((x & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((x >> 16) | 0x40u);
+    return (uint16_t)((x + 0x7FFFu + ((x >> 16) & 1u)) >> 16);
+}
+
+}  // namespace pulse

@@ -1,0 +1,141 @@
+// fp8_quant.hip -- row a7: projection fusion (stacking) + BF16 -> FP8-E4M3
+// quantisation per 128x128 block with FP32 scales.
+//
+// The sender rebuilds the full weight, fuses projections and quantises BF16
+// training weights for FP8 inference ("Weight transfer for RL post-training in
+// under 2 seconds", opening paragraph and "Potok zadan").  Format: OCP E4M3
+// "fn" (bias 7, largest finite 448, no Inf).  Per block: amax = max |x|,
+// s = amax / 448 (IEEE float32 division; 1 when amax == 0), code =
+// E4M3(x / s) with an IEEE division and round-to-nearest-even, saturating.
+//
+// One workgroup per (expert, block row, block column).  Thread t covers
+// columns [8*(t%16), +8) of rows t/16 + 16*i, i = 0..7: every load instruction
+// of a wave reads four complete 256-byte block rows, every store writes four
+// 128-byte code rows.  The block is read once (kept in registers between the
+// amax reduction and the quantisation).
+#include "device.hpp"
+
+namespace pulse {
+
+constexpr int FQ_MAXSRC = 8;
+
+struct QuantArgs {
+    const uint16_t *src[FQ_MAXSRC];
+    int64_t row0[FQ_MAXSRC + 1];  // first stacked row of each source, row0[nsrc] = R
+    int64_t bstride[FQ_MAXSRC];
+    int32_t nsrc;
+    int64_t cols;
+    int64_t R;
+    int64_t nbc;
+    uint8_t *codes;
+    float *scales;
+};
+
+// E4M3 "fn" code of a finite float32, round to nearest even, saturating
+__device__ __forceinline__ uint32_t e4m3_code(float q) {
+    const uint32_t bits = __float_as_uint(q);
+    const uint32_t sign = (bits >> 24) & 0x80u;
+    const uint32_t a = bits & 0x7FFFFFFFu;
+    uint32_t code;
+    if (a >= 0x43E00000u) {  // |q| >= 448: the largest finite value
+        code = 0x7Eu;
+    } else if (a < 0x3C800000u) {  // |q| < 2^-6: multiples of 2^-9
+        // adding 1.5*2^14 (ulp 2^-9) rounds |q| to the grid; the bit-pattern
+        // difference is the number of 2^-9 steps
+        const float r = __uint_as_float(a) + 24576.0f;
+        code = __float_as_uint(r) - 0x46C00000u;
+    } else {
+        // keep 3 mantissa bits with round-to-nearest-even on the other 20, then
+        // rebias the exponent from 127 to 7
+        code = ((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
+    }
+    return sign | code;
+}
+
+__global__ __launch_bounds__(256) void k_fp8_block_quant(QuantArgs a) {
+    __shared__ uint32_t s_red[4];
+    const int t = threadIdx.x;
+    const int64_t bc = blockIdx.x, br = blockIdx.y, e = blockIdx.z;
+    const int rg = t >> 4, seg = t & 15;
+    const int64_t col = bc * 128 + seg * 8;
+    const bool col_ok = col < a.cols;  // cols is a multiple of 8
+
+    uint4 v[8];
+    bool ok[8];
+    uint32_t amax = 0;  // max |x| as BF16 magnitude bits (ordered like the values)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t r = br * 128 + rg + 16 * i;
+        ok[i] = col_ok && r < a.R;
+        v[i] = make_uint4(0, 0, 0, 0);
+        if (ok[i]) {
+            int s = 0;
+#pragma unroll
+            for (int k = 1; k < FQ_MAXSRC; ++k)
+                if (k < a.nsrc && r >= a.row0[k]) s = k;
+            const uint16_t *p = a.src[s] + e * a.bstride[s] + (r - a.row0[s]) * a.cols + col;
+            v[i] = *reinterpret_cast<const uint4 *>(p);
+            const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t lo = w[k] & 0x7FFFu, hi = (w[k] >> 16) & 0x7FFFu;
+                amax = lo > amax ? lo : amax;
+                amax = hi > amax ? hi : amax;
+            }
+        }
+    }
+    amax = wave_reduce_max(amax);
+    if (lane_id() == 0) s_red[wave_id()] = amax;
+    __syncthreads();
+    amax = s_red[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) amax = s_red[w] > amax ? s_red[w] : amax;
+
+    const float amax_f = __uint_as_float(amax << 16);
+    const float s = amax == 0 ? 1.0f : amax_f / 448.0f;  // IEEE division
+    if (t == 0) a.scales[(e * ((a.R + 127) / 128) + br) * a.nbc + bc] = s;
+
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        if (!ok[i]) continue;
+        const int64_t r = br * 128 + rg + 16 * i;
+        const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+        uint32_t packed[2] = {0, 0};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float x0 = __uint_as_float(w[k] << 16);
+            const float x1 = __uint_as_float(w[k] & 0xFFFF0000u);
+            const uint32_t c0 = e4m3_code(x0 / s);  // IEEE division
+            const uint32_t c1 = e4m3_code(x1 / s);
+            packed[k >> 1] |= (c0 | (c1 << 8)) << (16 * (k & 1));
+        }
+        *reinterpret_cast<uint2 *>(a.codes + (e * a.R + r) * a.cols + col) = make_uint2(packed[0], packed[1]);
+    }
+}
+
+}  // namespace pulse
+
+using namespace pulse;
+
+extern "C" int pulse_launch_fp8_block_quant(const uint16_t *const *srcs, const int64_t *src_rows, int32_t nsrc,
+                                            int64_t cols, int64_t batch, const int64_t *src_batch_stride,
+                                            uint8_t *codes, float *scales, hipStream_t stream) {
+    QuantArgs a{};
+    int64_t R = 0;
+    for (int i = 0; i < nsrc; ++i) {
+        a.src[i] = srcs[i];
+        a.row0[i] = R;
+        a.bstride[i] = src_batch_stride ? src_batch_stride[i] : 0;
+        R += src_rows[i];
+    }
+    for (int i = nsrc; i <= FQ_MAXSRC; ++i) a.row0[i] = R;
+    a.nsrc = nsrc;
+    a.cols = cols;
+    a.R = R;
+    a.nbc = (cols + 127) / 128;
+    a.codes = codes;
+    a.scales = scales;
+    const dim3 g((unsigned)a.nbc, (unsigned)((R + 127) / 128), (unsigned)batch);
+    k_fp8_block_quant<<<g, dim3(256), 0, stream>>>(a);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}

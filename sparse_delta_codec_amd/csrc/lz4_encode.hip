@@ -1,0 +1,284 @@
+// lz4_encode.hip -- row a5: LZ4 block encoding of the XOR mask.
+//
+// The pages pick LZ4 because it codes long runs in few commands and RL masks
+// are long zero runs ("GPU weight teleportation" write-up, "Moving the
+// pipeline onto GPUs"; the masks are mostly zero, "XOR masks").  The byte
+// format is the public LZ4 block format.  LZ4 encodings are not unique; this
+// encoder emits the canonical "offset-1 run" parse: every maximal run of one
+// byte value [s, e) with i = s+1, j = min(e, n-5), j-i >= 4 and i <= n-12 is
+// one sequence (literals since the previous such run, then a match of offset 1
+// and length j-i); the rest of the block is the final literal run.  Because a
+// run's sequence depends only on its own (s, e, n), a block is parsed in
+// parallel and the output is bit-for-bit deterministic.
+//
+// One workgroup per 64 KiB block (dynamic block ids):
+//  1. coalesced 16-byte loads (XOR of two sources when given) into LDS, each
+//     256-byte thread chunk padded by 16 bytes so chunk reads avoid bank
+//     conflicts;
+//  2. per thread: SWAR run-boundary bitmask of its chunk (1 bit per byte);
+//  3. block scans: next boundary after each chunk (suffix min), last
+//     qualifying j before it (prefix max), first qualifying i after it (suffix
+//     min), then the byte size of each thread's sequences (prefix sum);
+//  4. decoupled look-back over blocks gives the block's payload offset;
+//  5. each thread writes its sequences' headers and the literal bytes of its
+//     own chunk at their final positions.
+#include "device.hpp"
+
+namespace pulse {
+
+constexpr int LZE_THREADS = 256;
+constexpr int LZE_MAX_BLOCK = 65536;
+constexpr int LZE_LDS = LZE_MAX_BLOCK + LZE_MAX_BLOCK / 16;  // 16 B pad per 256 B chunk
+constexpr int32_t LZE_INF = 0x7FFFFFFF;
+
+struct Lz4EncArgs {
+    const uint8_t *src;
+    const uint8_t *src_xor;
+    int64_t nbytes;
+    int32_t block_bytes;
+    int32_t chunk;  // block_bytes / 256, a multiple of 64
+    uint8_t *payload;
+    int64_t cap;
+    uint32_t *comp_sizes;
+    uint64_t *comp_offsets;
+    uint64_t *d_total;
+    uint32_t *d_status;
+    WsHeader *hdr;
+    uint64_t *status;
+    uint32_t nblocks;
+};
+
+__device__ __forceinline__ int32_t ext_bytes(int32_t v) { return v >= 15 ? (v - 15) / 255 + 1 : 0; }
+
+__device__ __forceinline__ int32_t seq_bytes(int32_t ll, int32_t ml) {
+    return 1 + ext_bytes(ll) + ll + 2 + ext_bytes(ml - 4);
+}
+
+// bit k of the result is set iff byte k of x is non-zero
+__device__ __forceinline__ uint32_t nonzero_bytes(uint32_t x) {
+    const uint32_t hi = (((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x) & 0x80808080u;
+    return (((hi >> 7) * 0x00204081u) >> 21) & 0xFu;
+}
+
+__device__ __forceinline__ int next_bit(const uint64_t m[4], int from) {
+    // first set bit at position >= from (chunk-relative), or -1
+    for (int w = from >> 6; w < 4; ++w) {
+        uint64_t x = m[w];
+        if (w == (from >> 6)) x &= (~0ull) << (from & 63);
+        if (x) return w * 64 + __builtin_ctzll(x);
+    }
+    return -1;
+}
+
+// calls f(s, e) for every run that starts in this thread's chunk
+template <class F>
+__device__ __forceinline__ void for_each_run(const uint64_t m[4], int32_t cs, int32_t next_after, F f) {
+    int cur = next_bit(m, 0);
+    while (cur >= 0) {
+        const int nxt = (cur + 1 < 256) ? next_bit(m, cur + 1) : -1;
+        f(cs + cur, nxt >= 0 ? cs + nxt : next_after);
+        cur = nxt;
+    }
+}
+
+// byte writer for one block's slot of the payload; never writes past `lim`
+struct Out {
+    uint8_t *p;
+    int32_t lim;
+    __device__ __forceinline__ void put(int32_t pos, uint32_t v) const {
+        if (pos >= 0 && pos < lim) p[pos] = (uint8_t)v;
+    }
+};
+
+__device__ __forceinline__ int32_t put_len(const Out &out, int32_t pos, int32_t v) {
+    // extra length bytes of a nibble capped at 15: 255s then a byte < 255
+    int32_t rem = v - 15;
+    while (rem >= 255) {
+        out.put(pos++, 255);
+        rem -= 255;
+    }
+    out.put(pos++, (uint32_t)rem);
+    return pos;
+}
+
+__global__ __launch_bounds__(LZE_THREADS) void k_lz4_encode(Lz4EncArgs a) {
+    __shared__ __align__(16) uint8_t s_buf[LZE_LDS];
+    __shared__ int32_t s_i32[LZE_THREADS / kWave];
+    __shared__ uint32_t s_tile, s_tag;
+    __shared__ uint64_t s_off;
+
+    const int t = threadIdx.x;
+    if (t == 0) {
+        uint32_t tile, tag;
+        ws_begin(a.hdr, &tile, &tag);
+        s_tile = tile;
+        s_tag = tag;
+    }
+    __syncthreads();
+    const uint32_t b = s_tile, tag = s_tag;
+    const int64_t blk_base = (int64_t)b * a.block_bytes;
+    const int32_t len = (int32_t)((a.nbytes - blk_base) < a.block_bytes ? (a.nbytes - blk_base) : a.block_bytes);
+    const int32_t CH = a.chunk, stride = CH + 16;
+
+    // 1. load
+    const int32_t npieces = a.block_bytes / 16;
+    for (int32_t q = t; q < npieces; q += LZE_THREADS) {
+        const int32_t off = q * 16;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (off + 16 <= len) {
+            v = *reinterpret_cast<const uint4 *>(a.src + blk_base + off);
+            if (a.src_xor) {
+                const uint4 x = *reinterpret_cast<const uint4 *>(a.src_xor + blk_base + off);
+                v.x ^= x.x; v.y ^= x.y; v.z ^= x.z; v.w ^= x.w;
+            }
+        } else if (off < len) {
+            uint32_t w[4] = {0, 0, 0, 0};
+            for (int k = 0; k < len - off; ++k) {
+                uint32_t byte = a.src[blk_base + off + k];
+                if (a.src_xor) byte ^= a.src_xor[blk_base + off + k];
+                w[k >> 2] |= byte << (8 * (k & 3));
+            }
+            v = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+        *reinterpret_cast<uint4 *>(s_buf + (off / CH) * stride + (off % CH)) = v;
+    }
+    __syncthreads();
+
+    // 2. run-boundary bitmask of this thread's chunk
+    const int32_t cs = t * CH;
+    const int32_t cl = len - cs < 0 ? 0 : (len - cs < CH ? len - cs : CH);
+    const uint8_t *mine = s_buf + t * stride;
+    uint64_t m[4] = {0, 0, 0, 0};
+    if (cl > 0) {
+        uint32_t pb = (t > 0) ? s_buf[(t - 1) * stride + CH - 1] : 0u;
+        for (int32_t q = 0; q < CH; q += 16) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(mine + q);
+            const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int32_t p0 = q + 4 * k;
+                uint32_t nib = nonzero_bytes(d[k] ^ ((d[k] << 8) | pb));
+                pb = d[k] >> 24;
+                if (t == 0 && p0 == 0) nib |= 1u;  // a run starts at the block start
+                if (p0 + 4 > cl) nib &= (p0 >= cl) ? 0u : ((1u << (cl - p0)) - 1u);
+                m[p0 >> 6] |= (uint64_t)nib << (p0 & 63);
+            }
+        }
+    }
+    const int fb = next_bit(m, 0);
+    const int32_t first_b = fb >= 0 ? cs + fb : len;
+    const int32_t next_after = block_excl_min_rev<LZE_THREADS / kWave>(first_b, len, s_i32);
+
+    // 3a. qualifying runs of this chunk
+    int32_t first_qi = LZE_INF, last_qj = 0;
+    for_each_run(m, cs, next_after, [&](int32_t s, int32_t e) {
+        const int32_t i = s + 1, j = e < len - 5 ? e : len - 5;
+        if (j - i >= 4 && i <= len - 12) {
+            if (first_qi == LZE_INF) first_qi = i;
+            last_qj = j;
+        }
+    });
+    int32_t a_final;
+    const int32_t carry_j = block_excl_max<LZE_THREADS / kWave>(last_qj, 0, s_i32, &a_final);
+    const int32_t next_qi = block_excl_min_rev<LZE_THREADS / kWave>(first_qi, LZE_INF, s_i32);
+
+    // 3b. bytes of the sequences this thread owns
+    int32_t tot = 0;
+    {
+        int32_t la = carry_j;
+        for_each_run(m, cs, next_after, [&](int32_t s, int32_t e) {
+            const int32_t i = s + 1, j = e < len - 5 ? e : len - 5;
+            if (j - i >= 4 && i <= len - 12) {
+                tot += seq_bytes(i - la, j - i);
+                la = j;
+            }
+        });
+    }
+    int32_t qsum;
+    const int32_t pos0 = block_excl_sum<LZE_THREADS / kWave>(tot, s_i32, &qsum);
+    const int32_t ll_final = len - a_final;
+    const uint64_t comp = (uint64_t)qsum + 1 + ext_bytes(ll_final) + ll_final;
+
+    // 4. place the block
+    if (wave_id() == 0) {
+        const uint64_t off = lookback_wave(a.status, b, tag, comp);
+        if (lane_id() == 0) {
+            s_off = off;
+            a.comp_sizes[b] = (uint32_t)comp;
+            a.comp_offsets[b] = off;
+            if (b == a.nblocks - 1) *a.d_total = off + comp;
+            if ((int64_t)(off + comp) > a.cap) or_agent32(a.d_status, 1u /*PULSE_DS_CAPACITY*/);
+            ws_end(a.hdr, a.nblocks);
+        }
+    }
+    __syncthreads();
+    const uint64_t off = s_off;
+    if ((int64_t)(off + comp) > a.cap) return;
+    const Out out{a.payload + off, (int32_t)comp};
+
+    // 5. emit
+    int32_t la = carry_j, pos = pos0;
+    const int32_t chunk_end = cs + cl;
+    for_each_run(m, cs, next_after, [&](int32_t s, int32_t e) {
+        const int32_t i = s + 1, j = e < len - 5 ? e : len - 5;
+        if (!(j - i >= 4 && i <= len - 12)) return;
+        const int32_t ll = i - la, ml = j - i;
+        const int32_t h = 1 + ext_bytes(ll);
+        out.put(pos, ((ll >= 15 ? 15 : ll) << 4) | (ml - 4 >= 15 ? 15 : ml - 4));
+        if (ll >= 15) put_len(out, pos + 1, ll);
+        const int32_t lo = la > cs ? la : cs;
+        for (int32_t p = lo; p < i; ++p) out.put(pos + h + (p - la), mine[p - cs]);
+        int32_t q = pos + h + ll;
+        out.put(q++, 1);
+        out.put(q++, 0);
+        if (ml - 4 >= 15) q = put_len(out, q, ml - 4);
+        pos = q;
+        la = j;
+    });
+    {
+        // literals of this chunk that belong to the next sequence after it
+        const int32_t lo = la > cs ? la : cs;
+        if (lo < chunk_end) {
+            const int32_t ll = (next_qi != LZE_INF ? next_qi : len) - la;
+            const int32_t h = 1 + ext_bytes(ll);
+            for (int32_t p = lo; p < chunk_end; ++p) out.put(pos + h + (p - la), mine[p - cs]);
+        }
+    }
+    if (t == 0) {
+        out.put(qsum, (ll_final >= 15 ? 15 : ll_final) << 4);
+        if (ll_final >= 15) put_len(out, qsum + 1, ll_final);
+    }
+}
+
+}  // namespace pulse
+
+using namespace pulse;
+
+extern "C" size_t pulse_lz4_encode_ws_bytes(int64_t nbytes, int32_t block_bytes) {
+    const int64_t nb = block_bytes > 0 ? (nbytes + block_bytes - 1) / block_bytes : 0;
+    return sizeof(WsHeader) + (size_t)(nb > 0 ? nb : 1) * sizeof(uint64_t);
+}
+
+extern "C" int pulse_launch_lz4_encode(const void *src, const void *src_xor, int64_t nbytes,
+                                       int32_t block_bytes, uint8_t *payload, int64_t cap,
+                                       uint32_t *comp_sizes, uint64_t *comp_offsets, uint64_t *d_total,
+                                       uint32_t *d_status, void *ws, hipStream_t stream) {
+    Lz4EncArgs a{};
+    a.src = static_cast<const uint8_t *>(src);
+    a.src_xor = static_cast<const uint8_t *>(src_xor);
+    a.nbytes = nbytes;
+    a.block_bytes = block_bytes;
+    a.chunk = block_bytes / LZE_THREADS;
+    a.payload = payload;
+    a.cap = cap;
+    a.comp_sizes = comp_sizes;
+    a.comp_offsets = comp_offsets;
+    a.d_total = d_total;
+    a.d_status = d_status;
+    a.hdr = reinterpret_cast<WsHeader *>(ws);
+    a.status = reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + sizeof(WsHeader));
+    const int64_t nb = (nbytes + block_bytes - 1) / block_bytes;
+    a.nblocks = (uint32_t)nb;
+    k_lz4_encode<<<dim3((unsigned)nb), dim3(LZE_THREADS), 0, stream>>>(a);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}

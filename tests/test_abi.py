@@ -1,0 +1,101 @@
+"""CPU checks of the C ABI: the library loads, exports every entry point that
+include/pulse.h declares, and rejects bad arguments before touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pulse.h")
+LIB = os.path.join(ROOT, "sparse_delta_codec_amd", "libpulse.so")
+
+EINVAL, EALIGN, ERANGE, EWORKSPACE = -1, -2, -3, -4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail(f"{LIB} missing: run __graft_entry__.build()")
+    L = ctypes.CDLL(LIB)
+    L.pulse_status_string.restype = ctypes.c_char_p
+    L.pulse_version.restype = ctypes.c_char_p
+    L.pulse_workspace_bytes.restype = ctypes.c_size_t
+    L.pulse_workspace_bytes.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64]
+    return L
+
+
+def test_header_declares_the_codec_calls():
+    fns = declared_functions()
+    for name in ("pulse_cast_diff", "pulse_compact", "pulse_apply_patch", "xor_mask_apply",
+                 "lz4_encode_blocks", "lz4_decode_blocks", "fp8_block_quant", "pulse_workspace_bytes",
+                 "pulse_workspace_init", "pulse_status_string", "pulse_version"):
+        assert name in fns, name
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version(lib):
+    assert lib.pulse_status_string(0) == b"PULSE_OK"
+    assert b"aligned" in lib.pulse_status_string(EALIGN)
+    assert lib.pulse_version().count(b".") == 2
+
+
+def test_workspace_sizes(lib):
+    ws = lib.pulse_workspace_bytes
+    assert ws(1, 4096, 0) == 256 + 8 and ws(1, 4097, 0) == 256 + 16
+    assert ws(3, 65536 * 3 + 1, 65536) == 256 + 4 * 8
+    assert ws(4, 10, 1 << 20) > (1 << 20) // 32
+    assert ws(99, 10, 0) == 0
+
+
+V = ctypes.c_void_p
+I64 = ctypes.c_int64
+
+
+def test_argument_errors_return_before_any_launch(lib):
+    al = V(0x10000)      # aligned fake pointers, never dereferenced on these paths
+    mis = V(0x10002)
+    cd = lib.pulse_cast_diff
+    cd.argtypes = [V, V, V, V, V, V, I64, V, V, I64, V, ctypes.c_size_t, V]
+    assert cd(None, None, al, None, None, None, 0, None, None, 10, None, 0, None) == EINVAL
+    assert cd(al, None, None, None, None, None, 0, None, None, 10, None, 0, None) == EINVAL   # no output
+    assert cd(al, None, None, al, None, None, 0, None, None, 10, None, 0, None) == EINVAL     # mask needs old
+    assert cd(mis, None, al, None, None, None, 0, None, None, 10, None, 0, None) == EALIGN
+    assert cd(al, al, al, None, al, al, 10, al, al, 1 << 31, al, 1 << 40, None) == ERANGE
+    assert cd(al, al, al, None, al, al, 10, al, al, 100000, al, 64, None) == EWORKSPACE
+    assert cd(al, al, al, None, al, None, 10, al, al, 100, al, 1 << 20, None) == EINVAL      # partial patch
+    enc = lib.lz4_encode_blocks
+    enc.argtypes = [V, V, I64, ctypes.c_int32, V, I64, V, V, V, V, V, ctypes.c_size_t, V]
+    assert enc(al, None, 1000, 1000, al, 10, al, al, al, al, al, 1 << 20, None) == EINVAL    # block size
+    assert enc(mis, None, 1000, 65536, al, 10, al, al, al, al, al, 1 << 20, None) == EALIGN
+    assert enc(al, None, 1000, 65536, al, 10, al, al, al, al, al, 8, None) == EWORKSPACE
+    dec = lib.lz4_decode_blocks
+    dec.argtypes = [V, I64, V, V, I64, ctypes.c_int32, I64, V, ctypes.c_int32, V, V, ctypes.c_size_t, V]
+    assert dec(al, 10, al, al, 2, 65536, 70000, al, 2, al, al, 1 << 20, None) == EINVAL     # mode
+    assert dec(al, 10, al, al, 3, 65536, 70000, al, 1, al, al, 1 << 20, None) == EINVAL     # nblocks
+    assert dec(al, 10, al, al, 2, 65536, 70000, mis, 1, al, al, 1 << 20, None) == EALIGN
+    assert dec(al, 10, al, al, 2, 65536, 70000, al, 1, al, al, 16, None) == EWORKSPACE
+    q = lib.fp8_block_quant
+    q.argtypes = [V, V, ctypes.c_int32, I64, I64, V, V, V, V]
+    ptrs = (V * 1)(0x10000)
+    rows = (I64 * 1)(128)
+    assert q(ctypes.cast(ptrs, V), ctypes.cast(rows, V), 1, 100, 1, None, al, al, None) == EINVAL  # cols % 8
+    assert q(ctypes.cast(ptrs, V), ctypes.cast(rows, V), 9, 128, 1, None, al, al, None) == EINVAL  # nsrc
+    mptrs = (V * 1)(0x10002)
+    assert q(ctypes.cast(mptrs, V), ctypes.cast(rows, V), 1, 128, 1, None, al, al, None) == EALIGN
+    ap = lib.pulse_apply_patch
+    ap.argtypes = [V, I64, V, V, V, I64, V, V]
+    assert ap(al, 10, None, al, al, 5, al, None) == EINVAL
+    x = lib.xor_mask_apply
+    x.argtypes = [V, V, I64, V]
+    assert x(mis, al, 100, None) == EALIGN and x(al, al, -1, None) == EINVAL

@@ -1,0 +1,491 @@
+"""GPU parity of every C-ABI entry point against the CPU oracle (bit-exact).
+
+Sizes span several tiles / blocks plus ragged tails; the edge cases are the
+empty input, single elements, tile boundaries, all-changed / none-changed
+inputs, the RNE edge patterns, capacity overflow, bad indices, corrupt LZ4
+blocks and streams that need the decoder's general path.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workload
+
+pytestmark = pytest.mark.gpu
+
+try:
+    import sparse_delta_codec_amd as pulse
+except ImportError:
+    if torch.cuda.is_available():
+        raise  # on a GPU machine the HIP library must be there
+    pulse = None
+
+from tests.gpu_util import dev, host, u16, zeros  # noqa: E402
+from tests import lz4_spec  # noqa: E402
+
+TILE = 4096
+SIZES = [1, 2, 63, 64, 65, TILE - 1, TILE, TILE + 1, 3 * TILE + 7, (1 << 20) + 7]
+
+
+def masters(n, seed, density=None):
+    """(w_old, w_new) float32: generator step, or a forced changed fraction."""
+    w0, w1 = workload.host_masters(n, seed)
+    if density is not None:
+        rng = np.random.default_rng(seed + 99)
+        w1 = w0.copy()
+        hit = rng.random(n) < density
+        w1[hit] = w0[hit] * np.float32(1.5) + np.float32(0.01)
+    return w0, w1
+
+
+def gpu_cast_diff(w1, b0, cap=None, want_new=True, want_mask=True, ws=None):
+    n = w1.size
+    cap = n if cap is None else cap
+    W, B0 = dev(w1), dev(b0)
+    bn = zeros(n, torch.int16) if want_new else None
+    mk = zeros(n, torch.int16) if want_mask else None
+    idx, val = zeros(cap, torch.int32), zeros(cap, torch.int16)
+    cnt, st = zeros(1, torch.int64), zeros(1, torch.int32)
+    if ws is None:
+        ws = pulse.workspace(pulse.PULSE_OP_CAST_DIFF, n)
+    pulse.pulse_cast_diff(W, B0, bn, mk, idx[:cap] if cap else idx[:0], val[:cap] if cap else val[:0], cnt, st, ws, n=n)
+    torch.cuda.synchronize()
+    c = int(host(cnt)[0])
+    k = min(c, cap)
+    return dict(b_new=None if bn is None else u16(bn)[:n], mask=None if mk is None else u16(mk)[:n],
+                idx=host(idx)[:k], val=u16(val)[:k], count=c, status=int(host(st)[0]))
+
+
+@pytest.mark.parametrize("n", SIZES)
+@pytest.mark.parametrize("density", [None, 0.0, 1.0, 0.5])
+def test_cast_diff_matches_oracle(n, density):
+    w0, w1 = masters(n, seed=n, density=density)
+    b0 = oracle.cast_bf16(w0)
+    ref = oracle.cast_diff(w1, b0)
+    got = gpu_cast_diff(w1, b0)
+    assert got["count"] == ref["count"] and got["status"] == 0
+    assert np.array_equal(got["b_new"], ref["b_new"])
+    assert np.array_equal(got["mask"], ref["mask"])
+    assert np.array_equal(got["idx"], ref["idx"])
+    assert np.array_equal(got["val"], ref["val"])
+
+
+def test_cast_diff_config1():
+    w0, w1 = workload.c1_masters()
+    b0 = oracle.cast_bf16(w0).reshape(-1)
+    ref = oracle.cast_diff(w1, b0)
+    got = gpu_cast_diff(w1.reshape(-1), b0)
+    assert got["count"] == ref["count"] == 337906
+    for k in ("b_new", "mask", "idx", "val"):
+        assert np.array_equal(got[k], ref[k]), k
+
+
+def test_changes_at_tile_edges_and_alternating():
+    n = 5 * TILE + 3
+    b0 = np.zeros(n, np.uint16)
+    w1 = np.zeros(n, np.float32)
+    for i in (0, TILE - 1, TILE, 2 * TILE - 1, 4 * TILE, n - 1):
+        w1[i] = 1.0
+    w1[3 * TILE:4 * TILE:2] = -2.0                     # alternating inside one tile
+    ref = oracle.cast_diff(w1, b0)
+    got = gpu_cast_diff(w1, b0)
+    assert got["count"] == ref["count"]
+    assert np.array_equal(got["idx"], ref["idx"]) and np.array_equal(got["val"], ref["val"])
+
+
+def test_signed_zero_flip_counts_as_change():
+    n = 1000
+    b0 = np.zeros(n, np.uint16)
+    w1 = np.zeros(n, np.float32)
+    w1[::7] = -0.0
+    got = gpu_cast_diff(w1, b0)
+    ref = oracle.cast_diff(w1, b0)
+    assert got["count"] == ref["count"] == len(range(0, n, 7))
+    assert np.all(got["val"] == 0x8000)
+
+
+def test_rne_edge_patterns_and_variants():
+    hi = np.arange(1 << 16, dtype=np.uint32)
+    lo = np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF], np.uint32)
+    bits = ((hi[:, None] << 16) | lo[None, :]).reshape(-1)
+    f = bits.view(np.float32)
+    ref = oracle.cast_bf16(f)
+    n = f.size
+    # pure cast
+    W = dev(f)
+    bn = zeros(n, torch.int16)
+    pulse.pulse_cast_diff(W, b_new=bn)
+    torch.cuda.synchronize()
+    assert np.array_equal(u16(bn), ref)
+    # mask only (no patch), against an arbitrary old view
+    b0 = np.random.default_rng(1).integers(0, 1 << 16, n, dtype=np.uint16)
+    mk = zeros(n, torch.int16)
+    pulse.pulse_cast_diff(W, b_old=dev(b0), xor_mask=mk)
+    torch.cuda.synchronize()
+    assert np.array_equal(u16(mk), b0 ^ ref)
+    # in place: b_new is b_old
+    B = dev(b0)
+    mk2 = zeros(n, torch.int16)
+    idx, val = zeros(n, torch.int32), zeros(n, torch.int16)
+    cnt, st = zeros(1, torch.int64), zeros(1, torch.int32)
+    pulse.pulse_cast_diff(W, B, B, mk2, idx, val, cnt, st, pulse.workspace(pulse.PULSE_OP_CAST_DIFF, n))
+    torch.cuda.synchronize()
+    r = oracle.cast_diff(f, b0)
+    assert np.array_equal(u16(B), ref) and np.array_equal(u16(mk2), r["mask"])
+    assert int(host(cnt)[0]) == r["count"] and np.array_equal(host(idx)[: r["count"]], r["idx"])
+
+
+def test_full_rne_sweep():
+    """All 2^32 FP32 patterns through the GPU cast, compared with the oracle."""
+    chunk = 1 << 26
+    bn = zeros(chunk, torch.int16)
+    for c in range((1 << 32) // chunk):
+        bits = np.arange(chunk, dtype=np.uint32) + np.uint32(c * chunk)
+        W = dev(bits.view(np.float32))
+        pulse.pulse_cast_diff(W, b_new=bn)
+        got = u16(bn)
+        ref = oracle.cast_bf16(bits.view(np.float32))
+        bad = np.flatnonzero(got != ref)
+        assert bad.size == 0, hex(int(bits[bad[0]]))
+
+
+def test_capacity_overflow():
+    n = 50_000
+    w0, w1 = masters(n, seed=5, density=0.3)
+    b0 = oracle.cast_bf16(w0)
+    ref = oracle.cast_diff(w1, b0)
+    cap = ref["count"] // 3
+    got = gpu_cast_diff(w1, b0, cap=cap)
+    assert got["count"] == ref["count"] and got["status"] == pulse.PULSE_DS_CAPACITY
+    assert np.array_equal(got["idx"], ref["idx"][:cap]) and np.array_equal(got["val"], ref["val"][:cap])
+
+
+def test_empty_input_writes_zero_count():
+    cnt = torch.full((1,), 123, dtype=torch.int64, device="cuda")
+    st = zeros(1, torch.int32)
+    ws = pulse.workspace(pulse.PULSE_OP_CAST_DIFF, 0)
+    pulse.pulse_cast_diff(zeros(1, torch.float32), zeros(1, torch.int16), zeros(1, torch.int16), None,
+                          zeros(1, torch.int32), zeros(1, torch.int16), cnt, st, ws, n=0)
+    torch.cuda.synchronize()
+    assert int(host(cnt)[0]) == 0
+
+
+def test_workspace_reuse_across_calls_and_sizes():
+    """One workspace, many calls of varying sizes: per-call epochs keep status
+    words of earlier calls from being read as this call's."""
+    big = 40 * TILE + 11
+    ws = pulse.workspace(pulse.PULSE_OP_CAST_DIFF, big)
+    rng = np.random.default_rng(3)
+    for it, n in enumerate([big, 5, 3 * TILE, big, 1, 17 * TILE + 1, big, TILE]):
+        w0, w1 = masters(n, seed=100 + it, density=float(rng.random()))
+        b0 = oracle.cast_bf16(w0)
+        ref = oracle.cast_diff(w1, b0)
+        got = gpu_cast_diff(w1, b0, ws=ws)
+        assert got["count"] == ref["count"]
+        assert np.array_equal(got["idx"], ref["idx"]) and np.array_equal(got["val"], ref["val"])
+
+
+def test_compact_matches_oracle():
+    rng = np.random.default_rng(11)
+    for n in SIZES + [0]:
+        b0 = rng.integers(0, 1 << 16, n, dtype=np.uint16)
+        b1 = b0.copy()
+        hit = rng.random(n) < 0.2
+        b1[hit] = rng.integers(0, 1 << 16, int(hit.sum()), dtype=np.uint16)
+        b1[::97] ^= 0x8000  # sign flips
+        idx_r, val_r, m, st_r = oracle.compact(b0, b1)
+        idx, val = zeros(n, torch.int32), zeros(n, torch.int16)  # at least one element: a valid pointer
+        cnt, st = zeros(1, torch.int64), zeros(1, torch.int32)
+        pulse.pulse_compact(dev(b0) if n else zeros(1, torch.int16), dev(b1) if n else zeros(1, torch.int16),
+                            idx, val, cnt, st, pulse.workspace(pulse.PULSE_OP_COMPACT, n), n=n)
+        torch.cuda.synchronize()
+        assert int(host(cnt)[0]) == m
+        assert np.array_equal(host(idx)[:m], idx_r) and np.array_equal(u16(val)[:m], val_r)
+
+
+def test_apply_patch_matches_oracle_and_rebuilds():
+    for n in SIZES:
+        w0, w1 = masters(n, seed=2 * n + 1)
+        b0 = oracle.cast_bf16(w0)
+        r = oracle.cast_diff(w1, b0)
+        B = dev(b0)
+        cnt, st = dev(np.array([r["count"]], np.int64)), zeros(1, torch.int32)
+        idx = dev(r["idx"]) if r["count"] else zeros(1, torch.int32)
+        val = dev(r["val"]) if r["count"] else zeros(1, torch.int16)
+        pulse.pulse_apply_patch(B, idx, val, cnt, st, max_count=max(r["count"], 1))
+        torch.cuda.synchronize()
+        assert np.array_equal(u16(B), r["b_new"]) and int(host(st)[0]) == 0
+
+
+def test_apply_bad_index_and_count_bound():
+    b = np.arange(100, dtype=np.uint16)
+    idx = np.array([1, 100, -5, 3, 7], np.int32)
+    val = np.array([11, 12, 13, 14, 15], np.uint16)
+    B = dev(b)
+    st = zeros(1, torch.int32)
+    pulse.pulse_apply_patch(B, dev(idx), dev(val), dev(np.array([4], np.int64)), st, max_count=5)
+    torch.cuda.synchronize()
+    ref, rst = oracle.apply_patch(b, idx, val, count=4)
+    assert np.array_equal(u16(B), ref) and int(host(st)[0]) == rst == pulse.PULSE_DS_BADINDEX
+    # device count above max_count: only max_count entries are applied
+    B = dev(b)
+    pulse.pulse_apply_patch(B, dev(idx), dev(val), dev(np.array([5], np.int64)), zeros(1, torch.int32), max_count=1)
+    torch.cuda.synchronize()
+    ref, _ = oracle.apply_patch(b, idx, val, count=1)
+    assert np.array_equal(u16(B), ref)
+
+
+def test_patch_chain_20_steps_no_drift():
+    """Encode -> apply on the device each step, no host sync between them; the
+    receiver stays bit-identical to the direct cast of every version."""
+    n = 300_007
+    ws_host = workload.host_masters(n, seed=21, steps=20)
+    b_send = dev(oracle.cast_bf16(ws_host[0]))
+    b_recv = b_send.clone()
+    idx, val = zeros(n, torch.int32), zeros(n, torch.int16)
+    cnt, st = zeros(1, torch.int64), zeros(1, torch.int32)
+    ws = pulse.workspace(pulse.PULSE_OP_CAST_DIFF, n)
+    for t in range(1, 21):
+        pulse.pulse_cast_diff(dev(ws_host[t]), b_send, b_send, None, idx, val, cnt, st, ws)
+        pulse.pulse_apply_patch(b_recv, idx, val, cnt, st, max_count=n)
+        torch.cuda.synchronize()
+        assert np.array_equal(u16(b_recv), oracle.cast_bf16(ws_host[t]))
+    assert int(host(st)[0]) == 0
+
+
+@pytest.mark.parametrize("nbytes", [1, 15, 16, 17, 4096, 1000003])
+def test_xor_mask_apply(nbytes):
+    rng = np.random.default_rng(nbytes)
+    d = rng.integers(0, 256, nbytes, dtype=np.uint8)
+    m = rng.integers(0, 256, nbytes, dtype=np.uint8)
+    D = dev(d)
+    pulse.xor_mask_apply(D, dev(m))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(D), oracle.xor_apply(d, m))
+
+
+# ---- LZ4 ---------------------------------------------------------------------------
+def mask_bytes(nbytes, density, seed):
+    rng = np.random.default_rng(seed)
+    m = np.zeros(nbytes, np.uint8)
+    hit = rng.random(nbytes) < density
+    m[hit] = rng.integers(1, 256, int(hit.sum()), dtype=np.uint8)
+    return m
+
+
+def gpu_encode(src, block_bytes=65536, src_xor=None, cap=None):
+    nbytes = src.size
+    nb = (nbytes + block_bytes - 1) // block_bytes
+    cap = pulse.lz4_payload_bound(nbytes, block_bytes) if cap is None else cap
+    payload = zeros(cap, torch.uint8)
+    sizes, offs = zeros(nb, torch.int32), zeros(nb, torch.int64)
+    tot, st = zeros(1, torch.int64), zeros(1, torch.int32)
+    ws = pulse.workspace(pulse.PULSE_OP_LZ4_ENCODE, nbytes, block_bytes)
+    pulse.lz4_encode_blocks(dev(src), payload[:cap] if cap else payload[:0], sizes, offs, tot, st, ws,
+                            src_xor=None if src_xor is None else dev(src_xor), block_bytes=block_bytes)
+    torch.cuda.synchronize()
+    t = int(host(tot)[0])
+    return dict(payload=host(payload)[:min(t, cap)], sizes=host(sizes, np.uint32)[:nb],
+                offsets=host(offs, np.uint64)[:nb], total=t, status=int(host(st)[0]))
+
+
+@pytest.mark.parametrize("nbytes", [1, 12, 13, 100, 65536, 65537, 3 * 65536 + 1234, 1 << 22])
+@pytest.mark.parametrize("density", [0.0, 0.01, 0.08, 0.5, 1.0])
+def test_lz4_encode_matches_oracle(nbytes, density):
+    m = mask_bytes(nbytes, density, seed=nbytes + int(density * 1000))
+    got = gpu_encode(m)
+    ref = oracle.lz4_encode_blocks(m, 65536)
+    assert got["total"] == ref["total"] and got["status"] == 0
+    assert np.array_equal(got["sizes"], ref["sizes"]) and np.array_equal(got["offsets"], ref["offsets"])
+    assert np.array_equal(got["payload"], ref["payload"])
+
+
+@pytest.mark.parametrize("block_bytes", [16384, 32768, 49152])
+def test_lz4_encode_other_block_sizes(block_bytes):
+    m = mask_bytes(5 * block_bytes + 77, 0.05, seed=block_bytes)
+    got = gpu_encode(m, block_bytes)
+    ref = oracle.lz4_encode_blocks(m, block_bytes)
+    assert np.array_equal(got["payload"], ref["payload"]) and np.array_equal(got["sizes"], ref["sizes"])
+
+
+def test_lz4_encode_runs_and_patterns():
+    """Long runs of non-zero values, runs crossing thread chunks and blocks, and
+    the closed-form blocks (all zero, no runs)."""
+    parts = [np.zeros(70000, np.uint8), np.full(1000, 7, np.uint8), (np.arange(65536) & 0xFF).astype(np.uint8),
+             np.full(300, 9, np.uint8), np.zeros(255, np.uint8), np.array([1, 2, 2, 2, 2, 2, 3], np.uint8),
+             np.full(65536 * 2 + 5, 0xAB, np.uint8)]
+    m = np.concatenate(parts)
+    got = gpu_encode(m)
+    ref = oracle.lz4_encode_blocks(m, 65536)
+    assert np.array_equal(got["payload"], ref["payload"]) and np.array_equal(got["sizes"], ref["sizes"])
+    z = gpu_encode(np.zeros(65536, np.uint8))
+    assert z["total"] == 267
+    r = gpu_encode((np.arange(65536) & 0xFF).astype(np.uint8))
+    assert r["total"] == 65794
+
+
+def test_lz4_encode_xor_of_two_views_and_capacity():
+    rng = np.random.default_rng(17)
+    a = rng.integers(0, 1 << 16, 200_003, dtype=np.uint16)
+    b = a.copy()
+    hit = rng.random(a.size) < 0.08
+    b[hit] ^= rng.integers(1, 1 << 16, int(hit.sum()), dtype=np.uint16)
+    ref = oracle.lz4_encode_blocks(a, 65536, src_xor=b)
+    got = gpu_encode(a.view(np.uint8), src_xor=b.view(np.uint8))
+    assert np.array_equal(got["payload"], ref["payload"])
+    cap = int(ref["offsets"][3]) + 5
+    got = gpu_encode(a.view(np.uint8), src_xor=b.view(np.uint8), cap=cap)
+    assert got["status"] == pulse.PULSE_DS_CAPACITY and got["total"] == ref["total"]
+    assert np.array_equal(got["payload"][: int(ref["offsets"][3])], ref["payload"][: int(ref["offsets"][3])])
+
+
+def gpu_decode(payload, offsets, sizes, dst, mode, block_bytes=65536, payload_bytes=None):
+    nbytes = dst.size
+    nb = (nbytes + block_bytes - 1) // block_bytes
+    P = dev(payload) if payload.size else zeros(1, torch.uint8)
+    D = dev(dst)
+    st = zeros(1, torch.int32)
+    pb = payload.size if payload_bytes is None else payload_bytes
+    ws = pulse.workspace(pulse.PULSE_OP_LZ4_DECODE, nb, pb)
+    pulse.lz4_decode_blocks(P, dev(offsets.astype(np.uint64)), dev(sizes.astype(np.uint32)), D, st, ws, mode=mode,
+                            block_bytes=block_bytes, nbytes=nbytes, payload_bytes=pb)
+    torch.cuda.synchronize()
+    return host(D), int(host(st)[0])
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("density", [0.0, 0.01, 0.08, 1.0])
+def test_lz4_decode_canonical_payloads(mode, density):
+    nbytes = 7 * 65536 + 999
+    m = mask_bytes(nbytes, density, seed=int(density * 100) + mode)
+    enc = oracle.lz4_encode_blocks(m, 65536)
+    dst = np.random.default_rng(5).integers(0, 256, nbytes, dtype=np.uint8)
+    got, st = gpu_decode(enc["payload"], enc["offsets"], enc["sizes"], dst, mode)
+    ref, rst = oracle.lz4_decode_blocks(enc["payload"], enc["offsets"], enc["sizes"], dst, mode=mode)
+    assert st == rst == 0 and np.array_equal(got, ref)
+
+
+def random_payload(rng, nblocks, last, block_bytes=65536, **kw):
+    comps, plains = [], []
+    for b in range(nblocks):
+        size = last if b == nblocks - 1 else block_bytes
+        c, p = lz4_spec.random_block(rng, size, **kw)
+        comps.append(c)
+        plains.append(p)
+    sizes = np.array([len(c) for c in comps], np.uint32)
+    offs = np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(np.uint64)
+    return np.frombuffer(b"".join(comps), np.uint8).copy(), offs, sizes, np.frombuffer(b"".join(plains), np.uint8)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_lz4_decode_general_streams(mode):
+    """Streams the canonical encoder never writes: long literal runs, matches
+    reaching into earlier sequences (general path), overlapping copies."""
+    rng = np.random.default_rng(31 + mode)
+    payload, offs, sizes, plain = random_payload(rng, 6, 12345)
+    dst = rng.integers(0, 256, plain.size, dtype=np.uint8)
+    got, st = gpu_decode(payload, offs, sizes, dst, mode)
+    ref, rst = oracle.lz4_decode_blocks(payload, offs, sizes, dst, mode=mode)
+    assert st == rst == 0 and np.array_equal(got, ref)
+    assert np.array_equal(ref, plain if mode == 0 else dst ^ plain)
+    # offset-1 matches only, mixing blocks for both decode paths
+    rng = np.random.default_rng(77)
+    payload, offs, sizes, plain = random_payload(rng, 5, 999, max_off=1)
+    dst2 = rng.integers(0, 256, plain.size, dtype=np.uint8)
+    got, st = gpu_decode(payload, offs, sizes, dst2, mode)
+    ref, _ = oracle.lz4_decode_blocks(payload, offs, sizes, dst2, mode=mode)
+    assert st == 0 and np.array_equal(got, ref)
+
+
+def test_lz4_decode_corrupt_blocks_leave_dst():
+    data = mask_bytes(4 * 65536, 0.05, seed=8)
+    enc = oracle.lz4_encode_blocks(data, 65536)
+    dst = np.full(data.size, 0x5A, np.uint8)
+    cases = []
+    p = enc["payload"].copy()
+    p[int(enc["offsets"][1])] ^= 0xFF
+    cases.append((p, enc["offsets"], enc["sizes"]))                       # broken token
+    s = enc["sizes"].copy()
+    s[2] -= 1
+    cases.append((enc["payload"], enc["offsets"], s))                      # truncated block
+    o = enc["offsets"].copy()
+    o[3] = o[2] + 1
+    cases.append((enc["payload"], o, enc["sizes"]))                        # overlaps an earlier block
+    s = enc["sizes"].copy()
+    s[3] += 100000
+    cases.append((enc["payload"], enc["offsets"], s))                      # outside the payload
+    for payload, offs, sizes in cases:
+        for mode in (0, 1):
+            got, st = gpu_decode(payload, offs, sizes, dst, mode)
+            ref, rst = oracle.lz4_decode_blocks(payload, offs, sizes, dst, mode=mode)
+            assert rst == pulse.PULSE_DS_CORRUPT and st == rst
+            assert np.array_equal(got, ref)
+
+
+def test_lz4_round_trip_restores_new_view():
+    """Sender: mask of two BF16 views -> encode; receiver: decode + XOR into the
+    old view gives the new view bit for bit; XOR twice is the identity."""
+    w0, w1 = workload.c1_masters()
+    b0, b1 = oracle.cast_bf16(w0).reshape(-1), oracle.cast_bf16(w1).reshape(-1)
+    enc = gpu_encode(b0.view(np.uint8), src_xor=b1.view(np.uint8))
+    got, st = gpu_decode(enc["payload"], enc["offsets"], enc["sizes"], b0.view(np.uint8), 1)
+    assert st == 0 and np.array_equal(got.view(np.uint16), b1)
+    back, st = gpu_decode(enc["payload"], enc["offsets"], enc["sizes"], got, 1)
+    assert np.array_equal(back.view(np.uint16), b0)
+
+
+# ---- FP8 -----------------------------------------------------------------------------
+def bf16_bits(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def gpu_quant(srcs, batch=1):
+    cols = srcs[0].shape[-1]
+    R = sum(s.shape[-2] for s in srcs)
+    codes = zeros(batch * R * cols, torch.uint8)
+    scales = zeros(batch * ((R + 127) // 128) * ((cols + 127) // 128), torch.float32)
+    pulse.fp8_block_quant([dev(s) for s in srcs], codes, scales, batch=batch)
+    torch.cuda.synchronize()
+    return (host(codes)[: batch * R * cols].reshape(batch, R, cols),
+            host(scales).reshape(batch, (R + 127) // 128, (cols + 127) // 128))
+
+
+@pytest.mark.parametrize("shape_list", [[(128, 128)], [(256, 384), (128, 384), (384, 384)],
+                                        [(200, 136)], [(7, 8)], [(130, 264), (5, 264)]])
+def test_fp8_quant_matches_oracle(shape_list):
+    rng = np.random.default_rng(len(shape_list) * 7 + shape_list[0][0])
+    srcs = [bf16_bits(rng.standard_normal(s) * rng.choice([0.02, 1.0, 100.0])) for s in shape_list]
+    codes, scales = gpu_quant(srcs)
+    rc, rs = oracle.fp8_block_quant(srcs)
+    assert np.array_equal(scales.view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(codes, rc)
+
+
+def test_fp8_quant_special_blocks_and_batch():
+    rng = np.random.default_rng(4)
+    w = bf16_bits(rng.standard_normal((384, 256)) * 0.02)
+    w[0:128, 0:128] = bf16_bits(rng.standard_normal((128, 128)) * 1e-38)   # subnormal scale
+    w[128:256, 128:256] = 0                                                # amax 0 -> s = 1
+    w[256:384, 0:128] = bf16_bits(np.full((128, 128), -2.0 ** -130))      # constant subnormal
+    w[256:384, 128:256] = bf16_bits(rng.standard_normal((128, 128)) * 3e4)
+    codes, scales = gpu_quant([w])
+    rc, rs = oracle.fp8_block_quant([w])
+    assert np.array_equal(scales.view(np.uint32), rs.view(np.uint32)) and np.array_equal(codes, rc)
+    g = bf16_bits(rng.standard_normal((3, 256, 128)) * 0.02)
+    u = bf16_bits(rng.standard_normal((3, 128, 128)) * 0.05)
+    codes, scales = gpu_quant([g, u], batch=3)
+    rc, rs = oracle.fp8_block_quant([g, u], batch=3)
+    assert np.array_equal(scales.view(np.uint32), rs.view(np.uint32)) and np.array_equal(codes, rc)
+
+
+def test_fp8_all_bf16_values_through_one_scale():
+    """Every finite BF16 value quantised against a range of scales (one 128x128
+    block holds 16384 values; 4 blocks cover all 65536 patterns)."""
+    pats = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    fin = np.isfinite((pats.astype(np.uint32) << 16).view(np.float32))
+    pats = np.where(fin, pats, np.uint16(0))
+    w = pats.reshape(512, 128)
+    codes, scales = gpu_quant([w])
+    rc, rs = oracle.fp8_block_quant([w])
+    assert np.array_equal(scales.view(np.uint32), rs.view(np.uint32)) and np.array_equal(codes, rc)

@@ -149,6 +149,11 @@ def test_corrupt_streams_are_rejected_and_leave_dst():
     assert np.array_equal(got[:65536], data[:65536])
     assert np.all(got[65536:131072] == 0x5A)
     assert np.array_equal(got[131072:], data[131072:])
+    # a block starting before the end of an earlier one
+    offs = r["offsets"].copy()
+    offs[2] = offs[1] + 1
+    got, st = oracle.lz4_decode_blocks(r["payload"], offs, r["sizes"], dst)
+    assert st == oracle.CORRUPT and np.array_equal(got[:131072], data[:131072]) and np.all(got[131072:] == 0x5A)
     # block lying outside the payload
     sizes = r["sizes"].copy()
     sizes[2] += 1000
