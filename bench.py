@@ -1,0 +1,364 @@
+"""Throughput of the trainer->sampler weight-delta codec on one MI355X.
+
+One step = one pass of the whole hot path over a Qwen2.5-32B-shaped weight set
+(32,763,876,352 parameters; FP32 masters, old BF16 view and the receiver's BF16
+view resident in HBM before timing starts), processed in 18 chunks of whole
+tensors (embed | 16 x four decoder layers | final norm + lm_head):
+
+  sender    pulse_cast_diff   FP32 -> BF16 RNE cast, bitwise diff against the
+                              old view, (int32 index, BF16 value) patch
+  receiver  pulse_apply_patch scatter the patch into the receiver's view (v0 -> v1)
+  receiver  fp8_block_quant   stacked [q;k;v], o, stacked [gate;up], down,
+                              embed, lm_head -> E4M3 + FP32 128x128 scales
+  sender    lz4_encode_blocks LZ4 blocks (64 KiB) of the XOR mask old ^ new,
+                              the mask never materialised
+  receiver  lz4_decode_blocks decode + XOR in place into the receiver's view
+
+The mask is symmetric, so the XOR step takes the receiver from v1 back to v0:
+every step does identical work on identical data with no untimed restore.  The
+sender writes its new view into a per-chunk staging buffer instead of over the
+old view for the same reason (the same bytes move either way).
+
+Prints one JSON line.  value = 2 * params / step time (BF16 weights processed
+per second), the HBM fraction of the whole step is reported beside it, and the
+roofline object covers the kernel that takes most of the step.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "weights processed GB/s (encode+apply) and % of MI355X HBM peak, 1 GPU"
+PEAK_HBM = 8.0e12
+BLOCK = 65536
+PATCH_CAP_FRAC = 0.125   # patch capacity per chunk (measured density ~8.06%)
+PAYLOAD_CAP_FRAC = 0.35  # LZ4 payload capacity per chunk, fraction of mask bytes
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--layers", type=int, default=64, help="decoder layers (64 = the full Qwen2.5-32B shape)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-frac", type=float, default=1.0, help="fraction of layer 0 the oracle times")
+    p.add_argument("--copy-probe-gib", type=float, default=0.0,
+                   help="also run a plain device copy of this size (scale reference for HBM counters)")
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------------------
+def build_plan(specs, layers_per_chunk=4):
+    """Chunks of whole tensors in tensor order: embed, groups of decoder layers,
+    the tail (final norm + lm_head).  Returns [(start, end, [tensor indices])]."""
+    offs, o = [], 0
+    for s in specs:
+        offs.append(o)
+        o += s.numel
+    chunks, cur, cur_layer_count, cur_layer = [], [], 0, None
+    for i, s in enumerate(specs):
+        if s.name == "embed":
+            chunks.append([i])
+            continue
+        if s.name[0] == "l" and s.name[1].isdigit():
+            layer = int(s.name[1:].split(".")[0])
+            if layer != cur_layer:
+                if cur_layer is not None and cur_layer_count == layers_per_chunk:
+                    chunks.append(cur)
+                    cur, cur_layer_count = [], 0
+                cur_layer = layer
+                cur_layer_count += 1
+            cur.append(i)
+        else:
+            if cur and cur_layer is not None:
+                chunks.append(cur)
+                cur, cur_layer = [], None
+            cur.append(i)
+    if cur:
+        chunks.append(cur)
+    out = []
+    for ch in chunks:
+        start = offs[ch[0]]
+        end = offs[ch[-1]] + specs[ch[-1]].numel
+        out.append((start, end, ch))
+    return out, offs
+
+
+def quant_groups(specs, tensor_ids):
+    """FP8 groups of a chunk: lists of tensor indices stacked along rows."""
+    names = {specs[i].name: i for i in tensor_ids}
+    groups = []
+    for i in tensor_ids:
+        nm = specs[i].name
+        if len(specs[i].shape) != 2:
+            continue
+        if nm.endswith(".q"):
+            p = nm[:-1]
+            groups.append([i, names[p + "k"], names[p + "v"]])
+        elif nm.endswith(".gate"):
+            groups.append([i, names[nm[:-4] + "up"]])
+        elif nm.endswith(".k") or nm.endswith(".v") or nm.endswith(".up"):
+            continue
+        else:
+            groups.append([i])
+    return groups
+
+
+def views_equal(a, b, chunk=1 << 30):
+    """Bitwise equality of two large device tensors, chunked to bound temporaries."""
+    for s in range(0, a.numel(), chunk):
+        if not bool((a[s:s + chunk] == b[s:s + chunk]).all()):
+            return False
+    return True
+
+
+def src_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the codec is single-device here, "
+              "see DESIGN.md for how it would shard", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_delta_codec_amd as pulse
+    import workload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_setup = time.time()
+
+    specs = workload.qwen25_32b_specs(args.layers)
+    n = workload.total_numel(specs)
+    chunks, offs = build_plan(specs)
+    max_chunk = max(e - s for s, e, _ in chunks)
+    max_tensor = max(s.numel for s in specs)
+
+    # ---- resident inputs: FP32 masters (after the step), old view, receiver view
+    W = torch.empty(n, dtype=torch.float32, device=dev)
+    b_old = torch.empty(n, dtype=torch.int16, device=dev)
+    tmp = torch.empty(max_tensor, dtype=torch.float32, device=dev)
+    for ti, s in enumerate(specs):
+        w = W[offs[ti]: offs[ti] + s.numel]
+        workload.fill_init(w, 2, ti, s.kind)
+        # the old served view is the library's own cast of the initial masters
+        pulse.pulse_cast_diff(w, b_new=b_old[offs[ti]: offs[ti] + s.numel])
+        workload.apply_step(w, 2, ti, 1, tmp=tmp)
+    del tmp
+    b_recv = b_old.clone()
+    torch.cuda.synchronize()
+
+    # ---- per-chunk scratch (reused by every chunk)
+    cap = int(max_chunk * PATCH_CAP_FRAC)
+    stage = torch.empty(max_chunk, dtype=torch.int16, device=dev)
+    idx = torch.empty(cap, dtype=torch.int32, device=dev)
+    val = torch.empty(cap, dtype=torch.int16, device=dev)
+    cnt = torch.zeros(len(chunks), dtype=torch.int64, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    pcap = int(2 * max_chunk * PAYLOAD_CAP_FRAC)
+    payload = torch.empty(pcap, dtype=torch.uint8, device=dev)
+    nbmax = (2 * max_chunk + BLOCK - 1) // BLOCK
+    csizes = torch.empty(nbmax, dtype=torch.int32, device=dev)
+    coffs = torch.empty(nbmax, dtype=torch.int64, device=dev)
+    ctotal = torch.zeros(len(chunks), dtype=torch.int64, device=dev)
+    ws_cd = pulse.workspace(pulse.PULSE_OP_CAST_DIFF, max_chunk, 0, dev)
+    ws_en = pulse.workspace(pulse.PULSE_OP_LZ4_ENCODE, 2 * max_chunk, BLOCK, dev)
+    ws_de = pulse.workspace(pulse.PULSE_OP_LZ4_DECODE, nbmax, pcap, dev)
+    qplans = []
+    max_codes = max_scales = 0
+    for (s0, e0, tids) in chunks:
+        plan = []
+        for g in quant_groups(specs, tids):
+            cols = specs[g[0]].shape[1]
+            rows = sum(specs[i].shape[0] for i in g)
+            plan.append((g, rows, cols))
+            max_codes = max(max_codes, rows * cols)
+            max_scales = max(max_scales, ((rows + 127) // 128) * ((cols + 127) // 128))
+        qplans.append(plan)
+    codes = torch.empty(max_codes, dtype=torch.uint8, device=dev)
+    scales = torch.empty(max_scales, dtype=torch.float32, device=dev)
+    n_quant = sum(rows * cols for plan in qplans for (_, rows, cols) in plan)
+    torch.cuda.synchronize()
+    t_setup = time.time() - t_setup
+
+    stages = ["cast_diff", "apply_patch", "fp8_quant", "lz4_encode", "lz4_decode"]
+    ev = {k: [] for k in stages}
+
+    def run_step(record):
+        for ci, (s0, e0, tids) in enumerate(chunks):
+            m = e0 - s0
+
+            def rec(name, fn):
+                if record:
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    fn()
+                    b.record()
+                    ev[name].append((a, b))
+                else:
+                    fn()
+
+            rec("cast_diff", lambda: pulse.pulse_cast_diff(W[s0:e0], b_old[s0:e0], stage[:m], None, idx, val,
+                                                           cnt[ci:ci + 1], status, ws_cd))
+            rec("apply_patch", lambda: pulse.pulse_apply_patch(b_recv[s0:e0], idx, val, cnt[ci:ci + 1], status))
+
+            def quant():
+                for (g, rows, cols) in qplans[ci]:
+                    srcs = [b_recv[offs[i]: offs[i] + specs[i].numel].view(specs[i].shape) for i in g]
+                    pulse.fp8_block_quant(srcs, codes, scales)
+            rec("fp8_quant", quant)
+            rec("lz4_encode", lambda: pulse.lz4_encode_blocks(b_old[s0:e0], payload, csizes, coffs, ctotal[ci:ci + 1],
+                                                              status, ws_en, src_xor=stage[:m]))
+            rec("lz4_decode", lambda: pulse.lz4_decode_blocks(payload, coffs, csizes, b_recv[s0:e0], status, ws_de,
+                                                              mode=1))
+
+    # ---- warm-up, with the end-to-end check after the first step
+    for w in range(max(args.warmup, 1)):
+        run_step(False)
+        torch.cuda.synchronize()
+        if w == 0:
+            st = int(status.item())
+            if st != 0:
+                raise SystemExit(f"device status {st} after the first step (capacity or corrupt payload)")
+            if not views_equal(b_recv, b_old):
+                raise SystemExit("receiver view did not return to v0 after patch apply + XOR decode")
+    counts = cnt.cpu().numpy()
+    totals = ctotal.cpu().numpy()
+    changed = int(counts.sum())
+    comp_bytes = int(totals.sum())
+    d = changed / n
+    c = comp_bytes / n  # compressed bytes per element
+
+    # ---- timed steps
+    for k in ev:
+        ev[k].clear()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        run_step(True)
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t0
+    if int(status.item()) != 0:
+        raise SystemExit(f"device status {int(status.item())} during the timed steps")
+    if not views_equal(b_recv, b_old):
+        raise SystemExit("receiver view drifted during the timed steps")
+
+    ms_step = 1e3 * t_total / args.steps
+    stage_ms = {k: sum(a.elapsed_time(b) for a, b in ev[k]) / args.steps for k in stages}
+    launches = {k: len(ev[k]) // args.steps for k in stages}
+    # algorithmic bytes per step (what the method must move)
+    alg = {
+        "cast_diff": n * (8 + 6 * d),           # read w (4) + old (2), write new (2) + patch (6 d)
+        "apply_patch": n * 8 * d,               # read patch (6 d), write 2 B per changed element
+        "fp8_quant": n_quant * 3 + 4 * n_quant / 16384,  # read 2, write 1 + scales
+        "lz4_encode": n * (4 + c),              # read old + new (4), write payload (c)
+        "lz4_decode": n * (4 + c),              # read payload (c), read + write dst (4)
+    }
+    alg_total = sum(alg.values())
+    st_out = {}
+    for k in stages:
+        secs = stage_ms[k] / 1e3
+        st_out[k] = {"ms": round(stage_ms[k], 3), "launches": launches[k], "alg_GB": round(alg[k] / 1e9, 3),
+                     "GBps": round(alg[k] / secs / 1e9, 1), "frac_hbm": round(alg[k] / secs / PEAK_HBM, 4)}
+    dom = max(stages, key=lambda k: stage_ms[k])
+    dom_secs = stage_ms[dom] / 1e3
+    achieved = alg[dom] / dom_secs / 1e9
+    kernel_files = {"cast_diff": "cast_diff.hip", "apply_patch": "apply.hip", "fp8_quant": "fp8_quant.hip",
+                    "lz4_encode": "lz4_encode.hip", "lz4_decode": "lz4_decode.hip"}
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9,
+                "unit": "GB/s", "frac": round(achieved * 1e9 / PEAK_HBM, 4), "traffic": None,
+                "alg_bytes_per_launch": round(alg[dom] / launches[dom]),
+                "avg_launch_ms": round(stage_ms[dom] / launches[dom], 4)}
+    # measured HBM traffic, when profiles/ holds counters taken on this kernel's current source
+    tfile = os.path.join(ROOT, "profiles", f"{dom}_qwen32b_traffic.json")
+    if os.path.exists(tfile):
+        try:
+            tr = json.load(open(tfile))
+            src = os.path.join(ROOT, "sparse_delta_codec_amd", "csrc", kernel_files[dom])
+            if tr.get("source_sha") == src_hash(src):
+                roofline["traffic"] = tr["bytes_per_launch"]
+        except Exception:
+            pass
+
+    value = 2 * n / (ms_step / 1e3) / 1e9
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"Qwen2.5-32B-shaped weight set ({args.layers} layers), one RL step at lr 3e-6, "
+                               "full hot path: cast+diff+compact, patch apply, stacked FP8 quant, "
+                               "LZ4 mask encode, LZ4 decode+XOR",
+                   "params": n, "chunks": len(chunks), "lz4_block_bytes": BLOCK,
+                   "changed_fraction": round(d, 6), "lz4_bytes_per_param": round(c, 5),
+                   "lz4_ratio_of_mask": round(comp_bytes / (2 * n), 5), "fp8_params": n_quant},
+        "hbm_frac_step": round(alg_total / (ms_step / 1e3) / PEAK_HBM, 4),
+        "alg_GB_per_step": round(alg_total / 1e9, 2),
+        "stages": st_out,
+        "roofline": roofline,
+        "setup_s": round(t_setup, 1),
+    }
+
+    if args.copy_probe_gib > 0:
+        nb = int(args.copy_probe_gib * 2**30)
+        a = torch.empty(nb, dtype=torch.uint8, device=dev)
+        b = torch.empty(nb, dtype=torch.uint8, device=dev)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        result["copy_probe"] = {"bytes": 2 * nb, "ms": round(e0.elapsed_time(e1), 3),
+                                "GBps": round(2 * nb / (e0.elapsed_time(e1) / 1e3) / 1e9, 1)}
+        del a, b
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(specs, offs, W, b_old, args.cpu_sample_frac)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(specs, offs, W, b_old, frac):
+    """The oracle (plain single-threaded C) on layer 0 of the same workload: the
+    same five steps over the same host copies of the inputs."""
+    import numpy as np
+
+    import oracle
+
+    lay = [i for i, s in enumerate(specs) if s.name.startswith("l0.")]
+    s0, e0 = offs[lay[0]], offs[lay[-1]] + specs[lay[-1]].numel
+    m = int((e0 - s0) * frac) // 8 * 8
+    w = W[s0:s0 + m].cpu().numpy()
+    bo = b_old[s0:s0 + m].cpu().numpy().view(np.uint16)
+    groups = []
+    if frac >= 1.0:
+        for g in quant_groups(specs, lay):
+            groups.append([(offs[i] - s0, specs[i].shape) for i in g])
+    t = time.perf_counter()
+    r = oracle.cast_diff(w, bo, want_mask=False)
+    recv, _ = oracle.apply_patch(bo, r["idx"], r["val"])
+    for g in groups:
+        oracle.fp8_block_quant([recv[o:o + sh[0] * sh[1]].reshape(sh) for o, sh in g])
+    enc = oracle.lz4_encode_blocks(bo, BLOCK, src_xor=r["b_new"])
+    oracle.lz4_decode_blocks(enc["payload"], enc["offsets"], enc["sizes"], recv, mode=1)
+    secs = time.perf_counter() - t
+    return {"value": round(2 * m / secs / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"layer 0 of the same workload ({m} params{'' if frac >= 1 else ', FP8 step skipped'}), "
+                      f"all five steps, {secs:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -76,7 +76,11 @@ extern "C" {
 #define PULSE_OP_LZ4_DECODE 4 /* n = number of blocks, aux = payload bytes         */
 
 /* Bytes of workspace the op needs for the given size (0 if it needs none).
- * A workspace sized for a larger call serves any smaller call of any op. */
+ * A workspace serves any number of calls of the op it was sized for, of any
+ * size up to the one it was sized for; it must not be shared between
+ * different ops (cast_diff and compact count as one op).  Its look-back
+ * status words live at offsets that depend only on the workspace size, so a
+ * call never reads another call's per-block data as status. */
 size_t pulse_workspace_bytes(int op, int64_t n, int64_t aux);
 
 /* Zero a workspace before its first use.  After that each call leaves it

@@ -20,7 +20,8 @@ int pulse_launch_lz4_encode(const void *, const void *, int64_t, int32_t, uint8_
                             uint64_t *, uint64_t *, uint32_t *, void *, hipStream_t);
 size_t pulse_lz4_decode_ws_bytes(int64_t nblocks, int64_t payload_bytes);
 int pulse_launch_lz4_decode(const uint8_t *, int64_t, const uint64_t *, const uint32_t *, int64_t, int32_t,
-                            int64_t, void *, int32_t, uint32_t *, void *, hipStream_t);
+                            int64_t, void *, int32_t, uint32_t *, void *, size_t, hipStream_t);
+int pulse_lz4_decode_ws_fits(size_t ws, int64_t nblocks, int64_t payload_bytes);
 int pulse_launch_fp8_block_quant(const uint16_t *const *, const int64_t *, int32_t, int64_t, int64_t,
                                  const int64_t *, uint8_t *, float *, hipStream_t);
 int pulse_launch_fill_zero(void *, size_t, hipStream_t);
@@ -151,9 +152,9 @@ int lz4_decode_blocks(const uint8_t *payload, int64_t payload_bytes, const uint6
     if (nblocks != (nbytes + block_bytes - 1) / block_bytes) return PULSE_EINVAL;
     if (!aligned16(dst)) return PULSE_EALIGN;
     if (payload_bytes > kMaxPayload || nblocks > 0x3FFFFFFFll) return PULSE_ERANGE;
-    if (!ws || ws_bytes < pulse_lz4_decode_ws_bytes(nblocks, payload_bytes)) return PULSE_EWORKSPACE;
+    if (!ws || !pulse_lz4_decode_ws_fits(ws_bytes, nblocks, payload_bytes)) return PULSE_EWORKSPACE;
     return pulse_launch_lz4_decode(payload, payload_bytes, comp_offsets, comp_sizes, nblocks, block_bytes, nbytes,
-                                   dst, mode, d_status, ws, stream);
+                                   dst, mode, d_status, ws, ws_bytes, stream);
 }
 
 int fp8_block_quant(const uint16_t *const *srcs, const int64_t *src_rows, int32_t nsrc, int64_t cols,

@@ -447,31 +447,52 @@ __global__ __launch_bounds__(256) void k_lz4_slow(Lz4DecArgs a) {
 using namespace pulse;
 
 namespace {
+// The regions of a decode workspace are a function of its size alone, so the
+// look-back status words of one call never overlap the per-block data another
+// call of a different size left behind (a stale word must never carry a
+// matching epoch tag).  Status: 1 word per KiB; block info and slow list:
+// ws/8 bytes each; bitmap: the rest.
 struct DecLayout {
-    size_t status, binfo, slow, bitmap, total;
+    size_t status, binfo, slow, bitmap;
+    size_t status_words, blocks, bitmap_words;
 };
-DecLayout dec_layout(int64_t nblocks, int64_t payload_bytes) {
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+DecLayout dec_layout(size_t ws) {
     DecLayout L;
-    const int64_t k1 = (nblocks + 255) / 256;
-    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
     L.status = sizeof(WsHeader);
-    L.binfo = al(L.status + (size_t)(k1 > 0 ? k1 : 1) * 8);
-    L.slow = al(L.binfo + (size_t)(nblocks > 0 ? nblocks : 1) * 4);
-    L.bitmap = al(L.slow + (size_t)(nblocks > 0 ? nblocks : 1) * 4);
-    L.total = L.bitmap + ((size_t)(payload_bytes >> 5) + (size_t)nblocks + 2) * 4;
+    L.status_words = ws >> 10;
+    L.binfo = al256(L.status + 8 * L.status_words);
+    L.blocks = ws >> 5;
+    L.slow = al256(L.binfo + 4 * L.blocks);
+    L.bitmap = al256(L.slow + 4 * L.blocks);
+    L.bitmap_words = ws > L.bitmap ? (ws - L.bitmap) / 4 : 0;
     return L;
+}
+bool dec_fits(size_t ws, int64_t nblocks, int64_t payload_bytes) {
+    const DecLayout L = dec_layout(ws);
+    const size_t k1 = (size_t)(nblocks + 255) / 256;
+    const size_t words = (size_t)(payload_bytes >> 5) + (size_t)nblocks + 2;
+    return ws >= L.bitmap && k1 <= L.status_words && (size_t)nblocks <= L.blocks && words <= L.bitmap_words;
 }
 }  // namespace
 
 extern "C" size_t pulse_lz4_decode_ws_bytes(int64_t nblocks, int64_t payload_bytes) {
-    return dec_layout(nblocks, payload_bytes).total;
+    if (nblocks < 0 || payload_bytes < 0) return 0;
+    const size_t words = (size_t)(payload_bytes >> 5) + (size_t)nblocks + 2;
+    size_t ws = al256(4096 + 32 * (size_t)nblocks + (4 * words) * 4 / 3);
+    while (!dec_fits(ws, nblocks, payload_bytes)) ws = al256(ws + ws / 8 + 256);
+    return ws;
+}
+
+extern "C" int pulse_lz4_decode_ws_fits(size_t ws, int64_t nblocks, int64_t payload_bytes) {
+    return dec_fits(ws, nblocks, payload_bytes) ? 1 : 0;
 }
 
 extern "C" int pulse_launch_lz4_decode(const uint8_t *payload, int64_t payload_bytes, const uint64_t *offs,
                                        const uint32_t *sizes, int64_t nblocks, int32_t block_bytes,
                                        int64_t nbytes, void *dst, int32_t mode, uint32_t *d_status, void *ws,
-                                       hipStream_t stream) {
-    const DecLayout L = dec_layout(nblocks, payload_bytes);
+                                       size_t ws_bytes, hipStream_t stream) {
+    const DecLayout L = dec_layout(ws_bytes);
     char *w = static_cast<char *>(ws);
     Lz4DecArgs a{};
     a.payload = payload;

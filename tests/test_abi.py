@@ -55,6 +55,12 @@ def test_workspace_sizes(lib):
     assert ws(1, 4096, 0) == 256 + 8 and ws(1, 4097, 0) == 256 + 16
     assert ws(3, 65536 * 3 + 1, 65536) == 256 + 4 * 8
     assert ws(4, 10, 1 << 20) > (1 << 20) // 32
+    # decode workspaces grow with both arguments and always fit their own call
+    prev = 0
+    for nb, pb in [(1, 10), (100, 10 ** 6), (60000, 1_400_000_000), (500000, 7 * 10 ** 9)]:
+        cur = ws(4, nb, pb)
+        assert cur > prev
+        prev = cur
     assert ws(99, 10, 0) == 0
 
 

@@ -489,3 +489,29 @@ def test_fp8_all_bf16_values_through_one_scale():
     codes, scales = gpu_quant([w])
     rc, rs = oracle.fp8_block_quant([w])
     assert np.array_equal(scales.view(np.uint32), rs.view(np.uint32)) and np.array_equal(codes, rc)
+
+
+def test_lz4_workspace_reuse_across_sizes():
+    """Encode and decode workspaces reused by many calls of different sizes: the
+    status words of one call never meet another call's per-block data."""
+    big = 9 * 65536 + 4321
+    enc_ws = pulse.workspace(pulse.PULSE_OP_LZ4_ENCODE, big, 65536)
+    cap = pulse.lz4_payload_bound(big)
+    dec_ws = pulse.workspace(pulse.PULSE_OP_LZ4_DECODE, (big + 65535) // 65536, cap)
+    payload = zeros(cap, torch.uint8)
+    nbm = (big + 65535) // 65536
+    sizes, offs = zeros(nbm, torch.int32), zeros(nbm, torch.int64)
+    tot, st = zeros(1, torch.int64), zeros(1, torch.int32)
+    rng = np.random.default_rng(44)
+    for it, nbytes in enumerate([big, 70000, 3 * 65536, big, 100, big, 2 * 65536 + 1, big, 65536, big]):
+        m = mask_bytes(nbytes, float(rng.choice([0.0, 0.02, 0.08, 0.6])), seed=200 + it)
+        pulse.lz4_encode_blocks(dev(m), payload, sizes, offs, tot, st, enc_ws)
+        dst = rng.integers(0, 256, nbytes, dtype=np.uint8)
+        D = dev(dst)
+        pulse.lz4_decode_blocks(payload, offs, sizes, D, st, dec_ws, mode=1, nbytes=nbytes, payload_bytes=cap)
+        torch.cuda.synchronize()
+        ref = oracle.lz4_encode_blocks(m, 65536)
+        t = int(host(tot)[0])
+        assert int(host(st)[0]) == 0, it
+        assert t == ref["total"] and np.array_equal(host(payload)[:t], ref["payload"]), it
+        assert np.array_equal(host(D), dst ^ m), it
