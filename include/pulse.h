@@ -68,6 +68,11 @@ extern "C" {
 #define PULSE_DS_BADINDEX 0x2u /* apply: entries with index >= n were skipped  */
 #define PULSE_DS_CORRUPT 0x4u  /* lz4 decode: >= 1 malformed block; the dst
                                   range of such a block is left untouched    */
+#define PULSE_DS_WORKSPACE 0x8u /* the workspace state was inconsistent (never
+                                  initialised, shared between ops, or used by
+                                  overlapping calls); this call's outputs are
+                                  invalid, but the call still terminates;
+                                  re-initialise the workspace               */
 
 /* ---- workspaces ------------------------------------------------------------ */
 #define PULSE_OP_CAST_DIFF 1  /* n = element count                               */

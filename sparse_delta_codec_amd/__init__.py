@@ -12,7 +12,7 @@ import os
 import torch
 
 __all__ = [
-    "PULSE_DS_CAPACITY", "PULSE_DS_BADINDEX", "PULSE_DS_CORRUPT",
+    "PULSE_DS_CAPACITY", "PULSE_DS_BADINDEX", "PULSE_DS_CORRUPT", "PULSE_DS_WORKSPACE",
     "PULSE_OP_CAST_DIFF", "PULSE_OP_COMPACT", "PULSE_OP_LZ4_ENCODE", "PULSE_OP_LZ4_DECODE",
     "pulse_version", "pulse_workspace_bytes", "pulse_workspace_init", "workspace",
     "pulse_cast_diff", "pulse_compact", "pulse_apply_patch", "xor_mask_apply",
@@ -30,6 +30,7 @@ _lib = ctypes.CDLL(_LIB_PATH)
 PULSE_DS_CAPACITY = 0x1
 PULSE_DS_BADINDEX = 0x2
 PULSE_DS_CORRUPT = 0x4
+PULSE_DS_WORKSPACE = 0x8
 PULSE_OP_CAST_DIFF = 1
 PULSE_OP_COMPACT = 2
 PULSE_OP_LZ4_ENCODE = 3

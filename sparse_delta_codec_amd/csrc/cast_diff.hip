@@ -7,19 +7,12 @@
 // Datacenter", Nan Jiang talk, 10:49-11:08 and 12:12-12:44); the patch carries
 // indices and new absolute values (PULSE technical summary, "1. PULSESync").
 //
-// Layout per tile (256 threads, 4096 elements): thread t owns four groups of
-// four contiguous elements at tile_base + g*1024 + 4t, so each group is one
-// float4 + one ushort4 load per lane and a wave reads 1 KiB / 512 B contiguous
-// per instruction.  Changed-element counts of the four groups are packed in
-// 16-bit fields of one u64 and scanned together; the tile total is placed by a
-// decoupled look-back; entries are staged in LDS and written out contiguously.
+// One launch streams the tensor once; the patch is written in ascending index
+// order by a single-pass decoupled look-back over 16384-element tiles (one
+// atomic ticket per tile, see device.hpp).
 #include "device.hpp"
 
 namespace pulse {
-
-constexpr int CD_THREADS = 256;
-constexpr int CD_GROUPS = 4;
-constexpr int CD_TILE = CD_THREADS * 4 * CD_GROUPS;  // 4096 elements
 
 struct CastDiffArgs {
     const float *w_new;      // FROM_F32 source
@@ -107,92 +100,116 @@ __global__ __launch_bounds__(256) void k_cast_stream(CastDiffArgs a) {
 }
 
 // ---- single-pass compaction -------------------------------------------------
+// Tile = 4 waves x 4096 elements.  Wave w owns [tile_base + 4096 w, +4096) as
+// 16 groups of 256: lane l holds elements g*256 + 4l + k (one float4 + one
+// ushort4 per group), so every load is 1 KiB / 512 B contiguous per wave.
+// Pass 1 streams the tile (cast, compare, b_new / mask stores) keeping the
+// changed flags (64 bits) and the new values (32 VGPRs) in registers; the
+// wave totals give the tile total; one look-back places the tile; pass 2
+// ranks each changed element with ballots (v_mbcnt) and stores it directly at
+// its final position, lanes of a wave writing consecutive entries.
+constexpr int CD_THREADS = 256;
+constexpr int CD_GROUPS = 16;
+constexpr int CD_WAVE_ELEMS = CD_GROUPS * 256;                    // 4096
+constexpr int CD_TILE = (CD_THREADS / kWave) * CD_WAVE_ELEMS;   // 16384
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 template <bool FROM_F32, bool W_NEW, bool W_MASK>
 __global__ __launch_bounds__(CD_THREADS) void k_cast_compact(CastDiffArgs a) {
     __shared__ uint32_t s_tile, s_tag;
-    __shared__ uint64_t s_scan[CD_THREADS / kWave];
+    __shared__ uint32_t s_wtot[CD_THREADS / kWave];
     __shared__ uint64_t s_prefix;
-    __shared__ uint16_t s_loc[CD_TILE];  // tile-local index of each entry
-    __shared__ uint16_t s_val[CD_TILE];
 
-    const int t = threadIdx.x;
+    const int t = threadIdx.x, w = wave_id(), l = lane_id();
     if (t == 0) {
         uint32_t tile, tag;
-        ws_begin(a.hdr, &tile, &tag);
+        ws_begin(a.hdr, a.ntiles, &tile, &tag);
         s_tile = tile;
         s_tag = tag;
     }
     __syncthreads();
     const uint32_t tile = s_tile, tag = s_tag;
-    const int64_t base = (int64_t)tile * CD_TILE;
+    if (tile >= a.ntiles) {  // inconsistent workspace state: touch nothing
+        if (t == 0) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
+        return;
+    }
+    const int64_t wbase = (int64_t)tile * CD_TILE + (int64_t)w * CD_WAVE_ELEMS;
 
-    uint16_t nv[CD_GROUPS][4];
-    uint32_t chg[CD_GROUPS];
-    uint64_t packed = 0;
+    uint32_t nvp[CD_GROUPS * 2];  // new values, two per register
+    uint64_t flags = 0;           // bit 4g+k: element g*256 + 4l + k changed
 #pragma unroll
-    for (int g = 0; g < CD_GROUPS; ++g) {
-        const int64_t e = base + g * (CD_THREADS * 4) + 4 * t;
-        uint16_t ov[4];
-        load_new4<FROM_F32>(a, e, nv[g]);
-        load_old4(a.b_old, e, a.n, ov);
-        uint32_t m = 0;
+    for (int h = 0; h < 2; ++h) {
+        uint16_t nv[8][4], ov[8][4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            if (e + k < a.n && nv[g][k] != ov[k]) m |= 1u << k;
-        chg[g] = m;
-        packed |= (uint64_t)__builtin_popcount(m) << (16 * g);
-        if constexpr (W_NEW) store4(a.b_new, e, a.n, nv[g]);
-        if constexpr (W_MASK) {
-            uint16_t mv[4];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) mv[k] = ov[k] ^ nv[g][k];
-            store4(a.mask, e, a.n, mv);
+        for (int j = 0; j < 8; ++j) {
+            const int64_t e = wbase + (h * 8 + j) * 256 + 4 * l;
+            load_new4<FROM_F32>(a, e, nv[j]);
+            load_old4(a.b_old, e, a.n, ov[j]);
         }
-    }
-
-    // exclusive scan of the four packed 16-bit counts (each field <= 1024)
-    uint64_t totals;
-    const uint64_t excl = block_excl_sum<CD_THREADS / kWave>(packed, s_scan, &totals);
-    uint32_t gbase[CD_GROUPS];
-    uint32_t run = 0;
 #pragma unroll
-    for (int g = 0; g < CD_GROUPS; ++g) {
-        gbase[g] = run + (uint32_t)((excl >> (16 * g)) & 0xFFFF);
-        run += (uint32_t)((totals >> (16 * g)) & 0xFFFF);
-    }
-    const uint32_t tile_count = run;
-
-    // stage entries in LDS in ascending element order
+        for (int j = 0; j < 8; ++j) {
+            const int g = h * 8 + j;
+            const int64_t e = wbase + g * 256 + 4 * l;
 #pragma unroll
-    for (int g = 0; g < CD_GROUPS; ++g) {
-        uint32_t m = chg[g], r = gbase[g];
+            for (int k = 0; k < 4; ++k)
+                if (e + k < a.n && nv[j][k] != ov[j][k]) flags |= 1ull << (4 * g + k);
+            nvp[2 * g] = (uint32_t)nv[j][0] | ((uint32_t)nv[j][1] << 16);
+            nvp[2 * g + 1] = (uint32_t)nv[j][2] | ((uint32_t)nv[j][3] << 16);
+            if constexpr (W_NEW) store4(a.b_new, e, a.n, nv[j]);
+            if constexpr (W_MASK) {
+                uint16_t mv[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            if (m & (1u << k)) {
-                s_loc[r] = (uint16_t)(g * (CD_THREADS * 4) + 4 * t + k);
-                s_val[r] = nv[g][k];
-                ++r;
+                for (int k = 0; k < 4; ++k) mv[k] = ov[j][k] ^ nv[j][k];
+                store4(a.mask, e, a.n, mv);
             }
         }
     }
 
-    if (wave_id() == 0) {
-        const uint64_t pre = lookback_wave(a.status, tile, tag, tile_count);
-        if (lane_id() == 0) {
+    const uint32_t wtot = wave_reduce_sum((uint32_t)__builtin_popcountll(flags));
+    if (l == 0) s_wtot[w] = wtot;
+    __syncthreads();
+    uint32_t tile_count = 0, wpre = 0;
+#pragma unroll
+    for (int i = 0; i < CD_THREADS / kWave; ++i) {
+        if (i < w) wpre += s_wtot[i];
+        tile_count += s_wtot[i];
+    }
+    if (w == 0) {
+        bool failed = false;
+        const uint64_t pre = lookback_wave(a.status, tile, tag, tile_count, &failed);
+        if (l == 0) {
+            if (failed) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
             s_prefix = pre;
             if (tile == a.ntiles - 1) *a.d_count = (int64_t)(pre + tile_count);
             if ((int64_t)(pre + tile_count) > a.cap) or_agent32(a.d_status, 1u /*PULSE_DS_CAPACITY*/);
-            ws_end(a.hdr, a.ntiles);
         }
     }
     __syncthreads();
-    const int64_t pre = (int64_t)s_prefix;
-    for (uint32_t r = t; r < tile_count; r += CD_THREADS) {
-        const int64_t pos = pre + r;
-        if (pos < a.cap) {
-            a.idx[pos] = (int32_t)(base + s_loc[r]);
-            a.val[pos] = s_val[r];
+    if (tile_count == 0) return;
+    int64_t run = (int64_t)s_prefix + wpre;
+#pragma unroll
+    for (int g = 0; g < CD_GROUPS; ++g) {
+        const uint32_t f = (uint32_t)(flags >> (4 * g)) & 0xFu;
+        const uint64_t m0 = __ballot(f & 1u), m1 = __ballot(f & 2u), m2 = __ballot(f & 4u), m3 = __ballot(f & 8u);
+        const uint32_t gtot = __builtin_popcountll(m0) + __builtin_popcountll(m1) + __builtin_popcountll(m2) +
+                              __builtin_popcountll(m3);
+        if (gtot == 0) continue;
+        int64_t pos = run + lanes_below(m0) + lanes_below(m1) + lanes_below(m2) + lanes_below(m3);
+        const int64_t e = wbase + g * 256 + 4 * l;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (f & (1u << k)) {
+                if (pos < a.cap) {
+                    a.idx[pos] = (int32_t)(e + k);
+                    a.val[pos] = (uint16_t)(nvp[2 * g + (k >> 1)] >> (16 * (k & 1)));
+                }
+                ++pos;
+            }
         }
+        run += gtot;
     }
 }
 

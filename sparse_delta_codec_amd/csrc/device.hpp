@@ -148,40 +148,49 @@ __device__ __forceinline__ void or_agent32(uint32_t *p, uint32_t v) {
 // ---- workspace layout shared by every single-pass (look-back) kernel --------
 // [0, 256): header; [256, ...): one 64-bit status word per tile.
 // status word: [63:40] epoch tag (never 0), [39] inclusive flag, [38:0] value.
+// The ticket is the one hot atomic (all tiles of a call hit it); the state every
+// tile reads and the op counters sit on their own 128-byte lines so those
+// accesses do not queue behind the ticket atomics.
 struct WsHeader {
-    uint32_t epoch;   // calls completed on this workspace, mod kTagMod
-    uint32_t ticket;  // dynamic tile ids handed out in the current call
-    uint32_t done;    // tiles finished in the current call
+    uint64_t ticket;  // tiles handed out on this workspace so far (never reset)
+    uint64_t pad0[15];
+    uint64_t state;   // [63:40] epoch (calls completed), [39:0] ticket at the start of this call
+    uint64_t pad1[7];
     uint32_t aux;     // per-op counter (decode: slow-block count)
     uint32_t aux2;    // per-op counter (decode: slow-kernel blocks finished)
-    uint32_t pad[59];
+    uint32_t pad2[14];
 };
 static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
 
 constexpr uint32_t kTagMod = 0xFFFFFFu;
 constexpr uint64_t kValueMask = (1ull << 39) - 1;
 constexpr uint64_t kInclusive = 1ull << 39;
+constexpr uint64_t kBaseMask = (1ull << 40) - 1;
 
 __device__ __forceinline__ uint64_t make_status(uint32_t tag, bool inclusive, uint64_t v) {
     return ((uint64_t)tag << 40) | (inclusive ? kInclusive : 0ull) | (v & kValueMask);
 }
 
-// Per-call prologue, thread 0 only: the tile id (ticket order == start order,
-// so every tile this one waits on is already resident) and this call's tag.
-__device__ __forceinline__ void ws_begin(WsHeader *h, uint32_t *tile, uint32_t *tag) {
-    *tile = add_agent32(&h->ticket, 1u);
-    *tag = (ld_agent32(&h->epoch) % kTagMod) + 1u;
+__device__ __forceinline__ uint64_t add_agent64(uint64_t *p, uint64_t v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Per-call epilogue, thread 0 only, after the tile's last status access: the
-// last tile to finish rearms the header for the next call on this workspace.
-__device__ __forceinline__ void ws_end(WsHeader *h, uint32_t ntiles) {
-    uint32_t d = add_agent32(&h->done, 1u);
-    if (d == ntiles - 1) {
-        st_agent32(&h->ticket, 0u);
-        st_agent32(&h->done, 0u);
-        st_agent32(&h->epoch, (ld_agent32(&h->epoch) + 1u) % kTagMod);
-    }
+// Per-call prologue, thread 0 only: a dynamic tile id (ticket order == start
+// order, so every tile this one waits on is already resident) and this call's
+// epoch tag, with one atomic per tile.  The call state is read before the
+// ticket is taken (the ticket address depends on it, so the load has returned
+// first); the tile that takes the call's last ticket therefore re-arms the
+// state only after every tile of the call has read it.
+__device__ __forceinline__ void ws_begin(WsHeader *h, uint32_t ntiles, uint32_t *tile, uint32_t *tag) {
+    const uint64_t st = ld_agent(&h->state);
+    uint64_t *tp = &h->ticket + (st == ~0ull ? 1 : 0);  // never taken: state is never all ones
+    const uint64_t t = add_agent64(tp, 1ull);
+    const uint64_t tl = (t - st) & kBaseMask;
+    const uint32_t ep = (uint32_t)(st >> 40);
+    *tile = (uint32_t)tl;
+    *tag = ep % kTagMod + 1u;
+    if (tl == (uint64_t)ntiles - 1)
+        st_agent(&h->state, ((uint64_t)((ep + 1u) % kTagMod) << 40) | ((t + 1) & kBaseMask));
 }
 
 // Decoupled look-back, executed by one full wave (all 64 lanes) of the tile.
@@ -189,10 +198,18 @@ __device__ __forceinline__ void ws_end(WsHeader *h, uint32_t ntiles) {
 // an inclusive prefix is found, publishes the tile's inclusive prefix and
 // returns the exclusive prefix (identical in every lane).
 // MAX = true combines with max instead of +.
+// The wait for a predecessor is bounded: a predecessor that never publishes
+// can only come from a workspace whose state is inconsistent (not initialised,
+// or shared by concurrent calls).  Past the budget the wave gives up, sets
+// *failed (the caller reports it) and still publishes, so its successors end
+// too and the kernel always terminates.
+constexpr uint32_t kSpinLimit = 1u << 20;
+
 template <bool MAX = false>
 __device__ __forceinline__ uint64_t lookback_wave(uint64_t *status, uint32_t tile, uint32_t tag,
-                                                  uint64_t aggregate) {
+                                                  uint64_t aggregate, bool *failed) {
     const int lane = lane_id();
+    uint32_t spins = 0;
     if (tile == 0) {
         if (lane == 0) st_agent(&status[0], make_status(tag, true, aggregate));
         return 0;
@@ -218,8 +235,13 @@ __device__ __forceinline__ uint64_t lookback_wave(uint64_t *status, uint32_t til
             } else if (vmask == ~0ull) {
                 break;
             }
+            if (++spins > kSpinLimit) {
+                *failed = true;
+                break;
+            }
             __builtin_amdgcn_s_sleep(1);
         }
+        if (*failed) break;
         const uint64_t imask = __ballot(incl);
         uint64_t mine = (p >= 0) ? (w & kValueMask) : 0;
         const int stop = imask ? __builtin_ctzll(imask) : kWave;
@@ -232,6 +254,7 @@ __device__ __forceinline__ uint64_t lookback_wave(uint64_t *status, uint32_t til
         }
         if (imask) break;
         j -= kWave;
+        if (j < 0) break;  // (never reached: tile 0 is always inclusive)
     }
     uint64_t incl_v;
     if constexpr (MAX) incl_v = aggregate > prefix ? aggregate : prefix;

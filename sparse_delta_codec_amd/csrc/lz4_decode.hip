@@ -101,12 +101,16 @@ __global__ __launch_bounds__(256) void k_lz4_parse(Lz4DecArgs a) {
     const int t = threadIdx.x;
     if (t == 0) {
         uint32_t tile, tag;
-        ws_begin(a.hdr, &tile, &tag);
+        ws_begin(a.hdr, a.k1_tiles, &tile, &tag);
         s_tile = tile;
         s_tag = tag;
     }
     __syncthreads();
     const uint32_t tile = s_tile, tag = s_tag;
+    if (tile >= a.k1_tiles) {  // inconsistent workspace state: touch nothing
+        if (t == 0) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
+        return;
+    }
     const int64_t b = (int64_t)tile * 256 + t;
     const bool live = b < a.nblocks;
 
@@ -127,10 +131,11 @@ __global__ __launch_bounds__(256) void k_lz4_parse(Lz4DecArgs a) {
     uint64_t tile_max;
     const uint64_t in_tile = block_excl_max<4>(end, (uint64_t)0, s_scan, &tile_max);
     if (wave_id() == 0) {
-        const uint64_t pre = lookback_wave<true>(a.status, tile, tag, tile_max);
+        bool failed = false;
+        const uint64_t pre = lookback_wave<true>(a.status, tile, tag, tile_max, &failed);
         if (lane_id() == 0) {
+            if (failed) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
             s_pre = pre;
-            ws_end(a.hdr, a.k1_tiles);
         }
     }
     __syncthreads();

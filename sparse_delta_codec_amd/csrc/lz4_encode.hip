@@ -110,12 +110,16 @@ __global__ __launch_bounds__(LZE_THREADS) void k_lz4_encode(Lz4EncArgs a) {
     const int t = threadIdx.x;
     if (t == 0) {
         uint32_t tile, tag;
-        ws_begin(a.hdr, &tile, &tag);
+        ws_begin(a.hdr, a.nblocks, &tile, &tag);
         s_tile = tile;
         s_tag = tag;
     }
     __syncthreads();
     const uint32_t b = s_tile, tag = s_tag;
+    if (b >= a.nblocks) {  // inconsistent workspace state: touch nothing
+        if (t == 0) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
+        return;
+    }
     const int64_t blk_base = (int64_t)b * a.block_bytes;
     const int32_t len = (int32_t)((a.nbytes - blk_base) < a.block_bytes ? (a.nbytes - blk_base) : a.block_bytes);
     const int32_t CH = a.chunk, stride = CH + 16;
@@ -201,14 +205,15 @@ __global__ __launch_bounds__(LZE_THREADS) void k_lz4_encode(Lz4EncArgs a) {
 
     // 4. place the block
     if (wave_id() == 0) {
-        const uint64_t off = lookback_wave(a.status, b, tag, comp);
+        bool failed = false;
+        const uint64_t off = lookback_wave(a.status, b, tag, comp, &failed);
         if (lane_id() == 0) {
+            if (failed) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
             s_off = off;
             a.comp_sizes[b] = (uint32_t)comp;
             a.comp_offsets[b] = off;
             if (b == a.nblocks - 1) *a.d_total = off + comp;
             if ((int64_t)(off + comp) > a.cap) or_agent32(a.d_status, 1u /*PULSE_DS_CAPACITY*/);
-            ws_end(a.hdr, a.nblocks);
         }
     }
     __syncthreads();

@@ -52,7 +52,7 @@ def test_status_strings_and_version(lib):
 
 def test_workspace_sizes(lib):
     ws = lib.pulse_workspace_bytes
-    assert ws(1, 4096, 0) == 256 + 8 and ws(1, 4097, 0) == 256 + 16
+    assert ws(1, 16384, 0) == 256 + 8 and ws(1, 16385, 0) == 256 + 16
     assert ws(3, 65536 * 3 + 1, 65536) == 256 + 4 * 8
     assert ws(4, 10, 1 << 20) > (1 << 20) // 32
     # decode workspaces grow with both arguments and always fit their own call

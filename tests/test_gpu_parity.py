@@ -24,8 +24,8 @@ except ImportError:
 from tests.gpu_util import dev, host, u16, zeros  # noqa: E402
 from tests import lz4_spec  # noqa: E402
 
-TILE = 4096
-SIZES = [1, 2, 63, 64, 65, TILE - 1, TILE, TILE + 1, 3 * TILE + 7, (1 << 20) + 7]
+TILE = 16384  # elements per compaction tile
+SIZES = [1, 2, 63, 64, 65, 4095, 4097, TILE - 1, TILE, TILE + 1, 3 * TILE + 7, (1 << 20) + 7]
 
 
 def masters(n, seed, density=None):
