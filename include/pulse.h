@@ -175,7 +175,7 @@ int xor_mask_apply(void *dst, const void *mask, int64_t nbytes, hipStream_t stre
  *   src_xor      [nbytes] or NULL; when given the encoded bytes are
  *                src[i] ^ src_xor[i] (the XOR mask of two views, never
  *                materialised).
- *   block_bytes  a multiple of 16384, at most 65536.
+ *   block_bytes  16384, 32768 or 65536.
  *   payload      [payload_cap] concatenated encoded blocks (written).
  *                nblocks * (block_bytes + block_bytes/255 + 16) always suffices.
  *   comp_sizes   [nblocks] uint32 encoded size per block (written).

@@ -131,7 +131,7 @@ int lz4_encode_blocks(const void *src, const void *src_xor, int64_t nbytes, int3
     if (!src || !payload || !comp_sizes || !comp_offsets || !d_total || !d_status || nbytes <= 0 ||
         payload_cap < 0)
         return PULSE_EINVAL;
-    if (block_bytes <= 0 || block_bytes > 65536 || block_bytes % 16384 != 0) return PULSE_EINVAL;
+    if (block_bytes != 16384 && block_bytes != 32768 && block_bytes != 65536) return PULSE_EINVAL;
     if (!aligned16(src) || (src_xor && !aligned16(src_xor))) return PULSE_EALIGN;
     const int64_t nb = (nbytes + block_bytes - 1) / block_bytes;
     if (nb > 0xFFFFFFFFll || nbytes > kMaxPayload / 2) return PULSE_ERANGE;

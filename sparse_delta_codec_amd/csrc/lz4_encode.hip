@@ -11,24 +11,30 @@
 // run's sequence depends only on its own (s, e, n), a block is parsed in
 // parallel and the output is bit-for-bit deterministic.
 //
-// One workgroup per 64 KiB block (dynamic block ids):
-//  1. coalesced 16-byte loads (XOR of two sources when given) into LDS, each
-//     256-byte thread chunk padded by 16 bytes so chunk reads avoid bank
-//     conflicts;
+// One workgroup of 1024 threads (16 waves) per block (dynamic block ids);
+// thread t owns the block bytes [t*CH, (t+1)*CH), CH = block_bytes / 1024 (64
+// for 64 KiB blocks, so a chunk's run boundaries fit one 64-bit mask):
+//  1. coalesced 16-byte loads (the XOR of two sources when given) into a 64 KiB
+//     LDS image whose 16-byte pieces are XOR-swizzled per chunk, so both the
+//     coalesced writes and each thread's reads of its own chunk are free of
+//     bank conflicts;
 //  2. per thread: SWAR run-boundary bitmask of its chunk (1 bit per byte);
-//  3. block scans: next boundary after each chunk (suffix min), last
-//     qualifying j before it (prefix max), first qualifying i after it (suffix
-//     min), then the byte size of each thread's sequences (prefix sum);
+//  3. one in-order pass over the chunk's runs (a run is complete when the next
+//     boundary is found) gives the thread's first/last qualifying run and the
+//     bytes of its sequences; block scans (next boundary after the chunk,
+//     last qualifying j before it, first qualifying i after it, byte offsets);
 //  4. decoupled look-back over blocks gives the block's payload offset;
-//  5. each thread writes its sequences' headers and the literal bytes of its
-//     own chunk at their final positions.
+//  5. emission: each thread writes its sequences' headers and the literal bytes
+//     of its own chunk; when the block's encoding fits the 14 KiB LDS window
+//     (every block of a sparse mask) the bytes go there and are copied out with
+//     16-byte stores, otherwise straight to the payload.
 #include "device.hpp"
 
 namespace pulse {
 
-constexpr int LZE_THREADS = 256;
+constexpr int LZE_THREADS = 1024;
 constexpr int LZE_MAX_BLOCK = 65536;
-constexpr int LZE_LDS = LZE_MAX_BLOCK + LZE_MAX_BLOCK / 16;  // 16 B pad per 256 B chunk
+constexpr int LZE_WIN = 14336;  // output staging window
 constexpr int32_t LZE_INF = 0x7FFFFFFF;
 
 struct Lz4EncArgs {
@@ -36,7 +42,6 @@ struct Lz4EncArgs {
     const uint8_t *src_xor;
     int64_t nbytes;
     int32_t block_bytes;
-    int32_t chunk;  // block_bytes / 256, a multiple of 64
     uint8_t *payload;
     int64_t cap;
     uint32_t *comp_sizes;
@@ -60,28 +65,38 @@ __device__ __forceinline__ uint32_t nonzero_bytes(uint32_t x) {
     return (((hi >> 7) * 0x00204081u) >> 21) & 0xFu;
 }
 
-__device__ __forceinline__ int next_bit(const uint64_t m[4], int from) {
-    // first set bit at position >= from (chunk-relative), or -1
-    for (int w = from >> 6; w < 4; ++w) {
-        uint64_t x = m[w];
-        if (w == (from >> 6)) x &= (~0ull) << (from & 63);
-        if (x) return w * 64 + __builtin_ctzll(x);
-    }
-    return -1;
+// LDS image of a block: chunk c (CH = 2^CHLOG bytes, NPC = CH/16 pieces) at
+// c*CH, its 16-byte piece k stored at slot k ^ ((c >> (4 - log2 NPC)) & (NPC-1)):
+// any 16 consecutive lanes, whether writing consecutive pieces or reading the
+// same piece of their own chunks, hit 16 distinct 16-byte bank groups.
+template <int CHLOG>
+__device__ __forceinline__ int32_t img_addr(int32_t p) {
+    constexpr int NPCLOG = CHLOG - 4;
+    const int32_t c = p >> CHLOG;
+    const int32_t k = (p >> 4) & ((1 << NPCLOG) - 1);
+    const int32_t sw = (c >> (4 - NPCLOG)) & ((1 << NPCLOG) - 1);
+    return (c << CHLOG) + ((k ^ sw) << 4) + (p & 15);
 }
 
-// calls f(s, e) for every run that starts in this thread's chunk
+// Calls f(s, e) for every run starting in this thread's chunk, in order: a run
+// is complete when the next boundary is found (or, for the last one, at
+// next_after, the first boundary after the chunk).
 template <class F>
-__device__ __forceinline__ void for_each_run(const uint64_t m[4], int32_t cs, int32_t next_after, F f) {
-    int cur = next_bit(m, 0);
-    while (cur >= 0) {
-        const int nxt = (cur + 1 < 256) ? next_bit(m, cur + 1) : -1;
-        f(cs + cur, nxt >= 0 ? cs + nxt : next_after);
-        cur = nxt;
+__device__ __forceinline__ void for_each_run(uint64_t m, int32_t cs, int32_t next_after, F f) {
+    if (!m) return;
+    int32_t prev = cs + __builtin_ctzll(m);
+    m &= m - 1;
+    while (m) {
+        const int32_t pos = cs + __builtin_ctzll(m);
+        m &= m - 1;
+        f(prev, pos);
+        prev = pos;
     }
+    f(prev, next_after);
 }
 
-// byte writer for one block's slot of the payload; never writes past `lim`
+// destination of the emitted bytes: the LDS window (offset by the payload's
+// misalignment) or the payload itself; never writes past the block's size
 struct Out {
     uint8_t *p;
     int32_t lim;
@@ -101,8 +116,11 @@ __device__ __forceinline__ int32_t put_len(const Out &out, int32_t pos, int32_t 
     return pos;
 }
 
+template <int CHLOG>
 __global__ __launch_bounds__(LZE_THREADS) void k_lz4_encode(Lz4EncArgs a) {
-    __shared__ __align__(16) uint8_t s_buf[LZE_LDS];
+    constexpr int32_t CH = 1 << CHLOG;
+    __shared__ __align__(16) uint8_t s_img[LZE_MAX_BLOCK];
+    __shared__ __align__(16) uint8_t s_win[LZE_WIN + 16];
     __shared__ int32_t s_i32[LZE_THREADS / kWave];
     __shared__ uint32_t s_tile, s_tag;
     __shared__ uint64_t s_off;
@@ -122,7 +140,6 @@ __global__ __launch_bounds__(LZE_THREADS) void k_lz4_encode(Lz4EncArgs a) {
     }
     const int64_t blk_base = (int64_t)b * a.block_bytes;
     const int32_t len = (int32_t)((a.nbytes - blk_base) < a.block_bytes ? (a.nbytes - blk_base) : a.block_bytes);
-    const int32_t CH = a.chunk, stride = CH + 16;
 
     // 1. load
     const int32_t npieces = a.block_bytes / 16;
@@ -144,60 +161,53 @@ __global__ __launch_bounds__(LZE_THREADS) void k_lz4_encode(Lz4EncArgs a) {
             }
             v = make_uint4(w[0], w[1], w[2], w[3]);
         }
-        *reinterpret_cast<uint4 *>(s_buf + (off / CH) * stride + (off % CH)) = v;
+        *reinterpret_cast<uint4 *>(s_img + img_addr<CHLOG>(off)) = v;
     }
     __syncthreads();
 
     // 2. run-boundary bitmask of this thread's chunk
     const int32_t cs = t * CH;
     const int32_t cl = len - cs < 0 ? 0 : (len - cs < CH ? len - cs : CH);
-    const uint8_t *mine = s_buf + t * stride;
-    uint64_t m[4] = {0, 0, 0, 0};
+    uint64_t m = 0;
     if (cl > 0) {
-        uint32_t pb = (t > 0) ? s_buf[(t - 1) * stride + CH - 1] : 0u;
+        uint32_t pb = (t > 0) ? s_img[img_addr<CHLOG>(cs - 1)] : 0u;
+#pragma unroll
         for (int32_t q = 0; q < CH; q += 16) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(mine + q);
+            const uint4 v = *reinterpret_cast<const uint4 *>(s_img + img_addr<CHLOG>(cs + q));
             const uint32_t d[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int32_t p0 = q + 4 * k;
                 uint32_t nib = nonzero_bytes(d[k] ^ ((d[k] << 8) | pb));
                 pb = d[k] >> 24;
-                if (t == 0 && p0 == 0) nib |= 1u;  // a run starts at the block start
+                if (p0 == 0 && t == 0) nib |= 1u;  // a run starts at the block start
                 if (p0 + 4 > cl) nib &= (p0 >= cl) ? 0u : ((1u << (cl - p0)) - 1u);
-                m[p0 >> 6] |= (uint64_t)nib << (p0 & 63);
+                m |= (uint64_t)nib << p0;
             }
         }
     }
-    const int fb = next_bit(m, 0);
-    const int32_t first_b = fb >= 0 ? cs + fb : len;
+    const int32_t first_b = m ? cs + __builtin_ctzll(m) : len;
     const int32_t next_after = block_excl_min_rev<LZE_THREADS / kWave>(first_b, len, s_i32);
 
-    // 3a. qualifying runs of this chunk
-    int32_t first_qi = LZE_INF, last_qj = 0;
+    // 3. one pass over the runs: first qualifying run (i1, its match length),
+    //    last qualifying j, and the bytes of the sequences after the first
+    int32_t first_qi = LZE_INF, first_ml = 0, last_qj = 0, rest = 0;
     for_each_run(m, cs, next_after, [&](int32_t s, int32_t e) {
         const int32_t i = s + 1, j = e < len - 5 ? e : len - 5;
         if (j - i >= 4 && i <= len - 12) {
-            if (first_qi == LZE_INF) first_qi = i;
+            if (first_qi == LZE_INF) {
+                first_qi = i;
+                first_ml = j - i;
+            } else {
+                rest += seq_bytes(i - last_qj, j - i);
+            }
             last_qj = j;
         }
     });
     int32_t a_final;
     const int32_t carry_j = block_excl_max<LZE_THREADS / kWave>(last_qj, 0, s_i32, &a_final);
     const int32_t next_qi = block_excl_min_rev<LZE_THREADS / kWave>(first_qi, LZE_INF, s_i32);
-
-    // 3b. bytes of the sequences this thread owns
-    int32_t tot = 0;
-    {
-        int32_t la = carry_j;
-        for_each_run(m, cs, next_after, [&](int32_t s, int32_t e) {
-            const int32_t i = s + 1, j = e < len - 5 ? e : len - 5;
-            if (j - i >= 4 && i <= len - 12) {
-                tot += seq_bytes(i - la, j - i);
-                la = j;
-            }
-        });
-    }
+    const int32_t tot = first_qi == LZE_INF ? 0 : seq_bytes(first_qi - carry_j, first_ml) + rest;
     int32_t qsum;
     const int32_t pos0 = block_excl_sum<LZE_THREADS / kWave>(tot, s_i32, &qsum);
     const int32_t ll_final = len - a_final;
@@ -219,7 +229,10 @@ __global__ __launch_bounds__(LZE_THREADS) void k_lz4_encode(Lz4EncArgs a) {
     __syncthreads();
     const uint64_t off = s_off;
     if ((int64_t)(off + comp) > a.cap) return;
-    const Out out{a.payload + off, (int32_t)comp};
+    uint8_t *dst = a.payload + off;
+    const int32_t shift = (int32_t)((uintptr_t)dst & 15);  // window byte 0 <-> 16-byte aligned address
+    const bool staged = (int32_t)comp + shift <= LZE_WIN + 16;
+    const Out out{staged ? s_win + shift : dst, (int32_t)comp};
 
     // 5. emit
     int32_t la = carry_j, pos = pos0;
@@ -231,8 +244,7 @@ __global__ __launch_bounds__(LZE_THREADS) void k_lz4_encode(Lz4EncArgs a) {
         const int32_t h = 1 + ext_bytes(ll);
         out.put(pos, ((ll >= 15 ? 15 : ll) << 4) | (ml - 4 >= 15 ? 15 : ml - 4));
         if (ll >= 15) put_len(out, pos + 1, ll);
-        const int32_t lo = la > cs ? la : cs;
-        for (int32_t p = lo; p < i; ++p) out.put(pos + h + (p - la), mine[p - cs]);
+        for (int32_t p = (la > cs ? la : cs); p < i; ++p) out.put(pos + h + (p - la), s_img[img_addr<CHLOG>(p)]);
         int32_t q = pos + h + ll;
         out.put(q++, 1);
         out.put(q++, 0);
@@ -246,12 +258,25 @@ __global__ __launch_bounds__(LZE_THREADS) void k_lz4_encode(Lz4EncArgs a) {
         if (lo < chunk_end) {
             const int32_t ll = (next_qi != LZE_INF ? next_qi : len) - la;
             const int32_t h = 1 + ext_bytes(ll);
-            for (int32_t p = lo; p < chunk_end; ++p) out.put(pos + h + (p - la), mine[p - cs]);
+            for (int32_t p = lo; p < chunk_end; ++p) out.put(pos + h + (p - la), s_img[img_addr<CHLOG>(p)]);
         }
     }
     if (t == 0) {
         out.put(qsum, (ll_final >= 15 ? 15 : ll_final) << 4);
         if (ll_final >= 15) put_len(out, qsum + 1, ll_final);
+    }
+    if (!staged) return;
+    __syncthreads();
+    // copy the window out: 16-byte stores for whole aligned pieces, bytes for
+    // the first and last piece (shared with the neighbouring blocks' bytes)
+    const int32_t end = shift + (int32_t)comp;
+    uint8_t *base = dst - shift;
+    for (int32_t q = 16 * t; q < end; q += 16 * LZE_THREADS) {
+        if (q >= shift && q + 16 <= end) {
+            *reinterpret_cast<uint4 *>(base + q) = *reinterpret_cast<const uint4 *>(s_win + q);
+        } else {
+            for (int32_t x = (q > shift ? q : shift); x < q + 16 && x < end; ++x) base[x] = s_win[x];
+        }
     }
 }
 
@@ -273,7 +298,6 @@ extern "C" int pulse_launch_lz4_encode(const void *src, const void *src_xor, int
     a.src_xor = static_cast<const uint8_t *>(src_xor);
     a.nbytes = nbytes;
     a.block_bytes = block_bytes;
-    a.chunk = block_bytes / LZE_THREADS;
     a.payload = payload;
     a.cap = cap;
     a.comp_sizes = comp_sizes;
@@ -284,6 +308,8 @@ extern "C" int pulse_launch_lz4_encode(const void *src, const void *src_xor, int
     a.status = reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + sizeof(WsHeader));
     const int64_t nb = (nbytes + block_bytes - 1) / block_bytes;
     a.nblocks = (uint32_t)nb;
-    k_lz4_encode<<<dim3((unsigned)nb), dim3(LZE_THREADS), 0, stream>>>(a);
+    if (block_bytes == 65536) k_lz4_encode<6><<<dim3((unsigned)nb), dim3(LZE_THREADS), 0, stream>>>(a);
+    else if (block_bytes == 32768) k_lz4_encode<5><<<dim3((unsigned)nb), dim3(LZE_THREADS), 0, stream>>>(a);
+    else k_lz4_encode<4><<<dim3((unsigned)nb), dim3(LZE_THREADS), 0, stream>>>(a);
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }
