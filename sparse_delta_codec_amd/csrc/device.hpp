@@ -11,6 +11,10 @@ namespace pulse {
 
 constexpr int kWave = 64;
 
+// native 16-byte vector: copies stay in registers (HIP's uint4 struct copies
+// can turn into memcpy through the stack)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 __device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
 
@@ -65,6 +69,16 @@ __device__ __forceinline__ T wave_reduce_sum(T v) {
     for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
     return v;
 }
+
+// Workgroup barrier that orders LDS only: waits for this wave's LDS accesses,
+// not for its global loads, so loads issued before it stay in flight across it
+// (__syncthreads would drain them).  The memory clobber keeps the compiler
+// from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Scheduling fence: the instruction scheduler moves nothing across it (no
+// instruction is emitted), e.g. to keep loads in the order their waits assume.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // ---- block-level scans (NW waves); `sh` holds NW entries, one barrier pair ---
 // exclusive sum; returns the thread's exclusive prefix, *total the block sum

@@ -6,27 +6,29 @@
 // pipeline ("Moving the pipeline onto GPUs").  The byte format is the public
 // LZ4 block format; any valid block is accepted, not only the canonical parse.
 //
-// The token chain of a block is inherently serial, so it is split from the
-// data movement:
-//  K1 k_lz4_parse   one LANE per block: checks the block table (inside the
-//                   payload, no block starting before the end of an earlier
-//                   one -- a prefix max over blocks by decoupled look-back),
-//                   walks the token chain with a 16-byte register window,
-//                   validates it, and records token positions in a bitmap
-//                   (1 bit per compressed byte, disjoint per block).  64 blocks
-//                   are parsed per wave, so the serial chains run in parallel.
-//  K2 k_lz4_decode  one WORKGROUP per block: bitmap -> token list (popcount
-//                   scan) -> per-sequence headers, one thread each -> output
-//                   offsets (block scan) -> each thread rebuilds 16-byte output
-//                   chunks directly from the compressed bytes and XORs them into
-//                   dst with coalesced 16-byte accesses (all-zero chunks are
-//                   skipped in XOR mode).  Valid when every match copies from
-//                   its own sequence's literals (offset <= literal length),
-//                   which holds for every block the canonical encoder writes.
-//  K3 k_lz4_slow    general path for the other blocks: sequential parse by one
-//                   thread, cooperative copies into a 64 KiB LDS image, then a
-//                   coalesced XOR/store.
-// K1 validates a block completely before K2/K3 write any byte of its range.
+// A block's token chain is serial, while applying it is a dense stream (a
+// sparse mask still changes nearly every cache line of dst).  Three kernels:
+//  K1 k_lz4_parse   one LANE per block, 64 blocks per wave.  Checks the block
+//                   table (inside the payload, no block starting before the
+//                   end of an earlier one: a prefix max over blocks by
+//                   decoupled look-back), then walks each block's token chain
+//                   from a 512-byte LDS ring of its compressed bytes that the
+//                   wave refills with coalesced loads when lanes run out.  A
+//                   block in the form the canonical encoder writes (every match
+//                   has offset 1 and follows >= 1 literal) is validated in full
+//                   and every 32nd sequence start (input, output position) is
+//                   recorded as a checkpoint; any other block is handed to K3.
+//  K2 k_lz4_fast    one WORKGROUP per checkpointed block: stages its compressed
+//                   bytes in LDS, starts the loads of its dst range (XOR mode),
+//                   rebuilds the block in a zeroed LDS image with one thread
+//                   per 32-sequence segment (long literal runs and non-zero
+//                   fills are deferred and copied by the whole workgroup), then
+//                   XORs (or stores) the image with 16-byte accesses; chunks
+//                   whose mask bytes are all zero are not written back.
+//  K3 k_lz4_slow    every other block: serial, fully validating parse by one
+//                   thread over LDS-staged input, cooperative copies into a
+//                   64 KiB LDS image, then a coalesced XOR / store.
+// No byte of a block's dst range is written unless the whole block is valid.
 #include "device.hpp"
 
 namespace pulse {
@@ -34,6 +36,13 @@ namespace pulse {
 constexpr uint32_t BI_BAD = 0x80000000u;
 constexpr uint32_t BI_SLOW = 0x40000000u;
 constexpr uint32_t BI_NSEQ = 0x3FFFFFFFu;
+
+// Checkpoints: one per kCkEvery sequences.  A sequence that is not the last
+// one takes >= 3 compressed bytes (token, 2-byte offset), so a block of S
+// bytes holds at most floor(S / 96) + 1 checkpoints; block b's checkpoints
+// start at off_b / 96 + 2 b, which keeps the blocks' regions disjoint.
+constexpr uint32_t kCkEvery = 32;
+constexpr uint64_t kCkBytes = 3 * kCkEvery;
 
 struct Lz4DecArgs {
     const uint8_t *payload;
@@ -47,59 +56,190 @@ struct Lz4DecArgs {
     int32_t mode;  // 0 store, 1 xor
     uint32_t *d_status;
     WsHeader *hdr;
-    uint64_t *status;  // look-back words of K1 (one per K1 workgroup)
-    uint32_t *binfo;   // per block: BI_BAD | BI_SLOW | number of sequences
-    uint32_t *slow_list;
-    uint32_t *bitmap;
+    uint64_t *status;    // look-back words of K1 (one per K1 workgroup)
+    uint32_t *binfo;     // per block: BI_BAD | BI_SLOW | number of sequences
+    uint32_t *slow_list; // blocks for K3
+    uint2 *ckpt;         // checkpoints (input position, output position)
     uint32_t k1_tiles;
 };
 
+__device__ __forceinline__ int64_t ck_base(uint64_t off, int64_t b) { return (int64_t)(off / kCkBytes) + 2 * b; }
+
+__device__ __forceinline__ uint32_t block_len(const Lz4DecArgs &a, int64_t b) {
+    const int64_t rest = a.nbytes - b * (int64_t)a.block_bytes;
+    return (uint32_t)(rest < a.block_bytes ? rest : a.block_bytes);
+}
+
 // ---- K1 ----------------------------------------------------------------------
-// Reads byte i of a block through an aligned 16-byte window; an aligned 16-byte
-// load that contains a byte of the payload never leaves that byte's 4 KiB page.
-struct Window {
-    uintptr_t base;  // address of byte 0 of the block
-    uintptr_t cur;   // aligned address held in w, or 1 (none)
-    uint4 w;
-    __device__ __forceinline__ uint32_t get(int64_t i) {
-        const uintptr_t a = base + (uintptr_t)i;
-        const uintptr_t al = a & ~(uintptr_t)15;
-        if (al != cur) {
-            w = *reinterpret_cast<const uint4 *>(al);
-            cur = al;
-        }
-        const uint32_t k = (uint32_t)(a - al);
-        const uint32_t d = (k < 8) ? ((k < 4) ? w.x : w.y) : ((k < 12) ? w.z : w.w);
-        return (d >> (8 * (k & 3))) & 0xFFu;
-    }
-};
+constexpr int K1_RING = 512;                   // bytes of compressed stream held per lane
+constexpr int K1_PIECES = K1_RING / 16;        // 16-byte pieces per ring
+constexpr int K1_RPI = kWave / K1_PIECES;      // rings filled by one load instruction
+constexpr int K1_BATCH = 8;                    // loads in flight per lane
+constexpr int K1_RPB = K1_RPI * K1_BATCH;      // rings per batch
+static_assert(kWave % K1_PIECES == 0 && kWave % K1_RPB == 0 && K1_RPB < 64, "ring geometry");
 
-struct BitWriter {
-    uint32_t *words;   // this block's bitmap words
-    int64_t cur;       // word being filled
-    uint32_t bits;
-    __device__ __forceinline__ void mark(int64_t pos) {
-        const int64_t w = pos >> 5;
-        if (w != cur) {
-            words[cur] = bits;
-            for (int64_t z = cur + 1; z < w; ++z) words[z] = 0u;
-            cur = w;
-            bits = 0u;
+// Refills the rings of the lanes that ask with the K1_RING bytes starting at
+// their position `ip` in the block rounded down to a 16-byte aligned address;
+// rb becomes the ring's start relative to the block.  Lanes fetch one piece
+// each, K1_BATCH loads in flight before the LDS writes; a lane without a piece
+// to fetch reloads the aligned piece holding payload byte 0 and drops it into
+// its spill slot past the rings.  Pieces starting past the payload end are not
+// fetched: an aligned 16-byte load that starts inside the payload never leaves
+// the page holding its first byte.
+__device__ __forceinline__ void ring_refill(uint8_t *rings, const uint8_t *pay, int64_t pay_bytes, int64_t boff,
+                                            int32_t &rb, bool need, uint32_t ip) {
+    const int64_t mis = (int64_t)(reinterpret_cast<uintptr_t>(pay) & 15);
+    int64_t rbo = 0;
+    if (need) {
+        rbo = ((boff + ip + mis) & ~(int64_t)15) - mis;  // pay + rbo is 16-byte aligned
+        rb = (int32_t)(rbo - boff);
+    }
+    const uint64_t nmask = __ballot(need);
+    const int lane = lane_id();
+    const int k = lane % K1_PIECES, r = lane / K1_PIECES;
+#pragma unroll
+    for (int g = 0; g < kWave; g += K1_RPB) {
+        if (((nmask >> g) & ((1ull << K1_RPB) - 1)) == 0) continue;
+        u32x4 v[K1_BATCH];
+        bool ok[K1_BATCH];
+#pragma unroll
+        for (int u = 0; u < K1_BATCH; ++u) {
+            const int j = g + u * K1_RPI + r;
+            const int64_t o = __shfl(rbo, j, kWave) + 16 * k;
+            ok[u] = ((nmask >> j) & 1ull) && o < pay_bytes;
+            v[u] = *reinterpret_cast<const u32x4 *>(pay + (ok[u] ? o : -mis));
         }
-        bits |= 1u << (pos & 31);
+        // unconditional stores keep all loads of the batch ahead of the first write
+#pragma unroll
+        for (int u = 0; u < K1_BATCH; ++u) {
+            const int j = g + u * K1_RPI + r;
+            uint8_t *to = ok[u] ? rings + j * K1_RING + 16 * k : rings + kWave * K1_RING + 16 * lane;
+            *reinterpret_cast<u32x4 *>(to) = v[u];
+        }
     }
-    __device__ __forceinline__ void finish(int64_t nwords) {
-        words[cur] = bits;
-        for (int64_t z = cur + 1; z < nwords; ++z) words[z] = 0u;
-    }
-};
+    __syncthreads();  // one-wave workgroup: the refilled rings are visible to their owners
+}
 
-__global__ __launch_bounds__(256) void k_lz4_parse(Lz4DecArgs a) {
+// One lane's walk over its block (S compressed bytes, len decoded bytes).
+// Each step consumes one sequence: the token (with literal-length bytes and
+// the skipped literals), then the offset (with match-length bytes).  A step
+// whose bytes lie past the ring stalls the lane until the wave's next refill;
+// a length chain longer than a whole ring (not possible within a 64 KiB block
+// without overflowing it, kept for safety) hands the block to K3.
+__device__ __forceinline__ void k1_walk(uint8_t *rings, const uint8_t *ring, bool active, const uint8_t *pay,
+                                        int64_t pay_bytes, int64_t boff, uint32_t S, uint32_t len, uint2 *ck,
+                                        bool &bad, bool &slow, uint32_t &nseq) {
+    int32_t rb = -(1 << 30);  // empty ring: every position maps past it
+    uint32_t ip = 0, op = 0, tok = 0;
+    bool at_off = false;
+    bool done = !active;
+    while (__ballot(!done)) {
+        bool stalled = false;
+        while (true) {
+            const bool run = !done && !stalled;
+            if (!__ballot(run)) break;
+            if (run) {
+                if (!at_off) {
+                    const uint32_t r = ip - (uint32_t)rb;
+                    if (ip >= S) {
+                        bad = true;
+                    } else if (r >= (uint32_t)K1_RING) {
+                        stalled = true;
+                    } else {
+                        tok = ring[r];
+                        uint32_t q = ip + 1, ll = tok >> 4;
+                        bool ok = true;
+                        if (ll == 15) {
+                            while (true) {
+                                if (q >= S) { bad = true; ok = false; break; }
+                                const uint32_t rq = q - (uint32_t)rb;
+                                if (rq >= (uint32_t)K1_RING) {
+                                    ok = false;
+                                    if (r < 16) slow = true;
+                                    else stalled = true;
+                                    break;
+                                }
+                                const uint32_t x = ring[rq];
+                                ++q;
+                                ll += x;
+                                if (ll > len) { bad = true; ok = false; break; }
+                                if (x != 255) break;
+                            }
+                        }
+                        if (ok) {
+                            if (ll > S - q || ll > len - op) {
+                                bad = true;
+                            } else {
+                                if (nseq % kCkEvery == 0) ck[nseq / kCkEvery] = make_uint2(ip, op);
+                                ++nseq;
+                                ip = q + ll;
+                                op += ll;
+                                if (ip == S) {
+                                    done = true;
+                                    if (op != len) bad = true;
+                                } else if (ll == 0) {
+                                    slow = true;  // a match right after a match: not the canonical form
+                                } else {
+                                    at_off = true;
+                                }
+                            }
+                        }
+                    }
+                }
+                if (at_off && !done && !stalled && !bad && !slow) {
+                    const uint32_t r = ip - (uint32_t)rb;
+                    if (S - ip < 2) {
+                        bad = true;
+                    } else if (r >= (uint32_t)(K1_RING - 2)) {
+                        stalled = true;
+                    } else {
+                        const uint32_t mo = (uint32_t)ring[r] | ((uint32_t)ring[r + 1] << 8);
+                        uint32_t x = ring[r + 2];  // first match-length byte, if there is one
+                        uint32_t q = ip + 2, ml = (tok & 15) + 4;
+                        bool ok = true;
+                        if ((tok & 15) == 15) {
+                            while (true) {
+                                if (q >= S) { bad = true; ok = false; break; }
+                                ++q;
+                                ml += x;
+                                if (ml > len) { bad = true; ok = false; break; }
+                                if (x != 255) break;
+                                const uint32_t rq = q - (uint32_t)rb;
+                                if (rq >= (uint32_t)K1_RING) {
+                                    if (q >= S) { bad = true; ok = false; break; }
+                                    ok = false;
+                                    if (r < 16) slow = true;
+                                    else stalled = true;
+                                    break;
+                                }
+                                x = ring[rq];
+                            }
+                        }
+                        if (ok) {
+                            if (mo == 0 || mo > op || ml > len - op) bad = true;
+                            else if (mo != 1) slow = true;
+                            else {
+                                op += ml;
+                                ip = q;
+                                at_off = false;
+                            }
+                        }
+                    }
+                }
+                if (bad || slow) done = true;
+            }
+        }
+        if (!__ballot(!done)) break;
+        ring_refill(rings, pay, pay_bytes, boff, rb, stalled && !done, ip);
+    }
+}
+
+__global__ __launch_bounds__(64) void k_lz4_parse(Lz4DecArgs a) {
+    __shared__ __align__(16) uint8_t s_rings[kWave * K1_RING + kWave * 16];  // rings, then spill slots
     __shared__ uint32_t s_tile, s_tag;
-    __shared__ uint64_t s_scan[4];
-    __shared__ uint64_t s_pre;
-    const int t = threadIdx.x;
-    if (t == 0) {
+    __shared__ uint64_t s_scan[1];
+    const int lane = lane_id();
+    if (lane == 0) {
         uint32_t tile, tag;
         ws_begin(a.hdr, a.k1_tiles, &tile, &tag);
         s_tile = tile;
@@ -108,10 +248,10 @@ __global__ __launch_bounds__(256) void k_lz4_parse(Lz4DecArgs a) {
     __syncthreads();
     const uint32_t tile = s_tile, tag = s_tag;
     if (tile >= a.k1_tiles) {  // inconsistent workspace state: touch nothing
-        if (t == 0) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
+        if (lane == 0) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
         return;
     }
-    const int64_t b = (int64_t)tile * 256 + t;
+    const int64_t b = (int64_t)tile * 64 + lane;
     const bool live = b < a.nblocks;
 
     // table checks: inside the payload, not before the end of any earlier block
@@ -129,264 +269,247 @@ __global__ __launch_bounds__(256) void k_lz4_parse(Lz4DecArgs a) {
         end = e < lim ? e : lim;
     }
     uint64_t tile_max;
-    const uint64_t in_tile = block_excl_max<4>(end, (uint64_t)0, s_scan, &tile_max);
-    if (wave_id() == 0) {
-        bool failed = false;
-        const uint64_t pre = lookback_wave<true>(a.status, tile, tag, tile_max, &failed);
-        if (lane_id() == 0) {
-            if (failed) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
-            s_pre = pre;
-        }
-    }
-    __syncthreads();
-    const uint64_t before = in_tile > s_pre ? in_tile : s_pre;
+    const uint64_t in_tile = block_excl_max<1>(end, (uint64_t)0, s_scan, &tile_max);
+    bool failed = false;
+    const uint64_t pre = lookback_wave<true>(a.status, tile, tag, tile_max, &failed);
+    if (failed && lane == 0) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
+    const uint64_t before = in_tile > pre ? in_tile : pre;
     if (live && b > 0 && off < before) bad = true;
-    if (!live) return;
 
-    const int64_t len = (a.nbytes - b * (int64_t)a.block_bytes) < a.block_bytes
-                            ? (a.nbytes - b * (int64_t)a.block_bytes)
-                            : a.block_bytes;
+    const uint32_t len = live ? block_len(a, b) : 0;
+    uint2 *ck = a.ckpt + (live ? ck_base(off, b) : 0);
     uint32_t nseq = 0;
     bool slow = false;
-    if (!bad) {
-        Window win{(uintptr_t)(a.payload + off), (uintptr_t)1, make_uint4(0, 0, 0, 0)};
-        BitWriter bw{a.bitmap + (off >> 5) + b, 0, 0u};
-        const int64_t Sb = (int64_t)S;
-        int64_t ip = 0, op = 0;
-        while (true) {
-            if (ip >= Sb) { bad = true; break; }
-            bw.mark(ip);
-            const uint32_t tok = win.get(ip++);
-            int64_t ll = tok >> 4;
-            if (ll == 15) {
-                uint32_t x;
-                do {
-                    if (ip >= Sb) { bad = true; break; }
-                    x = win.get(ip++);
-                    ll += x;
-                } while (x == 255 && ll <= len);
-                if (bad) break;
-            }
-            if (ll > Sb - ip || ll > len - op) { bad = true; break; }
-            ip += ll;
-            op += ll;
-            ++nseq;
-            if (ip == Sb) {
-                if (op != len) bad = true;
-                break;
-            }
-            if (Sb - ip < 2) { bad = true; break; }
-            const int64_t mo = (int64_t)win.get(ip) | ((int64_t)win.get(ip + 1) << 8);
-            ip += 2;
-            if (mo == 0 || mo > op) { bad = true; break; }
-            int64_t ml = (tok & 15) + 4;
-            if ((tok & 15) == 15) {
-                uint32_t x;
-                do {
-                    if (ip >= Sb) { bad = true; break; }
-                    x = win.get(ip++);
-                    ml += x;
-                } while (x == 255 && ml <= len);
-                if (bad) break;
-            }
-            if (ml > len - op) { bad = true; break; }
-            if (mo > ll) slow = true;  // the match reaches outside its own literals
-            op += ml;
+    k1_walk(s_rings, s_rings + lane * K1_RING, !bad, a.payload, a.payload_bytes, (int64_t)off, (uint32_t)S, len, ck,
+            bad, slow, nseq);
+    if (live) {
+        if (bad) {
+            a.binfo[b] = BI_BAD;
+            or_agent32(a.d_status, 4u /*PULSE_DS_CORRUPT*/);
+        } else if (slow) {
+            a.binfo[b] = BI_SLOW;
+            const uint32_t k = add_agent32(&a.hdr->aux, 1u);
+            if (k < a.nblocks) a.slow_list[k] = (uint32_t)b;
+        } else {
+            a.binfo[b] = nseq;
         }
-        if (!bad) bw.finish((Sb + 31) >> 5);
-    }
-    if (bad) {
-        a.binfo[b] = BI_BAD;
-        or_agent32(a.d_status, 4u /*PULSE_DS_CORRUPT*/);
-    } else if (slow) {
-        a.binfo[b] = BI_SLOW | nseq;
-        const uint32_t k = add_agent32(&a.hdr->aux, 1u);
-        if (k < a.nblocks) a.slow_list[k] = (uint32_t)b;
-    } else {
-        a.binfo[b] = nseq;
     }
 }
 
 // ---- K2 ----------------------------------------------------------------------
-constexpr int LZD_THREADS = 256;
-constexpr int LZD_BATCH = 2048;
+constexpr int K2_THREADS = 256;
+constexpr int K2_STAGE = 14336;  // compressed bytes staged in LDS (image + stage: 2 workgroups per CU)
+constexpr int K2_SPT = (K2_STAGE / 16 + K2_THREADS - 1) / K2_THREADS;
+constexpr uint32_t K2_LONG = 32;  // literal runs and fills longer than this are deferred
+constexpr int K2_QCAP = 128;
+constexpr uint32_t K2_FILL = 0x80000000u;
 
-struct SeqHdr {
-    uint32_t lit;   // literal start in the compressed block
-    uint32_t ll;    // literal length
-    uint32_t mo;    // match offset (0: final sequence)
-    uint32_t len;   // literal + match length
-    uint32_t next;  // position after the sequence
+struct K2Queue {
+    uint32_t op[K2_QCAP], n[K2_QCAP], src[K2_QCAP];  // src: input position, or K2_FILL | byte
+    uint32_t count;
 };
 
-__device__ __forceinline__ SeqHdr parse_seq(const uint8_t *in, uint32_t p, uint32_t S) {
-    SeqHdr h;
-    const uint32_t tok = in[p];
-    uint32_t q = p + 1;
-    uint32_t ll = tok >> 4;
-    if (ll == 15) {
-        uint32_t x;
-        do {
-            x = in[q++];
-            ll += x;
-        } while (x == 255);
-    }
-    h.lit = q;
-    h.ll = ll;
-    q += ll;
-    if (q >= S) {
-        h.mo = 0;
-        h.len = ll;
-        h.next = q;
-        return h;
-    }
-    h.mo = (uint32_t)in[q] | ((uint32_t)in[q + 1] << 8);
-    q += 2;
-    uint32_t ml = (tok & 15) + 4;
-    if ((tok & 15) == 15) {
-        uint32_t x;
-        do {
-            x = in[q++];
-            ml += x;
-        } while (x == 255);
-    }
-    h.len = ll + ml;
-    h.next = q;
-    return h;
+__device__ __forceinline__ bool k2_defer(K2Queue &qu, uint32_t op, uint32_t n, uint32_t src) {
+    const uint32_t e = atomicAdd(&qu.count, 1u);
+    if (e >= (uint32_t)K2_QCAP) return false;
+    qu.op[e] = op;
+    qu.n[e] = n;
+    qu.src[e] = src;
+    return true;
 }
 
-__global__ __launch_bounds__(LZD_THREADS) void k_lz4_decode(Lz4DecArgs a) {
-    __shared__ uint32_t s_lit[LZD_BATCH];  // token positions, then literal starts
-    __shared__ uint32_t s_ll[LZD_BATCH];
-    __shared__ uint16_t s_mo[LZD_BATCH];
-    __shared__ uint32_t s_out[LZD_BATCH + 1];
-    __shared__ __align__(16) uint8_t s_slot[LZD_THREADS * 16];
-    __shared__ uint32_t s_scan[LZD_THREADS / kWave];
+// Rebuild of one 32-sequence segment (starting at checkpoint c) of a validated
+// canonical block into the zeroed image: literal bytes and the offset-1 fills
+// that repeat a non-zero byte.
+template <typename Src>
+__device__ __forceinline__ void k2_segment(Src src, uint32_t S, uint32_t nseq, uint32_t s, uint2 c, uint8_t *img,
+                                           K2Queue &qu) {
+    uint32_t ip = c.x, op = c.y;
+    const uint32_t rest = nseq - s * kCkEvery;
+    const uint32_t kend = rest < kCkEvery ? rest : kCkEvery;
+    for (uint32_t k = 0; k < kend; ++k) {
+        const uint32_t tok = src[ip];
+        uint32_t q = ip + 1, ll = tok >> 4;
+        if (ll == 15) {
+            uint32_t x;
+            do {
+                x = src[q++];
+                ll += x;
+            } while (x == 255);
+        }
+        uint32_t last = 0;
+        if (ll > K2_LONG) {
+            last = src[q + ll - 1];
+            if (!k2_defer(qu, op, ll, q))
+                for (uint32_t i = 0; i < ll; ++i) img[op + i] = src[q + i];
+        } else {
+            for (uint32_t i = 0; i < ll; ++i) {
+                last = src[q + i];
+                if (last) img[op + i] = (uint8_t)last;
+            }
+        }
+        q += ll;
+        op += ll;
+        if (q >= S) break;  // the final sequence
+        q += 2;             // offset 1
+        uint32_t ml = (tok & 15) + 4;
+        if ((tok & 15) == 15) {
+            uint32_t x;
+            do {
+                x = src[q++];
+                ml += x;
+            } while (x == 255);
+        }
+        if (last) {
+            if (ml <= K2_LONG || !k2_defer(qu, op, ml, K2_FILL | last))
+                for (uint32_t i = 0; i < ml; ++i) img[op + i] = (uint8_t)last;
+        }
+        op += ml;
+        ip = q;
+    }
+}
 
+// Thread t rebuilds segments t, t + 256, ...; the first from the checkpoint c0
+// loaded early (no loop around it, so nothing waits for the dst loads).
+template <typename Src>
+__device__ __forceinline__ void k2_segments(Src src, uint32_t S, uint32_t nseq, const uint2 *ck, uint2 c0,
+                                            uint8_t *img, K2Queue &qu) {
+    const uint32_t nseg = (nseq + kCkEvery - 1) / kCkEvery;
+    const uint32_t t = threadIdx.x;
+    if (t < nseg) k2_segment(src, S, nseq, t, c0, img, qu);
+    for (uint32_t s = t + K2_THREADS; s < nseg; s += K2_THREADS) k2_segment(src, S, nseq, s, ck[s], img, qu);
+}
+
+template <typename Src>
+__device__ __forceinline__ void k2_deferred(Src src, uint8_t *img, const K2Queue &qu) {
+    const uint32_t nq = qu.count < (uint32_t)K2_QCAP ? qu.count : (uint32_t)K2_QCAP;
+    for (uint32_t e = 0; e < nq; ++e) {
+        const uint32_t o = qu.op[e], n = qu.n[e], sv = qu.src[e];
+        if (sv & K2_FILL) {
+            for (uint32_t i = threadIdx.x; i < n; i += K2_THREADS) img[o + i] = (uint8_t)sv;
+        } else {
+            for (uint32_t i = threadIdx.x; i < n; i += K2_THREADS) img[o + i] = src[sv + i];
+        }
+    }
+}
+
+// One block of K2.  STAGED: the compressed bytes fit the LDS stage (else they
+// are read from global memory); the two variants share no code path, so the
+// waits of the staged one never count the other's byte loads.
+template <int IMG, bool XOR, bool STAGED>
+__device__ __forceinline__ void k2_block(const Lz4DecArgs &a, int64_t b, uint32_t nseq, uint64_t off, uint32_t S,
+                                         uint8_t *s_img, uint8_t *s_stage, K2Queue &s_q) {
+    constexpr int CPT = IMG / (16 * K2_THREADS);  // 16-byte chunks per thread
     const int t = threadIdx.x;
+    const uint32_t len = block_len(a, b);
+    const uint8_t *in = a.payload + off;
+    const uint32_t mis = (uint32_t)(reinterpret_cast<uintptr_t>(in) & 15);
+    const uint32_t nfull = len >> 4, nchunk = (len + 15) >> 4;
+    uint4 *dst4 = reinterpret_cast<uint4 *>(a.dst + b * (int64_t)a.block_bytes);
+    uint4 *img4 = reinterpret_cast<uint4 *>(s_img);
+
+    // compressed bytes and the first checkpoint, then dst: waiting for the
+    // former leaves the dst loads in flight.  The stage loads are unconditional
+    // (a thread past the block reloads its first piece) so that none of them
+    // waits behind a branch.
+    u32x4 sv[K2_SPT];
+    const uint32_t nsc = STAGED ? (S + mis + 15) >> 4 : 0;
+    if constexpr (STAGED) {
+        const u32x4 *in4 = reinterpret_cast<const u32x4 *>(in - mis);
+#pragma unroll
+        for (int k = 0; k < K2_SPT; ++k) {
+            const uint32_t c = t + K2_THREADS * k;
+            sv[k] = in4[c < nsc ? c : 0u];
+        }
+    }
+    const uint2 *ck = a.ckpt + ck_base(off, b);
+    const uint32_t nseg = (nseq + kCkEvery - 1) / kCkEvery;
+    const uint2 c0 = ck[(uint32_t)t < nseg ? t : 0];
+    sched_fence();
+    u32x4 dv[CPT];
+    if constexpr (XOR) {
+        const u32x4 *d4 = reinterpret_cast<const u32x4 *>(dst4);
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+            const uint32_t c = t + K2_THREADS * k;
+            dv[k] = d4[c < nfull ? c : 0u];  // (past the block: a reload, never used)
+        }
+    }
+    if (t == 0) s_q.count = 0;
+    if constexpr (STAGED) {
+        // pieces past the block land in the thread's own first image chunk,
+        // which the same thread zeroes right after
+#pragma unroll
+        for (int k = 0; k < K2_SPT; ++k) {
+            const uint32_t c = t + K2_THREADS * k;
+            u32x4 *to = reinterpret_cast<u32x4 *>(c < nsc ? reinterpret_cast<uint4 *>(s_stage) + c : img4 + t);
+            *to = sv[k];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        const uint32_t c = t + K2_THREADS * k;
+        if (c < nchunk) img4[c] = make_uint4(0, 0, 0, 0);
+    }
+    lds_barrier();
+
+    if constexpr (STAGED) {
+        const uint8_t *src = s_stage + mis;
+        k2_segments(src, S, nseq, ck, c0, s_img, s_q);
+        lds_barrier();
+        k2_deferred(src, s_img, s_q);
+    } else {
+        k2_segments(in, S, nseq, ck, c0, s_img, s_q);
+        lds_barrier();
+        k2_deferred(in, s_img, s_q);
+    }
+    lds_barrier();
+
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+        const uint32_t c = t + K2_THREADS * k;
+        if (c < nfull) {
+            const u32x4 v = reinterpret_cast<const u32x4 *>(s_img)[c];
+            if constexpr (XOR) {
+                if ((v.x | v.y | v.z | v.w) != 0u) reinterpret_cast<u32x4 *>(dst4)[c] = dv[k] ^ v;
+            } else {
+                reinterpret_cast<u32x4 *>(dst4)[c] = v;
+            }
+        }
+    }
+    if (nfull < nchunk && (uint32_t)t == nfull % K2_THREADS) {  // ragged tail of the last block
+        uint8_t *d = reinterpret_cast<uint8_t *>(dst4 + nfull);
+        const uint8_t *v = s_img + 16 * nfull;
+        for (uint32_t x = 0; x < (len & 15); ++x) d[x] = XOR ? (uint8_t)(d[x] ^ v[x]) : v[x];
+    }
+}
+
+// IMG: image bytes, >= block_bytes (one instantiation per supported size class);
+// XOR: mode 1.  Both are compile-time so that every load is issued on one path
+// and the waits for the stage loads leave the dst loads in flight.
+template <int IMG, bool XOR>
+__global__ __launch_bounds__(K2_THREADS) void k_lz4_fast(Lz4DecArgs a) {
+    __shared__ __align__(16) uint8_t s_img[IMG];
+    __shared__ __align__(16) uint8_t s_stage[K2_STAGE];
+    __shared__ K2Queue s_q;
     const int64_t b = blockIdx.x;
     const uint32_t info = a.binfo[b];
     if (info & (BI_BAD | BI_SLOW)) return;
-    const uint32_t nseq = info & BI_NSEQ;
     const uint64_t off = a.offs[b];
     const uint32_t S = a.sizes[b];
-    const uint8_t *in = a.payload + off;
-    const int64_t blk = b * (int64_t)a.block_bytes;
-    const uint32_t len = (uint32_t)((a.nbytes - blk) < a.block_bytes ? (a.nbytes - blk) : a.block_bytes);
-    const uint32_t *words = a.bitmap + (off >> 5) + b;
-    const uint32_t nwords = (S + 31) >> 5;
-    const uint32_t wpt = (nwords + LZD_THREADS - 1) / LZD_THREADS;
-    uint8_t *slot = s_slot + t * 16;
-    uint8_t *dstb = a.dst + blk;
-
-    uint32_t out_carry = 0;
-    for (uint32_t bs = 0; bs < nseq; bs += LZD_BATCH) {
-        const uint32_t nb = (nseq - bs) < (uint32_t)LZD_BATCH ? (nseq - bs) : (uint32_t)LZD_BATCH;
-
-        // (1) token positions of ranks [bs, bs + nb)
-        const uint32_t w0 = t * wpt, w1 = (w0 + wpt) < nwords ? (w0 + wpt) : nwords;
-        uint32_t cnt = 0;
-        for (uint32_t w = w0; w < w1; ++w) cnt += __builtin_popcount(words[w]);
-        uint32_t ntok;
-        uint32_t r = block_excl_sum<LZD_THREADS / kWave>(cnt, s_scan, &ntok);
-        for (uint32_t w = w0; w < w1 && r < bs + nb; ++w) {
-            uint32_t x = words[w];
-            while (x) {
-                const uint32_t bit = __builtin_ctz(x);
-                x &= x - 1;
-                if (r >= bs && r < bs + nb) s_lit[r - bs] = (w << 5) + bit;
-                ++r;
-            }
-        }
-        __syncthreads();
-
-        // (2) headers: thread t owns sequences [t*spt, (t+1)*spt)
-        const uint32_t spt = (nb + LZD_THREADS - 1) / LZD_THREADS;
-        const uint32_t k0 = t * spt, k1 = (k0 + spt) < nb ? (k0 + spt) : nb;
-        uint32_t mysum = 0;
-        for (uint32_t k = k0; k < k1; ++k) {
-            const SeqHdr h = parse_seq(in, s_lit[k], S);
-            s_lit[k] = h.lit;
-            s_ll[k] = h.ll;
-            s_mo[k] = (uint16_t)h.mo;
-            s_out[k] = mysum;  // local offset for now
-            mysum += h.len;
-        }
-        uint32_t btot;
-        const uint32_t base = block_excl_sum<LZD_THREADS / kWave>(mysum, s_scan, &btot);
-        for (uint32_t k = k0; k < k1; ++k) s_out[k] += out_carry + base;
-        if (t == 0) s_out[nb] = out_carry + btot;
-        __syncthreads();
-
-        // (3) rebuild the output chunks of [lo, hi) and apply them
-        const uint32_t lo = out_carry, hi = out_carry + btot;
-        if (hi > lo) {
-            for (uint32_t c = (lo >> 4) + t; c <= ((hi - 1) >> 4); c += LZD_THREADS) {
-                const uint32_t q = c << 4;
-                uint32_t p = q > lo ? q : lo;
-                const uint32_t pend = (q + 16) < hi ? (q + 16) : hi;
-                // largest k with s_out[k] <= p
-                uint32_t kl = 0, kh = nb - 1;
-                while (kl < kh) {
-                    const uint32_t mid = (kl + kh + 1) >> 1;
-                    if (s_out[mid] <= p) kl = mid;
-                    else kh = mid - 1;
-                }
-                uint32_t k = kl;
-                *reinterpret_cast<uint4 *>(slot) = make_uint4(0, 0, 0, 0);
-                while (p < pend) {
-                    while (s_out[k + 1] <= p) ++k;
-                    const uint32_t sb = s_out[k], ll = s_ll[k], litend = sb + ll;
-                    if (p < litend) {
-                        const uint32_t e = pend < litend ? pend : litend;
-                        const uint8_t *src = in + s_lit[k] + (p - sb);
-                        for (; p < e; ++p, ++src) slot[p - q] = *src;
-                    } else {
-                        const uint32_t send = s_out[k + 1];
-                        const uint32_t e = pend < send ? pend : send;
-                        const uint32_t mo = s_mo[k];
-                        // byte m of the match = literal (ll - mo + m % mo) of this sequence
-                        const uint8_t *src = in + s_lit[k] + ll - mo;
-                        if (mo == 1) {
-                            const uint8_t v = *src;
-                            if (v)
-                                for (; p < e; ++p) slot[p - q] = v;
-                            p = e;
-                        } else {
-                            for (; p < e; ++p) slot[p - q] = src[(p - litend) % mo];
-                        }
-                    }
-                }
-                const uint4 v = *reinterpret_cast<const uint4 *>(slot);
-                const bool zero = (v.x | v.y | v.z | v.w) == 0u;
-                if (a.mode == 1) {
-                    if (zero) continue;
-                    if (q + 16 <= len) {
-                        uint4 d = *reinterpret_cast<const uint4 *>(dstb + q);
-                        d.x ^= v.x; d.y ^= v.y; d.z ^= v.z; d.w ^= v.w;
-                        *reinterpret_cast<uint4 *>(dstb + q) = d;
-                    } else {
-                        for (uint32_t x = q; x < len; ++x) dstb[x] ^= slot[x - q];
-                    }
-                } else {
-                    if (q >= lo && q + 16 <= hi) {
-                        *reinterpret_cast<uint4 *>(dstb + q) = v;
-                    } else {
-                        const uint32_t x0 = q > lo ? q : lo;
-                        for (uint32_t x = x0; x < pend; ++x) dstb[x] = slot[x - q];
-                    }
-                }
-            }
-        }
-        out_carry = hi;
-        __syncthreads();
-    }
+    const uint32_t mis = (uint32_t)(reinterpret_cast<uintptr_t>(a.payload + off) & 15);
+    if (S + mis <= (uint32_t)K2_STAGE) k2_block<IMG, XOR, true>(a, b, info & BI_NSEQ, off, S, s_img, s_stage, s_q);
+    else k2_block<IMG, XOR, false>(a, b, info & BI_NSEQ, off, S, s_img, s_stage, s_q);
 }
 
 // ---- K3 ----------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_lz4_slow(Lz4DecArgs a) {
+constexpr int K3_THREADS = 256;
+constexpr int K3_STAGE = 66 * 1024;  // holds any block up to the LZ4 bound of 64 KiB
+
+__global__ __launch_bounds__(K3_THREADS) void k_lz4_slow(Lz4DecArgs a) {
     __shared__ __align__(16) uint8_t s_dec[65536];
-    __shared__ uint32_t s_h[5];
+    __shared__ __align__(16) uint8_t s_in[K3_STAGE];
+    __shared__ uint32_t s_h[6];
     const int t = threadIdx.x;
     uint32_t count = ld_agent32(&a.hdr->aux);
     if (count > a.nblocks) count = (uint32_t)a.nblocks;
@@ -394,46 +517,102 @@ __global__ __launch_bounds__(256) void k_lz4_slow(Lz4DecArgs a) {
         const int64_t b = a.slow_list[i];
         const uint64_t off = a.offs[b];
         const uint32_t S = a.sizes[b];
+        const uint32_t len = block_len(a, b);
         const uint8_t *in = a.payload + off;
-        const int64_t blk = b * (int64_t)a.block_bytes;
-        const uint32_t len = (uint32_t)((a.nbytes - blk) < a.block_bytes ? (a.nbytes - blk) : a.block_bytes);
-        uint32_t ip = 0, op = 0;
-        while (true) {
-            // the stream was fully validated by k_lz4_parse
-            if (t == 0) {
-                const SeqHdr h = parse_seq(in, ip, S);
-                s_h[0] = h.lit;
-                s_h[1] = h.ll;
-                s_h[2] = h.mo;
-                s_h[3] = h.next;
-                s_h[4] = h.len - h.ll;
-            }
-            __syncthreads();
-            const uint32_t lit = s_h[0], ll = s_h[1], mo = s_h[2], next = s_h[3], ml = s_h[4];
-            for (uint32_t x = t; x < ll; x += 256) s_dec[op + x] = in[lit + x];
-            __syncthreads();
-            op += ll;
-            if (mo == 0) break;
-            // forward copy with overlap: byte x of the match repeats the mo bytes before it
-            for (uint32_t x = t; x < ml; x += 256) s_dec[op + x] = s_dec[op - mo + (x % mo)];
-            __syncthreads();
-            op += ml;
-            ip = next;
+        const uint32_t mis = (uint32_t)(reinterpret_cast<uintptr_t>(in) & 15);
+        const bool staged = S + mis <= (uint32_t)K3_STAGE;
+        if (staged) {
+            const uint4 *in4 = reinterpret_cast<const uint4 *>(in - mis);
+            for (uint32_t c = t; c < (S + mis + 15) >> 4; c += K3_THREADS)
+                reinterpret_cast<uint4 *>(s_in)[c] = in4[c];
         }
         __syncthreads();
-        for (uint32_t q = 16 * t; q < len; q += 16 * 256) {
-            if (q + 16 <= len) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(s_dec + q);
-                if (a.mode == 1) {
-                    uint4 d = *reinterpret_cast<const uint4 *>(a.dst + blk + q);
-                    d.x ^= v.x; d.y ^= v.y; d.z ^= v.z; d.w ^= v.w;
-                    *reinterpret_cast<uint4 *>(a.dst + blk + q) = d;
-                } else {
-                    *reinterpret_cast<uint4 *>(a.dst + blk + q) = v;
+        const uint8_t *src = staged ? static_cast<const uint8_t *>(s_in + mis) : in;
+        uint32_t ip = 0, op = 0;
+        bool bad = false;
+        while (true) {
+            if (t == 0) {
+                // one sequence, with every check of the block format
+                uint32_t lit = 0, ll = 0, mo = 0, ml = 0, fin = 0, err = 0;
+                if (ip >= S) err = 1;
+                const uint32_t tok = err ? 0u : src[ip++];
+                ll = tok >> 4;
+                if (!err && ll == 15) {
+                    while (true) {
+                        if (ip >= S) { err = 1; break; }
+                        const uint32_t x = src[ip++];
+                        ll += x;
+                        if (ll > len) { err = 1; break; }
+                        if (x != 255) break;
+                    }
                 }
-            } else {
-                for (uint32_t x = q; x < len; ++x)
-                    a.dst[blk + x] = a.mode == 1 ? (uint8_t)(a.dst[blk + x] ^ s_dec[x]) : s_dec[x];
+                if (!err && (ll > S - ip || ll > len - op)) err = 1;
+                if (!err) {
+                    lit = ip;
+                    ip += ll;
+                    if (ip == S) {
+                        fin = 1;
+                        if (op + ll != len) err = 1;
+                    } else if (S - ip < 2) {
+                        err = 1;
+                    } else {
+                        mo = (uint32_t)src[ip] | ((uint32_t)src[ip + 1] << 8);
+                        ip += 2;
+                        if (mo == 0 || mo > op + ll) err = 1;
+                        ml = (tok & 15) + 4;
+                        if (!err && (tok & 15) == 15) {
+                            while (true) {
+                                if (ip >= S) { err = 1; break; }
+                                const uint32_t x = src[ip++];
+                                ml += x;
+                                if (ml > len) { err = 1; break; }
+                                if (x != 255) break;
+                            }
+                        }
+                        if (!err && ml > len - op - ll) err = 1;
+                    }
+                }
+                s_h[0] = lit;
+                s_h[1] = ll;
+                s_h[2] = mo;
+                s_h[3] = ml;
+                s_h[4] = fin;
+                s_h[5] = err;
+            }
+            __syncthreads();
+            const uint32_t lit = s_h[0], ll = s_h[1], mo = s_h[2], ml = s_h[3], fin = s_h[4], err = s_h[5];
+            __syncthreads();
+            if (err) {
+                bad = true;
+                break;
+            }
+            for (uint32_t x = t; x < ll; x += K3_THREADS) s_dec[op + x] = src[lit + x];
+            __syncthreads();
+            op += ll;
+            if (fin) break;
+            // forward copy with overlap: byte x of the match repeats the mo bytes before it
+            for (uint32_t x = t; x < ml; x += K3_THREADS) s_dec[op + x] = s_dec[op - mo + (x % mo)];
+            __syncthreads();
+            op += ml;
+        }
+        if (bad) {
+            if (t == 0) or_agent32(a.d_status, 4u /*PULSE_DS_CORRUPT*/);
+        } else {
+            uint8_t *dstb = a.dst + b * (int64_t)a.block_bytes;
+            for (uint32_t q = 16 * t; q < len; q += 16 * K3_THREADS) {
+                if (q + 16 <= len) {
+                    const uint4 v = *reinterpret_cast<const uint4 *>(s_dec + q);
+                    if (a.mode == 1) {
+                        uint4 d = *reinterpret_cast<const uint4 *>(dstb + q);
+                        d.x ^= v.x; d.y ^= v.y; d.z ^= v.z; d.w ^= v.w;
+                        *reinterpret_cast<uint4 *>(dstb + q) = d;
+                    } else {
+                        *reinterpret_cast<uint4 *>(dstb + q) = v;
+                    }
+                } else {
+                    for (uint32_t x = q; x < len; ++x)
+                        dstb[x] = a.mode == 1 ? (uint8_t)(dstb[x] ^ s_dec[x]) : s_dec[x];
+                }
             }
         }
         __syncthreads();
@@ -456,10 +635,10 @@ namespace {
 // look-back status words of one call never overlap the per-block data another
 // call of a different size left behind (a stale word must never carry a
 // matching epoch tag).  Status: 1 word per KiB; block info and slow list:
-// ws/8 bytes each; bitmap: the rest.
+// ws/8 bytes each; checkpoints: the rest.
 struct DecLayout {
-    size_t status, binfo, slow, bitmap;
-    size_t status_words, blocks, bitmap_words;
+    size_t status, binfo, slow, ckpt;
+    size_t status_words, blocks, ck_entries;
 };
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 DecLayout dec_layout(size_t ws) {
@@ -469,22 +648,30 @@ DecLayout dec_layout(size_t ws) {
     L.binfo = al256(L.status + 8 * L.status_words);
     L.blocks = ws >> 5;
     L.slow = al256(L.binfo + 4 * L.blocks);
-    L.bitmap = al256(L.slow + 4 * L.blocks);
-    L.bitmap_words = ws > L.bitmap ? (ws - L.bitmap) / 4 : 0;
+    L.ckpt = al256(L.slow + 4 * L.blocks);
+    L.ck_entries = ws > L.ckpt ? (ws - L.ckpt) / sizeof(uint2) : 0;
     return L;
+}
+size_t ck_needed(int64_t nblocks, int64_t payload_bytes) {
+    return (size_t)payload_bytes / kCkBytes + 2 * (size_t)nblocks + 2;
 }
 bool dec_fits(size_t ws, int64_t nblocks, int64_t payload_bytes) {
     const DecLayout L = dec_layout(ws);
-    const size_t k1 = (size_t)(nblocks + 255) / 256;
-    const size_t words = (size_t)(payload_bytes >> 5) + (size_t)nblocks + 2;
-    return ws >= L.bitmap && k1 <= L.status_words && (size_t)nblocks <= L.blocks && words <= L.bitmap_words;
+    const size_t k1 = (size_t)(nblocks + 63) / 64;
+    return ws >= L.ckpt && k1 <= L.status_words && (size_t)nblocks <= L.blocks &&
+           ck_needed(nblocks, payload_bytes) <= L.ck_entries;
+}
+
+template <int IMG>
+void launch_fast(const Lz4DecArgs &a, hipStream_t stream) {
+    if (a.mode == 1) k_lz4_fast<IMG, true><<<dim3((unsigned)a.nblocks), dim3(K2_THREADS), 0, stream>>>(a);
+    else k_lz4_fast<IMG, false><<<dim3((unsigned)a.nblocks), dim3(K2_THREADS), 0, stream>>>(a);
 }
 }  // namespace
 
 extern "C" size_t pulse_lz4_decode_ws_bytes(int64_t nblocks, int64_t payload_bytes) {
     if (nblocks < 0 || payload_bytes < 0) return 0;
-    const size_t words = (size_t)(payload_bytes >> 5) + (size_t)nblocks + 2;
-    size_t ws = al256(4096 + 32 * (size_t)nblocks + (4 * words) * 4 / 3);
+    size_t ws = al256(4096 + 40 * (size_t)nblocks + 8 * ck_needed(nblocks, payload_bytes) * 4 / 3);
     while (!dec_fits(ws, nblocks, payload_bytes)) ws = al256(ws + ws / 8 + 256);
     return ws;
 }
@@ -514,12 +701,14 @@ extern "C" int pulse_launch_lz4_decode(const uint8_t *payload, int64_t payload_b
     a.status = reinterpret_cast<uint64_t *>(w + L.status);
     a.binfo = reinterpret_cast<uint32_t *>(w + L.binfo);
     a.slow_list = reinterpret_cast<uint32_t *>(w + L.slow);
-    a.bitmap = reinterpret_cast<uint32_t *>(w + L.bitmap);
-    const int64_t k1 = (nblocks + 255) / 256;
+    a.ckpt = reinterpret_cast<uint2 *>(w + L.ckpt);
+    const int64_t k1 = (nblocks + 63) / 64;
     a.k1_tiles = (uint32_t)k1;
-    k_lz4_parse<<<dim3((unsigned)k1), dim3(256), 0, stream>>>(a);
-    k_lz4_decode<<<dim3((unsigned)nblocks), dim3(LZD_THREADS), 0, stream>>>(a);
+    k_lz4_parse<<<dim3((unsigned)k1), dim3(64), 0, stream>>>(a);
+    if (block_bytes <= 16384) launch_fast<16384>(a, stream);
+    else if (block_bytes <= 32768) launch_fast<32768>(a, stream);
+    else launch_fast<65536>(a, stream);
     const int64_t g3 = nblocks < 512 ? nblocks : 512;
-    k_lz4_slow<<<dim3((unsigned)g3), dim3(256), 0, stream>>>(a);
+    k_lz4_slow<<<dim3((unsigned)g3), dim3(K3_THREADS), 0, stream>>>(a);
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }
