@@ -120,118 +120,111 @@ __device__ __forceinline__ void ring_refill(uint8_t *rings, const uint8_t *pay, 
     __syncthreads();  // one-wave workgroup: the refilled rings are visible to their owners
 }
 
+// Lane state of the walk, one word (bit flags in a VGPR keep divergent joins
+// free of per-flag lane-mask bookkeeping).
+constexpr uint32_t F_DONE = 1u, F_BAD = 2u, F_SLOW = 4u, F_STALL = 8u, F_OFF = 16u;
+
+// Reads a length extension (bytes added while they are 255) starting at
+// block position q into n.  r0: ring index of the step's first byte; a chain
+// that leaves a ring refilled at that step cannot be read from the ring at all.
+__device__ __forceinline__ uint32_t read_ext(const uint8_t *ring, int32_t rb, uint32_t S, uint32_t len,
+                                             uint32_t r0, uint32_t &q, uint32_t &n) {
+    while (true) {
+        if (q >= S) return F_BAD | F_DONE;
+        const uint32_t rq = q - (uint32_t)rb;
+        if (rq >= (uint32_t)K1_RING) return r0 < 16 ? (F_SLOW | F_DONE) : F_STALL;
+        const uint32_t x = ring[rq];
+        ++q;
+        n += x;
+        if (n > len) return F_BAD | F_DONE;
+        if (x != 255) return 0;
+    }
+}
+
+struct WalkResult {
+    uint32_t nseq, flags;
+};
+
 // One lane's walk over its block (S compressed bytes, len decoded bytes).
 // Each step consumes one sequence: the token (with literal-length bytes and
 // the skipped literals), then the offset (with match-length bytes).  A step
-// whose bytes lie past the ring stalls the lane until the wave's next refill;
-// a length chain longer than a whole ring (not possible within a 64 KiB block
-// without overflowing it, kept for safety) hands the block to K3.
-__device__ __forceinline__ void k1_walk(uint8_t *rings, const uint8_t *ring, bool active, const uint8_t *pay,
-                                        int64_t pay_bytes, int64_t boff, uint32_t S, uint32_t len, uint2 *ck,
-                                        bool &bad, bool &slow, uint32_t &nseq) {
+// whose bytes lie past the ring stalls the lane until the wave's next refill.
+// The block is handed to K3 (F_SLOW) at the first sequence not in canonical
+// form, or at a length chain longer than a whole ring (impossible within a
+// 64 KiB block without overflowing it; kept for safety).
+__device__ __forceinline__ WalkResult k1_walk(uint8_t *rings, const uint8_t *ring, bool active, const uint8_t *pay,
+                                              int64_t pay_bytes, int64_t boff, uint32_t S, uint32_t len, uint2 *ck) {
     int32_t rb = -(1 << 30);  // empty ring: every position maps past it
-    uint32_t ip = 0, op = 0, tok = 0;
-    bool at_off = false;
-    bool done = !active;
-    while (__ballot(!done)) {
-        bool stalled = false;
+    uint32_t ip = 0, op = 0, tok = 0, nseq = 0;
+    uint32_t f = active ? 0u : F_DONE;
+    while (__ballot(!(f & F_DONE))) {
+        f &= ~F_STALL;
         while (true) {
-            const bool run = !done && !stalled;
+            const bool run = !(f & (F_DONE | F_STALL));
             if (!__ballot(run)) break;
             if (run) {
-                if (!at_off) {
+                if (!(f & F_OFF)) {
                     const uint32_t r = ip - (uint32_t)rb;
                     if (ip >= S) {
-                        bad = true;
+                        f |= F_BAD | F_DONE;
                     } else if (r >= (uint32_t)K1_RING) {
-                        stalled = true;
+                        f |= F_STALL;
                     } else {
                         tok = ring[r];
-                        uint32_t q = ip + 1, ll = tok >> 4;
-                        bool ok = true;
-                        if (ll == 15) {
-                            while (true) {
-                                if (q >= S) { bad = true; ok = false; break; }
-                                const uint32_t rq = q - (uint32_t)rb;
-                                if (rq >= (uint32_t)K1_RING) {
-                                    ok = false;
-                                    if (r < 16) slow = true;
-                                    else stalled = true;
-                                    break;
-                                }
-                                const uint32_t x = ring[rq];
-                                ++q;
-                                ll += x;
-                                if (ll > len) { bad = true; ok = false; break; }
-                                if (x != 255) break;
-                            }
-                        }
-                        if (ok) {
-                            if (ll > S - q || ll > len - op) {
-                                bad = true;
-                            } else {
-                                if (nseq % kCkEvery == 0) ck[nseq / kCkEvery] = make_uint2(ip, op);
-                                ++nseq;
-                                ip = q + ll;
-                                op += ll;
-                                if (ip == S) {
-                                    done = true;
-                                    if (op != len) bad = true;
-                                } else if (ll == 0) {
-                                    slow = true;  // a match right after a match: not the canonical form
-                                } else {
-                                    at_off = true;
-                                }
-                            }
+                        uint32_t q = ip + 1, ll = tok >> 4, e = 0;
+                        if (ll == 15) e = read_ext(ring, rb, S, len, r, q, ll);
+                        if (!e && (ll > S - q || ll > len - op)) e = F_BAD | F_DONE;
+                        if (e) {
+                            f |= e;
+                        } else {
+                            if (nseq % kCkEvery == 0) ck[nseq / kCkEvery] = make_uint2(ip, op);
+                            ++nseq;
+                            ip = q + ll;
+                            op += ll;
+                            if (ip == S) f |= F_DONE | (op != len ? F_BAD : 0u);
+                            else if (ll == 0) f |= F_SLOW | F_DONE;  // a match right after a match
+                            else f |= F_OFF;
                         }
                     }
                 }
-                if (at_off && !done && !stalled && !bad && !slow) {
+                if ((f & (F_OFF | F_DONE | F_STALL)) == F_OFF) {
                     const uint32_t r = ip - (uint32_t)rb;
                     if (S - ip < 2) {
-                        bad = true;
+                        f |= F_BAD | F_DONE;
                     } else if (r >= (uint32_t)(K1_RING - 2)) {
-                        stalled = true;
+                        f |= F_STALL;
                     } else {
                         const uint32_t mo = (uint32_t)ring[r] | ((uint32_t)ring[r + 1] << 8);
-                        uint32_t x = ring[r + 2];  // first match-length byte, if there is one
-                        uint32_t q = ip + 2, ml = (tok & 15) + 4;
-                        bool ok = true;
+                        const uint32_t x0 = ring[r + 2];  // first match-length byte, if there is one
+                        uint32_t q = ip + 2, ml = (tok & 15) + 4, e = 0;
                         if ((tok & 15) == 15) {
-                            while (true) {
-                                if (q >= S) { bad = true; ok = false; break; }
+                            if (q < S && x0 != 255) {
                                 ++q;
-                                ml += x;
-                                if (ml > len) { bad = true; ok = false; break; }
-                                if (x != 255) break;
-                                const uint32_t rq = q - (uint32_t)rb;
-                                if (rq >= (uint32_t)K1_RING) {
-                                    if (q >= S) { bad = true; ok = false; break; }
-                                    ok = false;
-                                    if (r < 16) slow = true;
-                                    else stalled = true;
-                                    break;
-                                }
-                                x = ring[rq];
+                                ml += x0;
+                                if (ml > len) e = F_BAD | F_DONE;
+                            } else {
+                                e = read_ext(ring, rb, S, len, r, q, ml);
                             }
                         }
-                        if (ok) {
-                            if (mo == 0 || mo > op || ml > len - op) bad = true;
-                            else if (mo != 1) slow = true;
-                            else {
-                                op += ml;
-                                ip = q;
-                                at_off = false;
-                            }
+                        if (!e) {
+                            if (mo == 0 || mo > op || ml > len - op) e = F_BAD | F_DONE;
+                            else if (mo != 1) e = F_SLOW | F_DONE;
+                        }
+                        if (e) {
+                            f |= e;
+                        } else {
+                            op += ml;
+                            ip = q;
+                            f &= ~F_OFF;
                         }
                     }
                 }
-                if (bad || slow) done = true;
             }
         }
-        if (!__ballot(!done)) break;
-        ring_refill(rings, pay, pay_bytes, boff, rb, stalled && !done, ip);
+        if (!__ballot(!(f & F_DONE))) break;
+        ring_refill(rings, pay, pay_bytes, boff, rb, (f & (F_STALL | F_DONE)) == F_STALL, ip);
     }
+    return WalkResult{nseq, f};
 }
 
 __global__ __launch_bounds__(64) void k_lz4_parse(Lz4DecArgs a) {
@@ -278,10 +271,11 @@ __global__ __launch_bounds__(64) void k_lz4_parse(Lz4DecArgs a) {
 
     const uint32_t len = live ? block_len(a, b) : 0;
     uint2 *ck = a.ckpt + (live ? ck_base(off, b) : 0);
-    uint32_t nseq = 0;
-    bool slow = false;
-    k1_walk(s_rings, s_rings + lane * K1_RING, !bad, a.payload, a.payload_bytes, (int64_t)off, (uint32_t)S, len, ck,
-            bad, slow, nseq);
+    const WalkResult w =
+        k1_walk(s_rings, s_rings + lane * K1_RING, !bad, a.payload, a.payload_bytes, (int64_t)off, (uint32_t)S, len, ck);
+    const uint32_t nseq = w.nseq;
+    const bool slow = (w.flags & F_SLOW) != 0;
+    bad = bad || (w.flags & F_BAD) != 0;
     if (live) {
         if (bad) {
             a.binfo[b] = BI_BAD;
