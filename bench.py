@@ -118,6 +118,11 @@ def views_equal(a, b, chunk=1 << 30):
     return True
 
 
+def log(msg):
+    """Progress on stderr (the JSON result is the only stdout line)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def src_hash(path):
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -193,6 +198,7 @@ def main():
     n_quant = sum(rows * cols for plan in qplans for (_, rows, cols) in plan)
     torch.cuda.synchronize()
     t_setup = time.time() - t_setup
+    log(f"setup done in {t_setup:.1f} s: {n} params in {len(chunks)} chunks")
 
     stages = ["cast_diff", "apply_patch", "fp8_quant", "lz4_encode", "lz4_decode"]
     ev = {k: [] for k in stages}
@@ -235,6 +241,7 @@ def main():
                 raise SystemExit(f"device status {st} after the first step (capacity or corrupt payload)")
             if not views_equal(b_recv, b_old):
                 raise SystemExit("receiver view did not return to v0 after patch apply + XOR decode")
+    log(f"warm-up done ({max(args.warmup, 1)} steps, end-to-end check passed)")
     counts = cnt.cpu().numpy()
     totals = ctotal.cpu().numpy()
     changed = int(counts.sum())
@@ -256,6 +263,7 @@ def main():
     if not views_equal(b_recv, b_old):
         raise SystemExit("receiver view drifted during the timed steps")
 
+    log(f"timed {args.steps} steps in {t_total:.2f} s")
     ms_step = 1e3 * t_total / args.steps
     stage_ms = {k: sum(a.elapsed_time(b) for a, b in ev[k]) / args.steps for k in stages}
     launches = {k: len(ev[k]) // args.steps for k in stages}
@@ -327,6 +335,7 @@ def main():
         del a, b
 
     if not args.no_cpu_baseline:
+        log("timing the oracle on the host")
         result["cpu_baseline"] = cpu_baseline(specs, offs, W, b_old, args.cpu_sample_frac)
     print(json.dumps(result), flush=True)
 

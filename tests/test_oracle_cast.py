@@ -4,6 +4,8 @@ Each pin is independent of oracle.c: values printed on the pages, torch's CPU
 cast (a library routine), and a nearest-of-set search over all BF16 values in
 binary64.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -21,22 +23,51 @@ def bf16_value(h):
 
 
 # ---- values the pages print -------------------------------------------------
+def _golden(name):
+    vals = {}
+    with open(os.path.join(os.path.dirname(__file__), "golden", name)) as f:
+        for line in f:
+            line = line.split("#")[0].split()
+            if line:
+                vals[line[0]] = (float(line[1]), float(line[2]))
+    return vals
+
+
 def test_pages_worked_values_near_one():
-    """Near 1 the BF16 spacing is ~0.0078 and the rounding boundary ~0.0039; a
-    ~3e-6 Adam step is >1000x smaller and leaves the served value unchanged
-    [Jiang talk 07:49-09:42; Jiang report, "why served weights barely change";
-    PULSE summary, "Osservazione Centrale": threshold ~|w|/256, lr ~3e-6]."""
+    """The pages' worked example for a weight near 1 (tests/golden, with its
+    citation): the oracle's cast has that spacing and boundary, an update of the
+    printed size leaves the served value unchanged, and one just past the printed
+    boundary changes it."""
+    g = _golden("bf16_worked_values_near_one.txt")
     one = oracle.bf16_rne(f2u(1.0))
     assert one == 0x3F80
-    ulp = bf16_value(0x3F81) - bf16_value(0x3F80)
-    assert ulp == 2.0 ** -7 and abs(ulp - 0.0078) < 5e-5          # "~0.0078"
-    assert abs(ulp / 2 - 0.0039) < 5e-5                           # boundary "~0.0039"
-    assert oracle.bf16_rne(f2u(1.0 + 2.0 ** -8)) == 0x3F80         # exactly on the boundary: tie, even
-    assert oracle.bf16_rne(f2u(1.0 + 2.0 ** -8 + 2.0 ** -23)) == 0x3F81  # just above: visible
-    assert oracle.bf16_rne(f2u(1.0 + 3 * 2.0 ** -8)) == 0x3F82     # tie, even
-    assert oracle.bf16_rne(f2u(np.float32(1.0) + np.float32(3e-6))) == 0x3F80
-    assert oracle.bf16_rne(f2u(np.float32(1.0) - np.float32(3e-6))) == 0x3F80
-    assert (2.0 ** -8) / 3e-6 > 1000                               # ">1000x smaller"
+    # spacing: the value right above 1 the cast can produce
+    up = next(h for h in range(0x3F81, 0x3F90) if oracle.bf16_rne(f2u(bf16_value(h))) == h)
+    spacing = bf16_value(up) - 1.0
+    val, tol = g["bf16_spacing_near_one"]
+    assert abs(spacing - val) <= tol
+    # boundary: the smallest upward step that changes the served value
+    lo, hi = 0.0, spacing
+    for _ in range(60):
+        mid = (lo + hi) / 2
+        if oracle.bf16_rne(f2u(np.float32(1.0 + mid))) == one:
+            lo = mid
+        else:
+            hi = mid
+    boundary = hi
+    val, tol = g["rounding_boundary_near_one"]
+    assert abs(boundary - val) <= tol
+    val, _ = g["boundary_over_theta"]
+    assert abs(boundary - val * 1.0) <= 2.0 ** -23
+    step, _ = g["typical_adam_step"]
+    assert oracle.bf16_rne(f2u(np.float32(1.0) + np.float32(step))) == one
+    assert oracle.bf16_rne(f2u(np.float32(1.0) - np.float32(step))) == one
+    ratio, _ = g["min_boundary_over_step"]
+    assert boundary / step > ratio
+    # exact ties around the boundary go to even
+    assert oracle.bf16_rne(f2u(1.0 + 2.0 ** -8)) == 0x3F80
+    assert oracle.bf16_rne(f2u(1.0 + 2.0 ** -8 + 2.0 ** -23)) == 0x3F81
+    assert oracle.bf16_rne(f2u(1.0 + 3 * 2.0 ** -8)) == 0x3F82
 
 
 def test_push_vs_floor_threshold():
