@@ -199,8 +199,22 @@ def lz4_decode_blocks(payload, comp_offsets, comp_sizes, dst, d_status, ws, mode
         _dev(d_status, "d_status", torch.int32), wsp, wsb, _stream(stream)), "lz4_decode_blocks")
 
 
+def _batch_src(t, name):
+    """A [batch, rows, cols] source whose rows are contiguous; the batch stride
+    (elements) may be anything, e.g. one expert's gate inside [gate, up, down]
+    triples.  Returns (data pointer, batch stride)."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype not in _U16:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected 16-bit")
+    if t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != t.shape[2] or t.stride(0) < t.shape[1] * t.shape[2]:
+        raise ValueError(f"{name} must be [batch, rows, cols] with contiguous rows")
+    return t.data_ptr(), t.stride(0)
+
+
 def fp8_block_quant(srcs, codes, scales, batch=1, stream=None):
-    """srcs: list of BF16/uint16 GPU tensors [batch, rows_i, cols] (or [rows_i, cols] when batch == 1)."""
+    """srcs: list of BF16/uint16 GPU tensors [rows_i, cols] (contiguous), or, when
+    batch > 1, [batch, rows_i, cols] views with contiguous rows and any batch stride."""
     cols = srcs[0].shape[-1]
     R = sum(int(t.shape[-2]) for t in srcs)
     for i, t in enumerate(srcs):
@@ -208,9 +222,14 @@ def fp8_block_quant(srcs, codes, scales, batch=1, stream=None):
             raise ValueError(f"srcs[{i}] has shape {tuple(t.shape)}")
     _need(codes, batch * R * cols, "codes")
     _need(scales, 4 * batch * ((R + 127) // 128) * ((cols + 127) // 128), "scales")
-    ptrs = (ctypes.c_void_p * len(srcs))(*[_dev(s, f"srcs[{i}]", _U16) for i, s in enumerate(srcs)])
+    if batch > 1:
+        ps = [_batch_src(s, f"srcs[{i}]") for i, s in enumerate(srcs)]
+        ptrs = (ctypes.c_void_p * len(srcs))(*[p for p, _ in ps])
+        strides = (ctypes.c_int64 * len(srcs))(*[st for _, st in ps])
+    else:
+        ptrs = (ctypes.c_void_p * len(srcs))(*[_dev(s, f"srcs[{i}]", _U16) for i, s in enumerate(srcs)])
+        strides = None
     rows = (ctypes.c_int64 * len(srcs))(*[s.shape[-2] for s in srcs])
-    strides = (ctypes.c_int64 * len(srcs))(*[s.shape[-2] * cols for s in srcs]) if batch > 1 else None
     _check(_lib.fp8_block_quant(
         ctypes.cast(ptrs, ctypes.c_void_p), ctypes.cast(rows, ctypes.c_void_p), len(srcs), cols, batch,
         None if strides is None else ctypes.cast(strides, ctypes.c_void_p),
