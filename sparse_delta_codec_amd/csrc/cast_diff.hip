@@ -8,9 +8,14 @@
 // indices and new absolute values (PULSE technical summary, "1. PULSESync").
 //
 // One launch streams the tensor once; the patch is written in ascending index
-// order by a single-pass decoupled look-back over 16384-element tiles (one
-// atomic ticket per tile, see device.hpp).
+// order by a single-pass decoupled look-back over 16384-element tiles.  The
+// grid is persistent (as many workgroups as are resident at once, launched
+// cooperatively) and walks the tiles in a static order, so no tile waits for
+// one that has not been handed to a running workgroup, and no per-tile atomic
+// ticket is needed (one device-scope atomic per tile on a single address was
+// the throughput limit).
 #include "device.hpp"
+#include "launch.hpp"
 
 namespace pulse {
 
@@ -117,100 +122,171 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-template <bool FROM_F32, bool W_NEW, bool W_MASK>
-__global__ __launch_bounds__(CD_THREADS) void k_cast_compact(CastDiffArgs a) {
-    __shared__ uint32_t s_tile, s_tag;
-    __shared__ uint32_t s_wtot[CD_THREADS / kWave];
-    __shared__ uint64_t s_prefix;
+// Pass 1 of one tile for one thread: loads, cast, compare, the b_new / mask
+// stores; returns the changed flags (bit 4g+k: element g*256 + 4l + k) and
+// keeps the new values in nvp (two BF16 per register).  FULL: the whole tile
+// lies inside [0, n): the 8 groups of a half are loaded before any is used
+// (float4 + 8 bytes per group), and every compare and store works on pairs of
+// BF16 packed in 32 bits.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-    const int t = threadIdx.x, w = wave_id(), l = lane_id();
-    if (t == 0) {
-        uint32_t tile, tag;
-        ws_begin(a.hdr, a.ntiles, &tile, &tag);
-        s_tile = tile;
-        s_tag = tag;
-    }
-    __syncthreads();
-    const uint32_t tile = s_tile, tag = s_tag;
-    if (tile >= a.ntiles) {  // inconsistent workspace state: touch nothing
-        if (t == 0) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
-        return;
-    }
-    const int64_t wbase = (int64_t)tile * CD_TILE + (int64_t)w * CD_WAVE_ELEMS;
+__device__ __forceinline__ uint32_t cast_pair(float x, float y) {
+    return (uint32_t)bf16_rne(__float_as_uint(x)) | ((uint32_t)bf16_rne(__float_as_uint(y)) << 16);
+}
 
-    uint32_t nvp[CD_GROUPS * 2];  // new values, two per register
-    uint64_t flags = 0;           // bit 4g+k: element g*256 + 4l + k changed
+__device__ __forceinline__ uint64_t pair_flags(uint32_t x0, uint32_t x1) {
+    return (uint64_t)((x0 & 0xFFFFu) != 0) | ((uint64_t)((x0 >> 16) != 0) << 1) |
+           ((uint64_t)((x1 & 0xFFFFu) != 0) << 2) | ((uint64_t)((x1 >> 16) != 0) << 3);
+}
+
+template <bool FULL, bool FROM_F32, bool W_NEW, bool W_MASK>
+__device__ __forceinline__ uint64_t cd_pass1(const CastDiffArgs &a, int64_t wbase, int lo, uint32_t nvp[]) {
+    uint64_t flags = 0;
+    if constexpr (FULL) {
+        const float *pw = a.w_new + wbase + lo;
+        const uint16_t *pi = a.b_in + wbase + lo;
+        const uint16_t *po = a.b_old + wbase + lo;
+        uint16_t *pn = a.b_new + wbase + lo;
+        uint16_t *pm = a.mask + wbase + lo;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        uint16_t nv[8][4], ov[8][4];
+        for (int h = 0; h < 2; ++h) {
+            u32x4 fv[8];
+            u32x2 ov[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int64_t e = wbase + (h * 8 + j) * 256 + 4 * l;
-            load_new4<FROM_F32>(a, e, nv[j]);
-            load_old4(a.b_old, e, a.n, ov[j]);
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int g = h * 8 + j;
-            const int64_t e = wbase + g * 256 + 4 * l;
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                if (e + k < a.n && nv[j][k] != ov[j][k]) flags |= 1ull << (4 * g + k);
-            nvp[2 * g] = (uint32_t)nv[j][0] | ((uint32_t)nv[j][1] << 16);
-            nvp[2 * g + 1] = (uint32_t)nv[j][2] | ((uint32_t)nv[j][3] << 16);
-            if constexpr (W_NEW) store4(a.b_new, e, a.n, nv[j]);
-            if constexpr (W_MASK) {
-                uint16_t mv[4];
-#pragma unroll
-                for (int k = 0; k < 4; ++k) mv[k] = ov[j][k] ^ nv[j][k];
-                store4(a.mask, e, a.n, mv);
+            for (int j = 0; j < 8; ++j) {
+                const int off = (h * 8 + j) * 256;
+                if constexpr (FROM_F32) fv[j] = *reinterpret_cast<const u32x4 *>(pw + off);
+                else {
+                    const u32x2 v = *reinterpret_cast<const u32x2 *>(pi + off);
+                    fv[j] = u32x4{v.x, v.y, 0u, 0u};
+                }
+                ov[j] = *reinterpret_cast<const u32x2 *>(po + off);
             }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int g = h * 8 + j;
+                const int off = g * 256;
+                uint32_t p0, p1;
+                if constexpr (FROM_F32) {
+                    p0 = cast_pair(__uint_as_float(fv[j].x), __uint_as_float(fv[j].y));
+                    p1 = cast_pair(__uint_as_float(fv[j].z), __uint_as_float(fv[j].w));
+                } else {
+                    p0 = fv[j].x;
+                    p1 = fv[j].y;
+                }
+                const uint32_t x0 = p0 ^ ov[j].x, x1 = p1 ^ ov[j].y;
+                flags |= pair_flags(x0, x1) << (4 * g);
+                nvp[2 * g] = p0;
+                nvp[2 * g + 1] = p1;
+                if constexpr (W_NEW) *reinterpret_cast<u32x2 *>(pn + off) = u32x2{p0, p1};
+                if constexpr (W_MASK) *reinterpret_cast<u32x2 *>(pm + off) = u32x2{x0, x1};
+            }
+            sched_fence();  // eight groups of loads in flight at a time
+        }
+    } else {
+        // the tile that extends past n: element by element
+#pragma unroll 1
+        for (int g = 0; g < CD_GROUPS; ++g) {
+            const int64_t e = wbase + g * 256 + lo;
+            uint16_t nv[4], ov[4];
+            load_new4<FROM_F32>(a, e, nv);
+            load_old4(a.b_old, e, a.n, ov);
+            uint16_t mv[4];
+            uint64_t f = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                mv[k] = ov[k] ^ nv[k];
+                if (e + k < a.n && mv[k] != 0) f |= 1ull << k;
+            }
+            flags |= f << (4 * g);
+            nvp[2 * g] = (uint32_t)nv[0] | ((uint32_t)nv[1] << 16);
+            nvp[2 * g + 1] = (uint32_t)nv[2] | ((uint32_t)nv[3] << 16);
+            if constexpr (W_NEW) store4(a.b_new, e, a.n, nv);
+            if constexpr (W_MASK) store4(a.mask, e, a.n, mv);
         }
     }
+    return flags;
+}
+
+struct CdShared {
+    uint32_t wtot[CD_THREADS / kWave];
+    uint64_t prefix;
+};
+
+// One tile: pass 1, the tile total, its look-back, pass 2 (ranked stores).
+template <bool FULL, bool FROM_F32, bool W_NEW, bool W_MASK>
+__device__ __forceinline__ void cd_tile(const CastDiffArgs &a, uint32_t tile, uint32_t ep, CdShared &sh) {
+    const int w = wave_id(), l = lane_id();
+    const uint32_t tag = epoch_tag(ep);
+    const int64_t wbase = (int64_t)tile * CD_TILE + (int64_t)w * CD_WAVE_ELEMS;
+    const int lo = 4 * l;
+    uint32_t nvp[CD_GROUPS * 2];  // new values, two per register
+    const uint64_t flags = cd_pass1<FULL, FROM_F32, W_NEW, W_MASK>(a, wbase, lo, nvp);
 
     const uint32_t wtot = wave_reduce_sum((uint32_t)__builtin_popcountll(flags));
-    if (l == 0) s_wtot[w] = wtot;
+    if (l == 0) sh.wtot[w] = wtot;
     __syncthreads();
     uint32_t tile_count = 0, wpre = 0;
 #pragma unroll
     for (int i = 0; i < CD_THREADS / kWave; ++i) {
-        if (i < w) wpre += s_wtot[i];
-        tile_count += s_wtot[i];
+        if (i < w) wpre += sh.wtot[i];
+        tile_count += sh.wtot[i];
     }
     if (w == 0) {
         bool failed = false;
         const uint64_t pre = lookback_wave(a.status, tile, tag, tile_count, &failed);
         if (l == 0) {
             if (failed) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
-            s_prefix = pre;
-            if (tile == a.ntiles - 1) *a.d_count = (int64_t)(pre + tile_count);
+            sh.prefix = pre;
+            if (tile == a.ntiles - 1) {
+                *a.d_count = (int64_t)(pre + tile_count);
+                ws_epoch_advance(a.hdr, ep);
+            }
             if ((int64_t)(pre + tile_count) > a.cap) or_agent32(a.d_status, 1u /*PULSE_DS_CAPACITY*/);
         }
     }
     __syncthreads();
-    if (tile_count == 0) return;
-    int64_t run = (int64_t)s_prefix + wpre;
+    int64_t run = (int64_t)sh.prefix + wpre;
+    if (tile_count != 0) {
 #pragma unroll
-    for (int g = 0; g < CD_GROUPS; ++g) {
-        const uint32_t f = (uint32_t)(flags >> (4 * g)) & 0xFu;
-        const uint64_t m0 = __ballot(f & 1u), m1 = __ballot(f & 2u), m2 = __ballot(f & 4u), m3 = __ballot(f & 8u);
-        const uint32_t gtot = __builtin_popcountll(m0) + __builtin_popcountll(m1) + __builtin_popcountll(m2) +
-                              __builtin_popcountll(m3);
-        if (gtot == 0) continue;
-        int64_t pos = run + lanes_below(m0) + lanes_below(m1) + lanes_below(m2) + lanes_below(m3);
-        const int64_t e = wbase + g * 256 + 4 * l;
+        for (int g = 0; g < CD_GROUPS; ++g) {
+            const uint32_t f = (uint32_t)(flags >> (4 * g)) & 0xFu;
+            const uint64_t m0 = __ballot(f & 1u), m1 = __ballot(f & 2u), m2 = __ballot(f & 4u), m3 = __ballot(f & 8u);
+            const uint32_t gtot = __builtin_popcountll(m0) + __builtin_popcountll(m1) + __builtin_popcountll(m2) +
+                                  __builtin_popcountll(m3);
+            if (gtot == 0) continue;
+            int64_t pos = run + lanes_below(m0) + lanes_below(m1) + lanes_below(m2) + lanes_below(m3);
+            const int64_t e = wbase + g * 256 + lo;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            if (f & (1u << k)) {
-                if (pos < a.cap) {
-                    a.idx[pos] = (int32_t)(e + k);
-                    a.val[pos] = (uint16_t)(nvp[2 * g + (k >> 1)] >> (16 * (k & 1)));
+            for (int k = 0; k < 4; ++k) {
+                if (f & (1u << k)) {
+                    if (pos < a.cap) {
+                        a.idx[pos] = (int32_t)(e + k);
+                        a.val[pos] = (uint16_t)(nvp[2 * g + (k >> 1)] >> (16 * (k & 1)));
+                    }
+                    ++pos;
                 }
-                ++pos;
             }
+            run += gtot;
         }
-        run += gtot;
     }
+    __syncthreads();  // sh is reused by the next tile
+}
+
+// Persistent: workgroup b places tiles b, b + G, b + 2G, ... in order; the one
+// tile that extends past n (always the last) goes through the checked path.
+template <bool FROM_F32, bool W_NEW, bool W_MASK>
+__global__ __launch_bounds__(CD_THREADS) void k_cast_compact(CastDiffArgs a) {
+    __shared__ uint32_t s_ep;
+    __shared__ CdShared sh;
+    if (threadIdx.x == 0) s_ep = ws_epoch(a.hdr);
+    __syncthreads();
+    const uint32_t ep = s_ep;
+    const uint32_t nfull = (uint32_t)(a.n / CD_TILE);  // tiles entirely inside [0, n)
+    for (uint32_t tile = blockIdx.x; tile < nfull; tile += gridDim.x)
+        cd_tile<true, FROM_F32, W_NEW, W_MASK>(a, tile, ep, sh);
+    if (nfull < a.ntiles && nfull % gridDim.x == blockIdx.x)
+        cd_tile<false, FROM_F32, W_NEW, W_MASK>(a, nfull, ep, sh);
 }
 
 }  // namespace pulse
@@ -249,16 +325,16 @@ extern "C" int pulse_launch_cast_diff(const float *w_new, const uint16_t *b_in, 
     a.status = reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + sizeof(WsHeader));
     const int64_t ntiles = (n + CD_TILE - 1) / CD_TILE;
     a.ntiles = (uint32_t)ntiles;
-    const dim3 g((unsigned)ntiles), b(CD_THREADS);
+    const void *k;
     if (w_new) {
-        if (b_new && mask) k_cast_compact<true, true, true><<<g, b, 0, stream>>>(a);
-        else if (b_new) k_cast_compact<true, true, false><<<g, b, 0, stream>>>(a);
-        else if (mask) k_cast_compact<true, false, true><<<g, b, 0, stream>>>(a);
-        else k_cast_compact<true, false, false><<<g, b, 0, stream>>>(a);
+        if (b_new && mask) k = reinterpret_cast<const void *>(&k_cast_compact<true, true, true>);
+        else if (b_new) k = reinterpret_cast<const void *>(&k_cast_compact<true, true, false>);
+        else if (mask) k = reinterpret_cast<const void *>(&k_cast_compact<true, false, true>);
+        else k = reinterpret_cast<const void *>(&k_cast_compact<true, false, false>);
     } else {
-        k_cast_compact<false, false, false><<<g, b, 0, stream>>>(a);
+        k = reinterpret_cast<const void *>(&k_cast_compact<false, false, false>);
     }
-    return hipGetLastError() == hipSuccess ? 0 : -5;
+    return launch_persistent(k, ntiles, CD_THREADS, 0, a, stream);
 }
 
 extern "C" size_t pulse_cast_diff_ws_bytes(int64_t n) {
