@@ -11,7 +11,8 @@
 // run's sequence depends only on its own (s, e, n), a block is parsed in
 // parallel and the output is bit-for-bit deterministic.
 //
-// One workgroup of 1024 threads (16 waves) per block (dynamic block ids);
+// One workgroup of 1024 threads (16 waves) per block; a persistent grid
+// walks the blocks in a static order (launch.hpp);
 // thread t owns the block bytes [t*CH, (t+1)*CH), CH = block_bytes / 1024 (64
 // for 64 KiB blocks, so a chunk's run boundaries fit one 64-bit mask):
 //  1. coalesced 16-byte loads (the XOR of two sources when given) into a 64 KiB
@@ -29,6 +30,7 @@
 //     (every block of a sparse mask) the bytes go there and are copied out with
 //     16-byte stores, otherwise straight to the payload.
 #include "device.hpp"
+#include "launch.hpp"
 
 namespace pulse {
 
@@ -116,28 +118,26 @@ __device__ __forceinline__ int32_t put_len(const Out &out, int32_t pos, int32_t 
     return pos;
 }
 
-template <int CHLOG>
-__global__ __launch_bounds__(LZE_THREADS) void k_lz4_encode(Lz4EncArgs a) {
-    constexpr int32_t CH = 1 << CHLOG;
-    __shared__ __align__(16) uint8_t s_img[LZE_MAX_BLOCK];
-    __shared__ __align__(16) uint8_t s_win[LZE_WIN + 16];
-    __shared__ int32_t s_i32[LZE_THREADS / kWave];
-    __shared__ uint32_t s_tile, s_tag;
-    __shared__ uint64_t s_off;
+struct EncShared {
+    uint8_t img[LZE_MAX_BLOCK];
+    uint8_t win[LZE_WIN + 16];
+    int32_t i32[LZE_THREADS / kWave];
+    uint64_t off;
+};
 
-    const int t = threadIdx.x;
-    if (t == 0) {
-        uint32_t tile, tag;
-        ws_begin(a.hdr, a.nblocks, &tile, &tag);
-        s_tile = tile;
-        s_tag = tag;
-    }
-    __syncthreads();
-    const uint32_t b = s_tile, tag = s_tag;
-    if (b >= a.nblocks) {  // inconsistent workspace state: touch nothing
-        if (t == 0) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
-        return;
-    }
+// One block (b) of the encode, by the whole workgroup.
+template <int CHLOG>
+__device__ __forceinline__ void enc_block(const Lz4EncArgs &a, uint32_t b, uint32_t ep, EncShared &sh) {
+    constexpr int32_t CH = 1 << CHLOG;
+    uint8_t *const s_img = sh.img;
+    uint8_t *const s_win = sh.win;
+    int32_t *const s_i32 = sh.i32;
+    const uint32_t tag = epoch_tag(ep);
+    // thread index re-materialised per block (an empty asm the compiler cannot
+    // see through): values derived from it are not hoisted out of the block
+    // loop, which would hold them in registers across every block
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
     const int64_t blk_base = (int64_t)b * a.block_bytes;
     const int32_t len = (int32_t)((a.nbytes - blk_base) < a.block_bytes ? (a.nbytes - blk_base) : a.block_bytes);
 
@@ -219,15 +219,18 @@ __global__ __launch_bounds__(LZE_THREADS) void k_lz4_encode(Lz4EncArgs a) {
         const uint64_t off = lookback_wave(a.status, b, tag, comp, &failed);
         if (lane_id() == 0) {
             if (failed) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
-            s_off = off;
+            sh.off = off;
             a.comp_sizes[b] = (uint32_t)comp;
             a.comp_offsets[b] = off;
-            if (b == a.nblocks - 1) *a.d_total = off + comp;
+            if (b == a.nblocks - 1) {
+                *a.d_total = off + comp;
+                ws_epoch_advance(a.hdr, ep);
+            }
             if ((int64_t)(off + comp) > a.cap) or_agent32(a.d_status, 1u /*PULSE_DS_CAPACITY*/);
         }
     }
     __syncthreads();
-    const uint64_t off = s_off;
+    const uint64_t off = sh.off;
     if ((int64_t)(off + comp) > a.cap) return;
     uint8_t *dst = a.payload + off;
     const int32_t shift = (int32_t)((uintptr_t)dst & 15);  // window byte 0 <-> 16-byte aligned address
@@ -280,6 +283,22 @@ __global__ __launch_bounds__(LZE_THREADS) void k_lz4_encode(Lz4EncArgs a) {
     }
 }
 
+// Persistent: workgroup g encodes blocks g, g + G, g + 2G, ... in order (see
+// launch.hpp), so the look-back for a block's payload offset only ever waits
+// on running workgroups, without a per-block atomic ticket.
+template <int CHLOG>
+__global__ __launch_bounds__(LZE_THREADS, 8) void k_lz4_encode(Lz4EncArgs a) {
+    __shared__ __align__(16) EncShared sh;
+    __shared__ uint32_t s_ep;
+    if (threadIdx.x == 0) s_ep = ws_epoch(a.hdr);
+    __syncthreads();
+    const uint32_t ep = s_ep;
+    for (uint32_t b = blockIdx.x; b < a.nblocks; b += gridDim.x) {
+        enc_block<CHLOG>(a, b, ep, sh);
+        __syncthreads();  // the LDS image and window are reused by the next block
+    }
+}
+
 }  // namespace pulse
 
 using namespace pulse;
@@ -308,8 +327,8 @@ extern "C" int pulse_launch_lz4_encode(const void *src, const void *src_xor, int
     a.status = reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + sizeof(WsHeader));
     const int64_t nb = (nbytes + block_bytes - 1) / block_bytes;
     a.nblocks = (uint32_t)nb;
-    if (block_bytes == 65536) k_lz4_encode<6><<<dim3((unsigned)nb), dim3(LZE_THREADS), 0, stream>>>(a);
-    else if (block_bytes == 32768) k_lz4_encode<5><<<dim3((unsigned)nb), dim3(LZE_THREADS), 0, stream>>>(a);
-    else k_lz4_encode<4><<<dim3((unsigned)nb), dim3(LZE_THREADS), 0, stream>>>(a);
-    return hipGetLastError() == hipSuccess ? 0 : -5;
+    const void *k = block_bytes == 65536   ? reinterpret_cast<const void *>(&k_lz4_encode<6>)
+                    : block_bytes == 32768 ? reinterpret_cast<const void *>(&k_lz4_encode<5>)
+                                           : reinterpret_cast<const void *>(&k_lz4_encode<4>);
+    return launch_persistent(k, nb, LZE_THREADS, 0, a, stream);
 }
