@@ -39,9 +39,10 @@ constexpr uint32_t BI_NSEQ = 0x3FFFFFFFu;
 
 // Checkpoints: one per kCkEvery sequences.  A sequence that is not the last
 // one takes >= 3 compressed bytes (token, 2-byte offset), so a block of S
-// bytes holds at most floor(S / 96) + 1 checkpoints; block b's checkpoints
-// start at off_b / 96 + 2 b, which keeps the blocks' regions disjoint.
-constexpr uint32_t kCkEvery = 32;
+// bytes holds at most floor(S / (3 kCkEvery)) + 1 checkpoints; block b's
+// checkpoints start at off_b / (3 kCkEvery) + 2 b, which keeps the blocks'
+// regions disjoint.
+constexpr uint32_t kCkEvery = 16;
 constexpr uint64_t kCkBytes = 3 * kCkEvery;
 
 struct Lz4DecArgs {
@@ -312,66 +313,124 @@ __device__ __forceinline__ bool k2_defer(K2Queue &qu, uint32_t op, uint32_t n, u
     return true;
 }
 
-// Rebuild of one 32-sequence segment (starting at checkpoint c) of a validated
-// canonical block into the zeroed image: literal bytes and the offset-1 fills
-// that repeat a non-zero byte.
+// One sequence of a validated canonical block, byte by byte: literal bytes
+// into the zeroed image, then the offset-1 fill when it repeats a non-zero
+// byte.  Returns false at the final sequence.
+template <typename Src>
+__device__ __forceinline__ bool k2_seq_bytes(Src src, uint32_t S, uint32_t &ip, uint32_t &op, uint8_t *img,
+                                             K2Queue &qu) {
+    const uint32_t tok = src[ip];
+    uint32_t q = ip + 1, ll = tok >> 4;
+    if (ll == 15) {
+        uint32_t x;
+        do {
+            x = src[q++];
+            ll += x;
+        } while (x == 255);
+    }
+    uint32_t last = 0;
+    if (ll > K2_LONG) {
+        last = src[q + ll - 1];
+        if (!k2_defer(qu, op, ll, q))
+            for (uint32_t i = 0; i < ll; ++i) img[op + i] = src[q + i];
+    } else {
+        for (uint32_t i = 0; i < ll; ++i) {
+            last = src[q + i];
+            if (last) img[op + i] = (uint8_t)last;
+        }
+    }
+    q += ll;
+    op += ll;
+    if (q >= S) return false;  // the final sequence
+    q += 2;                    // offset 1
+    uint32_t ml = (tok & 15) + 4;
+    if ((tok & 15) == 15) {
+        uint32_t x;
+        do {
+            x = src[q++];
+            ml += x;
+        } while (x == 255);
+    }
+    if (last) {
+        if (ml <= K2_LONG || !k2_defer(qu, op, ml, K2_FILL | last))
+            for (uint32_t i = 0; i < ml; ++i) img[op + i] = (uint8_t)last;
+    }
+    op += ml;
+    ip = q;
+    return true;
+}
+
+// Rebuild of one kCkEvery-sequence segment (starting at checkpoint c).
 template <typename Src>
 __device__ __forceinline__ void k2_segment(Src src, uint32_t S, uint32_t nseq, uint32_t s, uint2 c, uint8_t *img,
                                            K2Queue &qu) {
     uint32_t ip = c.x, op = c.y;
     const uint32_t rest = nseq - s * kCkEvery;
     const uint32_t kend = rest < kCkEvery ? rest : kCkEvery;
+    for (uint32_t k = 0; k < kend; ++k)
+        if (!k2_seq_bytes(src, S, ip, op, img, qu)) break;
+}
+
+// The same from the LDS stage (the block's bytes start at stage + mis): a
+// sequence with at most 4 literals and at most one match-length byte (almost
+// every sequence of a sparse mask) is decoded from one 8-byte window, three
+// aligned dwords joined by byte-align shifts, so it costs one LDS round trip;
+// any other sequence goes byte by byte.
+__device__ __forceinline__ void k2_segment_lds(const uint8_t *stage, uint32_t mis, uint32_t S, uint32_t nseq,
+                                               uint32_t s, uint2 c, uint8_t *img, K2Queue &qu) {
+    const uint8_t *src = stage + mis;
+    uint32_t ip = c.x, op = c.y;
+    const uint32_t rest = nseq - s * kCkEvery;
+    const uint32_t kend = rest < kCkEvery ? rest : kCkEvery;
     for (uint32_t k = 0; k < kend; ++k) {
-        const uint32_t tok = src[ip];
-        uint32_t q = ip + 1, ll = tok >> 4;
-        if (ll == 15) {
-            uint32_t x;
-            do {
-                x = src[q++];
-                ll += x;
-            } while (x == 255);
-        }
-        uint32_t last = 0;
-        if (ll > K2_LONG) {
-            last = src[q + ll - 1];
-            if (!k2_defer(qu, op, ll, q))
-                for (uint32_t i = 0; i < ll; ++i) img[op + i] = src[q + i];
-        } else {
-            for (uint32_t i = 0; i < ll; ++i) {
-                last = src[q + i];
-                if (last) img[op + i] = (uint8_t)last;
+        const uint32_t P = mis + ip;
+        const uint32_t *d = reinterpret_cast<const uint32_t *>(stage + (P & ~3u));
+        const uint32_t d0 = d[0], d1 = d[1], d2 = d[2];  // (past the block: stage padding, unused)
+        const uint32_t w0 = __builtin_amdgcn_alignbyte(d1, d0, P & 3u);
+        const uint32_t w1 = __builtin_amdgcn_alignbyte(d2, d1, P & 3u);
+        const uint64_t u = ((uint64_t)w1 << 32) | w0;  // bytes ip .. ip+7
+        const uint32_t ll = (w0 >> 4) & 15u, mc = w0 & 15u;
+        const uint32_t x = (uint32_t)(u >> (8 * (ll <= 4 ? 3 + ll : 7u))) & 0xFFu;  // byte 3 + ll when ll <= 4
+        const bool fast = ll <= 4 && ip + 1 + ll < S && !(mc == 15 && x == 255);
+        if (fast) {
+            uint32_t last = 0;
+#pragma unroll
+            for (uint32_t i = 0; i < 4; ++i) {
+                if (i < ll) {
+                    last = (uint32_t)(u >> (8 * (i + 1))) & 0xFFu;
+                    if (last) img[op + i] = (uint8_t)last;
+                }
             }
+            const uint32_t ml = mc + 4 + (mc == 15 ? x : 0u);
+            op += ll;
+            if (last) {
+                if (ml <= K2_LONG || !k2_defer(qu, op, ml, K2_FILL | last))
+                    for (uint32_t i = 0; i < ml; ++i) img[op + i] = (uint8_t)last;
+            }
+            op += ml;
+            ip += 3 + ll + (mc == 15 ? 1u : 0u);
+        } else if (!k2_seq_bytes(src, S, ip, op, img, qu)) {
+            break;
         }
-        q += ll;
-        op += ll;
-        if (q >= S) break;  // the final sequence
-        q += 2;             // offset 1
-        uint32_t ml = (tok & 15) + 4;
-        if ((tok & 15) == 15) {
-            uint32_t x;
-            do {
-                x = src[q++];
-                ml += x;
-            } while (x == 255);
-        }
-        if (last) {
-            if (ml <= K2_LONG || !k2_defer(qu, op, ml, K2_FILL | last))
-                for (uint32_t i = 0; i < ml; ++i) img[op + i] = (uint8_t)last;
-        }
-        op += ml;
-        ip = q;
     }
 }
 
 // Thread t rebuilds segments t, t + 256, ...; the first from the checkpoint c0
 // loaded early (no loop around it, so nothing waits for the dst loads).
-template <typename Src>
-__device__ __forceinline__ void k2_segments(Src src, uint32_t S, uint32_t nseq, const uint2 *ck, uint2 c0,
-                                            uint8_t *img, K2Queue &qu) {
+// STAGED: src is the LDS stage (the block's bytes at src + mis).
+template <bool STAGED, typename Src>
+__device__ __forceinline__ void k2_segments(Src src, uint32_t mis, uint32_t S, uint32_t nseq, const uint2 *ck,
+                                            uint2 c0, uint8_t *img, K2Queue &qu) {
     const uint32_t nseg = (nseq + kCkEvery - 1) / kCkEvery;
     const uint32_t t = threadIdx.x;
-    if (t < nseg) k2_segment(src, S, nseq, t, c0, img, qu);
-    for (uint32_t s = t + K2_THREADS; s < nseg; s += K2_THREADS) k2_segment(src, S, nseq, s, ck[s], img, qu);
+    if constexpr (STAGED) {
+        if (t < nseg) k2_segment_lds(src, mis, S, nseq, t, c0, img, qu);
+        for (uint32_t s = t + K2_THREADS; s < nseg; s += K2_THREADS)
+            k2_segment_lds(src, mis, S, nseq, s, ck[s], img, qu);
+    } else {
+        if (t < nseg) k2_segment(src, S, nseq, t, c0, img, qu);
+        for (uint32_t s = t + K2_THREADS; s < nseg; s += K2_THREADS) k2_segment(src, S, nseq, s, ck[s], img, qu);
+    }
 }
 
 template <typename Src>
@@ -448,12 +507,11 @@ __device__ __forceinline__ void k2_block(const Lz4DecArgs &a, int64_t b, uint32_
     lds_barrier();
 
     if constexpr (STAGED) {
-        const uint8_t *src = s_stage + mis;
-        k2_segments(src, S, nseq, ck, c0, s_img, s_q);
+        k2_segments<true>(static_cast<const uint8_t *>(s_stage), mis, S, nseq, ck, c0, s_img, s_q);
         lds_barrier();
-        k2_deferred(src, s_img, s_q);
+        k2_deferred(static_cast<const uint8_t *>(s_stage + mis), s_img, s_q);
     } else {
-        k2_segments(in, S, nseq, ck, c0, s_img, s_q);
+        k2_segments<false>(in, 0u, S, nseq, ck, c0, s_img, s_q);
         lds_barrier();
         k2_deferred(in, s_img, s_q);
     }
@@ -484,7 +542,7 @@ __device__ __forceinline__ void k2_block(const Lz4DecArgs &a, int64_t b, uint32_
 template <int IMG, bool XOR>
 __global__ __launch_bounds__(K2_THREADS) void k_lz4_fast(Lz4DecArgs a) {
     __shared__ __align__(16) uint8_t s_img[IMG];
-    __shared__ __align__(16) uint8_t s_stage[K2_STAGE];
+    __shared__ __align__(16) uint8_t s_stage[K2_STAGE + 16];  // (+16: the 8-byte windows may read past the data)
     __shared__ K2Queue s_q;
     const int64_t b = blockIdx.x;
     const uint32_t info = a.binfo[b];
