@@ -371,18 +371,20 @@ __device__ __forceinline__ void k2_segment(Src src, uint32_t S, uint32_t nseq, u
         if (!k2_seq_bytes(src, S, ip, op, img, qu)) break;
 }
 
-// The same from the LDS stage (the block's bytes start at stage + mis): a
-// sequence with at most 4 literals and at most one match-length byte (almost
-// every sequence of a sparse mask) is decoded from one 8-byte window, three
-// aligned dwords joined by byte-align shifts, so it costs one LDS round trip;
-// any other sequence goes byte by byte.
+// The same from the LDS stage (the block's bytes start at stage + mis).  The
+// common sequence of a sparse mask -- 1 to 4 literals ending in a zero byte
+// (the first byte of the zero run the match repeats, so no fill), offset 1, at
+// most one match-length byte -- is decoded from one 8-byte window (three
+// aligned dwords joined by byte-align shifts): one LDS round trip and no
+// branches.  The first sequence of another shape ends the fast loop and the
+// rest of the segment goes byte by byte.
 __device__ __forceinline__ void k2_segment_lds(const uint8_t *stage, uint32_t mis, uint32_t S, uint32_t nseq,
                                                uint32_t s, uint2 c, uint8_t *img, K2Queue &qu) {
-    const uint8_t *src = stage + mis;
     uint32_t ip = c.x, op = c.y;
     const uint32_t rest = nseq - s * kCkEvery;
     const uint32_t kend = rest < kCkEvery ? rest : kCkEvery;
-    for (uint32_t k = 0; k < kend; ++k) {
+    uint32_t k = 0;
+    for (; k < kend; ++k) {
         const uint32_t P = mis + ip;
         const uint32_t *d = reinterpret_cast<const uint32_t *>(stage + (P & ~3u));
         const uint32_t d0 = d[0], d1 = d[1], d2 = d[2];  // (past the block: stage padding, unused)
@@ -390,29 +392,25 @@ __device__ __forceinline__ void k2_segment_lds(const uint8_t *stage, uint32_t mi
         const uint32_t w1 = __builtin_amdgcn_alignbyte(d2, d1, P & 3u);
         const uint64_t u = ((uint64_t)w1 << 32) | w0;  // bytes ip .. ip+7
         const uint32_t ll = (w0 >> 4) & 15u, mc = w0 & 15u;
-        const uint32_t x = (uint32_t)(u >> (8 * (ll <= 4 ? 3 + ll : 7u))) & 0xFFu;  // byte 3 + ll when ll <= 4
-        const bool fast = ll <= 4 && ip + 1 + ll < S && !(mc == 15 && x == 255);
-        if (fast) {
-            uint32_t last = 0;
-#pragma unroll
-            for (uint32_t i = 0; i < 4; ++i) {
-                if (i < ll) {
-                    last = (uint32_t)(u >> (8 * (i + 1))) & 0xFFu;
-                    if (last) img[op + i] = (uint8_t)last;
-                }
-            }
-            const uint32_t ml = mc + 4 + (mc == 15 ? x : 0u);
-            op += ll;
-            if (last) {
-                if (ml <= K2_LONG || !k2_defer(qu, op, ml, K2_FILL | last))
-                    for (uint32_t i = 0; i < ml; ++i) img[op + i] = (uint8_t)last;
-            }
-            op += ml;
-            ip += 3 + ll + (mc == 15 ? 1u : 0u);
-        } else if (!k2_seq_bytes(src, S, ip, op, img, qu)) {
-            break;
-        }
+        const uint32_t lsh = ll <= 4 ? ll : 4u;
+        const uint32_t lastb = (uint32_t)(u >> (8 * lsh)) & 0xFFu;     // literal byte ll
+        const uint32_t x = (uint32_t)(u >> (8 * (3 + lsh))) & 0xFFu;   // byte 3 + ll
+        // (bitwise, not short-circuit: one branch)
+        const uint32_t fast = (uint32_t)(ll - 1u < 4u) & (uint32_t)(lastb == 0) & (uint32_t)(ip + 1 + ll < S) &
+                              (uint32_t)((mc != 15) | (x != 255));
+        if (!fast) break;
+        // literal bytes 1 .. ll-1 (byte ll is zero and the image is zeroed)
+        const uint32_t b1 = (w0 >> 8) & 0xFFu, b2 = (w0 >> 16) & 0xFFu, b3 = w0 >> 24;
+        if (ll > 1 && b1) img[op] = (uint8_t)b1;
+        if (ll > 2 && b2) img[op + 1] = (uint8_t)b2;
+        if (ll > 3 && b3) img[op + 2] = (uint8_t)b3;
+        const uint32_t ext = mc == 15 ? 1u : 0u;
+        op += ll + mc + 4 + (ext ? x : 0u);
+        ip += 3 + ll + ext;
     }
+    const uint8_t *src = stage + mis;
+    for (; k < kend; ++k)
+        if (!k2_seq_bytes(src, S, ip, op, img, qu)) break;
 }
 
 // Thread t rebuilds segments t, t + 256, ...; the first from the checkpoint c0
