@@ -208,10 +208,31 @@ __device__ __forceinline__ uint64_t cd_pass1(const CastDiffArgs &a, int64_t wbas
     return flags;
 }
 
+constexpr int CD_SB = 512;  // patch entries staged per wave before a coalesced flush
+
 struct CdShared {
     uint32_t wtot[CD_THREADS / kWave];
     uint64_t prefix;
+    int32_t sbi[CD_THREADS / kWave][CD_SB];
+    uint16_t sbv[CD_THREADS / kWave][CD_SB];
 };
+
+// Writes the wave's staged entries [0, nb) to the patch at out (lanes write
+// consecutive entries: full-width stores) and empties the buffer.
+__device__ __forceinline__ void cd_flush(const CastDiffArgs &a, const int32_t *sbi, const uint16_t *sbv, uint32_t &nb,
+                                         int64_t &out) {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // the lanes' staged entries are visible to the wave
+    for (uint32_t i = lane_id(); i < nb; i += kWave) {
+        const int64_t pos = out + i;
+        if (pos < a.cap) {
+            a.idx[pos] = sbi[i];
+            a.val[pos] = sbv[i];
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // reads done before the buffer is refilled
+    out += nb;
+    nb = 0;
+}
 
 // One tile: pass 1, the tile total, its look-back, pass 2 (ranked stores).
 template <bool FULL, bool FROM_F32, bool W_NEW, bool W_MASK>
@@ -248,6 +269,12 @@ __device__ __forceinline__ void cd_tile(const CastDiffArgs &a, uint32_t tile, ui
     __syncthreads();
     int64_t run = (int64_t)sh.prefix + wpre;
     if (tile_count != 0) {
+        // pass 2: each changed element is ranked with ballots and staged in the
+        // wave's LDS buffer at its rank; the buffer goes out with coalesced
+        // stores (the wave's entries are one contiguous stretch of the patch)
+        int32_t *sbi = sh.sbi[w];
+        uint16_t *sbv = sh.sbv[w];
+        uint32_t nb = 0;
 #pragma unroll
         for (int g = 0; g < CD_GROUPS; ++g) {
             const uint32_t f = (uint32_t)(flags >> (4 * g)) & 0xFu;
@@ -255,20 +282,20 @@ __device__ __forceinline__ void cd_tile(const CastDiffArgs &a, uint32_t tile, ui
             const uint32_t gtot = __builtin_popcountll(m0) + __builtin_popcountll(m1) + __builtin_popcountll(m2) +
                                   __builtin_popcountll(m3);
             if (gtot == 0) continue;
-            int64_t pos = run + lanes_below(m0) + lanes_below(m1) + lanes_below(m2) + lanes_below(m3);
-            const int64_t e = wbase + g * 256 + lo;
+            if (nb + gtot > (uint32_t)CD_SB) cd_flush(a, sbi, sbv, nb, run);
+            uint32_t r = nb + lanes_below(m0) + lanes_below(m1) + lanes_below(m2) + lanes_below(m3);
+            const int32_t e = (int32_t)(wbase + g * 256 + lo);
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 if (f & (1u << k)) {
-                    if (pos < a.cap) {
-                        a.idx[pos] = (int32_t)(e + k);
-                        a.val[pos] = (uint16_t)(nvp[2 * g + (k >> 1)] >> (16 * (k & 1)));
-                    }
-                    ++pos;
+                    sbi[r] = e + k;
+                    sbv[r] = (uint16_t)(nvp[2 * g + (k >> 1)] >> (16 * (k & 1)));
+                    ++r;
                 }
             }
-            run += gtot;
+            nb += gtot;
         }
+        if (nb) cd_flush(a, sbi, sbv, nb, run);
     }
     __syncthreads();  // sh is reused by the next tile
 }
