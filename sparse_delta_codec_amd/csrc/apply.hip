@@ -3,9 +3,9 @@
 // Scatter: the receiver overrides the listed positions with the replacement
 // bits; no floating-point addition, so no drift ("Taking Reinforcement Learning
 // Cross Datacenter", Nan Jiang talk, 11:08-11:30; PULSE technical summary,
-// "1. PULSESync", Ricostruzione).  Entries are read coalesced, four per lane
-// (int4 + ushort4 when the arrays allow it); because indices ascend, the 2-byte
-// stores of a wave land in a few neighbouring cache lines.
+// "1. PULSESync", Ricostruzione).  Entries are read coalesced; because indices
+// ascend, the 2-byte stores of one instruction land in a few neighbouring
+// cache lines.
 //
 // XOR: dst ^= mask with 16-byte loads/stores ("GPU weight teleportation"
 // write-up, "XOR masks").
@@ -13,34 +13,33 @@
 
 namespace pulse {
 
+// Lanes take consecutive entries (entry = base + q*64 + lane for q < 4), so
+// one store instruction writes 64 consecutive entries of the ascending patch:
+// a few neighbouring cache lines per instruction instead of one line per lane.
 __global__ __launch_bounds__(256) void k_apply_patch(uint16_t *__restrict__ b, int64_t n,
                                                      const int32_t *__restrict__ idx,
                                                      const uint16_t *__restrict__ val,
                                                      const int64_t *__restrict__ d_count,
-                                                     int64_t max_count, uint32_t *d_status,
-                                                     bool vec) {
+                                                     int64_t max_count, uint32_t *d_status) {
     int64_t count = *d_count;
     if (count > max_count) count = max_count;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
+    const int64_t per_wave = 4 * kWave;
+    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
     bool bad = false;
-    for (int64_t k = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; k < count; k += stride) {
+    for (int64_t wb = ((int64_t)blockIdx.x * (blockDim.x / kWave) + wave_id()) * per_wave; wb < count;
+         wb += nwaves * per_wave) {
         int32_t ii[4];
         uint16_t vv[4];
-        if (vec && k + 3 < count) {
-            const int4 i4 = *reinterpret_cast<const int4 *>(idx + k);
-            const ushort4 v4 = *reinterpret_cast<const ushort4 *>(val + k);
-            ii[0] = i4.x; ii[1] = i4.y; ii[2] = i4.z; ii[3] = i4.w;
-            vv[0] = v4.x; vv[1] = v4.y; vv[2] = v4.z; vv[3] = v4.w;
-        } else {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                ii[q] = (k + q < count) ? idx[k + q] : -1;
-                vv[q] = (k + q < count) ? val[k + q] : 0;
-            }
+        for (int q = 0; q < 4; ++q) {
+            const int64_t k = wb + q * kWave + lane_id();
+            ii[q] = k < count ? idx[k] : -1;
+            vv[q] = k < count ? val[k] : 0;
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            if (k + q >= count) break;
+            const int64_t k = wb + q * kWave + lane_id();
+            if (k >= count) break;
             const int64_t i = ii[q];
             if (i >= 0 && i < n) b[i] = vv[q];
             else bad = true;
@@ -78,9 +77,7 @@ extern "C" int pulse_launch_apply_patch(uint16_t *b, int64_t n, const int32_t *i
     int64_t blocks = (max_count + 1023) / 1024;
     if (blocks > 256 * 32) blocks = 256 * 32;
     if (blocks < 1) blocks = 1;
-    const bool vec = ((uintptr_t)idx % 16 == 0) && ((uintptr_t)val % 8 == 0);
-    k_apply_patch<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(b, n, idx, val, d_count, max_count,
-                                                                   d_status, vec);
+    k_apply_patch<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(b, n, idx, val, d_count, max_count, d_status);
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
