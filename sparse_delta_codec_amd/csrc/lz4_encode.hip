@@ -80,42 +80,84 @@ __device__ __forceinline__ int32_t img_addr(int32_t p) {
     return (c << CHLOG) + ((k ^ sw) << 4) + (p & 15);
 }
 
-// Calls f(s, e) for every run starting in this thread's chunk, in order: a run
-// is complete when the next boundary is found (or, for the last one, at
-// next_after, the first boundary after the chunk).
-template <class F>
-__device__ __forceinline__ void for_each_run(uint64_t m, int32_t cs, int32_t next_after, F f) {
-    if (!m) return;
-    int32_t prev = cs + __builtin_ctzll(m);
-    m &= m - 1;
-    while (m) {
-        const int32_t pos = cs + __builtin_ctzll(m);
-        m &= m - 1;
-        f(prev, pos);
-        prev = pos;
+// Starts (chunk bit u = position cs + u) of the runs that become sequences:
+// no run boundary among the next four positions (the run is >= 5 bytes, so
+// j - i >= 4) and s <= len - 13 (so i <= len - 12; the end-of-block clamp
+// j = min(e, len - 5) then never shortens the match below 4).  hi: boundary
+// bits of the positions just past the chunk (only next_after can be one).
+template <int CH>
+__device__ __forceinline__ uint64_t qualifying_starts(uint64_t m, uint64_t hi, int32_t cs, int32_t len) {
+    uint64_t y;
+    if constexpr (CH == 64) {
+        y = (m >> 1) | (m >> 2) | (m >> 3) | (m >> 4) | (hi << 63) | (hi << 62) | (hi << 61) | (hi << 60);
+    } else {
+        const uint64_t M = m | (hi << CH);
+        y = (M >> 1) | (M >> 2) | (M >> 3) | (M >> 4);
     }
-    f(prev, next_after);
+    uint64_t q = m & ~y;
+    const int32_t lim = len - 13 - cs;  // largest qualifying bit
+    if (lim < 0) q = 0;
+    else if (lim < 63) q &= (2ull << lim) - 1;
+    return q;
 }
 
-// destination of the emitted bytes: the LDS window (offset by the payload's
-// misalignment) or the payload itself; never writes past the block's size
-struct Out {
-    uint8_t *p;
-    int32_t lim;
-    __device__ __forceinline__ void put(int32_t pos, uint32_t v) const {
-        if (pos >= 0 && pos < lim) p[pos] = (uint8_t)v;
-    }
-};
+// End of the run starting at chunk bit u: the next boundary in the chunk, or
+// the first one after it.
+__device__ __forceinline__ int32_t run_end(uint64_t m, int u, int32_t cs, int32_t next_after) {
+    const uint64_t after = u >= 63 ? 0ull : (m >> (u + 1));
+    return after ? cs + u + 1 + (int32_t)__builtin_ctzll(after) : next_after;
+}
 
-__device__ __forceinline__ int32_t put_len(const Out &out, int32_t pos, int32_t v) {
-    // extra length bytes of a nibble capped at 15: 255s then a byte < 255
+// extra length bytes of a nibble capped at 15: 255s then a byte < 255
+template <typename P>
+__device__ __forceinline__ int32_t put_len(P out, int32_t pos, int32_t v) {
     int32_t rem = v - 15;
     while (rem >= 255) {
-        out.put(pos++, 255);
+        out[pos++] = 255;
         rem -= 255;
     }
-    out.put(pos++, (uint32_t)rem);
+    out[pos++] = (uint8_t)rem;
     return pos;
+}
+
+// Emission of one thread's sequences and literal bytes into out (the LDS
+// window or the payload; every position written is < the block's encoded
+// size by construction).  Literal bytes come from the thread's own chunk of
+// the swizzled image: piece k of chunk c sits at slot k ^ sw.
+template <int CHLOG, typename P>
+__device__ __forceinline__ void emit_chunk(P out, const uint8_t *s_img, uint64_t Q, uint64_t m, int32_t cs,
+                                           int32_t chunk_end, int32_t next_after, int32_t len, int32_t carry_j,
+                                           int32_t pos0, int32_t next_qi, int32_t sw) {
+    auto lit = [&](int32_t p) -> uint32_t {
+        const int32_t o = p - cs;
+        return s_img[cs + ((((o >> 4) ^ sw)) << 4) + (o & 15)];
+    };
+    int32_t la = carry_j, pos = pos0;
+    while (Q) {
+        const int u = __builtin_ctzll(Q);
+        Q &= Q - 1;
+        const int32_t s = cs + u, e = run_end(m, u, cs, next_after);
+        const int32_t i = s + 1, j = e < len - 5 ? e : len - 5;
+        const int32_t ll = i - la, ml = j - i;
+        const int32_t h = 1 + ext_bytes(ll);
+        out[pos] = (uint8_t)(((ll >= 15 ? 15 : ll) << 4) | (ml - 4 >= 15 ? 15 : ml - 4));
+        if (ll >= 15) put_len(out, pos + 1, ll);
+        const int32_t base = pos + h - la;
+        for (int32_t p = (la > cs ? la : cs); p < i; ++p) out[base + p] = (uint8_t)lit(p);
+        int32_t q = pos + h + ll;
+        out[q++] = 1;
+        out[q++] = 0;
+        if (ml - 4 >= 15) q = put_len(out, q, ml - 4);
+        pos = q;
+        la = j;
+    }
+    // literals of this chunk that belong to the next sequence after it
+    const int32_t lo = la > cs ? la : cs;
+    if (lo < chunk_end) {
+        const int32_t ll = (next_qi != LZE_INF ? next_qi : len) - la;
+        const int32_t base = pos + 1 + ext_bytes(ll) - la;
+        for (int32_t p = lo; p < chunk_end; ++p) out[base + p] = (uint8_t)lit(p);
+    }
 }
 
 struct EncShared {
@@ -189,21 +231,29 @@ __device__ __forceinline__ void enc_block(const Lz4EncArgs &a, uint32_t b, uint3
     const int32_t first_b = m ? cs + __builtin_ctzll(m) : len;
     const int32_t next_after = block_excl_min_rev<LZE_THREADS / kWave>(first_b, len, s_i32);
 
-    // 3. one pass over the runs: first qualifying run (i1, its match length),
-    //    last qualifying j, and the bytes of the sequences after the first
+    // 3. the runs that become sequences (bit-parallel), then one pass over
+    //    them: first one (i1, its match length), last j, and the bytes of the
+    //    sequences after the first
+    uint64_t hi = 0;
+    {
+        const int32_t d = next_after - (cs + CH);
+        if (next_after < len && d >= 0 && d < 4) hi = 1ull << d;
+    }
+    const uint64_t Q = cl > 0 ? qualifying_starts<CH>(m, hi, cs, len) : 0ull;
     int32_t first_qi = LZE_INF, first_ml = 0, last_qj = 0, rest = 0;
-    for_each_run(m, cs, next_after, [&](int32_t s, int32_t e) {
-        const int32_t i = s + 1, j = e < len - 5 ? e : len - 5;
-        if (j - i >= 4 && i <= len - 12) {
-            if (first_qi == LZE_INF) {
-                first_qi = i;
-                first_ml = j - i;
-            } else {
-                rest += seq_bytes(i - last_qj, j - i);
-            }
-            last_qj = j;
+    for (uint64_t q = Q; q;) {
+        const int u = __builtin_ctzll(q);
+        q &= q - 1;
+        const int32_t e = run_end(m, u, cs, next_after);
+        const int32_t i = cs + u + 1, j = e < len - 5 ? e : len - 5;
+        if (first_qi == LZE_INF) {
+            first_qi = i;
+            first_ml = j - i;
+        } else {
+            rest += seq_bytes(i - last_qj, j - i);
         }
-    });
+        last_qj = j;
+    }
     int32_t a_final;
     const int32_t carry_j = block_excl_max<LZE_THREADS / kWave>(last_qj, 0, s_i32, &a_final);
     const int32_t next_qi = block_excl_min_rev<LZE_THREADS / kWave>(first_qi, LZE_INF, s_i32);
@@ -235,38 +285,14 @@ __device__ __forceinline__ void enc_block(const Lz4EncArgs &a, uint32_t b, uint3
     uint8_t *dst = a.payload + off;
     const int32_t shift = (int32_t)((uintptr_t)dst & 15);  // window byte 0 <-> 16-byte aligned address
     const bool staged = (int32_t)comp + shift <= LZE_WIN + 16;
-    const Out out{staged ? s_win + shift : dst, (int32_t)comp};
 
     // 5. emit
-    int32_t la = carry_j, pos = pos0;
-    const int32_t chunk_end = cs + cl;
-    for_each_run(m, cs, next_after, [&](int32_t s, int32_t e) {
-        const int32_t i = s + 1, j = e < len - 5 ? e : len - 5;
-        if (!(j - i >= 4 && i <= len - 12)) return;
-        const int32_t ll = i - la, ml = j - i;
-        const int32_t h = 1 + ext_bytes(ll);
-        out.put(pos, ((ll >= 15 ? 15 : ll) << 4) | (ml - 4 >= 15 ? 15 : ml - 4));
-        if (ll >= 15) put_len(out, pos + 1, ll);
-        for (int32_t p = (la > cs ? la : cs); p < i; ++p) out.put(pos + h + (p - la), s_img[img_addr<CHLOG>(p)]);
-        int32_t q = pos + h + ll;
-        out.put(q++, 1);
-        out.put(q++, 0);
-        if (ml - 4 >= 15) q = put_len(out, q, ml - 4);
-        pos = q;
-        la = j;
-    });
-    {
-        // literals of this chunk that belong to the next sequence after it
-        const int32_t lo = la > cs ? la : cs;
-        if (lo < chunk_end) {
-            const int32_t ll = (next_qi != LZE_INF ? next_qi : len) - la;
-            const int32_t h = 1 + ext_bytes(ll);
-            for (int32_t p = lo; p < chunk_end; ++p) out.put(pos + h + (p - la), s_img[img_addr<CHLOG>(p)]);
-        }
-    }
+    const int32_t sw = (t >> (4 - (CHLOG - 4))) & ((1 << (CHLOG - 4)) - 1);
+    uint8_t *const outp = staged ? s_win + shift : dst;
+    emit_chunk<CHLOG>(outp, s_img, Q, m, cs, cs + cl, next_after, len, carry_j, pos0, next_qi, sw);
     if (t == 0) {
-        out.put(qsum, (ll_final >= 15 ? 15 : ll_final) << 4);
-        if (ll_final >= 15) put_len(out, qsum + 1, ll_final);
+        outp[qsum] = (uint8_t)((ll_final >= 15 ? 15 : ll_final) << 4);
+        if (ll_final >= 15) put_len(outp, qsum + 1, ll_final);
     }
     if (!staged) return;
     __syncthreads();
