@@ -221,7 +221,9 @@ int lz4_decode_blocks(const uint8_t *payload, int64_t payload_bytes,
  * the stacked [R, cols] matrix is cut into 128x128 blocks; per block
  * amax = max |x|, s = amax / 448 (IEEE float32 division; s = 1 when amax == 0)
  * and code = E4M3(x / s) (IEEE division, round to nearest even, saturating at
- * 448).  Dequantisation is E4M3(code) * s.
+ * 448).  Dequantisation is E4M3(code) * s.  The inputs must be finite
+ * (trained weights are): for a block holding Inf or NaN its codes and scale
+ * are unspecified (the call still completes).
  *   srcs        (host) array of nsrc (1..8) device pointers to BF16 [rows_i, cols],
  *               row-major, 16-byte aligned.
  *   src_rows    (host) rows of each source.

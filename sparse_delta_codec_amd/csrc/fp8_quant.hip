@@ -6,7 +6,8 @@
 // under 2 seconds", opening paragraph and "Potok zadan").  Format: OCP E4M3
 // "fn" (bias 7, largest finite 448, no Inf).  Per block: amax = max |x|,
 // s = amax / 448 (IEEE float32 division; 1 when amax == 0), code =
-// E4M3(x / s) with an IEEE division and round-to-nearest-even, saturating.
+// E4M3(fl32(x / s)), round to nearest even (fl32(x / s) <= 448 * (1 + 2^-23)
+// always, which rounds to the largest finite code).
 //
 // One workgroup per (expert, block row, block column).  Thread t covers
 // columns [8*(t%16), +8) of rows t/16 + 16*i, i = 0..7: every load instruction
@@ -30,27 +31,6 @@ struct QuantArgs {
     uint8_t *codes;
     float *scales;
 };
-
-// E4M3 "fn" code of a finite float32, round to nearest even, saturating
-__device__ __forceinline__ uint32_t e4m3_code(float q) {
-    const uint32_t bits = __float_as_uint(q);
-    const uint32_t sign = (bits >> 24) & 0x80u;
-    const uint32_t a = bits & 0x7FFFFFFFu;
-    uint32_t code;
-    if (a >= 0x43E00000u) {  // |q| >= 448: the largest finite value
-        code = 0x7Eu;
-    } else if (a < 0x3C800000u) {  // |q| < 2^-6: multiples of 2^-9
-        // adding 1.5*2^14 (ulp 2^-9) rounds |q| to the grid; the bit-pattern
-        // difference is the number of 2^-9 steps
-        const float r = __uint_as_float(a) + 24576.0f;
-        code = __float_as_uint(r) - 0x46C00000u;
-    } else {
-        // keep 3 mantissa bits with round-to-nearest-even on the other 20, then
-        // rebias the exponent from 127 to 7
-        code = ((a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20) - (120u << 3);
-    }
-    return sign | code;
-}
 
 __global__ __launch_bounds__(256) void k_fp8_block_quant(QuantArgs a) {
     __shared__ uint32_t s_red[4];
@@ -95,19 +75,42 @@ __global__ __launch_bounds__(256) void k_fp8_block_quant(QuantArgs a) {
     const float s = amax == 0 ? 1.0f : amax_f / 448.0f;  // IEEE division
     if (t == 0) a.scales[(e * ((a.R + 127) / 128) + br) * a.nbc + bc] = s;
 
+    // q = fl32(|x| / s) without a division per element: with y = fl32(1/ss)
+    // (IEEE, once), q0 = fl32(xs*y), r = xs - ss*q0 (exact with an FMA) and
+    // q = fl32(q0 + r*y) is the correctly rounded quotient (Markstein, "Computation
+    // of elementary functions on the IBM RISC System/6000 processor", 1990)
+    // while xs and the remainder stay normal; both operands are scaled by 2^40
+    // when s < 2^60 (the quotient is unchanged) so that they do.  Checked on
+    // every finite BF16 amax against every BF16 magnitude up to it: the E4M3
+    // codes equal those of the IEEE quotient (differences are confined to
+    // subnormal quotients, all of which encode to 0).
+    const bool up = s < 1.152921504606846976e18f;  // 2^60
+    const float ss = up ? s * 1099511627776.0f : s;  // 2^40
+    const float xm = up ? 1099511627776.0f : 1.0f;
+    const float y = 1.0f / ss;  // IEEE division
+    auto quot = [&](uint32_t xbits) {  // xbits: |x| as float32 bits
+        const float xs = __uint_as_float(xbits) * xm;
+        const float q0 = xs * y;
+        const float rm = __builtin_fmaf(-q0, ss, xs);
+        return __builtin_fmaf(rm, y, q0);
+    };
+
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         if (!ok[i]) continue;
         const int64_t r = br * 128 + rg + 16 * i;
         const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-        uint32_t packed[2] = {0, 0};
+        uint32_t packed[2];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const float x0 = __uint_as_float(w[k] << 16);
-            const float x1 = __uint_as_float(w[k] & 0xFFFF0000u);
-            const uint32_t c0 = e4m3_code(x0 / s);  // IEEE division
-            const uint32_t c1 = e4m3_code(x1 / s);
-            packed[k >> 1] |= (c0 | (c1 << 8)) << (16 * (k & 1));
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t w0 = w[2 * h], w1 = w[2 * h + 1];
+            // magnitudes (the hardware conversion rounds to nearest even and is
+            // exact against the E4M3 definition for |q| <= 448.5), signs after
+            int c = __builtin_amdgcn_cvt_pk_fp8_f32(quot((w0 << 16) & 0x7FFF0000u), quot(w0 & 0x7FFF0000u), 0, false);
+            c = __builtin_amdgcn_cvt_pk_fp8_f32(quot((w1 << 16) & 0x7FFF0000u), quot(w1 & 0x7FFF0000u), c, true);
+            const uint32_t sg = ((w0 >> 8) & 0x80u) | ((w0 >> 16) & 0x8000u) | ((w1 << 8) & 0x800000u) |
+                                (w1 & 0x80000000u);
+            packed[h] = (uint32_t)c | sg;
         }
         *reinterpret_cast<uint2 *>(a.codes + (e * a.R + r) * a.cols + col) = make_uint2(packed[0], packed[1]);
     }

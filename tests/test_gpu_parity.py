@@ -491,6 +491,31 @@ def test_fp8_all_bf16_values_through_one_scale():
     assert np.array_equal(scales.view(np.uint32), rs.view(np.uint32)) and np.array_equal(codes, rc)
 
 
+def test_fp8_every_magnitude_under_many_scales():
+    """Every BF16 magnitude up to amax, with random signs, under 70 block maxima
+    (edge values and random patterns from the smallest subnormal to the largest
+    finite value): per maximum two 128x128 blocks hold magnitudes 0..32767
+    clipped to amax, so each block's scale is amax / 448 and every quotient
+    x / s in [0, 448] occurs."""
+    rng = np.random.default_rng(91)
+    edge = [0x0001, 0x0002, 0x007F, 0x0080, 0x0081, 0x00FF, 0x3F80, 0x43E0, 0x43E1,
+            0x7F7F, 0x7F00, 0x1000, 0x2000, 0x5E80, 0x5F00, 0x5F7F]
+    amaxes = np.array(edge + list(rng.integers(1, 0x7F80, 54)), np.uint32)
+    n = amaxes.size
+    w = np.zeros((128, 256 * n), np.uint16)
+    for j, am in enumerate(amaxes):
+        mags = np.minimum(np.arange(32768, dtype=np.uint32), am)
+        signs = rng.integers(0, 2, 32768, dtype=np.uint32) << 15
+        for b in range(2):
+            w[:, 256 * j + 128 * b: 256 * j + 128 * (b + 1)] = \
+                (mags[16384 * b: 16384 * (b + 1)] | signs[16384 * b: 16384 * (b + 1)]).reshape(128, 128)
+    codes, scales = gpu_quant([w])
+    rc, rs = oracle.fp8_block_quant([w])
+    assert np.array_equal(scales.view(np.uint32), rs.view(np.uint32))
+    bad = np.argwhere(codes != rc)
+    assert bad.size == 0, (bad[:4], amaxes[bad[0][2] // 256] if bad.size else None)
+
+
 def test_lz4_workspace_reuse_across_sizes():
     """Encode and decode workspaces reused by many calls of different sizes: the
     status words of one call never meet another call's per-block data."""
