@@ -48,6 +48,10 @@ def lib():
         L.oracle_e4m3_rne.argtypes = [ctypes.c_float]
         L.oracle_e4m3_rne.restype = ctypes.c_uint8
         L.oracle_fp8_block_quant.argtypes = [_P, _P, _I32, _I64, _I64, _P, _P, _P]
+        L.oracle_fp8_delta.argtypes = [_P, _P, _I64, _P, _P, _I64, _P, _P, _I64, _P, _P, _P, _I64, _P, _P]
+        L.oracle_fp8_apply_delta.argtypes = [_P, _I64, _P, _I64, _P, _P, _I64, _P, _P, _I64, _P]
+        L.oracle_loco_gate.argtypes = [_P, _P, _P, _I64, _P, _P, _I64, _P, _P]
+        L.oracle_loco_accumulate.argtypes = [_P, _I64, _P, _P, _I64, _P]
         _lib = L
     return _lib
 
@@ -197,3 +201,60 @@ def fp8_block_quant(srcs, batch=1):
     lib().oracle_fp8_block_quant(ctypes.cast(ptrs, ctypes.c_void_p), _ptr(rows), len(arrs), cols,
                                  batch, _ptr(strides), _ptr(codes), _ptr(scales))
     return codes, scales
+
+
+def fp8_delta(codes_old, codes_new, scales_old, scales_new, code_cap=None, scale_cap=None):
+    """Returns dict(code_idx, code_val, code_count, scale_idx, scale_val, scale_count, status)."""
+    co = _c(codes_old, np.uint8).reshape(-1)
+    cn = _c(codes_new, np.uint8).reshape(-1)
+    so = _c(scales_old, np.float32).reshape(-1)
+    sn = _c(scales_new, np.float32).reshape(-1)
+    assert co.size == cn.size and so.size == sn.size
+    code_cap = co.size if code_cap is None else int(code_cap)
+    scale_cap = so.size if scale_cap is None else int(scale_cap)
+    ci, cv = np.empty(max(code_cap, 1), np.int32), np.empty(max(code_cap, 1), np.uint8)
+    si, sv = np.empty(max(scale_cap, 1), np.int32), np.empty(max(scale_cap, 1), np.float32)
+    cc, sc = np.zeros(1, np.int64), np.zeros(1, np.int64)
+    status = np.zeros(1, np.uint32)
+    lib().oracle_fp8_delta(_ptr(co), _ptr(cn), co.size, _ptr(so), _ptr(sn), so.size, _ptr(ci), _ptr(cv),
+                           code_cap, _ptr(cc), _ptr(si), _ptr(sv), scale_cap, _ptr(sc), _ptr(status))
+    m, k = int(cc[0]), int(sc[0])
+    return dict(code_idx=ci[:min(m, code_cap)], code_val=cv[:min(m, code_cap)], code_count=m,
+                scale_idx=si[:min(k, scale_cap)], scale_val=sv[:min(k, scale_cap)], scale_count=k,
+                status=int(status[0]))
+
+
+def fp8_apply_delta(codes, scales, code_idx, code_val, scale_idx, scale_val):
+    """Applies to copies; returns (codes, scales, status)."""
+    c = _c(codes, np.uint8).reshape(-1).copy()
+    s = _c(scales, np.float32).reshape(-1).copy()
+    ci, cv = _c(code_idx, np.int32), _c(code_val, np.uint8)
+    si, sv = _c(scale_idx, np.int32), _c(scale_val, np.float32)
+    status = np.zeros(1, np.uint32)
+    lib().oracle_fp8_apply_delta(_ptr(c), c.size, _ptr(s), s.size, _ptr(ci), _ptr(cv), ci.size,
+                                 _ptr(si), _ptr(sv), si.size, _ptr(status))
+    return c, s, int(status[0])
+
+
+def loco_gate(theta, delta, resid, cap=None):
+    """Returns dict(idx, val, count, resid (new array), status)."""
+    th = _c(theta, np.float32).reshape(-1)
+    de = _c(delta, np.float32).reshape(-1)
+    r = _c(resid, np.float32).reshape(-1).copy()
+    n = th.size
+    assert de.size == n and r.size == n
+    cap = n if cap is None else int(cap)
+    idx, val = np.empty(max(cap, 1), np.int32), np.empty(max(cap, 1), np.float32)
+    count, status = np.zeros(1, np.int64), np.zeros(1, np.uint32)
+    lib().oracle_loco_gate(_ptr(th), _ptr(de), _ptr(r), n, _ptr(idx), _ptr(val), cap, _ptr(count), _ptr(status))
+    m = int(count[0])
+    return dict(idx=idx[:min(m, cap)], val=val[:min(m, cap)], count=m, resid=r, status=int(status[0]))
+
+
+def loco_accumulate(acc, idx, val):
+    """acc[idx[k]] += val[k] on a copy; returns (acc, status)."""
+    a = _c(acc, np.float32).reshape(-1).copy()
+    i, v = _c(idx, np.int32), _c(val, np.float32)
+    status = np.zeros(1, np.uint32)
+    lib().oracle_loco_accumulate(_ptr(a), a.size, _ptr(i), _ptr(v), i.size, _ptr(status))
+    return a, int(status[0])

@@ -19,6 +19,14 @@
  *   oracle_e4m3_rne, oracle_fp8_block_quant
  *                           pinned: torch.float8_e4m3fn, nearest-of-set search,
  *                           closed forms for constant blocks, stacking invariant.
+ *   oracle_fp8_delta, oracle_fp8_apply_delta
+ *                           pinned: numpy flatnonzero over the codes and the scale
+ *                           bit patterns; apply(quant(old), delta) == quant(new).
+ *   oracle_loco_gate, oracle_loco_accumulate
+ *                           pinned: torch's float32 add and BF16 cast, the exact
+ *                           conservation resid' + sent == resid + delta, closed
+ *                           forms for constant updates near 1 (sent every 4th
+ *                           round upward, every 2nd downward), numpy add.at.
  */
 #include "oracle.h"
 
@@ -379,4 +387,118 @@ void oracle_fp8_block_quant(const uint16_t *const *srcs, const int64_t *src_rows
         }
     }
     free(stk);
+}
+
+/* ------------------------------------------------------------------------ */
+/* f1  deltas of the FP8 served view.  When the rollout engine serves FP8,    */
+/* the view that must match bit for bit is the quantised one, and its coarser */
+/* cells change fewer values per step [Jiang talk, 13:06-14:40; PULSE summary,*/
+/* "Potenziale Futuro"].  Two quantised versions (codes and per-block scales) */
+/* are compared bitwise, exactly like the BF16 views; each changed position   */
+/* becomes an (index, new absolute value) entry, ascending.                   */
+/* ------------------------------------------------------------------------ */
+void oracle_fp8_delta(const uint8_t *codes_old, const uint8_t *codes_new, int64_t n_codes,
+                      const float *scales_old, const float *scales_new, int64_t n_scales,
+                      int32_t *code_idx, uint8_t *code_val, int64_t code_cap, int64_t *code_count,
+                      int32_t *scale_idx, float *scale_val, int64_t scale_cap, int64_t *scale_count,
+                      uint32_t *status)
+{
+    int64_t m = 0;
+    for (int64_t i = 0; i < n_codes; ++i) {
+        if (codes_old[i] != codes_new[i]) {
+            if (m < code_cap) {
+                code_idx[m] = (int32_t)i;
+                code_val[m] = codes_new[i];
+            }
+            ++m;
+        }
+    }
+    if (m > code_cap && status) *status |= ORACLE_CAPACITY;
+    *code_count = m;
+
+    m = 0;
+    for (int64_t i = 0; i < n_scales; ++i) {
+        uint32_t a, b; /* compared as 32-bit patterns */
+        memcpy(&a, &scales_old[i], 4);
+        memcpy(&b, &scales_new[i], 4);
+        if (a != b) {
+            if (m < scale_cap) {
+                scale_idx[m] = (int32_t)i;
+                scale_val[m] = scales_new[i];
+            }
+            ++m;
+        }
+    }
+    if (m > scale_cap && status) *status |= ORACLE_CAPACITY;
+    *scale_count = m;
+}
+
+void oracle_fp8_apply_delta(uint8_t *codes, int64_t n_codes, float *scales, int64_t n_scales,
+                            const int32_t *code_idx, const uint8_t *code_val, int64_t code_count,
+                            const int32_t *scale_idx, const float *scale_val, int64_t scale_count,
+                            uint32_t *status)
+{
+    for (int64_t k = 0; k < code_count; ++k) {
+        int64_t i = code_idx[k];
+        if (i < 0 || i >= n_codes) {
+            if (status) *status |= ORACLE_BADINDEX;
+            continue;
+        }
+        codes[i] = code_val[k];
+    }
+    for (int64_t k = 0; k < scale_count; ++k) {
+        int64_t i = scale_idx[k];
+        if (i < 0 || i >= n_scales) {
+            if (status) *status |= ORACLE_BADINDEX;
+            continue;
+        }
+        scales[i] = scale_val[k];
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* f3  PULSELoCo: the compute-visibility gate on FP32 pseudo-gradients with   */
+/* an FP32 error-feedback buffer [PULSE summary, "2. PULSELoCo" -- Processo]. */
+/* A worker's pseudo-gradient is its parameter update over H local steps;     */
+/* added to what was held back before, an entry is sent only if applying it  */
+/* to the shared checkpoint would change that entry's BF16 view; otherwise it */
+/* stays in the buffer and is looked at again next round.                     */
+/* ------------------------------------------------------------------------ */
+void oracle_loco_gate(const float *theta, const float *delta, float *resid, int64_t n,
+                      int32_t *idx, float *val, int64_t cap, int64_t *count, uint32_t *status)
+{
+    int64_t m = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        float a = resid[i] + delta[i];   /* accumulated update, FP32 */
+        float moved = theta[i] + a;      /* the checkpoint entry after it */
+        uint32_t tb, mb;
+        memcpy(&tb, &theta[i], 4);
+        memcpy(&mb, &moved, 4);
+        if (oracle_bf16_rne(mb) != oracle_bf16_rne(tb)) { /* visible: send it */
+            if (m < cap) {
+                idx[m] = (int32_t)i;
+                val[m] = a;
+            }
+            ++m;
+            resid[i] = 0.0f;
+        } else {
+            resid[i] = a; /* held back for the next round */
+        }
+    }
+    if (m > cap && status) *status |= ORACLE_CAPACITY;
+    *count = m;
+}
+
+/* The receiving trainer sums the workers' sparse updates: acc[idx[k]] += val[k]. */
+void oracle_loco_accumulate(float *acc, int64_t n, const int32_t *idx, const float *val,
+                            int64_t count, uint32_t *status)
+{
+    for (int64_t k = 0; k < count; ++k) {
+        int64_t i = idx[k];
+        if (i < 0 || i >= n) {
+            if (status) *status |= ORACLE_BADINDEX;
+            continue;
+        }
+        acc[i] = acc[i] + val[k];
+    }
 }

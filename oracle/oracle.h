@@ -103,6 +103,26 @@ void oracle_fp8_block_quant(const uint16_t *const *srcs, const int64_t *src_rows
                             int32_t nsrc, int64_t cols, int64_t batch,
                             const int64_t *src_batch_stride, uint8_t *codes, float *scales);
 
+/* f1: FP8-view deltas.  Codes compared as bytes, scales as 32-bit patterns;
+ * each changed position gives an ascending (index, new value) entry; counts
+ * exact, entries beyond a capacity not written (ORACLE_CAPACITY). */
+void oracle_fp8_delta(const uint8_t *codes_old, const uint8_t *codes_new, int64_t n_codes,
+                      const float *scales_old, const float *scales_new, int64_t n_scales,
+                      int32_t *code_idx, uint8_t *code_val, int64_t code_cap, int64_t *code_count,
+                      int32_t *scale_idx, float *scale_val, int64_t scale_cap, int64_t *scale_count,
+                      uint32_t *status);
+/* f1: codes[code_idx[k]] = code_val[k], scales[scale_idx[k]] = scale_val[k]. */
+void oracle_fp8_apply_delta(uint8_t *codes, int64_t n_codes, float *scales, int64_t n_scales,
+                            const int32_t *code_idx, const uint8_t *code_val, int64_t code_count,
+                            const int32_t *scale_idx, const float *scale_val, int64_t scale_count,
+                            uint32_t *status);
+/* f3: a = resid + delta; sent (index, a) and resid = 0 where
+ * bf16(theta + a) != bf16(theta), else resid = a.  All float32. */
+void oracle_loco_gate(const float *theta, const float *delta, float *resid, int64_t n,
+                      int32_t *idx, float *val, int64_t cap, int64_t *count, uint32_t *status);
+/* f3: acc[idx[k]] += val[k] (float32) for k < count. */
+void oracle_loco_accumulate(float *acc, int64_t n, const int32_t *idx, const float *val,
+                            int64_t count, uint32_t *status);
 #ifdef __cplusplus
 }
 #endif
