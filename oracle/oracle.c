@@ -478,9 +478,11 @@ void oracle_loco_gate(const float *theta, const float *delta, float *resid, int6
             if (m < cap) {
                 idx[m] = (int32_t)i;
                 val[m] = a;
+                resid[i] = 0.0f;
+            } else {
+                resid[i] = a; /* no room to send it: it is not sent, so it stays */
             }
             ++m;
-            resid[i] = 0.0f;
         } else {
             resid[i] = a; /* held back for the next round */
         }

@@ -117,7 +117,8 @@ void oracle_fp8_apply_delta(uint8_t *codes, int64_t n_codes, float *scales, int6
                             const int32_t *scale_idx, const float *scale_val, int64_t scale_count,
                             uint32_t *status);
 /* f3: a = resid + delta; sent (index, a) and resid = 0 where
- * bf16(theta + a) != bf16(theta), else resid = a.  All float32. */
+ * bf16(theta + a) != bf16(theta), else resid = a.  All float32.  Visible
+ * entries beyond the capacity are counted but not sent: resid = a. */
 void oracle_loco_gate(const float *theta, const float *delta, float *resid, int64_t n,
                       int32_t *idx, float *val, int64_t cap, int64_t *count, uint32_t *status);
 /* f3: acc[idx[k]] += val[k] (float32) for k < count. */
