@@ -79,6 +79,8 @@ extern "C" {
 #define PULSE_OP_COMPACT 2    /* n = element count                               */
 #define PULSE_OP_LZ4_ENCODE 3 /* n = source bytes, aux = block_bytes              */
 #define PULSE_OP_LZ4_DECODE 4 /* n = number of blocks, aux = payload bytes         */
+#define PULSE_OP_FP8_DELTA 5  /* n = max(code count, scale count)                 */
+#define PULSE_OP_LOCO_GATE 6  /* n = element count                               */
 
 /* Bytes of workspace the op needs for the given size (0 if it needs none).
  * A workspace serves any number of calls of the op it was sized for, of any
@@ -236,6 +238,67 @@ int lz4_decode_blocks(const uint8_t *payload, int64_t payload_bytes,
 int fp8_block_quant(const uint16_t *const *srcs, const int64_t *src_rows, int32_t nsrc,
                     int64_t cols, int64_t batch, const int64_t *src_batch_stride,
                     uint8_t *codes, float *scales, hipStream_t stream);
+
+/* ---- next: deltas of the FP8 served view ----------------------------------
+ * When the sampler serves FP8, the view it must rebuild bit for bit is the
+ * quantised one, and its coarser cells change fewer values per step ([Jiang
+ * talk] 13:06-14:40; [PULSE summary] "Potenziale Futuro").  Two versions of
+ * fp8_block_quant's output are compared bitwise (codes as bytes, scales as
+ * 32-bit patterns) and each changed position is sent with its new absolute
+ * value, as for the BF16 view.
+ *   codes_old, codes_new   [n_codes] E4M3 codes, 16-byte aligned (read).
+ *   scales_old, scales_new [n_scales] float32 block scales, 16-byte aligned.
+ *   n_codes, n_scales      1 .. 2^31 - 1.
+ *   code_idx, code_val     [code_cap] ascending int32 positions and new codes
+ *                          (written); *d_code_count = exact number of changes.
+ *   scale_idx, scale_val   [scale_cap] the same for the scales.
+ *   d_status               PULSE_DS_CAPACITY when either list exceeds its cap
+ *                          (entries beyond the cap are not written).
+ *   ws                     pulse_workspace_bytes(PULSE_OP_FP8_DELTA,
+ *                          max(n_codes, n_scales), 0). */
+int fp8_view_delta(const uint8_t *codes_old, const uint8_t *codes_new, int64_t n_codes,
+                   const float *scales_old, const float *scales_new, int64_t n_scales,
+                   int32_t *code_idx, uint8_t *code_val, int64_t code_cap, int64_t *d_code_count,
+                   int32_t *scale_idx, float *scale_val, int64_t scale_cap, int64_t *d_scale_count,
+                   uint32_t *d_status, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* The receiver's side: codes[code_idx[k]] = code_val[k] for
+ * k < min(*d_code_count, max_code_count), and the same for the scales; the
+ * result is the new quantisation bit for bit.  Entries with an index outside
+ * the buffer are skipped and set PULSE_DS_BADINDEX.  Indices must be unique
+ * (a delta's are). */
+int fp8_view_apply(uint8_t *codes, int64_t n_codes, float *scales, int64_t n_scales,
+                   const int32_t *code_idx, const uint8_t *code_val, const int64_t *d_code_count,
+                   int64_t max_code_count, const int32_t *scale_idx, const float *scale_val,
+                   const int64_t *d_scale_count, int64_t max_scale_count, uint32_t *d_status,
+                   hipStream_t stream);
+
+/* ---- next: PULSELoCo visibility gate with FP32 error feedback -------------
+ * Trainer-to-trainer sync ([PULSE summary] "2. PULSELoCo", Processo): each
+ * worker's pseudo-gradient (its parameter update over H local steps) is added
+ * to its error-feedback buffer, a = resid + delta (float32); the entry is sent
+ * only if it would change the BF16 view of the shared checkpoint,
+ * bf16(theta + a) != bf16(theta) (float32 add, round to nearest even), and
+ * otherwise stays in the buffer for the next round.
+ *   theta   [n] float32 shared checkpoint (read), 16-byte aligned.
+ *   delta   [n] float32 pseudo-gradient (read), 16-byte aligned.
+ *   resid   [n] float32 error-feedback buffer, 16-byte aligned: read, then
+ *           rewritten with 0 where the entry was sent and a elsewhere.
+ *   idx, val [cap] ascending int32 positions and the sent float32 values a.
+ *   d_count  exact number of visible entries.  Visible entries beyond cap are
+ *           not sent and stay in resid (PULSE_DS_CAPACITY): nothing is lost.
+ *   ws      pulse_workspace_bytes(PULSE_OP_LOCO_GATE, n, 0). */
+int pulse_loco_gate(const float *theta, const float *delta, float *resid, int64_t n,
+                    int32_t *idx, float *val, int64_t cap, int64_t *d_count, uint32_t *d_status,
+                    void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* The receiving trainer sums the workers' sparse updates before its outer
+ * step: acc[idx[k]] += val[k] (float32) for k < min(*d_count, max_count), in
+ * stream order, one patch per call (indices unique within a patch, so the
+ * result is deterministic).  Out-of-range indices set PULSE_DS_BADINDEX. */
+int pulse_loco_accumulate(float *acc, int64_t n, const int32_t *idx, const float *val,
+                          const int64_t *d_count, int64_t max_count, uint32_t *d_status,
+                          hipStream_t stream);
 
 #ifdef __cplusplus
 }

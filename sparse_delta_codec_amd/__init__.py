@@ -17,6 +17,8 @@ __all__ = [
     "pulse_version", "pulse_workspace_bytes", "pulse_workspace_init", "workspace",
     "pulse_cast_diff", "pulse_compact", "pulse_apply_patch", "xor_mask_apply",
     "lz4_encode_blocks", "lz4_decode_blocks", "fp8_block_quant", "lz4_payload_bound", "lib_path",
+    "PULSE_OP_FP8_DELTA", "PULSE_OP_LOCO_GATE", "fp8_view_delta", "fp8_view_apply",
+    "pulse_loco_gate", "pulse_loco_accumulate",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -35,6 +37,8 @@ PULSE_OP_CAST_DIFF = 1
 PULSE_OP_COMPACT = 2
 PULSE_OP_LZ4_ENCODE = 3
 PULSE_OP_LZ4_DECODE = 4
+PULSE_OP_FP8_DELTA = 5
+PULSE_OP_LOCO_GATE = 6
 
 _P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
 _lib.pulse_version.restype = ctypes.c_char_p
@@ -50,8 +54,13 @@ _lib.xor_mask_apply.argtypes = [_P, _P, _I64, _P]
 _lib.lz4_encode_blocks.argtypes = [_P, _P, _I64, _I32, _P, _I64, _P, _P, _P, _P, _P, _SZ, _P]
 _lib.lz4_decode_blocks.argtypes = [_P, _I64, _P, _P, _I64, _I32, _I64, _P, _I32, _P, _P, _SZ, _P]
 _lib.fp8_block_quant.argtypes = [_P, _P, _I32, _I64, _I64, _P, _P, _P, _P]
+_lib.fp8_view_delta.argtypes = [_P, _P, _I64, _P, _P, _I64, _P, _P, _I64, _P, _P, _P, _I64, _P, _P, _P, _SZ, _P]
+_lib.fp8_view_apply.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _I64, _P, _P, _P, _I64, _P, _P]
+_lib.pulse_loco_gate.argtypes = [_P, _P, _P, _I64, _P, _P, _I64, _P, _P, _P, _SZ, _P]
+_lib.pulse_loco_accumulate.argtypes = [_P, _I64, _P, _P, _P, _I64, _P, _P]
 for _f in ("pulse_workspace_init", "pulse_cast_diff", "pulse_compact", "pulse_apply_patch",
-           "xor_mask_apply", "lz4_encode_blocks", "lz4_decode_blocks", "fp8_block_quant"):
+           "xor_mask_apply", "lz4_encode_blocks", "lz4_decode_blocks", "fp8_block_quant",
+           "fp8_view_delta", "fp8_view_apply", "pulse_loco_gate", "pulse_loco_accumulate"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -235,3 +244,70 @@ def fp8_block_quant(srcs, codes, scales, batch=1, stream=None):
         None if strides is None else ctypes.cast(strides, ctypes.c_void_p),
         _dev(codes, "codes", torch.uint8), _dev(scales, "scales", torch.float32), _stream(stream)),
         "fp8_block_quant")
+
+
+def fp8_view_delta(codes_old, codes_new, scales_old, scales_new, code_idx, code_val, d_code_count,
+                   scale_idx, scale_val, d_scale_count, d_status, ws, code_cap=None, scale_cap=None,
+                   stream=None):
+    """Changed E4M3 codes and block scales between two quantisations (flat views)."""
+    nc, ns = codes_old.numel(), scales_old.numel()
+    code_cap = code_idx.numel() if code_cap is None else code_cap
+    scale_cap = scale_idx.numel() if scale_cap is None else scale_cap
+    _need(codes_new, nc, "codes_new")
+    _need(scales_new, 4 * ns, "scales_new")
+    _need(code_idx, 4 * code_cap, "code_idx")
+    _need(code_val, code_cap, "code_val")
+    _need(scale_idx, 4 * scale_cap, "scale_idx")
+    _need(scale_val, 4 * scale_cap, "scale_val")
+    wsp, wsb = _ws(ws)
+    _check(_lib.fp8_view_delta(
+        _dev(codes_old, "codes_old", torch.uint8), _dev(codes_new, "codes_new", torch.uint8), nc,
+        _dev(scales_old, "scales_old", torch.float32), _dev(scales_new, "scales_new", torch.float32), ns,
+        _dev(code_idx, "code_idx", torch.int32), _dev(code_val, "code_val", torch.uint8), code_cap,
+        _dev(d_code_count, "d_code_count", torch.int64), _dev(scale_idx, "scale_idx", torch.int32),
+        _dev(scale_val, "scale_val", torch.float32), scale_cap,
+        _dev(d_scale_count, "d_scale_count", torch.int64), _dev(d_status, "d_status", torch.int32),
+        wsp, wsb, _stream(stream)), "fp8_view_delta")
+
+
+def fp8_view_apply(codes, scales, code_idx, code_val, d_code_count, scale_idx, scale_val, d_scale_count,
+                   d_status, max_code_count=None, max_scale_count=None, stream=None):
+    mc = code_idx.numel() if max_code_count is None else max_code_count
+    ms = scale_idx.numel() if max_scale_count is None else max_scale_count
+    _need(code_idx, 4 * mc, "code_idx")
+    _need(code_val, mc, "code_val")
+    _need(scale_idx, 4 * ms, "scale_idx")
+    _need(scale_val, 4 * ms, "scale_val")
+    _check(_lib.fp8_view_apply(
+        _dev(codes, "codes", torch.uint8), codes.numel(), _dev(scales, "scales", torch.float32), scales.numel(),
+        _dev(code_idx, "code_idx", torch.int32), _dev(code_val, "code_val", torch.uint8),
+        _dev(d_code_count, "d_code_count", torch.int64), mc, _dev(scale_idx, "scale_idx", torch.int32),
+        _dev(scale_val, "scale_val", torch.float32), _dev(d_scale_count, "d_scale_count", torch.int64), ms,
+        _dev(d_status, "d_status", torch.int32), _stream(stream)), "fp8_view_apply")
+
+
+def pulse_loco_gate(theta, delta, resid, idx, val, d_count, d_status, ws, n=None, cap=None, stream=None):
+    """Visible entries of resid + delta against the BF16 view of theta; resid rewritten in place."""
+    n = theta.numel() if n is None else n
+    cap = idx.numel() if cap is None else cap
+    for t, nm in ((theta, "theta"), (delta, "delta"), (resid, "resid")):
+        _need(t, 4 * n, nm)
+    _need(idx, 4 * cap, "idx")
+    _need(val, 4 * cap, "val")
+    wsp, wsb = _ws(ws)
+    _check(_lib.pulse_loco_gate(
+        _dev(theta, "theta", torch.float32), _dev(delta, "delta", torch.float32),
+        _dev(resid, "resid", torch.float32), n, _dev(idx, "idx", torch.int32), _dev(val, "val", torch.float32),
+        cap, _dev(d_count, "d_count", torch.int64), _dev(d_status, "d_status", torch.int32),
+        wsp, wsb, _stream(stream)), "pulse_loco_gate")
+
+
+def pulse_loco_accumulate(acc, idx, val, d_count, d_status, max_count=None, stream=None):
+    max_count = idx.numel() if max_count is None else max_count
+    _need(idx, 4 * max_count, "idx")
+    _need(val, 4 * max_count, "val")
+    _check(_lib.pulse_loco_accumulate(
+        _dev(acc, "acc", torch.float32), acc.numel(), _dev(idx, "idx", torch.int32),
+        _dev(val, "val", torch.float32), _dev(d_count, "d_count", torch.int64), max_count,
+        _dev(d_status, "d_status", torch.int32), _stream(stream)), "pulse_loco_accumulate")
+

@@ -24,6 +24,17 @@ int pulse_launch_lz4_decode(const uint8_t *, int64_t, const uint64_t *, const ui
 int pulse_lz4_decode_ws_fits(size_t ws, int64_t nblocks, int64_t payload_bytes);
 int pulse_launch_fp8_block_quant(const uint16_t *const *, const int64_t *, int32_t, int64_t, int64_t,
                                  const int64_t *, uint8_t *, float *, hipStream_t);
+size_t pulse_delta_compact_ws_bytes(int64_t n);
+int pulse_launch_fp8_delta(const uint8_t *, const uint8_t *, int64_t, const float *, const float *, int64_t,
+                           int32_t *, uint8_t *, int64_t, int64_t *, int32_t *, float *, int64_t, int64_t *,
+                           uint32_t *, void *, hipStream_t);
+int pulse_launch_fp8_apply(uint8_t *, int64_t, float *, int64_t, const int32_t *, const uint8_t *,
+                           const int64_t *, int64_t, const int32_t *, const float *, const int64_t *, int64_t,
+                           uint32_t *, hipStream_t);
+int pulse_launch_loco_gate(const float *, const float *, float *, int64_t, int32_t *, float *, int64_t, int64_t *,
+                           uint32_t *, void *, hipStream_t);
+int pulse_launch_loco_accumulate(float *, int64_t, const int32_t *, const float *, const int64_t *, int64_t,
+                                 uint32_t *, hipStream_t);
 int pulse_launch_fill_zero(void *, size_t, hipStream_t);
 int pulse_launch_write_count(int64_t *, int64_t, hipStream_t);
 }
@@ -64,6 +75,8 @@ size_t pulse_workspace_bytes(int op, int64_t n, int64_t aux) {
     case PULSE_OP_LZ4_DECODE:
         if (aux < 0) return 0;
         return pulse_lz4_decode_ws_bytes(n, aux);
+    case PULSE_OP_FP8_DELTA:
+    case PULSE_OP_LOCO_GATE: return pulse_delta_compact_ws_bytes(n);
     default: return 0;
     }
 }
@@ -176,6 +189,58 @@ int fp8_block_quant(const uint16_t *const *srcs, const int64_t *src_rows, int32_
     if (reinterpret_cast<uintptr_t>(codes) % 8 != 0 || reinterpret_cast<uintptr_t>(scales) % 4 != 0)
         return PULSE_EALIGN;
     return pulse_launch_fp8_block_quant(srcs, src_rows, nsrc, cols, batch, src_batch_stride, codes, scales, stream);
+}
+
+int fp8_view_delta(const uint8_t *codes_old, const uint8_t *codes_new, int64_t n_codes, const float *scales_old,
+                   const float *scales_new, int64_t n_scales, int32_t *code_idx, uint8_t *code_val,
+                   int64_t code_cap, int64_t *d_code_count, int32_t *scale_idx, float *scale_val,
+                   int64_t scale_cap, int64_t *d_scale_count, uint32_t *d_status, void *ws, size_t ws_bytes,
+                   hipStream_t stream) {
+    if (!codes_old || !codes_new || !scales_old || !scales_new || !code_idx || !code_val || !d_code_count ||
+        !scale_idx || !scale_val || !d_scale_count || !d_status || n_codes < 1 || n_scales < 1 ||
+        code_cap < 0 || scale_cap < 0)
+        return PULSE_EINVAL;
+    if (!aligned16(codes_old) || !aligned16(codes_new) || !aligned16(scales_old) || !aligned16(scales_new))
+        return PULSE_EALIGN;
+    if (n_codes > kMaxIndexed || n_scales > kMaxIndexed) return PULSE_ERANGE;
+    const int64_t n = n_codes > n_scales ? n_codes : n_scales;
+    if (!ws || ws_bytes < pulse_delta_compact_ws_bytes(n)) return PULSE_EWORKSPACE;
+    return pulse_launch_fp8_delta(codes_old, codes_new, n_codes, scales_old, scales_new, n_scales, code_idx,
+                                  code_val, code_cap, d_code_count, scale_idx, scale_val, scale_cap,
+                                  d_scale_count, d_status, ws, stream);
+}
+
+int fp8_view_apply(uint8_t *codes, int64_t n_codes, float *scales, int64_t n_scales, const int32_t *code_idx,
+                   const uint8_t *code_val, const int64_t *d_code_count, int64_t max_code_count,
+                   const int32_t *scale_idx, const float *scale_val, const int64_t *d_scale_count,
+                   int64_t max_scale_count, uint32_t *d_status, hipStream_t stream) {
+    if (!codes || !scales || !code_idx || !code_val || !d_code_count || !scale_idx || !scale_val ||
+        !d_scale_count || !d_status || n_codes < 0 || n_scales < 0 || max_code_count < 0 || max_scale_count < 0)
+        return PULSE_EINVAL;
+    if (n_codes > kMaxIndexed + 1 || n_scales > kMaxIndexed + 1) return PULSE_ERANGE;
+    return pulse_launch_fp8_apply(codes, n_codes, scales, n_scales, code_idx, code_val, d_code_count,
+                                  max_code_count, scale_idx, scale_val, d_scale_count, max_scale_count, d_status,
+                                  stream);
+}
+
+int pulse_loco_gate(const float *theta, const float *delta, float *resid, int64_t n, int32_t *idx, float *val,
+                    int64_t cap, int64_t *d_count, uint32_t *d_status, void *ws, size_t ws_bytes,
+                    hipStream_t stream) {
+    if (!theta || !delta || !resid || !idx || !val || !d_count || !d_status || n < 0 || cap < 0)
+        return PULSE_EINVAL;
+    if (!aligned16(theta) || !aligned16(delta) || !aligned16(resid)) return PULSE_EALIGN;
+    if (n > kMaxIndexed) return PULSE_ERANGE;
+    if (!ws || ws_bytes < pulse_delta_compact_ws_bytes(n)) return PULSE_EWORKSPACE;
+    if (n == 0) return pulse_launch_write_count(d_count, 0, stream);
+    return pulse_launch_loco_gate(theta, delta, resid, n, idx, val, cap, d_count, d_status, ws, stream);
+}
+
+int pulse_loco_accumulate(float *acc, int64_t n, const int32_t *idx, const float *val, const int64_t *d_count,
+                          int64_t max_count, uint32_t *d_status, hipStream_t stream) {
+    if (!acc || !idx || !val || !d_count || !d_status || n < 0 || max_count < 0) return PULSE_EINVAL;
+    if (n > kMaxIndexed + 1) return PULSE_ERANGE;
+    if (max_count == 0) return PULSE_OK;
+    return pulse_launch_loco_accumulate(acc, n, idx, val, d_count, max_count, d_status, stream);
 }
 
 }  // extern "C"

@@ -105,3 +105,31 @@ def test_argument_errors_return_before_any_launch(lib):
     x = lib.xor_mask_apply
     x.argtypes = [V, V, I64, V]
     assert x(mis, al, 100, None) == EALIGN and x(al, al, -1, None) == EINVAL
+
+
+def test_next_rows_argument_errors(lib):
+    al = V(0x10000)
+    mis = V(0x10002)
+    SZ = ctypes.c_size_t
+    d = lib.fp8_view_delta
+    d.argtypes = [V, V, I64, V, V, I64, V, V, I64, V, V, V, I64, V, V, V, SZ, V]
+    args = [al, al, 1000, al, al, 10, al, al, 1000, al, al, al, 10, al, al, al, 1 << 20, None]
+    assert d(*args[:2], 0, *args[3:]) == EINVAL                                  # empty codes
+    assert d(None, *args[1:]) == EINVAL
+    assert d(mis, *args[1:]) == EALIGN
+    assert d(*args[:2], 1 << 31, *args[3:]) == ERANGE
+    assert d(*args[:16], 8, None) == EWORKSPACE
+    ap = lib.fp8_view_apply
+    ap.argtypes = [V, I64, V, I64, V, V, V, I64, V, V, V, I64, V, V]
+    assert ap(al, 10, al, 1, al, al, al, -1, al, al, al, 1, al, None) == EINVAL
+    g = lib.pulse_loco_gate
+    g.argtypes = [V, V, V, I64, V, V, I64, V, V, V, SZ, V]
+    assert g(al, al, None, 100, al, al, 10, al, al, al, 1 << 20, None) == EINVAL        # resid required
+    assert g(al, mis, al, 100, al, al, 10, al, al, al, 1 << 20, None) == EALIGN
+    assert g(al, al, al, 1 << 31, al, al, 10, al, al, al, 1 << 40, None) == ERANGE
+    assert g(al, al, al, 100000, al, al, 10, al, al, al, 64, None) == EWORKSPACE
+    acc = lib.pulse_loco_accumulate
+    acc.argtypes = [V, I64, V, V, V, I64, V, V]
+    assert acc(al, 10, None, al, al, 5, al, None) == EINVAL
+    ws = lib.pulse_workspace_bytes
+    assert ws(5, 16384, 0) == 256 + 8 and ws(6, 16385, 0) == 256 + 16

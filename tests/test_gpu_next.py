@@ -1,0 +1,197 @@
+"""GPU parity of the next rows through the C ABI: FP8-view deltas and the
+PULSELoCo gate, bit-exact against the oracle on the same seeded inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workload
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import sparse_delta_codec_amd as pulse
+    from tests.gpu_util import dev, host, zeros  # noqa: E402
+
+SIZES = [1, 15, 16, 17, 1000, 16383, 16384, 16385, 3 * 16384 + 5, 100_007]
+
+
+def u32(a):
+    return np.ascontiguousarray(a, np.float32).view(np.uint32)
+
+
+def gpu_fp8_delta(co, cn, so, sn, code_cap=None, scale_cap=None, ws=None):
+    nc, ns = co.size, so.size
+    code_cap = nc if code_cap is None else code_cap
+    scale_cap = ns if scale_cap is None else scale_cap
+    ci, cv = zeros(code_cap, torch.int32), zeros(code_cap, torch.uint8)
+    si, sv = zeros(scale_cap, torch.int32), zeros(scale_cap, torch.float32)
+    cc, sc, st = zeros(1, torch.int64), zeros(1, torch.int64), zeros(1, torch.int32)
+    if ws is None:
+        ws = pulse.workspace(pulse.PULSE_OP_FP8_DELTA, max(nc, ns))
+    pulse.fp8_view_delta(dev(co), dev(cn), dev(so), dev(sn), ci, cv, cc, si, sv, sc, st, ws,
+                         code_cap=code_cap, scale_cap=scale_cap)
+    torch.cuda.synchronize()
+    m, k = int(host(cc)[0]), int(host(sc)[0])
+    return dict(code_idx=host(ci)[:min(m, code_cap)], code_val=host(cv)[:min(m, code_cap)], code_count=m,
+                scale_idx=host(si)[:min(k, scale_cap)], scale_val=host(sv)[:min(k, scale_cap)], scale_count=k,
+                status=int(host(st)[0]))
+
+
+def same_delta(g, r):
+    assert g["code_count"] == r["code_count"] and g["scale_count"] == r["scale_count"]
+    assert np.array_equal(g["code_idx"], r["code_idx"]) and np.array_equal(g["code_val"], r["code_val"])
+    assert np.array_equal(g["scale_idx"], r["scale_idx"])
+    assert np.array_equal(u32(g["scale_val"]), u32(r["scale_val"]))
+    assert g["status"] == r["status"]
+
+
+@pytest.mark.parametrize("n", SIZES)
+@pytest.mark.parametrize("p", [0.0, 0.01, 0.5, 1.0])
+def test_fp8_view_delta_matches_oracle(n, p):
+    rng = np.random.default_rng(n * 7 + int(p * 100))
+    co = rng.integers(0, 256, n, dtype=np.uint8)
+    cn = np.where(rng.random(n) < p, (co + rng.integers(1, 256, n)).astype(np.uint8), co)
+    ns = max(1, n // 100 + (n % 3))
+    so = (np.abs(rng.standard_normal(ns)) * 1e-3).astype(np.float32)
+    sn = np.where(rng.random(ns) < p, np.nextafter(so, np.float32(1)), so).astype(np.float32)
+    same_delta(gpu_fp8_delta(co, cn, so, sn), oracle.fp8_delta(co, cn, so, sn))
+
+
+def test_fp8_view_delta_capacity_and_workspace_reuse():
+    rng = np.random.default_rng(5)
+    big = 5 * 16384 + 77
+    ws = pulse.workspace(pulse.PULSE_OP_FP8_DELTA, big)
+    for n, p, cap in [(big, 0.3, 1000), (2000, 0.5, None), (big, 0.02, None), (40000, 1.0, 5)]:
+        co = rng.integers(0, 256, n, dtype=np.uint8)
+        cn = np.where(rng.random(n) < p, (co ^ rng.integers(1, 256, n)).astype(np.uint8), co)
+        so = rng.random(n // 1000 + 1).astype(np.float32)
+        sn = so.copy()
+        sn[::3] *= np.float32(2)
+        g = gpu_fp8_delta(co, cn, so, sn, code_cap=cap, ws=ws)
+        r = oracle.fp8_delta(co, cn, so, sn, code_cap=cap)
+        same_delta(g, r)
+
+
+def test_fp8_view_round_trip_on_quantised_weights():
+    """Quantise two versions on the GPU, take the delta, apply it to the old
+    quantisation on the GPU: the new quantisation comes back bit for bit, and
+    the delta equals the oracle's."""
+    w0, w1 = workload.c1_masters()
+    b0 = oracle.cast_bf16(w0).reshape(4096, 1024)
+    b1 = oracle.cast_bf16(w1).reshape(4096, 1024)
+    nb = 32 * 8
+    c0, s0 = zeros(b0.size, torch.uint8), zeros(nb, torch.float32)
+    c1, s1 = zeros(b0.size, torch.uint8), zeros(nb, torch.float32)
+    pulse.fp8_block_quant([dev(b0)], c0, s0)
+    pulse.fp8_block_quant([dev(b1)], c1, s1)
+    ci, cv = zeros(b0.size, torch.int32), zeros(b0.size, torch.uint8)
+    si, sv = zeros(nb, torch.int32), zeros(nb, torch.float32)
+    cc, sc, st = zeros(1, torch.int64), zeros(1, torch.int64), zeros(1, torch.int32)
+    ws = pulse.workspace(pulse.PULSE_OP_FP8_DELTA, b0.size)
+    pulse.fp8_view_delta(c0, c1, s0, s1, ci, cv, cc, si, sv, sc, st, ws)
+    rc0, rs0 = oracle.fp8_block_quant([b0])
+    rc1, rs1 = oracle.fp8_block_quant([b1])
+    r = oracle.fp8_delta(rc0, rc1, rs0, rs1)
+    codes, scales = c0.clone(), s0.clone()
+    pulse.fp8_view_apply(codes, scales, ci, cv, cc, si, sv, sc, st)
+    torch.cuda.synchronize()
+    assert int(host(st)[0]) == 0
+    m = int(host(cc)[0])
+    assert m == r["code_count"] and np.array_equal(host(ci)[:m], r["code_idx"])
+    assert np.array_equal(host(cv)[:m], r["code_val"])
+    assert np.array_equal(host(codes), host(c1)) and np.array_equal(host(codes), rc1.reshape(-1))
+    assert np.array_equal(u32(host(scales)), u32(rs1).reshape(-1))
+
+
+def test_fp8_view_apply_bad_index():
+    codes, scales = zeros(100, torch.uint8), zeros(4, torch.float32)
+    ci = dev(np.array([5, 100, 7], np.int32))
+    cv = dev(np.array([1, 2, 3], np.uint8))
+    si, sv = dev(np.array([3], np.int32)), dev(np.array([2.5], np.float32))
+    cc, sc = dev(np.array([3], np.int64)), dev(np.array([1], np.int64))
+    st = zeros(1, torch.int32)
+    pulse.fp8_view_apply(codes, scales, ci, cv, cc, si, sv, sc, st)
+    torch.cuda.synchronize()
+    c = host(codes)
+    assert int(host(st)[0]) == pulse.PULSE_DS_BADINDEX and c[5] == 1 and c[7] == 3 and host(scales)[3] == 2.5
+
+
+# ---- PULSELoCo gate -----------------------------------------------------------------
+def gate_inputs(n, scale, seed):
+    rng = np.random.default_rng(seed)
+    theta = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    theta[: n // 8] = (1 + rng.standard_normal(n // 8) * 0.01).astype(np.float32)
+    delta = (rng.standard_normal(n) * scale).astype(np.float32)
+    resid = (rng.standard_normal(n) * scale * (rng.random(n) < 0.5)).astype(np.float32)
+    # subnormals, signed zeros and exact ties must survive on the device
+    k = min(n, 8)
+    resid[:k] = np.array([1e-40, -1e-41, -0.0, 0.0, 2.0 ** -8, -(2.0 ** -9), 3e-39, 0.0], np.float32)[:k]
+    theta[:k] = np.array([1e-38, 0.0, -0.0, 1e-39, 1.0, 1.0, -2e-38, 5.0], np.float32)[:k]
+    return theta, delta, resid
+
+
+def gpu_gate(theta, delta, resid, cap=None, ws=None):
+    n = theta.size
+    cap = n if cap is None else cap
+    idx, val = zeros(cap, torch.int32), zeros(cap, torch.float32)
+    cnt, st = zeros(1, torch.int64), zeros(1, torch.int32)
+    R = dev(resid)
+    if ws is None:
+        ws = pulse.workspace(pulse.PULSE_OP_LOCO_GATE, n)
+    pulse.pulse_loco_gate(dev(theta), dev(delta), R, idx, val, cnt, st, ws, cap=cap)
+    torch.cuda.synchronize()
+    m = int(host(cnt)[0])
+    return dict(idx=host(idx)[:min(m, cap)], val=host(val)[:min(m, cap)], count=m, resid=host(R),
+                status=int(host(st)[0]))
+
+
+def same_gate(g, r):
+    assert g["count"] == r["count"] and g["status"] == r["status"]
+    assert np.array_equal(g["idx"], r["idx"])
+    assert np.array_equal(u32(g["val"]), u32(r["val"]))
+    bad = np.flatnonzero(u32(g["resid"]) != u32(r["resid"]))
+    assert bad.size == 0, bad[:5]
+
+
+@pytest.mark.parametrize("n", SIZES)
+@pytest.mark.parametrize("scale", [3e-6, 1e-4, 1e-2])
+def test_loco_gate_matches_oracle(n, scale):
+    theta, delta, resid = gate_inputs(n, scale, n + int(scale * 1e6))
+    same_gate(gpu_gate(theta, delta, resid), oracle.loco_gate(theta, delta, resid))
+
+
+def test_loco_gate_capacity_keeps_unsent_entries():
+    n = 3 * 16384 + 11
+    theta, delta, resid = gate_inputs(n, 1e-2, 21)
+    for cap in (0, 1, 700, 20000):
+        same_gate(gpu_gate(theta, delta, resid, cap=cap), oracle.loco_gate(theta, delta, resid, cap=cap))
+
+
+def test_loco_rounds_and_accumulate():
+    """Eight rounds of one worker against a fixed checkpoint (the buffer carried
+    from round to round on the device), each round's patch summed into an FP32
+    accumulator: every round equals the oracle's."""
+    n = 200_003
+    rng = np.random.default_rng(31)
+    theta = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    R, A = zeros(n, torch.float32), zeros(n, torch.float32)
+    r_host, a_host = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    idx, val = zeros(n, torch.int32), zeros(n, torch.float32)
+    cnt, st = zeros(1, torch.int64), zeros(1, torch.int32)
+    ws = pulse.workspace(pulse.PULSE_OP_LOCO_GATE, n)
+    T = dev(theta)
+    for rnd in range(8):
+        delta = (rng.standard_normal(n) * 3e-5).astype(np.float32)
+        pulse.pulse_loco_gate(T, dev(delta), R, idx, val, cnt, st, ws)
+        pulse.pulse_loco_accumulate(A, idx, val, cnt, st)
+        torch.cuda.synchronize()
+        ref = oracle.loco_gate(theta, delta, r_host)
+        r_host = ref["resid"]
+        a_host, _ = oracle.loco_accumulate(a_host, ref["idx"], ref["val"])
+        m = int(host(cnt)[0])
+        assert m == ref["count"], rnd
+        assert np.array_equal(host(idx)[:m], ref["idx"]), rnd
+        assert np.array_equal(u32(host(R)), u32(r_host)), rnd
+        assert np.array_equal(u32(host(A)), u32(a_host)), rnd
+    assert int(host(st)[0]) == 0
