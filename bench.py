@@ -47,7 +47,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--layers", type=int, default=64, help="decoder layers (64 = the full Qwen2.5-32B shape)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-frac", type=float, default=1.0, help="fraction of layer 0 the oracle times")
+    p.add_argument("--cpu-sample-frac", type=float, default=1.0,
+                   help="fraction of the oracle's sample (the attention half of layer 0) it times")
+    p.add_argument("--next", default="loco", choices=["none", "loco", "fp8", "all"],
+                   help="next-row legs measured after the timed steps (PULSELoCo gate; FP8-view deltas)")
     p.add_argument("--copy-probe-gib", type=float, default=0.0,
                    help="also run a plain device copy of this size (scale reference for HBM counters)")
     return p.parse_args()
@@ -337,36 +340,240 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the oracle on the host")
         result["cpu_baseline"] = cpu_baseline(specs, offs, W, b_old, args.cpu_sample_frac)
+
+    if args.next != "none":
+        # the next rows, measured after (and outside) the timed steps
+        nxt = {}
+        if args.next in ("fp8", "all"):
+            nxt.update(fp8_view_leg(pulse, specs, chunks, offs, qplans, W, b_old, stage, dev,
+                                    not args.no_cpu_baseline))
+        del W, stage, b_recv, idx, val, payload, codes, scales
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        if args.next in ("loco", "all"):
+            nxt.update(loco_leg(pulse, dev, not args.no_cpu_baseline))
+        result["next_rows"] = nxt
     print(json.dumps(result), flush=True)
 
 
+def _leg(ms, launches, alg_bytes, **extra):
+    secs = ms / 1e3
+    out = {"ms": round(ms, 3), "launches": launches, "alg_GB": round(alg_bytes / 1e9, 3),
+           "GBps": round(alg_bytes / secs / 1e9, 1), "frac_hbm": round(alg_bytes / secs / PEAK_HBM, 4)}
+    out.update(extra)
+    return out
+
+
+def fp8_view_leg(pulse, specs, chunks, offs, qplans, W, b_old, stage, dev, with_oracle):
+    """Deltas of the FP8 served view over the whole weight set: per chunk, the
+    old view and the sender's new view are quantised (untimed, FP8 groups laid
+    end to end), then fp8_view_delta and fp8_view_apply are timed; the applied
+    old quantisation must equal the new one bit for bit."""
+    import torch
+
+    max_q = max(sum(r * c for _, r, c in plan) for plan in qplans)
+    max_s = max(sum(((r + 127) // 128) * ((c + 127) // 128) for _, r, c in plan) for plan in qplans)
+    co = torch.empty(max_q, dtype=torch.uint8, device=dev)
+    cn = torch.empty(max_q, dtype=torch.uint8, device=dev)
+    so = torch.empty(max_s, dtype=torch.float32, device=dev)
+    sn = torch.empty(max_s, dtype=torch.float32, device=dev)
+    ccap = max_q // 10
+    ci = torch.empty(ccap, dtype=torch.int32, device=dev)
+    cv = torch.empty(ccap, dtype=torch.uint8, device=dev)
+    si = torch.empty(max_s, dtype=torch.int32, device=dev)
+    sv = torch.empty(max_s, dtype=torch.float32, device=dev)
+    cc = torch.zeros(len(chunks), dtype=torch.int64, device=dev)
+    sc = torch.zeros(len(chunks), dtype=torch.int64, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = pulse.workspace(pulse.PULSE_OP_FP8_DELTA, max_q, 0, dev)
+    t_delta = t_apply = 0.0
+    nq_tot = ns_tot = 0
+    ok = True
+    sample = None
+    for k, (s0, e0, tids) in enumerate(chunks):
+        m = e0 - s0
+        pulse.pulse_cast_diff(W[s0:e0], b_new=stage[:m])
+        qo = so_o = 0
+        for (g, rows, cols) in qplans[k]:
+            nq, ns = rows * cols, ((rows + 127) // 128) * ((cols + 127) // 128)
+            pulse.fp8_block_quant([b_old[offs[i]: offs[i] + specs[i].numel].view(specs[i].shape) for i in g],
+                                  co[qo:qo + nq], so[so_o:so_o + ns])
+            pulse.fp8_block_quant([stage[offs[i] - s0: offs[i] - s0 + specs[i].numel].view(specs[i].shape)
+                                   for i in g], cn[qo:qo + nq], sn[so_o:so_o + ns])
+            qo, so_o = qo + nq, so_o + ns
+        if k == 1 and with_oracle:  # a host copy of 64 Mi codes for the oracle's timing
+            sample = (co[:1 << 26].cpu().numpy(), cn[:1 << 26].cpu().numpy())
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record()
+        pulse.fp8_view_delta(co[:qo], cn[:qo], so[:so_o], sn[:so_o], ci, cv, cc[k:k + 1], si, sv, sc[k:k + 1],
+                             st, ws)
+        ev[1].record()
+        pulse.fp8_view_apply(co[:qo], so[:so_o], ci, cv, cc[k:k + 1], si, sv, sc[k:k + 1], st)
+        ev[2].record()
+        torch.cuda.synchronize()
+        t_delta += ev[0].elapsed_time(ev[1])
+        t_apply += ev[1].elapsed_time(ev[2])
+        ok = ok and views_equal(co[:qo], cn[:qo]) and views_equal(so[:so_o].view(torch.int32),
+                                                                     sn[:so_o].view(torch.int32))
+        nq_tot, ns_tot = nq_tot + qo, ns_tot + so_o
+    if int(st.item()) != 0 or not ok:
+        raise SystemExit(f"FP8-view delta leg failed (status {int(st.item())}, round trip {ok})")
+    ncodes = int(cc.sum().item())
+    nscales = int(sc.sum().item())
+    dq = ncodes / nq_tot
+    log(f"FP8-view delta leg: {nq_tot} codes, {ncodes} changed ({100 * dq:.3f}%), {nscales} scales changed")
+    a_delta = 2 * nq_tot + 8 * ns_tot + 5 * ncodes + 8 * nscales
+    a_apply = 6 * ncodes + 12 * nscales
+    out = {"fp8_view_delta": _leg(t_delta, len(chunks), a_delta, changed_codes_fraction=round(dq, 6),
+                                  changed_scales=nscales, codes=nq_tot,
+                                  checked="apply(quant(old), delta) == quant(new) on every chunk"),
+           "fp8_view_apply": _leg(t_apply, len(chunks), a_apply)}
+    if sample is not None:  # the CPU baseline of this leg
+        import numpy as np
+
+        import oracle
+
+        ones = np.ones(1, np.float32)
+        t = time.perf_counter()
+        oracle.fp8_delta(sample[0], sample[1], ones, ones)
+        secs = time.perf_counter() - t
+        out["fp8_view_delta"]["cpu_baseline"] = {
+            "kind": "oracle", "GBps": round(2 * sample[0].size / secs / 1e9, 3), "cores": 1,
+            "sample": f"{sample[0].size} codes of chunk 1, {secs:.2f} s"}
+    return out
+
+
+LOCO_WORKLOAD = 6
+
+
+def loco_leg(pulse, dev, with_oracle):
+    """PULSELoCo gate over a Qwen2.5-7B-shaped FP32 checkpoint: round 1 (untimed)
+    fills the error-feedback buffer, round 2 is timed, chunk by chunk, with the
+    receiver's accumulation of each chunk's patch.  The round-2 entries of the
+    first 2^22 elements are checked against the gate's defining properties
+    (torch's float32 add and BF16 cast on the host copies)."""
+    import torch
+
+    import workload
+
+    specs = workload.qwen25_7b_specs()
+    n = workload.total_numel(specs)
+    chunks, offs = build_plan(specs, layers_per_chunk=8)
+    theta = torch.empty(n, dtype=torch.float32, device=dev)
+    delta = torch.empty(n, dtype=torch.float32, device=dev)
+    resid = torch.zeros(n, dtype=torch.float32, device=dev)
+    acc = torch.zeros(n, dtype=torch.float32, device=dev)
+    maxc = max(e - s for s, e, _ in chunks)
+    cap = maxc // 2
+    idx = torch.empty(cap, dtype=torch.int32, device=dev)
+    val = torch.empty(cap, dtype=torch.float32, device=dev)
+    cnt = torch.zeros(len(chunks), dtype=torch.int64, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = pulse.workspace(pulse.PULSE_OP_LOCO_GATE, maxc, 0, dev)
+    tmp = torch.empty(max(s.numel for s in specs), dtype=torch.float32, device=dev)
+    for ti, s in enumerate(specs):
+        workload.fill_init(theta[offs[ti]: offs[ti] + s.numel], LOCO_WORKLOAD, ti, s.kind)
+    log(f"LoCo leg: {n} params, checkpoint drawn")
+    for rnd in (1, 2):
+        for ti, s in enumerate(specs):
+            workload.pseudo_gradient(delta[offs[ti]: offs[ti] + s.numel], LOCO_WORKLOAD, ti, rnd, tmp=tmp)
+        torch.cuda.synchronize()
+        log(f"LoCo leg: round {rnd} pseudo-gradient drawn")
+        if rnd == 1:
+            for k, (s0, e0, _) in enumerate(chunks):
+                pulse.pulse_loco_gate(theta[s0:e0], delta[s0:e0], resid[s0:e0], idx, val, cnt[k:k + 1], st, ws)
+            continue
+        chk = 1 << 22
+        host_in = (theta[:chk].cpu().numpy(), delta[:chk].cpu().numpy(), resid[:chk].cpu().numpy())
+        t_gate = t_acc = 0.0
+        first = None
+        for k, (s0, e0, _) in enumerate(chunks):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            ev[0].record()
+            pulse.pulse_loco_gate(theta[s0:e0], delta[s0:e0], resid[s0:e0], idx, val, cnt[k:k + 1], st, ws)
+            ev[1].record()
+            pulse.pulse_loco_accumulate(acc[s0:e0], idx, val, cnt[k:k + 1], st)
+            ev[2].record()
+            torch.cuda.synchronize()
+            t_gate += ev[0].elapsed_time(ev[1])
+            t_acc += ev[1].elapsed_time(ev[2])
+            if k == 0:
+                m0 = int(cnt[0].item())
+                first = (idx[:min(m0, chk)].cpu().numpy(), val[:min(m0, chk)].cpu().numpy(),
+                         resid[:chk].cpu().numpy())
+    del tmp
+    if int(st.item()) != 0:
+        raise SystemExit(f"LoCo leg: device status {int(st.item())}")
+    sent = int(cnt.sum().item())
+    dg = sent / n
+    out = {}
+    # properties of the first 2^22 elements (any size): the sent entries carry
+    # a = resid + delta and leave 0 behind, the rest keep a, and exactly the
+    # entries whose BF16 view a would move were sent
+    th, de, r0 = (torch.from_numpy(x) for x in host_in)
+    gi, gv, gr = (torch.from_numpy(x) for x in first)
+    a = r0 + de
+    vis = (th + a).to(torch.bfloat16).view(torch.int16) != th.to(torch.bfloat16).view(torch.int16)
+    ref_idx = torch.nonzero(vis).flatten().to(torch.int32)
+    kk = ref_idx.numel()
+    keep = torch.where(vis, torch.zeros_like(a), a)
+    if not (torch.equal(gi[:kk], ref_idx) and torch.equal(gv[:kk].view(torch.int32), a[vis].view(torch.int32))
+            and torch.equal(gr.view(torch.int32), keep.view(torch.int32)) and (gi.numel() == kk or int(gi[kk]) >= chk)):
+        raise SystemExit("LoCo leg: the first 2^22 elements break the gate's properties")
+    log(f"LoCo leg: {n} params, {sent} entries sent ({100 * dg:.3f}%)")
+    a_gate = 16 * n + 8 * sent     # read theta, delta, resid; write resid; write the entries
+    a_acc = 16 * sent              # read the entries, read + write acc at them
+    out["loco_gate"] = _leg(t_gate, len(chunks), a_gate, sent_fraction=round(dg, 6), params=n,
+                            workload="Qwen2.5-7B-shaped FP32 checkpoint, round 2 of H=8 local steps at lr 3e-6",
+                            checked="first 2^22 elements: sent = visible, values and buffer exact")
+    out["loco_accumulate"] = _leg(t_acc, len(chunks), a_acc)
+    if with_oracle:  # the CPU baseline of this leg
+        import oracle
+
+        t = time.perf_counter()
+        oracle.loco_gate(*host_in)
+        secs = time.perf_counter() - t
+        out["loco_gate"]["cpu_baseline"] = {"kind": "oracle", "GBps": round(16 * chk / secs / 1e9, 3), "cores": 1,
+                                            "sample": f"first {chk} elements of round 2, {secs:.3f} s"}
+    return out
+
+
 def cpu_baseline(specs, offs, W, b_old, frac):
-    """The oracle (plain single-threaded C) on layer 0 of the same workload: the
-    same five steps over the same host copies of the inputs."""
+    """The oracle (plain single-threaded C) on a bounded sample of the same
+    workload: the attention half of layer 0 (in_ln, q, k, v and their biases,
+    o, post_ln; about 63 M parameters), all five steps over host copies of the
+    same inputs, FP8 on the stacked [q;k;v] and on o.  `frac` < 1 shortens the
+    sample further (the FP8 step is then skipped)."""
     import numpy as np
 
     import oracle
 
     lay = [i for i, s in enumerate(specs) if s.name.startswith("l0.")]
-    s0, e0 = offs[lay[0]], offs[lay[-1]] + specs[lay[-1]].numel
-    m = int((e0 - s0) * frac) // 8 * 8
+    last = next(i for i in lay if specs[i].name == "l0.post_ln")
+    lay = [i for i in lay if i <= last]
+    s0, e0 = offs[lay[0]], offs[last] + specs[last].numel
+    m = int((e0 - s0) * min(frac, 1.0)) // 8 * 8
     w = W[s0:s0 + m].cpu().numpy()
     bo = b_old[s0:s0 + m].cpu().numpy().view(np.uint16)
     groups = []
     if frac >= 1.0:
         for g in quant_groups(specs, lay):
             groups.append([(offs[i] - s0, specs[i].shape) for i in g])
+    log(f"oracle sample: {m} params")
     t = time.perf_counter()
     r = oracle.cast_diff(w, bo, want_mask=False)
     recv, _ = oracle.apply_patch(bo, r["idx"], r["val"])
+    log(f"oracle cast+diff+compact and apply done ({time.perf_counter() - t:.1f} s)")
     for g in groups:
         oracle.fp8_block_quant([recv[o:o + sh[0] * sh[1]].reshape(sh) for o, sh in g])
+    log(f"oracle FP8 done ({time.perf_counter() - t:.1f} s)")
     enc = oracle.lz4_encode_blocks(bo, BLOCK, src_xor=r["b_new"])
     oracle.lz4_decode_blocks(enc["payload"], enc["offsets"], enc["sizes"], recv, mode=1)
     secs = time.perf_counter() - t
+    log(f"oracle LZ4 done ({secs:.1f} s)")
     return {"value": round(2 * m / secs / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"layer 0 of the same workload ({m} params{'' if frac >= 1 else ', FP8 step skipped'}), "
-                      f"all five steps, {secs:.1f} s"}
+            "sample": f"attention half of layer 0 of the same workload ({m} params"
+                      f"{'' if frac >= 1 else ', FP8 step skipped'}), all five steps, {secs:.1f} s"}
 
 
 if __name__ == "__main__":

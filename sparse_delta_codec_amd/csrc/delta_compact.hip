@@ -12,20 +12,20 @@
 //    adding it to the shared checkpoint changes that entry's BF16 view; the
 //    rest stays in the buffer for the next round.
 //
-// Same scheme as the BF16 cast/diff kernel: a persistent cooperative grid of
-// 256-thread workgroups walks 16384-element tiles in a static order; pass 1
-// streams a tile with 16-byte loads and keeps the flags (64 per lane) and the
-// values in registers; a one-wave decoupled look-back over epoch-tagged status
-// words gives the tile's first entry; pass 2 ranks the flagged elements with
-// ballots, stages each wave's entries in LDS at their ranks and writes them
-// with coalesced stores.
+// One 256-thread workgroup per 16384-element tile; the tile is a ticket taken
+// with one atomic when the workgroup starts, so a tile only ever waits for
+// tiles whose workgroups are already running, whatever the device's residency
+// (no co-residency assumption).  Pass 1 streams the tile with 16-byte loads
+// and keeps the flags (64 per lane) and the values in registers; a one-wave
+// decoupled look-back over epoch-tagged status words gives the tile's first
+// entry; pass 2 ranks the flagged elements with ballots, stages each wave's
+// entries in LDS at their ranks and writes them with coalesced stores.
 //
 // Lane l of wave w holds elements wbase + g*64*K + K*l + k (g < G, k < K,
 // G*K = 64): K = 16 bytes per group for the codes, K = 4 words otherwise.
 #include <type_traits>
 
 #include "device.hpp"
-#include "launch.hpp"
 
 namespace pulse {
 
@@ -215,10 +215,9 @@ __device__ __forceinline__ void dc_flush(const DcArgs &a, const int32_t *sbi, co
 }
 
 template <int M, bool FULL>
-__device__ __forceinline__ void dc_tile(const DcArgs &a, uint32_t tile, uint32_t ep, DcShared<M> &sh) {
+__device__ __forceinline__ void dc_tile(const DcArgs &a, uint32_t tile, uint32_t tag, DcShared<M> &sh) {
     constexpr int K = DcShape<M>::K, G = DcShape<M>::G;
     const int w = wave_id(), l = lane_id();
-    const uint32_t tag = epoch_tag(ep);
     const int64_t wbase = (int64_t)tile * DC_TILE + (int64_t)w * DC_WAVE_ELEMS;
     uint32_t v[M == DC_U8 ? 16 : 64];
     uint64_t flags = dc_pass1<M, FULL>(a, wbase, l, v);
@@ -245,10 +244,7 @@ __device__ __forceinline__ void dc_tile(const DcArgs &a, uint32_t tile, uint32_t
         if (l == 0) {
             if (failed) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
             sh.prefix = pre;
-            if (tile == a.ntiles - 1) {
-                *a.d_count = (int64_t)(pre + tile_count);
-                ws_epoch_advance(a.hdr, ep);
-            }
+            if (tile == a.ntiles - 1) *a.d_count = (int64_t)(pre + tile_count);
             if ((int64_t)(pre + tile_count) > a.cap) or_agent32(a.d_status, 1u /*PULSE_DS_CAPACITY*/);
         }
     }
@@ -309,14 +305,22 @@ __device__ __forceinline__ void dc_tile(const DcArgs &a, uint32_t tile, uint32_t
 
 template <int M>
 __global__ __launch_bounds__(DC_THREADS) void k_delta_compact(DcArgs a) {
-    __shared__ uint32_t s_ep;
+    __shared__ uint32_t s_tile, s_tag;
     __shared__ DcShared<M> sh;
-    if (threadIdx.x == 0) s_ep = ws_epoch(a.hdr);
+    if (threadIdx.x == 0) {
+        uint32_t tile, tag;
+        ws_begin(a.hdr, a.ntiles, &tile, &tag);
+        s_tile = tile;
+        s_tag = tag;
+    }
     __syncthreads();
-    const uint32_t ep = s_ep;
-    const uint32_t nfull = (uint32_t)(a.n / DC_TILE);
-    for (uint32_t tile = blockIdx.x; tile < nfull; tile += gridDim.x) dc_tile<M, true>(a, tile, ep, sh);
-    if (nfull < a.ntiles && nfull % gridDim.x == blockIdx.x) dc_tile<M, false>(a, nfull, ep, sh);
+    const uint32_t tile = s_tile, tag = s_tag;
+    if (tile >= a.ntiles) {  // inconsistent workspace state: touch nothing
+        if (threadIdx.x == 0) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
+        return;
+    }
+    if (tile < (uint32_t)(a.n / DC_TILE)) dc_tile<M, true>(a, tile, tag, sh);
+    else dc_tile<M, false>(a, tile, tag, sh);
 }
 
 // ---- scatter of (index, value) entries: overwrite (codes, scales) or add ----
@@ -384,8 +388,8 @@ int launch_delta_compact(const void *x0, const void *x1, float *resid, int64_t n
     a.status = reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + sizeof(WsHeader));
     const int64_t ntiles = (n + DC_TILE - 1) / DC_TILE;
     a.ntiles = (uint32_t)ntiles;
-    return launch_persistent(reinterpret_cast<const void *>(&k_delta_compact<M>), ntiles, DC_THREADS, 0, a,
-                             stream);
+    k_delta_compact<M><<<dim3((unsigned)ntiles), dim3(DC_THREADS), 0, stream>>>(a);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
 }  // namespace pulse
@@ -398,7 +402,7 @@ extern "C" size_t pulse_delta_compact_ws_bytes(int64_t n) {
 }
 
 // FP8-view delta: the codes, then the scales, on one workspace (the second
-// launch starts after the first has advanced the workspace's epoch).
+// launch starts after the first has re-armed the workspace for the next call).
 extern "C" int pulse_launch_fp8_delta(const uint8_t *codes_old, const uint8_t *codes_new, int64_t n_codes,
                                       const float *scales_old, const float *scales_new, int64_t n_scales,
                                       int32_t *code_idx, uint8_t *code_val, int64_t code_cap,

@@ -14,6 +14,9 @@ Workloads (model shapes and learning rate):
   c4  the first 16e9 elements of c2's tensor order (XOR-mask path)
   c5  Kimi-K2-shaped MoE layer share: 384 experts x {gate, up [2048, 7168],
       down [7168, 2048]} plus q, k, v [8192, 7168]
+  6   trainer-to-trainer rounds on a Qwen2.5-7B-shaped set: FP32 checkpoint
+      drawn like the others, and per round a pseudo-gradient, the sum of H
+      synthetic local steps -lr * clip(u, -3, 3)
 The step is w' = fl32(w - fl32(lr * clip(u, -3, 3))), u ~ N(0, 1) per step,
 lr = 3e-6 (the RL learning rate the PULSE technical summary quotes, section
 "Osservazione Centrale").  Matrices and biases start N(0, 0.02); norm weights
@@ -74,6 +77,12 @@ def qwen25_32b_specs(layers=64):
 
 def llama3_8b_specs(layers=32):
     return _decoder_specs(layers, 4096, 32, 8, 128, 14336, 128256, False)
+
+
+def qwen25_7b_specs(layers=28):
+    """Qwen2.5-7B shape (one of the models the pages' PULSELoCo runs use): hidden
+    3584, 28 q / 4 kv heads x 128, MLP 18944, vocab 152064, q/k/v biases."""
+    return _decoder_specs(layers, 3584, 28, 4, 128, 18944, 152064, True)
 
 
 def kimi_k2_layer_specs(experts=384):
@@ -161,3 +170,24 @@ def apply_step(w, workload: int, tensor: int, step: int, lr: float = LR, tmp=Non
     u.clamp_(-3.0, 3.0).mul_(lr)
     w.sub_(u)
     return w
+
+
+def pseudo_gradient(out, workload: int, tensor: int, rnd: int, local_steps: int = 8, lr: float = LR,
+                    tmp=None):
+    """Write into `out` (float32 torch tensor) the synthetic pseudo-gradient of
+    round `rnd` >= 1: the sum, in float32 and in order, of `local_steps` updates
+    -lr * clip(u, -3, 3), u ~ N(0, 1) drawn with step numbers
+    (rnd - 1) * local_steps + 1 ... rnd * local_steps."""
+    import torch
+
+    out.zero_()
+    for h in range(local_steps):
+        g = torch.Generator(device=out.device)
+        g.manual_seed(seed_of(workload, tensor, (rnd - 1) * local_steps + h + 1))
+        u = torch.empty(out.shape, device=out.device, dtype=torch.float32) if tmp is None else \
+            tmp.view(-1)[: out.numel()].view(out.shape)
+        torch.randn(out.shape, generator=g, device=out.device, dtype=torch.float32, out=u)
+        u.clamp_(-3.0, 3.0).mul_(lr)
+        out.sub_(u)
+    return out
+
