@@ -52,6 +52,11 @@ def lib():
         L.oracle_fp8_apply_delta.argtypes = [_P, _I64, _P, _I64, _P, _P, _I64, _P, _P, _I64, _P]
         L.oracle_loco_gate.argtypes = [_P, _P, _P, _I64, _P, _P, _I64, _P, _P]
         L.oracle_loco_accumulate.argtypes = [_P, _I64, _P, _P, _I64, _P]
+        L.oracle_patch_packed_bytes.argtypes = [_I64]
+        L.oracle_patch_packed_bytes.restype = _I64
+        L.oracle_patch_pack.argtypes = [_P, _P, _I64, _P]
+        L.oracle_patch_unpack.argtypes = [_P, _I64, _P, _P]
+        L.oracle_patch_unpack.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -258,3 +263,30 @@ def loco_accumulate(acc, idx, val):
     status = np.zeros(1, np.uint32)
     lib().oracle_loco_accumulate(_ptr(a), a.size, _ptr(i), _ptr(v), i.size, _ptr(status))
     return a, int(status[0])
+
+
+PACK_GROUP = 65536
+
+
+def patch_pack(idx, val):
+    """Gap + byte-plane form of an ascending patch (uint8 array, whole groups)."""
+    i, v = _c(idx, np.int32), _c(val, np.uint16)
+    assert i.size == v.size
+    out = np.empty(max(int(lib().oracle_patch_packed_bytes(i.size)), 1), np.uint8)
+    lib().oracle_patch_pack(_ptr(i), _ptr(v), i.size, _ptr(out))
+    return out[: int(lib().oracle_patch_packed_bytes(i.size))]
+
+
+def patch_unpack(packed, count):
+    """Returns (idx, val), or None when the packed data overflows int32 indices."""
+    p = _c(packed, np.uint8)
+    idx, val = np.empty(max(count, 1), np.int32), np.empty(max(count, 1), np.uint16)
+    rc = lib().oracle_patch_unpack(_ptr(p), count, _ptr(idx), _ptr(val))
+    return None if rc else (idx[:count], val[:count])
+
+
+def patch_compress(idx, val, block_bytes=65536):
+    """The whole sender side: pack, then the canonical LZ4 block encoding."""
+    packed = patch_pack(idx, val)
+    return packed, lz4_encode_blocks(packed, block_bytes)
+

@@ -22,6 +22,10 @@
  *   oracle_fp8_delta, oracle_fp8_apply_delta
  *                           pinned: numpy flatnonzero over the codes and the scale
  *                           bit patterns; apply(quant(old), delta) == quant(new).
+ *   oracle_patch_pack, oracle_patch_unpack
+ *                           pinned: numpy diff + little-endian byte views; round
+ *                           trips; constant planes give 6 x 267 B (the closed form
+ *                           of a constant 64 KiB block); index overflow rejected.
  *   oracle_loco_gate, oracle_loco_accumulate
  *                           pinned: torch's float32 add and BF16 cast, the exact
  *                           conservation resid' + sent == resid + delta, closed
@@ -504,3 +508,62 @@ void oracle_loco_accumulate(float *acc, int64_t n, const int32_t *idx, const flo
         acc[i] = acc[i] + val[k];
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* f2  compression of the patch stream.  The sparse patches are compressed    */
+/* further with a generic lossless codec [PULSE summary, "1. PULSESync" --    */
+/* Compressione].  Reading: the codec is this codec's LZ4 block format (the   */
+/* canonical parse, 64 KiB blocks), and the patch is first put in a form whose */
+/* redundancy a run-based parse can see: each index becomes its gap to the    */
+/* previous one, gap = idx[k] - idx[k-1] - 1 (idx[-1] = -1), and every group   */
+/* of ORACLE_PACK_GROUP entries is laid out as six byte planes (gap bytes 0-3, */
+/* value bytes 0-1, little-endian), each plane ORACLE_PACK_GROUP bytes long;  */
+/* entries past the count in the last group are zero.                         */
+/* ------------------------------------------------------------------------ */
+int64_t oracle_patch_packed_bytes(int64_t count)
+{
+    return (count + ORACLE_PACK_GROUP - 1) / ORACLE_PACK_GROUP * 6 * ORACLE_PACK_GROUP;
+}
+
+void oracle_patch_pack(const int32_t *idx, const uint16_t *val, int64_t count, uint8_t *packed)
+{
+    const int64_t G = ORACLE_PACK_GROUP;
+    int64_t groups = (count + G - 1) / G;
+    for (int64_t g = 0; g < groups; ++g) {
+        uint8_t *base = packed + g * 6 * G;
+        for (int64_t j = 0; j < G; ++j) {
+            int64_t k = g * G + j;
+            uint32_t gap = 0;
+            uint16_t v = 0;
+            if (k < count) {
+                int64_t prev = k > 0 ? (int64_t)idx[k - 1] : -1;
+                gap = (uint32_t)((int64_t)idx[k] - prev - 1);
+                v = val[k];
+            }
+            for (int p = 0; p < 4; ++p) base[p * G + j] = (uint8_t)(gap >> (8 * p));
+            base[4 * G + j] = (uint8_t)(v & 0xFFu);
+            base[5 * G + j] = (uint8_t)(v >> 8);
+        }
+    }
+}
+
+/* Inverse of oracle_patch_pack: idx[k] = idx[k-1] + 1 + gap.  Returns 0, or -1
+ * when an index would pass INT32_MAX (such data cannot come from a pack). */
+int oracle_patch_unpack(const uint8_t *packed, int64_t count, int32_t *idx, uint16_t *val)
+{
+    const int64_t G = ORACLE_PACK_GROUP;
+    int64_t prev = -1;
+    for (int64_t k = 0; k < count; ++k) {
+        const uint8_t *base = packed + (k / G) * 6 * G;
+        int64_t j = k % G;
+        uint32_t gap = 0;
+        for (int p = 0; p < 4; ++p) gap |= (uint32_t)base[p * G + j] << (8 * p);
+        int64_t i = prev + 1 + (int64_t)gap;
+        if (i > 2147483647LL) return -1;
+        idx[k] = (int32_t)i;
+        val[k] = (uint16_t)(base[4 * G + j] | (base[5 * G + j] << 8));
+        prev = i;
+    }
+    return 0;
+}
+

@@ -33,6 +33,7 @@
 #define ORACLE_CAPACITY 1u
 #define ORACLE_BADINDEX 2u
 #define ORACLE_CORRUPT 4u
+#define ORACLE_PACK_GROUP 65536
 
 #ifdef __cplusplus
 extern "C" {
@@ -124,6 +125,12 @@ void oracle_loco_gate(const float *theta, const float *delta, float *resid, int6
 /* f3: acc[idx[k]] += val[k] (float32) for k < count. */
 void oracle_loco_accumulate(float *acc, int64_t n, const int32_t *idx, const float *val,
                             int64_t count, uint32_t *status);
+/* f2: bytes of the packed form of a patch of `count` entries (whole groups). */
+int64_t oracle_patch_packed_bytes(int64_t count);
+/* f2: gaps and byte planes, ORACLE_PACK_GROUP entries per group (see oracle.c). */
+void oracle_patch_pack(const int32_t *idx, const uint16_t *val, int64_t count, uint8_t *packed);
+/* f2: inverse; 0, or -1 when an index would pass INT32_MAX. */
+int oracle_patch_unpack(const uint8_t *packed, int64_t count, int32_t *idx, uint16_t *val);
 #ifdef __cplusplus
 }
 #endif

@@ -195,3 +195,69 @@ def test_accumulate_matches_numpy():
     assert st == 0 and np.array_equal(u32(ours), u32(ref))
     _, st = oracle.loco_accumulate(acc, np.array([n], np.int32), np.array([1.0], np.float32))
     assert st == oracle.BADINDEX
+
+
+# ---- patch-stream compression ---------------------------------------------------------
+def numpy_pack(idx, val, G=65536):
+    """The packed form built with numpy: np.diff for the gaps, little-endian byte
+    views for the planes."""
+    m = idx.size
+    groups = (m + G - 1) // G
+    gaps = np.zeros(groups * G, np.uint32)
+    vals = np.zeros(groups * G, np.uint16)
+    gaps[:m] = (np.diff(idx.astype(np.int64), prepend=-1) - 1).astype(np.uint32)
+    vals[:m] = val
+    gb = gaps.view(np.uint8).reshape(groups, G, 4)
+    vb = vals.view(np.uint8).reshape(groups, G, 2)
+    planes = np.concatenate([gb.transpose(0, 2, 1), vb.transpose(0, 2, 1)], axis=1)  # [groups, 6, G]
+    return planes.reshape(-1)
+
+
+def random_patch(m, n, seed):
+    rng = np.random.default_rng(seed)
+    idx = np.sort(rng.choice(n, m, replace=False)).astype(np.int32)
+    val = rng.integers(0, 1 << 16, m, dtype=np.uint16)
+    return idx, val
+
+
+def test_pack_matches_numpy_and_round_trips():
+    for m, n, seed in [(0, 10, 1), (1, 1, 2), (5, 2 ** 31 - 1, 3), (65535, 10 ** 6, 4), (65536, 65536, 5),
+                       (65537, 2 * 10 ** 6, 6), (200_000, 2 ** 31 - 1, 7), (150_000, 1_900_000, 8)]:
+        idx, val = random_patch(m, n, seed)
+        p = oracle.patch_pack(idx, val)
+        assert np.array_equal(p, numpy_pack(idx, val)), (m, n)
+        back = oracle.patch_unpack(p, m)
+        assert back is not None and np.array_equal(back[0], idx) and np.array_equal(back[1], val)
+
+
+def test_pack_closed_forms():
+    """Consecutive indices from 0 with one value: every plane of the group is a
+    constant 64 KiB block, whose canonical LZ4 encoding is 267 bytes (pinned in
+    test_oracle_lz4), so a full group compresses to 6 * 267 bytes."""
+    m = 65536
+    idx = np.arange(m, dtype=np.int32)
+    val = np.full(m, 0x3F80, np.uint16)
+    packed, enc = oracle.patch_compress(idx, val)
+    assert np.all(packed[: 4 * m] == 0) and np.all(packed[4 * m: 5 * m] == 0x80) and np.all(packed[5 * m:] == 0x3F)
+    assert enc["total"] == 6 * 267
+
+
+def test_unpack_rejects_index_overflow():
+    p = oracle.patch_pack(np.array([2 ** 31 - 2], np.int32), np.array([1], np.uint16))
+    assert oracle.patch_unpack(p, 1)[0][0] == 2 ** 31 - 2
+    p[0:4 * 65536:65536] = 0xFF  # gap 2^32 - 1
+    assert oracle.patch_unpack(p, 1) is None
+
+
+def test_compressed_patch_round_trip_on_the_c1_step():
+    """The whole path on the C1 step: cast/diff/compact, pack, LZ4 encode, LZ4
+    decode, unpack gives the patch back, smaller than the raw 6 B per entry."""
+    w0, w1 = workload.c1_masters()
+    r = oracle.cast_diff(w1, oracle.cast_bf16(w0), want_mask=False)
+    packed, enc = oracle.patch_compress(r["idx"], r["val"])
+    dec, st = oracle.lz4_decode_blocks(enc["payload"], enc["offsets"], enc["sizes"],
+                                       np.zeros(packed.size, np.uint8), mode=0)
+    assert st == 0 and np.array_equal(dec, packed)
+    back = oracle.patch_unpack(dec, r["count"])
+    assert np.array_equal(back[0], r["idx"]) and np.array_equal(back[1], r["val"])
+    assert enc["total"] < 6 * r["count"] * 0.6
