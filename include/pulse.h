@@ -81,6 +81,7 @@ extern "C" {
 #define PULSE_OP_LZ4_DECODE 4 /* n = number of blocks, aux = payload bytes         */
 #define PULSE_OP_FP8_DELTA 5  /* n = max(code count, scale count)                 */
 #define PULSE_OP_LOCO_GATE 6  /* n = element count                               */
+#define PULSE_OP_PATCH_UNPACK 7 /* n = patch entries                            */
 
 /* Bytes of workspace the op needs for the given size (0 if it needs none).
  * A workspace serves any number of calls of the op it was sized for, of any
@@ -299,6 +300,37 @@ int pulse_loco_gate(const float *theta, const float *delta, float *resid, int64_
 int pulse_loco_accumulate(float *acc, int64_t n, const int32_t *idx, const float *val,
                           const int64_t *d_count, int64_t max_count, uint32_t *d_status,
                           hipStream_t stream);
+
+/* ---- next: compression of the patch stream ---------------------------------
+ * The sparse patches are compressed further with a generic lossless codec
+ * ([PULSE summary] "1. PULSESync", Compressione).  Here the codec is this
+ * library's LZ4 block format (lz4_encode_blocks / lz4_decode_blocks with
+ * 65536-byte blocks), whose canonical parse only finds runs of one byte, so
+ * the patch is first packed: each index becomes its gap to the previous one
+ * (gap = idx[k] - idx[k-1] - 1, idx[-1] = -1) and every group of 65536
+ * entries becomes six 64 KiB byte planes (gap bytes 0-3, value bytes 0-1,
+ * little-endian); entries past the count in the last group are zero.  Each
+ * plane is one LZ4 block; the high gap planes compress to almost nothing.
+ *
+ * Bytes of the packed form of `count` entries (whole groups). */
+int64_t patch_packed_bytes(int64_t count);
+
+/*   idx, val   [count] ascending int32 positions and BF16 values (read),
+ *              16-byte aligned (a pulse_cast_diff / pulse_compact patch).
+ *   count      entries, host value, 0 .. 2^31.
+ *   packed     [patch_packed_bytes(count)] (written), 16-byte aligned. */
+int patch_pack(const int32_t *idx, const uint16_t *val, int64_t count, uint8_t *packed,
+               hipStream_t stream);
+
+/* Inverse of patch_pack (after lz4_decode_blocks in store mode): idx[k] is the
+ * running sum of gap + 1, less one, over the whole patch.
+ *   packed     [patch_packed_bytes(count)] (read).
+ *   idx, val   [count] (written), 16-byte aligned.
+ *   d_status   PULSE_DS_CORRUPT when a gap or an index passes 2^31 - 1 (data
+ *              that no pack produces); the indices are then unspecified.
+ *   ws         pulse_workspace_bytes(PULSE_OP_PATCH_UNPACK, count, 0). */
+int patch_unpack(const uint8_t *packed, int64_t count, int32_t *idx, uint16_t *val,
+                 uint32_t *d_status, void *ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

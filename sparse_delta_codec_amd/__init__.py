@@ -19,6 +19,7 @@ __all__ = [
     "lz4_encode_blocks", "lz4_decode_blocks", "fp8_block_quant", "lz4_payload_bound", "lib_path",
     "PULSE_OP_FP8_DELTA", "PULSE_OP_LOCO_GATE", "fp8_view_delta", "fp8_view_apply",
     "pulse_loco_gate", "pulse_loco_accumulate",
+    "PULSE_OP_PATCH_UNPACK", "patch_packed_bytes", "patch_pack", "patch_unpack",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -39,6 +40,7 @@ PULSE_OP_LZ4_ENCODE = 3
 PULSE_OP_LZ4_DECODE = 4
 PULSE_OP_FP8_DELTA = 5
 PULSE_OP_LOCO_GATE = 6
+PULSE_OP_PATCH_UNPACK = 7
 
 _P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
 _lib.pulse_version.restype = ctypes.c_char_p
@@ -58,7 +60,11 @@ _lib.fp8_view_delta.argtypes = [_P, _P, _I64, _P, _P, _I64, _P, _P, _I64, _P, _P
 _lib.fp8_view_apply.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _I64, _P, _P, _P, _I64, _P, _P]
 _lib.pulse_loco_gate.argtypes = [_P, _P, _P, _I64, _P, _P, _I64, _P, _P, _P, _SZ, _P]
 _lib.pulse_loco_accumulate.argtypes = [_P, _I64, _P, _P, _P, _I64, _P, _P]
-for _f in ("pulse_workspace_init", "pulse_cast_diff", "pulse_compact", "pulse_apply_patch",
+_lib.patch_packed_bytes.argtypes = [_I64]
+_lib.patch_packed_bytes.restype = _I64
+_lib.patch_pack.argtypes = [_P, _P, _I64, _P, _P]
+_lib.patch_unpack.argtypes = [_P, _I64, _P, _P, _P, _P, _SZ, _P]
+for _f in ("patch_pack", "patch_unpack", "pulse_workspace_init", "pulse_cast_diff", "pulse_compact", "pulse_apply_patch",
            "xor_mask_apply", "lz4_encode_blocks", "lz4_decode_blocks", "fp8_block_quant",
            "fp8_view_delta", "fp8_view_apply", "pulse_loco_gate", "pulse_loco_accumulate"):
     getattr(_lib, _f).restype = ctypes.c_int
@@ -310,4 +316,27 @@ def pulse_loco_accumulate(acc, idx, val, d_count, d_status, max_count=None, stre
         _dev(acc, "acc", torch.float32), acc.numel(), _dev(idx, "idx", torch.int32),
         _dev(val, "val", torch.float32), _dev(d_count, "d_count", torch.int64), max_count,
         _dev(d_status, "d_status", torch.int32), _stream(stream)), "pulse_loco_accumulate")
+
+
+def patch_packed_bytes(count: int) -> int:
+    return int(_lib.patch_packed_bytes(count))
+
+
+def patch_pack(idx, val, count, packed, stream=None):
+    """Gap + byte-plane form of the first `count` entries of a patch."""
+    _need(idx, 4 * count, "idx")
+    _need(val, 2 * count, "val")
+    _need(packed, patch_packed_bytes(count), "packed")
+    _check(_lib.patch_pack(_dev(idx, "idx", torch.int32), _dev(val, "val", _U16), count,
+                           _dev(packed, "packed", torch.uint8), _stream(stream)), "patch_pack")
+
+
+def patch_unpack(packed, count, idx, val, d_status, ws, stream=None):
+    _need(packed, patch_packed_bytes(count), "packed")
+    _need(idx, 4 * count, "idx")
+    _need(val, 2 * count, "val")
+    wsp, wsb = _ws(ws)
+    _check(_lib.patch_unpack(_dev(packed, "packed", torch.uint8), count, _dev(idx, "idx", torch.int32),
+                             _dev(val, "val", _U16), _dev(d_status, "d_status", torch.int32), wsp, wsb,
+                             _stream(stream)), "patch_unpack")
 

@@ -15,7 +15,8 @@ LIB = os.path.join(HERE, "libpulse.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 SOURCES = ["capi.cpp", "util.hip", "cast_diff.hip", "apply.hip", "lz4_encode.hip", "lz4_decode.hip",
-           "fp8_quant.hip", "delta_compact.hip"]
+           "fp8_quant.hip", "delta_compact.hip",
+           "patch_pack.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

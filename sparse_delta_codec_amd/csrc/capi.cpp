@@ -35,6 +35,10 @@ int pulse_launch_loco_gate(const float *, const float *, float *, int64_t, int32
                            uint32_t *, void *, hipStream_t);
 int pulse_launch_loco_accumulate(float *, int64_t, const int32_t *, const float *, const int64_t *, int64_t,
                                  uint32_t *, hipStream_t);
+size_t pulse_patch_unpack_ws_bytes(int64_t count);
+int64_t pulse_patch_packed_bytes_impl(int64_t count);
+int pulse_launch_patch_pack(const int32_t *, const uint16_t *, int64_t, uint8_t *, hipStream_t);
+int pulse_launch_patch_unpack(const uint8_t *, int64_t, int32_t *, uint16_t *, uint32_t *, void *, hipStream_t);
 int pulse_launch_fill_zero(void *, size_t, hipStream_t);
 int pulse_launch_write_count(int64_t *, int64_t, hipStream_t);
 }
@@ -77,6 +81,7 @@ size_t pulse_workspace_bytes(int op, int64_t n, int64_t aux) {
         return pulse_lz4_decode_ws_bytes(n, aux);
     case PULSE_OP_FP8_DELTA:
     case PULSE_OP_LOCO_GATE: return pulse_delta_compact_ws_bytes(n);
+    case PULSE_OP_PATCH_UNPACK: return pulse_patch_unpack_ws_bytes(n);
     default: return 0;
     }
 }
@@ -241,6 +246,29 @@ int pulse_loco_accumulate(float *acc, int64_t n, const int32_t *idx, const float
     if (n > kMaxIndexed + 1) return PULSE_ERANGE;
     if (max_count == 0) return PULSE_OK;
     return pulse_launch_loco_accumulate(acc, n, idx, val, d_count, max_count, d_status, stream);
+}
+
+int64_t patch_packed_bytes(int64_t count) {
+    if (count < 0) return 0;
+    return pulse_patch_packed_bytes_impl(count);
+}
+
+int patch_pack(const int32_t *idx, const uint16_t *val, int64_t count, uint8_t *packed, hipStream_t stream) {
+    if (!idx || !val || !packed || count < 0) return PULSE_EINVAL;
+    if (!aligned16(idx) || !aligned16(val) || !aligned16(packed)) return PULSE_EALIGN;
+    if (count > kMaxIndexed + 1) return PULSE_ERANGE;
+    if (count == 0) return PULSE_OK;
+    return pulse_launch_patch_pack(idx, val, count, packed, stream);
+}
+
+int patch_unpack(const uint8_t *packed, int64_t count, int32_t *idx, uint16_t *val, uint32_t *d_status, void *ws,
+                 size_t ws_bytes, hipStream_t stream) {
+    if (!packed || !idx || !val || !d_status || count < 0) return PULSE_EINVAL;
+    if (!aligned16(idx) || !aligned16(val) || !aligned16(packed)) return PULSE_EALIGN;
+    if (count > kMaxIndexed + 1) return PULSE_ERANGE;
+    if (count == 0) return PULSE_OK;
+    if (!ws || ws_bytes < pulse_patch_unpack_ws_bytes(count)) return PULSE_EWORKSPACE;
+    return pulse_launch_patch_unpack(packed, count, idx, val, d_status, ws, stream);
 }
 
 }  // extern "C"

@@ -133,3 +133,23 @@ def test_next_rows_argument_errors(lib):
     assert acc(al, 10, None, al, al, 5, al, None) == EINVAL
     ws = lib.pulse_workspace_bytes
     assert ws(5, 16384, 0) == 256 + 8 and ws(6, 16385, 0) == 256 + 16
+
+
+def test_patch_pack_argument_errors(lib):
+    al = V(0x10000)
+    mis = V(0x10008)
+    pb = lib.patch_packed_bytes
+    pb.argtypes = [I64]
+    pb.restype = I64
+    assert pb(0) == 0 and pb(1) == 6 * 65536 and pb(65536) == 6 * 65536 and pb(65537) == 12 * 65536
+    pk = lib.patch_pack
+    pk.argtypes = [V, V, I64, V, V]
+    assert pk(None, al, 10, al, None) == EINVAL
+    assert pk(al, mis, 10, al, None) == EALIGN
+    assert pk(al, al, (1 << 31) + 1, al, None) == ERANGE
+    up = lib.patch_unpack
+    up.argtypes = [V, I64, V, V, V, V, ctypes.c_size_t, V]
+    assert up(al, 10, al, al, None, al, 1 << 20, None) == EINVAL
+    assert up(al, 100000, al, al, al, al, 8, None) == EWORKSPACE
+    ws = lib.pulse_workspace_bytes
+    assert ws(7, 65536, 0) == 256 + 8 and ws(7, 65537, 0) == 256 + 16

@@ -195,3 +195,83 @@ def test_loco_rounds_and_accumulate():
         assert np.array_equal(u32(host(R)), u32(r_host)), rnd
         assert np.array_equal(u32(host(A)), u32(a_host)), rnd
     assert int(host(st)[0]) == 0
+
+
+# ---- patch-stream compression -------------------------------------------------------
+def random_patch(m, n, seed):
+    rng = np.random.default_rng(seed)
+    idx = np.sort(rng.choice(n, m, replace=False)).astype(np.int32)
+    val = rng.integers(0, 1 << 16, m, dtype=np.uint16)
+    return idx, val
+
+
+PATCH_CASES = [(1, 1, 1), (3, 100, 2), (4, 10, 3), (1000, 2 ** 31 - 1, 4), (65535, 10 ** 6, 5),
+               (65536, 65536, 6), (65537, 3 * 10 ** 6, 7), (200_003, 2_400_000, 8), (140_000, 2 ** 31 - 1, 9)]
+
+
+@pytest.mark.parametrize("m,n,seed", PATCH_CASES)
+def test_patch_pack_and_unpack_match_oracle(m, n, seed):
+    idx, val = random_patch(m, n, seed)
+    nb = pulse.patch_packed_bytes(m)
+    P = zeros(nb, torch.uint8)
+    pulse.patch_pack(dev(idx), dev(val), m, P)
+    torch.cuda.synchronize()
+    ref = oracle.patch_pack(idx, val)
+    assert nb == ref.size and np.array_equal(host(P)[:nb], ref)
+    I, V, st = zeros(m, torch.int32), zeros(m, torch.int16), zeros(1, torch.int32)
+    ws = pulse.workspace(pulse.PULSE_OP_PATCH_UNPACK, m)
+    pulse.patch_unpack(dev(ref), m, I, V, st, ws)
+    torch.cuda.synchronize()
+    assert int(host(st)[0]) == 0
+    assert np.array_equal(host(I)[:m], idx) and np.array_equal(host(V, np.uint16)[:m], val)
+
+
+def test_patch_unpack_flags_index_overflow_and_reuses_workspace():
+    ws = pulse.workspace(pulse.PULSE_OP_PATCH_UNPACK, 300_000)
+    for it, (m, n, seed) in enumerate([(300_000, 10 ** 7, 1), (5, 50, 2), (70_000, 2 ** 31 - 1, 3)]):
+        idx, val = random_patch(m, n, seed)
+        p = oracle.patch_pack(idx, val)
+        I, V, st = zeros(m, torch.int32), zeros(m, torch.int16), zeros(1, torch.int32)
+        pulse.patch_unpack(dev(p), m, I, V, st, ws)
+        torch.cuda.synchronize()
+        assert int(host(st)[0]) == 0 and np.array_equal(host(I)[:m], idx), it
+    p = oracle.patch_pack(np.array([2 ** 31 - 2, 2 ** 31 - 1], np.int32), np.array([1, 2], np.uint16))
+    p[1] = 1  # second gap 1: index 2^31
+    I, V, st = zeros(2, torch.int32), zeros(2, torch.int16), zeros(1, torch.int32)
+    pulse.patch_unpack(dev(p), 2, I, V, st, ws)
+    torch.cuda.synchronize()
+    assert int(host(st)[0]) & pulse.PULSE_DS_CORRUPT
+
+
+def test_compressed_patch_round_trip_through_the_lz4_kernels():
+    """The sender's cast/diff/compact patch of the C1 step, packed and LZ4-encoded
+    on the GPU, equals the oracle's payload byte for byte; decoded and unpacked
+    on the GPU it is the patch again, and applying it rebuilds the new view."""
+    w0, w1 = workload.c1_masters()
+    b0 = oracle.cast_bf16(w0).reshape(-1)
+    r = oracle.cast_diff(w1, b0, want_mask=False)
+    m = r["count"]
+    nb = pulse.patch_packed_bytes(m)
+    P = zeros(nb, torch.uint8)
+    pulse.patch_pack(dev(r["idx"]), dev(r["val"]), m, P)
+    cap = pulse.lz4_payload_bound(nb)
+    payload = zeros(cap, torch.uint8)
+    nblk = nb // 65536
+    sizes, offs = zeros(nblk, torch.int32), zeros(nblk, torch.int64)
+    tot, st = zeros(1, torch.int64), zeros(1, torch.int32)
+    pulse.lz4_encode_blocks(P, payload, sizes, offs, tot, st, pulse.workspace(pulse.PULSE_OP_LZ4_ENCODE, nb, 65536))
+    torch.cuda.synchronize()
+    packed_ref, enc = oracle.patch_compress(r["idx"], r["val"])
+    t = int(host(tot)[0])
+    assert int(host(st)[0]) == 0 and t == enc["total"] and np.array_equal(host(payload)[:t], enc["payload"])
+    D = zeros(nb, torch.uint8)
+    pulse.lz4_decode_blocks(payload, offs, sizes, D, st, pulse.workspace(pulse.PULSE_OP_LZ4_DECODE, nblk, cap),
+                            mode=0, nbytes=nb, payload_bytes=cap)
+    I, V = zeros(m, torch.int32), zeros(m, torch.int16)
+    pulse.patch_unpack(D, m, I, V, st, pulse.workspace(pulse.PULSE_OP_PATCH_UNPACK, m))
+    B = dev(b0)
+    pulse.pulse_apply_patch(B, I, V, dev(np.array([m], np.int64)), st)
+    torch.cuda.synchronize()
+    assert int(host(st)[0]) == 0
+    assert np.array_equal(host(I)[:m], r["idx"]) and np.array_equal(host(V, np.uint16)[:m], r["val"])
+    assert np.array_equal(host(B, np.uint16), r["b_new"])
