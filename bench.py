@@ -49,8 +49,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-frac", type=float, default=1.0,
                    help="fraction of the oracle's sample (the attention half of layer 0) it times")
-    p.add_argument("--next", default="loco", choices=["none", "loco", "fp8", "all"],
-                   help="next-row legs measured after the timed steps (PULSELoCo gate; FP8-view deltas)")
+    p.add_argument("--next", default="loco,patch", help="next-row legs measured after the timed steps, comma "
+                   "separated: loco (PULSELoCo gate), patch (patch-stream compression), fp8 (FP8-view deltas), none")
     p.add_argument("--copy-probe-gib", type=float, default=0.0,
                    help="also run a plain device copy of this size (scale reference for HBM counters)")
     return p.parse_args()
@@ -341,16 +341,20 @@ def main():
         log("timing the oracle on the host")
         result["cpu_baseline"] = cpu_baseline(specs, offs, W, b_old, args.cpu_sample_frac)
 
-    if args.next != "none":
+    legs = set(x for x in args.next.split(",") if x and x != "none")
+    if legs:
         # the next rows, measured after (and outside) the timed steps
         nxt = {}
-        if args.next in ("fp8", "all"):
+        if "patch" in legs:
+            nxt.update(patch_stream_leg(pulse, chunks, W, b_old, stage, idx, val, cnt, status, ws_cd, dev,
+                                        not args.no_cpu_baseline))
+        if "fp8" in legs:
             nxt.update(fp8_view_leg(pulse, specs, chunks, offs, qplans, W, b_old, stage, dev,
                                     not args.no_cpu_baseline))
         del W, stage, b_recv, idx, val, payload, codes, scales
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
-        if args.next in ("loco", "all"):
+        if "loco" in legs:
             nxt.update(loco_leg(pulse, dev, not args.no_cpu_baseline))
         result["next_rows"] = nxt
     print(json.dumps(result), flush=True)
@@ -361,6 +365,84 @@ def _leg(ms, launches, alg_bytes, **extra):
     out = {"ms": round(ms, 3), "launches": launches, "alg_GB": round(alg_bytes / 1e9, 3),
            "GBps": round(alg_bytes / secs / 1e9, 1), "frac_hbm": round(alg_bytes / secs / PEAK_HBM, 4)}
     out.update(extra)
+    return out
+
+
+def patch_stream_leg(pulse, chunks, W, b_old, stage, idx, val, cnt, status, ws_cd, dev, with_oracle):
+    """Compression of the patch stream over the whole weight set: per chunk the
+    sender's patch (cast/diff/compact, untimed) is packed and LZ4-encoded (timed,
+    the sender's side), then LZ4-decoded and unpacked (timed, the receiver's
+    side); the unpacked patch must equal the original entry for entry."""
+    import numpy as np
+    import torch
+
+    cap = idx.numel()
+    nb = pulse.patch_packed_bytes(cap)
+    packed = torch.empty(nb, dtype=torch.uint8, device=dev)
+    back = torch.empty(nb, dtype=torch.uint8, device=dev)
+    pcap = pulse.lz4_payload_bound(nb)
+    payload = torch.empty(pcap, dtype=torch.uint8, device=dev)
+    nblk = nb // BLOCK
+    sizes = torch.empty(nblk, dtype=torch.int32, device=dev)
+    offs = torch.empty(nblk, dtype=torch.int64, device=dev)
+    tot = torch.zeros(len(chunks), dtype=torch.int64, device=dev)
+    idx2 = torch.empty_like(idx)
+    val2 = torch.empty_like(val)
+    ws_en = pulse.workspace(pulse.PULSE_OP_LZ4_ENCODE, nb, BLOCK, dev)
+    ws_de = pulse.workspace(pulse.PULSE_OP_LZ4_DECODE, nblk, pcap, dev)
+    ws_up = pulse.workspace(pulse.PULSE_OP_PATCH_UNPACK, cap, 0, dev)
+    t = {"pack": 0.0, "encode": 0.0, "decode": 0.0, "unpack": 0.0}
+    entries = 0
+    packed_total = 0
+    sample = None
+    for k, (s0, e0, _) in enumerate(chunks):
+        m = e0 - s0
+        pulse.pulse_cast_diff(W[s0:e0], b_old[s0:e0], stage[:m], None, idx, val, cnt[k:k + 1], status, ws_cd)
+        count = int(cnt[k].item())
+        pb = pulse.patch_packed_bytes(count)
+        nbk = pb // BLOCK
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        ev[0].record()
+        pulse.patch_pack(idx, val, count, packed)
+        ev[1].record()
+        pulse.lz4_encode_blocks(packed, payload, sizes, offs, tot[k:k + 1], status, ws_en, nbytes=pb)
+        ev[2].record()
+        pulse.lz4_decode_blocks(payload, offs[:nbk], sizes[:nbk], back, status, ws_de, mode=0, nbytes=pb,
+                                payload_bytes=pcap)
+        ev[3].record()
+        pulse.patch_unpack(back, count, idx2, val2, status, ws_up)
+        ev[4].record()
+        torch.cuda.synchronize()
+        for i, key in enumerate(("pack", "encode", "decode", "unpack")):
+            t[key] += ev[i].elapsed_time(ev[i + 1])
+        if not (torch.equal(idx2[:count], idx[:count]) and torch.equal(val2[:count], val[:count])):
+            raise SystemExit(f"patch-stream leg: chunk {k} did not round-trip")
+        if k == 1 and with_oracle:
+            n_s = min(count, 1 << 22)
+            sample = (idx[:n_s].cpu().numpy(), val[:n_s].cpu().numpy().view(np.uint16))
+        entries += count
+        packed_total += pb
+    if int(status.item()) != 0:
+        raise SystemExit(f"patch-stream leg: device status {int(status.item())}")
+    comp = int(tot.sum().item())
+    cpe = comp / entries
+    log(f"patch-stream leg: {entries} entries, {comp} compressed bytes ({cpe:.3f} B per entry)")
+    L = len(chunks)
+    out = {"patch_pack": _leg(t["pack"], L, 12 * entries, entries=entries),
+           "patch_lz4_encode": _leg(t["encode"], L, packed_total + comp, compressed_bytes=comp,
+                                    bytes_per_entry=round(cpe, 4), raw_bytes_per_entry=6,
+                                    checked="decode + unpack == the patch, every chunk"),
+           "patch_lz4_decode": _leg(t["decode"], L, comp + packed_total),
+           "patch_unpack": _leg(t["unpack"], L, 12 * entries)}
+    if sample is not None:  # the CPU baseline of this leg
+        import oracle
+
+        t0 = time.perf_counter()
+        oracle.patch_compress(*sample)
+        secs = time.perf_counter() - t0
+        out["patch_lz4_encode"]["cpu_baseline"] = {
+            "kind": "oracle", "GBps": round(6 * sample[0].size / secs / 1e9, 3), "cores": 1,
+            "sample": f"first {sample[0].size} entries of chunk 1, pack + LZ4 encode, {secs:.2f} s"}
     return out
 
 
