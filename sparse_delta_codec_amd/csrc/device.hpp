@@ -232,16 +232,21 @@ __device__ __forceinline__ void ws_epoch_advance(WsHeader *h, uint32_t ep) {
 // too and the kernel always terminates.
 constexpr uint32_t kSpinLimit = 1u << 20;
 
+// The two halves of the look-back, for callers that overlap other work with
+// the wait: publish the tile's aggregate (tile 0: its inclusive value) ...
+__device__ __forceinline__ void lookback_publish(uint64_t *status, uint32_t tile, uint32_t tag,
+                                                 uint64_t aggregate) {
+    if (lane_id() == 0) st_agent(&status[tile], make_status(tag, tile == 0, aggregate));
+}
+
+// ... then, by the same full wave, wait for the predecessors, publish the
+// inclusive prefix and return the exclusive one.
 template <bool MAX = false>
-__device__ __forceinline__ uint64_t lookback_wave(uint64_t *status, uint32_t tile, uint32_t tag,
-                                                  uint64_t aggregate, bool *failed) {
+__device__ __forceinline__ uint64_t lookback_resolve(uint64_t *status, uint32_t tile, uint32_t tag,
+                                                     uint64_t aggregate, bool *failed) {
     const int lane = lane_id();
     uint32_t spins = 0;
-    if (tile == 0) {
-        if (lane == 0) st_agent(&status[0], make_status(tag, true, aggregate));
-        return 0;
-    }
-    if (lane == 0) st_agent(&status[tile], make_status(tag, false, aggregate));
+    if (tile == 0) return 0;
 
     uint64_t prefix = 0;
     int64_t j = (int64_t)tile - 1;  // newest predecessor the window starts at
@@ -288,6 +293,13 @@ __device__ __forceinline__ uint64_t lookback_wave(uint64_t *status, uint32_t til
     else incl_v = prefix + aggregate;
     if (lane == 0) st_agent(&status[tile], make_status(tag, true, incl_v));
     return prefix;
+}
+
+template <bool MAX = false>
+__device__ __forceinline__ uint64_t lookback_wave(uint64_t *status, uint32_t tile, uint32_t tag,
+                                                  uint64_t aggregate, bool *failed) {
+    lookback_publish(status, tile, tag, aggregate);
+    return lookback_resolve<MAX>(status, tile, tag, aggregate, failed);
 }
 
 __device__ __forceinline__ uint16_t bf16_rne(uint32_t x) {

@@ -27,8 +27,10 @@
 //  4. decoupled look-back over blocks gives the block's payload offset;
 //  5. emission: each thread writes its sequences' headers and the literal bytes
 //     of its own chunk; when the block's encoding fits the 14 KiB LDS window
-//     (every block of a sparse mask) the bytes go there and are copied out with
-//     16-byte stores, otherwise straight to the payload.
+//     (every block of a sparse mask) the bytes go there, relative to the
+//     block's start, while wave 0 waits for the predecessors' sizes, and are
+//     then copied out with 16-byte stores; otherwise the offset comes first
+//     and the bytes go straight to the payload.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -162,7 +164,7 @@ __device__ __forceinline__ void emit_chunk(P out, const uint8_t *s_img, uint64_t
 
 struct EncShared {
     uint8_t img[LZE_MAX_BLOCK];
-    uint8_t win[LZE_WIN + 16];
+    uint8_t win[LZE_WIN + 48];  // output byte x at win[16 + x]; 16-byte guards around it
     int32_t i32[LZE_THREADS / kWave];
     uint64_t off;
 };
@@ -263,48 +265,87 @@ __device__ __forceinline__ void enc_block(const Lz4EncArgs &a, uint32_t b, uint3
     const int32_t ll_final = len - a_final;
     const uint64_t comp = (uint64_t)qsum + 1 + ext_bytes(ll_final) + ll_final;
 
-    // 4. place the block
-    if (wave_id() == 0) {
-        bool failed = false;
-        const uint64_t off = lookback_wave(a.status, b, tag, comp, &failed);
-        if (lane_id() == 0) {
-            if (failed) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
-            sh.off = off;
-            a.comp_sizes[b] = (uint32_t)comp;
-            a.comp_offsets[b] = off;
-            if (b == a.nblocks - 1) {
-                *a.d_total = off + comp;
-                ws_epoch_advance(a.hdr, ep);
-            }
-            if ((int64_t)(off + comp) > a.cap) or_agent32(a.d_status, 1u /*PULSE_DS_CAPACITY*/);
-        }
-    }
-    __syncthreads();
-    const uint64_t off = sh.off;
-    if ((int64_t)(off + comp) > a.cap) return;
-    uint8_t *dst = a.payload + off;
-    const int32_t shift = (int32_t)((uintptr_t)dst & 15);  // window byte 0 <-> 16-byte aligned address
-    const bool staged = (int32_t)comp + shift <= LZE_WIN + 16;
-
-    // 5. emit
+    // 4 + 5. place the block and emit it.  A block whose encoding fits the LDS
+    // window (every block of a sparse mask) is emitted there first, relative to
+    // its own start: wave 0 publishes the block's size, every wave emits, and
+    // only then does wave 0 wait for the predecessors' sizes, so that wait
+    // overlaps the emission.  A larger block needs its offset first and is
+    // emitted straight into the payload.
     const int32_t sw = (t >> (4 - (CHLOG - 4))) & ((1 << (CHLOG - 4)) - 1);
-    uint8_t *const outp = staged ? s_win + shift : dst;
+    const bool staged = (int32_t)comp <= LZE_WIN;
+    auto place = [&](uint64_t off, bool failed) {  // lane 0 of wave 0
+        if (failed) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
+        sh.off = off;
+        a.comp_sizes[b] = (uint32_t)comp;
+        a.comp_offsets[b] = off;
+        if (b == a.nblocks - 1) {
+            *a.d_total = off + comp;
+            ws_epoch_advance(a.hdr, ep);
+        }
+        if ((int64_t)(off + comp) > a.cap) or_agent32(a.d_status, 1u /*PULSE_DS_CAPACITY*/);
+    };
+    uint8_t *outp;
+    if (staged) {
+        if (wave_id() == 0) lookback_publish(a.status, b, tag, comp);
+        outp = s_win + 16;
+    } else {
+        if (wave_id() == 0) {
+            bool failed = false;
+            const uint64_t off = lookback_wave(a.status, b, tag, comp, &failed);
+            if (lane_id() == 0) place(off, failed);
+        }
+        __syncthreads();
+        if ((int64_t)(sh.off + comp) > a.cap) return;
+        outp = a.payload + sh.off;
+    }
     emit_chunk<CHLOG>(outp, s_img, Q, m, cs, cs + cl, next_after, len, carry_j, pos0, next_qi, sw);
     if (t == 0) {
         outp[qsum] = (uint8_t)((ll_final >= 15 ? 15 : ll_final) << 4);
         if (ll_final >= 15) put_len(outp, qsum + 1, ll_final);
     }
     if (!staged) return;
+    if (wave_id() == 0) {
+        bool failed = false;
+        const uint64_t off = lookback_resolve(a.status, b, tag, comp, &failed);
+        if (lane_id() == 0) place(off, failed);
+    }
     __syncthreads();
-    // copy the window out: 16-byte stores for whole aligned pieces, bytes for
-    // the first and last piece (shared with the neighbouring blocks' bytes)
+    const uint64_t off = sh.off;
+    if ((int64_t)(off + comp) > a.cap) return;
+    uint8_t *dst = a.payload + off;
+    // copy the window out with 16-byte stores to aligned addresses (bytes for
+    // the first and last piece, shared with the neighbouring blocks' bytes):
+    // aligned piece u covers output bytes [16 u - shift, +16), which sit at
+    // window [16 u + 16 - shift, +16), inside the aligned pair 16 u, 16 u + 16
+    const int32_t shift = (int32_t)((uintptr_t)dst & 15);
     const int32_t end = shift + (int32_t)comp;
     uint8_t *base = dst - shift;
+    const int o = 16 - shift;  // 1 .. 16, the same for the whole block
     for (int32_t q = 16 * t; q < end; q += 16 * LZE_THREADS) {
         if (q >= shift && q + 16 <= end) {
-            *reinterpret_cast<uint4 *>(base + q) = *reinterpret_cast<const uint4 *>(s_win + q);
+            const u32x4 A = *reinterpret_cast<const u32x4 *>(s_win + q);
+            const u32x4 B = *reinterpret_cast<const u32x4 *>(s_win + q + 16);
+            const uint32_t wv[8] = {A.x, A.y, A.z, A.w, B.x, B.y, B.z, B.w};
+            u32x4 r;
+            const int wq = o >> 2, bs = o & 3;
+            if (o == 16) {
+                r = B;
+            } else if (wq == 0) {
+                r = u32x4{__builtin_amdgcn_alignbyte(wv[1], wv[0], bs), __builtin_amdgcn_alignbyte(wv[2], wv[1], bs),
+                          __builtin_amdgcn_alignbyte(wv[3], wv[2], bs), __builtin_amdgcn_alignbyte(wv[4], wv[3], bs)};
+            } else if (wq == 1) {
+                r = u32x4{__builtin_amdgcn_alignbyte(wv[2], wv[1], bs), __builtin_amdgcn_alignbyte(wv[3], wv[2], bs),
+                          __builtin_amdgcn_alignbyte(wv[4], wv[3], bs), __builtin_amdgcn_alignbyte(wv[5], wv[4], bs)};
+            } else if (wq == 2) {
+                r = u32x4{__builtin_amdgcn_alignbyte(wv[3], wv[2], bs), __builtin_amdgcn_alignbyte(wv[4], wv[3], bs),
+                          __builtin_amdgcn_alignbyte(wv[5], wv[4], bs), __builtin_amdgcn_alignbyte(wv[6], wv[5], bs)};
+            } else {
+                r = u32x4{__builtin_amdgcn_alignbyte(wv[4], wv[3], bs), __builtin_amdgcn_alignbyte(wv[5], wv[4], bs),
+                          __builtin_amdgcn_alignbyte(wv[6], wv[5], bs), __builtin_amdgcn_alignbyte(wv[7], wv[6], bs)};
+            }
+            *reinterpret_cast<u32x4 *>(base + q) = r;
         } else {
-            for (int32_t x = (q > shift ? q : shift); x < q + 16 && x < end; ++x) base[x] = s_win[x];
+            for (int32_t x = (q > shift ? q : shift); x < q + 16 && x < end; ++x) base[x] = s_win[16 + x - shift];
         }
     }
 }
