@@ -57,6 +57,8 @@ def lib():
         L.oracle_patch_pack.argtypes = [_P, _P, _I64, _P]
         L.oracle_patch_unpack.argtypes = [_P, _I64, _P, _P]
         L.oracle_patch_unpack.restype = ctypes.c_int
+        L.oracle_cast_diff_segments.argtypes = [_P, _P, _P, _P, _I32, _P, _P, _I64, _P, _P]
+        L.oracle_apply_patch_segments.argtypes = [_P, _P, _I32, _P, _P, _P, _P]
         _lib = L
     return _lib
 
@@ -289,4 +291,42 @@ def patch_compress(idx, val, block_bytes=65536):
     """The whole sender side: pack, then the canonical LZ4 block encoding."""
     packed = patch_pack(idx, val)
     return packed, lz4_encode_blocks(packed, block_bytes)
+
+
+def _ptrs(arrs):
+    return (ctypes.c_void_p * max(len(arrs), 1))(*[a.ctypes.data for a in arrs])
+
+
+def cast_diff_segments(ws_new, bs_old, cap=None):
+    """Lists of float32 masters and BF16 old views, one per tensor.  Returns
+    dict(b_new (list), idx, val, seg_offsets, count, status)."""
+    ws_new = [_c(w, np.float32).reshape(-1) for w in ws_new]
+    bs_old = [_c(b, np.uint16).reshape(-1) for b in bs_old]
+    ns = np.array([w.size for w in ws_new], np.int64)
+    total = int(ns.sum())
+    cap = total if cap is None else int(cap)
+    b_new = [np.empty(w.size, np.uint16) for w in ws_new]
+    idx, val = np.empty(max(cap, 1), np.int32), np.empty(max(cap, 1), np.uint16)
+    offs = np.zeros(len(ws_new) + 1, np.int64)
+    status = np.zeros(1, np.uint32)
+    pw, po, pn = _ptrs(ws_new), _ptrs(bs_old), _ptrs(b_new)
+    lib().oracle_cast_diff_segments(ctypes.cast(pw, ctypes.c_void_p), ctypes.cast(po, ctypes.c_void_p),
+                                    ctypes.cast(pn, ctypes.c_void_p), _ptr(ns), len(ws_new), _ptr(idx),
+                                    _ptr(val), cap, _ptr(offs), _ptr(status))
+    m = int(offs[-1])
+    return dict(b_new=b_new, idx=idx[:min(m, cap)], val=val[:min(m, cap)], seg_offsets=offs, count=m,
+                status=int(status[0]))
+
+
+def apply_patch_segments(views, idx, val, seg_offsets):
+    """Applies to copies of the views; returns (views, status)."""
+    vs = [_c(v, np.uint16).reshape(-1).copy() for v in views]
+    ns = np.array([v.size for v in vs], np.int64)
+    i, v = _c(idx, np.int32), _c(val, np.uint16)
+    offs = _c(seg_offsets, np.int64)
+    status = np.zeros(1, np.uint32)
+    pv = _ptrs(vs)
+    lib().oracle_apply_patch_segments(ctypes.cast(pv, ctypes.c_void_p), _ptr(ns), len(vs), _ptr(i), _ptr(v),
+                                      _ptr(offs), _ptr(status))
+    return vs, int(status[0])
 

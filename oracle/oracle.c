@@ -26,6 +26,9 @@
  *                           pinned: numpy diff + little-endian byte views; round
  *                           trips; constant planes give 6 x 267 B (the closed form
  *                           of a constant 64 KiB block); index overflow rejected.
+ *   oracle_cast_diff_segments, oracle_apply_patch_segments
+ *                           pinned: torch's cast + numpy flatnonzero per tensor,
+ *                           concatenated; apply over the list rebuilds every view.
  *   oracle_loco_gate, oracle_loco_accumulate
  *                           pinned: torch's float32 add and BF16 cast, the exact
  *                           conservation resid' + sent == resid + delta, closed
@@ -565,5 +568,49 @@ int oracle_patch_unpack(const uint8_t *packed, int64_t count, int32_t *idx, uint
         prev = i;
     }
     return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* f4  one call over a list of tensors.  The tiling and address-mapping       */
+/* metadata is prepared on the CPU so that one kernel launch covers the whole */
+/* model [Teleport, "Moving the pipeline onto GPUs"].  What it computes is    */
+/* exactly the per-tensor rows a1-a4: for each tensor in list order, the cast */
+/* / diff / compaction with indices local to the tensor; the entries of all   */
+/* tensors form one stream, seg_offsets[s] being tensor s's first entry and   */
+/* seg_offsets[nseg] the total.                                               */
+/* ------------------------------------------------------------------------ */
+void oracle_cast_diff_segments(const float *const *w_new, const uint16_t *const *b_old,
+                               uint16_t *const *b_new, const int64_t *n, int32_t nseg,
+                               int32_t *idx, uint16_t *val, int64_t cap, int64_t *seg_offsets,
+                               uint32_t *status)
+{
+    int64_t m = 0;
+    for (int32_t s = 0; s < nseg; ++s) {
+        seg_offsets[s] = m;
+        for (int64_t i = 0; i < n[s]; ++i) {
+            uint32_t bits;
+            memcpy(&bits, &w_new[s][i], 4);
+            uint16_t v = oracle_bf16_rne(bits);
+            if (b_new && b_new[s]) b_new[s][i] = v;
+            if (v != b_old[s][i]) {
+                if (m < cap) {
+                    idx[m] = (int32_t)i; /* local to the tensor */
+                    val[m] = v;
+                }
+                ++m;
+            }
+        }
+    }
+    seg_offsets[nseg] = m;
+    if (m > cap && status) *status |= ORACLE_CAPACITY;
+}
+
+void oracle_apply_patch_segments(uint16_t *const *views, const int64_t *n, int32_t nseg,
+                                 const int32_t *idx, const uint16_t *val,
+                                 const int64_t *seg_offsets, uint32_t *status)
+{
+    for (int32_t s = 0; s < nseg; ++s)
+        oracle_apply_patch(views[s], n[s], idx + seg_offsets[s], val + seg_offsets[s],
+                           seg_offsets[s + 1] - seg_offsets[s], status);
 }
 

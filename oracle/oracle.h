@@ -131,6 +131,16 @@ int64_t oracle_patch_packed_bytes(int64_t count);
 void oracle_patch_pack(const int32_t *idx, const uint16_t *val, int64_t count, uint8_t *packed);
 /* f2: inverse; 0, or -1 when an index would pass INT32_MAX. */
 int oracle_patch_unpack(const uint8_t *packed, int64_t count, int32_t *idx, uint16_t *val);
+/* f4: cast/diff/compact over a list of tensors, indices local to each tensor,
+ * one entry stream; seg_offsets [nseg + 1].  b_new may be NULL (or hold NULLs). */
+void oracle_cast_diff_segments(const float *const *w_new, const uint16_t *const *b_old,
+                               uint16_t *const *b_new, const int64_t *n, int32_t nseg,
+                               int32_t *idx, uint16_t *val, int64_t cap, int64_t *seg_offsets,
+                               uint32_t *status);
+/* f4: apply each tensor's slice of the stream to its view. */
+void oracle_apply_patch_segments(uint16_t *const *views, const int64_t *n, int32_t nseg,
+                                 const int32_t *idx, const uint16_t *val,
+                                 const int64_t *seg_offsets, uint32_t *status);
 #ifdef __cplusplus
 }
 #endif

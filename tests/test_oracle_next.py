@@ -261,3 +261,48 @@ def test_compressed_patch_round_trip_on_the_c1_step():
     back = oracle.patch_unpack(dec, r["count"])
     assert np.array_equal(back[0], r["idx"]) and np.array_equal(back[1], r["val"])
     assert enc["total"] < 6 * r["count"] * 0.6
+
+
+# ---- one call over a list of tensors ----------------------------------------------------
+def torch_cast(w):
+    return torch.from_numpy(np.ascontiguousarray(w, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(
+        np.uint16)
+
+
+def tensor_list(sizes, seed):
+    rng = np.random.default_rng(seed)
+    ws, bs = [], []
+    for n in sizes:
+        w0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+        w1 = (w0 - np.float32(3e-6) * np.clip(rng.standard_normal(n), -3, 3).astype(np.float32)).astype(np.float32)
+        ws.append(w1)
+        bs.append(torch_cast(w0))
+    return ws, bs
+
+
+def test_segments_match_per_tensor_brute_force():
+    """The list call equals, tensor by tensor, torch's cast compared with the
+    old view and numpy's flatnonzero, the entries concatenated in list order."""
+    sizes = [1, 16383, 16384, 16385, 5, 40000, 2, 3 * 16384 + 7]
+    ws, bs = tensor_list(sizes, 21)
+    r = oracle.cast_diff_segments(ws, bs)
+    pos = 0
+    for s, (w, b) in enumerate(zip(ws, bs)):
+        new = torch_cast(w)
+        loc = np.flatnonzero(new != b)
+        assert r["seg_offsets"][s] == pos
+        assert np.array_equal(r["idx"][pos:pos + loc.size], loc)
+        assert np.array_equal(r["val"][pos:pos + loc.size], new[loc])
+        assert np.array_equal(r["b_new"][s], new)
+        pos += loc.size
+    assert r["seg_offsets"][-1] == pos == r["count"] and r["status"] == 0
+    views, st = oracle.apply_patch_segments(bs, r["idx"], r["val"], r["seg_offsets"])
+    assert st == 0 and all(np.array_equal(v, nb) for v, nb in zip(views, r["b_new"]))
+
+
+def test_segments_capacity():
+    ws, bs = tensor_list([1000, 2000], 22)
+    full = oracle.cast_diff_segments(ws, bs)
+    r = oracle.cast_diff_segments(ws, bs, cap=10)
+    assert r["count"] == full["count"] and r["status"] == oracle.CAPACITY
+    assert np.array_equal(r["idx"], full["idx"][:10]) and np.array_equal(r["seg_offsets"], full["seg_offsets"])
