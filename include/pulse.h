@@ -73,6 +73,10 @@ extern "C" {
                                   overlapping calls); this call's outputs are
                                   invalid, but the call still terminates;
                                   re-initialise the workspace               */
+#define PULSE_DS_BADSEGMENT 0x10u /* a list call met a segment whose table entry
+                                  breaks its preconditions (size, alignment,
+                                  tile numbering, b_new presence); nothing
+                                  was written for its tiles                 */
 
 /* ---- workspaces ------------------------------------------------------------ */
 #define PULSE_OP_CAST_DIFF 1  /* n = element count                               */
@@ -82,6 +86,7 @@ extern "C" {
 #define PULSE_OP_FP8_DELTA 5  /* n = max(code count, scale count)                 */
 #define PULSE_OP_LOCO_GATE 6  /* n = element count                               */
 #define PULSE_OP_PATCH_UNPACK 7 /* n = patch entries                            */
+#define PULSE_OP_CAST_DIFF_SEGMENTS 8 /* n = tile count (pulse_segment_tiles)    */
 
 /* Bytes of workspace the op needs for the given size (0 if it needs none).
  * A workspace serves any number of calls of the op it was sized for, of any
@@ -331,6 +336,57 @@ int patch_pack(const int32_t *idx, const uint16_t *val, int64_t count, uint8_t *
  *   ws         pulse_workspace_bytes(PULSE_OP_PATCH_UNPACK, count, 0). */
 int patch_unpack(const uint8_t *packed, int64_t count, int32_t *idx, uint16_t *val,
                  uint32_t *d_status, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---- next: one launch over a list of tensors --------------------------------
+ * The tiling and address-mapping metadata is prepared on the CPU so that one
+ * kernel launch covers the whole model ([Teleport] "Moving the pipeline onto
+ * GPUs").  The result is exactly that of pulse_cast_diff (patch output, and
+ * b_new when given) on each tensor in list order, with indices local to each
+ * tensor: one entry stream in which tensor s holds
+ * [seg_offsets[s], seg_offsets[s + 1]).
+ *
+ * One tensor of the list (device table of nseg entries, 40 bytes each). */
+typedef struct pulse_segment {
+    const float *w_new;    /* [n] float32 masters (read), 16-byte aligned        */
+    const uint16_t *b_old; /* [n] previous BF16 view (read), 16-byte aligned     */
+    uint16_t *b_new;       /* [n] new view (written), 16-byte aligned, or NULL
+                              (all segments alike, see with_new)                */
+    int64_t n;             /* elements, 1 .. 2^31 - 1                            */
+    int64_t tile0;         /* first tile of the tensor: pulse_segment_tiles      */
+} pulse_segment;
+
+/* One view of the receiver (device table of nseg entries, 16 bytes each). */
+typedef struct pulse_view {
+    uint16_t *b; /* [n] BF16 view (read and written) */
+    int64_t n;
+} pulse_view;
+
+/* Host helper that prepares the tiling metadata: returns the number of
+ * 16384-element tiles of the list (or a negative PULSE_E* code), writes each
+ * tensor's first tile to tile0[nseg] and the tensor of every tile to
+ * tile_seg[tiles] (host arrays; either may be NULL).  n: host array. */
+int64_t pulse_segment_tiles(const int64_t *n, int32_t nseg, int64_t *tile0, uint32_t *tile_seg);
+
+/*   segs       device table [nseg].
+ *   tile_seg   device array [ntiles]: the tensor of every tile.
+ *   ntiles     the return value of pulse_segment_tiles.
+ *   patch_idx, patch_val [patch_cap] the entry stream (written).
+ *   seg_offsets [nseg + 1] int64 (written): first entry of each tensor, total.
+ *   with_new   1 if every segment has b_new, 0 if none has.
+ *   d_status   PULSE_DS_CAPACITY, PULSE_DS_BADSEGMENT, PULSE_DS_WORKSPACE.
+ *   ws         pulse_workspace_bytes(PULSE_OP_CAST_DIFF_SEGMENTS, ntiles, 0). */
+int pulse_cast_diff_segments(const pulse_segment *segs, int32_t nseg, const uint32_t *tile_seg,
+                             int64_t ntiles, int32_t *patch_idx, uint16_t *patch_val, int64_t patch_cap,
+                             int64_t *seg_offsets, uint32_t *d_status, void *ws, size_t ws_bytes,
+                             int32_t with_new, hipStream_t stream);
+
+/* The receiver's side of a list call: for every tensor s,
+ * views[s].b[patch_idx[k]] = patch_val[k] for k in [seg_offsets[s],
+ * seg_offsets[s + 1]), k < max_count; out-of-range indices set
+ * PULSE_DS_BADINDEX.  views: device table [nseg]. */
+int pulse_apply_patch_segments(const pulse_view *views, int32_t nseg, const int32_t *patch_idx,
+                               const uint16_t *patch_val, const int64_t *seg_offsets, int64_t max_count,
+                               uint32_t *d_status, hipStream_t stream);
 
 #ifdef __cplusplus
 }

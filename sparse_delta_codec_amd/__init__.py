@@ -20,6 +20,8 @@ __all__ = [
     "PULSE_OP_FP8_DELTA", "PULSE_OP_LOCO_GATE", "fp8_view_delta", "fp8_view_apply",
     "pulse_loco_gate", "pulse_loco_accumulate",
     "PULSE_OP_PATCH_UNPACK", "patch_packed_bytes", "patch_pack", "patch_unpack",
+    "PULSE_OP_CAST_DIFF_SEGMENTS", "PULSE_DS_BADSEGMENT", "pulse_segment_tiles", "SegmentTable", "ViewTable",
+    "pulse_cast_diff_segments", "pulse_apply_patch_segments",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -41,6 +43,8 @@ PULSE_OP_LZ4_DECODE = 4
 PULSE_OP_FP8_DELTA = 5
 PULSE_OP_LOCO_GATE = 6
 PULSE_OP_PATCH_UNPACK = 7
+PULSE_OP_CAST_DIFF_SEGMENTS = 8
+PULSE_DS_BADSEGMENT = 0x10
 
 _P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
 _lib.pulse_version.restype = ctypes.c_char_p
@@ -64,7 +68,12 @@ _lib.patch_packed_bytes.argtypes = [_I64]
 _lib.patch_packed_bytes.restype = _I64
 _lib.patch_pack.argtypes = [_P, _P, _I64, _P, _P]
 _lib.patch_unpack.argtypes = [_P, _I64, _P, _P, _P, _P, _SZ, _P]
-for _f in ("patch_pack", "patch_unpack", "pulse_workspace_init", "pulse_cast_diff", "pulse_compact", "pulse_apply_patch",
+_lib.pulse_segment_tiles.argtypes = [_P, _I32, _P, _P]
+_lib.pulse_segment_tiles.restype = _I64
+_lib.pulse_cast_diff_segments.argtypes = [_P, _I32, _P, _I64, _P, _P, _I64, _P, _P, _P, _SZ, _I32, _P]
+_lib.pulse_apply_patch_segments.argtypes = [_P, _I32, _P, _P, _P, _I64, _P, _P]
+for _f in ("pulse_cast_diff_segments", "pulse_apply_patch_segments", "patch_pack", "patch_unpack",
+           "pulse_workspace_init", "pulse_cast_diff", "pulse_compact", "pulse_apply_patch",
            "xor_mask_apply", "lz4_encode_blocks", "lz4_decode_blocks", "fp8_block_quant",
            "fp8_view_delta", "fp8_view_apply", "pulse_loco_gate", "pulse_loco_accumulate"):
     getattr(_lib, _f).restype = ctypes.c_int
@@ -339,4 +348,86 @@ def patch_unpack(packed, count, idx, val, d_status, ws, stream=None):
     _check(_lib.patch_unpack(_dev(packed, "packed", torch.uint8), count, _dev(idx, "idx", torch.int32),
                              _dev(val, "val", _U16), _dev(d_status, "d_status", torch.int32), wsp, wsb,
                              _stream(stream)), "patch_unpack")
+
+
+def pulse_segment_tiles(ns):
+    """Host tiling metadata of a list of tensor sizes: (ntiles, tile0, tile_seg) as numpy arrays."""
+    import numpy as np
+
+    n = np.ascontiguousarray(ns, dtype=np.int64)
+    t = int(_lib.pulse_segment_tiles(n.ctypes.data, n.size, None, None))
+    if t < 0:
+        raise RuntimeError(f"pulse_segment_tiles: {_lib.pulse_status_string(t).decode()} ({t})")
+    tile0 = np.empty(n.size, np.int64)
+    tile_seg = np.empty(max(t, 1), np.uint32)
+    _lib.pulse_segment_tiles(n.ctypes.data, n.size, tile0.ctypes.data, tile_seg.ctypes.data)
+    return t, tile0, tile_seg[:t]
+
+
+class SegmentTable:
+    """The device tables of a list call (pulse_segment[nseg] and the tile map),
+    prepared once on the host for a list of tensors and reused every step.
+    w_new: float32 GPU tensors; b_old, b_new: BF16/uint16 GPU tensors (b_new may be None)."""
+
+    def __init__(self, w_new, b_old, b_new=None, device="cuda"):
+        import numpy as np
+
+        if len(w_new) != len(b_old) or (b_new is not None and len(b_new) != len(w_new)) or not w_new:
+            raise ValueError("w_new, b_old (and b_new) must be lists of the same, non-zero length")
+        ns = [t.numel() for t in w_new]
+        for i, (w, b) in enumerate(zip(w_new, b_old)):
+            _dev(w, f"w_new[{i}]", torch.float32)
+            _dev(b, f"b_old[{i}]", _U16)
+            _need(b, 2 * ns[i], f"b_old[{i}]")
+            if b_new is not None:
+                _dev(b_new[i], f"b_new[{i}]", _U16)
+                _need(b_new[i], 2 * ns[i], f"b_new[{i}]")
+        self.ntiles, tile0, tile_seg = pulse_segment_tiles(ns)
+        tab = np.zeros((len(ns), 5), np.int64)
+        for i in range(len(ns)):
+            tab[i] = [w_new[i].data_ptr(), b_old[i].data_ptr(), 0 if b_new is None else b_new[i].data_ptr(),
+                      ns[i], tile0[i]]
+        self.nseg = len(ns)
+        self.with_new = b_new is not None
+        self.segs = torch.from_numpy(tab).to(device)
+        self.tile_seg = torch.from_numpy(tile_seg.view(np.int32)).to(device)
+        self._keep = (list(w_new), list(b_old), None if b_new is None else list(b_new))
+
+
+class ViewTable:
+    """Device table pulse_view[nseg] of the receiver's BF16 views (GPU tensors)."""
+
+    def __init__(self, views, device="cuda"):
+        import numpy as np
+
+        tab = np.zeros((len(views), 2), np.int64)
+        for i, v in enumerate(views):
+            _dev(v, f"views[{i}]", _U16)
+            tab[i] = [v.data_ptr(), v.numel()]
+        self.nseg = len(views)
+        self.views = torch.from_numpy(tab).to(device)
+        self._keep = list(views)
+
+
+def pulse_cast_diff_segments(table, patch_idx, patch_val, seg_offsets, d_status, ws, stream=None):
+    cap = patch_idx.numel()
+    _need(patch_val, 2 * cap, "patch_val")
+    _need(seg_offsets, 8 * (table.nseg + 1), "seg_offsets")
+    wsp, wsb = _ws(ws)
+    _check(_lib.pulse_cast_diff_segments(
+        table.segs.data_ptr(), table.nseg, table.tile_seg.data_ptr(), table.ntiles,
+        _dev(patch_idx, "patch_idx", torch.int32), _dev(patch_val, "patch_val", _U16), cap,
+        _dev(seg_offsets, "seg_offsets", torch.int64), _dev(d_status, "d_status", torch.int32), wsp, wsb,
+        1 if table.with_new else 0, _stream(stream)), "pulse_cast_diff_segments")
+
+
+def pulse_apply_patch_segments(views, patch_idx, patch_val, seg_offsets, d_status, max_count=None, stream=None):
+    max_count = patch_idx.numel() if max_count is None else max_count
+    _need(patch_idx, 4 * max_count, "patch_idx")
+    _need(patch_val, 2 * max_count, "patch_val")
+    _need(seg_offsets, 8 * (views.nseg + 1), "seg_offsets")
+    _check(_lib.pulse_apply_patch_segments(
+        views.views.data_ptr(), views.nseg, _dev(patch_idx, "patch_idx", torch.int32),
+        _dev(patch_val, "patch_val", _U16), _dev(seg_offsets, "seg_offsets", torch.int64), max_count,
+        _dev(d_status, "d_status", torch.int32), _stream(stream)), "pulse_apply_patch_segments")
 

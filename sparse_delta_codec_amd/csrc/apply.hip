@@ -67,9 +67,79 @@ __global__ __launch_bounds__(256) void k_xor_apply(uint8_t *__restrict__ dst,
     }
 }
 
+// Apply over a list of views: the patch stream of a list call, tensor s's
+// entries being [seg_offsets[s], seg_offsets[s + 1]).  Each wave takes one
+// contiguous range of 256-entry chunks, finds the tensor of its first entry by
+// a binary search over seg_offsets and then walks forward; lanes whose entry
+// lies past the current tensor step ahead on their own.
+struct ViewDesc {  // the layout of pulse_view
+    uint16_t *b;
+    int64_t n;
+};
+
+__global__ __launch_bounds__(256) void k_apply_patch_segments(const ViewDesc *__restrict__ views, int32_t nseg,
+                                                              const int32_t *__restrict__ idx,
+                                                              const uint16_t *__restrict__ val,
+                                                              const int64_t *__restrict__ seg_offsets,
+                                                              int64_t max_count, uint32_t *d_status) {
+    int64_t count = seg_offsets[nseg];
+    if (count > max_count) count = max_count;
+    const int64_t nchunks = (count + 255) / 256;
+    const int64_t nw = (int64_t)gridDim.x * (blockDim.x / kWave);
+    const int64_t gw = (int64_t)blockIdx.x * (blockDim.x / kWave) + wave_id();
+    const int64_t c0 = nchunks * gw / nw, c1 = nchunks * (gw + 1) / nw;
+    bool bad = false;
+    if (c0 < c1) {
+        // last tensor whose first entry is <= the range's first entry
+        const int64_t k0 = c0 * 256;
+        int32_t lo = 0, hi = nseg - 1;
+        while (lo < hi) {
+            const int32_t mid = (lo + hi + 1) >> 1;
+            if (seg_offsets[mid] <= k0) lo = mid;
+            else hi = mid - 1;
+        }
+        int32_t s = lo;
+        for (int64_t c = c0; c < c1; ++c) {
+            int32_t ii[4];
+            uint16_t vv[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t k = c * 256 + q * kWave + lane_id();
+                ii[q] = k < count ? idx[k] : -1;
+                vv[q] = k < count ? val[k] : 0;
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t k = c * 256 + q * kWave + lane_id();
+                if (k >= count) break;
+                int32_t sl = s;
+                while (sl + 1 < nseg && k >= seg_offsets[sl + 1]) ++sl;
+                const ViewDesc v = views[sl];
+                const int64_t i = ii[q];
+                if (i >= 0 && i < v.n) v.b[i] = vv[q];
+                else bad = true;
+            }
+            const int64_t kn = (c + 1) * 256;
+            while (s + 1 < nseg && seg_offsets[s + 1] <= kn) ++s;
+        }
+    }
+    if (__ballot(bad) && lane_id() == 0) or_agent32(d_status, 2u /*PULSE_DS_BADINDEX*/);
+}
+
 }  // namespace pulse
 
 using namespace pulse;
+
+extern "C" int pulse_launch_apply_patch_segments(const void *views, int32_t nseg, const int32_t *idx,
+                                                 const uint16_t *val, const int64_t *seg_offsets, int64_t max_count,
+                                                 uint32_t *d_status, hipStream_t stream) {
+    int64_t blocks = (max_count + 1023) / 1024;
+    if (blocks > 256 * 32) blocks = 256 * 32;
+    if (blocks < 1) blocks = 1;
+    k_apply_patch_segments<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(
+        static_cast<const ViewDesc *>(views), nseg, idx, val, seg_offsets, max_count, d_status);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}
 
 extern "C" int pulse_launch_apply_patch(uint16_t *b, int64_t n, const int32_t *idx, const uint16_t *val,
                                         const int64_t *d_count, int64_t max_count, uint32_t *d_status,

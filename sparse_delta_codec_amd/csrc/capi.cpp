@@ -39,6 +39,10 @@ size_t pulse_patch_unpack_ws_bytes(int64_t count);
 int64_t pulse_patch_packed_bytes_impl(int64_t count);
 int pulse_launch_patch_pack(const int32_t *, const uint16_t *, int64_t, uint8_t *, hipStream_t);
 int pulse_launch_patch_unpack(const uint8_t *, int64_t, int32_t *, uint16_t *, uint32_t *, void *, hipStream_t);
+int pulse_launch_cast_diff_segments(const void *, int32_t, const uint32_t *, int64_t, int32_t *, uint16_t *, int64_t,
+                                    int64_t *, uint32_t *, void *, int, hipStream_t);
+int pulse_launch_apply_patch_segments(const void *, int32_t, const int32_t *, const uint16_t *, const int64_t *,
+                                      int64_t, uint32_t *, hipStream_t);
 int pulse_launch_fill_zero(void *, size_t, hipStream_t);
 int pulse_launch_write_count(int64_t *, int64_t, hipStream_t);
 }
@@ -82,6 +86,7 @@ size_t pulse_workspace_bytes(int op, int64_t n, int64_t aux) {
     case PULSE_OP_FP8_DELTA:
     case PULSE_OP_LOCO_GATE: return pulse_delta_compact_ws_bytes(n);
     case PULSE_OP_PATCH_UNPACK: return pulse_patch_unpack_ws_bytes(n);
+    case PULSE_OP_CAST_DIFF_SEGMENTS: return sizeof(uint64_t) * 32 + (size_t)(n > 0 ? n : 1) * sizeof(uint64_t);
     default: return 0;
     }
 }
@@ -271,4 +276,45 @@ int patch_unpack(const uint8_t *packed, int64_t count, int32_t *idx, uint16_t *v
     return pulse_launch_patch_unpack(packed, count, idx, val, d_status, ws, stream);
 }
 
+static_assert(sizeof(pulse_segment) == 40, "pulse_segment is five 8-byte fields");
+static_assert(sizeof(pulse_view) == 16, "pulse_view is two 8-byte fields");
+
+int64_t pulse_segment_tiles(const int64_t *n, int32_t nseg, int64_t *tile0, uint32_t *tile_seg) {
+    if (!n || nseg < 1) return PULSE_EINVAL;
+    int64_t t = 0;
+    for (int32_t s = 0; s < nseg; ++s) {
+        if (n[s] < 1 || n[s] > kMaxIndexed) return PULSE_ERANGE;
+        const int64_t k = (n[s] + 16383) / 16384;
+        if (tile0) tile0[s] = t;
+        if (tile_seg)
+            for (int64_t j = 0; j < k; ++j) tile_seg[t + j] = (uint32_t)s;
+        t += k;
+    }
+    if (t > 0xFFFFFFFFll) return PULSE_ERANGE;
+    return t;
+}
+
+int pulse_cast_diff_segments(const pulse_segment *segs, int32_t nseg, const uint32_t *tile_seg, int64_t ntiles,
+                             int32_t *patch_idx, uint16_t *patch_val, int64_t patch_cap, int64_t *seg_offsets,
+                             uint32_t *d_status, void *ws, size_t ws_bytes, int32_t with_new, hipStream_t stream) {
+    if (!segs || !tile_seg || !patch_idx || !patch_val || !seg_offsets || !d_status || nseg < 1 || ntiles < nseg ||
+        patch_cap < 0 || (with_new != 0 && with_new != 1))
+        return PULSE_EINVAL;
+    if (ntiles > 0xFFFFFFFFll) return PULSE_ERANGE;
+    if (!ws || ws_bytes < pulse_workspace_bytes(PULSE_OP_CAST_DIFF_SEGMENTS, ntiles, 0)) return PULSE_EWORKSPACE;
+    return pulse_launch_cast_diff_segments(segs, nseg, tile_seg, ntiles, patch_idx, patch_val, patch_cap, seg_offsets,
+                                           d_status, ws, with_new, stream);
+}
+
+int pulse_apply_patch_segments(const pulse_view *views, int32_t nseg, const int32_t *patch_idx,
+                               const uint16_t *patch_val, const int64_t *seg_offsets, int64_t max_count,
+                               uint32_t *d_status, hipStream_t stream) {
+    if (!views || !patch_idx || !patch_val || !seg_offsets || !d_status || nseg < 1 || max_count < 0)
+        return PULSE_EINVAL;
+    if (max_count == 0) return PULSE_OK;
+    return pulse_launch_apply_patch_segments(views, nseg, patch_idx, patch_val, seg_offsets, max_count, d_status,
+                                             stream);
+}
+
 }  // extern "C"
+

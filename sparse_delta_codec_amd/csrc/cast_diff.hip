@@ -234,6 +234,36 @@ __device__ __forceinline__ void cd_flush(const CastDiffArgs &a, const int32_t *s
     nb = 0;
 }
 
+// Pass 2 of one wave: each changed element is ranked with ballots and staged
+// in the wave's LDS buffer at its rank; the buffer goes out with coalesced
+// stores (the wave's entries are one contiguous stretch of the patch, the
+// first at position run).
+__device__ __forceinline__ void cd_pass2(const CastDiffArgs &a, uint64_t flags, const uint32_t nvp[], int64_t wbase,
+                                         int lo, int64_t run, int32_t *sbi, uint16_t *sbv) {
+    uint32_t nb = 0;
+#pragma unroll
+    for (int g = 0; g < CD_GROUPS; ++g) {
+        const uint32_t f = (uint32_t)(flags >> (4 * g)) & 0xFu;
+        const uint64_t m0 = __ballot(f & 1u), m1 = __ballot(f & 2u), m2 = __ballot(f & 4u), m3 = __ballot(f & 8u);
+        const uint32_t gtot = __builtin_popcountll(m0) + __builtin_popcountll(m1) + __builtin_popcountll(m2) +
+                              __builtin_popcountll(m3);
+        if (gtot == 0) continue;
+        if (nb + gtot > (uint32_t)CD_SB) cd_flush(a, sbi, sbv, nb, run);
+        uint32_t r = nb + lanes_below(m0) + lanes_below(m1) + lanes_below(m2) + lanes_below(m3);
+        const int32_t e = (int32_t)(wbase + g * 256 + lo);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (f & (1u << k)) {
+                sbi[r] = e + k;
+                sbv[r] = (uint16_t)(nvp[2 * g + (k >> 1)] >> (16 * (k & 1)));
+                ++r;
+            }
+        }
+        nb += gtot;
+    }
+    if (nb) cd_flush(a, sbi, sbv, nb, run);
+}
+
 // One tile: pass 1, the tile total, its look-back, pass 2 (ranked stores).
 template <bool FULL, bool FROM_F32, bool W_NEW, bool W_MASK>
 __device__ __forceinline__ void cd_tile(const CastDiffArgs &a, uint32_t tile, uint32_t ep, CdShared &sh) {
@@ -267,36 +297,7 @@ __device__ __forceinline__ void cd_tile(const CastDiffArgs &a, uint32_t tile, ui
         }
     }
     __syncthreads();
-    int64_t run = (int64_t)sh.prefix + wpre;
-    if (tile_count != 0) {
-        // pass 2: each changed element is ranked with ballots and staged in the
-        // wave's LDS buffer at its rank; the buffer goes out with coalesced
-        // stores (the wave's entries are one contiguous stretch of the patch)
-        int32_t *sbi = sh.sbi[w];
-        uint16_t *sbv = sh.sbv[w];
-        uint32_t nb = 0;
-#pragma unroll
-        for (int g = 0; g < CD_GROUPS; ++g) {
-            const uint32_t f = (uint32_t)(flags >> (4 * g)) & 0xFu;
-            const uint64_t m0 = __ballot(f & 1u), m1 = __ballot(f & 2u), m2 = __ballot(f & 4u), m3 = __ballot(f & 8u);
-            const uint32_t gtot = __builtin_popcountll(m0) + __builtin_popcountll(m1) + __builtin_popcountll(m2) +
-                                  __builtin_popcountll(m3);
-            if (gtot == 0) continue;
-            if (nb + gtot > (uint32_t)CD_SB) cd_flush(a, sbi, sbv, nb, run);
-            uint32_t r = nb + lanes_below(m0) + lanes_below(m1) + lanes_below(m2) + lanes_below(m3);
-            const int32_t e = (int32_t)(wbase + g * 256 + lo);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                if (f & (1u << k)) {
-                    sbi[r] = e + k;
-                    sbv[r] = (uint16_t)(nvp[2 * g + (k >> 1)] >> (16 * (k & 1)));
-                    ++r;
-                }
-            }
-            nb += gtot;
-        }
-        if (nb) cd_flush(a, sbi, sbv, nb, run);
-    }
+    if (tile_count != 0) cd_pass2(a, flags, nvp, wbase, lo, (int64_t)sh.prefix + wpre, sh.sbi[w], sh.sbv[w]);
     __syncthreads();  // sh is reused by the next tile
 }
 
@@ -316,9 +317,125 @@ __global__ __launch_bounds__(CD_THREADS) void k_cast_compact(CastDiffArgs a) {
         cd_tile<false, FROM_F32, W_NEW, W_MASK>(a, nfull, ep, sh);
 }
 
+// ---- one launch over a list of tensors ---------------------------------------
+// The host prepares the tiling metadata (each tensor's first tile, and the
+// tensor of every tile), so one launch covers a whole list of tensors that
+// live anywhere in memory ("GPU weight teleportation" write-up, "Moving the
+// pipeline onto GPUs").  Tiles are tickets (one workgroup each, one atomic):
+// a tile only waits on tiles of workgroups already running.  Indices are local
+// to each tensor; the first tile of tensor s records its first entry.
+struct SegDesc {  // the layout of pulse_segment
+    const float *w_new;
+    const uint16_t *b_old;
+    uint16_t *b_new;
+    int64_t n;
+    int64_t tile0;
+};
+
+struct SegArgs {
+    const SegDesc *segs;
+    int32_t nseg;
+    const uint32_t *tile_seg;
+    uint32_t ntiles;
+    int32_t *idx;
+    uint16_t *val;
+    int64_t cap;
+    int64_t *seg_offsets;
+    uint32_t *d_status;
+    WsHeader *hdr;
+    uint64_t *status;
+};
+
+template <bool W_NEW>
+__global__ __launch_bounds__(CD_THREADS) void k_cast_compact_segments(SegArgs g) {
+    __shared__ uint32_t s_tile, s_tag;
+    __shared__ CdShared sh;
+    if (threadIdx.x == 0) {
+        uint32_t tile, tag;
+        ws_begin(g.hdr, g.ntiles, &tile, &tag);
+        s_tile = tile;
+        s_tag = tag;
+    }
+    __syncthreads();
+    const uint32_t tile = s_tile, tag = s_tag;
+    if (tile >= g.ntiles) {  // inconsistent workspace state: touch nothing
+        if (threadIdx.x == 0) or_agent32(g.d_status, 8u /*PULSE_DS_WORKSPACE*/);
+        return;
+    }
+    const uint32_t s = g.tile_seg[tile];
+    SegDesc d{};
+    if (s < (uint32_t)g.nseg) d = g.segs[s];
+    const int64_t lt = (int64_t)tile - d.tile0;  // tile within the tensor
+    const bool ok = s < (uint32_t)g.nseg && d.n >= 1 && d.n <= 2147483647ll && lt >= 0 && lt * CD_TILE < d.n &&
+                    ((reinterpret_cast<uintptr_t>(d.w_new) | reinterpret_cast<uintptr_t>(d.b_old) |
+                      reinterpret_cast<uintptr_t>(d.b_new)) & 15u) == 0 && (d.b_new != nullptr) == W_NEW;
+    CastDiffArgs a{};
+    a.w_new = d.w_new;
+    a.b_old = d.b_old;
+    a.b_new = d.b_new;
+    a.idx = g.idx;
+    a.val = g.val;
+    a.cap = g.cap;
+    a.d_status = g.d_status;
+    a.n = d.n;
+    const int w = wave_id(), l = lane_id();
+    const int64_t wbase = lt * CD_TILE + (int64_t)w * CD_WAVE_ELEMS;
+    const int lo = 4 * l;
+    uint32_t nvp[CD_GROUPS * 2];
+    uint64_t flags = 0;
+    if (ok) {
+        if ((lt + 1) * CD_TILE <= d.n) flags = cd_pass1<true, true, W_NEW, false>(a, wbase, lo, nvp);
+        else flags = cd_pass1<false, true, W_NEW, false>(a, wbase, lo, nvp);
+    }
+    const uint32_t wtot = wave_reduce_sum((uint32_t)__builtin_popcountll(flags));
+    if (l == 0) sh.wtot[w] = wtot;
+    __syncthreads();
+    uint32_t tile_count = 0, wpre = 0;
+#pragma unroll
+    for (int i = 0; i < CD_THREADS / kWave; ++i) {
+        if (i < w) wpre += sh.wtot[i];
+        tile_count += sh.wtot[i];
+    }
+    if (w == 0) {
+        bool failed = false;
+        const uint64_t pre = lookback_wave(g.status, tile, tag, tile_count, &failed);
+        if (l == 0) {
+            if (failed) or_agent32(g.d_status, 8u /*PULSE_DS_WORKSPACE*/);
+            if (!ok) or_agent32(g.d_status, 0x10u /*PULSE_DS_BADSEGMENT*/);
+            sh.prefix = pre;
+            if (ok && lt == 0) g.seg_offsets[s] = (int64_t)pre;
+            if (tile == g.ntiles - 1) g.seg_offsets[g.nseg] = (int64_t)(pre + tile_count);
+            if ((int64_t)(pre + tile_count) > g.cap) or_agent32(g.d_status, 1u /*PULSE_DS_CAPACITY*/);
+        }
+    }
+    __syncthreads();
+    if (tile_count != 0) cd_pass2(a, flags, nvp, wbase, lo, (int64_t)sh.prefix + wpre, sh.sbi[w], sh.sbv[w]);
+}
+
 }  // namespace pulse
 
 using namespace pulse;
+
+extern "C" int pulse_launch_cast_diff_segments(const void *segs, int32_t nseg, const uint32_t *tile_seg,
+                                               int64_t ntiles, int32_t *idx, uint16_t *val, int64_t cap,
+                                               int64_t *seg_offsets, uint32_t *d_status, void *ws, int with_new,
+                                               hipStream_t stream) {
+    SegArgs g{};
+    g.segs = static_cast<const SegDesc *>(segs);
+    g.nseg = nseg;
+    g.tile_seg = tile_seg;
+    g.ntiles = (uint32_t)ntiles;
+    g.idx = idx;
+    g.val = val;
+    g.cap = cap;
+    g.seg_offsets = seg_offsets;
+    g.d_status = d_status;
+    g.hdr = reinterpret_cast<WsHeader *>(ws);
+    g.status = reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + sizeof(WsHeader));
+    if (with_new) k_cast_compact_segments<true><<<dim3((unsigned)ntiles), dim3(CD_THREADS), 0, stream>>>(g);
+    else k_cast_compact_segments<false><<<dim3((unsigned)ntiles), dim3(CD_THREADS), 0, stream>>>(g);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}
 
 extern "C" int pulse_launch_cast_diff(const float *w_new, const uint16_t *b_in, const uint16_t *b_old,
                                       uint16_t *b_new, uint16_t *mask, int32_t *idx, uint16_t *val,

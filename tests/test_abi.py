@@ -153,3 +153,25 @@ def test_patch_pack_argument_errors(lib):
     assert up(al, 100000, al, al, al, al, 8, None) == EWORKSPACE
     ws = lib.pulse_workspace_bytes
     assert ws(7, 65536, 0) == 256 + 8 and ws(7, 65537, 0) == 256 + 16
+
+
+def test_segment_tiles_and_list_call_errors(lib):
+    st = lib.pulse_segment_tiles
+    st.argtypes = [V, ctypes.c_int32, V, V]
+    st.restype = I64
+    n = (I64 * 4)(1, 16384, 16385, 40000)
+    tile0 = (I64 * 4)()
+    tseg = (ctypes.c_uint32 * 8)()
+    assert st(ctypes.cast(n, V), 4, ctypes.cast(tile0, V), ctypes.cast(tseg, V)) == 1 + 1 + 2 + 3
+    assert list(tile0) == [0, 1, 2, 4] and list(tseg)[:7] == [0, 1, 2, 2, 3, 3, 3]
+    bad = (I64 * 2)(10, 0)
+    assert st(ctypes.cast(bad, V), 2, None, None) == ERANGE
+    cd = lib.pulse_cast_diff_segments
+    al = V(0x10000)
+    cd.argtypes = [V, ctypes.c_int32, V, I64, V, V, I64, V, V, V, ctypes.c_size_t, ctypes.c_int32, V]
+    assert cd(al, 2, al, 1, al, al, 10, al, al, al, 1 << 20, 0, None) == EINVAL      # fewer tiles than tensors
+    assert cd(al, 2, al, 5, al, al, 10, al, al, al, 16, 0, None) == EWORKSPACE
+    assert cd(al, 2, al, 5, al, al, 10, al, al, al, 1 << 20, 2, None) == EINVAL      # with_new 0/1
+    ap = lib.pulse_apply_patch_segments
+    ap.argtypes = [V, ctypes.c_int32, V, V, V, I64, V, V]
+    assert ap(al, 0, al, al, al, 10, al, None) == EINVAL

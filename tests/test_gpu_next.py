@@ -275,3 +275,83 @@ def test_compressed_patch_round_trip_through_the_lz4_kernels():
     assert int(host(st)[0]) == 0
     assert np.array_equal(host(I)[:m], r["idx"]) and np.array_equal(host(V, np.uint16)[:m], r["val"])
     assert np.array_equal(host(B, np.uint16), r["b_new"])
+
+
+# ---- one launch over a list of tensors -------------------------------------------------
+def tensor_list(sizes, seed):
+    rng = np.random.default_rng(seed)
+    ws, bs = [], []
+    for n in sizes:
+        w0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+        if n > 3:
+            w0[: n // 4] = (1 + rng.standard_normal(n // 4) * 0.01).astype(np.float32)
+        w1 = (w0 - np.float32(3e-6) * np.clip(rng.standard_normal(n), -3, 3).astype(np.float32)).astype(np.float32)
+        ws.append(w1)
+        bs.append(oracle.cast_bf16(w0))
+    return ws, bs
+
+
+def run_segments(ws, bs, with_new=True, cap=None):
+    W = [dev(w) for w in ws]
+    B = [dev(b) for b in bs]
+    N = [zeros(b.size, torch.int16) for b in bs] if with_new else None
+    table = pulse.SegmentTable(W, B, N)
+    total = sum(w.size for w in ws)
+    cap = total if cap is None else cap
+    idx, val = zeros(cap, torch.int32), zeros(cap, torch.int16)
+    offs, st = zeros(len(ws) + 1, torch.int64), zeros(1, torch.int32)
+    ws_ = pulse.workspace(pulse.PULSE_OP_CAST_DIFF_SEGMENTS, table.ntiles)
+    pulse.pulse_cast_diff_segments(table, idx[:cap] if cap else idx[:1], val, offs, st, ws_)
+    torch.cuda.synchronize()
+    return table, W, B, N, idx, val, offs, st
+
+
+@pytest.mark.parametrize("seed,sizes", [
+    (1, [1, 15, 16384, 16385, 40000, 3 * 16384 + 7, 2]),
+    (2, [5] * 40 + [70000]),
+    (3, list(np.random.default_rng(9).integers(1, 50000, 300))),
+])
+def test_cast_diff_segments_match_oracle(seed, sizes):
+    ws, bs = tensor_list(sizes, seed)
+    ref = oracle.cast_diff_segments(ws, bs)
+    table, W, B, N, idx, val, offs, st = run_segments(ws, bs)
+    assert int(host(st)[0]) == 0
+    assert np.array_equal(host(offs)[: len(ws) + 1], ref["seg_offsets"])
+    m = ref["count"]
+    assert np.array_equal(host(idx)[:m], ref["idx"]) and np.array_equal(host(val, np.uint16)[:m], ref["val"])
+    for s in range(len(ws)):
+        assert np.array_equal(host(N[s], np.uint16), ref["b_new"][s]), s
+    # the receiver's side over separately allocated views
+    R = [dev(b) for b in bs]
+    pulse.pulse_apply_patch_segments(pulse.ViewTable(R), idx, val, offs, st)
+    torch.cuda.synchronize()
+    assert int(host(st)[0]) == 0
+    for s in range(len(ws)):
+        assert np.array_equal(host(R[s], np.uint16), ref["b_new"][s]), s
+
+
+def test_cast_diff_segments_without_new_view_and_capacity():
+    ws, bs = tensor_list([20000, 33, 16384 * 2], 4)
+    ref = oracle.cast_diff_segments(ws, bs, cap=100)
+    table, W, B, N, idx, val, offs, st = run_segments(ws, bs, with_new=False, cap=100)
+    assert int(host(st)[0]) == pulse.PULSE_DS_CAPACITY
+    assert np.array_equal(host(offs)[:4], ref["seg_offsets"])
+    assert np.array_equal(host(idx)[:100], ref["idx"]) and np.array_equal(host(val, np.uint16)[:100], ref["val"])
+
+
+def test_cast_diff_segments_flags_a_broken_table_entry():
+    ws, bs = tensor_list([3000, 3000], 5)
+    W = [dev(w) for w in ws]
+    B = [dev(b) for b in bs]
+    table = pulse.SegmentTable(W, B)
+    tab = table.segs.cpu()
+    tab[1, 1] += 2  # b_old of tensor 1 no longer 16-byte aligned
+    table.segs = tab.cuda()
+    idx, val = zeros(6000, torch.int32), zeros(6000, torch.int16)
+    offs, st = zeros(3, torch.int64), zeros(1, torch.int32)
+    pulse.pulse_cast_diff_segments(table, idx, val, offs, st, pulse.workspace(pulse.PULSE_OP_CAST_DIFF_SEGMENTS, 2))
+    torch.cuda.synchronize()
+    ref = oracle.cast_diff_segments(ws[:1], bs[:1])
+    assert int(host(st)[0]) & pulse.PULSE_DS_BADSEGMENT
+    m = ref["count"]
+    assert host(offs)[2] == m and np.array_equal(host(idx)[:m], ref["idx"])
