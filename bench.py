@@ -49,8 +49,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-frac", type=float, default=1.0,
                    help="fraction of the oracle's sample (the attention half of layer 0) it times")
-    p.add_argument("--next", default="loco,patch", help="next-row legs measured after the timed steps, comma "
-                   "separated: loco (PULSELoCo gate), patch (patch-stream compression), fp8 (FP8-view deltas), none")
+    p.add_argument("--next", default="loco,patch,list", help="next-row legs measured after the timed steps, comma "
+                   "separated: loco (PULSELoCo gate), patch (patch-stream compression), list (one launch over the "
+                   "tensor list), fp8 (FP8-view deltas), none")
     p.add_argument("--copy-probe-gib", type=float, default=0.0,
                    help="also run a plain device copy of this size (scale reference for HBM counters)")
     return p.parse_args()
@@ -351,7 +352,12 @@ def main():
         if "fp8" in legs:
             nxt.update(fp8_view_leg(pulse, specs, chunks, offs, qplans, W, b_old, stage, dev,
                                     not args.no_cpu_baseline))
-        del W, stage, b_recv, idx, val, payload, codes, scales
+        del stage, b_recv, idx, val, payload, codes, scales
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        if "list" in legs:
+            nxt.update(tensor_list_leg(pulse, specs, offs, W, b_old, changed, dev))
+        del W, b_old
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
         if "loco" in legs:
@@ -366,6 +372,88 @@ def _leg(ms, launches, alg_bytes, **extra):
            "GBps": round(alg_bytes / secs / 1e9, 1), "frac_hbm": round(alg_bytes / secs / PEAK_HBM, 4)}
     out.update(extra)
     return out
+
+
+def tensor_list_leg(pulse, specs, offs, W, b_old, changed, dev):
+    """One launch over the whole tensor list (771 tensors of the Qwen2.5-32B
+    shape, each addressed through the host-prepared table) against one
+    pulse_cast_diff launch per tensor, both writing the patch only; then the
+    list apply into the old views.  Checks: the two patch streams are equal
+    tensor by tensor, their total is the main step's count, and the applied
+    views equal the cast of the masters."""
+    import torch
+
+    nt = len(specs)
+    views = [b_old[offs[i]: offs[i] + s.numel] for i, s in enumerate(specs)]
+    masters = [W[offs[i]: offs[i] + s.numel] for i, s in enumerate(specs)]
+    caps = [s.numel // 8 + 1024 for s in specs]  # 12.5% per tensor (+ slack for tiny ones)
+    coff = [0]
+    for c in caps:
+        coff.append(coff[-1] + (c + 3) // 4 * 4)
+    cap = coff[-1]
+    idx = torch.empty(cap, dtype=torch.int32, device=dev)
+    val = torch.empty(cap, dtype=torch.int16, device=dev)
+    idx2 = torch.empty(cap, dtype=torch.int32, device=dev)
+    val2 = torch.empty(cap, dtype=torch.int16, device=dev)
+    cnt = torch.zeros(nt, dtype=torch.int64, device=dev)
+    seg_off = torch.zeros(nt + 1, dtype=torch.int64, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    table = pulse.SegmentTable(masters, views)
+    ws_seg = pulse.workspace(pulse.PULSE_OP_CAST_DIFF_SEGMENTS, table.ntiles, 0, dev)
+    ws_cd = pulse.workspace(pulse.PULSE_OP_CAST_DIFF, max(s.numel for s in specs), 0, dev)
+    log(f"tensor-list leg: {nt} tensors, {table.ntiles} tiles")
+
+    def per_tensor():
+        for i in range(nt):
+            pulse.pulse_cast_diff(masters[i], views[i], None, None, idx2[coff[i]: coff[i] + caps[i]],
+                                  val2[coff[i]: coff[i] + caps[i]], cnt[i:i + 1], st, ws_cd)
+
+    def one_launch():
+        pulse.pulse_cast_diff_segments(table, idx, val, seg_off, st, ws_seg)
+
+    times = {}
+    for name, fn in (("per_tensor", per_tensor), ("list", one_launch)):
+        fn()  # warm-up
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        times[name] = ev[0].elapsed_time(ev[1])
+    if int(st.item()) != 0:
+        raise SystemExit(f"tensor-list leg: device status {int(st.item())}")
+    so = seg_off.cpu().tolist()
+    cn = cnt.cpu().tolist()
+    if so[-1] != changed:
+        raise SystemExit(f"tensor-list leg: {so[-1]} entries, the main step found {changed}")
+    for i in range(nt):
+        m = so[i + 1] - so[i]
+        if m != cn[i] or not (torch.equal(idx[so[i]: so[i + 1]], idx2[coff[i]: coff[i] + m]) and
+                              torch.equal(val[so[i]: so[i + 1]], val2[coff[i]: coff[i] + m])):
+            raise SystemExit(f"tensor-list leg: tensor {i} differs between the list call and its own call")
+    del idx2, val2
+    vt = pulse.ViewTable(views)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    pulse.pulse_apply_patch_segments(vt, idx, val, seg_off, st, max_count=so[-1])
+    ev[1].record()
+    torch.cuda.synchronize()
+    t_apply = ev[0].elapsed_time(ev[1])
+    tmp = torch.empty(max(s.numel for s in specs), dtype=torch.int16, device=dev)
+    for i in range(nt):
+        pulse.pulse_cast_diff(masters[i], b_new=tmp[: specs[i].numel])
+        if not views_equal(views[i], tmp[: specs[i].numel]):
+            raise SystemExit(f"tensor-list leg: view {i} differs from the cast of its masters after the apply")
+    if int(st.item()) != 0:
+        raise SystemExit(f"tensor-list leg: device status {int(st.item())} after the apply")
+    n = sum(s.numel for s in specs)
+    log(f"tensor-list leg: one launch {times['list']:.2f} ms, {nt} launches {times['per_tensor']:.2f} ms")
+    a_cd = n * 6 + 6 * changed  # read masters (4) + old view (2), write the patch
+    return {"cast_diff_list": _leg(times["list"], 1, a_cd, tensors=nt, tiles=table.ntiles,
+                                   checked="equal, tensor by tensor, to one pulse_cast_diff per tensor"),
+            "cast_diff_per_tensor": _leg(times["per_tensor"], nt, a_cd),
+            "apply_list": _leg(t_apply, 1, 8 * changed, checked="every view equals the cast of its masters")}
 
 
 def patch_stream_leg(pulse, chunks, W, b_old, stage, idx, val, cnt, status, ws_cd, dev, with_oracle):
