@@ -4,6 +4,8 @@
 // Decoupled Look-back", 2016) used to place per-tile outputs in order.
 #pragma once
 
+#include <limits>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -18,39 +20,98 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 __device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
 
-// ---- wave-level scans and reductions (ds_bpermute based shuffles) ----------
+// ---- wave-level scans and reductions -----------------------------------------
+// 32-bit scans use DPP (data-parallel primitives of the GFX9 ISA): row shifts
+// inside each 16-lane row, then the row broadcasts of lane 15 and lane 31, one
+// VALU operation per step and no LDS; wider types use ds_bpermute shuffles.
+// Lanes whose DPP source does not exist keep `old` (bound_ctrl off).
+template <int CTRL, int ROWM, int BANKM, typename T>
+__device__ __forceinline__ T dpp_mov(T old, T v) {
+    static_assert(sizeof(T) == 4, "32-bit DPP move");
+    return __builtin_bit_cast(T, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old), __builtin_bit_cast(int, v),
+                                                            CTRL, ROWM, BANKM, false));
+}
+namespace dppc {
+constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowShl1 = 0x101, kRowShl2 = 0x102, kRowShl4 = 0x104, kRowShl8 = 0x108;
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143, kWaveShr1 = 0x138, kWaveShl1 = 0x130;
+}  // namespace dppc
+
 template <typename T>
 __device__ __forceinline__ T wave_incl_sum(T v) {
-    const int lane = lane_id();
+    if constexpr (sizeof(T) == 4) {
+        using namespace dppc;
+        v += dpp_mov<kRowShr1, 0xf, 0xf>(T(0), v);
+        v += dpp_mov<kRowShr2, 0xf, 0xf>(T(0), v);
+        v += dpp_mov<kRowShr4, 0xf, 0xe>(T(0), v);
+        v += dpp_mov<kRowShr8, 0xf, 0xc>(T(0), v);
+        v += dpp_mov<kRowBcast15, 0xa, 0xf>(T(0), v);
+        v += dpp_mov<kRowBcast31, 0xc, 0xf>(T(0), v);
+        return v;
+    } else {
+        const int lane = lane_id();
 #pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        T o = __shfl_up(v, d, kWave);
-        if (lane >= d) v += o;
+        for (int d = 1; d < kWave; d <<= 1) {
+            T o = __shfl_up(v, d, kWave);
+            if (lane >= d) v += o;
+        }
+        return v;
     }
-    return v;
 }
 
 template <typename T>
 __device__ __forceinline__ T wave_incl_max(T v) {
-    const int lane = lane_id();
+    if constexpr (sizeof(T) == 4) {
+        using namespace dppc;
+        const T id = std::numeric_limits<T>::lowest();
+        T o;
+        o = dpp_mov<kRowShr1, 0xf, 0xf>(id, v); v = o > v ? o : v;
+        o = dpp_mov<kRowShr2, 0xf, 0xf>(id, v); v = o > v ? o : v;
+        o = dpp_mov<kRowShr4, 0xf, 0xe>(id, v); v = o > v ? o : v;
+        o = dpp_mov<kRowShr8, 0xf, 0xc>(id, v); v = o > v ? o : v;
+        o = dpp_mov<kRowBcast15, 0xa, 0xf>(id, v); v = o > v ? o : v;
+        o = dpp_mov<kRowBcast31, 0xc, 0xf>(id, v); v = o > v ? o : v;
+        return v;
+    } else {
+        const int lane = lane_id();
 #pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        T o = __shfl_up(v, d, kWave);
-        if (lane >= d) v = o > v ? o : v;
+        for (int d = 1; d < kWave; d <<= 1) {
+            T o = __shfl_up(v, d, kWave);
+            if (lane >= d) v = o > v ? o : v;
+        }
+        return v;
     }
-    return v;
 }
 
 // inclusive scan from the top lane down: lane l gets min(v[l..63])
 template <typename T>
 __device__ __forceinline__ T wave_incl_min_rev(T v) {
-    const int lane = lane_id();
+    if constexpr (sizeof(T) == 4) {
+        using namespace dppc;
+        const T id = std::numeric_limits<T>::max();
+        T o;
+        o = dpp_mov<kRowShl1, 0xf, 0xf>(id, v); v = o < v ? o : v;
+        o = dpp_mov<kRowShl2, 0xf, 0xf>(id, v); v = o < v ? o : v;
+        o = dpp_mov<kRowShl4, 0xf, 0x7>(id, v); v = o < v ? o : v;
+        o = dpp_mov<kRowShl8, 0xf, 0x3>(id, v); v = o < v ? o : v;
+        // lane 16 r now holds the minimum of row r; add the rows above
+        const T r1 = __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+        const T r2 = __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+        const T r3 = __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+        const T s2 = r2 < r3 ? r2 : r3;
+        const T s1 = r1 < s2 ? r1 : s2;
+        const int row = lane_id() >> 4;
+        const T above = row == 0 ? s1 : (row == 1 ? s2 : (row == 2 ? r3 : id));
+        return above < v ? above : v;
+    } else {
+        const int lane = lane_id();
 #pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        T o = __shfl_down(v, d, kWave);
-        if (lane + d < kWave) v = o < v ? o : v;
+        for (int d = 1; d < kWave; d <<= 1) {
+            T o = __shfl_down(v, d, kWave);
+            if (lane + d < kWave) v = o < v ? o : v;
+        }
+        return v;
     }
-    return v;
 }
 
 template <typename T>
@@ -103,8 +164,13 @@ __device__ __forceinline__ T block_excl_sum(T v, T *sh, T *total) {
 template <int NW, typename T>
 __device__ __forceinline__ T block_excl_max(T v, T lo, T *sh, T *total) {
     T incl = wave_incl_max(v);
-    T excl = __shfl_up(incl, 1, kWave);
-    if (lane_id() == 0) excl = lo;
+    T excl;
+    if constexpr (sizeof(T) == 4) {
+        excl = dpp_mov<dppc::kWaveShr1, 0xf, 0xf>(lo, incl);
+    } else {
+        excl = __shfl_up(incl, 1, kWave);
+        if (lane_id() == 0) excl = lo;
+    }
     if (lane_id() == kWave - 1) sh[wave_id()] = incl;
     __syncthreads();
     T base = lo, tot = lo;
@@ -123,8 +189,13 @@ __device__ __forceinline__ T block_excl_max(T v, T lo, T *sh, T *total) {
 template <int NW, typename T>
 __device__ __forceinline__ T block_excl_min_rev(T v, T hi, T *sh) {
     T incl = wave_incl_min_rev(v);
-    T excl = __shfl_down(incl, 1, kWave);
-    if (lane_id() == kWave - 1) excl = hi;
+    T excl;
+    if constexpr (sizeof(T) == 4) {
+        excl = dpp_mov<dppc::kWaveShl1, 0xf, 0xf>(hi, incl);
+    } else {
+        excl = __shfl_down(incl, 1, kWave);
+        if (lane_id() == kWave - 1) excl = hi;
+    }
     if (lane_id() == 0) sh[wave_id()] = incl;
     __syncthreads();
     T base = hi;
