@@ -63,12 +63,6 @@ __device__ __forceinline__ int32_t seq_bytes(int32_t ll, int32_t ml) {
     return 1 + ext_bytes(ll) + ll + 2 + ext_bytes(ml - 4);
 }
 
-// bit k of the result is set iff byte k of x is non-zero
-__device__ __forceinline__ uint32_t nonzero_bytes(uint32_t x) {
-    const uint32_t hi = (((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x) & 0x80808080u;
-    return (((hi >> 7) * 0x00204081u) >> 21) & 0xFu;
-}
-
 // LDS image of a block: chunk c (CH = 2^CHLOG bytes, NPC = CH/16 pieces) at
 // c*CH, its 16-byte piece k stored at slot k ^ ((c >> (4 - log2 NPC)) & (NPC-1)):
 // any 16 consecutive lanes, whether writing consecutive pieces or reading the
@@ -212,24 +206,47 @@ __device__ __forceinline__ void enc_block(const Lz4EncArgs &a, uint32_t b, uint3
     // 2. run-boundary bitmask of this thread's chunk
     const int32_t cs = t * CH;
     const int32_t cl = len - cs < 0 ? 0 : (len - cs < CH ? len - cs : CH);
-    uint64_t m = 0;
+    // byte p differs from byte p - 1: the high bit of each byte of
+    // ((x & 0x7F..) + 0x7F..) | x, x = d ^ (d << 8 | previous byte); the flags
+    // of two dwords (bits 7, 15, 23, 31 of each, the first shifted down by 4)
+    // are gathered into 8 bits by one multiply: no two of the shifted copies
+    // land on the same bit, so no carries
+    constexpr int NW = (CH + 31) / 32;
+    uint32_t mw[NW];
+#pragma unroll
+    for (int i = 0; i < NW; ++i) mw[i] = 0;
     if (cl > 0) {
-        uint32_t pb = (t > 0) ? s_img[img_addr<CHLOG>(cs - 1)] : 0u;
+        uint32_t prev = (t > 0) ? ((uint32_t)s_img[img_addr<CHLOG>(cs - 1)] << 24) : 0u;
 #pragma unroll
         for (int32_t q = 0; q < CH; q += 16) {
             const uint4 v = *reinterpret_cast<const uint4 *>(s_img + img_addr<CHLOG>(cs + q));
             const uint32_t d[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int32_t p0 = q + 4 * k;
-                uint32_t nib = nonzero_bytes(d[k] ^ ((d[k] << 8) | pb));
-                pb = d[k] >> 24;
-                if (p0 == 0 && t == 0) nib |= 1u;  // a run starts at the block start
-                if (p0 + 4 > cl) nib &= (p0 >= cl) ? 0u : ((1u << (cl - p0)) - 1u);
-                m |= (uint64_t)nib << p0;
+            for (int k = 0; k < 4; k += 2) {
+                uint32_t h[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const uint32_t x = d[k + e] ^ __builtin_amdgcn_alignbyte(d[k + e], prev, 3);
+                    prev = d[k + e];
+                    h[e] = (((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x) & 0x80808080u;
+                }
+                const uint32_t byte8 = (((h[0] >> 4) | h[1]) * 0x00204081u) >> 24;
+                const int p0 = q + 4 * k;
+                mw[p0 >> 5] |= byte8 << (p0 & 31);
+            }
+        }
+        if (t == 0) mw[0] |= 1u;  // a run starts at the block start
+        if (cl < CH) {            // the block's last, partial chunk
+#pragma unroll
+            for (int i = 0; i < NW; ++i) {
+                const int32_t lo = 32 * i;
+                mw[i] &= cl <= lo ? 0u : (cl - lo >= 32 ? ~0u : ((1u << (cl - lo)) - 1u));
             }
         }
     }
+    uint64_t m = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) m |= (uint64_t)mw[i] << (32 * i);
     const int32_t first_b = m ? cs + __builtin_ctzll(m) : len;
     const int32_t next_after = block_excl_min_rev<LZE_THREADS / kWave>(first_b, len, s_i32);
 
