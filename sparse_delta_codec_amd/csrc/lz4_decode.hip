@@ -372,45 +372,59 @@ __device__ __forceinline__ void k2_segment(Src src, uint32_t S, uint32_t nseq, u
 }
 
 // The same from the LDS stage (the block's bytes start at stage + mis).  The
-// common sequence of a sparse mask -- 1 to 4 literals ending in a zero byte
+// common sequence of a sparse mask -- 1 to 12 literals ending in a zero byte
 // (the first byte of the zero run the match repeats, so no fill), offset 1, at
-// most one match-length byte -- is decoded from one 8-byte window (three
-// aligned dwords joined by byte-align shifts): one LDS round trip and no
-// branches.  The first sequence of another shape ends the fast loop and the
-// rest of the segment goes byte by byte.
+// most one match-length byte -- is decoded from one 16-byte window (five
+// aligned dwords joined by byte-align shifts): one LDS round trip; only the
+// non-zero literal bytes are written (the image is zeroed).  Any other
+// sequence goes byte by byte, and the next one is tried on the fast path again.
+__device__ __forceinline__ uint32_t win_byte(uint64_t lo, uint64_t hi, uint32_t i) {
+    return (uint32_t)((i < 8 ? lo : hi) >> (8 * (i & 7))) & 0xFFu;
+}
+
 __device__ __forceinline__ void k2_segment_lds(const uint8_t *stage, uint32_t mis, uint32_t S, uint32_t nseq,
                                                uint32_t s, uint2 c, uint8_t *img, K2Queue &qu) {
     uint32_t ip = c.x, op = c.y;
     const uint32_t rest = nseq - s * kCkEvery;
     const uint32_t kend = rest < kCkEvery ? rest : kCkEvery;
-    uint32_t k = 0;
-    for (; k < kend; ++k) {
+    const uint8_t *src = stage + mis;
+    for (uint32_t k = 0; k < kend; ++k) {
         const uint32_t P = mis + ip;
         const uint32_t *d = reinterpret_cast<const uint32_t *>(stage + (P & ~3u));
-        const uint32_t d0 = d[0], d1 = d[1], d2 = d[2];  // (past the block: stage padding, unused)
-        const uint32_t w0 = __builtin_amdgcn_alignbyte(d1, d0, P & 3u);
-        const uint32_t w1 = __builtin_amdgcn_alignbyte(d2, d1, P & 3u);
-        const uint64_t u = ((uint64_t)w1 << 32) | w0;  // bytes ip .. ip+7
+        const uint32_t d0 = d[0], d1 = d[1], d2 = d[2], d3 = d[3], d4 = d[4];  // (past the block: padding, unused)
+        const uint32_t sh = P & 3u;
+        const uint32_t w0 = __builtin_amdgcn_alignbyte(d1, d0, sh), w1 = __builtin_amdgcn_alignbyte(d2, d1, sh);
+        const uint32_t w2 = __builtin_amdgcn_alignbyte(d3, d2, sh), w3 = __builtin_amdgcn_alignbyte(d4, d3, sh);
+        const uint64_t lo = ((uint64_t)w1 << 32) | w0, hi = ((uint64_t)w3 << 32) | w2;  // bytes ip .. ip+15
         const uint32_t ll = (w0 >> 4) & 15u, mc = w0 & 15u;
-        const uint32_t lsh = ll <= 4 ? ll : 4u;
-        const uint32_t lastb = (uint32_t)(u >> (8 * lsh)) & 0xFFu;     // literal byte ll
-        const uint32_t x = (uint32_t)(u >> (8 * (3 + lsh))) & 0xFFu;   // byte 3 + ll
+        const uint32_t lc = ll <= 12 ? ll : 12u;
+        const uint32_t lastb = win_byte(lo, hi, lc);  // literal byte ll
+        const uint32_t x = win_byte(lo, hi, lc + 3);  // byte 3 + ll
         // (bitwise, not short-circuit: one branch)
-        const uint32_t fast = (uint32_t)(ll - 1u < 4u) & (uint32_t)(lastb == 0) & (uint32_t)(ip + 1 + ll < S) &
+        const uint32_t fast = (uint32_t)(ll - 1u < 12u) & (uint32_t)(lastb == 0) & (uint32_t)(ip + 1 + ll < S) &
                               (uint32_t)((mc != 15) | (x != 255));
-        if (!fast) break;
-        // literal bytes 1 .. ll-1 (byte ll is zero and the image is zeroed)
-        const uint32_t b1 = (w0 >> 8) & 0xFFu, b2 = (w0 >> 16) & 0xFFu, b3 = w0 >> 24;
-        if (ll > 1 && b1) img[op] = (uint8_t)b1;
-        if (ll > 2 && b2) img[op + 1] = (uint8_t)b2;
-        if (ll > 3 && b3) img[op + 2] = (uint8_t)b3;
-        const uint32_t ext = mc == 15 ? 1u : 0u;
-        op += ll + mc + 4 + (ext ? x : 0u);
-        ip += 3 + ll + ext;
+        if (fast) {
+            // non-zero literal bytes 1 .. ll-1: high bit of each byte of
+            // ((w & 0x7F..) + 0x7F..) | w, two words' flags gathered per multiply
+            uint32_t h[4];
+            const uint32_t wv[4] = {w0, w1, w2, w3};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h[e] = (((wv[e] & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | wv[e]) & 0x80808080u;
+            const uint32_t nz16 = ((((h[0] >> 4) | h[1]) * 0x00204081u) >> 24) |
+                                  (((((h[2] >> 4) | h[3]) * 0x00204081u) >> 24) << 8);
+            uint32_t nz = nz16 & ((1u << ll) - 2u);
+            while (nz) {
+                const uint32_t i = (uint32_t)__builtin_ctz(nz);
+                nz &= nz - 1;
+                img[op + i - 1] = (uint8_t)win_byte(lo, hi, i);
+            }
+            const uint32_t ext = mc == 15 ? 1u : 0u;
+            op += ll + mc + 4 + (ext ? x : 0u);
+            ip += 3 + ll + ext;
+        } else if (!k2_seq_bytes(src, S, ip, op, img, qu)) {
+            break;
+        }
     }
-    const uint8_t *src = stage + mis;
-    for (; k < kend; ++k)
-        if (!k2_seq_bytes(src, S, ip, op, img, qu)) break;
 }
 
 // Thread t rebuilds segments t, t + 256, ...; the first from the checkpoint c0
@@ -540,7 +554,7 @@ __device__ __forceinline__ void k2_block(const Lz4DecArgs &a, int64_t b, uint32_
 template <int IMG, bool XOR>
 __global__ __launch_bounds__(K2_THREADS) void k_lz4_fast(Lz4DecArgs a) {
     __shared__ __align__(16) uint8_t s_img[IMG];
-    __shared__ __align__(16) uint8_t s_stage[K2_STAGE + 16];  // (+16: the 8-byte windows may read past the data)
+    __shared__ __align__(16) uint8_t s_stage[K2_STAGE + 32];  // (+32: the 16-byte windows may read past the data)
     __shared__ K2Queue s_q;
     const int64_t b = blockIdx.x;
     const uint32_t info = a.binfo[b];
