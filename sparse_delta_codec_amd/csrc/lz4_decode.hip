@@ -71,6 +71,11 @@ __device__ __forceinline__ uint32_t block_len(const Lz4DecArgs &a, int64_t b) {
     return (uint32_t)(rest < a.block_bytes ? rest : a.block_bytes);
 }
 
+// byte i (0 .. 15) of a 16-byte window held as two little-endian 64-bit halves
+__device__ __forceinline__ uint32_t win_byte(uint64_t lo, uint64_t hi, uint32_t i) {
+    return (uint32_t)((i < 8 ? lo : hi) >> (8 * (i & 7))) & 0xFFu;
+}
+
 // ---- K1 ----------------------------------------------------------------------
 constexpr int K1_RING = 512;                   // bytes of compressed stream held per lane
 constexpr int K1_PIECES = K1_RING / 16;        // 16-byte pieces per ring
@@ -164,7 +169,41 @@ __device__ __forceinline__ WalkResult k1_walk(uint8_t *rings, const uint8_t *rin
             const bool run = !(f & (F_DONE | F_STALL));
             if (!__ballot(run)) break;
             if (run) {
+                bool took = false;
                 if (!(f & F_OFF)) {
+                    // fast step: a whole canonical sequence (1 to 12 literals,
+                    // offset 1, at most one match-length byte, inside the
+                    // block and the output) from one 16-byte window of the
+                    // ring; everything the general step would check holds
+                    const uint32_t r = ip - (uint32_t)rb;
+                    if (ip < S && r + 20 <= (uint32_t)K1_RING) {
+                        const uint32_t *d = reinterpret_cast<const uint32_t *>(ring + (r & ~3u));
+                        const uint32_t d0 = d[0], d1 = d[1], d2 = d[2], d3 = d[3], d4 = d[4];
+                        const uint32_t sh = r & 3u;
+                        const uint32_t w0 = __builtin_amdgcn_alignbyte(d1, d0, sh);
+                        const uint32_t w1 = __builtin_amdgcn_alignbyte(d2, d1, sh);
+                        const uint32_t w2 = __builtin_amdgcn_alignbyte(d3, d2, sh);
+                        const uint32_t w3 = __builtin_amdgcn_alignbyte(d4, d3, sh);
+                        const uint64_t lo = ((uint64_t)w1 << 32) | w0, hi = ((uint64_t)w3 << 32) | w2;
+                        const uint32_t ll = (w0 >> 4) & 15u, mc = w0 & 15u;
+                        const uint32_t lc = ll <= 12 ? ll : 12u;
+                        const uint32_t mo = win_byte(lo, hi, lc + 1) | (win_byte(lo, hi, lc + 2) << 8);
+                        const uint32_t x = win_byte(lo, hi, lc + 3);
+                        const uint32_t ext = mc == 15 ? 1u : 0u;
+                        const uint32_t seq_in = 3 + ll + ext, ml = mc + 4 + (ext ? x : 0u);
+                        const uint32_t fast = (uint32_t)(ll - 1u < 12u) & (uint32_t)(mo == 1) &
+                                              (uint32_t)((mc != 15) | (x != 255)) & (uint32_t)(seq_in <= S - ip) &
+                                              (uint32_t)(ll + ml <= len - op);
+                        if (fast) {
+                            if (nseq % kCkEvery == 0) ck[nseq / kCkEvery] = make_uint2(ip, op);
+                            ++nseq;
+                            ip += seq_in;
+                            op += ll + ml;
+                            took = true;
+                        }
+                    }
+                }
+                if (!took && !(f & F_OFF)) {
                     const uint32_t r = ip - (uint32_t)rb;
                     if (ip >= S) {
                         f |= F_BAD | F_DONE;
@@ -188,7 +227,7 @@ __device__ __forceinline__ WalkResult k1_walk(uint8_t *rings, const uint8_t *rin
                         }
                     }
                 }
-                if ((f & (F_OFF | F_DONE | F_STALL)) == F_OFF) {
+                if (!took && (f & (F_OFF | F_DONE | F_STALL)) == F_OFF) {
                     const uint32_t r = ip - (uint32_t)rb;
                     if (S - ip < 2) {
                         f |= F_BAD | F_DONE;
@@ -378,10 +417,6 @@ __device__ __forceinline__ void k2_segment(Src src, uint32_t S, uint32_t nseq, u
 // aligned dwords joined by byte-align shifts): one LDS round trip; only the
 // non-zero literal bytes are written (the image is zeroed).  Any other
 // sequence goes byte by byte, and the next one is tried on the fast path again.
-__device__ __forceinline__ uint32_t win_byte(uint64_t lo, uint64_t hi, uint32_t i) {
-    return (uint32_t)((i < 8 ? lo : hi) >> (8 * (i & 7))) & 0xFFu;
-}
-
 __device__ __forceinline__ void k2_segment_lds(const uint8_t *stage, uint32_t mis, uint32_t S, uint32_t nseq,
                                                uint32_t s, uint2 c, uint8_t *img, K2Queue &qu) {
     uint32_t ip = c.x, op = c.y;
