@@ -264,6 +264,31 @@ __device__ __forceinline__ void cd_pass2(const CastDiffArgs &a, uint64_t flags, 
     if (nb) cd_flush(a, sbi, sbv, nb, run);
 }
 
+// Ranks and stages the wave's changed elements in its LDS buffer without
+// storing them (the caller guarantees they fit); nb becomes their number.
+__device__ __forceinline__ void cd_stage(uint64_t flags, const uint32_t nvp[], int64_t wbase, int lo, int32_t *sbi,
+                                         uint16_t *sbv, uint32_t &nb) {
+#pragma unroll
+    for (int g = 0; g < CD_GROUPS; ++g) {
+        const uint32_t f = (uint32_t)(flags >> (4 * g)) & 0xFu;
+        const uint64_t m0 = __ballot(f & 1u), m1 = __ballot(f & 2u), m2 = __ballot(f & 4u), m3 = __ballot(f & 8u);
+        const uint32_t gtot = __builtin_popcountll(m0) + __builtin_popcountll(m1) + __builtin_popcountll(m2) +
+                              __builtin_popcountll(m3);
+        if (gtot == 0) continue;
+        uint32_t r = nb + lanes_below(m0) + lanes_below(m1) + lanes_below(m2) + lanes_below(m3);
+        const int32_t e = (int32_t)(wbase + g * 256 + lo);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (f & (1u << k)) {
+                sbi[r] = e + k;
+                sbv[r] = (uint16_t)(nvp[2 * g + (k >> 1)] >> (16 * (k & 1)));
+                ++r;
+            }
+        }
+        nb += gtot;
+    }
+}
+
 // One tile: pass 1, the tile total, its look-back, pass 2 (ranked stores).
 template <bool FULL, bool FROM_F32, bool W_NEW, bool W_MASK>
 __device__ __forceinline__ void cd_tile(const CastDiffArgs &a, uint32_t tile, uint32_t ep, CdShared &sh) {
@@ -283,21 +308,41 @@ __device__ __forceinline__ void cd_tile(const CastDiffArgs &a, uint32_t tile, ui
         if (i < w) wpre += sh.wtot[i];
         tile_count += sh.wtot[i];
     }
-    if (w == 0) {
-        bool failed = false;
-        const uint64_t pre = lookback_wave(a.status, tile, tag, tile_count, &failed);
-        if (l == 0) {
-            if (failed) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
-            sh.prefix = pre;
-            if (tile == a.ntiles - 1) {
-                *a.d_count = (int64_t)(pre + tile_count);
-                ws_epoch_advance(a.hdr, ep);
-            }
-            if ((int64_t)(pre + tile_count) > a.cap) or_agent32(a.d_status, 1u /*PULSE_DS_CAPACITY*/);
+    uint32_t wmax = 0;
+#pragma unroll
+    for (int i = 0; i < CD_THREADS / kWave; ++i) wmax = sh.wtot[i] > wmax ? sh.wtot[i] : wmax;
+    auto place = [&](uint64_t pre, bool failed) {  // lane 0 of wave 0
+        if (failed) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
+        sh.prefix = pre;
+        if (tile == a.ntiles - 1) {
+            *a.d_count = (int64_t)(pre + tile_count);
+            ws_epoch_advance(a.hdr, ep);
         }
+        if ((int64_t)(pre + tile_count) > a.cap) or_agent32(a.d_status, 1u /*PULSE_DS_CAPACITY*/);
+    };
+    if (wmax <= (uint32_t)CD_SB) {
+        // every wave's entries fit its LDS buffer: publish the tile's count,
+        // rank and stage while the predecessors' counts arrive, then store
+        if (w == 0) lookback_publish(a.status, tile, tag, tile_count);
+        uint32_t nb = 0;
+        if (wtot != 0) cd_stage(flags, nvp, wbase, lo, sh.sbi[w], sh.sbv[w], nb);
+        if (w == 0) {
+            bool failed = false;
+            const uint64_t pre = lookback_resolve(a.status, tile, tag, tile_count, &failed);
+            if (l == 0) place(pre, failed);
+        }
+        __syncthreads();
+        int64_t run = (int64_t)sh.prefix + wpre;
+        if (nb) cd_flush(a, sh.sbi[w], sh.sbv[w], nb, run);
+    } else {
+        if (w == 0) {
+            bool failed = false;
+            const uint64_t pre = lookback_wave(a.status, tile, tag, tile_count, &failed);
+            if (l == 0) place(pre, failed);
+        }
+        __syncthreads();
+        if (tile_count != 0) cd_pass2(a, flags, nvp, wbase, lo, (int64_t)sh.prefix + wpre, sh.sbi[w], sh.sbv[w]);
     }
-    __syncthreads();
-    if (tile_count != 0) cd_pass2(a, flags, nvp, wbase, lo, (int64_t)sh.prefix + wpre, sh.sbi[w], sh.sbv[w]);
     __syncthreads();  // sh is reused by the next tile
 }
 
