@@ -567,13 +567,17 @@ __device__ __forceinline__ void k2_block(const Lz4DecArgs &a, int64_t b, uint32_
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
         const uint32_t c = t + K2_THREADS * k;
-        if (c < nfull) {
-            const u32x4 v = reinterpret_cast<const u32x4 *>(s_img)[c];
-            if constexpr (XOR) {
-                if ((v.x | v.y | v.z | v.w) != 0u) reinterpret_cast<u32x4 *>(dst4)[c] = dv[k] ^ v;
-            } else {
-                reinterpret_cast<u32x4 *>(dst4)[c] = v;
-            }
+        const u32x4 v = reinterpret_cast<const u32x4 *>(s_img)[c < nchunk ? c : 0];
+        if constexpr (XOR) {
+            // a 64-byte line (four 16-byte chunks, four neighbouring lanes) is
+            // written whole when any of its chunks changes, else not at all:
+            // no partially written lines
+            uint32_t nz = (v.x | v.y | v.z | v.w) != 0u ? 1u : 0u;
+            nz |= dpp_mov<0xB1, 0xf, 0xf>(0u, nz);  // quad_perm [1,0,3,2]
+            nz |= dpp_mov<0x4E, 0xf, 0xf>(0u, nz);  // quad_perm [2,3,0,1]
+            if (c < nfull && nz) reinterpret_cast<u32x4 *>(dst4)[c] = dv[k] ^ v;
+        } else {
+            if (c < nfull) reinterpret_cast<u32x4 *>(dst4)[c] = v;
         }
     }
     if (nfull < nchunk && (uint32_t)t == nfull % K2_THREADS) {  // ragged tail of the last block
