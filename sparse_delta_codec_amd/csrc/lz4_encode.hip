@@ -26,11 +26,11 @@
 //     last qualifying j before it, first qualifying i after it, byte offsets);
 //  4. decoupled look-back over blocks gives the block's payload offset;
 //  5. emission: each thread writes its sequences' headers and the literal bytes
-//     of its own chunk; when the block's encoding fits the 14 KiB LDS window
-//     (every block of a sparse mask) the bytes go there, relative to the
-//     block's start, while wave 0 waits for the predecessors' sizes, and are
-//     then copied out with 16-byte stores; otherwise the offset comes first
-//     and the bytes go straight to the payload.
+//     of its own chunk into a 14 KiB LDS window, relative to the block's
+//     start, while wave 0 waits for the predecessors' sizes; the window is
+//     then copied out with 16-byte stores.  Every block of a sparse mask fits
+//     one window; a larger encoding (incompressible bytes) takes several
+//     window passes, each thread emitting only in the passes its bytes reach.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -57,7 +57,12 @@ struct Lz4EncArgs {
     uint32_t nblocks;
 };
 
-__device__ __forceinline__ int32_t ext_bytes(int32_t v) { return v >= 15 ? (v - 15) / 255 + 1 : 0; }
+// extra length bytes of a length nibble: 0 below 15, else (v - 15) / 255 + 1,
+// which is (v + 240) / 255 for every v >= 0; the multiply-shift divides
+// exactly for v + 240 < 66299 (lengths here are at most 65536)
+__device__ __forceinline__ int32_t ext_bytes(int32_t v) {
+    return (int32_t)((uint32_t)__umul24((uint32_t)v + 240u, 0x8081u) >> 23);
+}
 
 __device__ __forceinline__ int32_t seq_bytes(int32_t ll, int32_t ml) {
     return 1 + ext_bytes(ll) + ll + 2 + ext_bytes(ml - 4);
@@ -104,29 +109,36 @@ __device__ __forceinline__ int32_t run_end(uint64_t m, int u, int32_t cs, int32_
     return after ? cs + u + 1 + (int32_t)__builtin_ctzll(after) : next_after;
 }
 
-// extra length bytes of a nibble capped at 15: 255s then a byte < 255
-template <typename P>
-__device__ __forceinline__ int32_t put_len(P out, int32_t pos, int32_t v) {
-    int32_t rem = v - 15;
-    while (rem >= 255) {
-        out[pos++] = 255;
-        rem -= 255;
-    }
-    out[pos++] = (uint8_t)rem;
-    return pos;
+// Output byte x of the window pass that holds bytes [wb, wb + LZE_WIN) lives
+// at win[x - wb]; a byte outside the pass goes to a guard byte past the window
+// (never copied out).
+__device__ __forceinline__ void win_put(uint8_t *win, int32_t wb, int32_t x, uint32_t v) {
+    const uint32_t r = (uint32_t)(x - wb);
+    win[r < (uint32_t)LZE_WIN ? r : (uint32_t)(LZE_WIN + 16)] = (uint8_t)v;
 }
 
-// Emission of one thread's sequences and literal bytes into out (the LDS
-// window or the payload; every position written is < the block's encoded
-// size by construction).  Literal bytes come from the thread's own chunk of
-// the swizzled image: piece k of chunk c sits at slot k ^ sw.
-template <int CHLOG, typename P>
-__device__ __forceinline__ void emit_chunk(P out, const uint8_t *s_img, uint64_t Q, uint64_t m, int32_t cs,
-                                           int32_t chunk_end, int32_t next_after, int32_t len, int32_t carry_j,
-                                           int32_t pos0, int32_t next_qi, int32_t sw) {
-    auto lit = [&](int32_t p) -> uint32_t {
-        const int32_t o = p - cs;
-        return s_img[cs + ((((o >> 4) ^ sw)) << 4) + (o & 15)];
+// extra length bytes of a nibble capped at 15: 255s then a byte < 255
+__device__ __forceinline__ int32_t put_len(uint8_t *win, int32_t wb, int32_t x, int32_t v) {
+    int32_t rem = v - 15;
+    for (; rem >= 255; rem -= 255) win_put(win, wb, x++, 255u);
+    win_put(win, wb, x++, (uint32_t)rem);
+    return x;
+}
+
+// Emission of one thread's sequences and of the literal bytes of its own
+// chunk, as far as they fall in the window pass [wb, wb + LZE_WIN).  Byte p
+// of the chunk sits at p ^ sw16 in the swizzled image (the swizzle only
+// permutes the chunk's 16-byte pieces).
+template <int CHLOG>
+__device__ __forceinline__ void emit_chunk(uint8_t *win, int32_t wb, const uint8_t *s_img, uint64_t Q, uint64_t m,
+                                           int32_t cs, int32_t chunk_end, int32_t next_after, int32_t len,
+                                           int32_t carry_j, int32_t pos0, int32_t next_qi, int32_t sw16) {
+    // chunk bytes [lo, hi) to output bytes base + p, clipped to the pass
+    auto lits = [&](int32_t base, int32_t lo, int32_t hi) {
+        const int32_t d = base - wb;
+        lo = lo > -d ? lo : -d;
+        hi = hi < LZE_WIN - d ? hi : LZE_WIN - d;
+        for (int32_t p = lo; p < hi; ++p) win[d + p] = s_img[p ^ sw16];
     };
     int32_t la = carry_j, pos = pos0;
     while (Q) {
@@ -136,14 +148,14 @@ __device__ __forceinline__ void emit_chunk(P out, const uint8_t *s_img, uint64_t
         const int32_t i = s + 1, j = e < len - 5 ? e : len - 5;
         const int32_t ll = i - la, ml = j - i;
         const int32_t h = 1 + ext_bytes(ll);
-        out[pos] = (uint8_t)(((ll >= 15 ? 15 : ll) << 4) | (ml - 4 >= 15 ? 15 : ml - 4));
-        if (ll >= 15) put_len(out, pos + 1, ll);
-        const int32_t base = pos + h - la;
-        for (int32_t p = (la > cs ? la : cs); p < i; ++p) out[base + p] = (uint8_t)lit(p);
+        win_put(win, wb, pos, (uint32_t)(((ll >= 15 ? 15 : ll) << 4) | (ml - 4 >= 15 ? 15 : ml - 4)));
+        if (ll >= 15) put_len(win, wb, pos + 1, ll);
+        lits(pos + h - la, la > cs ? la : cs, i);
         int32_t q = pos + h + ll;
-        out[q++] = 1;
-        out[q++] = 0;
-        if (ml - 4 >= 15) q = put_len(out, q, ml - 4);
+        win_put(win, wb, q, 1u);
+        win_put(win, wb, q + 1, 0u);
+        q += 2;
+        if (ml - 4 >= 15) q = put_len(win, wb, q, ml - 4);
         pos = q;
         la = j;
     }
@@ -151,15 +163,18 @@ __device__ __forceinline__ void emit_chunk(P out, const uint8_t *s_img, uint64_t
     const int32_t lo = la > cs ? la : cs;
     if (lo < chunk_end) {
         const int32_t ll = (next_qi != LZE_INF ? next_qi : len) - la;
-        const int32_t base = pos + 1 + ext_bytes(ll) - la;
-        for (int32_t p = lo; p < chunk_end; ++p) out[base + p] = (uint8_t)lit(p);
+        lits(pos + 1 + ext_bytes(ll) - la, lo, chunk_end);
     }
 }
 
+constexpr int LZE_NW = LZE_THREADS / kWave;
+
 struct EncShared {
     uint8_t img[LZE_MAX_BLOCK];
-    uint8_t win[LZE_WIN + 48];  // output byte x at win[16 + x]; 16-byte guards around it
-    int32_t i32[LZE_THREADS / kWave];
+    uint8_t win[LZE_WIN + 48];  // window byte x at win[16 + x]; guards around it
+    // one slot set per block scan; a set is written again only in the next
+    // block, after barriers every wave has passed, so each scan needs one barrier
+    int32_t scan[4][LZE_NW];
     uint64_t off;
 };
 
@@ -169,13 +184,13 @@ __device__ __forceinline__ void enc_block(const Lz4EncArgs &a, uint32_t b, uint3
     constexpr int32_t CH = 1 << CHLOG;
     uint8_t *const s_img = sh.img;
     uint8_t *const s_win = sh.win;
-    int32_t *const s_i32 = sh.i32;
     const uint32_t tag = epoch_tag(ep);
     // thread index re-materialised per block (an empty asm the compiler cannot
     // see through): values derived from it are not hoisted out of the block
     // loop, which would hold them in registers across every block
     int t = threadIdx.x;
     asm volatile("" : "+v"(t));
+    const int wv = t / kWave, ln = t % kWave;
     const int64_t blk_base = (int64_t)b * a.block_bytes;
     const int32_t len = (int32_t)((a.nbytes - blk_base) < a.block_bytes ? (a.nbytes - blk_base) : a.block_bytes);
 
@@ -247,8 +262,24 @@ __device__ __forceinline__ void enc_block(const Lz4EncArgs &a, uint32_t b, uint3
     uint64_t m = 0;
 #pragma unroll
     for (int i = 0; i < NW; ++i) m |= (uint64_t)mw[i] << (32 * i);
-    const int32_t first_b = m ? cs + __builtin_ctzll(m) : len;
-    const int32_t next_after = block_excl_min_rev<LZE_THREADS / kWave>(first_b, len, s_i32);
+
+    // first run boundary at or after the next chunk: exclusive minimum over
+    // the higher threads
+    int32_t next_after;
+    {
+        const int32_t first_b = m ? cs + __builtin_ctzll(m) : len;
+        const int32_t inc = wave_incl_min_rev(first_b);
+        const int32_t exc = dpp_mov<dppc::kWaveShl1, 0xf, 0xf>(len, inc);
+        if (ln == 0) sh.scan[0][wv] = inc;
+        __syncthreads();
+        int32_t above = len;
+#pragma unroll
+        for (int w = 0; w < LZE_NW; ++w) {
+            const int32_t x = sh.scan[0][w];
+            if (w > wv) above = x < above ? x : above;
+        }
+        next_after = exc < above ? exc : above;
+    }
 
     // 3. the runs that become sequences (bit-parallel), then one pass over
     //    them: first one (i1, its match length), last j, and the bytes of the
@@ -273,97 +304,136 @@ __device__ __forceinline__ void enc_block(const Lz4EncArgs &a, uint32_t b, uint3
         }
         last_qj = j;
     }
-    int32_t a_final;
-    const int32_t carry_j = block_excl_max<LZE_THREADS / kWave>(last_qj, 0, s_i32, &a_final);
-    const int32_t next_qi = block_excl_min_rev<LZE_THREADS / kWave>(first_qi, LZE_INF, s_i32);
-    const int32_t tot = first_qi == LZE_INF ? 0 : seq_bytes(first_qi - carry_j, first_ml) + rest;
-    int32_t qsum;
-    const int32_t pos0 = block_excl_sum<LZE_THREADS / kWave>(tot, s_i32, &qsum);
-    const int32_t ll_final = len - a_final;
-    const uint64_t comp = (uint64_t)qsum + 1 + ext_bytes(ll_final) + ll_final;
-
-    // 4 + 5. place the block and emit it.  A block whose encoding fits the LDS
-    // window (every block of a sparse mask) is emitted there first, relative to
-    // its own start: wave 0 publishes the block's size, every wave emits, and
-    // only then does wave 0 wait for the predecessors' sizes, so that wait
-    // overlaps the emission.  A larger block needs its offset first and is
-    // emitted straight into the payload.
-    const int32_t sw = (t >> (4 - (CHLOG - 4))) & ((1 << (CHLOG - 4)) - 1);
-    const bool staged = (int32_t)comp <= LZE_WIN;
-    auto place = [&](uint64_t off, bool failed) {  // lane 0 of wave 0
-        if (failed) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
-        sh.off = off;
-        a.comp_sizes[b] = (uint32_t)comp;
-        a.comp_offsets[b] = off;
-        if (b == a.nblocks - 1) {
-            *a.d_total = off + comp;
-            ws_epoch_advance(a.hdr, ep);
+    // the last j before this chunk (exclusive maximum, 0 if none) and the
+    // first qualifying i after it (exclusive minimum over the higher threads),
+    // under one barrier
+    int32_t carry_j, next_qi, a_final;
+    {
+        const int32_t inc_j = wave_incl_max(last_qj);
+        const int32_t exc_j = dpp_mov<dppc::kWaveShr1, 0xf, 0xf>(0, inc_j);
+        const int32_t inc_i = wave_incl_min_rev(first_qi);
+        const int32_t exc_i = dpp_mov<dppc::kWaveShl1, 0xf, 0xf>(LZE_INF, inc_i);
+        if (ln == kWave - 1) sh.scan[1][wv] = inc_j;
+        if (ln == 0) sh.scan[2][wv] = inc_i;
+        __syncthreads();
+        int32_t below = 0, all = 0, above = LZE_INF;
+#pragma unroll
+        for (int w = 0; w < LZE_NW; ++w) {
+            const int32_t xj = sh.scan[1][w], xi = sh.scan[2][w];
+            if (w < wv) below = xj > below ? xj : below;
+            all = xj > all ? xj : all;
+            if (w > wv) above = xi < above ? xi : above;
         }
-        if ((int64_t)(off + comp) > a.cap) or_agent32(a.d_status, 1u /*PULSE_DS_CAPACITY*/);
-    };
-    uint8_t *outp;
-    if (staged) {
-        if (wave_id() == 0) lookback_publish(a.status, b, tag, comp);
-        outp = s_win + 16;
-    } else {
-        if (wave_id() == 0) {
+        carry_j = exc_j > below ? exc_j : below;
+        next_qi = exc_i < above ? exc_i : above;
+        a_final = __builtin_amdgcn_readfirstlane(all);  // uniform: keep it in a scalar register
+    }
+    const int32_t tot = first_qi == LZE_INF ? 0 : seq_bytes(first_qi - carry_j, first_ml) + rest;
+    // byte offset of this thread's sequences (exclusive sum) and the block's
+    // sequence bytes
+    int32_t pos0, qsum;
+    {
+        const int32_t inc = wave_incl_sum(tot);
+        if (ln == kWave - 1) sh.scan[3][wv] = inc;
+        __syncthreads();
+        int32_t below = 0, all = 0;
+#pragma unroll
+        for (int w = 0; w < LZE_NW; ++w) {
+            const int32_t x = sh.scan[3][w];
+            if (w < wv) below += x;
+            all += x;
+        }
+        pos0 = below + inc - tot;
+        qsum = __builtin_amdgcn_readfirstlane(all);
+    }
+    const int32_t ll_final = len - a_final;
+    const int32_t comp = qsum + 1 + ext_bytes(ll_final) + ll_final;
+
+    // 4 + 5. place the block and emit it.  Wave 0 publishes the block's size;
+    // every wave emits into the LDS window (relative to the block's start),
+    // and only then does wave 0 wait for the predecessors' sizes, so the wait
+    // overlaps the emission.  A block whose encoding is larger than the window
+    // (incompressible data) is emitted in several window passes; a thread
+    // skips a pass that none of its bytes fall in.
+    const int32_t sw16 = ((t >> (4 - (CHLOG - 4))) & ((1 << (CHLOG - 4)) - 1)) << 4;
+    if (wv == 0) lookback_publish(a.status, b, tag, (uint64_t)comp);
+    // output bytes this thread writes: inside [pos0, whi)
+    int32_t whi = pos0 + tot;
+    {
+        const int32_t la = Q ? last_qj : carry_j;
+        if ((la > cs ? la : cs) < cs + cl) {
+            const int32_t ll = (next_qi != LZE_INF ? next_qi : len) - la;
+            whi += 1 + ext_bytes(ll) + (cs + cl - la);
+        }
+    }
+    uint8_t *const win = s_win + 16;
+    for (int32_t wb = 0; wb < comp; wb += LZE_WIN) {
+        if (whi > pos0 && pos0 < wb + LZE_WIN && whi > wb)
+            emit_chunk<CHLOG>(win, wb, s_img, Q, m, cs, cs + cl, next_after, len, carry_j, pos0, next_qi, sw16);
+        if (t == 0) {  // the final literal run's token and length bytes
+            win_put(win, wb, qsum, (uint32_t)((ll_final >= 15 ? 15 : ll_final) << 4));
+            if (ll_final >= 15) put_len(win, wb, qsum + 1, ll_final);
+        }
+        if (wb == 0 && wv == 0) {
             bool failed = false;
-            const uint64_t off = lookback_wave(a.status, b, tag, comp, &failed);
-            if (lane_id() == 0) place(off, failed);
+            const uint64_t off = lookback_resolve(a.status, b, tag, (uint64_t)comp, &failed);
+            if (ln == 0) {
+                if (failed) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
+                sh.off = off;
+                a.comp_sizes[b] = (uint32_t)comp;
+                a.comp_offsets[b] = off;
+                if (b == a.nblocks - 1) {
+                    *a.d_total = off + comp;
+                    ws_epoch_advance(a.hdr, ep);
+                }
+                if ((int64_t)(off + comp) > a.cap) or_agent32(a.d_status, 1u /*PULSE_DS_CAPACITY*/);
+            }
         }
         __syncthreads();
-        if ((int64_t)(sh.off + comp) > a.cap) return;
-        outp = a.payload + sh.off;
-    }
-    emit_chunk<CHLOG>(outp, s_img, Q, m, cs, cs + cl, next_after, len, carry_j, pos0, next_qi, sw);
-    if (t == 0) {
-        outp[qsum] = (uint8_t)((ll_final >= 15 ? 15 : ll_final) << 4);
-        if (ll_final >= 15) put_len(outp, qsum + 1, ll_final);
-    }
-    if (!staged) return;
-    if (wave_id() == 0) {
-        bool failed = false;
-        const uint64_t off = lookback_resolve(a.status, b, tag, comp, &failed);
-        if (lane_id() == 0) place(off, failed);
-    }
-    __syncthreads();
-    const uint64_t off = sh.off;
-    if ((int64_t)(off + comp) > a.cap) return;
-    uint8_t *dst = a.payload + off;
-    // copy the window out with 16-byte stores to aligned addresses (bytes for
-    // the first and last piece, shared with the neighbouring blocks' bytes):
-    // aligned piece u covers output bytes [16 u - shift, +16), which sit at
-    // window [16 u + 16 - shift, +16), inside the aligned pair 16 u, 16 u + 16
-    const int32_t shift = (int32_t)((uintptr_t)dst & 15);
-    const int32_t end = shift + (int32_t)comp;
-    uint8_t *base = dst - shift;
-    const int o = 16 - shift;  // 1 .. 16, the same for the whole block
-    for (int32_t q = 16 * t; q < end; q += 16 * LZE_THREADS) {
-        if (q >= shift && q + 16 <= end) {
-            const u32x4 A = *reinterpret_cast<const u32x4 *>(s_win + q);
-            const u32x4 B = *reinterpret_cast<const u32x4 *>(s_win + q + 16);
-            const uint32_t wv[8] = {A.x, A.y, A.z, A.w, B.x, B.y, B.z, B.w};
-            u32x4 r;
-            const int wq = o >> 2, bs = o & 3;
-            if (o == 16) {
-                r = B;
-            } else if (wq == 0) {
-                r = u32x4{__builtin_amdgcn_alignbyte(wv[1], wv[0], bs), __builtin_amdgcn_alignbyte(wv[2], wv[1], bs),
-                          __builtin_amdgcn_alignbyte(wv[3], wv[2], bs), __builtin_amdgcn_alignbyte(wv[4], wv[3], bs)};
-            } else if (wq == 1) {
-                r = u32x4{__builtin_amdgcn_alignbyte(wv[2], wv[1], bs), __builtin_amdgcn_alignbyte(wv[3], wv[2], bs),
-                          __builtin_amdgcn_alignbyte(wv[4], wv[3], bs), __builtin_amdgcn_alignbyte(wv[5], wv[4], bs)};
-            } else if (wq == 2) {
-                r = u32x4{__builtin_amdgcn_alignbyte(wv[3], wv[2], bs), __builtin_amdgcn_alignbyte(wv[4], wv[3], bs),
-                          __builtin_amdgcn_alignbyte(wv[5], wv[4], bs), __builtin_amdgcn_alignbyte(wv[6], wv[5], bs)};
+        // readfirstlane returns int: each half goes through uint32_t, so the
+        // low half is not sign-extended into the high one
+        const uint32_t off_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(sh.off >> 32));
+        const uint32_t off_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)sh.off);
+        const uint64_t off = ((uint64_t)off_hi << 32) | off_lo;
+        if ((int64_t)(off + comp) > a.cap) return;
+        const int32_t n = comp - wb < LZE_WIN ? comp - wb : LZE_WIN;
+        uint8_t *dst = a.payload + off + wb;
+        // copy the pass out with 16-byte stores to aligned addresses (bytes
+        // for the first and last piece, shared with the neighbouring bytes):
+        // aligned piece u covers pass bytes [16 u - shift, +16), which sit at
+        // s_win [16 u + 16 - shift, +16), inside the aligned pair 16 u, 16 u + 16
+        const int32_t shift = (int32_t)((uintptr_t)dst & 15);
+        const int32_t end = shift + n;
+        uint8_t *base = dst - shift;
+        const int o = 16 - shift;  // 1 .. 16, the same for the whole block
+        for (int32_t q = 16 * t; q < end; q += 16 * LZE_THREADS) {
+            if (q >= shift && q + 16 <= end) {
+                const u32x4 A = *reinterpret_cast<const u32x4 *>(s_win + q);
+                const u32x4 B = *reinterpret_cast<const u32x4 *>(s_win + q + 16);
+                const uint32_t wv8[8] = {A.x, A.y, A.z, A.w, B.x, B.y, B.z, B.w};
+                u32x4 r;
+                const int wq = o >> 2, bs = o & 3;
+                if (o == 16) {
+                    r = B;
+                } else if (wq == 0) {
+                    r = u32x4{__builtin_amdgcn_alignbyte(wv8[1], wv8[0], bs), __builtin_amdgcn_alignbyte(wv8[2], wv8[1], bs),
+                              __builtin_amdgcn_alignbyte(wv8[3], wv8[2], bs), __builtin_amdgcn_alignbyte(wv8[4], wv8[3], bs)};
+                } else if (wq == 1) {
+                    r = u32x4{__builtin_amdgcn_alignbyte(wv8[2], wv8[1], bs), __builtin_amdgcn_alignbyte(wv8[3], wv8[2], bs),
+                              __builtin_amdgcn_alignbyte(wv8[4], wv8[3], bs), __builtin_amdgcn_alignbyte(wv8[5], wv8[4], bs)};
+                } else if (wq == 2) {
+                    r = u32x4{__builtin_amdgcn_alignbyte(wv8[3], wv8[2], bs), __builtin_amdgcn_alignbyte(wv8[4], wv8[3], bs),
+                              __builtin_amdgcn_alignbyte(wv8[5], wv8[4], bs), __builtin_amdgcn_alignbyte(wv8[6], wv8[5], bs)};
+                } else {
+                    r = u32x4{__builtin_amdgcn_alignbyte(wv8[4], wv8[3], bs), __builtin_amdgcn_alignbyte(wv8[5], wv8[4], bs),
+                              __builtin_amdgcn_alignbyte(wv8[6], wv8[5], bs), __builtin_amdgcn_alignbyte(wv8[7], wv8[6], bs)};
+                }
+                *reinterpret_cast<u32x4 *>(base + q) = r;
             } else {
-                r = u32x4{__builtin_amdgcn_alignbyte(wv[4], wv[3], bs), __builtin_amdgcn_alignbyte(wv[5], wv[4], bs),
-                          __builtin_amdgcn_alignbyte(wv[6], wv[5], bs), __builtin_amdgcn_alignbyte(wv[7], wv[6], bs)};
+                for (int32_t x = (q > shift ? q : shift); x < q + 16 && x < end; ++x) base[x] = s_win[16 + x - shift];
             }
-            *reinterpret_cast<u32x4 *>(base + q) = r;
-        } else {
-            for (int32_t x = (q > shift ? q : shift); x < q + 16 && x < end; ++x) base[x] = s_win[16 + x - shift];
         }
+        if (wb + LZE_WIN < comp) __syncthreads();  // the next pass rewrites the window
     }
 }
 
