@@ -12,7 +12,12 @@ tensors (embed | 16 x four decoder layers | final norm + lm_head):
                               embed, lm_head -> E4M3 + FP32 128x128 scales
   sender    lz4_encode_blocks LZ4 blocks (64 KiB) of the XOR mask old ^ new,
                               the mask never materialised
-  receiver  lz4_decode_blocks decode + XOR in place into the receiver's view
+  receiver  lz4_decode_parse  the serial token-chain parse of every block, on a
+                              second stream, while the receiver's FP8 quant of
+                              the same chunk keeps HBM busy
+  receiver  lz4_decode_apply  rebuild + XOR in place into the receiver's view
+                              (--serial-decode: one lz4_decode_blocks call on
+                              the main stream instead)
 
 The mask is symmetric, so the XOR step takes the receiver from v1 back to v0:
 every step does identical work on identical data with no untimed restore.  The
@@ -47,6 +52,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--layers", type=int, default=64, help="decoder layers (64 = the full Qwen2.5-32B shape)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--serial-decode", action="store_true",
+                   help="decode each chunk with one lz4_decode_blocks call on the main stream (no overlap)")
     p.add_argument("--cpu-sample-frac", type=float, default=1.0,
                    help="fraction of the oracle's sample (the attention half of layer 0) it times")
     p.add_argument("--next", default="loco,patch,list", help="next-row legs measured after the timed steps, comma "
@@ -207,33 +214,53 @@ def main():
     stages = ["cast_diff", "apply_patch", "fp8_quant", "lz4_encode", "lz4_decode"]
     ev = {k: [] for k in stages}
 
+    main_stream = torch.cuda.current_stream()
+    side_stream = torch.cuda.Stream()  # default priority, like every stream here
+    parse_ev = {"lz4_decode": []}      # parse events (side stream), added to the decode stage
+
     def run_step(record):
         for ci, (s0, e0, tids) in enumerate(chunks):
             m = e0 - s0
 
-            def rec(name, fn):
+            def rec(name, fn, store=None):
+                # events on the stream the kernels run on (the current one)
                 if record:
                     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                     a.record()
                     fn()
                     b.record()
-                    ev[name].append((a, b))
+                    (ev if store is None else store)[name].append((a, b))
                 else:
                     fn()
-
-            rec("cast_diff", lambda: pulse.pulse_cast_diff(W[s0:e0], b_old[s0:e0], stage[:m], None, idx, val,
-                                                           cnt[ci:ci + 1], status, ws_cd))
-            rec("apply_patch", lambda: pulse.pulse_apply_patch(b_recv[s0:e0], idx, val, cnt[ci:ci + 1], status))
 
             def quant():
                 for (g, rows, cols) in qplans[ci]:
                     srcs = [b_recv[offs[i]: offs[i] + specs[i].numel].view(specs[i].shape) for i in g]
                     pulse.fp8_block_quant(srcs, codes, scales)
-            rec("fp8_quant", quant)
+
+            rec("cast_diff", lambda: pulse.pulse_cast_diff(W[s0:e0], b_old[s0:e0], stage[:m], None, idx, val,
+                                                           cnt[ci:ci + 1], status, ws_cd))
+            rec("apply_patch", lambda: pulse.pulse_apply_patch(b_recv[s0:e0], idx, val, cnt[ci:ci + 1], status))
             rec("lz4_encode", lambda: pulse.lz4_encode_blocks(b_old[s0:e0], payload, csizes, coffs, ctotal[ci:ci + 1],
                                                               status, ws_en, src_xor=stage[:m]))
-            rec("lz4_decode", lambda: pulse.lz4_decode_blocks(payload, coffs, csizes, b_recv[s0:e0], status, ws_de,
-                                                              mode=1))
+            if args.serial_decode:
+                rec("fp8_quant", quant)
+                rec("lz4_decode", lambda: pulse.lz4_decode_blocks(payload, coffs, csizes, b_recv[s0:e0], status,
+                                                                  ws_de, mode=1))
+                continue
+            # the parse reads this chunk's payload (after the encode) and the
+            # decode workspace (free once the previous chunk's apply is done,
+            # which the main stream has queued before this encode)
+            side_stream.wait_stream(main_stream)
+            with torch.cuda.stream(side_stream):
+                rec("lz4_decode", lambda: pulse.lz4_decode_parse(payload, coffs, csizes, 2 * m, status, ws_de,
+                                                                 stream=side_stream), store=parse_ev)
+                parsed = torch.cuda.Event()
+                parsed.record(side_stream)
+            rec("fp8_quant", quant)  # reads the receiver's view before the XOR rewrites it
+            main_stream.wait_event(parsed)
+            rec("lz4_decode", lambda: pulse.lz4_decode_apply(payload, coffs, csizes, b_recv[s0:e0], status, ws_de,
+                                                             mode=1))
 
     # ---- warm-up, with the end-to-end check after the first step
     for w in range(max(args.warmup, 1)):
@@ -256,6 +283,7 @@ def main():
     # ---- timed steps
     for k in ev:
         ev[k].clear()
+    parse_ev["lz4_decode"].clear()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -271,6 +299,9 @@ def main():
     ms_step = 1e3 * t_total / args.steps
     stage_ms = {k: sum(a.elapsed_time(b) for a, b in ev[k]) / args.steps for k in stages}
     launches = {k: len(ev[k]) // args.steps for k in stages}
+    # the decode stage is its parse (side stream, overlapped) plus its apply
+    parse_ms = sum(a.elapsed_time(b) for a, b in parse_ev["lz4_decode"]) / args.steps
+    stage_ms["lz4_decode"] += parse_ms
     # algorithmic bytes per step (what the method must move)
     alg = {
         "cast_diff": n * (8 + 6 * d),           # read w (4) + old (2), write new (2) + patch (6 d)
@@ -285,6 +316,8 @@ def main():
         secs = stage_ms[k] / 1e3
         st_out[k] = {"ms": round(stage_ms[k], 3), "launches": launches[k], "alg_GB": round(alg[k] / 1e9, 3),
                      "GBps": round(alg[k] / secs / 1e9, 1), "frac_hbm": round(alg[k] / secs / PEAK_HBM, 4)}
+    if not args.serial_decode:
+        st_out["lz4_decode"]["parse_ms_on_side_stream"] = round(parse_ms, 3)
     dom = max(stages, key=lambda k: stage_ms[k])
     dom_secs = stage_ms[dom] / 1e3
     achieved = alg[dom] / dom_secs / 1e9
@@ -314,6 +347,8 @@ def main():
                                "full hot path: cast+diff+compact, patch apply, stacked FP8 quant, "
                                "LZ4 mask encode, LZ4 decode+XOR",
                    "params": n, "chunks": len(chunks), "lz4_block_bytes": BLOCK,
+                   "decode_schedule": "one call, main stream" if args.serial_decode
+                   else "parse on a second stream beside fp8_quant, apply on the main stream",
                    "changed_fraction": round(d, 6), "lz4_bytes_per_param": round(c, 5),
                    "lz4_ratio_of_mask": round(comp_bytes / (2 * n), 5), "fp8_params": n_quant},
         "hbm_frac_step": round(alg_total / (ms_step / 1e3) / PEAK_HBM, 4),

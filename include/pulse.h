@@ -221,6 +221,27 @@ int lz4_decode_blocks(const uint8_t *payload, int64_t payload_bytes,
                       int32_t mode, uint32_t *d_status, void *ws, size_t ws_bytes,
                       hipStream_t stream);
 
+/* The same decode in two calls, so that a caller can run the serial part (the
+ * token-chain parse of every block, latency-bound) on one stream while other
+ * work keeps HBM busy, and the apply (the dense XOR or store into dst) later.
+ * lz4_decode_parse validates the block table and parses every block into ws;
+ * lz4_decode_apply then rebuilds each block and applies it to dst, exactly as
+ * lz4_decode_blocks does.  Both take the same payload, block table, sizes and
+ * ws (arguments as above); apply must run after its parse has completed (same
+ * stream, or an event), and a workspace holds one parse at a time: every parse
+ * is followed by its apply before the next parse on that workspace.  Corrupt
+ * blocks are found by the parse and reported (PULSE_DS_CORRUPT) by either
+ * call; their dst range is left untouched. */
+int lz4_decode_parse(const uint8_t *payload, int64_t payload_bytes,
+                     const uint64_t *comp_offsets, const uint32_t *comp_sizes,
+                     int64_t nblocks, int32_t block_bytes, int64_t nbytes,
+                     uint32_t *d_status, void *ws, size_t ws_bytes, hipStream_t stream);
+int lz4_decode_apply(const uint8_t *payload, int64_t payload_bytes,
+                     const uint64_t *comp_offsets, const uint32_t *comp_sizes,
+                     int64_t nblocks, int32_t block_bytes, int64_t nbytes, void *dst,
+                     int32_t mode, uint32_t *d_status, void *ws, size_t ws_bytes,
+                     hipStream_t stream);
+
 /* ---- a7: projection fusion + FP8-E4M3 block quantisation -----------------
  * The sender rebuilds the full weight, fuses projections and quantises BF16
  * training weights for FP8 inference ([Perplexity] opening paragraph and

@@ -21,7 +21,7 @@ __all__ = [
     "pulse_loco_gate", "pulse_loco_accumulate",
     "PULSE_OP_PATCH_UNPACK", "patch_packed_bytes", "patch_pack", "patch_unpack",
     "PULSE_OP_CAST_DIFF_SEGMENTS", "PULSE_DS_BADSEGMENT", "pulse_segment_tiles", "SegmentTable", "ViewTable",
-    "pulse_cast_diff_segments", "pulse_apply_patch_segments",
+    "pulse_cast_diff_segments", "pulse_apply_patch_segments", "lz4_decode_parse", "lz4_decode_apply",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -59,6 +59,8 @@ _lib.pulse_apply_patch.argtypes = [_P, _I64, _P, _P, _P, _I64, _P, _P]
 _lib.xor_mask_apply.argtypes = [_P, _P, _I64, _P]
 _lib.lz4_encode_blocks.argtypes = [_P, _P, _I64, _I32, _P, _I64, _P, _P, _P, _P, _P, _SZ, _P]
 _lib.lz4_decode_blocks.argtypes = [_P, _I64, _P, _P, _I64, _I32, _I64, _P, _I32, _P, _P, _SZ, _P]
+_lib.lz4_decode_parse.argtypes = [_P, _I64, _P, _P, _I64, _I32, _I64, _P, _P, _SZ, _P]
+_lib.lz4_decode_apply.argtypes = [_P, _I64, _P, _P, _I64, _I32, _I64, _P, _I32, _P, _P, _SZ, _P]
 _lib.fp8_block_quant.argtypes = [_P, _P, _I32, _I64, _I64, _P, _P, _P, _P]
 _lib.fp8_view_delta.argtypes = [_P, _P, _I64, _P, _P, _I64, _P, _P, _I64, _P, _P, _P, _I64, _P, _P, _P, _SZ, _P]
 _lib.fp8_view_apply.argtypes = [_P, _I64, _P, _I64, _P, _P, _P, _I64, _P, _P, _P, _I64, _P, _P]
@@ -75,7 +77,8 @@ _lib.pulse_apply_patch_segments.argtypes = [_P, _I32, _P, _P, _P, _I64, _P, _P]
 for _f in ("pulse_cast_diff_segments", "pulse_apply_patch_segments", "patch_pack", "patch_unpack",
            "pulse_workspace_init", "pulse_cast_diff", "pulse_compact", "pulse_apply_patch",
            "xor_mask_apply", "lz4_encode_blocks", "lz4_decode_blocks", "fp8_block_quant",
-           "fp8_view_delta", "fp8_view_apply", "pulse_loco_gate", "pulse_loco_accumulate"):
+           "fp8_view_delta", "fp8_view_apply", "pulse_loco_gate", "pulse_loco_accumulate",
+           "lz4_decode_parse", "lz4_decode_apply"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -207,20 +210,44 @@ def lz4_encode_blocks(src, payload, comp_sizes, comp_offsets, d_total, d_status,
         _stream(stream)), "lz4_encode_blocks")
 
 
-def lz4_decode_blocks(payload, comp_offsets, comp_sizes, dst, d_status, ws, mode=1, block_bytes=65536,
-                      nbytes=None, payload_bytes=None, stream=None):
-    nbytes = dst.numel() * dst.element_size() if nbytes is None else nbytes
+def _decode_table(payload, comp_offsets, comp_sizes, nbytes, payload_bytes, block_bytes):
     payload_bytes = payload.numel() if payload_bytes is None else payload_bytes
     nb = (nbytes + block_bytes - 1) // block_bytes
-    _need(dst, nbytes, "dst")
     _need(payload, payload_bytes, "payload")
     _need(comp_sizes, 4 * nb, "comp_sizes")
     _need(comp_offsets, 8 * nb, "comp_offsets")
+    return (_dev(payload, "payload", torch.uint8), payload_bytes, _dev(comp_offsets, "comp_offsets", torch.int64),
+            _dev(comp_sizes, "comp_sizes", torch.int32), nb, block_bytes, nbytes)
+
+
+def lz4_decode_blocks(payload, comp_offsets, comp_sizes, dst, d_status, ws, mode=1, block_bytes=65536,
+                      nbytes=None, payload_bytes=None, stream=None):
+    nbytes = dst.numel() * dst.element_size() if nbytes is None else nbytes
+    _need(dst, nbytes, "dst")
+    tab = _decode_table(payload, comp_offsets, comp_sizes, nbytes, payload_bytes, block_bytes)
     wsp, wsb = _ws(ws)
-    _check(_lib.lz4_decode_blocks(
-        _dev(payload, "payload", torch.uint8), payload_bytes, _dev(comp_offsets, "comp_offsets", torch.int64),
-        _dev(comp_sizes, "comp_sizes", torch.int32), nb, block_bytes, nbytes, _dev(dst, "dst"), mode,
-        _dev(d_status, "d_status", torch.int32), wsp, wsb, _stream(stream)), "lz4_decode_blocks")
+    _check(_lib.lz4_decode_blocks(*tab, _dev(dst, "dst"), mode, _dev(d_status, "d_status", torch.int32), wsp, wsb,
+                                  _stream(stream)), "lz4_decode_blocks")
+
+
+def lz4_decode_parse(payload, comp_offsets, comp_sizes, nbytes, d_status, ws, block_bytes=65536,
+                     payload_bytes=None, stream=None):
+    """First half of lz4_decode_blocks: parse every block into ws (no dst)."""
+    tab = _decode_table(payload, comp_offsets, comp_sizes, nbytes, payload_bytes, block_bytes)
+    wsp, wsb = _ws(ws)
+    _check(_lib.lz4_decode_parse(*tab, _dev(d_status, "d_status", torch.int32), wsp, wsb, _stream(stream)),
+           "lz4_decode_parse")
+
+
+def lz4_decode_apply(payload, comp_offsets, comp_sizes, dst, d_status, ws, mode=1, block_bytes=65536,
+                     nbytes=None, payload_bytes=None, stream=None):
+    """Second half: apply what the last lz4_decode_parse on ws found to dst."""
+    nbytes = dst.numel() * dst.element_size() if nbytes is None else nbytes
+    _need(dst, nbytes, "dst")
+    tab = _decode_table(payload, comp_offsets, comp_sizes, nbytes, payload_bytes, block_bytes)
+    wsp, wsb = _ws(ws)
+    _check(_lib.lz4_decode_apply(*tab, _dev(dst, "dst"), mode, _dev(d_status, "d_status", torch.int32), wsp, wsb,
+                                 _stream(stream)), "lz4_decode_apply")
 
 
 def _batch_src(t, name):

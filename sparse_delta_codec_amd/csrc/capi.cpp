@@ -22,6 +22,10 @@ size_t pulse_lz4_decode_ws_bytes(int64_t nblocks, int64_t payload_bytes);
 int pulse_launch_lz4_decode(const uint8_t *, int64_t, const uint64_t *, const uint32_t *, int64_t, int32_t,
                             int64_t, void *, int32_t, uint32_t *, void *, size_t, hipStream_t);
 int pulse_lz4_decode_ws_fits(size_t ws, int64_t nblocks, int64_t payload_bytes);
+int pulse_launch_lz4_decode_parse(const uint8_t *, int64_t, const uint64_t *, const uint32_t *, int64_t, int32_t,
+                                  int64_t, uint32_t *, void *, size_t, hipStream_t);
+int pulse_launch_lz4_decode_apply(const uint8_t *, int64_t, const uint64_t *, const uint32_t *, int64_t, int32_t,
+                                  int64_t, void *, int32_t, uint32_t *, void *, size_t, hipStream_t);
 int pulse_launch_fp8_block_quant(const uint16_t *const *, const int64_t *, int32_t, int64_t, int64_t,
                                  const int64_t *, uint8_t *, float *, hipStream_t);
 size_t pulse_delta_compact_ws_bytes(int64_t n);
@@ -163,21 +167,53 @@ int lz4_encode_blocks(const void *src, const void *src_xor, int64_t nbytes, int3
                                    comp_offsets, d_total, d_status, ws, stream);
 }
 
-int lz4_decode_blocks(const uint8_t *payload, int64_t payload_bytes, const uint64_t *comp_offsets,
-                      const uint32_t *comp_sizes, int64_t nblocks, int32_t block_bytes, int64_t nbytes,
-                      void *dst, int32_t mode, uint32_t *d_status, void *ws, size_t ws_bytes,
-                      hipStream_t stream) {
-    if (!payload || !comp_offsets || !comp_sizes || !dst || !d_status || payload_bytes < 0 || nbytes <= 0 ||
-        nblocks <= 0)
+namespace {
+// argument checks shared by the decode calls (dst and mode only where given)
+int check_decode(const uint8_t *payload, int64_t payload_bytes, const uint64_t *comp_offsets,
+                 const uint32_t *comp_sizes, int64_t nblocks, int32_t block_bytes, int64_t nbytes, const void *dst,
+                 bool need_dst, int32_t mode, const uint32_t *d_status, const void *ws, size_t ws_bytes) {
+    if (!payload || !comp_offsets || !comp_sizes || (need_dst && !dst) || !d_status || payload_bytes < 0 ||
+        nbytes <= 0 || nblocks <= 0)
         return PULSE_EINVAL;
     if (mode != 0 && mode != 1) return PULSE_EINVAL;
     if (block_bytes <= 0 || block_bytes > 65536 || block_bytes % 16 != 0) return PULSE_EINVAL;
     if (nblocks != (nbytes + block_bytes - 1) / block_bytes) return PULSE_EINVAL;
-    if (!aligned16(dst)) return PULSE_EALIGN;
+    if (need_dst && !aligned16(dst)) return PULSE_EALIGN;
     if (payload_bytes > kMaxPayload || nblocks > 0x3FFFFFFFll) return PULSE_ERANGE;
     if (!ws || !pulse_lz4_decode_ws_fits(ws_bytes, nblocks, payload_bytes)) return PULSE_EWORKSPACE;
+    return PULSE_OK;
+}
+}  // namespace
+
+int lz4_decode_blocks(const uint8_t *payload, int64_t payload_bytes, const uint64_t *comp_offsets,
+                      const uint32_t *comp_sizes, int64_t nblocks, int32_t block_bytes, int64_t nbytes,
+                      void *dst, int32_t mode, uint32_t *d_status, void *ws, size_t ws_bytes,
+                      hipStream_t stream) {
+    const int rc = check_decode(payload, payload_bytes, comp_offsets, comp_sizes, nblocks, block_bytes, nbytes, dst,
+                                true, mode, d_status, ws, ws_bytes);
+    if (rc != PULSE_OK) return rc;
     return pulse_launch_lz4_decode(payload, payload_bytes, comp_offsets, comp_sizes, nblocks, block_bytes, nbytes,
                                    dst, mode, d_status, ws, ws_bytes, stream);
+}
+
+int lz4_decode_parse(const uint8_t *payload, int64_t payload_bytes, const uint64_t *comp_offsets,
+                     const uint32_t *comp_sizes, int64_t nblocks, int32_t block_bytes, int64_t nbytes,
+                     uint32_t *d_status, void *ws, size_t ws_bytes, hipStream_t stream) {
+    const int rc = check_decode(payload, payload_bytes, comp_offsets, comp_sizes, nblocks, block_bytes, nbytes,
+                                nullptr, false, 0, d_status, ws, ws_bytes);
+    if (rc != PULSE_OK) return rc;
+    return pulse_launch_lz4_decode_parse(payload, payload_bytes, comp_offsets, comp_sizes, nblocks, block_bytes,
+                                         nbytes, d_status, ws, ws_bytes, stream);
+}
+
+int lz4_decode_apply(const uint8_t *payload, int64_t payload_bytes, const uint64_t *comp_offsets,
+                     const uint32_t *comp_sizes, int64_t nblocks, int32_t block_bytes, int64_t nbytes, void *dst,
+                     int32_t mode, uint32_t *d_status, void *ws, size_t ws_bytes, hipStream_t stream) {
+    const int rc = check_decode(payload, payload_bytes, comp_offsets, comp_sizes, nblocks, block_bytes, nbytes, dst,
+                                true, mode, d_status, ws, ws_bytes);
+    if (rc != PULSE_OK) return rc;
+    return pulse_launch_lz4_decode_apply(payload, payload_bytes, comp_offsets, comp_sizes, nblocks, block_bytes,
+                                         nbytes, dst, mode, d_status, ws, ws_bytes, stream);
 }
 
 int fp8_block_quant(const uint16_t *const *srcs, const int64_t *src_rows, int32_t nsrc, int64_t cols,

@@ -783,10 +783,10 @@ extern "C" int pulse_lz4_decode_ws_fits(size_t ws, int64_t nblocks, int64_t payl
     return dec_fits(ws, nblocks, payload_bytes) ? 1 : 0;
 }
 
-extern "C" int pulse_launch_lz4_decode(const uint8_t *payload, int64_t payload_bytes, const uint64_t *offs,
-                                       const uint32_t *sizes, int64_t nblocks, int32_t block_bytes,
-                                       int64_t nbytes, void *dst, int32_t mode, uint32_t *d_status, void *ws,
-                                       size_t ws_bytes, hipStream_t stream) {
+namespace {
+Lz4DecArgs dec_args(const uint8_t *payload, int64_t payload_bytes, const uint64_t *offs, const uint32_t *sizes,
+                    int64_t nblocks, int32_t block_bytes, int64_t nbytes, void *dst, int32_t mode,
+                    uint32_t *d_status, void *ws, size_t ws_bytes) {
     const DecLayout L = dec_layout(ws_bytes);
     char *w = static_cast<char *>(ws);
     Lz4DecArgs a{};
@@ -805,13 +805,46 @@ extern "C" int pulse_launch_lz4_decode(const uint8_t *payload, int64_t payload_b
     a.binfo = reinterpret_cast<uint32_t *>(w + L.binfo);
     a.slow_list = reinterpret_cast<uint32_t *>(w + L.slow);
     a.ckpt = reinterpret_cast<uint2 *>(w + L.ckpt);
-    const int64_t k1 = (nblocks + 63) / 64;
-    a.k1_tiles = (uint32_t)k1;
-    k_lz4_parse<<<dim3((unsigned)k1), dim3(64), 0, stream>>>(a);
+    a.k1_tiles = (uint32_t)((nblocks + 63) / 64);
+    return a;
+}
+}  // namespace
+
+// K1 alone: validates the block table and parses every block into the
+// workspace (per-block info, checkpoints, the list of blocks for K3).
+extern "C" int pulse_launch_lz4_decode_parse(const uint8_t *payload, int64_t payload_bytes, const uint64_t *offs,
+                                             const uint32_t *sizes, int64_t nblocks, int32_t block_bytes,
+                                             int64_t nbytes, uint32_t *d_status, void *ws, size_t ws_bytes,
+                                             hipStream_t stream) {
+    const Lz4DecArgs a = dec_args(payload, payload_bytes, offs, sizes, nblocks, block_bytes, nbytes, nullptr, 0,
+                                  d_status, ws, ws_bytes);
+    k_lz4_parse<<<dim3(a.k1_tiles), dim3(64), 0, stream>>>(a);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+// K2 and K3 over what the parse left in the workspace; K3's last workgroup
+// clears the workspace's slow-block counters, so the next parse starts clean.
+extern "C" int pulse_launch_lz4_decode_apply(const uint8_t *payload, int64_t payload_bytes, const uint64_t *offs,
+                                             const uint32_t *sizes, int64_t nblocks, int32_t block_bytes,
+                                             int64_t nbytes, void *dst, int32_t mode, uint32_t *d_status, void *ws,
+                                             size_t ws_bytes, hipStream_t stream) {
+    const Lz4DecArgs a = dec_args(payload, payload_bytes, offs, sizes, nblocks, block_bytes, nbytes, dst, mode,
+                                  d_status, ws, ws_bytes);
     if (block_bytes <= 16384) launch_fast<16384>(a, stream);
     else if (block_bytes <= 32768) launch_fast<32768>(a, stream);
     else launch_fast<65536>(a, stream);
     const int64_t g3 = nblocks < 512 ? nblocks : 512;
     k_lz4_slow<<<dim3((unsigned)g3), dim3(K3_THREADS), 0, stream>>>(a);
     return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+extern "C" int pulse_launch_lz4_decode(const uint8_t *payload, int64_t payload_bytes, const uint64_t *offs,
+                                       const uint32_t *sizes, int64_t nblocks, int32_t block_bytes,
+                                       int64_t nbytes, void *dst, int32_t mode, uint32_t *d_status, void *ws,
+                                       size_t ws_bytes, hipStream_t stream) {
+    const int rc = pulse_launch_lz4_decode_parse(payload, payload_bytes, offs, sizes, nblocks, block_bytes, nbytes,
+                                                 d_status, ws, ws_bytes, stream);
+    if (rc != 0) return rc;
+    return pulse_launch_lz4_decode_apply(payload, payload_bytes, offs, sizes, nblocks, block_bytes, nbytes, dst,
+                                         mode, d_status, ws, ws_bytes, stream);
 }

@@ -34,7 +34,8 @@ def lib():
 def test_header_declares_the_codec_calls():
     fns = declared_functions()
     for name in ("pulse_cast_diff", "pulse_compact", "pulse_apply_patch", "xor_mask_apply",
-                 "lz4_encode_blocks", "lz4_decode_blocks", "fp8_block_quant", "pulse_workspace_bytes",
+                 "lz4_encode_blocks", "lz4_decode_blocks", "lz4_decode_parse", "lz4_decode_apply",
+                 "fp8_block_quant", "pulse_workspace_bytes",
                  "pulse_workspace_init", "pulse_status_string", "pulse_version"):
         assert name in fns, name
 
@@ -91,6 +92,17 @@ def test_argument_errors_return_before_any_launch(lib):
     assert dec(al, 10, al, al, 3, 65536, 70000, al, 1, al, al, 1 << 20, None) == EINVAL     # nblocks
     assert dec(al, 10, al, al, 2, 65536, 70000, mis, 1, al, al, 1 << 20, None) == EALIGN
     assert dec(al, 10, al, al, 2, 65536, 70000, al, 1, al, al, 16, None) == EWORKSPACE
+    par = lib.lz4_decode_parse
+    par.argtypes = [V, I64, V, V, I64, ctypes.c_int32, I64, V, V, ctypes.c_size_t, V]
+    assert par(al, 10, al, al, 3, 65536, 70000, al, al, 1 << 20, None) == EINVAL          # nblocks
+    assert par(al, 10, None, al, 2, 65536, 70000, al, al, 1 << 20, None) == EINVAL        # no offsets
+    assert par(al, 10, al, al, 2, 65536, 70000, al, al, 16, None) == EWORKSPACE
+    app = lib.lz4_decode_apply
+    app.argtypes = dec.argtypes
+    assert app(al, 10, al, al, 2, 65536, 70000, al, 2, al, al, 1 << 20, None) == EINVAL     # mode
+    assert app(al, 10, al, al, 2, 65536, 70000, None, 1, al, al, 1 << 20, None) == EINVAL   # no dst
+    assert app(al, 10, al, al, 2, 65536, 70000, mis, 1, al, al, 1 << 20, None) == EALIGN
+    assert app(al, 10, al, al, 2, 65536, 70000, al, 1, al, al, 16, None) == EWORKSPACE
     q = lib.fp8_block_quant
     q.argtypes = [V, V, ctypes.c_int32, I64, I64, V, V, V, V]
     ptrs = (V * 1)(0x10000)

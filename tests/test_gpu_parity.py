@@ -423,6 +423,45 @@ def test_lz4_decode_corrupt_blocks_leave_dst():
             assert np.array_equal(got, ref)
 
 
+def test_lz4_decode_in_two_calls_on_two_streams():
+    """parse on one stream, apply on another after an event, several payloads in
+    a row on one workspace (canonical, general and corrupt blocks): the same
+    bytes and status as the one-call decode and the oracle, every time."""
+    rng = np.random.default_rng(91)
+    cases = []
+    m = mask_bytes(5 * 65536 + 4321, 0.08, seed=12)
+    enc = oracle.lz4_encode_blocks(m, 65536)
+    cases.append((enc["payload"], enc["offsets"], enc["sizes"], m.size))
+    payload, offs, sizes, plain = random_payload(rng, 4, 7777)
+    cases.append((payload, offs, sizes, plain.size))
+    bad = enc["payload"].copy()
+    bad[int(enc["offsets"][2])] ^= 0xFF
+    cases.append((bad, enc["offsets"], enc["sizes"], m.size))
+    cases.append((enc["payload"], enc["offsets"], enc["sizes"], m.size))
+    nbmax = max(len(c[1]) for c in cases)
+    pbmax = max(c[0].size for c in cases)
+    ws = pulse.workspace(pulse.PULSE_OP_LZ4_DECODE, nbmax, pbmax)
+    side = torch.cuda.Stream()
+    main = torch.cuda.current_stream()
+    for k, (payload, offs, sizes, nbytes) in enumerate(cases):
+        for mode in (0, 1):
+            dst = rng.integers(0, 256, nbytes, dtype=np.uint8)
+            P, O, S, D = dev(payload), dev(offs.astype(np.uint64)), dev(sizes.astype(np.uint32)), dev(dst)
+            st = zeros(1, torch.int32)
+            side.wait_stream(main)
+            with torch.cuda.stream(side):
+                pulse.lz4_decode_parse(P, O, S, nbytes, st, ws, stream=side)
+                done = torch.cuda.Event()
+                done.record(side)
+            main.wait_event(done)
+            pulse.lz4_decode_apply(P, O, S, D, st, ws, mode=mode)
+            torch.cuda.synchronize()
+            ref, rst = oracle.lz4_decode_blocks(payload, offs, sizes, dst, mode=mode)
+            one, ost = gpu_decode(payload, offs, sizes, dst, mode)
+            assert int(host(st)[0]) == rst == ost, (k, mode)
+            assert np.array_equal(host(D), ref) and np.array_equal(one, ref), (k, mode)
+
+
 def test_lz4_round_trip_restores_new_view():
     """Sender: mask of two BF16 views -> encode; receiver: decode + XOR into the
     old view gives the new view bit for bit; XOR twice is the identity."""
