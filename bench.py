@@ -7,17 +7,16 @@ tensors (embed | 16 x four decoder layers | final norm + lm_head):
 
   sender    pulse_cast_diff   FP32 -> BF16 RNE cast, bitwise diff against the
                               old view, (int32 index, BF16 value) patch
-  receiver  pulse_apply_patch scatter the patch into the receiver's view (v0 -> v1)
-  receiver  fp8_block_quant   stacked [q;k;v], o, stacked [gate;up], down,
-                              embed, lm_head -> E4M3 + FP32 128x128 scales
   sender    lz4_encode_blocks LZ4 blocks (64 KiB) of the XOR mask old ^ new,
                               the mask never materialised
   receiver  lz4_decode_parse  the serial token-chain parse of every block, on a
-                              second stream, while the receiver's FP8 quant of
-                              the same chunk keeps HBM busy
+                              second stream, while the next two keep HBM busy
+  receiver  pulse_apply_patch scatter the patch into the receiver's view (v0 -> v1)
+  receiver  fp8_block_quant   stacked [q;k;v], o, stacked [gate;up], down,
+                              embed, lm_head -> E4M3 + FP32 128x128 scales
   receiver  lz4_decode_apply  rebuild + XOR in place into the receiver's view
                               (--serial-decode: one lz4_decode_blocks call on
-                              the main stream instead)
+                              the main stream, no second stream)
 
 The mask is symmetric, so the XOR step takes the receiver from v1 back to v0:
 every step does identical work on identical data with no untimed restore.  The
@@ -240,10 +239,10 @@ def main():
 
             rec("cast_diff", lambda: pulse.pulse_cast_diff(W[s0:e0], b_old[s0:e0], stage[:m], None, idx, val,
                                                            cnt[ci:ci + 1], status, ws_cd))
-            rec("apply_patch", lambda: pulse.pulse_apply_patch(b_recv[s0:e0], idx, val, cnt[ci:ci + 1], status))
             rec("lz4_encode", lambda: pulse.lz4_encode_blocks(b_old[s0:e0], payload, csizes, coffs, ctotal[ci:ci + 1],
                                                               status, ws_en, src_xor=stage[:m]))
             if args.serial_decode:
+                rec("apply_patch", lambda: pulse.pulse_apply_patch(b_recv[s0:e0], idx, val, cnt[ci:ci + 1], status))
                 rec("fp8_quant", quant)
                 rec("lz4_decode", lambda: pulse.lz4_decode_blocks(payload, coffs, csizes, b_recv[s0:e0], status,
                                                                   ws_de, mode=1))
@@ -257,6 +256,9 @@ def main():
                                                                  stream=side_stream), store=parse_ev)
                 parsed = torch.cuda.Event()
                 parsed.record(side_stream)
+            # the receiver's patch apply (v0 -> v1) and FP8 quant of v1 run beside the parse;
+            # the main stream takes no other kernel until the parse is done
+            rec("apply_patch", lambda: pulse.pulse_apply_patch(b_recv[s0:e0], idx, val, cnt[ci:ci + 1], status))
             rec("fp8_quant", quant)  # reads the receiver's view before the XOR rewrites it
             main_stream.wait_event(parsed)
             rec("lz4_decode", lambda: pulse.lz4_decode_apply(payload, coffs, csizes, b_recv[s0:e0], status, ws_de,
@@ -299,9 +301,9 @@ def main():
     ms_step = 1e3 * t_total / args.steps
     stage_ms = {k: sum(a.elapsed_time(b) for a, b in ev[k]) / args.steps for k in stages}
     launches = {k: len(ev[k]) // args.steps for k in stages}
-    # the decode stage is its parse (side stream, overlapped) plus its apply
+    # the decode stage is its apply (main stream); the parse runs on the side
+    # stream beside apply_patch and fp8_quant and is reported beside it
     parse_ms = sum(a.elapsed_time(b) for a, b in parse_ev["lz4_decode"]) / args.steps
-    stage_ms["lz4_decode"] += parse_ms
     # algorithmic bytes per step (what the method must move)
     alg = {
         "cast_diff": n * (8 + 6 * d),           # read w (4) + old (2), write new (2) + patch (6 d)
@@ -316,8 +318,6 @@ def main():
         secs = stage_ms[k] / 1e3
         st_out[k] = {"ms": round(stage_ms[k], 3), "launches": launches[k], "alg_GB": round(alg[k] / 1e9, 3),
                      "GBps": round(alg[k] / secs / 1e9, 1), "frac_hbm": round(alg[k] / secs / PEAK_HBM, 4)}
-    if not args.serial_decode:
-        st_out["lz4_decode"]["parse_ms_on_side_stream"] = round(parse_ms, 3)
     dom = max(stages, key=lambda k: stage_ms[k])
     dom_secs = stage_ms[dom] / 1e3
     achieved = alg[dom] / dom_secs / 1e9
@@ -348,12 +348,16 @@ def main():
                                "LZ4 mask encode, LZ4 decode+XOR",
                    "params": n, "chunks": len(chunks), "lz4_block_bytes": BLOCK,
                    "decode_schedule": "one call, main stream" if args.serial_decode
-                   else "parse on a second stream beside fp8_quant, apply on the main stream",
+                   else "parse on a second stream beside apply_patch and fp8_quant, apply on the main stream",
                    "changed_fraction": round(d, 6), "lz4_bytes_per_param": round(c, 5),
                    "lz4_ratio_of_mask": round(comp_bytes / (2 * n), 5), "fp8_params": n_quant},
         "hbm_frac_step": round(alg_total / (ms_step / 1e3) / PEAK_HBM, 4),
         "alg_GB_per_step": round(alg_total / 1e9, 2),
         "stages": st_out,
+        "decode_parse": None if args.serial_decode else {
+            "ms": round(parse_ms, 3), "launches": len(parse_ev["lz4_decode"]) // args.steps,
+            "stream": "second stream, beside apply_patch and fp8_quant of the same chunk",
+            "note": "lz4_decode above is the apply; the one-call decode is both"},
         "roofline": roofline,
         "setup_s": round(t_setup, 1),
     }

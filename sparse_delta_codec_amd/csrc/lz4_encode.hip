@@ -11,9 +11,10 @@
 // run's sequence depends only on its own (s, e, n), a block is parsed in
 // parallel and the output is bit-for-bit deterministic.
 //
-// One workgroup of 1024 threads (16 waves) per block; a persistent grid
-// walks the blocks in a static order (launch.hpp);
-// thread t owns the block bytes [t*CH, (t+1)*CH), CH = block_bytes / 1024 (64
+// One workgroup of 1024 threads (16 waves) per block, the block taken as a
+// ticket (one atomic) when the workgroup starts, so a block only ever waits
+// for blocks already handed to running workgroups (the encoder can share the
+// GPU with any other kernel); thread t owns the block bytes [t*CH, (t+1)*CH), CH = block_bytes / 1024 (64
 // for 64 KiB blocks, so a chunk's run boundaries fit one 64-bit mask):
 //  1. coalesced 16-byte loads (the XOR of two sources when given) into a 64 KiB
 //     LDS image whose 16-byte pieces are XOR-swizzled per chunk, so both the
@@ -32,7 +33,6 @@
 //     one window; a larger encoding (incompressible bytes) takes several
 //     window passes, each thread emitting only in the passes its bytes reach.
 #include "device.hpp"
-#include "launch.hpp"
 
 namespace pulse {
 
@@ -180,16 +180,11 @@ struct EncShared {
 
 // One block (b) of the encode, by the whole workgroup.
 template <int CHLOG>
-__device__ __forceinline__ void enc_block(const Lz4EncArgs &a, uint32_t b, uint32_t ep, EncShared &sh) {
+__device__ __forceinline__ void enc_block(const Lz4EncArgs &a, uint32_t b, uint32_t tag, EncShared &sh) {
     constexpr int32_t CH = 1 << CHLOG;
     uint8_t *const s_img = sh.img;
     uint8_t *const s_win = sh.win;
-    const uint32_t tag = epoch_tag(ep);
-    // thread index re-materialised per block (an empty asm the compiler cannot
-    // see through): values derived from it are not hoisted out of the block
-    // loop, which would hold them in registers across every block
-    int t = threadIdx.x;
-    asm volatile("" : "+v"(t));
+    const int t = threadIdx.x;
     const int wv = t / kWave, ln = t % kWave;
     const int64_t blk_base = (int64_t)b * a.block_bytes;
     const int32_t len = (int32_t)((a.nbytes - blk_base) < a.block_bytes ? (a.nbytes - blk_base) : a.block_bytes);
@@ -382,10 +377,7 @@ __device__ __forceinline__ void enc_block(const Lz4EncArgs &a, uint32_t b, uint3
                 sh.off = off;
                 a.comp_sizes[b] = (uint32_t)comp;
                 a.comp_offsets[b] = off;
-                if (b == a.nblocks - 1) {
-                    *a.d_total = off + comp;
-                    ws_epoch_advance(a.hdr, ep);
-                }
+                if (b == a.nblocks - 1) *a.d_total = off + comp;
                 if ((int64_t)(off + comp) > a.cap) or_agent32(a.d_status, 1u /*PULSE_DS_CAPACITY*/);
             }
         }
@@ -437,20 +429,23 @@ __device__ __forceinline__ void enc_block(const Lz4EncArgs &a, uint32_t b, uint3
     }
 }
 
-// Persistent: workgroup g encodes blocks g, g + G, g + 2G, ... in order (see
-// launch.hpp), so the look-back for a block's payload offset only ever waits
-// on running workgroups, without a per-block atomic ticket.
 template <int CHLOG>
 __global__ __launch_bounds__(LZE_THREADS, 8) void k_lz4_encode(Lz4EncArgs a) {
     __shared__ __align__(16) EncShared sh;
-    __shared__ uint32_t s_ep;
-    if (threadIdx.x == 0) s_ep = ws_epoch(a.hdr);
-    __syncthreads();
-    const uint32_t ep = s_ep;
-    for (uint32_t b = blockIdx.x; b < a.nblocks; b += gridDim.x) {
-        enc_block<CHLOG>(a, b, ep, sh);
-        __syncthreads();  // the LDS image and window are reused by the next block
+    __shared__ uint32_t s_b, s_tag;
+    if (threadIdx.x == 0) {
+        uint32_t b, tag;
+        ws_begin(a.hdr, a.nblocks, &b, &tag);
+        s_b = b;
+        s_tag = tag;
     }
+    __syncthreads();
+    const uint32_t b = s_b, tag = s_tag;
+    if (b >= a.nblocks) {  // inconsistent workspace state: touch nothing
+        if (threadIdx.x == 0) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
+        return;
+    }
+    enc_block<CHLOG>(a, b, tag, sh);
 }
 
 }  // namespace pulse
@@ -481,8 +476,9 @@ extern "C" int pulse_launch_lz4_encode(const void *src, const void *src_xor, int
     a.status = reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + sizeof(WsHeader));
     const int64_t nb = (nbytes + block_bytes - 1) / block_bytes;
     a.nblocks = (uint32_t)nb;
-    const void *k = block_bytes == 65536   ? reinterpret_cast<const void *>(&k_lz4_encode<6>)
-                    : block_bytes == 32768 ? reinterpret_cast<const void *>(&k_lz4_encode<5>)
-                                           : reinterpret_cast<const void *>(&k_lz4_encode<4>);
-    return launch_persistent(k, nb, LZE_THREADS, 0, a, stream);
+    const dim3 grid((unsigned)nb), block(LZE_THREADS);
+    if (block_bytes == 65536) k_lz4_encode<6><<<grid, block, 0, stream>>>(a);
+    else if (block_bytes == 32768) k_lz4_encode<5><<<grid, block, 0, stream>>>(a);
+    else k_lz4_encode<4><<<grid, block, 0, stream>>>(a);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
 }
