@@ -8,14 +8,11 @@
 // indices and new absolute values (PULSE technical summary, "1. PULSESync").
 //
 // One launch streams the tensor once; the patch is written in ascending index
-// order by a single-pass decoupled look-back over 16384-element tiles.  The
-// grid is persistent (as many workgroups as are resident at once, launched
-// cooperatively) and walks the tiles in a static order, so no tile waits for
-// one that has not been handed to a running workgroup, and no per-tile atomic
-// ticket is needed (one device-scope atomic per tile on a single address was
-// the throughput limit).
+// order by a single-pass decoupled look-back over 16384-element tiles, one
+// workgroup per tile.  Tiles are handed out as tickets (one device-scope atomic
+// when a workgroup starts), so no tile ever waits for one that has not been
+// handed to a running workgroup, whatever else shares the GPU.
 #include "device.hpp"
-#include "launch.hpp"
 
 namespace pulse {
 
@@ -291,9 +288,8 @@ __device__ __forceinline__ void cd_stage(uint64_t flags, const uint32_t nvp[], i
 
 // One tile: pass 1, the tile total, its look-back, pass 2 (ranked stores).
 template <bool FULL, bool FROM_F32, bool W_NEW, bool W_MASK>
-__device__ __forceinline__ void cd_tile(const CastDiffArgs &a, uint32_t tile, uint32_t ep, CdShared &sh) {
+__device__ __forceinline__ void cd_tile(const CastDiffArgs &a, uint32_t tile, uint32_t tag, CdShared &sh) {
     const int w = wave_id(), l = lane_id();
-    const uint32_t tag = epoch_tag(ep);
     const int64_t wbase = (int64_t)tile * CD_TILE + (int64_t)w * CD_WAVE_ELEMS;
     const int lo = 4 * l;
     uint32_t nvp[CD_GROUPS * 2];  // new values, two per register
@@ -314,10 +310,7 @@ __device__ __forceinline__ void cd_tile(const CastDiffArgs &a, uint32_t tile, ui
     auto place = [&](uint64_t pre, bool failed) {  // lane 0 of wave 0
         if (failed) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
         sh.prefix = pre;
-        if (tile == a.ntiles - 1) {
-            *a.d_count = (int64_t)(pre + tile_count);
-            ws_epoch_advance(a.hdr, ep);
-        }
+        if (tile == a.ntiles - 1) *a.d_count = (int64_t)(pre + tile_count);
         if ((int64_t)(pre + tile_count) > a.cap) or_agent32(a.d_status, 1u /*PULSE_DS_CAPACITY*/);
     };
     if (wmax <= (uint32_t)CD_SB) {
@@ -343,23 +336,31 @@ __device__ __forceinline__ void cd_tile(const CastDiffArgs &a, uint32_t tile, ui
         __syncthreads();
         if (tile_count != 0) cd_pass2(a, flags, nvp, wbase, lo, (int64_t)sh.prefix + wpre, sh.sbi[w], sh.sbv[w]);
     }
-    __syncthreads();  // sh is reused by the next tile
 }
 
-// Persistent: workgroup b places tiles b, b + G, b + 2G, ... in order; the one
-// tile that extends past n (always the last) goes through the checked path.
+// One workgroup per tile, the tile taken as a ticket (one atomic) when the
+// workgroup starts: a tile only waits on tiles of workgroups already running,
+// so the kernel can share the GPU with any other.  The one tile that extends
+// past n (always the last) goes through the checked path.
 template <bool FROM_F32, bool W_NEW, bool W_MASK>
 __global__ __launch_bounds__(CD_THREADS) void k_cast_compact(CastDiffArgs a) {
-    __shared__ uint32_t s_ep;
+    __shared__ uint32_t s_tile, s_tag;
     __shared__ CdShared sh;
-    if (threadIdx.x == 0) s_ep = ws_epoch(a.hdr);
+    if (threadIdx.x == 0) {
+        uint32_t tile, tag;
+        ws_begin(a.hdr, a.ntiles, &tile, &tag);
+        s_tile = tile;
+        s_tag = tag;
+    }
     __syncthreads();
-    const uint32_t ep = s_ep;
+    const uint32_t tile = s_tile, tag = s_tag;
+    if (tile >= a.ntiles) {  // inconsistent workspace state: touch nothing
+        if (threadIdx.x == 0) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
+        return;
+    }
     const uint32_t nfull = (uint32_t)(a.n / CD_TILE);  // tiles entirely inside [0, n)
-    for (uint32_t tile = blockIdx.x; tile < nfull; tile += gridDim.x)
-        cd_tile<true, FROM_F32, W_NEW, W_MASK>(a, tile, ep, sh);
-    if (nfull < a.ntiles && nfull % gridDim.x == blockIdx.x)
-        cd_tile<false, FROM_F32, W_NEW, W_MASK>(a, nfull, ep, sh);
+    if (tile < nfull) cd_tile<true, FROM_F32, W_NEW, W_MASK>(a, tile, tag, sh);
+    else cd_tile<false, FROM_F32, W_NEW, W_MASK>(a, tile, tag, sh);
 }
 
 // ---- one launch over a list of tensors ---------------------------------------
@@ -514,16 +515,16 @@ extern "C" int pulse_launch_cast_diff(const float *w_new, const uint16_t *b_in, 
     a.status = reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + sizeof(WsHeader));
     const int64_t ntiles = (n + CD_TILE - 1) / CD_TILE;
     a.ntiles = (uint32_t)ntiles;
-    const void *k;
+    const dim3 g((unsigned)ntiles), b(CD_THREADS);
     if (w_new) {
-        if (b_new && mask) k = reinterpret_cast<const void *>(&k_cast_compact<true, true, true>);
-        else if (b_new) k = reinterpret_cast<const void *>(&k_cast_compact<true, true, false>);
-        else if (mask) k = reinterpret_cast<const void *>(&k_cast_compact<true, false, true>);
-        else k = reinterpret_cast<const void *>(&k_cast_compact<true, false, false>);
+        if (b_new && mask) k_cast_compact<true, true, true><<<g, b, 0, stream>>>(a);
+        else if (b_new) k_cast_compact<true, true, false><<<g, b, 0, stream>>>(a);
+        else if (mask) k_cast_compact<true, false, true><<<g, b, 0, stream>>>(a);
+        else k_cast_compact<true, false, false><<<g, b, 0, stream>>>(a);
     } else {
-        k = reinterpret_cast<const void *>(&k_cast_compact<false, false, false>);
+        k_cast_compact<false, false, false><<<g, b, 0, stream>>>(a);
     }
-    return launch_persistent(k, ntiles, CD_THREADS, 0, a, stream);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
 extern "C" size_t pulse_cast_diff_ws_bytes(int64_t n) {

@@ -278,19 +278,6 @@ __device__ __forceinline__ void ws_begin(WsHeader *h, uint32_t ntiles, uint32_t 
         st_agent(&h->state, ((uint64_t)((ep + 1u) % kTagMod) << 40) | ((t + 1) & kBaseMask));
 }
 
-// Per-call epoch of a workspace used by a persistent kernel (static tile order,
-// no tickets): every workgroup reads it before its first tile; the workgroup
-// that places the call's last tile advances it.  That tile's look-back only
-// ends once every other tile has published, i.e. once every workgroup has
-// read the epoch, so no workgroup of this call can see the next value.
-__device__ __forceinline__ uint32_t ws_epoch(const WsHeader *h) {
-    return (uint32_t)(ld_agent(&h->state) >> 40);
-}
-__device__ __forceinline__ uint32_t epoch_tag(uint32_t ep) { return ep % kTagMod + 1u; }
-__device__ __forceinline__ void ws_epoch_advance(WsHeader *h, uint32_t ep) {
-    st_agent(&h->state, (uint64_t)((ep + 1u) % kTagMod) << 40);
-}
-
 // Decoupled look-back, executed by one full wave (all 64 lanes) of the tile.
 // Publishes the tile's aggregate, sums predecessors' aggregates until one with
 // an inclusive prefix is found, publishes the tile's inclusive prefix and
