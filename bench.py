@@ -5,10 +5,12 @@ One step = one pass of the whole hot path over a Qwen2.5-32B-shaped weight set
 view resident in HBM before timing starts), processed in 18 chunks of whole
 tensors (embed | 16 x four decoder layers | final norm + lm_head):
 
-  sender    pulse_cast_diff   FP32 -> BF16 RNE cast, bitwise diff against the
-                              old view, (int32 index, BF16 value) patch
-  sender    lz4_encode_blocks LZ4 blocks (64 KiB) of the XOR mask old ^ new,
-                              the mask never materialised
+  sender    pulse_cast_diff_lz4  one pass: FP32 -> BF16 RNE cast, bitwise diff
+                              against the old view, (int32 index, BF16 value)
+                              patch, and the LZ4 blocks (64 KiB) of the XOR mask
+                              old ^ new, the mask never leaving the chip
+                              (--separate-encode: pulse_cast_diff, then
+                              lz4_encode_blocks over old and new)
   receiver  lz4_decode_parse  the serial token-chain parse of every block, on a
                               second stream, while the next two keep HBM busy
   receiver  pulse_apply_patch scatter the patch into the receiver's view (v0 -> v1)
@@ -51,6 +53,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--layers", type=int, default=64, help="decoder layers (64 = the full Qwen2.5-32B shape)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--separate-encode", action="store_true",
+                   help="sender as two calls (pulse_cast_diff, then lz4_encode_blocks) instead of the fused pass")
     p.add_argument("--serial-decode", action="store_true",
                    help="decode each chunk with one lz4_decode_blocks call on the main stream (no overlap)")
     p.add_argument("--cpu-sample-frac", type=float, default=1.0,
@@ -191,6 +195,7 @@ def main():
     ctotal = torch.zeros(len(chunks), dtype=torch.int64, device=dev)
     ws_cd = pulse.workspace(pulse.PULSE_OP_CAST_DIFF, max_chunk, 0, dev)
     ws_en = pulse.workspace(pulse.PULSE_OP_LZ4_ENCODE, 2 * max_chunk, BLOCK, dev)
+    ws_fz = pulse.workspace(pulse.PULSE_OP_CAST_DIFF_LZ4, max_chunk, BLOCK, dev)
     ws_de = pulse.workspace(pulse.PULSE_OP_LZ4_DECODE, nbmax, pcap, dev)
     qplans = []
     max_codes = max_scales = 0
@@ -210,7 +215,8 @@ def main():
     t_setup = time.time() - t_setup
     log(f"setup done in {t_setup:.1f} s: {n} params in {len(chunks)} chunks")
 
-    stages = ["cast_diff", "apply_patch", "fp8_quant", "lz4_encode", "lz4_decode"]
+    fused = not args.separate_encode
+    stages = (["encode"] if fused else ["cast_diff", "lz4_encode"]) + ["apply_patch", "fp8_quant", "lz4_decode"]
     ev = {k: [] for k in stages}
 
     main_stream = torch.cuda.current_stream()
@@ -237,10 +243,16 @@ def main():
                     srcs = [b_recv[offs[i]: offs[i] + specs[i].numel].view(specs[i].shape) for i in g]
                     pulse.fp8_block_quant(srcs, codes, scales)
 
-            rec("cast_diff", lambda: pulse.pulse_cast_diff(W[s0:e0], b_old[s0:e0], stage[:m], None, idx, val,
-                                                           cnt[ci:ci + 1], status, ws_cd))
-            rec("lz4_encode", lambda: pulse.lz4_encode_blocks(b_old[s0:e0], payload, csizes, coffs, ctotal[ci:ci + 1],
-                                                              status, ws_en, src_xor=stage[:m]))
+            if fused:
+                rec("encode", lambda: pulse.pulse_cast_diff_lz4(W[s0:e0], b_old[s0:e0], stage[:m], idx, val,
+                                                                cnt[ci:ci + 1], payload, csizes, coffs,
+                                                                ctotal[ci:ci + 1], status, ws_fz))
+            else:
+                rec("cast_diff", lambda: pulse.pulse_cast_diff(W[s0:e0], b_old[s0:e0], stage[:m], None, idx, val,
+                                                               cnt[ci:ci + 1], status, ws_cd))
+                rec("lz4_encode", lambda: pulse.lz4_encode_blocks(b_old[s0:e0], payload, csizes, coffs,
+                                                                  ctotal[ci:ci + 1], status, ws_en,
+                                                                  src_xor=stage[:m]))
             if args.serial_decode:
                 rec("apply_patch", lambda: pulse.pulse_apply_patch(b_recv[s0:e0], idx, val, cnt[ci:ci + 1], status))
                 rec("fp8_quant", quant)
@@ -306,12 +318,14 @@ def main():
     parse_ms = sum(a.elapsed_time(b) for a, b in parse_ev["lz4_decode"]) / args.steps
     # algorithmic bytes per step (what the method must move)
     alg = {
+        "encode": n * (8 + 6 * d + c),          # read w (4) + old (2), write new (2) + patch (6 d) + payload (c)
         "cast_diff": n * (8 + 6 * d),           # read w (4) + old (2), write new (2) + patch (6 d)
         "apply_patch": n * 8 * d,               # read patch (6 d), write 2 B per changed element
         "fp8_quant": n_quant * 3 + 4 * n_quant / 16384,  # read 2, write 1 + scales
         "lz4_encode": n * (4 + c),              # read old + new (4), write payload (c)
         "lz4_decode": n * (4 + c),              # read payload (c), read + write dst (4)
     }
+    alg = {k: alg[k] for k in stages}
     alg_total = sum(alg.values())
     st_out = {}
     for k in stages:
@@ -321,7 +335,8 @@ def main():
     dom = max(stages, key=lambda k: stage_ms[k])
     dom_secs = stage_ms[dom] / 1e3
     achieved = alg[dom] / dom_secs / 1e9
-    kernel_files = {"cast_diff": "cast_diff.hip", "apply_patch": "apply.hip", "fp8_quant": "fp8_quant.hip",
+    kernel_files = {"encode": "lz4_encode.hip", "cast_diff": "cast_diff.hip", "apply_patch": "apply.hip",
+                    "fp8_quant": "fp8_quant.hip",
                     "lz4_encode": "lz4_encode.hip", "lz4_decode": "lz4_decode.hip"}
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9,
                 "unit": "GB/s", "frac": round(achieved * 1e9 / PEAK_HBM, 4), "traffic": None,
@@ -347,6 +362,8 @@ def main():
                                "full hot path: cast+diff+compact, patch apply, stacked FP8 quant, "
                                "LZ4 mask encode, LZ4 decode+XOR",
                    "params": n, "chunks": len(chunks), "lz4_block_bytes": BLOCK,
+                   "encode_schedule": "one fused pass (pulse_cast_diff_lz4)" if fused
+                   else "pulse_cast_diff, then lz4_encode_blocks",
                    "decode_schedule": "one call, main stream" if args.serial_decode
                    else "parse on a second stream beside apply_patch and fp8_quant, apply on the main stream",
                    "changed_fraction": round(d, 6), "lz4_bytes_per_param": round(c, 5),

@@ -87,6 +87,7 @@ extern "C" {
 #define PULSE_OP_LOCO_GATE 6  /* n = element count                               */
 #define PULSE_OP_PATCH_UNPACK 7 /* n = patch entries                            */
 #define PULSE_OP_CAST_DIFF_SEGMENTS 8 /* n = tile count (pulse_segment_tiles)    */
+#define PULSE_OP_CAST_DIFF_LZ4 9 /* n = element count, aux = block_bytes           */
 
 /* Bytes of workspace the op needs for the given size (0 if it needs none).
  * A workspace serves any number of calls of the op it was sized for, of any
@@ -147,6 +148,38 @@ int pulse_compact(const uint16_t *b_old, const uint16_t *b_new, int32_t *patch_i
                   uint16_t *patch_val, int64_t patch_cap, int64_t *d_count,
                   uint32_t *d_status, int64_t n, void *ws, size_t ws_bytes,
                   hipStream_t stream);
+
+/* ---- a1 + a2 + a3 + a5 in one pass ----------------------------------------
+ * The sender's whole encode in one launch: exactly the results of
+ *   pulse_cast_diff(w_new, b_old, b_new, NULL, patch_idx, patch_val, patch_cap,
+ *                   d_count, d_status, n, ...)
+ * followed by
+ *   lz4_encode_blocks(b_old, b_new, 2 n, block_bytes, payload, payload_cap,
+ *                     comp_sizes, comp_offsets, d_total, d_status, ...),
+ * i.e. the served view cast from the masters ([Jiang talk] 10:49-10:56), the
+ * patch of changed elements with their new absolute values ([PULSE summary]
+ * "1. PULSESync") and the LZ4 blocks of the XOR mask old ^ new ([Teleport]
+ * "XOR masks", "Moving the pipeline onto GPUs"), with the mask kept on chip and
+ * each view read once.  Where the separate calls would run two passes over
+ * the views, this runs one.
+ *   w_new      [n] float32 masters (read), 16-byte aligned.
+ *   b_old      [n] previous BF16 view (read), 16-byte aligned.
+ *   b_new      [n] new BF16 view (written), 16-byte aligned, or NULL; it may
+ *              be b_old itself (the view is updated in place).
+ *   patch_idx, patch_val, d_count  the patch as for pulse_cast_diff, or all
+ *              three NULL (mask blocks only).
+ *   block_bytes, payload .. d_total  as for lz4_encode_blocks, over the 2 n
+ *              bytes of the mask.
+ *   d_status   PULSE_DS_CAPACITY when the patch or the payload exceeds its
+ *              capacity (counts and totals stay exact).
+ *   ws         pulse_workspace_bytes(PULSE_OP_CAST_DIFF_LZ4, n, block_bytes).
+ * n >= 1, and n <= 2^31 - 1 when a patch is asked for. */
+int pulse_cast_diff_lz4(const float *w_new, const uint16_t *b_old, uint16_t *b_new,
+                        int32_t *patch_idx, uint16_t *patch_val, int64_t patch_cap,
+                        int64_t *d_count, int64_t n, int32_t block_bytes, uint8_t *payload,
+                        int64_t payload_cap, uint32_t *comp_sizes, uint64_t *comp_offsets,
+                        uint64_t *d_total, uint32_t *d_status, void *ws, size_t ws_bytes,
+                        hipStream_t stream);
 
 /* ---- a4: patch scatter-apply ---------------------------------------------
  * Selective override: b[patch_idx[k]] = patch_val[k] for k < count, bit-level

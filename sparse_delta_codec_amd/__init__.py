@@ -20,7 +20,7 @@ __all__ = [
     "PULSE_OP_FP8_DELTA", "PULSE_OP_LOCO_GATE", "fp8_view_delta", "fp8_view_apply",
     "pulse_loco_gate", "pulse_loco_accumulate",
     "PULSE_OP_PATCH_UNPACK", "patch_packed_bytes", "patch_pack", "patch_unpack",
-    "PULSE_OP_CAST_DIFF_SEGMENTS", "PULSE_DS_BADSEGMENT", "pulse_segment_tiles", "SegmentTable", "ViewTable",
+    "PULSE_OP_CAST_DIFF_SEGMENTS", "PULSE_DS_BADSEGMENT", "PULSE_OP_CAST_DIFF_LZ4", "pulse_cast_diff_lz4", "pulse_segment_tiles", "SegmentTable", "ViewTable",
     "pulse_cast_diff_segments", "pulse_apply_patch_segments", "lz4_decode_parse", "lz4_decode_apply",
 ]
 
@@ -44,6 +44,7 @@ PULSE_OP_FP8_DELTA = 5
 PULSE_OP_LOCO_GATE = 6
 PULSE_OP_PATCH_UNPACK = 7
 PULSE_OP_CAST_DIFF_SEGMENTS = 8
+PULSE_OP_CAST_DIFF_LZ4 = 9
 PULSE_DS_BADSEGMENT = 0x10
 
 _P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
@@ -74,11 +75,12 @@ _lib.pulse_segment_tiles.argtypes = [_P, _I32, _P, _P]
 _lib.pulse_segment_tiles.restype = _I64
 _lib.pulse_cast_diff_segments.argtypes = [_P, _I32, _P, _I64, _P, _P, _I64, _P, _P, _P, _SZ, _I32, _P]
 _lib.pulse_apply_patch_segments.argtypes = [_P, _I32, _P, _P, _P, _I64, _P, _P]
+_lib.pulse_cast_diff_lz4.argtypes = [_P, _P, _P, _P, _P, _I64, _P, _I64, _I32, _P, _I64, _P, _P, _P, _P, _P, _SZ, _P]
 for _f in ("pulse_cast_diff_segments", "pulse_apply_patch_segments", "patch_pack", "patch_unpack",
            "pulse_workspace_init", "pulse_cast_diff", "pulse_compact", "pulse_apply_patch",
            "xor_mask_apply", "lz4_encode_blocks", "lz4_decode_blocks", "fp8_block_quant",
            "fp8_view_delta", "fp8_view_apply", "pulse_loco_gate", "pulse_loco_accumulate",
-           "lz4_decode_parse", "lz4_decode_apply"):
+           "lz4_decode_parse", "lz4_decode_apply", "pulse_cast_diff_lz4"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -208,6 +210,29 @@ def lz4_encode_blocks(src, payload, comp_sizes, comp_offsets, d_total, d_status,
         payload.numel(), _dev(comp_sizes, "comp_sizes", torch.int32), _dev(comp_offsets, "comp_offsets", torch.int64),
         _dev(d_total, "d_total", torch.int64), _dev(d_status, "d_status", torch.int32), wsp, wsb,
         _stream(stream)), "lz4_encode_blocks")
+
+
+def pulse_cast_diff_lz4(w_new, b_old, b_new, patch_idx, patch_val, d_count, payload, comp_sizes, comp_offsets,
+                        d_total, d_status, ws, block_bytes=65536, n=None, stream=None):
+    """cast + diff + patch + LZ4 blocks of the XOR mask in one pass (patch_idx,
+    patch_val and d_count all None: mask blocks only)."""
+    n = w_new.numel() if n is None else n
+    nb = (2 * n + block_bytes - 1) // block_bytes
+    cap = 0 if patch_idx is None else patch_idx.numel()
+    _need(w_new, 4 * n, "w_new")
+    _need(b_old, 2 * n, "b_old")
+    _need(b_new, 2 * n, "b_new")
+    _need(patch_val, 2 * cap, "patch_val")
+    _need(comp_sizes, 4 * nb, "comp_sizes")
+    _need(comp_offsets, 8 * nb, "comp_offsets")
+    wsp, wsb = _ws(ws)
+    _check(_lib.pulse_cast_diff_lz4(
+        _dev(w_new, "w_new", torch.float32), _dev(b_old, "b_old", _U16), _dev(b_new, "b_new", _U16),
+        _dev(patch_idx, "patch_idx", torch.int32), _dev(patch_val, "patch_val", _U16), cap,
+        _dev(d_count, "d_count", torch.int64), n, block_bytes, _dev(payload, "payload", torch.uint8), payload.numel(),
+        _dev(comp_sizes, "comp_sizes", torch.int32), _dev(comp_offsets, "comp_offsets", torch.int64),
+        _dev(d_total, "d_total", torch.int64), _dev(d_status, "d_status", torch.int32), wsp, wsb,
+        _stream(stream)), "pulse_cast_diff_lz4")
 
 
 def _decode_table(payload, comp_offsets, comp_sizes, nbytes, payload_bytes, block_bytes):

@@ -48,6 +48,10 @@ int pulse_launch_cast_diff_segments(const void *, int32_t, const uint32_t *, int
 int pulse_launch_apply_patch_segments(const void *, int32_t, const int32_t *, const uint16_t *, const int64_t *,
                                       int64_t, uint32_t *, hipStream_t);
 int pulse_launch_fill_zero(void *, size_t, hipStream_t);
+size_t pulse_cast_diff_lz4_ws_bytes(int64_t n, int32_t block_bytes);
+int pulse_launch_cast_diff_lz4(const float *, const uint16_t *, uint16_t *, int32_t *, uint16_t *, int64_t,
+                               int64_t *, int64_t, int32_t, uint8_t *, int64_t, uint32_t *, uint64_t *, uint64_t *,
+                               uint32_t *, void *, hipStream_t);
 int pulse_launch_write_count(int64_t *, int64_t, hipStream_t);
 }
 
@@ -91,6 +95,9 @@ size_t pulse_workspace_bytes(int op, int64_t n, int64_t aux) {
     case PULSE_OP_LOCO_GATE: return pulse_delta_compact_ws_bytes(n);
     case PULSE_OP_PATCH_UNPACK: return pulse_patch_unpack_ws_bytes(n);
     case PULSE_OP_CAST_DIFF_SEGMENTS: return sizeof(uint64_t) * 32 + (size_t)(n > 0 ? n : 1) * sizeof(uint64_t);
+    case PULSE_OP_CAST_DIFF_LZ4:
+        if (aux != 16384 && aux != 32768 && aux != 65536) return 0;
+        return pulse_cast_diff_lz4_ws_bytes(n, (int32_t)aux);
     default: return 0;
     }
 }
@@ -134,6 +141,26 @@ int pulse_compact(const uint16_t *b_old, const uint16_t *b_new, int32_t *patch_i
     if (n == 0) return pulse_launch_write_count(d_count, 0, stream);
     return pulse_launch_cast_diff(nullptr, b_new, b_old, nullptr, nullptr, patch_idx, patch_val, patch_cap,
                                   d_count, d_status, n, ws, stream);
+}
+
+int pulse_cast_diff_lz4(const float *w_new, const uint16_t *b_old, uint16_t *b_new, int32_t *patch_idx,
+                        uint16_t *patch_val, int64_t patch_cap, int64_t *d_count, int64_t n, int32_t block_bytes,
+                        uint8_t *payload, int64_t payload_cap, uint32_t *comp_sizes, uint64_t *comp_offsets,
+                        uint64_t *d_total, uint32_t *d_status, void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (!w_new || !b_old || !payload || !comp_sizes || !comp_offsets || !d_total || !d_status || n <= 0 ||
+        payload_cap < 0 || patch_cap < 0)
+        return PULSE_EINVAL;
+    const bool patch = patch_idx || patch_val || d_count;
+    if (patch && !(patch_idx && patch_val && d_count)) return PULSE_EINVAL;
+    if (block_bytes != 16384 && block_bytes != 32768 && block_bytes != 65536) return PULSE_EINVAL;
+    if (!aligned16(w_new) || !aligned16(b_old) || (b_new && !aligned16(b_new))) return PULSE_EALIGN;
+    if (patch && n > kMaxIndexed) return PULSE_ERANGE;
+    const int64_t nb = (2 * n + block_bytes - 1) / block_bytes;
+    if (nb > 0xFFFFFFFFll || 2 * n > kMaxPayload / 2) return PULSE_ERANGE;
+    if (!ws || ws_bytes < pulse_cast_diff_lz4_ws_bytes(n, block_bytes)) return PULSE_EWORKSPACE;
+    return pulse_launch_cast_diff_lz4(w_new, b_old, b_new, patch ? patch_idx : nullptr, patch_val, patch_cap,
+                                      d_count, n, block_bytes, payload, payload_cap, comp_sizes, comp_offsets,
+                                      d_total, d_status, ws, stream);
 }
 
 int pulse_apply_patch(uint16_t *b, int64_t n, const int32_t *patch_idx, const uint16_t *patch_val,

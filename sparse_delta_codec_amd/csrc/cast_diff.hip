@@ -115,9 +115,6 @@ constexpr int CD_GROUPS = 16;
 constexpr int CD_WAVE_ELEMS = CD_GROUPS * 256;                    // 4096
 constexpr int CD_TILE = (CD_THREADS / kWave) * CD_WAVE_ELEMS;   // 16384
 
-__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
-    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-}
 
 // Pass 1 of one tile for one thread: loads, cast, compare, the b_new / mask
 // stores; returns the changed flags (bit 4g+k: element g*256 + 4l + k) and
@@ -125,17 +122,6 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
 // lies inside [0, n): the 8 groups of a half are loaded before any is used
 // (float4 + 8 bytes per group), and every compare and store works on pairs of
 // BF16 packed in 32 bits.
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint32_t cast_pair(float x, float y) {
-    return (uint32_t)bf16_rne(__float_as_uint(x)) | ((uint32_t)bf16_rne(__float_as_uint(y)) << 16);
-}
-
-__device__ __forceinline__ uint64_t pair_flags(uint32_t x0, uint32_t x1) {
-    return (uint64_t)((x0 & 0xFFFFu) != 0) | ((uint64_t)((x0 >> 16) != 0) << 1) |
-           ((uint64_t)((x1 & 0xFFFFu) != 0) << 2) | ((uint64_t)((x1 >> 16) != 0) << 3);
-}
-
 template <bool FULL, bool FROM_F32, bool W_NEW, bool W_MASK>
 __device__ __forceinline__ uint64_t cd_pass1(const CastDiffArgs &a, int64_t wbase, int lo, uint32_t nvp[]) {
     uint64_t flags = 0;

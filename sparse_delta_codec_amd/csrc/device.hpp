@@ -366,4 +366,22 @@ __device__ __forceinline__ uint16_t bf16_rne(uint32_t x) {
     return (uint16_t)((x + 0x7FFFu + ((x >> 16) & 1u)) >> 16);
 }
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// lanes below this one whose bit is set in m (rank of the lane among them)
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// two FP32 masters to two BF16 packed low-first in 32 bits
+__device__ __forceinline__ uint32_t cast_pair(float x, float y) {
+    return (uint32_t)bf16_rne(__float_as_uint(x)) | ((uint32_t)bf16_rne(__float_as_uint(y)) << 16);
+}
+
+// changed flags of four BF16 (two XOR words): bit k for element k
+__device__ __forceinline__ uint64_t pair_flags(uint32_t x0, uint32_t x1) {
+    return (uint64_t)((x0 & 0xFFFFu) != 0) | ((uint64_t)((x0 >> 16) != 0) << 1) |
+           ((uint64_t)((x1 & 0xFFFFu) != 0) << 2) | ((uint64_t)((x1 >> 16) != 0) << 3);
+}
+
 }  // namespace pulse

@@ -32,6 +32,16 @@
 //     then copied out with 16-byte stores.  Every block of a sparse mask fits
 //     one window; a larger encoding (incompressible bytes) takes several
 //     window passes, each thread emitting only in the passes its bytes reach.
+//
+// The fused sender pass (pulse_cast_diff_lz4) runs the same block encoder on a
+// mask it makes itself: step 1 becomes the FP32 -> BF16 cast of the block's
+// 32768 masters (64 KiB blocks), the compare with the old view, the store of
+// the new view and of old ^ new into the LDS image, so the mask never leaves
+// the chip and neither view is read twice.  The changed elements of the
+// block are ranked as they are found (ballots, in index order) and staged in
+// the output window, which is idle until step 5; a second look-back over the
+// blocks' patch counts, resolved while the block is analysed, places them in
+// the ascending (index, new value) patch.
 #include "device.hpp"
 
 namespace pulse {
@@ -176,11 +186,144 @@ struct EncShared {
     // block, after barriers every wave has passed, so each scan needs one barrier
     int32_t scan[4][LZE_NW];
     uint64_t off;
+    uint32_t pw[LZE_NW];  // fused pass: changed elements of each wave
+    uint64_t poff;        // fused pass: the block's first patch entry
 };
 
-// One block (b) of the encode, by the whole workgroup.
+// ---- fused sender pass: cast + diff + compaction feeding the block encoder ----
+struct FusedArgs {
+    const float *w_new;    // [n] FP32 masters
+    const uint16_t *b_old; // [n] previous view
+    uint16_t *b_new;       // [n] new view, or NULL (may equal b_old)
+    int32_t *idx;          // patch, or NULL (then val, d_count, pstatus unused)
+    uint16_t *val;
+    int64_t cap;
+    int64_t *d_count;
+    uint64_t *pstatus;     // look-back words over the blocks' patch counts
+    int64_t n;
+};
+
+// entries staged per wave in the output window: (offset in block, value) as
+// one 32-bit word; a wave with more falls back to direct stores
+constexpr int LZF_STAGE = (LZE_WIN + 48) / 4 / LZE_NW;
+
+// Step 1 of the fused pass for one wave: wave wv owns the block's elements
+// [wv * NG * 256, +NG * 256) as NG groups of 256, lane l holding elements
+// 256 g + 4 l + k (a 16-byte load of masters and an 8-byte load of the old
+// view per group, 1 KiB / 512 B contiguous per wave).  Cast, compare, store
+// the new view, put old ^ new into the image; with PATCH, rank each changed
+// element among the wave's (ballots, index order) and stage it.  Returns the
+// wave's number of changed elements.
+template <int CHLOG, bool PATCH>
+__device__ __forceinline__ uint32_t fused_pass1(const FusedArgs &f, int64_t blk_e0, uint8_t *s_img, uint32_t *stg) {
+    constexpr int BLK_E = (1 << CHLOG) * LZE_THREADS / 2;
+    constexpr int NG = BLK_E / (LZE_NW * 256);
+    constexpr int GI = NG < 4 ? NG : 4;  // groups in flight
+    const int wv = threadIdx.x / kWave, ln = threadIdx.x % kWave;
+    const int32_t w0 = wv * NG * 256 + 4 * ln;
+    const bool full = blk_e0 + BLK_E <= f.n;
+    uint32_t nb = 0;
+#pragma unroll
+    for (int h = 0; h < NG; h += GI) {
+        u32x4 fv[GI];
+        u32x2 ov[GI];
+#pragma unroll
+        for (int j = 0; j < GI; ++j) {
+            const int64_t e = blk_e0 + w0 + (h + j) * 256;
+            if (full) {
+                fv[j] = *reinterpret_cast<const u32x4 *>(f.w_new + e);
+                ov[j] = *reinterpret_cast<const u32x2 *>(f.b_old + e);
+            } else {  // the call's last block: elements past n read as zero
+                uint32_t fw[4], ow[2] = {0u, 0u};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const bool in = e + k < f.n;
+                    fw[k] = in ? __float_as_uint(f.w_new[e + k]) : 0u;
+                    ow[k >> 1] |= (in ? (uint32_t)f.b_old[e + k] : 0u) << (16 * (k & 1));
+                }
+                fv[j] = u32x4{fw[0], fw[1], fw[2], fw[3]};
+                ov[j] = u32x2{ow[0], ow[1]};
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < GI; ++j) {
+            const int32_t eo = w0 + (h + j) * 256;
+            const int64_t e = blk_e0 + eo;
+            const uint32_t p0 = cast_pair(__uint_as_float(fv[j].x), __uint_as_float(fv[j].y));
+            const uint32_t p1 = cast_pair(__uint_as_float(fv[j].z), __uint_as_float(fv[j].w));
+            const uint32_t x0 = p0 ^ ov[j].x, x1 = p1 ^ ov[j].y;  // zero past n
+            if (f.b_new) {
+                if (full) {
+                    *reinterpret_cast<u32x2 *>(f.b_new + e) = u32x2{p0, p1};
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        if (e + k < f.n) f.b_new[e + k] = (uint16_t)((k < 2 ? p0 : p1) >> (16 * (k & 1)));
+                }
+            }
+            *reinterpret_cast<u32x2 *>(s_img + img_addr<CHLOG>(2 * eo)) = u32x2{x0, x1};
+            if constexpr (PATCH) {
+                const uint32_t fl = (uint32_t)pair_flags(x0, x1);
+                const uint64_t m0 = __ballot(fl & 1u), m1 = __ballot(fl & 2u), m2 = __ballot(fl & 4u),
+                               m3 = __ballot(fl & 8u);
+                const uint32_t gtot = __builtin_popcountll(m0) + __builtin_popcountll(m1) +
+                                      __builtin_popcountll(m2) + __builtin_popcountll(m3);
+                uint32_t r = nb + lanes_below(m0) + lanes_below(m1) + lanes_below(m2) + lanes_below(m3);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    if (fl & (1u << k)) {
+                        if (r < (uint32_t)LZF_STAGE)
+                            stg[r] = (uint32_t)(eo + k) | (((k < 2 ? p0 : p1) >> (16 * (k & 1))) << 16);
+                        ++r;
+                    }
+                }
+                nb += gtot;
+            }
+        }
+        sched_fence();  // GI groups of loads in flight at a time
+    }
+    return nb;
+}
+
+// Patch stores of a block whose waves could not all stage their entries: the
+// flags come back from the image, the values from the masters (the old view
+// may already be overwritten by the new one).
 template <int CHLOG>
-__device__ __forceinline__ void enc_block(const Lz4EncArgs &a, uint32_t b, uint32_t tag, EncShared &sh) {
+__device__ __forceinline__ void fused_patch_direct(const FusedArgs &f, int64_t blk_e0, const uint8_t *s_img,
+                                                   int64_t run) {
+    constexpr int BLK_E = (1 << CHLOG) * LZE_THREADS / 2;
+    constexpr int NG = BLK_E / (LZE_NW * 256);
+    const int wv = threadIdx.x / kWave, ln = threadIdx.x % kWave;
+    const int32_t w0 = wv * NG * 256 + 4 * ln;
+#pragma unroll 1
+    for (int g = 0; g < NG; ++g) {
+        const int32_t eo = w0 + g * 256;
+        const u32x2 x = *reinterpret_cast<const u32x2 *>(s_img + img_addr<CHLOG>(2 * eo));
+        const uint32_t fl = (uint32_t)pair_flags(x.x, x.y);
+        const uint64_t m0 = __ballot(fl & 1u), m1 = __ballot(fl & 2u), m2 = __ballot(fl & 4u), m3 = __ballot(fl & 8u);
+        const uint32_t gtot = __builtin_popcountll(m0) + __builtin_popcountll(m1) + __builtin_popcountll(m2) +
+                              __builtin_popcountll(m3);
+        int64_t r = run + lanes_below(m0) + lanes_below(m1) + lanes_below(m2) + lanes_below(m3);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if (fl & (1u << k)) {
+                const int64_t e = blk_e0 + eo + k;
+                if (r < f.cap) {
+                    f.idx[r] = (int32_t)e;
+                    f.val[r] = bf16_rne(__float_as_uint(f.w_new[e]));
+                }
+                ++r;
+            }
+        }
+        run += gtot;
+    }
+}
+
+// One block (b) of the encode, by the whole workgroup.  FUSED: the mask is
+// made from (f.w_new, f.b_old) by the fused pass; PATCH: with its patch.
+template <int CHLOG, bool FUSED = false, bool PATCH = false>
+__device__ __forceinline__ void enc_block(const Lz4EncArgs &a, const FusedArgs &f, uint32_t b, uint32_t tag,
+                                          EncShared &sh) {
     constexpr int32_t CH = 1 << CHLOG;
     uint8_t *const s_img = sh.img;
     uint8_t *const s_win = sh.win;
@@ -189,8 +332,14 @@ __device__ __forceinline__ void enc_block(const Lz4EncArgs &a, uint32_t b, uint3
     const int64_t blk_base = (int64_t)b * a.block_bytes;
     const int32_t len = (int32_t)((a.nbytes - blk_base) < a.block_bytes ? (a.nbytes - blk_base) : a.block_bytes);
 
-    // 1. load
-    const int32_t npieces = a.block_bytes / 16;
+    // 1. load (or make) the mask
+    uint32_t *const stg = reinterpret_cast<uint32_t *>(s_win) + wv * LZF_STAGE;
+    const int64_t blk_e0 = blk_base / 2;
+    if constexpr (FUSED) {
+        const uint32_t nb = fused_pass1<CHLOG, PATCH>(f, blk_e0, s_img, stg);
+        if (PATCH && ln == 0) sh.pw[wv] = nb;
+    }
+    const int32_t npieces = FUSED ? 0 : a.block_bytes / 16;
     for (int32_t q = t; q < npieces; q += LZE_THREADS) {
         const int32_t off = q * 16;
         uint4 v = make_uint4(0, 0, 0, 0);
@@ -212,6 +361,26 @@ __device__ __forceinline__ void enc_block(const Lz4EncArgs &a, uint32_t b, uint3
         *reinterpret_cast<uint4 *>(s_img + img_addr<CHLOG>(off)) = v;
     }
     __syncthreads();
+    // the block's patch count goes out at once, so later blocks' look-backs
+    // can sum it while this block is still being analysed
+    if constexpr (PATCH) {
+        // wave 1 places the block's patch among the others: every block
+        // publishes its count right after its pass 1, so the look-back only
+        // waits for blocks that are still loading
+        if (wv == 1) {
+            uint32_t p_count = 0;
+#pragma unroll
+            for (int w = 0; w < LZE_NW; ++w) p_count += sh.pw[w];
+            bool failed = false;
+            const uint64_t pre = lookback_wave(f.pstatus, b, tag, (uint64_t)p_count, &failed);
+            if (ln == 0) {
+                if (failed) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
+                sh.poff = pre;
+                if (b == a.nblocks - 1) *f.d_count = (int64_t)(pre + p_count);
+                if ((int64_t)(pre + p_count) > f.cap) or_agent32(a.d_status, 1u /*PULSE_DS_CAPACITY*/);
+            }
+        }
+    }
 
     // 2. run-boundary bitmask of this thread's chunk
     const int32_t cs = t * CH;
@@ -274,6 +443,35 @@ __device__ __forceinline__ void enc_block(const Lz4EncArgs &a, uint32_t b, uint3
             if (w > wv) above = x < above ? x : above;
         }
         next_after = exc < above ? exc : above;
+    }
+
+    // the fused pass's patch, placed by wave 1 before the barrier above: the
+    // staged entries go out with coalesced stores (the window is next written
+    // by the emission, two barriers later)
+    if constexpr (PATCH) {
+        uint32_t p_wpre = 0, p_wmax = 0, p_mine = 0;
+#pragma unroll
+        for (int w = 0; w < LZE_NW; ++w) {
+            const uint32_t x = sh.pw[w];
+            if (w < wv) p_wpre += x;
+            if (w == wv) p_mine = x;
+            p_wmax = x > p_wmax ? x : p_wmax;
+        }
+        const uint32_t po_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(sh.poff >> 32));
+        const uint32_t po_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)sh.poff);
+        const int64_t run = (int64_t)(((uint64_t)po_hi << 32) | po_lo) + p_wpre;
+        if (p_wmax <= (uint32_t)LZF_STAGE) {
+            for (uint32_t i = ln; i < p_mine; i += kWave) {
+                const int64_t pos = run + i;
+                if (pos < f.cap) {
+                    const uint32_t v = stg[i];
+                    f.idx[pos] = (int32_t)(blk_e0 + (v & 0xFFFFu));
+                    f.val[pos] = (uint16_t)(v >> 16);
+                }
+            }
+        } else {
+            fused_patch_direct<CHLOG>(f, blk_e0, s_img, run);
+        }
     }
 
     // 3. the runs that become sequences (bit-parallel), then one pass over
@@ -445,7 +643,26 @@ __global__ __launch_bounds__(LZE_THREADS, 8) void k_lz4_encode(Lz4EncArgs a) {
         if (threadIdx.x == 0) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
         return;
     }
-    enc_block<CHLOG>(a, b, tag, sh);
+    enc_block<CHLOG>(a, FusedArgs{}, b, tag, sh);
+}
+
+template <int CHLOG, bool PATCH>
+__global__ __launch_bounds__(LZE_THREADS, 8) void k_cast_diff_lz4(Lz4EncArgs a, FusedArgs f) {
+    __shared__ __align__(16) EncShared sh;
+    __shared__ uint32_t s_b, s_tag;
+    if (threadIdx.x == 0) {
+        uint32_t b, tag;
+        ws_begin(a.hdr, a.nblocks, &b, &tag);
+        s_b = b;
+        s_tag = tag;
+    }
+    __syncthreads();
+    const uint32_t b = s_b, tag = s_tag;
+    if (b >= a.nblocks) {  // inconsistent workspace state: touch nothing
+        if (threadIdx.x == 0) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
+        return;
+    }
+    enc_block<CHLOG, true, PATCH>(a, f, b, tag, sh);
 }
 
 }  // namespace pulse
@@ -480,5 +697,58 @@ extern "C" int pulse_launch_lz4_encode(const void *src, const void *src_xor, int
     if (block_bytes == 65536) k_lz4_encode<6><<<grid, block, 0, stream>>>(a);
     else if (block_bytes == 32768) k_lz4_encode<5><<<grid, block, 0, stream>>>(a);
     else k_lz4_encode<4><<<grid, block, 0, stream>>>(a);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+// Workspace of the fused pass: the header, the blocks' payload-size words, then
+// their patch-count words.
+extern "C" size_t pulse_cast_diff_lz4_ws_bytes(int64_t n, int32_t block_bytes) {
+    const int64_t nb = block_bytes > 0 ? (2 * n + block_bytes - 1) / block_bytes : 0;
+    return sizeof(WsHeader) + 2 * (size_t)(nb > 0 ? nb : 1) * sizeof(uint64_t);
+}
+
+extern "C" int pulse_launch_cast_diff_lz4(const float *w_new, const uint16_t *b_old, uint16_t *b_new, int32_t *idx,
+                                          uint16_t *val, int64_t cap, int64_t *d_count, int64_t n,
+                                          int32_t block_bytes, uint8_t *payload, int64_t payload_cap,
+                                          uint32_t *comp_sizes, uint64_t *comp_offsets, uint64_t *d_total,
+                                          uint32_t *d_status, void *ws, hipStream_t stream) {
+    const int64_t nbytes = 2 * n;
+    const int64_t nb = (nbytes + block_bytes - 1) / block_bytes;
+    Lz4EncArgs a{};
+    a.src = nullptr;
+    a.src_xor = nullptr;
+    a.nbytes = nbytes;
+    a.block_bytes = block_bytes;
+    a.payload = payload;
+    a.cap = payload_cap;
+    a.comp_sizes = comp_sizes;
+    a.comp_offsets = comp_offsets;
+    a.d_total = d_total;
+    a.d_status = d_status;
+    a.hdr = reinterpret_cast<WsHeader *>(ws);
+    a.status = reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + sizeof(WsHeader));
+    a.nblocks = (uint32_t)nb;
+    FusedArgs f{};
+    f.w_new = w_new;
+    f.b_old = b_old;
+    f.b_new = b_new;
+    f.idx = idx;
+    f.val = val;
+    f.cap = cap;
+    f.d_count = d_count;
+    f.pstatus = a.status + nb;
+    f.n = n;
+    const dim3 grid((unsigned)nb), block(LZE_THREADS);
+    const bool patch = idx != nullptr;
+    if (block_bytes == 65536) {
+        if (patch) k_cast_diff_lz4<6, true><<<grid, block, 0, stream>>>(a, f);
+        else k_cast_diff_lz4<6, false><<<grid, block, 0, stream>>>(a, f);
+    } else if (block_bytes == 32768) {
+        if (patch) k_cast_diff_lz4<5, true><<<grid, block, 0, stream>>>(a, f);
+        else k_cast_diff_lz4<5, false><<<grid, block, 0, stream>>>(a, f);
+    } else {
+        if (patch) k_cast_diff_lz4<4, true><<<grid, block, 0, stream>>>(a, f);
+        else k_cast_diff_lz4<4, false><<<grid, block, 0, stream>>>(a, f);
+    }
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }

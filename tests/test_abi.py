@@ -35,7 +35,7 @@ def test_header_declares_the_codec_calls():
     fns = declared_functions()
     for name in ("pulse_cast_diff", "pulse_compact", "pulse_apply_patch", "xor_mask_apply",
                  "lz4_encode_blocks", "lz4_decode_blocks", "lz4_decode_parse", "lz4_decode_apply",
-                 "fp8_block_quant", "pulse_workspace_bytes",
+                 "fp8_block_quant", "pulse_cast_diff_lz4", "pulse_workspace_bytes",
                  "pulse_workspace_init", "pulse_status_string", "pulse_version"):
         assert name in fns, name
 
@@ -63,6 +63,9 @@ def test_workspace_sizes(lib):
         assert cur > prev
         prev = cur
     assert ws(99, 10, 0) == 0
+    # fused sender pass: header + two status words per mask block
+    assert ws(9, 32768 * 3 + 1, 65536) == 256 + 2 * 4 * 8
+    assert ws(9, 1000, 1000) == 0
 
 
 V = ctypes.c_void_p
@@ -97,6 +100,16 @@ def test_argument_errors_return_before_any_launch(lib):
     assert par(al, 10, al, al, 3, 65536, 70000, al, al, 1 << 20, None) == EINVAL          # nblocks
     assert par(al, 10, None, al, 2, 65536, 70000, al, al, 1 << 20, None) == EINVAL        # no offsets
     assert par(al, 10, al, al, 2, 65536, 70000, al, al, 16, None) == EWORKSPACE
+    fz = lib.pulse_cast_diff_lz4
+    fz.argtypes = [V, V, V, V, V, I64, V, I64, ctypes.c_int32, V, I64, V, V, V, V, V, ctypes.c_size_t, V]
+    fargs = [al, al, al, al, al, 10, al, 1000, 65536, al, 100, al, al, al, al, al, 1 << 20, None]
+    assert fz(None, *fargs[1:]) == EINVAL                                         # no masters
+    assert fz(*fargs[:7], 0, *fargs[8:]) == EINVAL                                # n = 0
+    assert fz(*fargs[:8], 4096, *fargs[9:]) == EINVAL                             # block size
+    assert fz(*fargs[:4], None, *fargs[5:]) == EINVAL                             # partial patch
+    assert fz(*fargs[:2], mis, *fargs[3:]) == EALIGN                              # b_new
+    assert fz(*fargs[:7], 1 << 31, *fargs[8:]) == ERANGE                          # int32 indices
+    assert fz(*fargs[:16], 16, None) == EWORKSPACE
     app = lib.lz4_decode_apply
     app.argtypes = dec.argtypes
     assert app(al, 10, al, al, 2, 65536, 70000, al, 2, al, al, 1 << 20, None) == EINVAL     # mode

@@ -220,20 +220,73 @@ def test_apply_patch_matches_oracle_and_rebuilds():
 
 def test_apply_bad_index_and_count_bound():
     b = np.arange(100, dtype=np.uint16)
-    idx = np.array([1, 100, -5, 3, 7], np.int32)
+    idx = np.array([-5, 1, 3, 7, 100], np.int32)
     val = np.array([11, 12, 13, 14, 15], np.uint16)
-    B = dev(b)
-    st = zeros(1, torch.int32)
-    pulse.pulse_apply_patch(B, dev(idx), dev(val), dev(np.array([4], np.int64)), st, max_count=5)
+    for count, want in ((4, pulse.PULSE_DS_BADINDEX), (3, pulse.PULSE_DS_BADINDEX), (5, pulse.PULSE_DS_BADINDEX)):
+        B = dev(b)
+        st = zeros(1, torch.int32)
+        pulse.pulse_apply_patch(B, dev(idx), dev(val), dev(np.array([count], np.int64)), st, max_count=5)
+        torch.cuda.synchronize()
+        ref, rst = oracle.apply_patch(b, idx, val, count=count)
+        assert np.array_equal(u16(B), ref) and int(host(st)[0]) == rst == want
+    # in-range entries only: no status
+    B, st = dev(b), zeros(1, torch.int32)
+    pulse.pulse_apply_patch(B, dev(idx[1:]), dev(val[1:]), dev(np.array([3], np.int64)), st, max_count=4)
     torch.cuda.synchronize()
-    ref, rst = oracle.apply_patch(b, idx, val, count=4)
-    assert np.array_equal(u16(B), ref) and int(host(st)[0]) == rst == pulse.PULSE_DS_BADINDEX
+    ref, rst = oracle.apply_patch(b, idx[1:], val[1:], count=3)
+    assert np.array_equal(u16(B), ref) and int(host(st)[0]) == rst == 0
     # device count above max_count: only max_count entries are applied
     B = dev(b)
-    pulse.pulse_apply_patch(B, dev(idx), dev(val), dev(np.array([5], np.int64)), zeros(1, torch.int32), max_count=1)
+    pulse.pulse_apply_patch(B, dev(idx[1:]), dev(val[1:]), dev(np.array([4], np.int64)), zeros(1, torch.int32),
+                            max_count=1)
     torch.cuda.synchronize()
-    ref, _ = oracle.apply_patch(b, idx, val, count=1)
+    ref, _ = oracle.apply_patch(b, idx[1:], val[1:], count=1)
     assert np.array_equal(u16(B), ref)
+
+
+@pytest.mark.parametrize("density", [1.0, 0.5, 0.08, 0.004])
+def test_apply_every_line_offset(density):
+    """The view may start anywhere in a 64-byte line (any 2-byte offset): the
+    lines cut by either end of it, and lines whose entries straddle chunk and
+    wave boundaries, against the oracle.  The entries always include the first
+    and the last element."""
+    rng = np.random.default_rng(int(density * 1000) + 7)
+    backing = rng.integers(0, 1 << 16, 70_000, dtype=np.uint16)
+    Back = dev(backing)
+    for off in list(range(0, 33)) + [47, 63]:
+        n = 66_000 - 37 * off
+        pos = np.flatnonzero(rng.random(n) < density)
+        pos = np.union1d(pos, [0, n - 1]).astype(np.int32)
+        val = rng.integers(0, 1 << 16, pos.size, dtype=np.uint16)
+        B = Back.clone()
+        st = zeros(1, torch.int32)
+        pad = np.zeros(13, np.int32)   # capacity above the count
+        pulse.pulse_apply_patch(B[off:off + n], dev(np.concatenate([pos, pad])),
+                                dev(np.concatenate([val, pad.astype(np.uint16)])),
+                                dev(np.array([pos.size], np.int64)), st, max_count=pos.size + 13)
+        torch.cuda.synchronize()
+        ref = backing.copy()
+        ref[off:off + n], rst = oracle.apply_patch(backing[off:off + n], pos, val)
+        got = u16(B)
+        assert np.array_equal(got, ref), (off, np.flatnonzero(got != ref)[:8])
+        assert int(host(st)[0]) == rst == 0
+
+
+def test_apply_many_waves_large_patch():
+    """A patch long enough for every wave of the launch to take several chunks
+    (entries 2^22 over 2^23 + 11 elements), and a sparse one whose chunks own
+    more lines than one LDS pass holds."""
+    rng = np.random.default_rng(12)
+    n = (1 << 23) + 11
+    b = rng.integers(0, 1 << 16, n, dtype=np.uint16)
+    for density in (0.5, 0.0015):
+        pos = np.flatnonzero(rng.random(n) < density).astype(np.int32)
+        val = rng.integers(0, 1 << 16, pos.size, dtype=np.uint16)
+        B, st = dev(b), zeros(1, torch.int32)
+        pulse.pulse_apply_patch(B, dev(pos), dev(val), dev(np.array([pos.size], np.int64)), st, max_count=pos.size)
+        torch.cuda.synchronize()
+        ref, rst = oracle.apply_patch(b, pos, val)
+        assert np.array_equal(u16(B), ref) and int(host(st)[0]) == rst == 0
 
 
 def test_patch_chain_20_steps_no_drift():

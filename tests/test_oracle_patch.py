@@ -82,8 +82,8 @@ def test_apply_rebuilds_new_version():
 
 def test_apply_skips_bad_indices():
     b = np.arange(10, dtype=np.uint16)
-    got, st = oracle.apply_patch(b, np.array([1, 10, -1, 3], np.int32),
-                                 np.array([100, 200, 300, 400], np.uint16))
+    got, st = oracle.apply_patch(b, np.array([-1, 1, 3, 10], np.int32),
+                                 np.array([300, 100, 400, 200], np.uint16))
     assert st == oracle.BADINDEX
     assert list(got) == [0, 100, 2, 400, 4, 5, 6, 7, 8, 9]
 
