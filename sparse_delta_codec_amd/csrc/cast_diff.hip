@@ -38,10 +38,11 @@ __device__ __forceinline__ void load_new4(const CastDiffArgs &a, int64_t e, uint
     if (e + 3 < a.n) {
         if constexpr (FROM_F32) {
             const float4 f = *reinterpret_cast<const float4 *>(a.w_new + e);
-            out[0] = bf16_rne(__float_as_uint(f.x));
-            out[1] = bf16_rne(__float_as_uint(f.y));
-            out[2] = bf16_rne(__float_as_uint(f.z));
-            out[3] = bf16_rne(__float_as_uint(f.w));
+            const uint32_t p0 = cast_pair(f.x, f.y), p1 = cast_pair(f.z, f.w);
+            out[0] = (uint16_t)p0;
+            out[1] = (uint16_t)(p0 >> 16);
+            out[2] = (uint16_t)p1;
+            out[3] = (uint16_t)(p1 >> 16);
         } else {
             const ushort4 h = *reinterpret_cast<const ushort4 *>(a.b_in + e);
             out[0] = h.x; out[1] = h.y; out[2] = h.z; out[3] = h.w;

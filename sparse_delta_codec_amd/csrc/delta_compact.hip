@@ -71,7 +71,8 @@ __device__ __forceinline__ bool dc_gate(uint32_t th, uint32_t de, uint32_t re, u
     const float a = __uint_as_float(re) + __uint_as_float(de);
     const float moved = __uint_as_float(th) + a;
     a_bits = __float_as_uint(a);
-    return bf16_rne(__float_as_uint(moved)) != bf16_rne(th);
+    const uint32_t pr = cast_pair(moved, __uint_as_float(th));  // both views in one conversion
+    return (pr & 0xFFFFu) != (pr >> 16);
 }
 
 __device__ __forceinline__ uint32_t lanes_below_dc(uint64_t m) {
