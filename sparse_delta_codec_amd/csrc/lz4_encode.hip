@@ -210,77 +210,88 @@ constexpr int LZF_STAGE = (LZE_WIN + 48) / 4 / LZE_NW;
 // Step 1 of the fused pass for one wave: wave wv owns the block's elements
 // [wv * NG * 256, +NG * 256) as NG groups of 256, lane l holding elements
 // 256 g + 4 l + k (a 16-byte load of masters and an 8-byte load of the old
-// view per group, 1 KiB / 512 B contiguous per wave).  Cast, compare, store
-// the new view, put old ^ new into the image; with PATCH, rank each changed
-// element among the wave's (ballots, index order) and stage it.  Returns the
-// wave's number of changed elements.
-template <int CHLOG, bool PATCH>
-__device__ __forceinline__ uint32_t fused_pass1(const FusedArgs &f, int64_t blk_e0, uint8_t *s_img, uint32_t *stg) {
-    constexpr int BLK_E = (1 << CHLOG) * LZE_THREADS / 2;
-    constexpr int NG = BLK_E / (LZE_NW * 256);
-    constexpr int GI = NG < 4 ? NG : 4;  // groups in flight
-    const int wv = threadIdx.x / kWave, ln = threadIdx.x % kWave;
+// view per group, 1 KiB / 512 B contiguous per wave).  fused_load issues the
+// loads; fused_consume casts, compares, stores the new view, puts old ^ new
+// into the image and, with PATCH, ranks each changed element among the
+// wave's (ballots, index order) and stages it.  Between the two the loads
+// stay in flight while the workgroup finishes its previous block.
+template <int CHLOG>
+struct FusedGeom {
+    static constexpr int BLK_E = (1 << CHLOG) * LZE_THREADS / 2;  // elements per block
+    static constexpr int NG = BLK_E / (LZE_NW * 256);              // groups per wave
+};
+
+template <int CHLOG, int G0, int GN>
+__device__ __forceinline__ void fused_load(const FusedArgs &f, int64_t blk_e0, u32x4 *fv, u32x2 *ov, int tid) {
+    constexpr int BLK_E = FusedGeom<CHLOG>::BLK_E, NG = FusedGeom<CHLOG>::NG;
+    const int wv = tid / kWave, ln = tid % kWave;
+    const int32_t w0 = wv * NG * 256 + 4 * ln;
+    if (blk_e0 + BLK_E <= f.n) {
+#pragma unroll
+        for (int j = 0; j < GN; ++j) {
+            const int64_t e = blk_e0 + w0 + (G0 + j) * 256;
+            fv[j] = *reinterpret_cast<const u32x4 *>(f.w_new + e);
+            ov[j] = *reinterpret_cast<const u32x2 *>(f.b_old + e);
+        }
+    } else {  // the call's last block: elements past n read as zero
+#pragma unroll
+        for (int j = 0; j < GN; ++j) {
+            const int64_t e = blk_e0 + w0 + (G0 + j) * 256;
+            uint32_t fw[4], ow[2] = {0u, 0u};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const bool in = e + k < f.n;
+                fw[k] = in ? __float_as_uint(f.w_new[e + k]) : 0u;
+                ow[k >> 1] |= (in ? (uint32_t)f.b_old[e + k] : 0u) << (16 * (k & 1));
+            }
+            fv[j] = u32x4{fw[0], fw[1], fw[2], fw[3]};
+            ov[j] = u32x2{ow[0], ow[1]};
+        }
+    }
+}
+
+template <int CHLOG, bool PATCH, int G0, int GN>
+__device__ __forceinline__ uint32_t fused_consume(const FusedArgs &f, int64_t blk_e0, const u32x4 *fv,
+                                                  const u32x2 *ov, uint8_t *s_img, uint32_t *stg, int tid,
+                                                  uint32_t nb) {
+    constexpr int BLK_E = FusedGeom<CHLOG>::BLK_E, NG = FusedGeom<CHLOG>::NG;
+    const int wv = tid / kWave, ln = tid % kWave;
     const int32_t w0 = wv * NG * 256 + 4 * ln;
     const bool full = blk_e0 + BLK_E <= f.n;
-    uint32_t nb = 0;
 #pragma unroll
-    for (int h = 0; h < NG; h += GI) {
-        u32x4 fv[GI];
-        u32x2 ov[GI];
-#pragma unroll
-        for (int j = 0; j < GI; ++j) {
-            const int64_t e = blk_e0 + w0 + (h + j) * 256;
+    for (int j = 0; j < GN; ++j) {
+        const int32_t eo = w0 + (G0 + j) * 256;
+        const int64_t e = blk_e0 + eo;
+        const uint32_t p0 = cast_pair(__uint_as_float(fv[j].x), __uint_as_float(fv[j].y));
+        const uint32_t p1 = cast_pair(__uint_as_float(fv[j].z), __uint_as_float(fv[j].w));
+        const uint32_t x0 = p0 ^ ov[j].x, x1 = p1 ^ ov[j].y;  // zero past n
+        if (f.b_new) {
             if (full) {
-                fv[j] = *reinterpret_cast<const u32x4 *>(f.w_new + e);
-                ov[j] = *reinterpret_cast<const u32x2 *>(f.b_old + e);
-            } else {  // the call's last block: elements past n read as zero
-                uint32_t fw[4], ow[2] = {0u, 0u};
+                *reinterpret_cast<u32x2 *>(f.b_new + e) = u32x2{p0, p1};
+            } else {
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const bool in = e + k < f.n;
-                    fw[k] = in ? __float_as_uint(f.w_new[e + k]) : 0u;
-                    ow[k >> 1] |= (in ? (uint32_t)f.b_old[e + k] : 0u) << (16 * (k & 1));
-                }
-                fv[j] = u32x4{fw[0], fw[1], fw[2], fw[3]};
-                ov[j] = u32x2{ow[0], ow[1]};
+                for (int k = 0; k < 4; ++k)
+                    if (e + k < f.n) f.b_new[e + k] = (uint16_t)((k < 2 ? p0 : p1) >> (16 * (k & 1)));
             }
         }
+        *reinterpret_cast<u32x2 *>(s_img + img_addr<CHLOG>(2 * eo)) = u32x2{x0, x1};
+        if constexpr (PATCH) {
+            const uint32_t fl = (uint32_t)pair_flags(x0, x1);
+            const uint64_t m0 = __ballot(fl & 1u), m1 = __ballot(fl & 2u), m2 = __ballot(fl & 4u),
+                           m3 = __ballot(fl & 8u);
+            const uint32_t gtot = __builtin_popcountll(m0) + __builtin_popcountll(m1) +
+                                  __builtin_popcountll(m2) + __builtin_popcountll(m3);
+            uint32_t r = nb + lanes_below(m0) + lanes_below(m1) + lanes_below(m2) + lanes_below(m3);
 #pragma unroll
-        for (int j = 0; j < GI; ++j) {
-            const int32_t eo = w0 + (h + j) * 256;
-            const int64_t e = blk_e0 + eo;
-            const uint32_t p0 = cast_pair(__uint_as_float(fv[j].x), __uint_as_float(fv[j].y));
-            const uint32_t p1 = cast_pair(__uint_as_float(fv[j].z), __uint_as_float(fv[j].w));
-            const uint32_t x0 = p0 ^ ov[j].x, x1 = p1 ^ ov[j].y;  // zero past n
-            if (f.b_new) {
-                if (full) {
-                    *reinterpret_cast<u32x2 *>(f.b_new + e) = u32x2{p0, p1};
-                } else {
-#pragma unroll
-                    for (int k = 0; k < 4; ++k)
-                        if (e + k < f.n) f.b_new[e + k] = (uint16_t)((k < 2 ? p0 : p1) >> (16 * (k & 1)));
+            for (int k = 0; k < 4; ++k) {
+                if (fl & (1u << k)) {
+                    if (r < (uint32_t)LZF_STAGE)
+                        stg[r] = (uint32_t)(eo + k) | (((k < 2 ? p0 : p1) >> (16 * (k & 1))) << 16);
+                    ++r;
                 }
             }
-            *reinterpret_cast<u32x2 *>(s_img + img_addr<CHLOG>(2 * eo)) = u32x2{x0, x1};
-            if constexpr (PATCH) {
-                const uint32_t fl = (uint32_t)pair_flags(x0, x1);
-                const uint64_t m0 = __ballot(fl & 1u), m1 = __ballot(fl & 2u), m2 = __ballot(fl & 4u),
-                               m3 = __ballot(fl & 8u);
-                const uint32_t gtot = __builtin_popcountll(m0) + __builtin_popcountll(m1) +
-                                      __builtin_popcountll(m2) + __builtin_popcountll(m3);
-                uint32_t r = nb + lanes_below(m0) + lanes_below(m1) + lanes_below(m2) + lanes_below(m3);
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    if (fl & (1u << k)) {
-                        if (r < (uint32_t)LZF_STAGE)
-                            stg[r] = (uint32_t)(eo + k) | (((k < 2 ? p0 : p1) >> (16 * (k & 1))) << 16);
-                        ++r;
-                    }
-                }
-                nb += gtot;
-            }
+            nb += gtot;
         }
-        sched_fence();  // GI groups of loads in flight at a time
     }
     return nb;
 }
@@ -290,10 +301,10 @@ __device__ __forceinline__ uint32_t fused_pass1(const FusedArgs &f, int64_t blk_
 // may already be overwritten by the new one).
 template <int CHLOG>
 __device__ __forceinline__ void fused_patch_direct(const FusedArgs &f, int64_t blk_e0, const uint8_t *s_img,
-                                                   int64_t run) {
+                                                   int64_t run, int tid) {
     constexpr int BLK_E = (1 << CHLOG) * LZE_THREADS / 2;
     constexpr int NG = BLK_E / (LZE_NW * 256);
-    const int wv = threadIdx.x / kWave, ln = threadIdx.x % kWave;
+    const int wv = tid / kWave, ln = tid % kWave;
     const int32_t w0 = wv * NG * 256 + 4 * ln;
 #pragma unroll 1
     for (int g = 0; g < NG; ++g) {
@@ -319,27 +330,14 @@ __device__ __forceinline__ void fused_patch_direct(const FusedArgs &f, int64_t b
     }
 }
 
-// One block (b) of the encode, by the whole workgroup.  FUSED: the mask is
-// made from (f.w_new, f.b_old) by the fused pass; PATCH: with its patch.
-template <int CHLOG, bool FUSED = false, bool PATCH = false>
-__device__ __forceinline__ void enc_block(const Lz4EncArgs &a, const FusedArgs &f, uint32_t b, uint32_t tag,
-                                          EncShared &sh) {
-    constexpr int32_t CH = 1 << CHLOG;
-    uint8_t *const s_img = sh.img;
-    uint8_t *const s_win = sh.win;
+// Step 1 of the plain encoder: the block's bytes (or the XOR of two sources)
+// into the image, with coalesced 16-byte loads.
+template <int CHLOG>
+__device__ __forceinline__ void enc_load(const Lz4EncArgs &a, uint32_t b, uint8_t *s_img) {
     const int t = threadIdx.x;
-    const int wv = t / kWave, ln = t % kWave;
     const int64_t blk_base = (int64_t)b * a.block_bytes;
     const int32_t len = (int32_t)((a.nbytes - blk_base) < a.block_bytes ? (a.nbytes - blk_base) : a.block_bytes);
-
-    // 1. load (or make) the mask
-    uint32_t *const stg = reinterpret_cast<uint32_t *>(s_win) + wv * LZF_STAGE;
-    const int64_t blk_e0 = blk_base / 2;
-    if constexpr (FUSED) {
-        const uint32_t nb = fused_pass1<CHLOG, PATCH>(f, blk_e0, s_img, stg);
-        if (PATCH && ln == 0) sh.pw[wv] = nb;
-    }
-    const int32_t npieces = FUSED ? 0 : a.block_bytes / 16;
+    const int32_t npieces = a.block_bytes / 16;
     for (int32_t q = t; q < npieces; q += LZE_THREADS) {
         const int32_t off = q * 16;
         uint4 v = make_uint4(0, 0, 0, 0);
@@ -360,7 +358,22 @@ __device__ __forceinline__ void enc_block(const Lz4EncArgs &a, const FusedArgs &
         }
         *reinterpret_cast<uint4 *>(s_img + img_addr<CHLOG>(off)) = v;
     }
-    __syncthreads();
+}
+
+// Steps 2-5 of block b, by the whole workgroup, once the image is complete
+// (and, for the fused pass, the patch counts of the waves are in sh.pw and
+// their entries staged).  Ends with the block's output written.
+template <int CHLOG, bool PATCH = false>
+__device__ __forceinline__ void enc_rest(const Lz4EncArgs &a, const FusedArgs &f, uint32_t b, uint32_t tag,
+                                         EncShared &sh, int t) {
+    constexpr int32_t CH = 1 << CHLOG;
+    uint8_t *const s_img = sh.img;
+    uint8_t *const s_win = sh.win;
+    const int wv = t / kWave, ln = t % kWave;
+    const int64_t blk_base = (int64_t)b * a.block_bytes;
+    const int32_t len = (int32_t)((a.nbytes - blk_base) < a.block_bytes ? (a.nbytes - blk_base) : a.block_bytes);
+    [[maybe_unused]] uint32_t *const stg = reinterpret_cast<uint32_t *>(s_win) + wv * LZF_STAGE;
+    [[maybe_unused]] const int64_t blk_e0 = blk_base / 2;
     // the block's patch count goes out at once, so later blocks' look-backs
     // can sum it while this block is still being analysed
     if constexpr (PATCH) {
@@ -470,7 +483,7 @@ __device__ __forceinline__ void enc_block(const Lz4EncArgs &a, const FusedArgs &
                 }
             }
         } else {
-            fused_patch_direct<CHLOG>(f, blk_e0, s_img, run);
+            fused_patch_direct<CHLOG>(f, blk_e0, s_img, run, t);
         }
     }
 
@@ -643,14 +656,21 @@ __global__ __launch_bounds__(LZE_THREADS, 8) void k_lz4_encode(Lz4EncArgs a) {
         if (threadIdx.x == 0) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
         return;
     }
-    enc_block<CHLOG>(a, FusedArgs{}, b, tag, sh);
+    enc_load<CHLOG>(a, b, sh.img);
+    __syncthreads();
+    enc_rest<CHLOG>(a, FusedArgs{}, b, tag, sh, threadIdx.x);
 }
 
+// The fused pass: one 1024-thread workgroup per 64 KiB mask block (32768
+// elements), the block taken as a ticket when the workgroup starts; two
+// workgroups share a CU, so one's loads overlap the other's analysis.
 template <int CHLOG, bool PATCH>
 __global__ __launch_bounds__(LZE_THREADS, 8) void k_cast_diff_lz4(Lz4EncArgs a, FusedArgs f) {
+    constexpr int BLK_E = FusedGeom<CHLOG>::BLK_E, NG = FusedGeom<CHLOG>::NG;
     __shared__ __align__(16) EncShared sh;
     __shared__ uint32_t s_b, s_tag;
-    if (threadIdx.x == 0) {
+    const int t = threadIdx.x;
+    if (t == 0) {
         uint32_t b, tag;
         ws_begin(a.hdr, a.nblocks, &b, &tag);
         s_b = b;
@@ -659,10 +679,30 @@ __global__ __launch_bounds__(LZE_THREADS, 8) void k_cast_diff_lz4(Lz4EncArgs a, 
     __syncthreads();
     const uint32_t b = s_b, tag = s_tag;
     if (b >= a.nblocks) {  // inconsistent workspace state: touch nothing
-        if (threadIdx.x == 0) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
+        if (t == 0) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
         return;
     }
-    enc_block<CHLOG, true, PATCH>(a, f, b, tag, sh);
+    // step 1 in rounds of (up to) four groups: loads in flight, then consumed
+    constexpr int GI = NG < 4 ? NG : 4;
+    uint32_t *const stg = reinterpret_cast<uint32_t *>(sh.win) + (t / kWave) * LZF_STAGE;
+    uint32_t nw = 0;
+    {
+        u32x4 fv[GI];
+        u32x2 ov[GI];
+        fused_load<CHLOG, 0, GI>(f, (int64_t)b * BLK_E, fv, ov, t);
+        nw = fused_consume<CHLOG, PATCH, 0, GI>(f, (int64_t)b * BLK_E, fv, ov, sh.img, stg, t, nw);
+    }
+    if constexpr (NG > GI) {
+        sched_fence();
+        u32x4 fv[NG - GI];
+        u32x2 ov[NG - GI];
+        fused_load<CHLOG, GI, NG - GI>(f, (int64_t)b * BLK_E, fv, ov, t);
+        nw = fused_consume<CHLOG, PATCH, GI, NG - GI>(f, (int64_t)b * BLK_E, fv, ov, sh.img, stg, t, nw);
+    }
+    sched_fence();  // keeps the later steps' code out of step 1
+    if (PATCH && (t % kWave) == 0) sh.pw[t / kWave] = nw;
+    __syncthreads();
+    enc_rest<CHLOG, PATCH>(a, f, b, tag, sh, t);
 }
 
 }  // namespace pulse
