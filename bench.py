@@ -58,7 +58,7 @@ def parse():
     p.add_argument("--serial-decode", action="store_true",
                    help="decode each chunk with one lz4_decode_blocks call on the main stream (no overlap)")
     p.add_argument("--cpu-sample-frac", type=float, default=1.0,
-                   help="fraction of the oracle's sample (the attention half of layer 0) it times")
+                   help="fraction of the oracle's sample (decoder layer 0) it times")
     p.add_argument("--next", default="loco,patch,list", help="next-row legs measured after the timed steps, comma "
                    "separated: loco (PULSELoCo gate), patch (patch-stream compression), list (one launch over the "
                    "tensor list), fp8 (FP8-view deltas), none")
@@ -766,17 +766,16 @@ def loco_leg(pulse, dev, with_oracle):
 
 def cpu_baseline(specs, offs, W, b_old, frac):
     """The oracle (plain single-threaded C) on a bounded sample of the same
-    workload: the attention half of layer 0 (in_ln, q, k, v and their biases,
-    o, post_ln; about 63 M parameters), all five steps over host copies of the
-    same inputs, FP8 on the stacked [q;k;v] and on o.  `frac` < 1 shortens the
-    sample further (the FP8 step is then skipped)."""
+    workload: decoder layer 0 (its 12 tensors, about 488 M parameters, some
+    10-15 s of CPU work), all five steps over host copies of the same inputs,
+    FP8 on the layer's stacked groups.  `frac` < 1 shortens the sample (the
+    FP8 step is then skipped)."""
     import numpy as np
 
     import oracle
 
     lay = [i for i, s in enumerate(specs) if s.name.startswith("l0.")]
-    last = next(i for i in lay if specs[i].name == "l0.post_ln")
-    lay = [i for i in lay if i <= last]
+    last = lay[-1]
     s0, e0 = offs[lay[0]], offs[last] + specs[last].numel
     m = int((e0 - s0) * min(frac, 1.0)) // 8 * 8
     w = W[s0:s0 + m].cpu().numpy()
@@ -798,7 +797,7 @@ def cpu_baseline(specs, offs, W, b_old, frac):
     secs = time.perf_counter() - t
     log(f"oracle LZ4 done ({secs:.1f} s)")
     return {"value": round(2 * m / secs / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"attention half of layer 0 of the same workload ({m} params"
+            "sample": f"decoder layer 0 of the same workload ({m} params"
                       f"{'' if frac >= 1 else ', FP8 step skipped'}), all five steps, {secs:.1f} s"}
 
 

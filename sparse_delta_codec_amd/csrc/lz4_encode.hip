@@ -369,7 +369,9 @@ __device__ __forceinline__ void enc_rest(const Lz4EncArgs &a, const FusedArgs &f
     constexpr int32_t CH = 1 << CHLOG;
     uint8_t *const s_img = sh.img;
     uint8_t *const s_win = sh.win;
-    const int wv = t / kWave, ln = t % kWave;
+    // the wave index is the same in every lane: held in a scalar register, the
+    // per-wave comparisons of the block scans stay scalar
+    const int wv = __builtin_amdgcn_readfirstlane(t / kWave), ln = t % kWave;
     const int64_t blk_base = (int64_t)b * a.block_bytes;
     const int32_t len = (int32_t)((a.nbytes - blk_base) < a.block_bytes ? (a.nbytes - blk_base) : a.block_bytes);
     [[maybe_unused]] uint32_t *const stg = reinterpret_cast<uint32_t *>(s_win) + wv * LZF_STAGE;
@@ -381,9 +383,8 @@ __device__ __forceinline__ void enc_rest(const Lz4EncArgs &a, const FusedArgs &f
         // publishes its count right after its pass 1, so the look-back only
         // waits for blocks that are still loading
         if (wv == 1) {
-            uint32_t p_count = 0;
-#pragma unroll
-            for (int w = 0; w < LZE_NW; ++w) p_count += sh.pw[w];
+            const uint32_t x = ln < LZE_NW ? sh.pw[ln] : 0u;
+            const uint32_t p_count = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_sum(x), LZE_NW - 1);
             bool failed = false;
             const uint64_t pre = lookback_wave(f.pstatus, b, tag, (uint64_t)p_count, &failed);
             if (ln == 0) {
@@ -462,14 +463,13 @@ __device__ __forceinline__ void enc_rest(const Lz4EncArgs &a, const FusedArgs &f
     // staged entries go out with coalesced stores (the window is next written
     // by the emission, two barriers later)
     if constexpr (PATCH) {
-        uint32_t p_wpre = 0, p_wmax = 0, p_mine = 0;
-#pragma unroll
-        for (int w = 0; w < LZE_NW; ++w) {
-            const uint32_t x = sh.pw[w];
-            if (w < wv) p_wpre += x;
-            if (w == wv) p_mine = x;
-            p_wmax = x > p_wmax ? x : p_wmax;
-        }
+        // the waves' counts in lanes 0..15: prefix, own count and maximum by
+        // DPP scans, read back as scalars
+        const uint32_t x = ln < LZE_NW ? sh.pw[ln] : 0u;
+        const uint32_t incl = wave_incl_sum(x), mx = wave_incl_max(x);
+        const uint32_t p_mine = (uint32_t)__builtin_amdgcn_readlane((int)x, wv);
+        const uint32_t p_wpre = (uint32_t)__builtin_amdgcn_readlane((int)incl, wv) - p_mine;
+        const uint32_t p_wmax = (uint32_t)__builtin_amdgcn_readlane((int)mx, LZE_NW - 1);
         const uint32_t po_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(sh.poff >> 32));
         const uint32_t po_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)sh.poff);
         const int64_t run = (int64_t)(((uint64_t)po_hi << 32) | po_lo) + p_wpre;
