@@ -297,23 +297,36 @@ __device__ __forceinline__ void lookback_publish(uint64_t *status, uint32_t tile
     if (lane_id() == 0) st_agent(&status[tile], make_status(tag, tile == 0, aggregate));
 }
 
+// The first window of a look-back, read ahead of time: lane l reads the status
+// word of tile - 1 - l.  A wave that issues it early and resolves later (with
+// `first`) has the round trip overlap its other work.
+__device__ __forceinline__ uint64_t lookback_prefetch(const uint64_t *status, uint32_t tile) {
+    const int64_t p = (int64_t)tile - 1 - lane_id();
+    return p >= 0 ? ld_agent(&status[p]) : 0ull;
+}
+
 // ... then, by the same full wave, wait for the predecessors, publish the
-// inclusive prefix and return the exclusive one.
+// inclusive prefix and return the exclusive one.  `first`, when given, is the
+// wave's lookback_prefetch of this tile, used as the first poll.
 template <bool MAX = false>
 __device__ __forceinline__ uint64_t lookback_resolve(uint64_t *status, uint32_t tile, uint32_t tag,
-                                                     uint64_t aggregate, bool *failed) {
+                                                     uint64_t aggregate, bool *failed,
+                                                     const uint64_t *first = nullptr) {
     const int lane = lane_id();
     uint32_t spins = 0;
     if (tile == 0) return 0;
 
     uint64_t prefix = 0;
     int64_t j = (int64_t)tile - 1;  // newest predecessor the window starts at
+    bool use_first = first != nullptr;
     while (true) {
         const int64_t p = j - lane;
         uint64_t w = 0;
         bool valid, incl;
         while (true) {
-            if (p >= 0) w = ld_agent(&status[p]);
+            if (use_first) w = *first;
+            else if (p >= 0) w = ld_agent(&status[p]);
+            use_first = false;
             valid = p < 0 || (uint32_t)(w >> 40) == tag;
             incl = p >= 0 && valid && (w & kInclusive);
             const uint64_t vmask = __ballot(valid);

@@ -378,22 +378,13 @@ __device__ __forceinline__ void enc_rest(const Lz4EncArgs &a, const FusedArgs &f
     [[maybe_unused]] const int64_t blk_e0 = blk_base / 2;
     // the block's patch count goes out at once, so later blocks' look-backs
     // can sum it while this block is still being analysed
+    // and wave 1 places it among the others later (step 3), when the
+    // predecessors' counts are long published
+    uint32_t p_count = 0;
     if constexpr (PATCH) {
-        // wave 1 places the block's patch among the others: every block
-        // publishes its count right after its pass 1, so the look-back only
-        // waits for blocks that are still loading
-        if (wv == 1) {
-            const uint32_t x = ln < LZE_NW ? sh.pw[ln] : 0u;
-            const uint32_t p_count = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_sum(x), LZE_NW - 1);
-            bool failed = false;
-            const uint64_t pre = lookback_wave(f.pstatus, b, tag, (uint64_t)p_count, &failed);
-            if (ln == 0) {
-                if (failed) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
-                sh.poff = pre;
-                if (b == a.nblocks - 1) *f.d_count = (int64_t)(pre + p_count);
-                if ((int64_t)(pre + p_count) > f.cap) or_agent32(a.d_status, 1u /*PULSE_DS_CAPACITY*/);
-            }
-        }
+        const uint32_t x = ln < LZE_NW ? sh.pw[ln] : 0u;
+        p_count = (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_sum(x), LZE_NW - 1);
+        if (wv == 1) lookback_publish(f.pstatus, b, tag, (uint64_t)p_count);
     }
 
     // 2. run-boundary bitmask of this thread's chunk
@@ -459,33 +450,10 @@ __device__ __forceinline__ void enc_rest(const Lz4EncArgs &a, const FusedArgs &f
         next_after = exc < above ? exc : above;
     }
 
-    // the fused pass's patch, placed by wave 1 before the barrier above: the
-    // staged entries go out with coalesced stores (the window is next written
-    // by the emission, two barriers later)
-    if constexpr (PATCH) {
-        // the waves' counts in lanes 0..15: prefix, own count and maximum by
-        // DPP scans, read back as scalars
-        const uint32_t x = ln < LZE_NW ? sh.pw[ln] : 0u;
-        const uint32_t incl = wave_incl_sum(x), mx = wave_incl_max(x);
-        const uint32_t p_mine = (uint32_t)__builtin_amdgcn_readlane((int)x, wv);
-        const uint32_t p_wpre = (uint32_t)__builtin_amdgcn_readlane((int)incl, wv) - p_mine;
-        const uint32_t p_wmax = (uint32_t)__builtin_amdgcn_readlane((int)mx, LZE_NW - 1);
-        const uint32_t po_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(sh.poff >> 32));
-        const uint32_t po_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)sh.poff);
-        const int64_t run = (int64_t)(((uint64_t)po_hi << 32) | po_lo) + p_wpre;
-        if (p_wmax <= (uint32_t)LZF_STAGE) {
-            for (uint32_t i = ln; i < p_mine; i += kWave) {
-                const int64_t pos = run + i;
-                if (pos < f.cap) {
-                    const uint32_t v = stg[i];
-                    f.idx[pos] = (int32_t)(blk_e0 + (v & 0xFFFFu));
-                    f.val[pos] = (uint16_t)(v >> 16);
-                }
-            }
-        } else {
-            fused_patch_direct<CHLOG>(f, blk_e0, s_img, run, t);
-        }
-    }
+    // the first poll of the patch look-back goes out now; wave 1 reads it
+    // after its run analysis
+    uint64_t p_first = 0;
+    if (PATCH && wv == 1) p_first = lookback_prefetch(f.pstatus, b);
 
     // 3. the runs that become sequences (bit-parallel), then one pass over
     //    them: first one (i1, its match length), last j, and the bytes of the
@@ -521,6 +489,18 @@ __device__ __forceinline__ void enc_rest(const Lz4EncArgs &a, const FusedArgs &f
         const int32_t exc_i = dpp_mov<dppc::kWaveShl1, 0xf, 0xf>(LZE_INF, inc_i);
         if (ln == kWave - 1) sh.scan[1][wv] = inc_j;
         if (ln == 0) sh.scan[2][wv] = inc_i;
+        if constexpr (PATCH) {
+            if (wv == 1) {
+                bool failed = false;
+                const uint64_t pre = lookback_resolve(f.pstatus, b, tag, (uint64_t)p_count, &failed, &p_first);
+                if (ln == 0) {
+                    if (failed) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
+                    sh.poff = pre;
+                    if (b == a.nblocks - 1) *f.d_count = (int64_t)(pre + p_count);
+                    if ((int64_t)(pre + p_count) > f.cap) or_agent32(a.d_status, 1u /*PULSE_DS_CAPACITY*/);
+                }
+            }
+        }
         __syncthreads();
         int32_t below = 0, all = 0, above = LZE_INF;
 #pragma unroll
@@ -533,6 +513,33 @@ __device__ __forceinline__ void enc_rest(const Lz4EncArgs &a, const FusedArgs &f
         carry_j = exc_j > below ? exc_j : below;
         next_qi = exc_i < above ? exc_i : above;
         a_final = __builtin_amdgcn_readfirstlane(all);  // uniform: keep it in a scalar register
+    }
+    // the fused pass's patch, placed by wave 1 before the barrier above: the
+    // staged entries go out with coalesced stores (the window is next written
+    // by the emission, after the next barrier)
+    if constexpr (PATCH) {
+        // the waves' counts in lanes 0..15: prefix, own count and maximum by
+        // DPP scans, read back as scalars
+        const uint32_t x = ln < LZE_NW ? sh.pw[ln] : 0u;
+        const uint32_t incl = wave_incl_sum(x), mx = wave_incl_max(x);
+        const uint32_t p_mine = (uint32_t)__builtin_amdgcn_readlane((int)x, wv);
+        const uint32_t p_wpre = (uint32_t)__builtin_amdgcn_readlane((int)incl, wv) - p_mine;
+        const uint32_t p_wmax = (uint32_t)__builtin_amdgcn_readlane((int)mx, LZE_NW - 1);
+        const uint32_t po_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(sh.poff >> 32));
+        const uint32_t po_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)sh.poff);
+        const int64_t run = (int64_t)(((uint64_t)po_hi << 32) | po_lo) + p_wpre;
+        if (p_wmax <= (uint32_t)LZF_STAGE) {
+            for (uint32_t i = ln; i < p_mine; i += kWave) {
+                const int64_t pos = run + i;
+                if (pos < f.cap) {
+                    const uint32_t v = stg[i];
+                    f.idx[pos] = (int32_t)(blk_e0 + (v & 0xFFFFu));
+                    f.val[pos] = (uint16_t)(v >> 16);
+                }
+            }
+        } else {
+            fused_patch_direct<CHLOG>(f, blk_e0, s_img, run, t);
+        }
     }
     const int32_t tot = first_qi == LZE_INF ? 0 : seq_bytes(first_qi - carry_j, first_ml) + rest;
     // byte offset of this thread's sequences (exclusive sum) and the block's
