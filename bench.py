@@ -14,8 +14,12 @@ tensors (embed | 16 x four decoder layers | final norm + lm_head):
   receiver  lz4_decode_parse  the serial token-chain parse of every block, on a
                               second stream, while the next two keep HBM busy
   receiver  pulse_apply_patch scatter the patch into the receiver's view (v0 -> v1)
-  receiver  fp8_block_quant   stacked [q;k;v], o, stacked [gate;up], down,
-                              embed, lm_head -> E4M3 + FP32 128x128 scales
+                              (--apply-tiled: pulse_apply_patch_tiled with the
+                              tile index the sender writes)
+  receiver  fp8_block_quant_groups  stacked [q;k;v], o, stacked [gate;up],
+                              down, embed, lm_head -> E4M3 + FP32 128x128
+                              scales, up to 8 groups per launch
+                              (--quant-per-group: one fp8_block_quant each)
   receiver  lz4_decode_apply  rebuild + XOR in place into the receiver's view
                               (--serial-decode: one lz4_decode_blocks call on
                               the main stream, no second stream)
@@ -55,6 +59,11 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--separate-encode", action="store_true",
                    help="sender as two calls (pulse_cast_diff, then lz4_encode_blocks) instead of the fused pass")
+    p.add_argument("--apply-tiled", action="store_true",
+                   help="patch apply with pulse_apply_patch_tiled and the tile index the sender writes (faster "
+                        "alone, slower beside the decode parse) instead of pulse_apply_patch")
+    p.add_argument("--quant-per-group", action="store_true",
+                   help="one fp8_block_quant launch per stacked group instead of grouped launches")
     p.add_argument("--serial-decode", action="store_true",
                    help="decode each chunk with one lz4_decode_blocks call on the main stream (no overlap)")
     p.add_argument("--cpu-sample-frac", type=float, default=1.0,
@@ -196,6 +205,7 @@ def main():
     ws_cd = pulse.workspace(pulse.PULSE_OP_CAST_DIFF, max_chunk, 0, dev)
     ws_en = pulse.workspace(pulse.PULSE_OP_LZ4_ENCODE, 2 * max_chunk, BLOCK, dev)
     ws_fz = pulse.workspace(pulse.PULSE_OP_CAST_DIFF_LZ4, max_chunk, BLOCK, dev)
+    tiles = torch.zeros(pulse.patch_tile_count(max_chunk), dtype=torch.int64, device=dev)  # the patch's tile index
     ws_de = pulse.workspace(pulse.PULSE_OP_LZ4_DECODE, nbmax, pcap, dev)
     qplans = []
     max_codes = max_scales = 0
@@ -208,9 +218,23 @@ def main():
             max_codes = max(max_codes, rows * cols)
             max_scales = max(max_scales, ((rows + 127) // 128) * ((cols + 127) // 128))
         qplans.append(plan)
-    codes = torch.empty(max_codes, dtype=torch.uint8, device=dev)
-    scales = torch.empty(max_scales, dtype=torch.float32, device=dev)
+    # every group of a chunk writes its own codes and scales (the grouped
+    # launch quantises them together)
+    max_chunk_codes = max(sum(r * c for _, r, c in plan) for plan in qplans)
+    max_chunk_scales = max(sum(((r + 127) // 128) * ((c + 127) // 128) for _, r, c in plan) for plan in qplans)
+    codes = torch.empty(max(max_codes, max_chunk_codes), dtype=torch.uint8, device=dev)
+    scales = torch.empty(max(max_scales, max_chunk_scales), dtype=torch.float32, device=dev)
     n_quant = sum(rows * cols for plan in qplans for (_, rows, cols) in plan)
+    gplans = []  # per chunk: lists of at most 8 (srcs, codes, scales) for fp8_block_quant_groups
+    for ci, plan in enumerate(qplans):
+        lst, co, so = [], 0, 0
+        for (g, rows, cols) in plan:
+            srcs = [b_recv[offs[i]: offs[i] + specs[i].numel].view(specs[i].shape) for i in g]
+            nsc = ((rows + 127) // 128) * ((cols + 127) // 128)
+            lst.append((srcs, codes[co: co + rows * cols], scales[so: so + nsc]))
+            co += rows * cols
+            so += nsc
+        gplans.append([lst[k: k + pulse.PULSE_QUANT_MAX_GROUPS] for k in range(0, len(lst), pulse.PULSE_QUANT_MAX_GROUPS)])
     torch.cuda.synchronize()
     t_setup = time.time() - t_setup
     log(f"setup done in {t_setup:.1f} s: {n} params in {len(chunks)} chunks")
@@ -239,22 +263,35 @@ def main():
                     fn()
 
             def quant():
-                for (g, rows, cols) in qplans[ci]:
-                    srcs = [b_recv[offs[i]: offs[i] + specs[i].numel].view(specs[i].shape) for i in g]
-                    pulse.fp8_block_quant(srcs, codes, scales)
+                if args.quant_per_group:
+                    for (g, rows, cols) in qplans[ci]:
+                        srcs = [b_recv[offs[i]: offs[i] + specs[i].numel].view(specs[i].shape) for i in g]
+                        pulse.fp8_block_quant(srcs, codes, scales)
+                else:
+                    for batch in gplans[ci]:
+                        pulse.fp8_block_quant_groups(batch)
 
             if fused:
                 rec("encode", lambda: pulse.pulse_cast_diff_lz4(W[s0:e0], b_old[s0:e0], stage[:m], idx, val,
                                                                 cnt[ci:ci + 1], payload, csizes, coffs,
-                                                                ctotal[ci:ci + 1], status, ws_fz))
+                                                                ctotal[ci:ci + 1], status, ws_fz,
+                                                                tile_first=tiles if args.apply_tiled else None))
             else:
                 rec("cast_diff", lambda: pulse.pulse_cast_diff(W[s0:e0], b_old[s0:e0], stage[:m], None, idx, val,
                                                                cnt[ci:ci + 1], status, ws_cd))
                 rec("lz4_encode", lambda: pulse.lz4_encode_blocks(b_old[s0:e0], payload, csizes, coffs,
                                                                   ctotal[ci:ci + 1], status, ws_en,
                                                                   src_xor=stage[:m]))
+            def apply():
+                if not args.apply_tiled:
+                    pulse.pulse_apply_patch(b_recv[s0:e0], idx, val, cnt[ci:ci + 1], status)
+                    return
+                if not fused:  # the receiver builds the tile index itself
+                    pulse.pulse_patch_tiles(idx, cnt[ci:ci + 1], tiles, m)
+                pulse.pulse_apply_patch_tiled(b_recv[s0:e0], idx, val, tiles, status)
+
             if args.serial_decode:
-                rec("apply_patch", lambda: pulse.pulse_apply_patch(b_recv[s0:e0], idx, val, cnt[ci:ci + 1], status))
+                rec("apply_patch", apply)
                 rec("fp8_quant", quant)
                 rec("lz4_decode", lambda: pulse.lz4_decode_blocks(payload, coffs, csizes, b_recv[s0:e0], status,
                                                                   ws_de, mode=1))
@@ -270,7 +307,7 @@ def main():
                 parsed.record(side_stream)
             # the receiver's patch apply (v0 -> v1) and FP8 quant of v1 run beside the parse;
             # the main stream takes no other kernel until the parse is done
-            rec("apply_patch", lambda: pulse.pulse_apply_patch(b_recv[s0:e0], idx, val, cnt[ci:ci + 1], status))
+            rec("apply_patch", apply)
             rec("fp8_quant", quant)  # reads the receiver's view before the XOR rewrites it
             main_stream.wait_event(parsed)
             rec("lz4_decode", lambda: pulse.lz4_decode_apply(payload, coffs, csizes, b_recv[s0:e0], status, ws_de,

@@ -168,6 +168,9 @@ int pulse_compact(const uint16_t *b_old, const uint16_t *b_new, int32_t *patch_i
  *              be b_old itself (the view is updated in place).
  *   patch_idx, patch_val, d_count  the patch as for pulse_cast_diff, or all
  *              three NULL (mask blocks only).
+ *   tile_first [ceil(n/16384) + 1] int64 (written) or NULL (NULL without a
+ *              patch): the patch's tile index, as pulse_patch_tiles writes it;
+ *              the pass knows every tile's place and writes it at no cost.
  *   block_bytes, payload .. d_total  as for lz4_encode_blocks, over the 2 n
  *              bytes of the mask.
  *   d_status   PULSE_DS_CAPACITY when the patch or the payload exceeds its
@@ -176,7 +179,8 @@ int pulse_compact(const uint16_t *b_old, const uint16_t *b_new, int32_t *patch_i
  * n >= 1, and n <= 2^31 - 1 when a patch is asked for. */
 int pulse_cast_diff_lz4(const float *w_new, const uint16_t *b_old, uint16_t *b_new,
                         int32_t *patch_idx, uint16_t *patch_val, int64_t patch_cap,
-                        int64_t *d_count, int64_t n, int32_t block_bytes, uint8_t *payload,
+                        int64_t *d_count, int64_t *tile_first, int64_t n, int32_t block_bytes,
+                        uint8_t *payload,
                         int64_t payload_cap, uint32_t *comp_sizes, uint64_t *comp_offsets,
                         uint64_t *d_total, uint32_t *d_status, void *ws, size_t ws_bytes,
                         hipStream_t stream);
@@ -195,6 +199,33 @@ int pulse_cast_diff_lz4(const float *w_new, const uint16_t *b_old, uint16_t *b_n
 int pulse_apply_patch(uint16_t *b, int64_t n, const int32_t *patch_idx,
                       const uint16_t *patch_val, const int64_t *d_count, int64_t max_count,
                       uint32_t *d_status, hipStream_t stream);
+
+/* ---- a4 with the patch's tile index ---------------------------------------
+ * The tile index of an ascending patch: tile_first[t] = the first entry whose
+ * index is >= 16384 t, for t = 0 .. ntiles (ntiles = ceil(n / 16384);
+ * tile_first[ntiles] = count).  A small companion of the patch (8 bytes per
+ * 32 KiB of view) with which the receiver finds each tile's entries at once.
+ *   patch_idx  [count] ascending positions (read); d_count as for apply,
+ *              count = min(*d_count, max_count).
+ *   tile_first [ntiles + 1] int64 (written). */
+int pulse_patch_tiles(const int32_t *patch_idx, const int64_t *d_count, int64_t max_count,
+                      int64_t n, int64_t *tile_first, hipStream_t stream);
+
+/* The same result as pulse_apply_patch, for a patch with its tile index
+ * (pulse_patch_tiles or pulse_cast_diff_lz4): every 16384-element tile of b is
+ * updated by one workgroup; a tile holding 1024 or more entries is read
+ * whole, patched on chip and written back whole (no partially written lines),
+ * a sparser one takes the entries' 2-byte stores.
+ *   b          [n] BF16 view, 16-byte aligned, updated in place.
+ *   tile_first the patch's tile index (read); entries are read only in
+ *              [0, max_count).
+ *   d_status   PULSE_DS_BADINDEX for an entry outside its tile (an index
+ *              outside [0, n), or a tile index that does not fit the patch):
+ *              such entries are skipped and no element outside a tile's own
+ *              range is written. */
+int pulse_apply_patch_tiled(uint16_t *b, int64_t n, const int32_t *patch_idx,
+                            const uint16_t *patch_val, const int64_t *tile_first, int64_t max_count,
+                            uint32_t *d_status, hipStream_t stream);
 
 /* ---- a2/a6: dense XOR apply ------------------------------------------------
  * dst ^= mask over nbytes bytes: the sampler XORs the same-size mask into its
@@ -298,6 +329,29 @@ int lz4_decode_apply(const uint8_t *payload, int64_t payload_bytes,
 int fp8_block_quant(const uint16_t *const *srcs, const int64_t *src_rows, int32_t nsrc,
                     int64_t cols, int64_t batch, const int64_t *src_batch_stride,
                     uint8_t *codes, float *scales, hipStream_t stream);
+
+/* Several stacked groups quantised in one launch: exactly the results of one
+ * fp8_block_quant call (batch 1) per group, with the blocks of all groups
+ * sharing the GPU, so that small groups (a layer's [q;k;v] or o projection)
+ * do not run as launches too small to fill it.
+ *   groups     (host) array of ngroups (1..PULSE_QUANT_MAX_GROUPS) descriptors,
+ *              read during the call only.
+ *   per group: src[0..nsrc) device BF16 sources [rows[i], cols], row-major,
+ *              16-byte aligned, nsrc in 1..4; cols a multiple of 8; codes
+ *              [R][cols] (8-byte aligned) and scales [ceil(R/128)][ceil(cols/128)]
+ *              written, R = sum of rows > 0.  Groups must not overlap in their
+ *              outputs. */
+#define PULSE_QUANT_MAX_GROUPS 8
+typedef struct {
+    const uint16_t *src[4];
+    int64_t rows[4];
+    int32_t nsrc;
+    int32_t reserved; /* 0 */
+    int64_t cols;
+    uint8_t *codes;
+    float *scales;
+} pulse_quant_group;
+int fp8_block_quant_groups(const pulse_quant_group *groups, int32_t ngroups, hipStream_t stream);
 
 /* ---- next: deltas of the FP8 served view ----------------------------------
  * When the sampler serves FP8, the view it must rebuild bit for bit is the

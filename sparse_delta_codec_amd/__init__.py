@@ -20,7 +20,8 @@ __all__ = [
     "PULSE_OP_FP8_DELTA", "PULSE_OP_LOCO_GATE", "fp8_view_delta", "fp8_view_apply",
     "pulse_loco_gate", "pulse_loco_accumulate",
     "PULSE_OP_PATCH_UNPACK", "patch_packed_bytes", "patch_pack", "patch_unpack",
-    "PULSE_OP_CAST_DIFF_SEGMENTS", "PULSE_DS_BADSEGMENT", "PULSE_OP_CAST_DIFF_LZ4", "pulse_cast_diff_lz4", "pulse_segment_tiles", "SegmentTable", "ViewTable",
+    "PULSE_OP_CAST_DIFF_SEGMENTS", "PULSE_DS_BADSEGMENT", "PULSE_OP_CAST_DIFF_LZ4", "pulse_cast_diff_lz4", "fp8_block_quant_groups", "PULSE_QUANT_MAX_GROUPS", "pulse_patch_tiles",
+    "pulse_apply_patch_tiled", "patch_tile_count", "pulse_segment_tiles", "SegmentTable", "ViewTable",
     "pulse_cast_diff_segments", "pulse_apply_patch_segments", "lz4_decode_parse", "lz4_decode_apply",
 ]
 
@@ -75,12 +76,17 @@ _lib.pulse_segment_tiles.argtypes = [_P, _I32, _P, _P]
 _lib.pulse_segment_tiles.restype = _I64
 _lib.pulse_cast_diff_segments.argtypes = [_P, _I32, _P, _I64, _P, _P, _I64, _P, _P, _P, _SZ, _I32, _P]
 _lib.pulse_apply_patch_segments.argtypes = [_P, _I32, _P, _P, _P, _I64, _P, _P]
-_lib.pulse_cast_diff_lz4.argtypes = [_P, _P, _P, _P, _P, _I64, _P, _I64, _I32, _P, _I64, _P, _P, _P, _P, _P, _SZ, _P]
+_lib.fp8_block_quant_groups.argtypes = [_P, _I32, _P]
+_lib.pulse_cast_diff_lz4.argtypes = [_P, _P, _P, _P, _P, _I64, _P, _P, _I64, _I32, _P, _I64, _P, _P, _P, _P, _P, _SZ,
+                                     _P]
+_lib.pulse_patch_tiles.argtypes = [_P, _P, _I64, _I64, _P, _P]
+_lib.pulse_apply_patch_tiled.argtypes = [_P, _I64, _P, _P, _P, _I64, _P, _P]
 for _f in ("pulse_cast_diff_segments", "pulse_apply_patch_segments", "patch_pack", "patch_unpack",
            "pulse_workspace_init", "pulse_cast_diff", "pulse_compact", "pulse_apply_patch",
            "xor_mask_apply", "lz4_encode_blocks", "lz4_decode_blocks", "fp8_block_quant",
            "fp8_view_delta", "fp8_view_apply", "pulse_loco_gate", "pulse_loco_accumulate",
-           "lz4_decode_parse", "lz4_decode_apply", "pulse_cast_diff_lz4"):
+           "lz4_decode_parse", "lz4_decode_apply", "pulse_cast_diff_lz4", "fp8_block_quant_groups",
+           "pulse_patch_tiles", "pulse_apply_patch_tiled"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -212,11 +218,43 @@ def lz4_encode_blocks(src, payload, comp_sizes, comp_offsets, d_total, d_status,
         _stream(stream)), "lz4_encode_blocks")
 
 
+PATCH_TILE = 16384
+
+
+def patch_tile_count(n: int) -> int:
+    """Entries of a patch's tile index over n elements (ceil(n / 16384) + 1)."""
+    return (n + PATCH_TILE - 1) // PATCH_TILE + 1
+
+
+def pulse_patch_tiles(patch_idx, d_count, tile_first, n, max_count=None, stream=None):
+    max_count = patch_idx.numel() if max_count is None else max_count
+    _need(patch_idx, 4 * max_count, "patch_idx")
+    _need(tile_first, 8 * patch_tile_count(n), "tile_first")
+    _check(_lib.pulse_patch_tiles(_dev(patch_idx, "patch_idx", torch.int32), _dev(d_count, "d_count", torch.int64),
+                                  max_count, n, _dev(tile_first, "tile_first", torch.int64), _stream(stream)),
+           "pulse_patch_tiles")
+
+
+def pulse_apply_patch_tiled(b, patch_idx, patch_val, tile_first, d_status, max_count=None, n=None, stream=None):
+    n = b.numel() if n is None else n
+    max_count = patch_idx.numel() if max_count is None else max_count
+    _need(b, 2 * n, "b")
+    _need(patch_idx, 4 * max_count, "patch_idx")
+    _need(patch_val, 2 * max_count, "patch_val")
+    _need(tile_first, 8 * patch_tile_count(n), "tile_first")
+    _check(_lib.pulse_apply_patch_tiled(
+        _dev(b, "b", _U16), n, _dev(patch_idx, "patch_idx", torch.int32), _dev(patch_val, "patch_val", _U16),
+        _dev(tile_first, "tile_first", torch.int64), max_count, _dev(d_status, "d_status", torch.int32),
+        _stream(stream)), "pulse_apply_patch_tiled")
+
+
 def pulse_cast_diff_lz4(w_new, b_old, b_new, patch_idx, patch_val, d_count, payload, comp_sizes, comp_offsets,
-                        d_total, d_status, ws, block_bytes=65536, n=None, stream=None):
+                        d_total, d_status, ws, block_bytes=65536, n=None, tile_first=None, stream=None):
     """cast + diff + patch + LZ4 blocks of the XOR mask in one pass (patch_idx,
-    patch_val and d_count all None: mask blocks only)."""
+    patch_val and d_count all None: mask blocks only); tile_first, when given,
+    receives the patch's tile index."""
     n = w_new.numel() if n is None else n
+    _need(tile_first, 8 * patch_tile_count(n), "tile_first")
     nb = (2 * n + block_bytes - 1) // block_bytes
     cap = 0 if patch_idx is None else patch_idx.numel()
     _need(w_new, 4 * n, "w_new")
@@ -229,7 +267,8 @@ def pulse_cast_diff_lz4(w_new, b_old, b_new, patch_idx, patch_val, d_count, payl
     _check(_lib.pulse_cast_diff_lz4(
         _dev(w_new, "w_new", torch.float32), _dev(b_old, "b_old", _U16), _dev(b_new, "b_new", _U16),
         _dev(patch_idx, "patch_idx", torch.int32), _dev(patch_val, "patch_val", _U16), cap,
-        _dev(d_count, "d_count", torch.int64), n, block_bytes, _dev(payload, "payload", torch.uint8), payload.numel(),
+        _dev(d_count, "d_count", torch.int64), _dev(tile_first, "tile_first", torch.int64), n, block_bytes,
+        _dev(payload, "payload", torch.uint8), payload.numel(),
         _dev(comp_sizes, "comp_sizes", torch.int32), _dev(comp_offsets, "comp_offsets", torch.int64),
         _dev(d_total, "d_total", torch.int64), _dev(d_status, "d_status", torch.int32), wsp, wsb,
         _stream(stream)), "pulse_cast_diff_lz4")
@@ -311,6 +350,43 @@ def fp8_block_quant(srcs, codes, scales, batch=1, stream=None):
         None if strides is None else ctypes.cast(strides, ctypes.c_void_p),
         _dev(codes, "codes", torch.uint8), _dev(scales, "scales", torch.float32), _stream(stream)),
         "fp8_block_quant")
+
+
+PULSE_QUANT_MAX_GROUPS = 8
+
+
+class _QuantGroup(ctypes.Structure):
+    """The layout of pulse_quant_group."""
+    _fields_ = [("src", ctypes.c_void_p * 4), ("rows", ctypes.c_int64 * 4), ("nsrc", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("cols", ctypes.c_int64), ("codes", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p)]
+
+
+def fp8_block_quant_groups(groups, stream=None):
+    """groups: list (1..8) of (srcs, codes, scales), srcs a list (1..4) of
+    contiguous BF16/uint16 GPU tensors [rows_i, cols]: one launch for all."""
+    if not 1 <= len(groups) <= PULSE_QUANT_MAX_GROUPS:
+        raise ValueError(f"{len(groups)} groups (1..{PULSE_QUANT_MAX_GROUPS} per call)")
+    arr = (_QuantGroup * len(groups))()
+    for g, (srcs, codes, scales) in enumerate(groups):
+        if not 1 <= len(srcs) <= 4:
+            raise ValueError(f"group {g}: {len(srcs)} sources (1..4)")
+        cols = srcs[0].shape[-1]
+        R = 0
+        for i, t in enumerate(srcs):
+            if t.dim() != 2 or t.shape[-1] != cols:
+                raise ValueError(f"group {g} source {i} has shape {tuple(t.shape)}")
+            arr[g].src[i] = _dev(t, f"groups[{g}].srcs[{i}]", _U16)
+            arr[g].rows[i] = int(t.shape[0])
+            R += int(t.shape[0])
+        _need(codes, R * cols, f"groups[{g}].codes")
+        _need(scales, 4 * ((R + 127) // 128) * ((cols + 127) // 128), f"groups[{g}].scales")
+        arr[g].nsrc = len(srcs)
+        arr[g].cols = cols
+        arr[g].codes = _dev(codes, f"groups[{g}].codes", torch.uint8)
+        arr[g].scales = _dev(scales, f"groups[{g}].scales", torch.float32)
+    _check(_lib.fp8_block_quant_groups(ctypes.cast(arr, ctypes.c_void_p), len(groups), _stream(stream)),
+           "fp8_block_quant_groups")
 
 
 def fp8_view_delta(codes_old, codes_new, scales_old, scales_new, code_idx, code_val, d_code_count,

@@ -48,6 +48,84 @@ __global__ __launch_bounds__(256) void k_apply_patch(uint16_t *__restrict__ b, i
     if (__ballot(bad) && lane_id() == 0) or_agent32(d_status, 2u /*PULSE_DS_BADINDEX*/);
 }
 
+// ---- apply with the patch's tile index -----------------------------------------
+// tile_first[t] is the first entry whose index is >= 16384 t (tile_first[ntiles]
+// the count).  One workgroup per tile: a tile with many entries is read whole
+// into LDS, its entries written there, and the tile written back with 16-byte
+// stores, so no line of the view is left partially written; a tile with few
+// entries (or the partial last tile) takes the entries' 2-byte stores.  Every
+// write stays inside the workgroup's own tile; an entry outside it is skipped
+// and reported (PULSE_DS_BADINDEX).
+constexpr int kAtTile = 16384;
+constexpr int64_t kAtDenseMin = 1024;  // entries per tile (6.25%) from which the tile is rewritten whole
+
+__global__ __launch_bounds__(256) void k_apply_patch_tiled(uint16_t *__restrict__ b, int64_t n,
+                                                           const int32_t *__restrict__ idx,
+                                                           const uint16_t *__restrict__ val,
+                                                           const int64_t *__restrict__ tile_first,
+                                                           int64_t max_count, uint32_t *d_status) {
+    __shared__ u32x4 img[kAtTile / 8];
+    const int t = threadIdx.x;
+    const int64_t tile = blockIdx.x;
+    const int64_t e0 = tile * kAtTile;
+    const int64_t len = n - e0 < kAtTile ? n - e0 : kAtTile;
+    int64_t k0 = tile_first[tile], k1 = tile_first[tile + 1];
+    k0 = k0 < 0 ? 0 : (k0 > max_count ? max_count : k0);
+    k1 = k1 < k0 ? k0 : (k1 > max_count ? max_count : k1);
+    bool bad = false;
+    if (k1 - k0 < kAtDenseMin || len < kAtTile) {
+        for (int64_t k = k0 + t; k < k1; k += 256) {
+            const int64_t i = idx[k];
+            if (i >= e0 && i < e0 + len) b[i] = val[k];
+            else bad = true;
+        }
+    } else {
+        u32x4 v[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const u32x4 *>(b + e0 + 8 * (t + 256 * i));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) img[t + 256 * i] = v[i];
+        __syncthreads();
+        uint16_t *img16 = reinterpret_cast<uint16_t *>(img);
+        for (int64_t k = k0 + t; k < k1; k += 256) {
+            const int64_t i = (int64_t)idx[k] - e0;
+            if (i >= 0 && i < kAtTile) img16[i] = val[k];
+            else bad = true;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4 *>(b + e0 + 8 * (t + 256 * i)) = img[t + 256 * i];
+    }
+    if (__ballot(bad) && lane_id() == 0) or_agent32(d_status, 2u /*PULSE_DS_BADINDEX*/);
+}
+
+// The tile index of an ascending patch: entry k writes tile_first[t] = k for
+// every tile t in (tile of entry k - 1, tile of entry k]; entry `count` (one
+// past the last) closes the index up to ntiles.  Four entries per thread.
+__global__ __launch_bounds__(256) void k_patch_tiles(const int32_t *__restrict__ idx, const int64_t *d_count,
+                                                     int64_t max_count, int64_t n, int64_t *__restrict__ tile_first) {
+    int64_t count = *d_count;
+    if (count > max_count) count = max_count;
+    if (count < 0) count = 0;
+    const int64_t ntiles = (n + kAtTile - 1) / kAtTile;
+    const int64_t k0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    if (k0 > count) return;
+    auto tile_of = [&](int64_t k) -> int64_t {  // tile of entry k (count: ntiles; out-of-range clamped)
+        if (k >= count) return ntiles;
+        const int64_t i = idx[k];
+        return i < 0 ? 0 : (i >= n ? ntiles - 1 : i / kAtTile);
+    };
+    int64_t prev = k0 > 0 ? tile_of(k0 - 1) : -1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int64_t k = k0 + j;
+        if (k > count) break;
+        const int64_t cur = tile_of(k);
+        for (int64_t tt = prev + 1; tt <= cur && tt <= ntiles; ++tt) tile_first[tt] = k;
+        prev = cur > prev ? cur : prev;
+    }
+}
+
 __global__ __launch_bounds__(256) void k_xor_apply(uint8_t *__restrict__ dst,
                                                    const uint8_t *__restrict__ mask,
                                                    int64_t nbytes) {
@@ -157,5 +235,22 @@ extern "C" int pulse_launch_xor_apply(void *dst, const void *mask, int64_t nbyte
     if (blocks < 1) blocks = 1;
     k_xor_apply<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(static_cast<uint8_t *>(dst),
                                                                  static_cast<const uint8_t *>(mask), nbytes);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+extern "C" int pulse_launch_apply_patch_tiled(uint16_t *b, int64_t n, const int32_t *idx, const uint16_t *val,
+                                              const int64_t *tile_first, int64_t max_count, uint32_t *d_status,
+                                              hipStream_t stream) {
+    const int64_t ntiles = (n + kAtTile - 1) / kAtTile;
+    k_apply_patch_tiled<<<dim3((unsigned)ntiles), dim3(256), 0, stream>>>(b, n, idx, val, tile_first, max_count,
+                                                                         d_status);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+extern "C" int pulse_launch_patch_tiles(const int32_t *idx, const int64_t *d_count, int64_t max_count, int64_t n,
+                                        int64_t *tile_first, hipStream_t stream) {
+    const int64_t threads = max_count / 4 + 1;
+    k_patch_tiles<<<dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream>>>(idx, d_count, max_count, n,
+                                                                                     tile_first);
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }

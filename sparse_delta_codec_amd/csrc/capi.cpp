@@ -48,10 +48,14 @@ int pulse_launch_cast_diff_segments(const void *, int32_t, const uint32_t *, int
 int pulse_launch_apply_patch_segments(const void *, int32_t, const int32_t *, const uint16_t *, const int64_t *,
                                       int64_t, uint32_t *, hipStream_t);
 int pulse_launch_fill_zero(void *, size_t, hipStream_t);
+int pulse_launch_fp8_block_quant_groups(const void *, int32_t, hipStream_t);
 size_t pulse_cast_diff_lz4_ws_bytes(int64_t n, int32_t block_bytes);
 int pulse_launch_cast_diff_lz4(const float *, const uint16_t *, uint16_t *, int32_t *, uint16_t *, int64_t,
                                int64_t *, int64_t, int32_t, uint8_t *, int64_t, uint32_t *, uint64_t *, uint64_t *,
-                               uint32_t *, void *, hipStream_t);
+                               uint32_t *, int64_t *, void *, hipStream_t);
+int pulse_launch_apply_patch_tiled(uint16_t *, int64_t, const int32_t *, const uint16_t *, const int64_t *, int64_t,
+                                   uint32_t *, hipStream_t);
+int pulse_launch_patch_tiles(const int32_t *, const int64_t *, int64_t, int64_t, int64_t *, hipStream_t);
 int pulse_launch_write_count(int64_t *, int64_t, hipStream_t);
 }
 
@@ -144,7 +148,8 @@ int pulse_compact(const uint16_t *b_old, const uint16_t *b_new, int32_t *patch_i
 }
 
 int pulse_cast_diff_lz4(const float *w_new, const uint16_t *b_old, uint16_t *b_new, int32_t *patch_idx,
-                        uint16_t *patch_val, int64_t patch_cap, int64_t *d_count, int64_t n, int32_t block_bytes,
+                        uint16_t *patch_val, int64_t patch_cap, int64_t *d_count, int64_t *tile_first,
+                        int64_t n, int32_t block_bytes,
                         uint8_t *payload, int64_t payload_cap, uint32_t *comp_sizes, uint64_t *comp_offsets,
                         uint64_t *d_total, uint32_t *d_status, void *ws, size_t ws_bytes, hipStream_t stream) {
     if (!w_new || !b_old || !payload || !comp_sizes || !comp_offsets || !d_total || !d_status || n <= 0 ||
@@ -152,6 +157,7 @@ int pulse_cast_diff_lz4(const float *w_new, const uint16_t *b_old, uint16_t *b_n
         return PULSE_EINVAL;
     const bool patch = patch_idx || patch_val || d_count;
     if (patch && !(patch_idx && patch_val && d_count)) return PULSE_EINVAL;
+    if (tile_first && !patch) return PULSE_EINVAL;
     if (block_bytes != 16384 && block_bytes != 32768 && block_bytes != 65536) return PULSE_EINVAL;
     if (!aligned16(w_new) || !aligned16(b_old) || (b_new && !aligned16(b_new))) return PULSE_EALIGN;
     if (patch && n > kMaxIndexed) return PULSE_ERANGE;
@@ -160,7 +166,22 @@ int pulse_cast_diff_lz4(const float *w_new, const uint16_t *b_old, uint16_t *b_n
     if (!ws || ws_bytes < pulse_cast_diff_lz4_ws_bytes(n, block_bytes)) return PULSE_EWORKSPACE;
     return pulse_launch_cast_diff_lz4(w_new, b_old, b_new, patch ? patch_idx : nullptr, patch_val, patch_cap,
                                       d_count, n, block_bytes, payload, payload_cap, comp_sizes, comp_offsets,
-                                      d_total, d_status, ws, stream);
+                                      d_total, d_status, tile_first, ws, stream);
+}
+
+int pulse_patch_tiles(const int32_t *patch_idx, const int64_t *d_count, int64_t max_count, int64_t n,
+                      int64_t *tile_first, hipStream_t stream) {
+    if (!patch_idx || !d_count || !tile_first || max_count < 0 || n < 1) return PULSE_EINVAL;
+    if (n > kMaxIndexed + 1) return PULSE_ERANGE;
+    return pulse_launch_patch_tiles(patch_idx, d_count, max_count, n, tile_first, stream);
+}
+
+int pulse_apply_patch_tiled(uint16_t *b, int64_t n, const int32_t *patch_idx, const uint16_t *patch_val,
+                            const int64_t *tile_first, int64_t max_count, uint32_t *d_status, hipStream_t stream) {
+    if (!b || !patch_idx || !patch_val || !tile_first || !d_status || n < 1 || max_count < 0) return PULSE_EINVAL;
+    if (!aligned16(b)) return PULSE_EALIGN;
+    if (n > kMaxIndexed + 1) return PULSE_ERANGE;
+    return pulse_launch_apply_patch_tiled(b, n, patch_idx, patch_val, tile_first, max_count, d_status, stream);
 }
 
 int pulse_apply_patch(uint16_t *b, int64_t n, const int32_t *patch_idx, const uint16_t *patch_val,
@@ -262,6 +283,27 @@ int fp8_block_quant(const uint16_t *const *srcs, const int64_t *src_rows, int32_
     if (reinterpret_cast<uintptr_t>(codes) % 8 != 0 || reinterpret_cast<uintptr_t>(scales) % 4 != 0)
         return PULSE_EALIGN;
     return pulse_launch_fp8_block_quant(srcs, src_rows, nsrc, cols, batch, src_batch_stride, codes, scales, stream);
+}
+
+int fp8_block_quant_groups(const pulse_quant_group *groups, int32_t ngroups, hipStream_t stream) {
+    if (!groups || ngroups < 1 || ngroups > PULSE_QUANT_MAX_GROUPS) return PULSE_EINVAL;
+    int64_t total = 0;
+    for (int g = 0; g < ngroups; ++g) {
+        const pulse_quant_group &q = groups[g];
+        if (q.nsrc < 1 || q.nsrc > 4 || q.cols <= 0 || q.cols % 8 != 0 || !q.codes || !q.scales) return PULSE_EINVAL;
+        int64_t R = 0;
+        for (int i = 0; i < q.nsrc; ++i) {
+            if (!q.src[i] || q.rows[i] < 0) return PULSE_EINVAL;
+            if (!aligned16(q.src[i])) return PULSE_EALIGN;
+            R += q.rows[i];
+        }
+        if (R == 0) return PULSE_EINVAL;
+        if (reinterpret_cast<uintptr_t>(q.codes) % 8 != 0 || reinterpret_cast<uintptr_t>(q.scales) % 4 != 0)
+            return PULSE_EALIGN;
+        total += ((R + 127) / 128) * ((q.cols + 127) / 128);
+        if (total > 0x7FFFFFFFll) return PULSE_ERANGE;
+    }
+    return pulse_launch_fp8_block_quant_groups(groups, ngroups, stream);
 }
 
 int fp8_view_delta(const uint8_t *codes_old, const uint8_t *codes_new, int64_t n_codes, const float *scales_old,

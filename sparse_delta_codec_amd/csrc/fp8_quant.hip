@@ -32,10 +32,22 @@ struct QuantArgs {
     float *scales;
 };
 
-__global__ __launch_bounds__(256) void k_fp8_block_quant(QuantArgs a) {
-    __shared__ uint32_t s_red[4];
+// One 128x128 block (row block br, column block bc, matrix e) of a stacked
+// matrix whose source s holds rows [row0[s], row0[s + 1]); by the whole
+// 256-thread workgroup.
+struct QBlock {
+    const uint16_t *const *src;
+    const int64_t *row0;
+    const int64_t *bstride;  // per-source matrix stride (elements), or NULL
+    int32_t nsrc;
+    int64_t cols, R, nbc;
+    uint8_t *codes;
+    float *scales;
+};
+
+template <int MAXS>
+__device__ __forceinline__ void quant_block(const QBlock &a, int64_t br, int64_t bc, int64_t e, uint32_t *s_red) {
     const int t = threadIdx.x;
-    const int64_t bc = blockIdx.x, br = blockIdx.y, e = blockIdx.z;
     const int rg = t >> 4, seg = t & 15;
     const int64_t col = bc * 128 + seg * 8;
     const bool col_ok = col < a.cols;  // cols is a multiple of 8
@@ -51,9 +63,9 @@ __global__ __launch_bounds__(256) void k_fp8_block_quant(QuantArgs a) {
         if (ok[i]) {
             int s = 0;
 #pragma unroll
-            for (int k = 1; k < FQ_MAXSRC; ++k)
+            for (int k = 1; k < MAXS; ++k)
                 if (k < a.nsrc && r >= a.row0[k]) s = k;
-            const uint16_t *p = a.src[s] + e * a.bstride[s] + (r - a.row0[s]) * a.cols + col;
+            const uint16_t *p = a.src[s] + (a.bstride ? e * a.bstride[s] : 0) + (r - a.row0[s]) * a.cols + col;
             v[i] = *reinterpret_cast<const uint4 *>(p);
             const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
@@ -116,6 +128,48 @@ __global__ __launch_bounds__(256) void k_fp8_block_quant(QuantArgs a) {
     }
 }
 
+__global__ __launch_bounds__(256) void k_fp8_block_quant(QuantArgs a) {
+    __shared__ uint32_t s_red[4];
+    const QBlock q{a.src, a.row0, a.bstride, a.nsrc, a.cols, a.R, a.nbc, a.codes, a.scales};
+    quant_block<FQ_MAXSRC>(q, blockIdx.y, blockIdx.x, blockIdx.z, s_red);
+}
+
+// ---- several stacked groups in one launch -------------------------------------
+// The launch covers the blocks of up to FQ_MAXG groups back to back (group g's
+// blocks are [block0[g], block0[g + 1]), row-block major), so small groups
+// (a layer's [q;k;v] or o) share the GPU with the others instead of running
+// as launches too small to fill it.
+constexpr int FQ_MAXG = 8;
+constexpr int FQ_GSRC = 4;
+
+struct QGroup {
+    const uint16_t *src[FQ_GSRC];
+    int64_t row0[FQ_GSRC + 1];
+    int64_t cols, R, nbc;
+    uint8_t *codes;
+    float *scales;
+    int32_t nsrc;
+};
+
+struct QuantGroupsArgs {
+    QGroup g[FQ_MAXG];
+    int64_t block0[FQ_MAXG + 1];
+    int32_t ng;
+};
+
+__global__ __launch_bounds__(256) void k_fp8_block_quant_groups(QuantGroupsArgs a) {
+    __shared__ uint32_t s_red[4];
+    const int64_t blk = blockIdx.x;
+    int g = 0;  // the group of this block (uniform)
+#pragma unroll
+    for (int i = 1; i < FQ_MAXG; ++i)
+        if (i < a.ng && blk >= a.block0[i]) g = i;
+    const QGroup &G = a.g[g];  // read in place from the argument block
+    const int64_t lb = blk - a.block0[g];
+    const QBlock q{G.src, G.row0, nullptr, G.nsrc, G.cols, G.R, G.nbc, G.codes, G.scales};
+    quant_block<FQ_GSRC>(q, lb / G.nbc, lb % G.nbc, 0, s_red);
+}
+
 }  // namespace pulse
 
 using namespace pulse;
@@ -140,5 +194,47 @@ extern "C" int pulse_launch_fp8_block_quant(const uint16_t *const *srcs, const i
     a.scales = scales;
     const dim3 g((unsigned)a.nbc, (unsigned)((R + 127) / 128), (unsigned)batch);
     k_fp8_block_quant<<<g, dim3(256), 0, stream>>>(a);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+// groups: (host) descriptors in the layout of pulse_quant_group
+struct QGroupHost {
+    const uint16_t *src[4];
+    int64_t rows[4];
+    int32_t nsrc;
+    int32_t pad;
+    int64_t cols;
+    uint8_t *codes;
+    float *scales;
+};
+
+extern "C" int pulse_launch_fp8_block_quant_groups(const void *groups, int32_t ngroups, hipStream_t stream) {
+    const QGroupHost *h = static_cast<const QGroupHost *>(groups);
+    QuantGroupsArgs a{};
+    int64_t total = 0;
+    for (int g = 0; g < ngroups; ++g) {
+        QGroup &G = a.g[g];
+        int64_t R = 0;
+        for (int i = 0; i < FQ_GSRC; ++i) {
+            G.src[i] = i < h[g].nsrc ? h[g].src[i] : h[g].src[0];
+            G.row0[i] = R;
+            if (i < h[g].nsrc) R += h[g].rows[i];
+        }
+        G.row0[FQ_GSRC] = R;
+        for (int i = h[g].nsrc; i < FQ_GSRC; ++i) G.row0[i] = R;
+        G.cols = h[g].cols;
+        G.R = R;
+        G.nbc = (h[g].cols + 127) / 128;
+        G.codes = h[g].codes;
+        G.scales = h[g].scales;
+        G.nsrc = h[g].nsrc;
+        a.block0[g] = total;
+        total += ((R + 127) / 128) * G.nbc;
+    }
+    for (int g = ngroups; g <= FQ_MAXG; ++g) a.block0[g] = total;
+    for (int g = ngroups; g < FQ_MAXG; ++g) a.g[g] = a.g[0];
+    a.ng = ngroups;
+    if (total > 0x7FFFFFFF) return -3;
+    k_fp8_block_quant_groups<<<dim3((unsigned)total), dim3(256), 0, stream>>>(a);
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }

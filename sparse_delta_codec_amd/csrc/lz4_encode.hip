@@ -201,7 +201,11 @@ struct FusedArgs {
     int64_t *d_count;
     uint64_t *pstatus;     // look-back words over the blocks' patch counts
     int64_t n;
+    int64_t *tile_first;   // first patch entry of each 16384-element tile [ntiles + 1], or NULL
+    int64_t ntiles;
 };
+
+constexpr int kPatchTile = 16384;  // elements per tile of the patch's tile index
 
 // entries staged per wave in the output window: (offset in block, value) as
 // one 32-bit word; a wave with more falls back to direct stores
@@ -499,6 +503,21 @@ __device__ __forceinline__ void enc_rest(const Lz4EncArgs &a, const FusedArgs &f
                     if (b == a.nblocks - 1) *f.d_count = (int64_t)(pre + p_count);
                     if ((int64_t)(pre + p_count) > f.cap) or_agent32(a.d_status, 1u /*PULSE_DS_CAPACITY*/);
                 }
+                if (f.tile_first) {
+                    // the tile index: every tile that starts in this block starts
+                    // at a wave boundary, so its first entry is the block's place
+                    // plus the counts of the waves before it
+                    constexpr int BLK_E = FusedGeom<CHLOG>::BLK_E, WAVE_E = FusedGeom<CHLOG>::NG * 256;
+                    const uint32_t x = ln < LZE_NW ? sh.pw[ln] : 0u;
+                    const uint32_t incl = wave_incl_sum(x);
+                    const int64_t t1 = (blk_e0 + BLK_E + kPatchTile - 1) / kPatchTile;
+                    for (int64_t tt = (blk_e0 + kPatchTile - 1) / kPatchTile; tt < t1 && tt < f.ntiles; ++tt) {
+                        const int wj = (int)((tt * kPatchTile - blk_e0) / WAVE_E);
+                        const uint32_t before = wj > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)incl, wj - 1) : 0u;
+                        if (ln == 0) f.tile_first[tt] = (int64_t)(pre + before);
+                    }
+                    if (b == a.nblocks - 1 && ln == 0) f.tile_first[f.ntiles] = (int64_t)(pre + p_count);
+                }
             }
         }
         __syncthreads();
@@ -758,7 +777,7 @@ extern "C" int pulse_launch_cast_diff_lz4(const float *w_new, const uint16_t *b_
                                           uint16_t *val, int64_t cap, int64_t *d_count, int64_t n,
                                           int32_t block_bytes, uint8_t *payload, int64_t payload_cap,
                                           uint32_t *comp_sizes, uint64_t *comp_offsets, uint64_t *d_total,
-                                          uint32_t *d_status, void *ws, hipStream_t stream) {
+                                          uint32_t *d_status, int64_t *tile_first, void *ws, hipStream_t stream) {
     const int64_t nbytes = 2 * n;
     const int64_t nb = (nbytes + block_bytes - 1) / block_bytes;
     Lz4EncArgs a{};
@@ -785,6 +804,8 @@ extern "C" int pulse_launch_cast_diff_lz4(const float *w_new, const uint16_t *b_
     f.d_count = d_count;
     f.pstatus = a.status + nb;
     f.n = n;
+    f.tile_first = idx ? tile_first : nullptr;
+    f.ntiles = (n + kPatchTile - 1) / kPatchTile;
     const dim3 grid((unsigned)nb), block(LZE_THREADS);
     const bool patch = idx != nullptr;
     if (block_bytes == 65536) {

@@ -35,7 +35,8 @@ def test_header_declares_the_codec_calls():
     fns = declared_functions()
     for name in ("pulse_cast_diff", "pulse_compact", "pulse_apply_patch", "xor_mask_apply",
                  "lz4_encode_blocks", "lz4_decode_blocks", "lz4_decode_parse", "lz4_decode_apply",
-                 "fp8_block_quant", "pulse_cast_diff_lz4", "pulse_workspace_bytes",
+                 "fp8_block_quant", "fp8_block_quant_groups", "pulse_cast_diff_lz4", "pulse_patch_tiles",
+                 "pulse_apply_patch_tiled", "pulse_workspace_bytes",
                  "pulse_workspace_init", "pulse_status_string", "pulse_version"):
         assert name in fns, name
 
@@ -100,16 +101,40 @@ def test_argument_errors_return_before_any_launch(lib):
     assert par(al, 10, al, al, 3, 65536, 70000, al, al, 1 << 20, None) == EINVAL          # nblocks
     assert par(al, 10, None, al, 2, 65536, 70000, al, al, 1 << 20, None) == EINVAL        # no offsets
     assert par(al, 10, al, al, 2, 65536, 70000, al, al, 16, None) == EWORKSPACE
+    import sparse_delta_codec_amd as pk  # the binding's layout of pulse_quant_group
+    fq = lib.fp8_block_quant_groups
+    fq.argtypes = [V, ctypes.c_int32, V]
+    grp = (pk._QuantGroup * 2)()
+    for g in grp:
+        g.src[0], g.rows[0], g.nsrc, g.cols, g.codes, g.scales = 0x10000, 128, 1, 128, 0x20000, 0x30000
+    gp = ctypes.cast(grp, V)
+    assert fq(gp, 0, None) == EINVAL and fq(gp, 9, None) == EINVAL and fq(None, 1, None) == EINVAL
+    grp[1].cols = 100
+    assert fq(gp, 2, None) == EINVAL                                              # cols % 8
+    grp[1].cols, grp[1].nsrc = 128, 5
+    assert fq(gp, 2, None) == EINVAL                                              # nsrc
+    grp[1].nsrc, grp[1].src[0] = 1, 0x10002
+    assert fq(gp, 2, None) == EALIGN                                              # source alignment
+    grp[1].src[0], grp[1].rows[0] = 0x10000, 0
+    assert fq(gp, 2, None) == EINVAL                                              # no rows
     fz = lib.pulse_cast_diff_lz4
-    fz.argtypes = [V, V, V, V, V, I64, V, I64, ctypes.c_int32, V, I64, V, V, V, V, V, ctypes.c_size_t, V]
-    fargs = [al, al, al, al, al, 10, al, 1000, 65536, al, 100, al, al, al, al, al, 1 << 20, None]
+    fz.argtypes = [V, V, V, V, V, I64, V, V, I64, ctypes.c_int32, V, I64, V, V, V, V, V, ctypes.c_size_t, V]
+    fargs = [al, al, al, al, al, 10, al, al, 1000, 65536, al, 100, al, al, al, al, al, 1 << 20, None]
     assert fz(None, *fargs[1:]) == EINVAL                                         # no masters
-    assert fz(*fargs[:7], 0, *fargs[8:]) == EINVAL                                # n = 0
-    assert fz(*fargs[:8], 4096, *fargs[9:]) == EINVAL                             # block size
+    assert fz(*fargs[:8], 0, *fargs[9:]) == EINVAL                                # n = 0
+    assert fz(*fargs[:9], 4096, *fargs[10:]) == EINVAL                            # block size
     assert fz(*fargs[:4], None, *fargs[5:]) == EINVAL                             # partial patch
+    assert fz(*fargs[:3], None, None, 10, None, al, *fargs[8:]) == EINVAL         # tile index without patch
     assert fz(*fargs[:2], mis, *fargs[3:]) == EALIGN                              # b_new
-    assert fz(*fargs[:7], 1 << 31, *fargs[8:]) == ERANGE                          # int32 indices
-    assert fz(*fargs[:16], 16, None) == EWORKSPACE
+    assert fz(*fargs[:8], 1 << 31, *fargs[9:]) == ERANGE                          # int32 indices
+    assert fz(*fargs[:17], 16, None) == EWORKSPACE
+    pt = lib.pulse_patch_tiles
+    pt.argtypes = [V, V, I64, I64, V, V]
+    assert pt(None, al, 10, 100, al, None) == EINVAL and pt(al, al, 10, 0, al, None) == EINVAL
+    assert pt(al, al, 10, (1 << 31) + 1, al, None) == ERANGE
+    at = lib.pulse_apply_patch_tiled
+    at.argtypes = [V, I64, V, V, V, I64, V, V]
+    assert at(mis, 100, al, al, al, 10, al, None) == EALIGN and at(al, 100, al, al, None, 10, al, None) == EINVAL
     app = lib.lz4_decode_apply
     app.argtypes = dec.argtypes
     assert app(al, 10, al, al, 2, 65536, 70000, al, 2, al, al, 1 << 20, None) == EINVAL     # mode

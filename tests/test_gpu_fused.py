@@ -38,6 +38,12 @@ def masters(n, seed, density=None):
     return w0, w1
 
 
+def tile_index(idx, count, n):
+    """The patch's tile index from its definition: first entry >= 16384 t."""
+    starts = np.arange(0, (n + 16383) // 16384, dtype=np.int64) * 16384
+    return np.append(np.searchsorted(idx[:count].astype(np.int64), starts, side="left"), count).astype(np.int64)
+
+
 def fused(w1, b0, block_bytes=65536, cap=None, pcap=None, want_new=True, want_patch=True, in_place=False, ws=None):
     n = w1.size
     nb = (2 * n + block_bytes - 1) // block_bytes
@@ -48,12 +54,14 @@ def fused(w1, b0, block_bytes=65536, cap=None, pcap=None, want_new=True, want_pa
     idx = zeros(cap, torch.int32)[:cap] if want_patch else None
     val = zeros(cap, torch.int16)[:cap] if want_patch else None
     cnt = zeros(1, torch.int64) if want_patch else None
+    tf = torch.full((pulse.patch_tile_count(n),), -7, dtype=torch.int64, device="cuda") if want_patch else None
     payload = zeros(pcap, torch.uint8)[:pcap] if pcap else zeros(1, torch.uint8)[:0]
     sizes, offs = zeros(nb, torch.int32), zeros(nb, torch.int64)
     tot, st = zeros(1, torch.int64), zeros(1, torch.int32)
     if ws is None:
         ws = pulse.workspace(pulse.PULSE_OP_CAST_DIFF_LZ4, n, block_bytes)
-    pulse.pulse_cast_diff_lz4(W, B0, bn, idx, val, cnt, payload, sizes, offs, tot, st, ws, block_bytes=block_bytes)
+    pulse.pulse_cast_diff_lz4(W, B0, bn, idx, val, cnt, payload, sizes, offs, tot, st, ws, block_bytes=block_bytes,
+                              tile_first=tf)
     torch.cuda.synchronize()
     t = int(host(tot)[0])
     out = dict(total=t, status=int(host(st)[0]), sizes=host(sizes, np.uint32)[:nb], offsets=host(offs, np.uint64)[:nb],
@@ -62,7 +70,7 @@ def fused(w1, b0, block_bytes=65536, cap=None, pcap=None, want_new=True, want_pa
     if want_patch:
         c = int(host(cnt)[0])
         k = min(c, cap)
-        out.update(count=c, idx=host(idx)[:k], val=u16(val)[:k])
+        out.update(count=c, idx=host(idx)[:k], val=u16(val)[:k], tile_first=host(tf))
     return out
 
 
@@ -78,6 +86,7 @@ def check(got, w1, b0, block_bytes=65536, cap=None):
         k = ref["count"] if cap is None else min(cap, ref["count"])
         assert got["count"] == ref["count"]
         assert np.array_equal(got["idx"], ref["idx"][:k]) and np.array_equal(got["val"], ref["val"][:k])
+        assert np.array_equal(got["tile_first"], tile_index(ref["idx"], ref["count"], w1.size))
     return ref
 
 
@@ -175,3 +184,24 @@ def test_fused_chain_and_workspace_reuse():
         assert np.array_equal(u16(send), want)
         assert np.array_equal(u16(recv_p), want) and np.array_equal(u16(recv_x), want)
     assert int(host(st)[0]) == 0
+
+
+@pytest.mark.parametrize("density", [None, 0.004, 0.3])
+def test_patch_tiles_and_tiled_apply(density):
+    """The tile index written by pulse_patch_tiles equals the one the fused pass
+    writes (and the definition); the tiled apply rebuilds the new view."""
+    n = 9 * 16384 + 1234
+    w0, w1 = masters(n, seed=600 + (0 if density is None else int(density * 1000)), density=density)
+    b0 = oracle.cast_bf16(w0)
+    got = fused(w1, b0)
+    ref = check(got, w1, b0)
+    m = ref["count"]
+    I = dev(ref["idx"]) if m else zeros(1, torch.int32)
+    V = dev(ref["val"]) if m else zeros(1, torch.int16)
+    tf = torch.full((pulse.patch_tile_count(n),), -3, dtype=torch.int64, device="cuda")
+    pulse.pulse_patch_tiles(I, dev(np.array([m], np.int64)), tf, n, max_count=max(m, 1))
+    B, st = dev(b0), zeros(1, torch.int32)
+    pulse.pulse_apply_patch_tiled(B, I, V, tf, st, max_count=max(m, 1))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(tf), got["tile_first"])
+    assert np.array_equal(u16(B), ref["b_new"]) and int(host(st)[0]) == 0

@@ -289,6 +289,34 @@ def test_apply_many_waves_large_patch():
         assert np.array_equal(u16(B), ref) and int(host(st)[0]) == rst == 0
 
 
+@pytest.mark.parametrize("density", [1.0, 0.3, 0.07, 0.05, 0.01, 0.0])
+def test_apply_tiled_matches_oracle(density):
+    """The tiled apply against the oracle, with tiles above and below the dense
+    threshold in one patch, a ragged last tile, and the tile index built on the
+    device; the same with out-of-range entries at both ends (reported, skipped)."""
+    rng = np.random.default_rng(int(density * 100) + 3)
+    n = 13 * 16384 + 4321
+    b = rng.integers(0, 1 << 16, n, dtype=np.uint16)
+    d = np.full(n, density)
+    d[5 * 16384: 7 * 16384] = 0.9       # two dense tiles in any patch
+    d[9 * 16384: 10 * 16384] = 0.001     # a sparse one
+    pos = np.flatnonzero(rng.random(n) < d).astype(np.int32)
+    for extra in (False, True):
+        p = np.concatenate([np.array([-9, -1], np.int32), pos, np.array([n, n + 77], np.int32)]) if extra else pos
+        val = rng.integers(0, 1 << 16, p.size, dtype=np.uint16)
+        m = p.size
+        I, V = (dev(p), dev(val)) if m else (zeros(1, torch.int32), zeros(1, torch.int16))
+        tf = zeros(pulse.patch_tile_count(n), torch.int64)
+        cnt = dev(np.array([m], np.int64))
+        pulse.pulse_patch_tiles(I, cnt, tf, n, max_count=max(m, 1))
+        B, st = dev(b), zeros(1, torch.int32)
+        pulse.pulse_apply_patch_tiled(B, I, V, tf, st, max_count=max(m, 1))
+        torch.cuda.synchronize()
+        ref, rst = oracle.apply_patch(b, p, val)
+        assert np.array_equal(u16(B), ref), np.flatnonzero(u16(B) != ref)[:8]
+        assert int(host(st)[0]) == rst == (pulse.PULSE_DS_BADINDEX if extra else 0)
+
+
 def test_patch_chain_20_steps_no_drift():
     """Encode -> apply on the device each step, no host sync between them; the
     receiver stays bit-identical to the direct cast of every version."""
@@ -569,6 +597,42 @@ def test_fp8_quant_special_blocks_and_batch():
     codes, scales = gpu_quant([g, u], batch=3)
     rc, rs = oracle.fp8_block_quant([g, u], batch=3)
     assert np.array_equal(scales.view(np.uint32), rs.view(np.uint32)) and np.array_equal(codes, rc)
+
+
+def test_fp8_groups_in_one_launch_match_per_group_oracle():
+    """Eight stacked groups of different shapes (1 to 4 sources, rows and
+    columns that are and are not multiples of 128, a lone block) in one launch:
+    every group's codes and scales equal the oracle's quantisation of that
+    group alone; then a second call with one group."""
+    rng = np.random.default_rng(44)
+    shapes = [[(128, 256), (32, 256), (32, 256)],      # [q; k; v]-like
+              [(256, 256)],                             # o-like
+              [(200, 136), (72, 136)],                  # [gate; up]-like, ragged
+              [(128, 1024)],                            # down-like
+              [(1, 8)],                                 # one partial block
+              [(130, 64), (2, 64), (5, 64), (7, 64)],   # four sources
+              [(384, 128)],
+              [(64, 520)]]
+    groups, refs, outs = [], [], []
+    for g, sh in enumerate(shapes):
+        srcs = [bf16_bits(rng.standard_normal(s) * rng.choice([0.02, 1.0, 300.0])) for s in sh]
+        R, cols = sum(s[0] for s in sh), sh[0][1]
+        codes = zeros(R * cols, torch.uint8)
+        scales = zeros(((R + 127) // 128) * ((cols + 127) // 128), torch.float32)
+        groups.append(([dev(x) for x in srcs], codes, scales))
+        refs.append(oracle.fp8_block_quant(srcs))
+        outs.append((R, cols))
+    pulse.fp8_block_quant_groups(groups)
+    torch.cuda.synchronize()
+    for (srcs, codes, scales), (rc, rs), (R, cols) in zip(groups, refs, outs):
+        nsc = ((R + 127) // 128) * ((cols + 127) // 128)
+        assert np.array_equal(host(scales)[:nsc].view(np.uint32), rs.reshape(-1).view(np.uint32))
+        assert np.array_equal(host(codes)[:R * cols], rc.reshape(-1))
+    srcs, codes, scales = groups[3]
+    codes.zero_()
+    pulse.fp8_block_quant_groups([groups[3]])
+    torch.cuda.synchronize()
+    assert np.array_equal(host(codes)[:128 * 1024], refs[3][0].reshape(-1))
 
 
 def test_fp8_all_bf16_values_through_one_scale():
