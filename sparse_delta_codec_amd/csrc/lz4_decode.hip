@@ -78,6 +78,10 @@ __device__ __forceinline__ uint32_t win_byte(uint64_t lo, uint64_t hi, uint32_t 
 
 // ---- K1 ----------------------------------------------------------------------
 constexpr int K1_RING = 512;                   // bytes of compressed stream held per lane
+// Rings sit K1_STRIDE bytes apart: lanes refilled together read at nearly the
+// same ring offsets, and with a stride of 512 bytes those reads would all fall
+// in one LDS bank; 16 more bytes per ring move each lane four banks along.
+constexpr int K1_STRIDE = K1_RING + 16;
 constexpr int K1_PIECES = K1_RING / 16;        // 16-byte pieces per ring
 constexpr int K1_RPI = kWave / K1_PIECES;      // rings filled by one load instruction
 constexpr int K1_BATCH = 8;                    // loads in flight per lane
@@ -119,7 +123,7 @@ __device__ __forceinline__ void ring_refill(uint8_t *rings, const uint8_t *pay, 
 #pragma unroll
         for (int u = 0; u < K1_BATCH; ++u) {
             const int j = g + u * K1_RPI + r;
-            uint8_t *to = ok[u] ? rings + j * K1_RING + 16 * k : rings + kWave * K1_RING + 16 * lane;
+            uint8_t *to = ok[u] ? rings + j * K1_STRIDE + 16 * k : rings + kWave * K1_STRIDE + 16 * lane;
             *reinterpret_cast<u32x4 *>(to) = v[u];
         }
     }
@@ -268,7 +272,7 @@ __device__ __forceinline__ WalkResult k1_walk(uint8_t *rings, const uint8_t *rin
 }
 
 __global__ __launch_bounds__(64) void k_lz4_parse(Lz4DecArgs a) {
-    __shared__ __align__(16) uint8_t s_rings[kWave * K1_RING + kWave * 16];  // rings, then spill slots
+    __shared__ __align__(16) uint8_t s_rings[kWave * K1_STRIDE + kWave * 16];  // rings, then spill slots
     __shared__ uint32_t s_tile, s_tag;
     __shared__ uint64_t s_scan[1];
     const int lane = lane_id();
@@ -312,7 +316,7 @@ __global__ __launch_bounds__(64) void k_lz4_parse(Lz4DecArgs a) {
     const uint32_t len = live ? block_len(a, b) : 0;
     uint2 *ck = a.ckpt + (live ? ck_base(off, b) : 0);
     const WalkResult w =
-        k1_walk(s_rings, s_rings + lane * K1_RING, !bad, a.payload, a.payload_bytes, (int64_t)off, (uint32_t)S, len, ck);
+        k1_walk(s_rings, s_rings + lane * K1_STRIDE, !bad, a.payload, a.payload_bytes, (int64_t)off, (uint32_t)S, len, ck);
     const uint32_t nseq = w.nseq;
     const bool slow = (w.flags & F_SLOW) != 0;
     bad = bad || (w.flags & F_BAD) != 0;
