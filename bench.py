@@ -133,6 +133,20 @@ def quant_groups(specs, tensor_ids):
     return groups
 
 
+def grouped_quant_plan(pulse, specs, offs, plan, b_recv, codes, scales):
+    """A chunk's FP8 groups as batches for fp8_block_quant_groups, each group
+    with its own codes and scales (views into the shared buffers)."""
+    lst, co, so = [], 0, 0
+    for (g, rows, cols) in plan:
+        srcs = [b_recv[offs[i]: offs[i] + specs[i].numel].view(specs[i].shape) for i in g]
+        nsc = ((rows + 127) // 128) * ((cols + 127) // 128)
+        lst.append((srcs, codes[co: co + rows * cols], scales[so: so + nsc]))
+        co += rows * cols
+        so += nsc
+    m = pulse.PULSE_QUANT_MAX_GROUPS
+    return [lst[k: k + m] for k in range(0, len(lst), m)]
+
+
 def views_equal(a, b, chunk=1 << 30):
     """Bitwise equality of two large device tensors, chunked to bound temporaries."""
     for s in range(0, a.numel(), chunk):
@@ -185,7 +199,7 @@ def main():
         # the old served view is the library's own cast of the initial masters
         pulse.pulse_cast_diff(w, b_new=b_old[offs[ti]: offs[ti] + s.numel])
         workload.apply_step(w, 2, ti, 1, tmp=tmp)
-    del tmp
+    del tmp, w  # w is a view of W
     b_recv = b_old.clone()
     torch.cuda.synchronize()
 
@@ -225,16 +239,8 @@ def main():
     codes = torch.empty(max(max_codes, max_chunk_codes), dtype=torch.uint8, device=dev)
     scales = torch.empty(max(max_scales, max_chunk_scales), dtype=torch.float32, device=dev)
     n_quant = sum(rows * cols for plan in qplans for (_, rows, cols) in plan)
-    gplans = []  # per chunk: lists of at most 8 (srcs, codes, scales) for fp8_block_quant_groups
-    for ci, plan in enumerate(qplans):
-        lst, co, so = [], 0, 0
-        for (g, rows, cols) in plan:
-            srcs = [b_recv[offs[i]: offs[i] + specs[i].numel].view(specs[i].shape) for i in g]
-            nsc = ((rows + 127) // 128) * ((cols + 127) // 128)
-            lst.append((srcs, codes[co: co + rows * cols], scales[so: so + nsc]))
-            co += rows * cols
-            so += nsc
-        gplans.append([lst[k: k + pulse.PULSE_QUANT_MAX_GROUPS] for k in range(0, len(lst), pulse.PULSE_QUANT_MAX_GROUPS)])
+    # per chunk: lists of at most 8 (srcs, codes, scales) for fp8_block_quant_groups
+    gplans = [grouped_quant_plan(pulse, specs, offs, plan, b_recv, codes, scales) for plan in qplans]
     torch.cuda.synchronize()
     t_setup = time.time() - t_setup
     log(f"setup done in {t_setup:.1f} s: {n} params in {len(chunks)} chunks")
@@ -445,7 +451,7 @@ def main():
         if "fp8" in legs:
             nxt.update(fp8_view_leg(pulse, specs, chunks, offs, qplans, W, b_old, stage, dev,
                                     not args.no_cpu_baseline))
-        del stage, b_recv, idx, val, payload, codes, scales
+        del stage, b_recv, idx, val, payload, codes, scales, gplans, tiles  # gplans holds views of b_recv
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
         if "list" in legs:
