@@ -12,16 +12,19 @@ tensors (embed | 16 x four decoder layers | final norm + lm_head):
                               (--separate-encode: pulse_cast_diff, then
                               lz4_encode_blocks over old and new)
   receiver  lz4_decode_parse  the serial token-chain parse of every block, on a
-                              second stream, while the next two keep HBM busy
+                              second stream, beside the next two (--schedule)
   receiver  pulse_apply_patch scatter the patch into the receiver's view (v0 -> v1)
                               (--apply-tiled: pulse_apply_patch_tiled with the
                               tile index the sender writes)
   receiver  fp8_block_quant_groups  stacked [q;k;v], o, stacked [gate;up],
                               down, embed, lm_head -> E4M3 + FP32 128x128
                               scales, up to 8 groups per launch
-                              (--quant-per-group: one fp8_block_quant each)
+                              (--quant-per-group: one fp8_block_quant each;
+                              --receiver fused: pulse_apply_quant, the patch
+                              apply and the quantisation in one pass per
+                              128x128 block)
   receiver  lz4_decode_apply  rebuild + XOR in place into the receiver's view
-                              (--serial-decode: one lz4_decode_blocks call on
+                              (--schedule serial: one lz4_decode_blocks call on
                               the main stream, no second stream)
 
 The mask is symmetric, so the XOR step takes the receiver from v1 back to v0:
@@ -44,6 +47,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "weights processed GB/s (encode+apply) and % of MI355X HBM peak, 1 GPU"
+SCHEDULES = {
+    "ahead": "parse of chunk c on a second stream beside the encode of chunk c + 1 and the receiver's pass of "
+             "chunk c; decode apply on the main stream",
+    "side": "parse on a second stream beside the receiver's pass of the same chunk, apply on the main stream",
+    "pipeline": "encode and parse of chunk c on a second stream while the main stream receives and decodes "
+                "chunk c - 1",
+    "serial": "one lz4_decode_blocks call per chunk, main stream",
+}
 PEAK_HBM = 8.0e12
 BLOCK = 65536
 PATCH_CAP_FRAC = 0.125   # patch capacity per chunk (measured density ~8.06%)
@@ -64,8 +75,14 @@ def parse():
                         "alone, slower beside the decode parse) instead of pulse_apply_patch")
     p.add_argument("--quant-per-group", action="store_true",
                    help="one fp8_block_quant launch per stacked group instead of grouped launches")
-    p.add_argument("--serial-decode", action="store_true",
-                   help="decode each chunk with one lz4_decode_blocks call on the main stream (no overlap)")
+    p.add_argument("--receiver", choices=["fused", "separate"], default="separate",
+                   help="fused: pulse_apply_quant (patch apply + FP8 quantisation in one read of the view); "
+                        "separate: pulse_apply_patch, then fp8_block_quant_groups")
+    p.add_argument("--schedule", choices=["ahead", "side", "pipeline", "serial"], default="side",
+                   help="ahead: the decode parse of chunk c on a second stream beside the encode of chunk c + 1 "
+                        "and the receiver's pass of chunk c; side: beside the receiver's pass of chunk c only; "
+                        "pipeline: encode and parse of chunk c on the second stream while the main stream "
+                        "receives chunk c - 1; serial: one lz4_decode_blocks call per chunk, one stream")
     p.add_argument("--cpu-sample-frac", type=float, default=1.0,
                    help="fraction of the oracle's sample (decoder layer 0) it times")
     p.add_argument("--next", default="loco,patch,list", help="next-row legs measured after the timed steps, comma "
@@ -145,6 +162,26 @@ def grouped_quant_plan(pulse, specs, offs, plan, b_recv, codes, scales):
         so += nsc
     m = pulse.PULSE_QUANT_MAX_GROUPS
     return [lst[k: k + m] for k in range(0, len(lst), m)]
+
+
+def receiver_plan(pulse, specs, offs, chunk, plan, codes, scales, dev):
+    """The receiver's pass over a chunk: its FP8 groups (codes and scales laid
+    out as in grouped_quant_plan) and its other tensors, patched only."""
+    s0, e0, tids = chunk
+    groups, co, so, seen = [], 0, 0, set()
+    for (g, rows, cols) in plan:
+        nsc = ((rows + 127) // 128) * ((cols + 127) // 128)
+        groups.append(([(offs[i] - s0, specs[i].shape[0]) for i in g], cols, codes[co: co + rows * cols],
+                       scales[so: so + nsc]))
+        co += rows * cols
+        so += nsc
+        seen.update(g)
+    for i in tids:
+        if i not in seen:
+            sh = specs[i].shape
+            rows, cols = (sh[0], sh[1]) if len(sh) == 2 else (1, specs[i].numel)
+            groups.append(([(offs[i] - s0, rows)], cols, None, None))
+    return pulse.pulse_apply_quant_plan(groups, e0 - s0, device=dev)
 
 
 def views_equal(a, b, chunk=1 << 30):
@@ -246,78 +283,163 @@ def main():
     log(f"setup done in {t_setup:.1f} s: {n} params in {len(chunks)} chunks")
 
     fused = not args.separate_encode
-    stages = (["encode"] if fused else ["cast_diff", "lz4_encode"]) + ["apply_patch", "fp8_quant", "lz4_decode"]
+    recv_fused = args.receiver == "fused"
+    sched = args.schedule
+    if sched in ("ahead", "pipeline") and not fused:
+        raise SystemExit(f"--schedule {sched} goes with the fused encode")
+    if args.apply_tiled and (recv_fused or sched in ("ahead", "pipeline")):
+        raise SystemExit("--apply-tiled goes with --receiver separate and --schedule side or serial")
+    if args.quant_per_group and recv_fused:
+        raise SystemExit("--quant-per-group goes with --receiver separate")
+    recv_stages = ["receiver"] if recv_fused else ["apply_patch", "fp8_quant"]
+    stages = (["encode"] if fused else ["cast_diff", "lz4_encode"]) + recv_stages + ["lz4_decode"]
     ev = {k: [] for k in stages}
+
+    if recv_fused:
+        ws_aq = pulse.workspace(pulse.PULSE_OP_APPLY_QUANT, max_chunk, 0, dev)
+        aq_plans = [receiver_plan(pulse, specs, offs, ch, plan, codes, scales, dev)
+                    for ch, plan in zip(chunks, qplans)]
+    # buffer sets: what a chunk's sender output and parse live in until the
+    # receiver is done with them (two when a chunk's encode overlaps another's)
+    bufs = [(idx, val, payload, csizes, coffs, ws_de)]
+    if sched in ("ahead", "pipeline"):
+        bufs.append((torch.empty_like(idx), torch.empty_like(val), torch.empty_like(payload),
+                     torch.empty_like(csizes), torch.empty_like(coffs),
+                     pulse.workspace(pulse.PULSE_OP_LZ4_DECODE, nbmax, pcap, dev)))
 
     main_stream = torch.cuda.current_stream()
     side_stream = torch.cuda.Stream()  # default priority, like every stream here
     parse_ev = {"lz4_decode": []}      # parse events (side stream), added to the decode stage
 
-    def run_step(record):
-        for ci, (s0, e0, tids) in enumerate(chunks):
-            m = e0 - s0
+    def rec(record, name, fn, store=None):
+        # events on the stream the kernels run on (the current one)
+        if record:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            (ev if store is None else store)[name].append((a, b))
+        else:
+            fn()
 
-            def rec(name, fn, store=None):
-                # events on the stream the kernels run on (the current one)
-                if record:
-                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    a.record()
-                    fn()
-                    b.record()
-                    (ev if store is None else store)[name].append((a, b))
-                else:
-                    fn()
+    def encode(record, ci, B):
+        s0, e0, _ = chunks[ci]
+        m = e0 - s0
+        I, V, P, CS, CO, _ = B
+        if fused:
+            rec(record, "encode", lambda: pulse.pulse_cast_diff_lz4(
+                W[s0:e0], b_old[s0:e0], stage[:m], I, V, cnt[ci:ci + 1], P, CS, CO, ctotal[ci:ci + 1], status,
+                ws_fz, tile_first=tiles if args.apply_tiled else None, stream=torch.cuda.current_stream()))
+        else:
+            rec(record, "cast_diff", lambda: pulse.pulse_cast_diff(W[s0:e0], b_old[s0:e0], stage[:m], None, I, V,
+                                                                   cnt[ci:ci + 1], status, ws_cd))
+            rec(record, "lz4_encode", lambda: pulse.lz4_encode_blocks(b_old[s0:e0], P, CS, CO, ctotal[ci:ci + 1],
+                                                                      status, ws_en, src_xor=stage[:m]))
 
-            def quant():
-                if args.quant_per_group:
-                    for (g, rows, cols) in qplans[ci]:
-                        srcs = [b_recv[offs[i]: offs[i] + specs[i].numel].view(specs[i].shape) for i in g]
-                        pulse.fp8_block_quant(srcs, codes, scales)
-                else:
-                    for batch in gplans[ci]:
-                        pulse.fp8_block_quant_groups(batch)
+    def receive(record, ci, B):
+        """The patch apply (v0 -> v1) and the FP8 quantisation of v1."""
+        s0, e0, _ = chunks[ci]
+        m = e0 - s0
+        I, V = B[0], B[1]
+        if recv_fused:
+            rec(record, "receiver", lambda: pulse.pulse_apply_quant(b_recv[s0:e0], I, V, cnt[ci:ci + 1],
+                                                                    aq_plans[ci], status, ws_aq))
+            return
 
-            if fused:
-                rec("encode", lambda: pulse.pulse_cast_diff_lz4(W[s0:e0], b_old[s0:e0], stage[:m], idx, val,
-                                                                cnt[ci:ci + 1], payload, csizes, coffs,
-                                                                ctotal[ci:ci + 1], status, ws_fz,
-                                                                tile_first=tiles if args.apply_tiled else None))
+        def apply():
+            if not args.apply_tiled:
+                pulse.pulse_apply_patch(b_recv[s0:e0], I, V, cnt[ci:ci + 1], status)
+                return
+            if not fused:  # the receiver builds the tile index itself
+                pulse.pulse_patch_tiles(I, cnt[ci:ci + 1], tiles, m)
+            pulse.pulse_apply_patch_tiled(b_recv[s0:e0], I, V, tiles, status)
+
+        def quant():
+            if args.quant_per_group:
+                for (g, rows, cols) in qplans[ci]:
+                    srcs = [b_recv[offs[i]: offs[i] + specs[i].numel].view(specs[i].shape) for i in g]
+                    pulse.fp8_block_quant(srcs, codes, scales)
             else:
-                rec("cast_diff", lambda: pulse.pulse_cast_diff(W[s0:e0], b_old[s0:e0], stage[:m], None, idx, val,
-                                                               cnt[ci:ci + 1], status, ws_cd))
-                rec("lz4_encode", lambda: pulse.lz4_encode_blocks(b_old[s0:e0], payload, csizes, coffs,
-                                                                  ctotal[ci:ci + 1], status, ws_en,
-                                                                  src_xor=stage[:m]))
-            def apply():
-                if not args.apply_tiled:
-                    pulse.pulse_apply_patch(b_recv[s0:e0], idx, val, cnt[ci:ci + 1], status)
-                    return
-                if not fused:  # the receiver builds the tile index itself
-                    pulse.pulse_patch_tiles(idx, cnt[ci:ci + 1], tiles, m)
-                pulse.pulse_apply_patch_tiled(b_recv[s0:e0], idx, val, tiles, status)
+                for batch in gplans[ci]:
+                    pulse.fp8_block_quant_groups(batch)
 
-            if args.serial_decode:
-                rec("apply_patch", apply)
-                rec("fp8_quant", quant)
-                rec("lz4_decode", lambda: pulse.lz4_decode_blocks(payload, coffs, csizes, b_recv[s0:e0], status,
-                                                                  ws_de, mode=1))
-                continue
-            # the parse reads this chunk's payload (after the encode) and the
-            # decode workspace (free once the previous chunk's apply is done,
-            # which the main stream has queued before this encode)
-            side_stream.wait_stream(main_stream)
-            with torch.cuda.stream(side_stream):
-                rec("lz4_decode", lambda: pulse.lz4_decode_parse(payload, coffs, csizes, 2 * m, status, ws_de,
-                                                                 stream=side_stream), store=parse_ev)
-                parsed = torch.cuda.Event()
-                parsed.record(side_stream)
-            # the receiver's patch apply (v0 -> v1) and FP8 quant of v1 run beside the parse;
-            # the main stream takes no other kernel until the parse is done
-            rec("apply_patch", apply)
-            rec("fp8_quant", quant)  # reads the receiver's view before the XOR rewrites it
-            main_stream.wait_event(parsed)
-            rec("lz4_decode", lambda: pulse.lz4_decode_apply(payload, coffs, csizes, b_recv[s0:e0], status, ws_de,
-                                                             mode=1))
+        rec(record, "apply_patch", apply)
+        rec(record, "fp8_quant", quant)  # reads the receiver's view before the XOR rewrites it
+
+    def parse_chunk(record, ci, B):
+        """The decode's token-chain parse, on the side stream."""
+        s0, e0, _ = chunks[ci]
+        _, _, P, CS, CO, WD = B
+        with torch.cuda.stream(side_stream):
+            rec(record, "lz4_decode", lambda: pulse.lz4_decode_parse(P, CO, CS, 2 * (e0 - s0), status, WD,
+                                                                     stream=side_stream), store=parse_ev)
+            parsed = torch.cuda.Event()
+            parsed.record(side_stream)
+        return parsed
+
+    def decode_apply(record, ci, B):
+        s0, e0, _ = chunks[ci]
+        _, _, P, CS, CO, WD = B
+        rec(record, "lz4_decode", lambda: pulse.lz4_decode_apply(P, CO, CS, b_recv[s0:e0], status, WD, mode=1))
+
+    def after(stream):
+        e = torch.cuda.Event()
+        e.record(stream)
+        return e
+
+    last_decode = [None, None]  # pipeline: the decode apply that last used each buffer set
+    seq = [0]                   # pipeline: chunks run so far (the sets alternate across steps)
+
+    def run_step(record):
+        N = len(chunks)
+        if sched == "serial":
+            for ci in range(N):
+                s0, e0, _ = chunks[ci]
+                encode(record, ci, bufs[0])
+                receive(record, ci, bufs[0])
+                rec(record, "lz4_decode", lambda: pulse.lz4_decode_blocks(payload, coffs, csizes, b_recv[s0:e0],
+                                                                          status, ws_de, mode=1))
+        elif sched == "side":
+            # the parse of chunk c beside its apply and quant
+            for ci in range(N):
+                encode(record, ci, bufs[0])
+                side_stream.wait_stream(main_stream)
+                parsed = parse_chunk(record, ci, bufs[0])
+                receive(record, ci, bufs[0])
+                main_stream.wait_event(parsed)
+                decode_apply(record, ci, bufs[0])
+        elif sched == "ahead":
+            # the parse of chunk c beside the encode of chunk c + 1 and the
+            # receiver's pass of chunk c; each set is rewritten by the encode of
+            # chunk c + 2, which the main stream queues after chunk c's decode
+            encode(record, 0, bufs[0])
+            encoded = after(main_stream)
+            for ci in range(N):
+                B = bufs[ci % 2]
+                side_stream.wait_event(encoded)
+                parsed = parse_chunk(record, ci, B)
+                if ci + 1 < N:
+                    encode(record, ci + 1, bufs[(ci + 1) % 2])
+                    encoded = after(main_stream)
+                receive(record, ci, B)
+                main_stream.wait_event(parsed)
+                decode_apply(record, ci, B)
+        else:  # pipeline: encode and parse of chunk c on the side stream while the main stream receives chunk c - 1
+            for ci in range(N):
+                p = seq[0] % 2
+                seq[0] += 1
+                B = bufs[p]
+                with torch.cuda.stream(side_stream):
+                    if last_decode[p] is not None:
+                        side_stream.wait_event(last_decode[p])
+                    encode(record, ci, B)
+                    encoded = after(side_stream)
+                parsed = parse_chunk(record, ci, B)
+                main_stream.wait_event(encoded)
+                receive(record, ci, B)
+                main_stream.wait_event(parsed)
+                decode_apply(record, ci, B)
+                last_decode[p] = after(main_stream)
 
     # ---- warm-up, with the end-to-end check after the first step
     for w in range(max(args.warmup, 1)):
@@ -363,6 +485,7 @@ def main():
     alg = {
         "encode": n * (8 + 6 * d + c),          # read w (4) + old (2), write new (2) + patch (6 d) + payload (c)
         "cast_diff": n * (8 + 6 * d),           # read w (4) + old (2), write new (2) + patch (6 d)
+        "receiver": n * 8 * d + n_quant * 3 + 4 * n_quant / 16384,  # apply_patch + fp8_quant
         "apply_patch": n * 8 * d,               # read patch (6 d), write 2 B per changed element
         "fp8_quant": n_quant * 3 + 4 * n_quant / 16384,  # read 2, write 1 + scales
         "lz4_encode": n * (4 + c),              # read old + new (4), write payload (c)
@@ -379,6 +502,7 @@ def main():
     dom_secs = stage_ms[dom] / 1e3
     achieved = alg[dom] / dom_secs / 1e9
     kernel_files = {"encode": "lz4_encode.hip", "cast_diff": "cast_diff.hip", "apply_patch": "apply.hip",
+                    "receiver": "fp8_quant.hip",
                     "fp8_quant": "fp8_quant.hip",
                     "lz4_encode": "lz4_encode.hip", "lz4_decode": "lz4_decode.hip"}
     roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_HBM / 1e9,
@@ -407,16 +531,17 @@ def main():
                    "params": n, "chunks": len(chunks), "lz4_block_bytes": BLOCK,
                    "encode_schedule": "one fused pass (pulse_cast_diff_lz4)" if fused
                    else "pulse_cast_diff, then lz4_encode_blocks",
-                   "decode_schedule": "one call, main stream" if args.serial_decode
-                   else "parse on a second stream beside apply_patch and fp8_quant, apply on the main stream",
+                   "receiver": "one pass (pulse_apply_quant)" if recv_fused
+                   else "pulse_apply_patch, then fp8_block_quant_groups",
+                   "decode_schedule": SCHEDULES[sched],
                    "changed_fraction": round(d, 6), "lz4_bytes_per_param": round(c, 5),
                    "lz4_ratio_of_mask": round(comp_bytes / (2 * n), 5), "fp8_params": n_quant},
         "hbm_frac_step": round(alg_total / (ms_step / 1e3) / PEAK_HBM, 4),
         "alg_GB_per_step": round(alg_total / 1e9, 2),
         "stages": st_out,
-        "decode_parse": None if args.serial_decode else {
+        "decode_parse": None if sched == "serial" else {
             "ms": round(parse_ms, 3), "launches": len(parse_ev["lz4_decode"]) // args.steps,
-            "stream": "second stream, beside apply_patch and fp8_quant of the same chunk",
+            "stream": "second stream",
             "note": "lz4_decode above is the apply; the one-call decode is both"},
         "roofline": roofline,
         "setup_s": round(t_setup, 1),
@@ -451,7 +576,9 @@ def main():
         if "fp8" in legs:
             nxt.update(fp8_view_leg(pulse, specs, chunks, offs, qplans, W, b_old, stage, dev,
                                     not args.no_cpu_baseline))
-        del stage, b_recv, idx, val, payload, codes, scales, gplans, tiles  # gplans holds views of b_recv
+        del stage, b_recv, idx, val, payload, codes, scales, gplans, tiles, bufs  # gplans holds views of b_recv
+        if recv_fused:
+            del aq_plans, ws_aq  # the plans hold the codes and scales they point into
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
         if "list" in legs:

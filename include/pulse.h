@@ -88,6 +88,7 @@ extern "C" {
 #define PULSE_OP_PATCH_UNPACK 7 /* n = patch entries                            */
 #define PULSE_OP_CAST_DIFF_SEGMENTS 8 /* n = tile count (pulse_segment_tiles)    */
 #define PULSE_OP_CAST_DIFF_LZ4 9 /* n = element count, aux = block_bytes           */
+#define PULSE_OP_APPLY_QUANT 10 /* n = element count of the view (segment index)   */
 
 /* Bytes of workspace the op needs for the given size (0 if it needs none).
  * A workspace serves any number of calls of the op it was sized for, of any
@@ -352,6 +353,67 @@ typedef struct {
     float *scales;
 } pulse_quant_group;
 int fp8_block_quant_groups(const pulse_quant_group *groups, int32_t ngroups, hipStream_t stream);
+
+/* ---- a4 + a7: the receiver's pass, patch apply and FP8 quantisation -------
+ * The receiver overrides the patch's positions in its BF16 view ([Jiang talk]
+ * 11:08-11:30; [PULSE summary] "1. PULSESync", Ricostruzione) and serves the
+ * new weights quantised to FP8 in 128x128 blocks ([Perplexity] opening
+ * paragraph and "Potok zadan").  pulse_apply_quant gives exactly the results
+ * of pulse_apply_patch on the view followed by one fp8_block_quant call per
+ * quantised group, in one read of the view: each 128x128 block is read once,
+ * patched on chip, its changed 16-byte pieces written back and its codes
+ * computed from the patched values.
+ *
+ * A plan describes the view as groups.  A group stacks 1..4 sources along
+ * rows; every source is a row-major [rows, cols] matrix inside the view at an
+ * element offset.  A quantised group (quantise = 1) writes codes [R][cols]
+ * (8-byte aligned) and scales [ceil(R/128)][ceil(cols/128)] as fp8_block_quant
+ * does, R = sum of rows; a group with quantise = 0 is only patched (norms,
+ * biases: describe a 1-D tensor as [1, len]).  cols is a multiple of 8, every
+ * offset a multiple of 8, and the sources of all groups together tile the view
+ * [0, n) with neither gap nor overlap (so every entry of the patch is applied
+ * exactly once).  Groups must not overlap in their outputs. */
+typedef struct {
+    int64_t src_offset[4]; /* element offset of source i in the view          */
+    int64_t rows[4];
+    int32_t nsrc;          /* 1..4                                          */
+    int32_t quantise;      /* 1: codes + scales, 0: patch only                */
+    int64_t cols;
+    uint8_t *codes;        /* device, quantise = 1                          */
+    float *scales;         /* device, quantise = 1                          */
+} pulse_aq_group;
+
+/* Bytes of a plan for ngroups groups (0 when ngroups < 1). */
+int64_t pulse_apply_quant_plan_bytes(int32_t ngroups);
+
+/* Checks the groups against a view of n elements (n <= 2^31 - 1) and writes
+ * the plan into plan (device, 16-byte aligned, plan_bytes >= the size above);
+ * the copy is synchronous, so groups may be freed on return.  *nblocks (host)
+ * receives the number of 128x128 blocks, to be passed to pulse_apply_quant.
+ * PULSE_EINVAL for a bad group or sources that do not tile [0, n),
+ * PULSE_EALIGN for a misaligned offset or output, PULSE_EWORKSPACE when
+ * plan_bytes is too small, PULSE_EHIP when the copy fails. */
+int pulse_apply_quant_plan(const pulse_aq_group *groups, int32_t ngroups, int64_t n, void *plan,
+                           int64_t plan_bytes, int64_t *nblocks);
+
+/* The receiver's pass over a view b [n] (16-byte aligned, updated in place).
+ *   patch_idx, patch_val  the patch, indices strictly ascending (as the
+ *              compaction writes them); count = min(*d_count, max_count),
+ *              max_count >= 1 (the buffers hold at least one entry, which
+ *              is read even when count is 0).
+ *   plan, nblocks  from pulse_apply_quant_plan for this n; the codes and
+ *              scales go where the plan's groups say.
+ *   d_status   PULSE_DS_BADINDEX when an index lies outside [0, n) or does
+ *              not ascend (the view is then unspecified, but nothing outside
+ *              it and the outputs is written); PULSE_DS_WORKSPACE when the
+ *              plan was made for another n or block count (nothing written).
+ *   ws         pulse_workspace_bytes(PULSE_OP_APPLY_QUANT, n, 0): the patch's
+ *              segment index (first entry at or past every 128th element),
+ *              rebuilt by every call.
+ * The inputs must be finite, as for fp8_block_quant. */
+int pulse_apply_quant(uint16_t *b, int64_t n, const int32_t *patch_idx, const uint16_t *patch_val,
+                      const int64_t *d_count, int64_t max_count, const void *plan, int64_t nblocks,
+                      uint32_t *d_status, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---- next: deltas of the FP8 served view ----------------------------------
  * When the sampler serves FP8, the view it must rebuild bit for bit is the

@@ -20,7 +20,7 @@ __all__ = [
     "PULSE_OP_FP8_DELTA", "PULSE_OP_LOCO_GATE", "fp8_view_delta", "fp8_view_apply",
     "pulse_loco_gate", "pulse_loco_accumulate",
     "PULSE_OP_PATCH_UNPACK", "patch_packed_bytes", "patch_pack", "patch_unpack",
-    "PULSE_OP_CAST_DIFF_SEGMENTS", "PULSE_DS_BADSEGMENT", "PULSE_OP_CAST_DIFF_LZ4", "pulse_cast_diff_lz4", "fp8_block_quant_groups", "PULSE_QUANT_MAX_GROUPS", "pulse_patch_tiles",
+    "PULSE_OP_CAST_DIFF_SEGMENTS", "PULSE_DS_BADSEGMENT", "PULSE_OP_CAST_DIFF_LZ4", "pulse_cast_diff_lz4", "fp8_block_quant_groups", "PULSE_QUANT_MAX_GROUPS", "pulse_patch_tiles", "PULSE_OP_APPLY_QUANT", "ApplyQuantPlan", "pulse_apply_quant_plan", "pulse_apply_quant",
     "pulse_apply_patch_tiled", "patch_tile_count", "pulse_segment_tiles", "SegmentTable", "ViewTable",
     "pulse_cast_diff_segments", "pulse_apply_patch_segments", "lz4_decode_parse", "lz4_decode_apply",
 ]
@@ -46,6 +46,7 @@ PULSE_OP_LOCO_GATE = 6
 PULSE_OP_PATCH_UNPACK = 7
 PULSE_OP_CAST_DIFF_SEGMENTS = 8
 PULSE_OP_CAST_DIFF_LZ4 = 9
+PULSE_OP_APPLY_QUANT = 10
 PULSE_DS_BADSEGMENT = 0x10
 
 _P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
@@ -81,12 +82,16 @@ _lib.pulse_cast_diff_lz4.argtypes = [_P, _P, _P, _P, _P, _I64, _P, _P, _I64, _I3
                                      _P]
 _lib.pulse_patch_tiles.argtypes = [_P, _P, _I64, _I64, _P, _P]
 _lib.pulse_apply_patch_tiled.argtypes = [_P, _I64, _P, _P, _P, _I64, _P, _P]
+_lib.pulse_apply_quant_plan_bytes.argtypes = [_I32]
+_lib.pulse_apply_quant_plan_bytes.restype = _I64
+_lib.pulse_apply_quant_plan.argtypes = [_P, _I32, _I64, _P, _I64, _P]
+_lib.pulse_apply_quant.argtypes = [_P, _I64, _P, _P, _P, _I64, _P, _I64, _P, _P, _SZ, _P]
 for _f in ("pulse_cast_diff_segments", "pulse_apply_patch_segments", "patch_pack", "patch_unpack",
            "pulse_workspace_init", "pulse_cast_diff", "pulse_compact", "pulse_apply_patch",
            "xor_mask_apply", "lz4_encode_blocks", "lz4_decode_blocks", "fp8_block_quant",
            "fp8_view_delta", "fp8_view_apply", "pulse_loco_gate", "pulse_loco_accumulate",
            "lz4_decode_parse", "lz4_decode_apply", "pulse_cast_diff_lz4", "fp8_block_quant_groups",
-           "pulse_patch_tiles", "pulse_apply_patch_tiled"):
+           "pulse_patch_tiles", "pulse_apply_patch_tiled", "pulse_apply_quant_plan", "pulse_apply_quant"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -387,6 +392,71 @@ def fp8_block_quant_groups(groups, stream=None):
         arr[g].scales = _dev(scales, f"groups[{g}].scales", torch.float32)
     _check(_lib.fp8_block_quant_groups(ctypes.cast(arr, ctypes.c_void_p), len(groups), _stream(stream)),
            "fp8_block_quant_groups")
+
+
+class _AQGroup(ctypes.Structure):
+    """The layout of pulse_aq_group."""
+    _fields_ = [("src_offset", ctypes.c_int64 * 4), ("rows", ctypes.c_int64 * 4), ("nsrc", ctypes.c_int32),
+                ("quantise", ctypes.c_int32), ("cols", ctypes.c_int64), ("codes", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p)]
+
+
+class ApplyQuantPlan:
+    """A view's groups for pulse_apply_quant, resident on the device.  Holds
+    the output tensors it points into, so they live as long as the plan."""
+
+    def __init__(self, tensor, nblocks, n, outputs):
+        self.tensor, self.nblocks, self.n, self._outputs = tensor, nblocks, n, outputs
+
+
+def pulse_apply_quant_plan(groups, n, device="cuda"):
+    """groups: list of (sources, cols, codes, scales); sources a list (1..4) of
+    (element offset, rows) of row-major [rows, cols] matrices inside the view
+    of n elements, stacked in that order; codes [R * cols] uint8 and scales
+    [ceil(R/128) * ceil(cols/128)] float32 GPU tensors, or both None for a
+    group that is only patched.  The sources of all groups must tile [0, n)."""
+    arr = (_AQGroup * len(groups))()
+    outs = []
+    for g, (srcs, cols, codes, scales) in enumerate(groups):
+        if not 1 <= len(srcs) <= 4:
+            raise ValueError(f"group {g}: {len(srcs)} sources (1..4)")
+        R = 0
+        for i, (off, rows) in enumerate(srcs):
+            arr[g].src_offset[i] = int(off)
+            arr[g].rows[i] = int(rows)
+            R += int(rows)
+        arr[g].nsrc = len(srcs)
+        arr[g].cols = int(cols)
+        if (codes is None) != (scales is None):
+            raise ValueError(f"group {g}: codes and scales go together")
+        if codes is not None:
+            _need(codes, R * cols, f"groups[{g}].codes")
+            _need(scales, 4 * ((R + 127) // 128) * ((cols + 127) // 128), f"groups[{g}].scales")
+            arr[g].quantise = 1
+            arr[g].codes = _dev(codes, f"groups[{g}].codes", torch.uint8)
+            arr[g].scales = _dev(scales, f"groups[{g}].scales", torch.float32)
+            outs += [codes, scales]
+    nbytes = int(_lib.pulse_apply_quant_plan_bytes(len(groups)))
+    plan = torch.empty((max(nbytes, 16) + 15) // 16 * 16, dtype=torch.uint8, device=device)
+    nblocks = ctypes.c_int64(0)
+    _check(_lib.pulse_apply_quant_plan(ctypes.cast(arr, ctypes.c_void_p), len(groups), n, _dev(plan, "plan"),
+                                       plan.numel(), ctypes.byref(nblocks)), "pulse_apply_quant_plan")
+    return ApplyQuantPlan(plan, int(nblocks.value), n, outs)
+
+
+def pulse_apply_quant(b, patch_idx, patch_val, d_count, plan, d_status, ws, max_count=None, stream=None):
+    """The receiver's pass: the patch applied to the view b and the plan's
+    groups quantised to FP8 from the patched values, in one read of b."""
+    n = plan.n
+    max_count = patch_idx.numel() if max_count is None else max_count
+    _need(b, 2 * n, "b")
+    _need(patch_idx, 4 * max_count, "patch_idx")
+    _need(patch_val, 2 * max_count, "patch_val")
+    wsp, wsb = _ws(ws)
+    _check(_lib.pulse_apply_quant(
+        _dev(b, "b", _U16), n, _dev(patch_idx, "patch_idx", torch.int32), _dev(patch_val, "patch_val", _U16),
+        _dev(d_count, "d_count", torch.int64), max_count, _dev(plan.tensor, "plan"), plan.nblocks,
+        _dev(d_status, "d_status", torch.int32), wsp, wsb, _stream(stream)), "pulse_apply_quant")
 
 
 def fp8_view_delta(codes_old, codes_new, scales_old, scales_new, code_idx, code_val, d_code_count,

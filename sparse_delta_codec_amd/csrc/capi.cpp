@@ -57,6 +57,10 @@ int pulse_launch_apply_patch_tiled(uint16_t *, int64_t, const int32_t *, const u
                                    uint32_t *, hipStream_t);
 int pulse_launch_patch_tiles(const int32_t *, const int64_t *, int64_t, int64_t, int64_t *, hipStream_t);
 int pulse_launch_write_count(int64_t *, int64_t, hipStream_t);
+int64_t pulse_apply_quant_plan_size(int32_t);
+int pulse_build_apply_quant_plan(const void *, int32_t, int64_t, void *, int64_t, int64_t *);
+int pulse_launch_apply_quant(uint16_t *, int64_t, const int32_t *, const uint16_t *, const int64_t *, int64_t,
+                             const void *, int64_t, uint32_t *, int32_t *, hipStream_t);
 }
 
 namespace {
@@ -102,6 +106,7 @@ size_t pulse_workspace_bytes(int op, int64_t n, int64_t aux) {
     case PULSE_OP_CAST_DIFF_LZ4:
         if (aux != 16384 && aux != 32768 && aux != 65536) return 0;
         return pulse_cast_diff_lz4_ws_bytes(n, (int32_t)aux);
+    case PULSE_OP_APPLY_QUANT: return (size_t)(((n + 127) / 128 + 1) * 4 + 15) / 16 * 16;
     default: return 0;
     }
 }
@@ -423,3 +428,37 @@ int pulse_apply_patch_segments(const pulse_view *views, int32_t nseg, const int3
 
 }  // extern "C"
 
+
+extern "C" {
+
+int64_t pulse_apply_quant_plan_bytes(int32_t ngroups) { return pulse_apply_quant_plan_size(ngroups); }
+
+int pulse_apply_quant_plan(const pulse_aq_group *groups, int32_t ngroups, int64_t n, void *plan, int64_t plan_bytes,
+                           int64_t *nblocks) {
+    if (!groups || ngroups < 1 || !plan || !nblocks || n < 1) return PULSE_EINVAL;
+    if (n > kMaxIndexed) return PULSE_ERANGE;
+    if (!aligned16(plan)) return PULSE_EALIGN;
+    const int r = pulse_build_apply_quant_plan(groups, ngroups, n, plan, plan_bytes, nblocks);
+    switch (r) {
+    case 0: return PULSE_OK;
+    case -2: return PULSE_EALIGN;
+    case -3: return PULSE_ERANGE;
+    case -4: return PULSE_EWORKSPACE;
+    case -5: return PULSE_EHIP;
+    default: return PULSE_EINVAL;
+    }
+}
+
+int pulse_apply_quant(uint16_t *b, int64_t n, const int32_t *patch_idx, const uint16_t *patch_val,
+                      const int64_t *d_count, int64_t max_count, const void *plan, int64_t nblocks,
+                      uint32_t *d_status, void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (!b || !patch_idx || !patch_val || !d_count || !plan || !d_status || n < 1 || max_count < 1 || nblocks < 1)
+        return PULSE_EINVAL;
+    if (!aligned16(b) || !aligned16(plan)) return PULSE_EALIGN;
+    if (n > kMaxIndexed || max_count > kMaxIndexed || nblocks > kMaxIndexed) return PULSE_ERANGE;
+    if (!ws || ws_bytes < pulse_workspace_bytes(PULSE_OP_APPLY_QUANT, n, 0)) return PULSE_EWORKSPACE;
+    return pulse_launch_apply_quant(b, n, patch_idx, patch_val, d_count, max_count, plan, nblocks, d_status,
+                                    static_cast<int32_t *>(ws), stream);
+}
+
+}  // extern "C"

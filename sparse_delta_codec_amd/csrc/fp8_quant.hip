@@ -16,6 +16,10 @@
 // amax reduction and the quantisation).
 #include "device.hpp"
 
+#include <algorithm>
+#include <utility>
+#include <vector>
+
 namespace pulse {
 
 constexpr int FQ_MAXSRC = 8;
@@ -45,47 +49,39 @@ struct QBlock {
     float *scales;
 };
 
-template <int MAXS>
-__device__ __forceinline__ void quant_block(const QBlock &a, int64_t br, int64_t bc, int64_t e, uint32_t *s_red) {
+// Thread t of the 256-thread workgroup holds v[i] = columns [8 (t % 16), +8)
+// of row t / 16 + 16 i of a 128x128 block (ok[i]: the piece lies inside the
+// matrix).  Block amax, the scale (written by thread 0 to *scale) and the
+// codes of the thread's pieces (piece i to codes_row0 + (t / 16 + 16 i) * cols,
+// codes_row0 being the code of the block's first row at the thread's first
+// column).  s_red[w * red_stride], w < 4: LDS words for the waves' maxima,
+// free when the call starts.
+__device__ __forceinline__ void quant_regs(const uint4 (&v)[8], const bool (&ok)[8], uint32_t *s_red,
+                                           int red_stride, uint8_t *codes_row0, int64_t cols, float *scale) {
     const int t = threadIdx.x;
-    const int rg = t >> 4, seg = t & 15;
-    const int64_t col = bc * 128 + seg * 8;
-    const bool col_ok = col < a.cols;  // cols is a multiple of 8
-
-    uint4 v[8];
-    bool ok[8];
+    const int rg = t >> 4;
     uint32_t amax = 0;  // max |x| as BF16 magnitude bits (ordered like the values)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const int64_t r = br * 128 + rg + 16 * i;
-        ok[i] = col_ok && r < a.R;
-        v[i] = make_uint4(0, 0, 0, 0);
-        if (ok[i]) {
-            int s = 0;
+        if (!ok[i]) continue;
+        const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
-            for (int k = 1; k < MAXS; ++k)
-                if (k < a.nsrc && r >= a.row0[k]) s = k;
-            const uint16_t *p = a.src[s] + (a.bstride ? e * a.bstride[s] : 0) + (r - a.row0[s]) * a.cols + col;
-            v[i] = *reinterpret_cast<const uint4 *>(p);
-            const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint32_t lo = w[k] & 0x7FFFu, hi = (w[k] >> 16) & 0x7FFFu;
-                amax = lo > amax ? lo : amax;
-                amax = hi > amax ? hi : amax;
-            }
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t lo = w[k] & 0x7FFFu, hi = (w[k] >> 16) & 0x7FFFu;
+            amax = lo > amax ? lo : amax;
+            amax = hi > amax ? hi : amax;
         }
     }
     amax = wave_reduce_max(amax);
-    if (lane_id() == 0) s_red[wave_id()] = amax;
+    if (lane_id() == 0) s_red[wave_id() * red_stride] = amax;
     __syncthreads();
     amax = s_red[0];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) amax = s_red[w] > amax ? s_red[w] : amax;
+    for (int w = 1; w < 4; ++w) amax = s_red[w * red_stride] > amax ? s_red[w * red_stride] : amax;
 
     const float amax_f = __uint_as_float(amax << 16);
     const float s = amax == 0 ? 1.0f : amax_f / 448.0f;  // IEEE division
-    if (t == 0) a.scales[(e * ((a.R + 127) / 128) + br) * a.nbc + bc] = s;
+    if (t == 0) *scale = s;
 
     // q = fl32(|x| / s) without a division per element: with y = fl32(1/ss)
     // (IEEE, once), q0 = fl32(xs*y), r = xs - ss*q0 (exact with an FMA) and
@@ -110,7 +106,6 @@ __device__ __forceinline__ void quant_block(const QBlock &a, int64_t br, int64_t
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         if (!ok[i]) continue;
-        const int64_t r = br * 128 + rg + 16 * i;
         const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
         uint32_t packed[2];
 #pragma unroll
@@ -124,8 +119,35 @@ __device__ __forceinline__ void quant_block(const QBlock &a, int64_t br, int64_t
                                 (w1 & 0x80000000u);
             packed[h] = (uint32_t)c | sg;
         }
-        *reinterpret_cast<uint2 *>(a.codes + (e * a.R + r) * a.cols + col) = make_uint2(packed[0], packed[1]);
+        *reinterpret_cast<uint2 *>(codes_row0 + (int64_t)(rg + 16 * i) * cols) = make_uint2(packed[0], packed[1]);
     }
+}
+
+template <int MAXS>
+__device__ __forceinline__ void quant_block(const QBlock &a, int64_t br, int64_t bc, int64_t e, uint32_t *s_red) {
+    const int t = threadIdx.x;
+    const int rg = t >> 4, seg = t & 15;
+    const int64_t col = bc * 128 + seg * 8;
+    const bool col_ok = col < a.cols;  // cols is a multiple of 8
+
+    uint4 v[8];
+    bool ok[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int64_t r = br * 128 + rg + 16 * i;
+        ok[i] = col_ok && r < a.R;
+        v[i] = make_uint4(0, 0, 0, 0);
+        if (ok[i]) {
+            int s = 0;
+#pragma unroll
+            for (int k = 1; k < MAXS; ++k)
+                if (k < a.nsrc && r >= a.row0[k]) s = k;
+            const uint16_t *p = a.src[s] + (a.bstride ? e * a.bstride[s] : 0) + (r - a.row0[s]) * a.cols + col;
+            v[i] = *reinterpret_cast<const uint4 *>(p);
+        }
+    }
+    quant_regs(v, ok, s_red, 1, a.codes + (e * a.R + br * 128) * a.cols + col, a.cols,
+               a.scales + (e * ((a.R + 127) / 128) + br) * a.nbc + bc);
 }
 
 __global__ __launch_bounds__(256) void k_fp8_block_quant(QuantArgs a) {
@@ -169,6 +191,298 @@ __global__ __launch_bounds__(256) void k_fp8_block_quant_groups(QuantGroupsArgs 
     const QBlock q{G.src, G.row0, nullptr, G.nsrc, G.cols, G.R, G.nbc, G.codes, G.scales};
     quant_block<FQ_GSRC>(q, lb / G.nbc, lb % G.nbc, 0, s_red);
 }
+
+// ---- the receiver's pass: patch apply and FP8 quantisation in one read ----------
+// The receiver overrides the patch's positions in its BF16 view and quantises
+// the new view for FP8 serving.  Done apart, the apply's 2-byte stores leave
+// three quarters of the view's 32-byte sectors partially written and the
+// quantisation reads the whole view again; here one workgroup per 128x128
+// block reads the block once into an LDS image, writes the block's entries
+// there, stores back the 16-byte pieces that changed and quantises from the
+// patched values.  A group is a stack of sources that are row-major matrices
+// inside the view (FP8 groups), or a source that is only patched (norms,
+// biases).  The entries of a block row are found through the patch's segment
+// index seg_first[s] = first entry with index >= 128 s; the groups' sources
+// tile the view, so every entry inside it is applied by exactly one workgroup.
+constexpr int kSegLog = 7;
+
+struct AQGroupDev {
+    int64_t off[FQ_GSRC];  // element offset of each source in the view
+    int64_t row0[FQ_GSRC + 1];
+    int64_t cols, R, nbc;
+    uint8_t *codes;  // [R][cols], or unused when quant == 0
+    float *scales;   // [ceil(R/128)][nbc]
+    int32_t nsrc;
+    int32_t quant;
+};
+
+struct AQPlanHeader {
+    int64_t n, ngroups, nblocks, reserved;
+};
+
+// plan: header, block0[ngroups + 1] (rounded up to 16 bytes), groups[ngroups]
+__host__ __device__ inline int64_t aq_groups_offset(int64_t ng) {
+    return (int64_t)sizeof(AQPlanHeader) + ((8 * (ng + 1) + 15) / 16) * 16;
+}
+
+// Segment index of an ascending patch: seg_first[s] for s in (segment of
+// entry k - 1, segment of entry k] is k (entry `count` closes the index up to
+// nseg).  Eight consecutive entries a lane (two 16-byte loads); a gap of more
+// than 8 segments (a long unchanged run) is filled by the whole wave, 64
+// stores an instruction.  An index outside [0, n), or one not above its
+// predecessor, sets PULSE_DS_BADINDEX.
+constexpr int kSegPer = 8;
+
+__global__ __launch_bounds__(256) void k_patch_segments(const int32_t *__restrict__ idx, const int64_t *d_count,
+                                                        int64_t max_count, int64_t n, int32_t *__restrict__ seg_first,
+                                                        uint32_t *d_status) {
+    int64_t count = *d_count;
+    if (count > max_count) count = max_count;
+    if (count < 0) count = 0;
+    const int64_t nseg = (n + 127) >> kSegLog;
+    auto seg_of = [&](int64_t i) -> int64_t { return i < 0 ? 0 : (i >= n ? nseg : i >> kSegLog); };
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x * kSegPer;
+    bool bad = false;
+    // base is uniform across the wave, so every lane runs every iteration
+    for (int64_t base = ((int64_t)blockIdx.x * blockDim.x + wave_id() * kWave) * kSegPer; base <= count;
+         base += stride) {
+        const int64_t k0 = base + lane_id() * kSegPer;
+        int64_t iv[kSegPer + 1];  // entries k0 - 1 .. k0 + 7 (n past the count)
+        iv[0] = k0 > 0 && k0 - 1 < count ? (int64_t)idx[k0 - 1] : -1;
+        if (k0 + kSegPer <= count && (reinterpret_cast<uintptr_t>(idx + k0) & 15) == 0) {
+            const int4 a = *reinterpret_cast<const int4 *>(idx + k0);
+            const int4 c = *reinterpret_cast<const int4 *>(idx + k0 + 4);
+            iv[1] = a.x; iv[2] = a.y; iv[3] = a.z; iv[4] = a.w;
+            iv[5] = c.x; iv[6] = c.y; iv[7] = c.z; iv[8] = c.w;
+        } else {
+#pragma unroll
+            for (int j = 0; j < kSegPer; ++j) iv[j + 1] = k0 + j < count ? (int64_t)idx[k0 + j] : n;
+        }
+#pragma unroll
+        for (int j = 0; j < kSegPer; ++j) {
+            const int64_t k = k0 + j;
+            int64_t a = 0, z = -1;  // the segments [a, z] take the value k
+            if (k <= count) {
+                const int64_t i = iv[j + 1], ip = iv[j];
+                if (k < count) bad |= i < 0 || i >= n || (k > 0 && i <= ip);
+                a = (k == 0 ? -1 : seg_of(ip)) + 1;
+                z = seg_of(i);
+            }
+            const bool wide = z - a >= 8;
+            if (!wide)
+                for (int64_t s = a; s <= z; ++s) seg_first[s] = (int32_t)k;
+            uint64_t m = __ballot(wide);
+            while (m) {
+                const int l = __builtin_ctzll(m);
+                m &= m - 1;
+                const int64_t la = __shfl((long long)a, l), lz = __shfl((long long)z, l);
+                const int32_t lk = (int32_t)(base + l * kSegPer + j);
+                for (int64_t s = la + lane_id(); s <= lz; s += kWave) seg_first[s] = lk;
+            }
+        }
+    }
+    if (__ballot(bad) && lane_id() == 0) or_agent32(d_status, 2u /*PULSE_DS_BADINDEX*/);
+}
+
+// One block's description, uniform across the workgroup, held in plain
+// scalars (a struct kept in a loop is left in private memory, and selects
+// among its fields become indexed loads from there).  Every offset and size
+// inside a view is below 2^31 (int32 patch indices), so 32 bits suffice.
+#define AQ_FIELDS(X)                                                                                                  \
+    X(int32_t, o0) X(int32_t, o1) X(int32_t, o2) X(int32_t, o3) X(int32_t, r1) X(int32_t, r2) X(int32_t, r3)        \
+    X(int32_t, cols) X(int32_t, R) X(int32_t, nbc) X(int32_t, br) X(int32_t, bc) X(int32_t, quant)                   \
+    X(uint8_t *, codes) X(float *, scales)
+
+// The block blk of the plan: its group (last g with block0[g] <= blk) and its
+// place in it.
+#define AQ_LOCATE(P, blk)                                                                                             \
+    do {                                                                                                              \
+        const int64_t *block0_ = reinterpret_cast<const int64_t *>(plan + sizeof(AQPlanHeader));                     \
+        int64_t lo_ = 0, hi_ = ng - 1;                                                                                \
+        while (lo_ < hi_) {                                                                                           \
+            const int64_t mid_ = (lo_ + hi_ + 1) >> 1;                                                                \
+            if (block0_[mid_] <= (blk)) lo_ = mid_;                                                                   \
+            else hi_ = mid_ - 1;                                                                                      \
+        }                                                                                                             \
+        const AQGroupDev &G_ = reinterpret_cast<const AQGroupDev *>(plan + aq_groups_offset(ng))[lo_];               \
+        P##o0 = (int32_t)G_.off[0];                                                                                   \
+        P##o1 = (int32_t)G_.off[1];                                                                                   \
+        P##o2 = (int32_t)G_.off[2];                                                                                   \
+        P##o3 = (int32_t)G_.off[3];                                                                                   \
+        P##r1 = (int32_t)G_.row0[1];                                                                                  \
+        P##r2 = (int32_t)G_.row0[2];                                                                                  \
+        P##r3 = (int32_t)G_.row0[3];                                                                                  \
+        P##cols = (int32_t)G_.cols;                                                                                   \
+        P##R = (int32_t)G_.R;                                                                                         \
+        P##nbc = (int32_t)G_.nbc;                                                                                     \
+        const int32_t lb_ = (int32_t)((blk) - block0_[lo_]);                                                          \
+        P##br = lb_ / P##nbc;                                                                                         \
+        P##bc = lb_ - P##br * P##nbc;                                                                                 \
+        P##quant = G_.quant;                                                                                          \
+        P##codes = G_.codes;                                                                                          \
+        P##scales = G_.scales;                                                                                        \
+    } while (0)
+
+// View index of (row r < R, column c) of a stack of up to four sources; a
+// source past nsrc starts at row R (as the plan sets it), so it is never
+// picked.  Selects only: no indexed load, no branch.
+__device__ __forceinline__ int32_t aq_elem(int32_t o0, int32_t o1, int32_t o2, int32_t o3, int32_t r1, int32_t r2,
+                                           int32_t r3, int32_t cols, int32_t r, int32_t c) {
+    const bool in1 = r >= r1, in2 = r >= r2, in3 = r >= r3;
+    const int32_t o = in3 ? o3 : (in2 ? o2 : (in1 ? o1 : o0));
+    const int32_t r0 = in3 ? r3 : (in2 ? r2 : (in1 ? r1 : 0));
+    return o + (r - r0) * cols + c;
+}
+
+// Persistent: each XCD (workgroups go to the 8 XCDs in turn) takes a
+// contiguous run of blocks, which its workgroups share in turn, so that
+// neighbouring column blocks (the same rows, whose entries share lines of the
+// patch and of its index) meet in one L2.  A workgroup looks up the next
+// block's entry range while it patches and quantises the current block, so a
+// block's own loads (the view and the entries) go out together.
+constexpr int kAqMaxGroups = 320 * 8;
+
+__global__ __launch_bounds__(256, 4) void k_apply_quant(uint16_t *__restrict__ b, int64_t n,
+                                                       const int32_t *__restrict__ idx,
+                                                       const uint16_t *__restrict__ val,
+                                                       const int64_t *__restrict__ d_count, int64_t max_count,
+                                                       const int32_t *__restrict__ seg_first,
+                                                       const uint8_t *__restrict__ plan, int64_t nblk,
+                                                       uint32_t *d_status) {
+    static_assert(FQ_GSRC == 4, "four sources a group");
+    __shared__ uint4 img[128 * 16];  // the block, 256 bytes a row
+    const AQPlanHeader *hdr = reinterpret_cast<const AQPlanHeader *>(plan);
+    const int t = threadIdx.x;
+    if (hdr->n != n || hdr->nblocks != nblk) {  // a plan made for another view
+        if (blockIdx.x == 0 && t == 0) or_agent32(d_status, 8u /*PULSE_DS_WORKSPACE*/);
+        return;
+    }
+    const int64_t ng = hdr->ngroups;
+    const int64_t x = blockIdx.x % 8, per = gridDim.x / 8, q = nblk / 8, rem = nblk % 8;
+    const int64_t x1 = x * q + (x < rem ? x : rem) + q + (x < rem ? 1 : 0);
+    int64_t blk = x * q + (x < rem ? x : rem) + blockIdx.x / 8;
+    if (blk >= x1) return;
+
+    int32_t count;
+    {
+        int64_t c = *d_count;
+        c = c > max_count ? max_count : c;
+        count = (int32_t)(c < 0 ? 0 : c);
+    }
+    const int rl = t >> 1, h = t & 1;   // entries: block row rl, alternate entries
+    const int rg = t >> 4, seg = t & 15; // view: rows rg + 16 i, columns [8 seg, +8)
+
+#define AQ_DECL(T, f) T c_##f; T n_##f;
+    AQ_FIELDS(AQ_DECL)
+#undef AQ_DECL
+#define ELEM(P, r, c) aq_elem(P##o0, P##o1, P##o2, P##o3, P##r1, P##r2, P##r3, P##cols, (r), (c))
+    // the entry range of row rl of a block: its first element and the index
+    // words around it
+#define LOOKUP(P, e, sf0, sf1)                                                                                        \
+    do {                                                                                                              \
+        const int32_t len_ = P##cols - P##bc * 128 < 128 ? P##cols - P##bc * 128 : 128;                              \
+        e = ELEM(P, P##br * 128 + rl < P##R ? P##br * 128 + rl : P##R - 1, P##bc * 128);                               \
+        sf0 = seg_first[e >> kSegLog];                                                                                \
+        sf1 = seg_first[((e + len_ - 1) >> kSegLog) + 1];                                                             \
+    } while (0)
+
+    AQ_LOCATE(c_, blk);
+    int32_t e, sf0, sf1;
+    LOOKUP(c_, e, sf0, sf1);
+
+    for (;;) {
+        const int32_t col = c_bc * 128 + seg * 8;
+        const bool col_ok = col < c_cols;
+        const int32_t len = c_cols - c_bc * 128 < 128 ? c_cols - c_bc * 128 : 128;
+        // The block's pieces: a piece outside the matrix reads the last row or
+        // the first column instead (never written back nor quantised), so the
+        // loads are unconditional and all in flight at once.
+        uint4 v[8];
+        bool ok[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int32_t r = c_br * 128 + rg + 16 * i;
+            ok[i] = col_ok && r < c_R;
+            v[i] = *reinterpret_cast<const uint4 *>(b + ELEM(c_, r < c_R ? r : c_R - 1, col_ok ? col : 0));
+        }
+        // the row's first 16 entries (8 a thread); past the row's last entry
+        // a thread reads entry 0 (the patch buffer holds at least one) and
+        // drops it
+        const bool row_ok = c_br * 128 + rl < c_R;
+        int32_t k0 = row_ok ? sf0 : 0, k1 = row_ok ? sf1 : 0;
+        k0 = k0 < 0 ? 0 : (k0 > count ? count : k0);
+        k1 = k1 < k0 ? k0 : (k1 > count ? count : k1);
+        int32_t ii[8];
+        uint16_t vv[8];
+#pragma unroll
+        for (int qq = 0; qq < 8; ++qq) {
+            const int32_t kk = k0 + h + 2 * qq;
+            const int32_t kc = kk < k1 ? kk : 0;
+            const int32_t xi = idx[kc];
+            const uint16_t yv = val[kc];
+            ii[qq] = kk < k1 ? xi : -1;
+            vv[qq] = yv;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) img[(rg + 16 * i) * 16 + seg] = v[i];
+        __syncthreads();
+
+        // the next block and its entry range (the current one again at the end)
+        const int64_t nb = blk + per;
+        const bool more = nb < x1;
+        AQ_LOCATE(n_, more ? nb : blk);
+        int32_t ne, nsf0, nsf1;
+        LOOKUP(n_, ne, nsf0, nsf1);
+
+        uint16_t *row = reinterpret_cast<uint16_t *>(img) + rl * 128;
+#pragma unroll
+        for (int qq = 0; qq < 8; ++qq) {
+            const int32_t rel = ii[qq] - e;
+            if (ii[qq] >= 0 && rel >= 0 && rel < len) row[rel] = vv[qq];
+        }
+        for (int32_t k = k0 + h + 16; k < k1; k += 16) {  // rows with more than 16 entries
+#pragma unroll
+            for (int qq = 0; qq < 8; ++qq) {
+                const int32_t kk = k + 2 * qq;
+                ii[qq] = kk < k1 ? idx[kk] : -1;
+                vv[qq] = kk < k1 ? val[kk] : 0;
+            }
+#pragma unroll
+            for (int qq = 0; qq < 8; ++qq) {
+                const int32_t rel = ii[qq] - e;
+                if (ii[qq] >= 0 && rel >= 0 && rel < len) row[rel] = vv[qq];
+            }
+        }
+        __syncthreads();
+
+        // the patched block: written back whole (a block row is two full
+        // lines) and quantised
+        uint4 u[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            u[i] = img[(rg + 16 * i) * 16 + seg];
+            if (ok[i]) *reinterpret_cast<uint4 *>(b + ELEM(c_, c_br * 128 + rg + 16 * i, col)) = u[i];
+        }
+        if (c_quant) {
+            __syncthreads();  // the image is read; its first words hold the waves' maxima
+            quant_regs(u, ok, reinterpret_cast<uint32_t *>(img), 1, c_codes + (int64_t)c_br * 128 * c_cols + col,
+                       c_cols, c_scales + (int64_t)c_br * c_nbc + c_bc);
+        }
+        if (!more) break;
+        __syncthreads();  // the image (and the maxima) read before the next block is stored
+        blk = nb;
+#define AQ_NEXT(T, f) c_##f = n_##f;
+        AQ_FIELDS(AQ_NEXT)
+#undef AQ_NEXT
+        e = ne;
+        sf0 = nsf0;
+        sf1 = nsf1;
+    }
+#undef LOOKUP
+#undef ELEM
+}
+#undef AQ_LOCATE
+#undef AQ_FIELDS
 
 }  // namespace pulse
 
@@ -236,5 +550,103 @@ extern "C" int pulse_launch_fp8_block_quant_groups(const void *groups, int32_t n
     a.ng = ngroups;
     if (total > 0x7FFFFFFF) return -3;
     k_fp8_block_quant_groups<<<dim3((unsigned)total), dim3(256), 0, stream>>>(a);
+    return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+// ---- the receiver's pass ------------------------------------------------------
+struct AQGroupHost {  // the layout of pulse_aq_group
+    int64_t src_offset[4];
+    int64_t rows[4];
+    int32_t nsrc;
+    int32_t quantise;
+    int64_t cols;
+    uint8_t *codes;
+    float *scales;
+};
+
+extern "C" int64_t pulse_apply_quant_plan_size(int32_t ngroups) {
+    if (ngroups < 1) return 0;
+    return aq_groups_offset(ngroups) + (int64_t)ngroups * (int64_t)sizeof(AQGroupDev);
+}
+
+// Checks the groups (-1 bad value, -2 misaligned) and that their sources tile
+// [0, n); writes the plan to device memory (synchronously).
+extern "C" int pulse_build_apply_quant_plan(const void *groups, int32_t ngroups, int64_t n, void *plan,
+                                            int64_t plan_bytes, int64_t *nblocks) {
+    const AQGroupHost *h = static_cast<const AQGroupHost *>(groups);
+    const int64_t need = pulse_apply_quant_plan_size(ngroups);
+    if (need == 0 || !groups || !plan || !nblocks || n < 1) return -1;
+    if (plan_bytes < need) return -4;
+    std::vector<uint8_t> host((size_t)need, 0);
+    AQPlanHeader *hdr = reinterpret_cast<AQPlanHeader *>(host.data());
+    int64_t *block0 = reinterpret_cast<int64_t *>(host.data() + sizeof(AQPlanHeader));
+    AQGroupDev *gd = reinterpret_cast<AQGroupDev *>(host.data() + aq_groups_offset(ngroups));
+    std::vector<std::pair<int64_t, int64_t>> spans;  // (offset, length) of every source
+    int64_t total = 0;
+    for (int g = 0; g < ngroups; ++g) {
+        const AQGroupHost &q = h[g];
+        if (q.nsrc < 1 || q.nsrc > FQ_GSRC || q.cols < 8 || q.cols % 8 != 0) return -1;
+        if (q.quantise != 0 && q.quantise != 1) return -1;
+        if (q.quantise && (!q.codes || !q.scales)) return -1;
+        if (q.quantise && (reinterpret_cast<uintptr_t>(q.codes) % 8 != 0 ||
+                           reinterpret_cast<uintptr_t>(q.scales) % 4 != 0))
+            return -2;
+        AQGroupDev &G = gd[g];
+        int64_t R = 0;
+        for (int i = 0; i < q.nsrc; ++i) {
+            if (q.rows[i] < 1 || q.src_offset[i] < 0) return -1;
+            if (q.src_offset[i] % 8 != 0) return -2;
+            if (q.rows[i] > n / q.cols || q.src_offset[i] > n - q.rows[i] * q.cols) return -1;
+            spans.emplace_back(q.src_offset[i], q.rows[i] * q.cols);
+            G.off[i] = q.src_offset[i];
+            G.row0[i] = R;
+            R += q.rows[i];
+        }
+        for (int i = q.nsrc; i < FQ_GSRC; ++i) {
+            G.off[i] = G.off[0];
+            G.row0[i] = R;
+        }
+        G.row0[FQ_GSRC] = R;
+        G.cols = q.cols;
+        G.R = R;
+        G.nbc = (q.cols + 127) / 128;
+        G.codes = q.codes;
+        G.scales = q.scales;
+        G.nsrc = q.nsrc;
+        G.quant = q.quantise;
+        block0[g] = total;
+        total += ((R + 127) / 128) * G.nbc;
+    }
+    block0[ngroups] = total;
+    if (total > 0x7FFFFFFF) return -3;
+    std::sort(spans.begin(), spans.end());
+    int64_t end = 0;
+    for (const auto &sp : spans) {
+        if (sp.first != end) return -1;  // a gap or an overlap
+        end += sp.second;
+    }
+    if (end != n) return -1;
+    hdr->n = n;
+    hdr->ngroups = ngroups;
+    hdr->nblocks = total;
+    if (hipMemcpy(plan, host.data(), (size_t)need, hipMemcpyHostToDevice) != hipSuccess) return -5;
+    *nblocks = total;
+    return 0;
+}
+
+extern "C" int pulse_launch_apply_quant(uint16_t *b, int64_t n, const int32_t *idx, const uint16_t *val,
+                                        const int64_t *d_count, int64_t max_count, const void *plan, int64_t nblocks,
+                                        uint32_t *d_status, int32_t *seg_first, hipStream_t stream) {
+    int64_t blocks = (max_count + 1 + 256 * kSegPer - 1) / (256 * kSegPer);
+    if (blocks > 256 * 8) blocks = 256 * 8;
+    k_patch_segments<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(idx, d_count, max_count, n, seg_first,
+                                                                       d_status);
+    if (hipGetLastError() != hipSuccess) return -5;
+    if (nblocks < 1) return 0;
+    int64_t per = (nblocks + 7) / 8;  // workgroups per XCD
+    if (per > kAqMaxGroups / 8) per = kAqMaxGroups / 8;
+    k_apply_quant<<<dim3((unsigned)(8 * per)), dim3(256), 0, stream>>>(b, n, idx, val, d_count, max_count, seg_first,
+                                                                       static_cast<const uint8_t *>(plan), nblocks,
+                                                                       d_status);
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }

@@ -36,7 +36,8 @@ def test_header_declares_the_codec_calls():
     for name in ("pulse_cast_diff", "pulse_compact", "pulse_apply_patch", "xor_mask_apply",
                  "lz4_encode_blocks", "lz4_decode_blocks", "lz4_decode_parse", "lz4_decode_apply",
                  "fp8_block_quant", "fp8_block_quant_groups", "pulse_cast_diff_lz4", "pulse_patch_tiles",
-                 "pulse_apply_patch_tiled", "pulse_workspace_bytes",
+                 "pulse_apply_patch_tiled", "pulse_apply_quant_plan_bytes", "pulse_apply_quant_plan",
+                 "pulse_apply_quant", "pulse_workspace_bytes",
                  "pulse_workspace_init", "pulse_status_string", "pulse_version"):
         assert name in fns, name
 
@@ -67,6 +68,8 @@ def test_workspace_sizes(lib):
     # fused sender pass: header + two status words per mask block
     assert ws(9, 32768 * 3 + 1, 65536) == 256 + 2 * 4 * 8
     assert ws(9, 1000, 1000) == 0
+    # receiver's pass: one int32 segment start per 128 elements, plus the closing one
+    assert ws(10, 128 * 5, 0) == 32 and ws(10, 128 * 5 + 1, 0) == 32 and ws(10, 128 * 8, 0) == 48
 
 
 V = ctypes.c_void_p
@@ -225,3 +228,62 @@ def test_segment_tiles_and_list_call_errors(lib):
     ap = lib.pulse_apply_patch_segments
     ap.argtypes = [V, ctypes.c_int32, V, V, V, I64, V, V]
     assert ap(al, 0, al, al, al, 10, al, None) == EINVAL
+
+
+def test_receiver_pass_plan_and_argument_errors(lib):
+    """pulse_apply_quant_plan checks every group and that the sources tile the
+    view before it copies anything; pulse_apply_quant checks its arguments."""
+    import sparse_delta_codec_amd as pk  # the binding's layout of pulse_aq_group
+    al = V(0x10000)
+    mis = V(0x10002)
+    pb = lib.pulse_apply_quant_plan_bytes
+    pb.argtypes, pb.restype = [ctypes.c_int32], I64
+    assert pb(0) == 0 and pb(1) > 0 and pb(9) > pb(8) + ctypes.sizeof(pk._AQGroup)
+    assert ctypes.sizeof(pk._AQGroup) == 4 * 8 + 4 * 8 + 4 + 4 + 8 + 8 + 8
+    mk = lib.pulse_apply_quant_plan
+    mk.argtypes = [V, ctypes.c_int32, I64, V, I64, V]
+    nb = I64(0)
+
+    def plan(groups, n, plan_bytes=1 << 20, ptr=al):
+        arr = (pk._AQGroup * len(groups))()
+        for g, (srcs, cols, quant) in enumerate(groups):
+            for i, (off, rows) in enumerate(srcs):
+                arr[g].src_offset[i], arr[g].rows[i] = off, rows
+            arr[g].nsrc, arr[g].cols, arr[g].quantise = len(srcs), cols, quant
+            arr[g].codes, arr[g].scales = (0x20000, 0x30000) if quant else (None, None)
+        return mk(ctypes.cast(arr, V), len(groups), n, ptr, plan_bytes, ctypes.byref(nb))
+
+    qkv = ([(0, 4), (512, 2), (768, 2)], 128, 1)    # 1024 elements in three sources
+    mid = ([(1024, 1)], 16, 0)
+    assert plan([qkv], 1040) == EINVAL                                  # [1024, 1040) not covered (gap)
+    assert plan([qkv, mid], 1032) == EINVAL                             # past the view
+    assert plan([qkv, mid, ([(1032, 1)], 8, 0)], 1040) == EINVAL        # overlap
+    assert plan([([(0, 4), (520, 2), (776, 2)], 128, 1), ([(1032, 1)], 16, 0)], 1048) == EINVAL  # gap in a stack
+    assert plan([([(0, 1)], 8, 0), ([(12, 1)], 8, 0)], 20) == EALIGN   # offset % 8
+    assert plan([([(0, 1)], 1036, 0), ([(1036, 1)], 4, 0)], 1040) == EINVAL    # cols % 8
+    assert plan([([(0, 1)], 1028, 0), ([(1028, 1)], 12, 0)], 1040) == EINVAL   # cols % 8
+    assert plan([([(0, 1)], 1024, 0), ([(1024, 1)], 16, 0)], 1040, ptr=mis) == EALIGN
+    assert plan([([(0, 1)], 4, 0)], 4) == EINVAL                         # cols 4
+    assert plan([qkv, mid], 1040, plan_bytes=16) == EWORKSPACE
+    assert plan([qkv, mid], 1 << 31) == ERANGE
+    assert plan([([(0, 0)], 8, 0)], 8) == EINVAL                        # no rows
+    assert mk(None, 1, 8, al, 1 << 20, ctypes.byref(nb)) == EINVAL
+    arr = (pk._AQGroup * 1)()
+    arr[0].src_offset[0], arr[0].rows[0], arr[0].nsrc, arr[0].cols, arr[0].quantise = 0, 1, 1, 8, 1
+    assert mk(ctypes.cast(arr, V), 1, 8, al, 1 << 20, ctypes.byref(nb)) == EINVAL   # quantised, no outputs
+    arr[0].codes, arr[0].scales = 0x20004, 0x30000
+    assert mk(ctypes.cast(arr, V), 1, 8, al, 1 << 20, ctypes.byref(nb)) == EALIGN   # codes 8-byte aligned
+    arr[0].quantise = 2
+    assert mk(ctypes.cast(arr, V), 1, 8, al, 1 << 20, ctypes.byref(nb)) == EINVAL
+    arr[0].quantise, arr[0].nsrc = 0, 5
+    assert mk(ctypes.cast(arr, V), 1, 8, al, 1 << 20, ctypes.byref(nb)) == EINVAL   # five sources
+    aq = lib.pulse_apply_quant
+    aq.argtypes = [V, I64, V, V, V, I64, V, I64, V, V, ctypes.c_size_t, V]
+    args = [al, 1000, al, al, al, 10, al, 3, al, al, 1 << 20, None]
+    assert aq(None, *args[1:]) == EINVAL
+    assert aq(*args[:6], None, *args[7:]) == EINVAL                    # no plan
+    assert aq(*args[:7], 0, *args[8:]) == EINVAL                       # no blocks
+    assert aq(*args[:5], 0, *args[6:]) == EINVAL                       # empty patch buffers
+    assert aq(mis, *args[1:]) == EALIGN and aq(*args[:6], mis, *args[7:]) == EALIGN
+    assert aq(al, 1 << 31, *args[2:]) == ERANGE
+    assert aq(*args[:10], 16, None) == EWORKSPACE and aq(*args[:9], None, 1 << 20, None) == EWORKSPACE
