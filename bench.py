@@ -12,17 +12,16 @@ tensors (embed | 16 x four decoder layers | final norm + lm_head):
                               (--separate-encode: pulse_cast_diff, then
                               lz4_encode_blocks over old and new)
   receiver  lz4_decode_parse  the serial token-chain parse of every block, on a
-                              second stream, beside the next two (--schedule)
-  receiver  pulse_apply_patch scatter the patch into the receiver's view (v0 -> v1)
-                              (--apply-tiled: pulse_apply_patch_tiled with the
-                              tile index the sender writes)
-  receiver  fp8_block_quant_groups  stacked [q;k;v], o, stacked [gate;up],
-                              down, embed, lm_head -> E4M3 + FP32 128x128
-                              scales, up to 8 groups per launch
-                              (--quant-per-group: one fp8_block_quant each;
-                              --receiver fused: pulse_apply_quant, the patch
-                              apply and the quantisation in one pass per
-                              128x128 block)
+                              second stream, beside the next one (--schedule)
+  receiver  pulse_apply_quant one pass per 128x128 block: the patch applied to the
+                              receiver's view (v0 -> v1) and the stacked [q;k;v],
+                              o, [gate;up], down, embed, lm_head groups
+                              quantised to E4M3 + FP32 scales from the patched
+                              values; norms and biases only patched
+                              (--receiver separate: pulse_apply_patch, then
+                              fp8_block_quant_groups, up to 8 groups a launch;
+                              --apply-tiled, --quant-per-group select their
+                              variants)
   receiver  lz4_decode_apply  rebuild + XOR in place into the receiver's view
                               (--schedule serial: one lz4_decode_blocks call on
                               the main stream, no second stream)
@@ -48,8 +47,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "weights processed GB/s (encode+apply) and % of MI355X HBM peak, 1 GPU"
 SCHEDULES = {
-    "ahead": "parse of chunk c on a second stream beside the encode of chunk c + 1 and the receiver's pass of "
-             "chunk c; decode apply on the main stream",
+    "ahead": "parse of chunk c on a second stream beside the encode of chunk c + 1; the receiver's pass and "
+             "the decode apply of chunk c on the main stream after it",
     "side": "parse on a second stream beside the receiver's pass of the same chunk, apply on the main stream",
     "pipeline": "encode and parse of chunk c on a second stream while the main stream receives and decodes "
                 "chunk c - 1",
@@ -75,12 +74,12 @@ def parse():
                         "alone, slower beside the decode parse) instead of pulse_apply_patch")
     p.add_argument("--quant-per-group", action="store_true",
                    help="one fp8_block_quant launch per stacked group instead of grouped launches")
-    p.add_argument("--receiver", choices=["fused", "separate"], default="separate",
+    p.add_argument("--receiver", choices=["fused", "separate"], default="fused",
                    help="fused: pulse_apply_quant (patch apply + FP8 quantisation in one read of the view); "
                         "separate: pulse_apply_patch, then fp8_block_quant_groups")
     p.add_argument("--schedule", choices=["ahead", "side", "pipeline", "serial"], default="side",
-                   help="ahead: the decode parse of chunk c on a second stream beside the encode of chunk c + 1 "
-                        "and the receiver's pass of chunk c; side: beside the receiver's pass of chunk c only; "
+                   help="ahead: the decode parse of chunk c on a second stream beside the encode of chunk c + 1; "
+                        "side: beside the receiver's pass of chunk c; "
                         "pipeline: encode and parse of chunk c on the second stream while the main stream "
                         "receives chunk c - 1; serial: one lz4_decode_blocks call per chunk, one stream")
     p.add_argument("--cpu-sample-frac", type=float, default=1.0,
@@ -287,8 +286,8 @@ def main():
     sched = args.schedule
     if sched in ("ahead", "pipeline") and not fused:
         raise SystemExit(f"--schedule {sched} goes with the fused encode")
-    if args.apply_tiled and (recv_fused or sched in ("ahead", "pipeline")):
-        raise SystemExit("--apply-tiled goes with --receiver separate and --schedule side or serial")
+    if args.apply_tiled and recv_fused:
+        raise SystemExit("--apply-tiled goes with --receiver separate")
     if args.quant_per_group and recv_fused:
         raise SystemExit("--quant-per-group goes with --receiver separate")
     recv_stages = ["receiver"] if recv_fused else ["apply_patch", "fp8_quant"]
@@ -301,11 +300,11 @@ def main():
                     for ch, plan in zip(chunks, qplans)]
     # buffer sets: what a chunk's sender output and parse live in until the
     # receiver is done with them (two when a chunk's encode overlaps another's)
-    bufs = [(idx, val, payload, csizes, coffs, ws_de)]
+    bufs = [(idx, val, payload, csizes, coffs, ws_de, tiles)]
     if sched in ("ahead", "pipeline"):
         bufs.append((torch.empty_like(idx), torch.empty_like(val), torch.empty_like(payload),
                      torch.empty_like(csizes), torch.empty_like(coffs),
-                     pulse.workspace(pulse.PULSE_OP_LZ4_DECODE, nbmax, pcap, dev)))
+                     pulse.workspace(pulse.PULSE_OP_LZ4_DECODE, nbmax, pcap, dev), torch.zeros_like(tiles)))
 
     main_stream = torch.cuda.current_stream()
     side_stream = torch.cuda.Stream()  # default priority, like every stream here
@@ -325,11 +324,11 @@ def main():
     def encode(record, ci, B):
         s0, e0, _ = chunks[ci]
         m = e0 - s0
-        I, V, P, CS, CO, _ = B
+        I, V, P, CS, CO, _, T = B
         if fused:
             rec(record, "encode", lambda: pulse.pulse_cast_diff_lz4(
                 W[s0:e0], b_old[s0:e0], stage[:m], I, V, cnt[ci:ci + 1], P, CS, CO, ctotal[ci:ci + 1], status,
-                ws_fz, tile_first=tiles if args.apply_tiled else None, stream=torch.cuda.current_stream()))
+                ws_fz, tile_first=T if args.apply_tiled else None, stream=torch.cuda.current_stream()))
         else:
             rec(record, "cast_diff", lambda: pulse.pulse_cast_diff(W[s0:e0], b_old[s0:e0], stage[:m], None, I, V,
                                                                    cnt[ci:ci + 1], status, ws_cd))
@@ -340,7 +339,7 @@ def main():
         """The patch apply (v0 -> v1) and the FP8 quantisation of v1."""
         s0, e0, _ = chunks[ci]
         m = e0 - s0
-        I, V = B[0], B[1]
+        I, V, T = B[0], B[1], B[6]
         if recv_fused:
             rec(record, "receiver", lambda: pulse.pulse_apply_quant(b_recv[s0:e0], I, V, cnt[ci:ci + 1],
                                                                     aq_plans[ci], status, ws_aq))
@@ -351,8 +350,8 @@ def main():
                 pulse.pulse_apply_patch(b_recv[s0:e0], I, V, cnt[ci:ci + 1], status)
                 return
             if not fused:  # the receiver builds the tile index itself
-                pulse.pulse_patch_tiles(I, cnt[ci:ci + 1], tiles, m)
-            pulse.pulse_apply_patch_tiled(b_recv[s0:e0], I, V, tiles, status)
+                pulse.pulse_patch_tiles(I, cnt[ci:ci + 1], T, m)
+            pulse.pulse_apply_patch_tiled(b_recv[s0:e0], I, V, T, status)
 
         def quant():
             if args.quant_per_group:
@@ -369,7 +368,7 @@ def main():
     def parse_chunk(record, ci, B):
         """The decode's token-chain parse, on the side stream."""
         s0, e0, _ = chunks[ci]
-        _, _, P, CS, CO, WD = B
+        _, _, P, CS, CO, WD, _ = B
         with torch.cuda.stream(side_stream):
             rec(record, "lz4_decode", lambda: pulse.lz4_decode_parse(P, CO, CS, 2 * (e0 - s0), status, WD,
                                                                      stream=side_stream), store=parse_ev)
@@ -379,7 +378,7 @@ def main():
 
     def decode_apply(record, ci, B):
         s0, e0, _ = chunks[ci]
-        _, _, P, CS, CO, WD = B
+        _, _, P, CS, CO, WD, _ = B
         rec(record, "lz4_decode", lambda: pulse.lz4_decode_apply(P, CO, CS, b_recv[s0:e0], status, WD, mode=1))
 
     def after(stream):
@@ -409,18 +408,17 @@ def main():
                 main_stream.wait_event(parsed)
                 decode_apply(record, ci, bufs[0])
         elif sched == "ahead":
-            # the parse of chunk c beside the encode of chunk c + 1 and the
-            # receiver's pass of chunk c; each set is rewritten by the encode of
-            # chunk c + 2, which the main stream queues after chunk c's decode
+            # the parse of chunk c starts with the encode of chunk c + 1 (the
+            # event before that encode also follows chunk c - 1's decode, the
+            # last user of the buffer set chunk c + 1 writes), then the main
+            # stream receives chunk c and decodes it once the parse is done
             encode(record, 0, bufs[0])
-            encoded = after(main_stream)
             for ci in range(N):
                 B = bufs[ci % 2]
-                side_stream.wait_event(encoded)
+                side_stream.wait_event(after(main_stream))
                 parsed = parse_chunk(record, ci, B)
                 if ci + 1 < N:
                     encode(record, ci + 1, bufs[(ci + 1) % 2])
-                    encoded = after(main_stream)
                 receive(record, ci, B)
                 main_stream.wait_event(parsed)
                 decode_apply(record, ci, B)

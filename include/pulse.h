@@ -191,7 +191,7 @@ int pulse_cast_diff_lz4(const float *w_new, const uint16_t *b_old, uint16_t *b_n
  * writes with no floating-point addition ([Jiang talk] 11:08-11:30; [PULSE
  * summary] "1. PULSESync", Ricostruzione); applied in sequence the patches of
  * consecutive versions bring a lagging copy up to date (16:52-16:58).
- *   b          [n] BF16 view, updated in place.
+ *   b          [n] BF16 view, updated in place; n <= 2^31 - 1 (PULSE_ERANGE).
  *   patch_idx, patch_val  the patch (indices unique, as produced above).
  *   d_count    (device) number of entries; count = min(*d_count, max_count).
  *   max_count  (host) bound used to size the launch, e.g. the patch capacity.

@@ -13,9 +13,18 @@
 
 namespace pulse {
 
-// Lanes take consecutive entries (entry = base + q*64 + lane for q < 4), so
+// Lanes take consecutive entries (entry = base + q*64 + lane for q < 8), so
 // one store instruction writes 64 consecutive entries of the ascending patch:
 // a few neighbouring cache lines per instruction instead of one line per lane.
+// Stores and loads share one in-order completion counter, so each iteration
+// issues the next iteration's entry loads before its own stores: waiting for
+// those loads then never waits for the stores (which only need to drain).
+// Neither is masked: a load past the count reads the last entry and is
+// dropped, a store that must not happen goes to the buffer's end and is
+// dropped by the hardware, so the counter's waits stay exact.  (The view's
+// byte size, 2 n, fits the 32-bit range field: n < 2^31.)
+constexpr int kApPer = 8;
+
 __global__ __launch_bounds__(256) void k_apply_patch(uint16_t *__restrict__ b, int64_t n,
                                                      const int32_t *__restrict__ idx,
                                                      const uint16_t *__restrict__ val,
@@ -23,26 +32,52 @@ __global__ __launch_bounds__(256) void k_apply_patch(uint16_t *__restrict__ b, i
                                                      int64_t max_count, uint32_t *d_status) {
     int64_t count = *d_count;
     if (count > max_count) count = max_count;
-    const int64_t per_wave = 4 * kWave;
-    const int64_t nwaves = (int64_t)gridDim.x * (blockDim.x / kWave);
+    const int64_t per_wave = kApPer * kWave;
+    const int64_t stride = (int64_t)gridDim.x * (blockDim.x / kWave) * per_wave;
+    int64_t wb = ((int64_t)blockIdx.x * (blockDim.x / kWave) + wave_id()) * per_wave;  // uniform
     bool bad = false;
-    for (int64_t wb = ((int64_t)blockIdx.x * (blockDim.x / kWave) + wave_id()) * per_wave; wb < count;
-         wb += nwaves * per_wave) {
-        int32_t ii[4];
-        uint16_t vv[4];
+    if (wb < count) {
+        auto load = [&](int64_t base, int32_t (&ii)[kApPer], uint16_t (&vv)[kApPer]) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int64_t k = wb + q * kWave + lane_id();
-            ii[q] = k < count ? idx[k] : -1;
-            vv[q] = k < count ? val[k] : 0;
-        }
+            for (int q = 0; q < kApPer; ++q) {
+                int64_t k = base + q * kWave + lane_id();
+                k = k < count ? k : count - 1;
+                ii[q] = idx[k];
+                vv[q] = val[k];
+            }
+        };
+        // the entries are waited for where they were loaded (before the
+        // stores issued after them on the loop's back edge, none on entry),
+        // so the loop head has nothing to wait for
+        auto ready = [](int32_t (&ii)[kApPer], uint16_t (&vv)[kApPer]) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int64_t k = wb + q * kWave + lane_id();
-            if (k >= count) break;
-            const int64_t i = ii[q];
-            if (i >= 0 && i < n) b[i] = vv[q];
-            else bad = true;
+            for (int q = 0; q < kApPer; ++q) asm volatile("" ::"v"(ii[q]), "v"((uint32_t)vv[q]));
+        };
+        const i32x4_t rsrc = buffer_rsrc(b, (uint32_t)(2 * n));
+        const int32_t off_none = (int32_t)(uint32_t)(2 * n);
+        int32_t ii[kApPer];
+        uint16_t vv[kApPer];
+        load(wb, ii, vv);
+        ready(ii, vv);
+        for (; wb < count; wb += stride) {
+            int32_t ni[kApPer];
+            uint16_t nv[kApPer];
+            load(wb + stride < count ? wb + stride : wb, ni, nv);
+#pragma unroll
+            for (int q = 0; q < kApPer; ++q) {
+                const int64_t k = wb + q * kWave + lane_id();
+                const int32_t i = ii[q];
+                const bool live = k < count;
+                const bool in = i >= 0 && i < n;
+                bad |= live && !in;
+                raw_buffer_store_u16(vv[q], rsrc, live && in ? 2 * i : off_none, 0, 0);
+            }
+            ready(ni, nv);
+#pragma unroll
+            for (int q = 0; q < kApPer; ++q) {
+                ii[q] = ni[q];
+                vv[q] = nv[q];
+            }
         }
     }
     if (__ballot(bad) && lane_id() == 0) or_agent32(d_status, 2u /*PULSE_DS_BADINDEX*/);
@@ -222,7 +257,7 @@ extern "C" int pulse_launch_apply_patch_segments(const void *views, int32_t nseg
 extern "C" int pulse_launch_apply_patch(uint16_t *b, int64_t n, const int32_t *idx, const uint16_t *val,
                                         const int64_t *d_count, int64_t max_count, uint32_t *d_status,
                                         hipStream_t stream) {
-    int64_t blocks = (max_count + 1023) / 1024;
+    int64_t blocks = (max_count + 256 * kApPer - 1) / (256 * kApPer);
     if (blocks > 256 * 32) blocks = 256 * 32;
     if (blocks < 1) blocks = 1;
     k_apply_patch<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(b, n, idx, val, d_count, max_count, d_status);

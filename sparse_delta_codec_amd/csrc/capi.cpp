@@ -193,7 +193,7 @@ int pulse_apply_patch(uint16_t *b, int64_t n, const int32_t *patch_idx, const ui
                       const int64_t *d_count, int64_t max_count, uint32_t *d_status, hipStream_t stream) {
     if (!b || !patch_idx || !patch_val || !d_count || !d_status || n < 0 || max_count < 0)
         return PULSE_EINVAL;
-    if (n > kMaxIndexed + 1) return PULSE_ERANGE;
+    if (n > kMaxIndexed) return PULSE_ERANGE;  // the stores address the view's 2 n bytes in 32 bits
     if (max_count == 0) return PULSE_OK;
     return pulse_launch_apply_patch(b, n, patch_idx, patch_val, d_count, max_count, d_status, stream);
 }

@@ -11,6 +11,29 @@
 
 namespace pulse {
 
+// ---- raw buffer stores ------------------------------------------------------
+// A buffer resource (CDNA3/4 layout: 48-bit base, stride 0, num_records in
+// bytes, word 3 = 0x00020000 for the gfx9 family) and the raw 16-bit buffer
+// store.  A raw buffer store whose offset is at or past num_records is
+// dropped by the hardware, so a lane that must not write is given the offset
+// num_records instead of being masked off: every store instruction is then
+// issued, and the memory counter's waits for earlier loads stay exact.
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ void raw_buffer_store_u16(uint16_t v, i32x4_t rsrc, int32_t voffset, int32_t soffset,
+                                     int32_t aux) __asm("llvm.amdgcn.raw.buffer.store.i16");
+
+__device__ __forceinline__ i32x4_t buffer_rsrc(const void *p, uint32_t num_bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    i32x4_t r;
+    r.x = (int32_t)(uint32_t)a;
+    r.y = (int32_t)(uint32_t)((a >> 32) & 0xFFFFu);
+    r.z = (int32_t)num_bytes;
+    r.w = 0x00020000;
+    return r;
+}
+
+
 constexpr int kWave = 64;
 
 // native 16-byte vector: copies stay in registers (HIP's uint4 struct copies

@@ -369,8 +369,14 @@ __global__ __launch_bounds__(256, 4) void k_apply_quant(uint16_t *__restrict__ b
         c = c > max_count ? max_count : c;
         count = (int32_t)(c < 0 ? 0 : c);
     }
-    const int rl = t >> 1, h = t & 1;   // entries: block row rl, alternate entries
+    // Lanes t = 2 rl, 2 rl + 1 hold the entry range of block row rl (looked up
+    // a block ahead).  The entries are loaded 16 lanes a row, one entry a lane:
+    // lane l of wave w takes entry (l % 16) of rows 32 w + 4 j + l / 16,
+    // j < 8, so one load instruction reads four rows' runs of the patch.
+    const int rl = t >> 1;
     const int rg = t >> 4, seg = t & 15; // view: rows rg + 16 i, columns [8 seg, +8)
+    const int lane = t & 63, l16 = lane & 15;
+    const int erow0 = (t >> 6) * 32 + (lane >> 4);  // + 4 j: the rows whose entries this lane loads
 
 #define AQ_DECL(T, f) T c_##f; T n_##f;
     AQ_FIELDS(AQ_DECL)
@@ -405,9 +411,8 @@ __global__ __launch_bounds__(256, 4) void k_apply_quant(uint16_t *__restrict__ b
             ok[i] = col_ok && r < c_R;
             v[i] = *reinterpret_cast<const uint4 *>(b + ELEM(c_, r < c_R ? r : c_R - 1, col_ok ? col : 0));
         }
-        // the row's first 16 entries (8 a thread); past the row's last entry
-        // a thread reads entry 0 (the patch buffer holds at least one) and
-        // drops it
+        // every row's first 16 entries; past a row's last entry a lane reads
+        // entry 0 (the patch buffer holds at least one) and drops it
         const bool row_ok = c_br * 128 + rl < c_R;
         int32_t k0 = row_ok ? sf0 : 0, k1 = row_ok ? sf1 : 0;
         k0 = k0 < 0 ? 0 : (k0 > count ? count : k0);
@@ -415,13 +420,15 @@ __global__ __launch_bounds__(256, 4) void k_apply_quant(uint16_t *__restrict__ b
         int32_t ii[8];
         uint16_t vv[8];
 #pragma unroll
-        for (int qq = 0; qq < 8; ++qq) {
-            const int32_t kk = k0 + h + 2 * qq;
-            const int32_t kc = kk < k1 ? kk : 0;
+        for (int j = 0; j < 8; ++j) {
+            const int src = 8 * j + 2 * (lane >> 4);  // the lane holding row erow0 + 4 j's range
+            const int32_t a0 = __shfl(k0, src), a1 = __shfl(k1, src);
+            const int32_t kk = a0 + l16;
+            const int32_t kc = kk < a1 ? kk : 0;
             const int32_t xi = idx[kc];
             const uint16_t yv = val[kc];
-            ii[qq] = kk < k1 ? xi : -1;
-            vv[qq] = yv;
+            ii[j] = kk < a1 ? xi : -1;
+            vv[j] = yv;
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) img[(rg + 16 * i) * 16 + seg] = v[i];
@@ -434,24 +441,19 @@ __global__ __launch_bounds__(256, 4) void k_apply_quant(uint16_t *__restrict__ b
         int32_t ne, nsf0, nsf1;
         LOOKUP(n_, ne, nsf0, nsf1);
 
-        uint16_t *row = reinterpret_cast<uint16_t *>(img) + rl * 128;
+        uint16_t *img16 = reinterpret_cast<uint16_t *>(img);
 #pragma unroll
-        for (int qq = 0; qq < 8; ++qq) {
-            const int32_t rel = ii[qq] - e;
-            if (ii[qq] >= 0 && rel >= 0 && rel < len) row[rel] = vv[qq];
+        for (int j = 0; j < 8; ++j) {
+            const int r = erow0 + 4 * j;  // block row
+            const int32_t er = __shfl(e, 8 * j + 2 * (lane >> 4));
+            const int32_t rel = ii[j] - er;
+            if (ii[j] >= 0 && rel >= 0 && rel < len) img16[r * 128 + rel] = vv[j];
         }
-        for (int32_t k = k0 + h + 16; k < k1; k += 16) {  // rows with more than 16 entries
-#pragma unroll
-            for (int qq = 0; qq < 8; ++qq) {
-                const int32_t kk = k + 2 * qq;
-                ii[qq] = kk < k1 ? idx[kk] : -1;
-                vv[qq] = kk < k1 ? val[kk] : 0;
-            }
-#pragma unroll
-            for (int qq = 0; qq < 8; ++qq) {
-                const int32_t rel = ii[qq] - e;
-                if (ii[qq] >= 0 && rel >= 0 && rel < len) row[rel] = vv[qq];
-            }
+        // rows with more than 16 entries: the two lanes of the row take the
+        // rest in turn
+        for (int32_t k = k0 + 16 + (t & 1); k < k1; k += 2) {
+            const int32_t rel = idx[k] - e;
+            if (rel >= 0 && rel < len) img16[rl * 128 + rel] = val[k];
         }
         __syncthreads();
 

@@ -77,9 +77,13 @@ __device__ __forceinline__ uint32_t win_byte(uint64_t lo, uint64_t hi, uint32_t 
 }
 
 // ---- K1 ----------------------------------------------------------------------
-constexpr int K1_RING = 512;                   // bytes of compressed stream held per lane
+// Bytes of compressed stream held per lane.  The parse runs beside the
+// receiver's pass and shares the CUs' LDS with it: 256 bytes (17 KB a wave)
+// take twice the refills of 512 but leave the other kernel twice the room,
+// and the step is faster for it.
+constexpr int K1_RING = 256;
 // Rings sit K1_STRIDE bytes apart: lanes refilled together read at nearly the
-// same ring offsets, and with a stride of 512 bytes those reads would all fall
+// same ring offsets, and with a power-of-two stride those reads would all fall
 // in one LDS bank; 16 more bytes per ring move each lane four banks along.
 constexpr int K1_STRIDE = K1_RING + 16;
 constexpr int K1_PIECES = K1_RING / 16;        // 16-byte pieces per ring

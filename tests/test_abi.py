@@ -155,6 +155,7 @@ def test_argument_errors_return_before_any_launch(lib):
     ap = lib.pulse_apply_patch
     ap.argtypes = [V, I64, V, V, V, I64, V, V]
     assert ap(al, 10, None, al, al, 5, al, None) == EINVAL
+    assert ap(al, 1 << 31, al, al, al, 5, al, None) == ERANGE
     x = lib.xor_mask_apply
     x.argtypes = [V, V, I64, V]
     assert x(mis, al, 100, None) == EALIGN and x(al, al, -1, None) == EINVAL

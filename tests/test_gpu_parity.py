@@ -235,6 +235,16 @@ def test_apply_bad_index_and_count_bound():
     torch.cuda.synchronize()
     ref, rst = oracle.apply_patch(b, idx[1:], val[1:], count=3)
     assert np.array_equal(u16(B), ref) and int(host(st)[0]) == rst == 0
+    # indices just past the view inside a larger buffer: skipped, the rest of
+    # the buffer untouched
+    G = dev(np.concatenate([b, np.full(64, 0x7777, np.uint16)]))
+    bad = np.array([2, 99, 100, 101, 163], np.int32)
+    st = zeros(1, torch.int32)
+    pulse.pulse_apply_patch(G[:100], dev(bad), dev(val), dev(np.array([5], np.int64)), st, max_count=5)
+    torch.cuda.synchronize()
+    ref, rst = oracle.apply_patch(b, bad, val)
+    got = u16(G)
+    assert np.array_equal(got[:100], ref) and np.all(got[100:] == 0x7777) and int(host(st)[0]) == rst
     # device count above max_count: only max_count entries are applied
     B = dev(b)
     pulse.pulse_apply_patch(B, dev(idx[1:]), dev(val[1:]), dev(np.array([4], np.int64)), zeros(1, torch.int32),
