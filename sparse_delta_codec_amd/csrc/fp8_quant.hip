@@ -56,6 +56,7 @@ struct QBlock {
 // codes_row0 being the code of the block's first row at the thread's first
 // column).  s_red[w * red_stride], w < 4: LDS words for the waves' maxima,
 // free when the call starts.
+template <bool STREAM = false>
 __device__ __forceinline__ void quant_regs(const uint4 (&v)[8], const bool (&ok)[8], uint32_t *s_red,
                                            int red_stride, uint8_t *codes_row0, int64_t cols, float *scale) {
     const int t = threadIdx.x;
@@ -119,7 +120,11 @@ __device__ __forceinline__ void quant_regs(const uint4 (&v)[8], const bool (&ok)
                                 (w1 & 0x80000000u);
             packed[h] = (uint32_t)c | sg;
         }
-        *reinterpret_cast<uint2 *>(codes_row0 + (int64_t)(rg + 16 * i) * cols) = make_uint2(packed[0], packed[1]);
+        uint8_t *dst = codes_row0 + (int64_t)(rg + 16 * i) * cols;
+        if (STREAM)  // written once, not read again here: kept out of the caches
+            __builtin_nontemporal_store(u32x2{packed[0], packed[1]}, reinterpret_cast<u32x2 *>(dst));
+        else
+            *reinterpret_cast<uint2 *>(dst) = make_uint2(packed[0], packed[1]);
     }
 }
 
@@ -335,12 +340,17 @@ __device__ __forceinline__ int32_t aq_elem(int32_t o0, int32_t o1, int32_t o2, i
 }
 
 // Persistent: each XCD (workgroups go to the 8 XCDs in turn) takes a
-// contiguous run of blocks, which its workgroups share in turn, so that
-// neighbouring column blocks (the same rows, whose entries share lines of the
-// patch and of its index) meet in one L2.  A workgroup looks up the next
-// block's entry range while it patches and quantises the current block, so a
-// block's own loads (the view and the entries) go out together.
+// contiguous range of blocks, and its workgroups take runs of kAqRun
+// consecutive blocks of it in turn.  Consecutive blocks are neighbouring
+// column blocks of the same rows, whose entries continue in the same lines of
+// the patch: a block row uses some 60 bytes of its rows' 128-byte lines, and
+// the next block of the run finds the rest still in L2.  The view, the
+// write-back and the codes are streamed (non-temporal) so they do not evict
+// those lines.  A workgroup looks up the next block's entry range while it
+// patches and quantises the current block, so a block's own loads (the view
+// and the entries) go out together.
 constexpr int kAqMaxGroups = 320 * 8;
+constexpr int kAqRun = 8;
 
 __global__ __launch_bounds__(256, 4) void k_apply_quant(uint16_t *__restrict__ b, int64_t n,
                                                        const int32_t *__restrict__ idx,
@@ -350,7 +360,7 @@ __global__ __launch_bounds__(256, 4) void k_apply_quant(uint16_t *__restrict__ b
                                                        const uint8_t *__restrict__ plan, int64_t nblk,
                                                        uint32_t *d_status) {
     static_assert(FQ_GSRC == 4, "four sources a group");
-    __shared__ uint4 img[128 * 16];  // the block, 256 bytes a row
+    __shared__ u32x4 img[128 * 16];  // the block, 256 bytes a row
     const AQPlanHeader *hdr = reinterpret_cast<const AQPlanHeader *>(plan);
     const int t = threadIdx.x;
     if (hdr->n != n || hdr->nblocks != nblk) {  // a plan made for another view
@@ -359,8 +369,12 @@ __global__ __launch_bounds__(256, 4) void k_apply_quant(uint16_t *__restrict__ b
     }
     const int64_t ng = hdr->ngroups;
     const int64_t x = blockIdx.x % 8, per = gridDim.x / 8, q = nblk / 8, rem = nblk % 8;
-    const int64_t x1 = x * q + (x < rem ? x : rem) + q + (x < rem ? 1 : 0);
-    int64_t blk = x * q + (x < rem ? x : rem) + blockIdx.x / 8;
+    const int64_t x0 = x * q + (x < rem ? x : rem), x1 = x0 + q + (x < rem ? 1 : 0);
+    // this workgroup's m-th block: run j0 + (m / kAqRun) per, block m % kAqRun of it
+    const int64_t j0 = blockIdx.x / 8;
+    auto block_of = [&](int64_t m) { return x0 + (j0 + (m / kAqRun) * per) * kAqRun + m % kAqRun; };
+    int64_t m = 0;
+    int64_t blk = block_of(0);
     if (blk >= x1) return;
 
     int32_t count;
@@ -409,7 +423,9 @@ __global__ __launch_bounds__(256, 4) void k_apply_quant(uint16_t *__restrict__ b
         for (int i = 0; i < 8; ++i) {
             const int32_t r = c_br * 128 + rg + 16 * i;
             ok[i] = col_ok && r < c_R;
-            v[i] = *reinterpret_cast<const uint4 *>(b + ELEM(c_, r < c_R ? r : c_R - 1, col_ok ? col : 0));
+            const u32x4 w = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4 *>(b + ELEM(c_, r < c_R ? r : c_R - 1, col_ok ? col : 0)));
+        v[i] = make_uint4(w.x, w.y, w.z, w.w);
         }
         // every row's first 16 entries; past a row's last entry a lane reads
         // entry 0 (the patch buffer holds at least one) and drops it
@@ -431,11 +447,11 @@ __global__ __launch_bounds__(256, 4) void k_apply_quant(uint16_t *__restrict__ b
             vv[j] = yv;
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) img[(rg + 16 * i) * 16 + seg] = v[i];
+        for (int i = 0; i < 8; ++i) img[(rg + 16 * i) * 16 + seg] = u32x4{v[i].x, v[i].y, v[i].z, v[i].w};
         __syncthreads();
 
         // the next block and its entry range (the current one again at the end)
-        const int64_t nb = blk + per;
+        const int64_t nb = block_of(m + 1);
         const bool more = nb < x1;
         AQ_LOCATE(n_, more ? nb : blk);
         int32_t ne, nsf0, nsf1;
@@ -462,17 +478,21 @@ __global__ __launch_bounds__(256, 4) void k_apply_quant(uint16_t *__restrict__ b
         uint4 u[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            u[i] = img[(rg + 16 * i) * 16 + seg];
-            if (ok[i]) *reinterpret_cast<uint4 *>(b + ELEM(c_, c_br * 128 + rg + 16 * i, col)) = u[i];
+            const u32x4 w = img[(rg + 16 * i) * 16 + seg];
+            u[i] = make_uint4(w.x, w.y, w.z, w.w);
+            if (ok[i])
+                __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(b + ELEM(c_, c_br * 128 + rg + 16 * i, col)));
         }
         if (c_quant) {
             __syncthreads();  // the image is read; its first words hold the waves' maxima
-            quant_regs(u, ok, reinterpret_cast<uint32_t *>(img), 1, c_codes + (int64_t)c_br * 128 * c_cols + col,
-                       c_cols, c_scales + (int64_t)c_br * c_nbc + c_bc);
+            quant_regs<true>(u, ok, reinterpret_cast<uint32_t *>(img), 1,
+                             c_codes + (int64_t)c_br * 128 * c_cols + col, c_cols,
+                             c_scales + (int64_t)c_br * c_nbc + c_bc);
         }
         if (!more) break;
         __syncthreads();  // the image (and the maxima) read before the next block is stored
         blk = nb;
+        ++m;
 #define AQ_NEXT(T, f) c_##f = n_##f;
         AQ_FIELDS(AQ_NEXT)
 #undef AQ_NEXT
@@ -645,7 +665,7 @@ extern "C" int pulse_launch_apply_quant(uint16_t *b, int64_t n, const int32_t *i
                                                                        d_status);
     if (hipGetLastError() != hipSuccess) return -5;
     if (nblocks < 1) return 0;
-    int64_t per = (nblocks + 7) / 8;  // workgroups per XCD
+    int64_t per = ((nblocks + 7) / 8 + kAqRun - 1) / kAqRun;  // workgroups per XCD: one run each at most
     if (per > kAqMaxGroups / 8) per = kAqMaxGroups / 8;
     k_apply_quant<<<dim3((unsigned)(8 * per)), dim3(256), 0, stream>>>(b, n, idx, val, d_count, max_count, seg_first,
                                                                        static_cast<const uint8_t *>(plan), nblocks,
