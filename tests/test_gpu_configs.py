@@ -7,7 +7,8 @@ At these sizes the oracle cannot redo the whole job, so each test checks
   * sampled outputs against the oracle, element by element: cast+diff+compact
     on windows of the weights, LZ4 blocks byte for byte, FP8 codes and scales of
     whole experts and of 128-row bands of the stacked q/k/v.
-The calls and chunking are the ones bench.py times.  Every input comes from
+C2 makes the calls bench.py times, with its chunking; the other configurations
+use the single-purpose calls.  Every input comes from
 workload/ (seeded); only host copies of the sampled windows go to the oracle.
 """
 import numpy as np
@@ -75,8 +76,14 @@ def new_ws(op, n, aux=0):
 
 # ---------------------------------------------------------------------------
 def test_c2_qwen32b_encode_and_apply_full_size():
-    """C2: the whole Qwen2.5-32B-shaped set, one step; cast+diff+compact per chunk,
-    patch applied to the old view, which must then equal the new cast everywhere."""
+    """C2: the whole Qwen2.5-32B-shaped set, one step, with bench.py's calls per
+    chunk: the fused sender pass (pulse_cast_diff_lz4: new view, patch, LZ4
+    blocks of the mask) and the receiver's pass (pulse_apply_quant over the
+    chunk's FP8 groups and patched-only tensors).  Every element: the patched
+    old view equals the new view.  Sampled against the oracle: windows of the
+    patch, the first LZ4 block of every chunk, and 128-row bands of the FP8
+    codes and scales of two groups per chunk."""
+    from bench import quant_groups, receiver_plan
     dev = torch.device("cuda")
     rng = np.random.default_rng(22)
     specs = workload.qwen25_32b_specs()
@@ -91,7 +98,7 @@ def test_c2_qwen32b_encode_and_apply_full_size():
         workload.fill_init(w, 2, ti, s.kind)
         pulse.pulse_cast_diff(w, b_new=b[offs[ti]: offs[ti] + s.numel])
         workload.apply_step(w, 2, ti, 1, tmp=tmp)
-    del tmp
+    del tmp, w
     torch.cuda.synchronize()
     say(f"C2 generated: {n} params")
     cap = int(max_chunk * 0.125)
@@ -100,20 +107,61 @@ def test_c2_qwen32b_encode_and_apply_full_size():
     val = torch.empty(cap, dtype=torch.int16, device=dev)
     cnt = torch.zeros(1, dtype=torch.int64, device=dev)
     st = torch.zeros(1, dtype=torch.int32, device=dev)
-    ws = new_ws(pulse.PULSE_OP_CAST_DIFF, max_chunk)
-    total = checked = 0
-    for ci, (s0, e0, _) in enumerate(chunks):
+    nbmax = (2 * max_chunk + BLOCK - 1) // BLOCK
+    pcap = int(2 * max_chunk * 0.35)
+    payload = torch.empty(pcap, dtype=torch.uint8, device=dev)
+    csizes = torch.empty(nbmax, dtype=torch.int32, device=dev)
+    coffs = torch.empty(nbmax, dtype=torch.int64, device=dev)
+    ctotal = torch.zeros(1, dtype=torch.int64, device=dev)
+    ws_fz = new_ws(pulse.PULSE_OP_CAST_DIFF_LZ4, max_chunk, BLOCK)
+    ws_aq = new_ws(pulse.PULSE_OP_APPLY_QUANT, max_chunk)
+    codes = torch.empty(max_chunk, dtype=torch.uint8, device=dev)
+    scales = torch.empty(max_chunk // 16384 + 4096, dtype=torch.float32, device=dev)
+    total = checked = bands = 0
+    for ci, ch in enumerate(chunks):
+        s0, e0, tids = ch
         m = e0 - s0
-        pulse.pulse_cast_diff(W[s0:e0], b[s0:e0], stage[:m], None, idx, val, cnt, st, ws)
+        pulse.pulse_cast_diff_lz4(W[s0:e0], b[s0:e0], stage[:m], idx, val, cnt, payload, csizes, coffs, ctotal, st,
+                                  ws_fz)
         count = int(cnt.item())
         assert int(st.item()) == 0 and 0 < count <= cap
         for o in [0, m - WIN] + [int(x) for x in rng.integers(0, m - WIN, 2)]:
             checked += check_patch_window(W[s0:e0], b[s0:e0], idx, val, count, o)
-        pulse.pulse_apply_patch(b[s0:e0], idx, val, cnt, st, max_count=count)
+        # the first mask block, byte for byte
+        old0, new0 = h16(b[s0:s0 + BLOCK // 2]), h16(stage[:BLOCK // 2])
+        enc = oracle.lz4_encode_blocks(old0, BLOCK, src_xor=new0)
+        sz = int(csizes[0].item())
+        assert int(coffs[0].item()) == 0 and sz == enc["total"]
+        assert np.array_equal(payload[:sz].cpu().numpy(), enc["payload"])
+        # the receiver's pass
+        plan = [(g, sum(specs[i].shape[0] for i in g), specs[g[0]].shape[1]) for g in quant_groups(specs, tids)]
+        aq = receiver_plan(pulse, specs, offs, ch, plan, codes, scales, dev)
+        pulse.pulse_apply_quant(b[s0:e0], idx, val, cnt, aq, st, ws_aq, max_count=count)
+        torch.cuda.synchronize()
         assert int(st.item()) == 0
-        assert views_equal(b[s0:e0], stage[:m]), f"chunk {ci}: patched old view != new cast"
+        assert views_equal(b[s0:e0], stage[:m]), f"chunk {ci}: patched old view != new view"
+        # two groups, one 128-row band each, against the oracle's quantisation
+        co = so = 0
+        picks = set(int(x) for x in rng.integers(0, len(plan), 2))
+        for gi, (g, rows, cols) in enumerate(plan):
+            nbc = (cols + 127) // 128
+            if gi in picks:
+                br = int(rng.integers(0, (rows + 127) // 128))
+                r0, r1 = br * 128, min(rows, br * 128 + 128)
+                stack = torch.cat([b[offs[i]: offs[i] + specs[i].numel].view(specs[i].shape) for i in g])
+                band = h16(stack[r0:r1].contiguous().view(-1)).reshape(r1 - r0, cols)
+                rc, rs = oracle.fp8_block_quant([band])
+                assert np.array_equal(codes[co + r0 * cols: co + r1 * cols].cpu().numpy(), rc.reshape(-1)), (ci, gi, br)
+                got_s = scales[so + br * nbc: so + (br + 1) * nbc].cpu().numpy().view(np.uint32)
+                assert np.array_equal(got_s, rs.reshape(-1).view(np.uint32)), (ci, gi, br)
+                bands += 1
+                del stack
+            co += rows * cols
+            so += ((rows + 127) // 128) * nbc
+        del aq
         total += count
-    say(f"C2: {total} changed ({total / n:.4%}); {checked} patch entries checked against the oracle")
+    say(f"C2: {total} changed ({total / n:.4%}); {checked} patch entries, {len(chunks)} LZ4 blocks and "
+        f"{bands} FP8 bands checked against the oracle")
     assert 0.07 < total / n < 0.09
 
 
