@@ -517,7 +517,9 @@ __device__ __forceinline__ void k2_block(const Lz4DecArgs &a, int64_t b, uint32_
     uint4 *img4 = reinterpret_cast<uint4 *>(s_img);
 
     // compressed bytes and the first checkpoint, then dst: waiting for the
-    // former leaves the dst loads in flight.  The stage loads are unconditional
+    // former leaves the dst loads in flight.  The view is read and written
+    // once per call, so its accesses are non-temporal (they would otherwise
+    // push the next blocks' compressed bytes out of the L2).  The stage loads are unconditional
     // (a thread past the block reloads its first piece) so that none of them
     // waits behind a branch.
     u32x4 sv[K2_SPT];
@@ -540,7 +542,7 @@ __device__ __forceinline__ void k2_block(const Lz4DecArgs &a, int64_t b, uint32_
 #pragma unroll
         for (int k = 0; k < CPT; ++k) {
             const uint32_t c = t + K2_THREADS * k;
-            dv[k] = d4[c < nfull ? c : 0u];  // (past the block: a reload, never used)
+            dv[k] = __builtin_nontemporal_load(d4 + (c < nfull ? c : 0u));  // (past the block: a reload, never used)
         }
     }
     if (t == 0) s_q.count = 0;
@@ -583,9 +585,9 @@ __device__ __forceinline__ void k2_block(const Lz4DecArgs &a, int64_t b, uint32_
             uint32_t nz = (v.x | v.y | v.z | v.w) != 0u ? 1u : 0u;
             nz |= dpp_mov<0xB1, 0xf, 0xf>(0u, nz);  // quad_perm [1,0,3,2]
             nz |= dpp_mov<0x4E, 0xf, 0xf>(0u, nz);  // quad_perm [2,3,0,1]
-            if (c < nfull && nz) reinterpret_cast<u32x4 *>(dst4)[c] = dv[k] ^ v;
+            if (c < nfull && nz) __builtin_nontemporal_store(dv[k] ^ v, reinterpret_cast<u32x4 *>(dst4) + c);
         } else {
-            if (c < nfull) reinterpret_cast<u32x4 *>(dst4)[c] = v;
+            if (c < nfull) __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst4) + c);
         }
     }
     if (nfull < nchunk && (uint32_t)t == nfull % K2_THREADS) {  // ragged tail of the last block

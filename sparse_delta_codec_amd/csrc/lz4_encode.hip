@@ -218,7 +218,9 @@ constexpr int LZF_STAGE = (LZE_WIN + 48) / 4 / LZE_NW;
 // loads; fused_consume casts, compares, stores the new view, puts old ^ new
 // into the image and, with PATCH, ranks each changed element among the
 // wave's (ballots, index order) and stages it.  Between the two the loads
-// stay in flight while the workgroup finishes its previous block.
+// stay in flight while the workgroup finishes its previous block.  The masters
+// and the two views are streamed (non-temporal: each byte is touched once),
+// which leaves the L2 to the status words and the payload window.
 template <int CHLOG>
 struct FusedGeom {
     static constexpr int BLK_E = (1 << CHLOG) * LZE_THREADS / 2;  // elements per block
@@ -234,8 +236,8 @@ __device__ __forceinline__ void fused_load(const FusedArgs &f, int64_t blk_e0, u
 #pragma unroll
         for (int j = 0; j < GN; ++j) {
             const int64_t e = blk_e0 + w0 + (G0 + j) * 256;
-            fv[j] = *reinterpret_cast<const u32x4 *>(f.w_new + e);
-            ov[j] = *reinterpret_cast<const u32x2 *>(f.b_old + e);
+            fv[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(f.w_new + e));
+            ov[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(f.b_old + e));
         }
     } else {  // the call's last block: elements past n read as zero
 #pragma unroll
@@ -271,7 +273,7 @@ __device__ __forceinline__ uint32_t fused_consume(const FusedArgs &f, int64_t bl
         const uint32_t x0 = p0 ^ ov[j].x, x1 = p1 ^ ov[j].y;  // zero past n
         if (f.b_new) {
             if (full) {
-                *reinterpret_cast<u32x2 *>(f.b_new + e) = u32x2{p0, p1};
+                __builtin_nontemporal_store(u32x2{p0, p1}, reinterpret_cast<u32x2 *>(f.b_new + e));
             } else {
 #pragma unroll
                 for (int k = 0; k < 4; ++k)
