@@ -186,6 +186,28 @@ int pulse_cast_diff_lz4(const float *w_new, const uint16_t *b_old, uint16_t *b_n
                         uint64_t *d_total, uint32_t *d_status, void *ws, size_t ws_bytes,
                         hipStream_t stream);
 
+/* ---- the same pass without a workspace argument ----------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * pulse_cast_diff_lz4 with every argument but ws / ws_bytes, its results
+ * identical.  Its scratch (look-back words) is a static array of
+ * PULSE_NOALLOC_SCRATCH_BYTES in the library, one per GPU, held until the
+ * process ends; the call allocates nothing.  The array holds the workspace
+ * of up to 262144 mask blocks, so every n <= 2^31 - 1 at every block size
+ * fits; a call that needs more returns PULSE_ERANGE before enqueuing
+ * anything.  Every call on a GPU shares that GPU's array: calls that overlap
+ * on one GPU (concurrent streams, threads) race and must be ordered by the
+ * caller.  The first call on a device also clears the array, with a fill
+ * kernel on `stream` ahead of its own kernels.  PULSE_EHIP when the array's
+ * address cannot be obtained. */
+#define PULSE_NOALLOC_SCRATCH_BYTES (256 + 2 * 262144 * 8)
+int pulse_cast_diff_lz4_noalloc(const float *w_new, const uint16_t *b_old, uint16_t *b_new,
+                                int32_t *patch_idx, uint16_t *patch_val, int64_t patch_cap,
+                                int64_t *d_count, int64_t *tile_first, int64_t n,
+                                int32_t block_bytes, uint8_t *payload, int64_t payload_cap,
+                                uint32_t *comp_sizes, uint64_t *comp_offsets, uint64_t *d_total,
+                                uint32_t *d_status, hipStream_t stream);
+
 /* ---- a4: patch scatter-apply ---------------------------------------------
  * Selective override: b[patch_idx[k]] = patch_val[k] for k < count, bit-level
  * writes with no floating-point addition ([Jiang talk] 11:08-11:30; [PULSE

@@ -23,6 +23,7 @@ __all__ = [
     "PULSE_OP_CAST_DIFF_SEGMENTS", "PULSE_DS_BADSEGMENT", "PULSE_OP_CAST_DIFF_LZ4", "pulse_cast_diff_lz4", "fp8_block_quant_groups", "PULSE_QUANT_MAX_GROUPS", "pulse_patch_tiles", "PULSE_OP_APPLY_QUANT", "ApplyQuantPlan", "pulse_apply_quant_plan", "pulse_apply_quant",
     "pulse_apply_patch_tiled", "patch_tile_count", "pulse_segment_tiles", "SegmentTable", "ViewTable",
     "pulse_cast_diff_segments", "pulse_apply_patch_segments", "lz4_decode_parse", "lz4_decode_apply",
+    "pulse_cast_diff_lz4_noalloc", "PULSE_NOALLOC_SCRATCH_BYTES",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -48,6 +49,7 @@ PULSE_OP_CAST_DIFF_SEGMENTS = 8
 PULSE_OP_CAST_DIFF_LZ4 = 9
 PULSE_OP_APPLY_QUANT = 10
 PULSE_DS_BADSEGMENT = 0x10
+PULSE_NOALLOC_SCRATCH_BYTES = 256 + 2 * 262144 * 8
 
 _P, _I64, _I32, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
 _lib.pulse_version.restype = ctypes.c_char_p
@@ -80,6 +82,8 @@ _lib.pulse_apply_patch_segments.argtypes = [_P, _I32, _P, _P, _P, _I64, _P, _P]
 _lib.fp8_block_quant_groups.argtypes = [_P, _I32, _P]
 _lib.pulse_cast_diff_lz4.argtypes = [_P, _P, _P, _P, _P, _I64, _P, _P, _I64, _I32, _P, _I64, _P, _P, _P, _P, _P, _SZ,
                                      _P]
+_lib.pulse_cast_diff_lz4_noalloc.argtypes = [_P, _P, _P, _P, _P, _I64, _P, _P, _I64, _I32, _P, _I64, _P, _P, _P,
+                                             _P, _P]
 _lib.pulse_patch_tiles.argtypes = [_P, _P, _I64, _I64, _P, _P]
 _lib.pulse_apply_patch_tiled.argtypes = [_P, _I64, _P, _P, _P, _I64, _P, _P]
 _lib.pulse_apply_quant_plan_bytes.argtypes = [_I32]
@@ -91,7 +95,8 @@ for _f in ("pulse_cast_diff_segments", "pulse_apply_patch_segments", "patch_pack
            "xor_mask_apply", "lz4_encode_blocks", "lz4_decode_blocks", "fp8_block_quant",
            "fp8_view_delta", "fp8_view_apply", "pulse_loco_gate", "pulse_loco_accumulate",
            "lz4_decode_parse", "lz4_decode_apply", "pulse_cast_diff_lz4", "fp8_block_quant_groups",
-           "pulse_patch_tiles", "pulse_apply_patch_tiled", "pulse_apply_quant_plan", "pulse_apply_quant"):
+           "pulse_patch_tiles", "pulse_apply_patch_tiled", "pulse_apply_quant_plan", "pulse_apply_quant",
+           "pulse_cast_diff_lz4_noalloc"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -277,6 +282,31 @@ def pulse_cast_diff_lz4(w_new, b_old, b_new, patch_idx, patch_val, d_count, payl
         _dev(comp_sizes, "comp_sizes", torch.int32), _dev(comp_offsets, "comp_offsets", torch.int64),
         _dev(d_total, "d_total", torch.int64), _dev(d_status, "d_status", torch.int32), wsp, wsb,
         _stream(stream)), "pulse_cast_diff_lz4")
+
+
+def pulse_cast_diff_lz4_noalloc(w_new, b_old, b_new, patch_idx, patch_val, d_count, payload, comp_sizes,
+                                comp_offsets, d_total, d_status, block_bytes=65536, n=None, tile_first=None,
+                                stream=None):
+    """pulse_cast_diff_lz4 with the library's static per-GPU scratch instead of
+    a workspace: the call allocates nothing (calls overlapping on one GPU race)."""
+    n = w_new.numel() if n is None else n
+    _need(tile_first, 8 * patch_tile_count(n), "tile_first")
+    nb = (2 * n + block_bytes - 1) // block_bytes
+    cap = 0 if patch_idx is None else patch_idx.numel()
+    _need(w_new, 4 * n, "w_new")
+    _need(b_old, 2 * n, "b_old")
+    _need(b_new, 2 * n, "b_new")
+    _need(patch_val, 2 * cap, "patch_val")
+    _need(comp_sizes, 4 * nb, "comp_sizes")
+    _need(comp_offsets, 8 * nb, "comp_offsets")
+    _check(_lib.pulse_cast_diff_lz4_noalloc(
+        _dev(w_new, "w_new", torch.float32), _dev(b_old, "b_old", _U16), _dev(b_new, "b_new", _U16),
+        _dev(patch_idx, "patch_idx", torch.int32), _dev(patch_val, "patch_val", _U16), cap,
+        _dev(d_count, "d_count", torch.int64), _dev(tile_first, "tile_first", torch.int64), n, block_bytes,
+        _dev(payload, "payload", torch.uint8), payload.numel(),
+        _dev(comp_sizes, "comp_sizes", torch.int32), _dev(comp_offsets, "comp_offsets", torch.int64),
+        _dev(d_total, "d_total", torch.int64), _dev(d_status, "d_status", torch.int32),
+        _stream(stream)), "pulse_cast_diff_lz4_noalloc")
 
 
 def _decode_table(payload, comp_offsets, comp_sizes, nbytes, payload_bytes, block_bytes):

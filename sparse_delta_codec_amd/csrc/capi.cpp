@@ -57,6 +57,8 @@ int pulse_launch_apply_patch_tiled(uint16_t *, int64_t, const int32_t *, const u
                                    uint32_t *, hipStream_t);
 int pulse_launch_patch_tiles(const int32_t *, const int64_t *, int64_t, int64_t, int64_t *, hipStream_t);
 int pulse_launch_write_count(int64_t *, int64_t, hipStream_t);
+size_t pulse_noalloc_scratch_bytes(void);
+void *pulse_noalloc_scratch(hipStream_t);
 int64_t pulse_apply_quant_plan_size(int32_t);
 int pulse_build_apply_quant_plan(const void *, int32_t, int64_t, void *, int64_t, int64_t *);
 int pulse_launch_apply_quant(uint16_t *, int64_t, const int32_t *, const uint16_t *, const int64_t *, int64_t,
@@ -152,11 +154,16 @@ int pulse_compact(const uint16_t *b_old, const uint16_t *b_new, int32_t *patch_i
                                   d_count, d_status, n, ws, stream);
 }
 
-int pulse_cast_diff_lz4(const float *w_new, const uint16_t *b_old, uint16_t *b_new, int32_t *patch_idx,
-                        uint16_t *patch_val, int64_t patch_cap, int64_t *d_count, int64_t *tile_first,
-                        int64_t n, int32_t block_bytes,
-                        uint8_t *payload, int64_t payload_cap, uint32_t *comp_sizes, uint64_t *comp_offsets,
-                        uint64_t *d_total, uint32_t *d_status, void *ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by pulse_cast_diff_lz4 and its allocation-free form
+// (everything but the workspace).
+int check_cast_diff_lz4(const float *w_new, const uint16_t *b_old, uint16_t *b_new, int32_t *patch_idx,
+                        uint16_t *patch_val, int64_t patch_cap, int64_t *d_count, int64_t *tile_first, int64_t n,
+                        int32_t block_bytes, uint8_t *payload, int64_t payload_cap, uint32_t *comp_sizes,
+                        uint64_t *comp_offsets, uint64_t *d_total, uint32_t *d_status) {
     if (!w_new || !b_old || !payload || !comp_sizes || !comp_offsets || !d_total || !d_status || n <= 0 ||
         payload_cap < 0 || patch_cap < 0)
         return PULSE_EINVAL;
@@ -168,10 +175,43 @@ int pulse_cast_diff_lz4(const float *w_new, const uint16_t *b_old, uint16_t *b_n
     if (patch && n > kMaxIndexed) return PULSE_ERANGE;
     const int64_t nb = (2 * n + block_bytes - 1) / block_bytes;
     if (nb > 0xFFFFFFFFll || 2 * n > kMaxPayload / 2) return PULSE_ERANGE;
+    return PULSE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pulse_cast_diff_lz4(const float *w_new, const uint16_t *b_old, uint16_t *b_new, int32_t *patch_idx,
+                        uint16_t *patch_val, int64_t patch_cap, int64_t *d_count, int64_t *tile_first,
+                        int64_t n, int32_t block_bytes,
+                        uint8_t *payload, int64_t payload_cap, uint32_t *comp_sizes, uint64_t *comp_offsets,
+                        uint64_t *d_total, uint32_t *d_status, void *ws, size_t ws_bytes, hipStream_t stream) {
+    const int rc = check_cast_diff_lz4(w_new, b_old, b_new, patch_idx, patch_val, patch_cap, d_count, tile_first, n,
+                                       block_bytes, payload, payload_cap, comp_sizes, comp_offsets, d_total,
+                                       d_status);
+    if (rc != PULSE_OK) return rc;
     if (!ws || ws_bytes < pulse_cast_diff_lz4_ws_bytes(n, block_bytes)) return PULSE_EWORKSPACE;
-    return pulse_launch_cast_diff_lz4(w_new, b_old, b_new, patch ? patch_idx : nullptr, patch_val, patch_cap,
-                                      d_count, n, block_bytes, payload, payload_cap, comp_sizes, comp_offsets,
-                                      d_total, d_status, tile_first, ws, stream);
+    return pulse_launch_cast_diff_lz4(w_new, b_old, b_new, patch_idx, patch_val, patch_cap, d_count, n,
+                                      block_bytes, payload, payload_cap, comp_sizes, comp_offsets, d_total,
+                                      d_status, tile_first, ws, stream);
+}
+
+int pulse_cast_diff_lz4_noalloc(const float *w_new, const uint16_t *b_old, uint16_t *b_new, int32_t *patch_idx,
+                                uint16_t *patch_val, int64_t patch_cap, int64_t *d_count, int64_t *tile_first,
+                                int64_t n, int32_t block_bytes, uint8_t *payload, int64_t payload_cap,
+                                uint32_t *comp_sizes, uint64_t *comp_offsets, uint64_t *d_total, uint32_t *d_status,
+                                hipStream_t stream) {
+    const int rc = check_cast_diff_lz4(w_new, b_old, b_new, patch_idx, patch_val, patch_cap, d_count, tile_first, n,
+                                       block_bytes, payload, payload_cap, comp_sizes, comp_offsets, d_total,
+                                       d_status);
+    if (rc != PULSE_OK) return rc;
+    if (pulse_cast_diff_lz4_ws_bytes(n, block_bytes) > pulse_noalloc_scratch_bytes()) return PULSE_ERANGE;
+    void *ws = pulse_noalloc_scratch(stream);
+    if (!ws) return PULSE_EHIP;
+    return pulse_launch_cast_diff_lz4(w_new, b_old, b_new, patch_idx, patch_val, patch_cap, d_count, n,
+                                      block_bytes, payload, payload_cap, comp_sizes, comp_offsets, d_total,
+                                      d_status, tile_first, ws, stream);
 }
 
 int pulse_patch_tiles(const int32_t *patch_idx, const int64_t *d_count, int64_t max_count, int64_t n,

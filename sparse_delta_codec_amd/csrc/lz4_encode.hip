@@ -42,7 +42,12 @@
 // the output window, which is idle until step 5; a second look-back over the
 // blocks' patch counts, resolved while the block is analysed, places them in
 // the ascending (index, new value) patch.
+#include "../../include/pulse.h"
 #include "device.hpp"
+
+#include <mutex>
+
+extern "C" int pulse_launch_fill_zero(void *, size_t, hipStream_t);
 
 namespace pulse {
 
@@ -821,4 +826,42 @@ extern "C" int pulse_launch_cast_diff_lz4(const float *w_new, const uint16_t *b_
         else k_cast_diff_lz4<4, false><<<grid, block, 0, stream>>>(a, f);
     }
     return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+// ---- scratch of the allocation-free fused pass ------------------------------
+// pulse_cast_diff_lz4_noalloc takes its workspace from this array instead of
+// the caller: the header and two look-back words per mask block for up to
+// kNoAllocMaxBlocks blocks, enough for every n <= 2^31 - 1 at every block size
+// (4 MiB + 256 bytes).  Each GPU the library runs on holds its own copy until
+// the process ends.  On the host the array's name is only a stand-in for the
+// symbol, never a device address: host code uses the address that
+// hipGetSymbolAddress returns for the current device, once per device.
+constexpr int64_t kNoAllocMaxBlocks = 262144;
+constexpr size_t kNoAllocScratchBytes = sizeof(pulse::WsHeader) + 2 * (size_t)kNoAllocMaxBlocks * sizeof(uint64_t);
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+static_assert(kNoAllocScratchBytes == PULSE_NOALLOC_SCRATCH_BYTES, "the header states the scratch size");
+
+namespace {
+constexpr int kNoAllocMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kNoAllocMaxDevices];  // device address of `scratch`, per device
+}  // namespace
+
+extern "C" size_t pulse_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+// The current device's scratch address.  On a device's first call the symbol
+// is looked up (with that device current) and the array is cleared by a fill
+// kernel on `stream`, ahead of the kernels of that call; the epoch-tagged
+// look-back words need no clearing after that.  nullptr on failure.
+extern "C" void *pulse_noalloc_scratch(hipStream_t stream) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kNoAllocMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+        if (pulse_launch_fill_zero(p, kNoAllocScratchBytes, stream) != 0) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
 }

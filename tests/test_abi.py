@@ -288,3 +288,24 @@ def test_receiver_pass_plan_and_argument_errors(lib):
     assert aq(mis, *args[1:]) == EALIGN and aq(*args[:6], mis, *args[7:]) == EALIGN
     assert aq(al, 1 << 31, *args[2:]) == ERANGE
     assert aq(*args[:10], 16, None) == EWORKSPACE and aq(*args[:9], None, 1 << 20, None) == EWORKSPACE
+
+
+def test_noalloc_entry_rejects_oversize_calls_before_any_launch(lib):
+    """The allocation-free fused pass: sizes past its static scratch return
+    PULSE_ERANGE before anything is enqueued; the header states the scratch
+    size the library holds."""
+    import sparse_delta_codec_amd as pk
+    text = open(HEADER).read()
+    m = re.search(r"#define PULSE_NOALLOC_SCRATCH_BYTES \((.*)\)", text)
+    assert m and eval(m.group(1)) == pk.PULSE_NOALLOC_SCRATCH_BYTES == 256 + 2 * 262144 * 8
+    f = lib.pulse_cast_diff_lz4_noalloc
+    f.argtypes = [V, V, V, V, V, I64, V, V, I64, ctypes.c_int32, V, I64, V, V, V, V, V]
+    al, mis = V(0x10000), V(0x10002)
+    # 2^34 elements without a patch: 524288 blocks of 64 KiB, twice the scratch's 262144
+    assert f(al, al, al, None, None, 0, None, None, 1 << 34, 65536, al, 10, al, al, al, al, None) == ERANGE
+    # 2^32 + 1 elements at 32 KiB blocks: one block past the scratch
+    assert f(al, al, al, None, None, 0, None, None, (1 << 32) + 1, 32768, al, 10, al, al, al, al, None) == ERANGE
+    assert f(al, al, al, al, al, 10, al, None, 1 << 31, 65536, al, 10, al, al, al, al, None) == ERANGE  # int32 idx
+    assert f(mis, al, al, None, None, 0, None, None, 1000, 65536, al, 10, al, al, al, al, None) == EALIGN
+    assert f(al, al, al, None, None, 0, None, None, 1000, 1000, al, 10, al, al, al, al, None) == EINVAL
+    assert f(al, al, al, al, None, 10, al, None, 1000, 65536, al, 10, al, al, al, al, None) == EINVAL  # partial
