@@ -210,6 +210,26 @@ def fp8_block_quant(srcs, batch=1):
     return codes, scales
 
 
+def fp8_block_quant_strided(base, src_offsets, src_rows, cols, batch, batch_strides):
+    """Sources inside one flat uint16 buffer: source i of batch entry e is the
+    row-major [src_rows[i], cols] matrix that starts at element
+    src_offsets[i] + e * batch_strides[i] of `base` (the experts of an MoE
+    layer laid gate, up, down after one another).  Returns (codes, scales) as
+    fp8_block_quant does."""
+    base = _c(base, np.uint16).reshape(-1)
+    rows = np.array(src_rows, np.int64)
+    strides = np.array(batch_strides, np.int64)
+    for o, r, st in zip(src_offsets, rows, strides):
+        assert 0 <= o and o + (batch - 1) * st + r * cols <= base.size
+    R = int(rows.sum())
+    codes = np.empty((batch, R, cols), np.uint8)
+    scales = np.empty((batch, (R + 127) // 128, (cols + 127) // 128), np.float32)
+    ptrs = (ctypes.c_void_p * len(rows))(*[base.ctypes.data + 2 * int(o) for o in src_offsets])
+    lib().oracle_fp8_block_quant(ctypes.cast(ptrs, ctypes.c_void_p), _ptr(rows), len(rows), cols,
+                                 batch, _ptr(strides), _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
 def fp8_delta(codes_old, codes_new, scales_old, scales_new, code_cap=None, scale_cap=None):
     """Returns dict(code_idx, code_val, code_count, scale_idx, scale_val, scale_count, status)."""
     co = _c(codes_old, np.uint8).reshape(-1)

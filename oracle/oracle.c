@@ -11,14 +11,19 @@
  *                           textbook nearest-value in binary64.  NaN results are
  *                           our own reading (quiet bit set): parity unpinned.
  *   oracle_cast_diff/compact pinned: numpy flatnonzero, exhaustive tiny inputs.
- *   oracle_apply_patch      pinned: apply(old, patch) == new, version chains.
+ *   oracle_apply_patch      pinned: apply(old, patch) == new, version chains,
+ *                           numpy's fancy assignment on entries in any order.
  *   oracle_lz4_encode_*     pinned: closed-form block sizes and bytes, an
  *                           independent decoder, brute force on tiny inputs.
  *   oracle_lz4_decode_*     pinned: spec-valid random streams with known output,
  *                           corrupt streams.
  *   oracle_e4m3_rne, oracle_fp8_block_quant
  *                           pinned: torch.float8_e4m3fn, nearest-of-set search,
- *                           closed forms for constant blocks, stacking invariant.
+ *                           closed forms for constant blocks, stacking invariant;
+ *                           block by block against numpy's float32 division and
+ *                           torch's E4M3 on ragged edge blocks, stacks whose
+ *                           sources end inside a 128-row band, and batches read
+ *                           at an expert stride larger than the stack.
  *   oracle_fp8_delta, oracle_fp8_apply_delta
  *                           pinned: numpy flatnonzero over the codes and the scale
  *                           bit patterns; apply(quant(old), delta) == quant(new).
@@ -291,8 +296,10 @@ void oracle_lz4_decode_blocks(const uint8_t *payload, int64_t payload_bytes,
         uint64_t off = comp_offsets[bi];
         uint64_t sz = comp_sizes[bi];
         uint64_t end = off + sz < off ? UINT64_MAX : off + sz;
-        /* blocks lie inside the payload, one after another: a block that starts
-         * before the end of an earlier one is malformed (our reading) */
+        /* the payload is the blocks' encodings end to end in block order, the
+         * offsets being the exclusive scan of the sizes; a table in which a
+         * block starts before the end of an earlier one describes no such
+         * payload, and the block is malformed (our reading of that layout) */
         int bad = off > (uint64_t)payload_bytes || sz > (uint64_t)payload_bytes - off ||
                   (bi > 0 && off < end_so_far);
         if (end > end_so_far) end_so_far = end;

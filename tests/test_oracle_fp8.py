@@ -111,6 +111,76 @@ def test_block_quant_against_numpy_division_and_torch():
             assert np.array_equal(codes[0, br * 128:(br + 1) * 128, bc * 128:(bc + 1) * 128], ref)
 
 
+def quant_by_numpy_and_torch(x_u16):
+    """Block by block over a stacked [R, C] BF16 matrix: amax by numpy over the
+    block's valid elements, s = fl32(amax / 448) (numpy float32 division),
+    q = fl32(x / s) (numpy float32 division), codes by torch's E4M3 conversion
+    (|q| stays below 464, where torch and the saturating rule agree)."""
+    xf = as_f32(x_u16)
+    R, C = xf.shape
+    codes = np.empty((R, C), np.uint8)
+    scales = np.empty(((R + 127) // 128, (C + 127) // 128), np.float32)
+    for br in range(scales.shape[0]):
+        for bc in range(scales.shape[1]):
+            rs, cs = slice(br * 128, min(R, br * 128 + 128)), slice(bc * 128, min(C, bc * 128 + 128))
+            blk = xf[rs, cs]
+            amax = np.float32(np.abs(blk).max())
+            s = np.float32(1.0) if amax == 0 else np.float32(amax / np.float32(448.0))
+            q = (blk / s).astype(np.float32)
+            assert np.all(np.abs(q) < 464)
+            codes[rs, cs] = torch.from_numpy(np.ascontiguousarray(q)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            scales[br, bc] = s
+    return codes, scales
+
+
+def ragged_source(rng, shape, seed_scale=0.02):
+    """BF16 weights with blocks at very different scales: normal, subnormal,
+    all zero and constant stretches, so edge blocks see every scale rule."""
+    w = bf16(rng.standard_normal(shape) * seed_scale)
+    r, c = shape
+    if r > 3 and c > 3:
+        w[: r // 3, : c // 3] = bf16(rng.standard_normal((r // 3, c // 3)) * 1e-39)
+        w[r // 2:, c // 2:] = 0
+        w[r - 1, :] = bf16([0.75])[0]
+    return w
+
+
+def test_block_quant_ragged_shapes_against_numpy_and_torch():
+    """Edge blocks (rows or columns not a multiple of 128) use only their valid
+    elements; each of them checked against numpy's division and torch's E4M3,
+    block by block, for single sources and for a stack whose second source
+    starts and ends inside a 128-row band."""
+    rng = np.random.default_rng(12)
+    for shapes in ([(200, 136)], [(7, 8)], [(130, 264), (5, 264)], [(1, 1)], [(129, 127)]):
+        srcs = [ragged_source(rng, sh) for sh in shapes]
+        codes, scales = oracle.fp8_block_quant(srcs)
+        ref_c, ref_s = quant_by_numpy_and_torch(np.concatenate(srcs, 0))
+        assert np.array_equal(codes[0], ref_c), shapes
+        assert np.array_equal(scales[0].view(np.uint32), ref_s.view(np.uint32)), shapes
+
+
+def test_block_quant_batch_strides_against_numpy_and_torch():
+    """A batch of 3 experts laid [gate; up; down] one after another in one
+    buffer: [gate; up] of expert e read at a stride of the whole expert (not
+    the stacked sources' own size), with ragged rows and columns."""
+    rng = np.random.default_rng(13)
+    F, H = 72, 136  # gate/up [F, H], down [H, F]
+    E = 3
+    expert = 3 * F * H
+    base = np.concatenate([ragged_source(rng, (F, H), 0.02 * (1 + e)).reshape(-1) for e in range(3 * E)])
+    assert base.size == E * expert
+    codes, scales = oracle.fp8_block_quant_strided(base, [0, F * H], [F, F], H, E, [expert, expert])
+    downc, downs = oracle.fp8_block_quant_strided(base, [2 * F * H], [H], F, E, [expert])
+    for e in range(E):
+        g = base[e * expert: e * expert + F * H].reshape(F, H)
+        u = base[e * expert + F * H: e * expert + 2 * F * H].reshape(F, H)
+        d = base[e * expert + 2 * F * H: (e + 1) * expert].reshape(H, F)
+        rc, rs = quant_by_numpy_and_torch(np.concatenate([g, u], 0))
+        assert np.array_equal(codes[e], rc) and np.array_equal(scales[e].view(np.uint32), rs.view(np.uint32)), e
+        rc, rs = quant_by_numpy_and_torch(d)
+        assert np.array_equal(downc[e], rc) and np.array_equal(downs[e].view(np.uint32), rs.view(np.uint32)), e
+
+
 def test_constant_block_closed_form():
     for c in (0.75, -3.0, 1e-3, 2.0 ** -130):
         w = np.full((128, 128), bf16([c])[0], np.uint16)

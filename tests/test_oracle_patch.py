@@ -88,6 +88,25 @@ def test_apply_skips_bad_indices():
     assert list(got) == [0, 100, 2, 400, 4, 5, 6, 7, 8, 9]
 
 
+def test_apply_in_any_entry_order():
+    """The definition b[idx[k]] = val[k] does not depend on the entries' order
+    when the indices are unique: a patch in random order equals numpy's fancy
+    assignment, and out-of-range entries met in any order are skipped."""
+    rng = np.random.default_rng(17)
+    b = rng.integers(0, 1 << 16, 5000, dtype=np.uint16)
+    idx = rng.permutation(5000)[:1700].astype(np.int32)
+    assert np.any(np.diff(idx) < 0)
+    val = rng.integers(0, 1 << 16, idx.size, dtype=np.uint16)
+    got, st = oracle.apply_patch(b, idx, val)
+    ref = b.copy()
+    ref[idx] = val
+    assert st == 0 and np.array_equal(got, ref)
+    b10 = np.arange(10, dtype=np.uint16)
+    got, st = oracle.apply_patch(b10, np.array([1, 10, -1, 3], np.int32), np.array([100, 200, 300, 400], np.uint16))
+    assert st == oracle.BADINDEX
+    assert list(got) == [0, 100, 2, 400, 4, 5, 6, 7, 8, 9]
+
+
 def test_patch_chain_has_no_drift():
     """B_t = apply(B_{t-1}, P_t) equals the direct cast of W_t at every step
     [Jiang talk 11:08-11:30: replacement bits, no additive drift; 16:52-16:58:
