@@ -70,7 +70,11 @@ __global__ __launch_bounds__(256) void k_apply_patch(uint16_t *__restrict__ b, i
                 const bool live = k < count;
                 const bool in = i >= 0 && i < n;
                 bad |= live && !in;
-                raw_buffer_store_u16(vv[q], rsrc, live && in ? 2 * i : off_none, 0, 0);
+                // byte offset of element i: 2 i < 2^32 because n <= 2^31 - 1 (the
+                // entry point's range check), computed unsigned so that
+                // i >= 2^30 does not overflow a signed product
+                const int32_t off = (int32_t)(2u * (uint32_t)i);
+                raw_buffer_store_u16(vv[q], rsrc, live && in ? off : off_none, 0, 0);
             }
             ready(ni, nv);
 #pragma unroll
