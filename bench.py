@@ -84,7 +84,7 @@ def parse():
                         "receives chunk c - 1; serial: one lz4_decode_blocks call per chunk, one stream")
     p.add_argument("--cpu-sample-frac", type=float, default=1.0,
                    help="fraction of the oracle's sample (decoder layer 0) it times")
-    p.add_argument("--next", default="loco,patch,list", help="next-row legs measured after the timed steps, comma "
+    p.add_argument("--next", default="loco,patch,list,fp8", help="next-row legs measured after the timed steps, comma "
                    "separated: loco (PULSELoCo gate), patch (patch-stream compression), list (one launch over the "
                    "tensor list), fp8 (FP8-view deltas), none")
     p.add_argument("--copy-probe-gib", type=float, default=0.0,
