@@ -87,8 +87,14 @@ def parse():
     p.add_argument("--next", default="loco,patch,list,fp8", help="next-row legs measured after the timed steps, comma "
                    "separated: loco (PULSELoCo gate), patch (patch-stream compression), list (one launch over the "
                    "tensor list), fp8 (FP8-view deltas), none")
-    p.add_argument("--copy-probe-gib", type=float, default=0.0,
-                   help="also run a plain device copy of this size (scale reference for HBM counters)")
+    p.add_argument("--probe-gib", type=float, default=4.0,
+                   help="GiB per stream of the achievable-bandwidth probes (0: skip them)")
+    p.add_argument("--encode-apply-reps", type=int, default=3,
+                   help="timed passes of the patch path alone (pulse_cast_diff + pulse_apply_patch; 0: skip)")
+    p.add_argument("--lr-sweep", default="2.5e-7,3e-8",
+                   help="learning rates at which the step is measured again (comma separated; empty: skip)")
+    p.add_argument("--configs", default="c1,c3,c4,c5",
+                   help="other configurations measured after the main one (c1,c3,c4,c5 or none)")
     return p.parse_args()
 
 
@@ -545,48 +551,106 @@ def main():
         "setup_s": round(t_setup, 1),
     }
 
-    if args.copy_probe_gib > 0:
-        nb = int(args.copy_probe_gib * 2**30)
-        a = torch.empty(nb, dtype=torch.uint8, device=dev)
-        b = torch.empty(nb, dtype=torch.uint8, device=dev)
-        b.copy_(a)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        b.copy_(a)
-        e1.record()
-        torch.cuda.synchronize()
-        result["copy_probe"] = {"bytes": 2 * nb, "ms": round(e0.elapsed_time(e1), 3),
-                                "GBps": round(2 * nb / (e0.elapsed_time(e1) / 1e3) / 1e9, 1)}
-        del a, b
+    # ---- the metric's own quantity: patch-path encode + apply (pulse_cast_diff,
+    # then pulse_apply_patch), per chunk over the same set, outside the step
+    if args.encode_apply_reps > 0:
+        result["encode_apply"] = encode_apply_leg(pulse, chunks, W, b_old, b_recv, stage, idx, val, status, ws_cd,
+                                                  args.encode_apply_reps, dev)
+        log(f"encode+apply: {result['encode_apply']['ms']:.2f} ms, {result['encode_apply']['GBps_weights']:.1f} "
+            "GB/s of weights")
+
+    # ---- the same step at the pages' densities (lr sweep), then the masters at lr 3e-6 again
+    lrs = [float(x) for x in args.lr_sweep.split(",") if x]
+    if lrs:
+        sweep = []
+        tmp = torch.empty(max_tensor, dtype=torch.float32, device=dev)
+
+        def masters_at(lr):
+            for ti, s in enumerate(specs):
+                w = W[offs[ti]: offs[ti] + s.numel]
+                workload.fill_init(w, 2, ti, s.kind)
+                workload.apply_step(w, 2, ti, 1, lr=lr, tmp=tmp)
+            torch.cuda.synchronize()
+
+        for lr in lrs:
+            masters_at(lr)
+            run_step(False)
+            torch.cuda.synchronize()
+            if int(status.item()) != 0 or not views_equal(b_recv, b_old):
+                raise SystemExit(f"lr {lr}: status {int(status.item())} or the receiver did not return to v0")
+            for k in ev:
+                ev[k].clear()
+            parse_ev["lz4_decode"].clear()
+            ks = max(1, min(args.steps, 5))
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(ks):
+                run_step(True)
+            torch.cuda.synchronize()
+            ms_lr = 1e3 * (time.perf_counter() - t0) / ks
+            d_lr = int(cnt.sum().item()) / n
+            c_lr = int(ctotal.sum().item()) / n
+            sms = {k: round(sum(a.elapsed_time(b) for a, b in ev[k]) / ks, 3) for k in stages}
+            sweep.append({"lr": lr, "changed_fraction": round(d_lr, 6), "lz4_bytes_per_param": round(c_lr, 5),
+                          "ms_per_step": round(ms_lr, 3), "GBps_weights_step": round(2 * n / (ms_lr / 1e3) / 1e9, 1),
+                          "stage_ms": sms, "steps": ks})
+            log(f"lr {lr}: {ms_lr:.2f} ms per step, changed {100 * d_lr:.3f}%")
+        masters_at(workload.LR)
+        del tmp
+        result["lr_sweep"] = sweep
 
     if not args.no_cpu_baseline:
         log("timing the oracle on the host")
         result["cpu_baseline"] = cpu_baseline(specs, offs, W, b_old, args.cpu_sample_frac)
 
     legs = set(x for x in args.next.split(",") if x and x != "none")
-    if legs:
-        # the next rows, measured after (and outside) the timed steps
-        nxt = {}
-        if "patch" in legs:
-            nxt.update(patch_stream_leg(pulse, chunks, W, b_old, stage, idx, val, cnt, status, ws_cd, dev,
-                                        not args.no_cpu_baseline))
-        if "fp8" in legs:
-            nxt.update(fp8_view_leg(pulse, specs, chunks, offs, qplans, W, b_old, stage, dev,
+    nxt = {}
+    if "patch" in legs:
+        nxt.update(patch_stream_leg(pulse, chunks, W, b_old, stage, idx, val, cnt, status, ws_cd, dev,
                                     not args.no_cpu_baseline))
-        del stage, b_recv, idx, val, payload, codes, scales, gplans, tiles, bufs  # gplans holds views of b_recv
-        if recv_fused:
-            del aq_plans, ws_aq  # the plans hold the codes and scales they point into
-        torch.cuda.synchronize()
-        torch.cuda.empty_cache()
-        if "list" in legs:
-            nxt.update(tensor_list_leg(pulse, specs, offs, W, b_old, changed, dev))
-        del W, b_old
-        torch.cuda.synchronize()
-        torch.cuda.empty_cache()
-        if "loco" in legs:
-            nxt.update(loco_leg(pulse, dev, not args.no_cpu_baseline))
+    if "fp8" in legs:
+        nxt.update(fp8_view_leg(pulse, specs, chunks, offs, qplans, W, b_old, stage, dev,
+                                not args.no_cpu_baseline))
+    del stage, b_recv, idx, val, payload, codes, scales, gplans, tiles, bufs  # gplans holds views of b_recv
+    if recv_fused:
+        del aq_plans, ws_aq  # the plans hold the codes and scales they point into
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if "list" in legs:
+        nxt.update(tensor_list_leg(pulse, specs, offs, W, b_old, changed, dev))
+    del W, b_old
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if "loco" in legs:
+        nxt.update(loco_leg(pulse, dev, not args.no_cpu_baseline))
+    if nxt:
         result["next_rows"] = nxt
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    # ---- achievable bandwidth on this GPU, and each stage against the probe of its mix
+    if args.probe_gib > 0:
+        ach = achievable_probes(dev, gib=args.probe_gib)
+        result["achievable"] = ach
+        for k in stages:
+            add_achievable(st_out[k], ach, READ_FRACTION[k](d, c))
+        if "encode_apply" in result:
+            add_achievable(result["encode_apply"], ach, READ_FRACTION["encode_apply"](d, c))
+        rf = READ_FRACTION[dom](d, c)
+        name, gbps = nearest_probe(ach, rf)
+        roofline["achievable"] = {"probe": name, "GBps": gbps, "frac": round(roofline["achieved"] / gbps, 4)}
+
+    # ---- the other configurations, each on its own
+    cfgs = [x for x in args.configs.split(",") if x and x != "none"]
+    if cfgs:
+        per = {}
+        fns = {"c1": config_c1, "c3": config_c3, "c4": config_c4, "c5": config_c5}
+        for k in cfgs:
+            log(f"configuration {k}")
+            per[k] = fns[k](pulse, dev)
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+        result["configs"] = per
     print(json.dumps(result), flush=True)
 
 
@@ -932,41 +996,497 @@ def loco_leg(pulse, dev, with_oracle):
     return out
 
 
-def cpu_baseline(specs, offs, W, b_old, frac):
-    """The oracle (plain single-threaded C) on a bounded sample of the same
-    workload: decoder layer 0 (its 12 tensors, about 488 M parameters, some
-    10-15 s of CPU work), all five steps over host copies of the same inputs,
-    FP8 on the layer's stacked groups.  `frac` < 1 shortens the sample (the
-    FP8 step is then skipped)."""
+# ---------------------------------------------------------------------------
+# read share of each stage's algorithmic bytes (d: changed fraction, c: LZ4
+# bytes per element), to pick the probe with the same read:write mix
+READ_FRACTION = {
+    "encode": lambda d, c: 6 / (8 + 6 * d + c),
+    "cast_diff": lambda d, c: 6 / (8 + 6 * d),
+    "receiver": lambda d, c: (2 + 6 * d) / (3 + 8 * d),
+    "apply_patch": lambda d, c: 0.75,
+    "fp8_quant": lambda d, c: 2 / 3,
+    "lz4_encode": lambda d, c: 4 / (4 + c),
+    "lz4_decode": lambda d, c: (2 + c) / (4 + c),
+    "encode_apply": lambda d, c: (6 + 6 * d) / (8 + 14 * d),
+}
+
+
+def encode_apply_leg(pulse, chunks, W, b_old, b_recv, stage, idx, val, status, ws_cd, reps, dev):
+    """The metric's own quantity, the patch path alone: pulse_cast_diff (cast,
+    diff and compaction against the old view, the new view written) then
+    pulse_apply_patch into the receiver's view, chunk by chunk over the same
+    set; one checked pass, then `reps` timed passes.  Every pass after the
+    first writes the same values to the same positions (the same stores); the
+    receiver's view is set back to the old view afterwards."""
+    import torch
+
+    cnt = torch.zeros(len(chunks), dtype=torch.int64, device=dev)
+    cap = idx.numel()
+    te = ta = 0.0
+    for r in range(reps + 1):
+        ev = []
+        for ci, (s0, e0, _) in enumerate(chunks):
+            m = e0 - s0
+            e = [_ev() for _ in range(3)]
+            e[0].record()
+            pulse.pulse_cast_diff(W[s0:e0], b_old[s0:e0], stage[:m], None, idx, val, cnt[ci:ci + 1], status, ws_cd)
+            e[1].record()
+            pulse.pulse_apply_patch(b_recv[s0:e0], idx, val, cnt[ci:ci + 1], status, max_count=cap)
+            e[2].record()
+            ev.append(e)
+            if r == 0 and not views_equal(b_recv[s0:e0], stage[:m]):
+                raise SystemExit(f"encode+apply: chunk {ci}: the patched view differs from the new view")
+        torch.cuda.synchronize()
+        if r:
+            te += sum(e[0].elapsed_time(e[1]) for e in ev)
+            ta += sum(e[1].elapsed_time(e[2]) for e in ev)
+    if int(status.item()) != 0:
+        raise SystemExit(f"encode+apply: device status {int(status.item())}")
+    b_recv.copy_(b_old)
+    torch.cuda.synchronize()
+    n = sum(e - s for s, e, _ in chunks)
+    d = int(cnt.sum().item()) / n
+    me, ma = te / reps, ta / reps
+    a_enc, a_app = n * (8 + 6 * d), n * 8 * d
+    secs = (me + ma) / 1e3
+    return {"ms": round(me + ma, 3), "encode_ms": round(me, 3), "apply_ms": round(ma, 3),
+            "GBps_weights": round(2 * n / secs / 1e9, 1), "alg_GB": round((a_enc + a_app) / 1e9, 3),
+            "GBps": round((a_enc + a_app) / secs / 1e9, 1), "frac_hbm": round((a_enc + a_app) / secs / PEAK_HBM, 4),
+            "encode_frac_hbm": round(a_enc / (me / 1e3) / PEAK_HBM, 4),
+            "apply_frac_hbm": round(a_app / (ma / 1e3) / PEAK_HBM, 4), "launches": 2 * len(chunks),
+            "calls": "pulse_cast_diff, then pulse_apply_patch, per chunk",
+            "alg_bytes_per_element": "8 + 6 d (encode) + 8 d (apply)"}
+
+
+# ---------------------------------------------------------------------------
+# achievable bandwidth: our own 16-byte non-temporal streams
+PROBE_MIXES = {"read": (1, 0), "write": (0, 1), "copy": (1, 1), "read2_write1": (2, 1), "read3_write1": (3, 1)}
+
+
+def achievable_probes(dev, gib=4.0, reps=5, blocks=4096):
+    """Plain streams (sparse_delta_codec_amd/csrc/probe.hip, 16-byte
+    non-temporal loads and stores, 4 KiB per wave and stream per step) over
+    `gib` GiB per stream, at the read:write mixes of the codec's kernels; the
+    median of `reps` timed launches after one untimed.  A torch device copy is
+    reported beside them."""
+    import ctypes
+
+    import torch
+
+    L = ctypes.CDLL(os.path.join(ROOT, "sparse_delta_codec_amd", "libpulse_probe.so"))
+    L.probe_stream.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                                       ctypes.c_int32, ctypes.c_void_p]
+    L.probe_stream.restype = ctypes.c_int
+    n = int(gib * 2 ** 30) // 16
+    bufs = [torch.full((n * 16,), k + 1, dtype=torch.uint8, device=dev) for k in range(4)]
+    ptr = [ctypes.c_void_p(b.data_ptr()) for b in bufs]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    out = {}
+
+    def timed(fn):
+        ts = []
+        for r in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            if r:
+                ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[len(ts) // 2]
+
+    for name, (nr, w) in PROBE_MIXES.items():
+        def fn():
+            rc = L.probe_stream(ptr[0], ptr[1], ptr[2], ptr[3], n, nr, w, blocks, stream)
+            if rc != 0:
+                raise SystemExit(f"probe {name}: launch failed ({rc})")
+        ms = timed(fn)
+        out[name] = {"GBps": round((nr + w) * n * 16 / (ms / 1e3) / 1e9, 1), "read_fraction": round(nr / (nr + w), 3)}
+    ms = timed(lambda: bufs[3].copy_(bufs[0]))
+    out["torch_copy"] = {"GBps": round(2 * n * 16 / (ms / 1e3) / 1e9, 1), "read_fraction": 0.5}
+    del bufs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def nearest_probe(achievable, read_fraction):
+    """The probe whose read:write mix is closest to a kernel's (by read share of its bytes)."""
+    name = min(PROBE_MIXES, key=lambda k: abs(PROBE_MIXES[k][0] / sum(PROBE_MIXES[k]) - read_fraction))
+    return name, achievable[name]["GBps"]
+
+
+def add_achievable(block, achievable, read_fraction):
+    name, gbps = nearest_probe(achievable, read_fraction)
+    block["achievable"] = {"probe": name, "GBps": gbps, "frac": round(block["GBps"] / gbps, 4)}
+
+
+# ---------------------------------------------------------------------------
+# the oracle on the host cores
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_sample_run(w, bo, groups, workers, block=BLOCK):
+    """The whole hot path on the oracle over host arrays (w: float32 masters,
+    bo: the old BF16 view, groups: FP8 stacks as [(offset, shape)]), its calls
+    spread over `workers` threads, one independent piece per call: ranges of
+    whole LZ4 blocks for cast + diff + compaction, apply, LZ4 encode and
+    decode + XOR; 128-row bands for FP8.  Returns the seconds taken."""
+    import concurrent.futures
+
     import numpy as np
 
     import oracle
 
+    piece = 1 << 24
+    rng = [(a, min(w.size, a + piece)) for a in range(0, w.size, piece)]
+    pool = concurrent.futures.ThreadPoolExecutor(workers)
+    recv = np.empty_like(bo)
+    t = time.perf_counter()
+
+    def step_patch(r):
+        a, b = r
+        res = oracle.cast_diff(w[a:b], bo[a:b], want_mask=False)
+        recv[a:b] = oracle.apply_patch(bo[a:b], res["idx"], res["val"])[0]
+        enc = oracle.lz4_encode_blocks(bo[a:b], block, src_xor=res["b_new"])
+        oracle.lz4_decode_blocks(enc["payload"], enc["offsets"], enc["sizes"], recv[a:b], mode=1)
+    list(pool.map(step_patch, rng))
+    bands = []
+    for g in groups:
+        R, cols = sum(sh[0] for _, sh in g), g[0][1][1]
+        for r0 in range(0, R, 128):
+            bands.append((g, r0, min(R, r0 + 128), cols))
+
+    def step_fp8(band):
+        g, r0, r1, cols = band
+        parts, base = [], 0
+        for off, sh in g:
+            a, b = max(r0, base), min(r1, base + sh[0])
+            if a < b:
+                parts.append(recv[off + (a - base) * cols: off + (b - base) * cols].reshape(b - a, cols))
+            base += sh[0]
+        oracle.fp8_block_quant([parts[0] if len(parts) == 1 else np.concatenate(parts, 0)])
+    list(pool.map(step_fp8, bands))
+    secs = time.perf_counter() - t
+    pool.shutdown()
+    return secs
+
+
+def cpu_baseline(specs, offs, W, b_old, frac):
+    """The oracle (plain single-threaded C calls) on a bounded sample of the same
+    workload, decoder layer 0 (its 12 tensors, about 488 M parameters): all
+    five steps over host copies of the same inputs, FP8 on the layer's stacked
+    groups.  Timed with its calls on one host thread (about 13 s) and spread
+    over every usable host core (one independent piece per call).  `frac` < 1
+    shortens the sample (the FP8 step is then skipped)."""
     lay = [i for i, s in enumerate(specs) if s.name.startswith("l0.")]
     last = lay[-1]
     s0, e0 = offs[lay[0]], offs[last] + specs[last].numel
     m = int((e0 - s0) * min(frac, 1.0)) // 8 * 8
+    import numpy as np
+
     w = W[s0:s0 + m].cpu().numpy()
     bo = b_old[s0:s0 + m].cpu().numpy().view(np.uint16)
     groups = []
     if frac >= 1.0:
         for g in quant_groups(specs, lay):
             groups.append([(offs[i] - s0, specs[i].shape) for i in g])
-    log(f"oracle sample: {m} params")
-    t = time.perf_counter()
-    r = oracle.cast_diff(w, bo, want_mask=False)
-    recv, _ = oracle.apply_patch(bo, r["idx"], r["val"])
-    log(f"oracle cast+diff+compact and apply done ({time.perf_counter() - t:.1f} s)")
-    for g in groups:
-        oracle.fp8_block_quant([recv[o:o + sh[0] * sh[1]].reshape(sh) for o, sh in g])
-    log(f"oracle FP8 done ({time.perf_counter() - t:.1f} s)")
-    enc = oracle.lz4_encode_blocks(bo, BLOCK, src_xor=r["b_new"])
-    oracle.lz4_decode_blocks(enc["payload"], enc["offsets"], enc["sizes"], recv, mode=1)
-    secs = time.perf_counter() - t
-    log(f"oracle LZ4 done ({secs:.1f} s)")
-    return {"value": round(2 * m / secs / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"decoder layer 0 of the same workload ({m} params"
-                      f"{'' if frac >= 1 else ', FP8 step skipped'}), all five steps, {secs:.1f} s"}
+    cores = len(os.sched_getaffinity(0))
+    log(f"oracle sample: {m} params, 1 thread")
+    t1 = oracle_sample_run(w, bo, groups, 1)
+    log(f"oracle sample: {t1:.1f} s on 1 thread; now {cores} threads")
+    tn = oracle_sample_run(w, bo, groups, cores)
+    log(f"oracle sample: {tn:.1f} s on {cores} threads")
+    what = (f"decoder layer 0 of the same workload ({m} params{'' if frac >= 1 else ', FP8 step skipped'}), "
+            f"all five steps")
+    return {"value": round(2 * m / tn / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{what}, {tn:.2f} s on {cores} host threads", "cpu_model": cpu_model(),
+            "one_core": {"value": round(2 * m / t1 / 1e9, 3), "unit": "GB/s", "cores": 1,
+                         "sample": f"{what}, {t1:.1f} s on one host thread"}}
+
+
+# ---------------------------------------------------------------------------
+# the other configurations (each on its own, after the main workload is freed)
+def _ev():
+    import torch
+
+    return torch.cuda.Event(enable_timing=True)
+
+
+def _flush(buf, k):
+    buf.fill_(k & 0xFF)  # rewrites 512 MiB: the 256 MB MALL and the L2s hold none of the next inputs
+
+
+def config_c1(pulse, dev, reps=20):
+    """C1: one 4096 x 1024 FP32 tensor (numpy default_rng(0)), one step:
+    pulse_cast_diff (cast, diff, patch; new view written) then
+    pulse_apply_patch into a copy of the old view; caches flushed before each
+    rep, median of `reps`."""
+    import numpy as np
+    import torch
+
+    import workload
+
+    w0, w1 = workload.c1_masters()
+    n = w0.size
+    W0 = torch.from_numpy(w0.reshape(-1)).to(dev)
+    W1 = torch.from_numpy(w1.reshape(-1)).to(dev)
+    b0 = torch.empty(n, dtype=torch.int16, device=dev)
+    pulse.pulse_cast_diff(W0, b_new=b0)
+    recv, stage = torch.empty_like(b0), torch.empty_like(b0)
+    idx, val = torch.empty(n, dtype=torch.int32, device=dev), torch.empty(n, dtype=torch.int16, device=dev)
+    cnt, st = torch.zeros(1, dtype=torch.int64, device=dev), torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = pulse.workspace(pulse.PULSE_OP_CAST_DIFF, n, 0, dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    te, ta = [], []
+    for r in range(reps + 2):
+        recv.copy_(b0)
+        _flush(flush, r)
+        e = [_ev() for _ in range(3)]
+        e[0].record()
+        pulse.pulse_cast_diff(W1, b0, stage, None, idx, val, cnt, st, ws)
+        e[1].record()
+        pulse.pulse_apply_patch(recv, idx, val, cnt, st, max_count=n)
+        e[2].record()
+        torch.cuda.synchronize()
+        if r >= 2:
+            te.append(e[0].elapsed_time(e[1]))
+            ta.append(e[1].elapsed_time(e[2]))
+    if int(st.item()) != 0 or not torch.equal(recv, stage):
+        raise SystemExit("C1: the patched old view differs from the new view")
+    count = int(cnt.item())
+    d = count / n
+    me, ma = float(np.median(te)), float(np.median(ta))
+    a = n * (8 + 6 * d) + n * 8 * d
+    return {"workload": "C1: 4096x1024 FP32, one step at lr 3e-6", "params": n, "changed_fraction": round(d, 6),
+            "encode_us": round(1e3 * me, 1), "apply_us": round(1e3 * ma, 1),
+            "GBps_weights": round(2 * n / ((me + ma) / 1e3) / 1e9, 1),
+            "alg_GB": round(a / 1e9, 4), "frac_hbm": round(a / ((me + ma) / 1e3) / PEAK_HBM, 4),
+            "note": f"median of {reps}, caches flushed before each rep; launch-bound at this size"}
+
+
+def config_c3(pulse, dev, steps=20):
+    """C3: the Llama-3-8B-shaped set, 20 chained steps.  Per step and chunk:
+    pulse_cast_diff against the sender's view (updated in place) and
+    pulse_apply_patch into the receiver's view; after the last step the
+    receiver's view must equal the sender's."""
+    import torch
+
+    import workload
+
+    specs = workload.llama3_8b_specs()
+    n = workload.total_numel(specs)
+    chunks, offs = build_plan(specs)
+    mc = max(e - s for s, e, _ in chunks)
+    W = torch.empty(n, dtype=torch.float32, device=dev)
+    prev = torch.empty(n, dtype=torch.int16, device=dev)
+    for ti, s in enumerate(specs):
+        workload.fill_init(W[offs[ti]: offs[ti] + s.numel], 3, ti, s.kind)
+        pulse.pulse_cast_diff(W[offs[ti]: offs[ti] + s.numel], b_new=prev[offs[ti]: offs[ti] + s.numel])
+    recv = prev.clone()
+    cap = int(mc * PATCH_CAP_FRAC)
+    idx, val = torch.empty(cap, dtype=torch.int32, device=dev), torch.empty(cap, dtype=torch.int16, device=dev)
+    cnt = torch.zeros(len(chunks), dtype=torch.int64, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = pulse.workspace(pulse.PULSE_OP_CAST_DIFF, mc, 0, dev)
+    tmp = torch.empty(max(s.numel for s in specs), dtype=torch.float32, device=dev)
+    te = ta = 0.0
+    changed = 0
+    for step in range(1, steps + 1):
+        for ti, s in enumerate(specs):
+            workload.apply_step(W[offs[ti]: offs[ti] + s.numel], 3, ti, step, tmp=tmp)
+        ev = []
+        for ci, (s0, e0, _) in enumerate(chunks):
+            e = [_ev() for _ in range(3)]
+            e[0].record()
+            pulse.pulse_cast_diff(W[s0:e0], prev[s0:e0], prev[s0:e0], None, idx, val, cnt[ci:ci + 1], st, ws)
+            e[1].record()
+            pulse.pulse_apply_patch(recv[s0:e0], idx, val, cnt[ci:ci + 1], st, max_count=cap)
+            e[2].record()
+            ev.append(e)
+        torch.cuda.synchronize()
+        te += sum(e[0].elapsed_time(e[1]) for e in ev)
+        ta += sum(e[1].elapsed_time(e[2]) for e in ev)
+        changed += int(cnt.sum().item())
+    if int(st.item()) != 0 or not views_equal(recv, prev):
+        raise SystemExit("C3: the chained receiver view differs from the sender's after the last step")
+    d = changed / (n * steps)
+    me, ma = te / steps, ta / steps
+    a = n * (8 + 6 * d) + n * 8 * d
+    return {"workload": f"C3: Llama-3-8B-shaped set, {steps} chained steps at lr 3e-6", "params": n,
+            "changed_fraction": round(d, 6), "encode_ms_per_step": round(me, 3), "apply_ms_per_step": round(ma, 3),
+            "GBps_weights": round(2 * n / ((me + ma) / 1e3) / 1e9, 1), "alg_GB_per_step": round(a / 1e9, 3),
+            "frac_hbm": round(a / ((me + ma) / 1e3) / PEAK_HBM, 4),
+            "checked": "receiver view == sender view after the last step"}
+
+
+def config_c4(pulse, dev, reps=3):
+    """C4: the first 16e9 elements of the C2 set as two BF16 views; the XOR
+    mask LZ4-encoded in 64 KiB blocks (lz4_encode_blocks over both views, the
+    mask never written), then decoded and XORed into the old view in place
+    (lz4_decode_blocks); every second decode takes the view back."""
+    import torch
+
+    import workload
+
+    specs = workload.qwen25_32b_specs()
+    n = workload.C4_NUMEL
+    old = torch.empty(n, dtype=torch.int16, device=dev)
+    new = torch.empty(n, dtype=torch.int16, device=dev)
+    tmp = torch.empty(max(s.numel for s in specs), dtype=torch.float32, device=dev)
+    tmp2 = torch.empty_like(tmp)
+    o = 0
+    for ti, s in enumerate(specs):
+        if o >= n:
+            break
+        k = min(s.numel, n - o)
+        w = tmp[: s.numel]
+        workload.fill_init(w, 2, ti, s.kind)
+        pulse.pulse_cast_diff(w[:k], b_new=old[o:o + k])
+        workload.apply_step(w, 2, ti, 1, tmp=tmp2)
+        pulse.pulse_cast_diff(w[:k], b_new=new[o:o + k])
+        o += k
+    del tmp, tmp2
+    nbytes = 2 * n
+    nb = (nbytes + BLOCK - 1) // BLOCK
+    payload = torch.empty(int(nbytes * PAYLOAD_CAP_FRAC), dtype=torch.uint8, device=dev)
+    sizes = torch.empty(nb, dtype=torch.int32, device=dev)
+    offsets = torch.empty(nb, dtype=torch.int64, device=dev)
+    total = torch.zeros(1, dtype=torch.int64, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = pulse.workspace(pulse.PULSE_OP_LZ4_ENCODE, nbytes, BLOCK, dev)
+    te, td = [], []
+    for r in range(reps + 1):
+        e = [_ev() for _ in range(2)]
+        e[0].record()
+        pulse.lz4_encode_blocks(old, payload, sizes, offsets, total, st, ws, src_xor=new)
+        e[1].record()
+        torch.cuda.synchronize()
+        if r:
+            te.append(e[0].elapsed_time(e[1]))
+    tot = int(total.item())
+    dws = pulse.workspace(pulse.PULSE_OP_LZ4_DECODE, nb, tot, dev)
+    for r in range(2 * reps):
+        e = [_ev() for _ in range(2)]
+        e[0].record()
+        pulse.lz4_decode_blocks(payload, offsets, sizes, old, st, dws, mode=1, payload_bytes=tot)
+        e[1].record()
+        torch.cuda.synchronize()
+        td.append(e[0].elapsed_time(e[1]))
+        if r == 0 and not views_equal(old, new):
+            raise SystemExit("C4: decode + XOR did not rebuild the new view")
+    if int(st.item()) != 0:
+        raise SystemExit(f"C4: device status {int(st.item())}")
+    c = tot / n
+    me, md = sum(te) / len(te), sum(td) / len(td)
+    a_enc, a_dec = n * (4 + c), n * (4 + c)
+    return {"workload": "C4: first 16e9 elements of the C2 set, XOR mask LZ4 path", "params": n,
+            "compressed_bytes": tot, "ratio_of_mask": round(tot / nbytes, 5),
+            "encode_ms": round(me, 3), "encode_GBps_alg": round(a_enc / (me / 1e3) / 1e9, 1),
+            "encode_frac_hbm": round(a_enc / (me / 1e3) / PEAK_HBM, 4),
+            "decode_ms": round(md, 3), "decode_GBps_mask": round(nbytes / (md / 1e3) / 1e9, 1),
+            "decode_frac_hbm": round(a_dec / (md / 1e3) / PEAK_HBM, 4),
+            "GBps_weights": round(2 * n / ((me + md) / 1e3) / 1e9, 1),
+            "checked": "decode + XOR rebuilds the new view"}
+
+
+def config_c5(pulse, dev, reps=3, experts_per_chunk=48):
+    """C5: the Kimi-K2-shaped MoE layer share.  The sender: pulse_cast_diff
+    (new view written) per chunk of 48 experts (and one for q/k/v); the
+    receiver: pulse_apply_quant per chunk, the patch applied and [gate; up]
+    per expert, down per expert and [q; k; v] quantised to E4M3 with FP32
+    128x128 scales in one read of the view."""
+    import torch
+
+    import workload
+
+    specs = workload.kimi_k2_layer_specs()
+    n = workload.total_numel(specs)
+    offs = [0]
+    for s in specs:
+        offs.append(offs[-1] + s.numel)
+    E = 384
+    chunks = [(3 * e0, 3 * min(E, e0 + experts_per_chunk)) for e0 in range(0, E, experts_per_chunk)]
+    chunks.append((3 * E, len(specs)))
+    mc = max(offs[b] - offs[a] for a, b in chunks)
+    W = torch.empty(n, dtype=torch.float32, device=dev)
+    b = torch.empty(n, dtype=torch.int16, device=dev)
+    tmp = torch.empty(max(s.numel for s in specs), dtype=torch.float32, device=dev)
+    for ti, s in enumerate(specs):
+        w = W[offs[ti]: offs[ti + 1]]
+        workload.fill_init(w, 5, ti, s.kind)
+        pulse.pulse_cast_diff(w, b_new=b[offs[ti]: offs[ti + 1]])
+        workload.apply_step(w, 5, ti, 1, tmp=tmp)
+    del tmp
+    recv = b.clone()
+    stage = torch.empty(mc, dtype=torch.int16, device=dev)
+    cap = int(mc * PATCH_CAP_FRAC)
+    idx, val = torch.empty(cap, dtype=torch.int32, device=dev), torch.empty(cap, dtype=torch.int16, device=dev)
+    cnt = torch.zeros(len(chunks), dtype=torch.int64, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = pulse.workspace(pulse.PULSE_OP_CAST_DIFF, mc, 0, dev)
+    ws_aq = pulse.workspace(pulse.PULSE_OP_APPLY_QUANT, mc, 0, dev)
+    codes = torch.empty(mc, dtype=torch.uint8, device=dev)
+    scales = torch.empty(mc // 16384 + 1024, dtype=torch.float32, device=dev)
+    plans = []
+    n_quant = 0
+    for a, z in chunks:
+        base = offs[a]
+        groups, co, so = [], 0, 0
+        ts = list(range(a, z))
+        if specs[a].name == "q":
+            srcs = [(offs[t] - base, specs[t].shape[0]) for t in ts]
+            stacks = [(srcs, specs[a].shape[1])]
+        else:
+            stacks = []
+            for t in range(a, z, 3):  # gate, up, down of one expert
+                stacks.append(([(offs[t] - base, specs[t].shape[0]), (offs[t + 1] - base, specs[t + 1].shape[0])],
+                               specs[t].shape[1]))
+                stacks.append(([(offs[t + 2] - base, specs[t + 2].shape[0])], specs[t + 2].shape[1]))
+        for srcs, cols in stacks:
+            R = sum(r for _, r in srcs)
+            nsc = ((R + 127) // 128) * ((cols + 127) // 128)
+            groups.append((srcs, cols, codes[co: co + R * cols], scales[so: so + nsc]))
+            co, so = co + R * cols, so + nsc
+        n_quant += co
+        plans.append(pulse.pulse_apply_quant_plan(groups, offs[z] - base, device=dev))
+    te, tr = [], []
+    for r in range(reps + 1):
+        recv.copy_(b)
+        torch.cuda.synchronize()
+        ev = []
+        for ci, (a, z) in enumerate(chunks):
+            s0, e0 = offs[a], offs[z]
+            e = [_ev() for _ in range(3)]
+            e[0].record()
+            pulse.pulse_cast_diff(W[s0:e0], b[s0:e0], stage[:e0 - s0], None, idx, val, cnt[ci:ci + 1], st, ws)
+            e[1].record()
+            pulse.pulse_apply_quant(recv[s0:e0], idx, val, cnt[ci:ci + 1], plans[ci], st, ws_aq, max_count=cap)
+            e[2].record()
+            ev.append(e)
+        torch.cuda.synchronize()
+        if r:
+            te.append(sum(e[0].elapsed_time(e[1]) for e in ev))
+            tr.append(sum(e[1].elapsed_time(e[2]) for e in ev))
+    if int(st.item()) != 0:
+        raise SystemExit(f"C5: device status {int(st.item())}")
+    changed = int(cnt.sum().item())
+    d = changed / n
+    me, mr = sum(te) / len(te), sum(tr) / len(tr)
+    a = n * (8 + 6 * d) + n * 8 * d + 3 * n_quant + 4 * n_quant / 16384
+    return {"workload": "C5: Kimi-K2-shaped MoE layer share (384 experts + q/k/v), one step at lr 3e-6",
+            "params": n, "changed_fraction": round(d, 6), "fp8_params": n_quant,
+            "encode_ms": round(me, 3), "receiver_ms": round(mr, 3),
+            "GBps_weights": round(2 * n / ((me + mr) / 1e3) / 1e9, 1), "alg_GB": round(a / 1e9, 3),
+            "frac_hbm": round(a / ((me + mr) / 1e3) / PEAK_HBM, 4),
+            "launches": 2 * len(chunks), "receiver": "pulse_apply_quant ([gate; up], down per expert; [q; k; v])"}
 
 
 if __name__ == "__main__":

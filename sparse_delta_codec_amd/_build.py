@@ -51,7 +51,24 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(LIB + ".tmp", LIB)
+    build_probe(verbose)
     return LIB
+
+
+PROBE_LIB = os.path.join(HERE, "libpulse_probe.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The bandwidth probes the benchmark sets the kernels against (csrc/probe.hip),
+    in a library of their own: the codec's library does not contain them."""
+    cmd = [HIPCC, *FLAGS, "-shared", os.path.join(SRC, "probe.hip"), "-o", PROBE_LIB + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for probe.hip:\n{r.stdout}\n{r.stderr}")
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":

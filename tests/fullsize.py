@@ -211,3 +211,69 @@ def check_fp8(view_h, sources, cols, codes_h, scales_h, what, bands_per_task=4, 
         return bad
     bad = [b for lst in pmap(one, range((nbr + bands_per_task - 1) // bands_per_task)) for b in lst]
     assert not bad, f"{what}: FP8 bands differ: {bad[:5]} (of {nbr})"
+
+
+def oracle_fp8(view_h, sources, cols, codes_out, scales_out, bands_per_task=4):
+    """The oracle's codes [R, cols] and scales of the stack of `sources`
+    (element offsets into view_h, row counts), written into the host arrays
+    codes_out (R * cols) and scales_out, one 128-row band per oracle call."""
+    R = sum(r for _, r in sources)
+    nbr, nbc = (R + 127) // 128, (cols + 127) // 128
+    codes_out = codes_out.reshape(R, cols)
+    scales_out = scales_out.reshape(nbr, nbc)
+    row_src, r = [], 0
+    for off, rows in sources:
+        row_src.append((r, r + rows, off))
+        r += rows
+
+    def one(k):
+        for br in range(k * bands_per_task, min(nbr, (k + 1) * bands_per_task)):
+            r0, r1 = br * 128, min(R, br * 128 + 128)
+            parts = []
+            for s0, s1, off in row_src:
+                a, b = max(r0, s0), min(r1, s1)
+                if a < b:
+                    parts.append(view_h[off + (a - s0) * cols: off + (b - s0) * cols].reshape(b - a, cols))
+            band = parts[0] if len(parts) == 1 else np.concatenate(parts, 0)
+            rc, rs = oracle.fp8_block_quant([band])
+            codes_out[r0:r1] = rc[0]
+            scales_out[br] = rs[0, 0]
+    pmap(one, range((nbr + bands_per_task - 1) // bands_per_task))
+
+
+class OracleDelta:
+    """The oracle's FP8-view delta of two quantised views (codes compared as
+    bytes, scales as 32-bit patterns), by pieces of the codes."""
+
+    def __init__(self, co, cn, so, sn):
+        self.ranges = pieces(co.size)
+        e = np.zeros(0, np.float32)
+
+        def one(r):
+            a, b = r
+            d = oracle.fp8_delta(co[a:b], cn[a:b], e, e)
+            assert d["status"] == 0
+            return d["code_idx"].copy(), d["code_val"].copy()
+        out = pmap(one, self.ranges)
+        self.idx = [o[0] for o in out]
+        self.val = [o[1] for o in out]
+        self.starts = np.concatenate([[0], np.cumsum([i.size for i in self.idx])]).astype(np.int64)
+        self.count = int(self.starts[-1])
+        z = np.zeros(0, np.uint8)
+        d = oracle.fp8_delta(z, z, so, sn)
+        assert d["status"] == 0
+        self.scale_idx, self.scale_val, self.scale_count = d["scale_idx"], d["scale_val"], d["scale_count"]
+
+    def check(self, count, idx_h, val_h, scount, sidx_h, sval_h, what):
+        assert count == self.count, (what, count, self.count)
+        assert scount == self.scale_count, (what, scount, self.scale_count)
+
+        def one(p):
+            a = self.ranges[p][0]
+            c0, c1 = int(self.starts[p]), int(self.starts[p + 1])
+            ok = same(idx_h[c0:c1], self.idx[p] + np.int32(a)) and same(val_h[c0:c1], self.val[p])
+            return None if ok else p
+        bad = [p for p in pmap(one, range(len(self.ranges))) if p is not None]
+        assert not bad, f"{what}: code entries differ in pieces {bad[:5]}"
+        assert same(sidx_h, self.scale_idx) and same(sval_h.view(np.uint32), self.scale_val.view(np.uint32)), \
+            f"{what}: scale entries"

@@ -97,3 +97,36 @@ def test_fp8_by_bands():
     with pytest.raises(AssertionError):
         fs.check_fp8(view, [(8, 300), (8 + a.size, 70)], 136, codes.reshape(-1), scales.reshape(-1), "more",
                      more=[(c2, scales.reshape(-1))])
+
+
+def test_fp8_views_and_delta_by_pieces(small_pieces):
+    rng = np.random.default_rng(10)
+    rows, cols = 1024, 384
+    old = oracle.cast_bf16(rng.standard_normal(rows * cols).astype(np.float32) * 0.02)
+    new = old.copy()
+    hit = rng.random(old.size) < 0.05
+    new[hit] = oracle.cast_bf16(rng.standard_normal(int(hit.sum())).astype(np.float32) * 0.02)
+    srcs = [(0, 640), (640 * cols, 384)]
+    ref_o = oracle.fp8_block_quant([old.reshape(rows, cols)])
+    ref_n = oracle.fp8_block_quant([new.reshape(rows, cols)])
+    co, so = np.empty(rows * cols, np.uint8), np.empty(8 * 3, np.float32)
+    cn, sn = np.empty_like(co), np.empty_like(so)
+    fs.oracle_fp8(old, srcs, cols, co, so)
+    fs.oracle_fp8(new, srcs, cols, cn, sn)
+    assert np.array_equal(co, ref_o[0].reshape(-1)) and np.array_equal(sn, ref_n[1].reshape(-1))
+    whole = oracle.fp8_delta(co, cn, so, sn)
+    d = fs.OracleDelta(co, cn, so, sn)
+    assert len(d.ranges) == 6 and d.count == whole["code_count"] > 0
+    args = (whole["code_count"], whole["code_idx"], whole["code_val"], whole["scale_count"], whole["scale_idx"],
+            whole["scale_val"])
+    d.check(*args, "whole call")
+    bad = list(args)
+    bad[1] = bad[1].copy()
+    bad[1][0] += 1
+    with pytest.raises(AssertionError):
+        d.check(*bad, "shifted code index")
+    bad = list(args)
+    bad[5] = bad[5].copy()
+    bad[5][0] = np.float32(bad[5][0]) * np.float32(2)
+    with pytest.raises(AssertionError):
+        d.check(*bad, "scale value")

@@ -317,3 +317,92 @@ def test_c5_kimi_layer_every_element():
                  fs.to_host(scales[:(RQ // 128) * (H // 128)], "scales"), "C5 [q; k; v]")
     say("C5: every FP8 code and scale of [gate; up], down and [q; k; v] equals the oracle's")
     fs.release()
+
+
+# ---------------------------------------------------------------------------
+F1_ORACLE_CHUNKS = (1, 17)  # a four-layer decoder chunk and the final norm + lm_head
+
+
+def test_f1_fp8_view_delta_full_size():
+    """Next row f1 on the C2 set, bench.py's FP8-view leg: per chunk the old
+    and new views are quantised (the chunk's groups laid end to end) and
+    fp8_view_delta / fp8_view_apply run over the codes and scales.  Every
+    chunk: the old quantisation with the delta applied equals the new one,
+    every code and scale.  Chunks 1 and 17: the delta's count and every entry,
+    codes and scales, against the oracle's delta of its own quantisation of
+    its own casts of the host masters."""
+    dev = torch.device("cuda")
+    specs = workload.qwen25_32b_specs()
+    chunks, offs = build_plan(specs)
+    max_chunk = max(e - s for s, e, _ in chunks)
+    plans = [[(g, sum(specs[i].shape[0] for i in g), specs[g[0]].shape[1]) for g in quant_groups(specs, tids)]
+             for _, _, tids in chunks]
+    max_q = max(sum(r * c for _, r, c in p) for p in plans)
+    max_s = max(sum(((r + 127) // 128) * ((c + 127) // 128) for _, r, c in p) for p in plans)
+    W = torch.empty(max_chunk, dtype=torch.float32, device=dev)
+    old = torch.empty(max_chunk, dtype=torch.int16, device=dev)
+    new = torch.empty(max_chunk, dtype=torch.int16, device=dev)
+    co = torch.empty(max_q, dtype=torch.uint8, device=dev)
+    cn = torch.empty(max_q, dtype=torch.uint8, device=dev)
+    so = torch.empty(max_s, dtype=torch.float32, device=dev)
+    sn = torch.empty(max_s, dtype=torch.float32, device=dev)
+    ccap = max_q // 10
+    ci_, cv_ = torch.empty(ccap, dtype=torch.int32, device=dev), torch.empty(ccap, dtype=torch.uint8, device=dev)
+    si_, sv_ = torch.empty(max_s, dtype=torch.int32, device=dev), torch.empty(max_s, dtype=torch.float32, device=dev)
+    cc, sc = torch.zeros(1, dtype=torch.int64, device=dev), torch.zeros(1, dtype=torch.int64, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    ws = new_ws(pulse.PULSE_OP_FP8_DELTA, max_q)
+    tmp = torch.empty(max(s.numel for s in specs), dtype=torch.float32, device=dev)
+    total_codes = total_changed = 0
+    for ci, (s0, e0, tids) in enumerate(chunks):
+        m = e0 - s0
+        with_oracle = ci in F1_ORACLE_CHUNKS
+        host = {}
+        for which, view in (("old", old), ("new", new)):
+            for ti in tids:
+                a, b = offs[ti] - s0, offs[ti] - s0 + specs[ti].numel
+                if which == "old":
+                    workload.fill_init(W[a:b], 2, ti, specs[ti].kind)
+                else:
+                    workload.apply_step(W[a:b], 2, ti, 1, tmp=tmp)
+                pulse.pulse_cast_diff(W[a:b], b_new=view[a:b])
+            if with_oracle:
+                host[which] = fs.oracle_cast(fs.to_host(W[:m], "w"))
+        qo = so_o = 0
+        groups = []
+        for (g, rows, cols) in plans[ci]:
+            nq, ns = rows * cols, ((rows + 127) // 128) * ((cols + 127) // 128)
+            for view, c, s_ in ((old, co, so), (new, cn, sn)):
+                pulse.fp8_block_quant([view[offs[i] - s0: offs[i] - s0 + specs[i].numel].view(specs[i].shape)
+                                       for i in g], c[qo:qo + nq], s_[so_o:so_o + ns])
+            groups.append(([(offs[i] - s0, specs[i].shape[0]) for i in g], cols, qo, nq, so_o, ns))
+            qo, so_o = qo + nq, so_o + ns
+        pulse.fp8_view_delta(co[:qo], cn[:qo], so[:so_o], sn[:so_o], ci_, cv_, cc, si_, sv_, sc, st, ws)
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0
+        count, scount = int(cc.item()), int(sc.item())
+        assert count <= ccap
+        if with_oracle:
+            ref_q = {}
+            for which in ("old", "new"):
+                c_h, s_h = np.empty(qo, np.uint8), np.empty(so_o, np.float32)
+                for srcs, cols, q0, nq, s0_, ns in groups:
+                    fs.oracle_fp8(host[which], srcs, cols, c_h[q0:q0 + nq], s_h[s0_:s0_ + ns])
+                ref_q[which] = (c_h, s_h)
+            fs.check_equal(fs.to_host(co[:qo], "codes"), ref_q["old"][0], f"f1 chunk {ci}: old codes")
+            fs.check_equal(fs.to_host(cn[:qo], "codes"), ref_q["new"][0], f"f1 chunk {ci}: new codes")
+            ref = fs.OracleDelta(ref_q["old"][0], ref_q["new"][0], ref_q["old"][1], ref_q["new"][1])
+            ref.check(count, fs.to_host(ci_[:count], "idx"), fs.to_host(cv_[:count], "val"), scount,
+                      fs.to_host(si_[:scount], "sidx"), fs.to_host(sv_[:scount], "sval"), f"f1 chunk {ci}")
+        pulse.fp8_view_apply(co[:qo], so[:so_o], ci_, cv_, cc, si_, sv_, sc, st)
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0
+        assert torch.equal(co[:qo], cn[:qo]), f"f1 chunk {ci}: apply(quant(old), delta) != quant(new) (codes)"
+        assert torch.equal(so[:so_o].view(torch.int32), sn[:so_o].view(torch.int32)), f"f1 chunk {ci}: scales"
+        total_codes += qo
+        total_changed += count
+        if with_oracle:
+            say(f"f1 chunk {ci}: {qo} codes, {count} changed, {scount} scales changed: every entry equals the oracle")
+    say(f"f1: {total_codes} codes, {total_changed} changed ({total_changed / total_codes:.3%}); "
+        "apply(quant(old), delta) == quant(new) on every chunk")
+    fs.release()
