@@ -430,8 +430,10 @@ int pulse_apply_quant_plan(const pulse_aq_group *groups, int32_t ngroups, int64_
  *              it and the outputs is written); PULSE_DS_WORKSPACE when the
  *              plan was made for another n or block count (nothing written).
  *   ws         pulse_workspace_bytes(PULSE_OP_APPLY_QUANT, n, 0): the patch's
- *              segment index (first entry at or past every 128th element),
- *              rebuilt by every call.
+ *              segment index (first entry at or past every 128th element) and
+ *              the counters from which the pass's workgroups take their
+ *              blocks, both rebuilt by every call (no initialisation needed;
+ *              calls sharing a workspace must not overlap).
  * The inputs must be finite, as for fp8_block_quant. */
 int pulse_apply_quant(uint16_t *b, int64_t n, const int32_t *patch_idx, const uint16_t *patch_val,
                       const int64_t *d_count, int64_t max_count, const void *plan, int64_t nblocks,

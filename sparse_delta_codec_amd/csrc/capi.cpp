@@ -62,7 +62,8 @@ void *pulse_noalloc_scratch(hipStream_t);
 int64_t pulse_apply_quant_plan_size(int32_t);
 int pulse_build_apply_quant_plan(const void *, int32_t, int64_t, void *, int64_t, int64_t *);
 int pulse_launch_apply_quant(uint16_t *, int64_t, const int32_t *, const uint16_t *, const int64_t *, int64_t,
-                             const void *, int64_t, uint32_t *, int32_t *, hipStream_t);
+                             const void *, int64_t, uint32_t *, void *, hipStream_t);
+size_t pulse_apply_quant_ws_bytes(int64_t n);
 }
 
 namespace {
@@ -108,7 +109,7 @@ size_t pulse_workspace_bytes(int op, int64_t n, int64_t aux) {
     case PULSE_OP_CAST_DIFF_LZ4:
         if (aux != 16384 && aux != 32768 && aux != 65536) return 0;
         return pulse_cast_diff_lz4_ws_bytes(n, (int32_t)aux);
-    case PULSE_OP_APPLY_QUANT: return (size_t)(((n + 127) / 128 + 1) * 4 + 15) / 16 * 16;
+    case PULSE_OP_APPLY_QUANT: return pulse_apply_quant_ws_bytes(n);
     default: return 0;
     }
 }
@@ -497,8 +498,8 @@ int pulse_apply_quant(uint16_t *b, int64_t n, const int32_t *patch_idx, const ui
     if (!aligned16(b) || !aligned16(plan)) return PULSE_EALIGN;
     if (n > kMaxIndexed || max_count > kMaxIndexed || nblocks > kMaxIndexed) return PULSE_ERANGE;
     if (!ws || ws_bytes < pulse_workspace_bytes(PULSE_OP_APPLY_QUANT, n, 0)) return PULSE_EWORKSPACE;
-    return pulse_launch_apply_quant(b, n, patch_idx, patch_val, d_count, max_count, plan, nblocks, d_status,
-                                    static_cast<int32_t *>(ws), stream);
+    return pulse_launch_apply_quant(b, n, patch_idx, patch_val, d_count, max_count, plan, nblocks, d_status, ws,
+                                    stream);
 }
 
 }  // extern "C"

@@ -237,10 +237,15 @@ __host__ __device__ inline int64_t aq_groups_offset(int64_t ng) {
 // stores an instruction.  An index outside [0, n), or one not above its
 // predecessor, sets PULSE_DS_BADINDEX.
 constexpr int kSegPer = 8;
+constexpr int kAqXcds = 8;            // the XCDs workgroups are dispatched to in turn
+constexpr int kAqTicketStride = 32;   // uint32 words between the per-XCD counters (128 bytes)
 
 __global__ __launch_bounds__(256) void k_patch_segments(const int32_t *__restrict__ idx, const int64_t *d_count,
                                                         int64_t max_count, int64_t n, int32_t *__restrict__ seg_first,
-                                                        uint32_t *d_status) {
+                                                        uint32_t *d_status, uint32_t *tickets) {
+    // the receiver pass that follows on the stream takes its blocks from
+    // these counters (one per XCD, each on its own 128-byte line)
+    if (blockIdx.x == 0 && threadIdx.x < kAqXcds) tickets[threadIdx.x * kAqTicketStride] = 0u;
     int64_t count = *d_count;
     if (count > max_count) count = max_count;
     if (count < 0) count = 0;
@@ -339,18 +344,23 @@ __device__ __forceinline__ int32_t aq_elem(int32_t o0, int32_t o1, int32_t o2, i
     return o + (r - r0) * cols + c;
 }
 
-// Persistent: each XCD (workgroups go to the 8 XCDs in turn) takes a
-// contiguous range of blocks, and its workgroups take runs of kAqRun
-// consecutive blocks of it in turn.  Consecutive blocks are neighbouring
-// column blocks of the same rows, whose entries continue in the same lines of
-// the patch: a block row uses some 60 bytes of its rows' 128-byte lines, and
-// the next block of the run finds the rest still in L2.  The view, the
-// write-back and the codes are streamed (non-temporal) so they do not evict
-// those lines.  A workgroup looks up the next block's entry range while it
-// patches and quantises the current block, so a block's own loads (the view
-// and the entries) go out together.
-constexpr int kAqMaxGroups = 320 * 8;
-constexpr int kAqRun = 8;
+// Persistent workgroups.  Each XCD (workgroups go to the 8 XCDs in turn)
+// takes a contiguous range of blocks, and its workgroups take the blocks of
+// that range one at a time from a counter of their own XCD (a ticket, taken
+// one block ahead).  The blocks an XCD works on at any moment are thus a
+// compact window of about as many consecutive blocks as it holds
+// workgroups: neighbouring column blocks of the same rows, whose entries lie
+// in the same 128-byte lines of the patch (a block row uses some 60 bytes of
+// its row's lines).  The window's lines, about 1 MB, stay in the XCD's 4 MB
+// L2 while its neighbours read them; a workgroup walking its own strided runs
+// of blocks would instead keep some 8 MB of lines open and fetch each line
+// several times.  The view, the write-back and the codes are streamed
+// (non-temporal) so they do not evict those lines.  A workgroup looks up the
+// next block's entry range while it patches and quantises the current block,
+// so a block's own loads (the view and the entries) go out together.  Blocks
+// are independent of one another, so the order in which workgroups take them
+// is free.
+constexpr int kAqMaxGroups = 128 * 8;  // 4 workgroups on each of the 256 CUs
 
 __global__ __launch_bounds__(256, 4) void k_apply_quant(uint16_t *__restrict__ b, int64_t n,
                                                        const int32_t *__restrict__ idx,
@@ -358,9 +368,10 @@ __global__ __launch_bounds__(256, 4) void k_apply_quant(uint16_t *__restrict__ b
                                                        const int64_t *__restrict__ d_count, int64_t max_count,
                                                        const int32_t *__restrict__ seg_first,
                                                        const uint8_t *__restrict__ plan, int64_t nblk,
-                                                       uint32_t *d_status) {
+                                                       uint32_t *d_status, uint32_t *tickets) {
     static_assert(FQ_GSRC == 4, "four sources a group");
     __shared__ u32x4 img[128 * 16];  // the block, 256 bytes a row
+    __shared__ uint32_t s_next;      // the ticket of the workgroup's next block
     const AQPlanHeader *hdr = reinterpret_cast<const AQPlanHeader *>(plan);
     const int t = threadIdx.x;
     if (hdr->n != n || hdr->nblocks != nblk) {  // a plan made for another view
@@ -368,13 +379,13 @@ __global__ __launch_bounds__(256, 4) void k_apply_quant(uint16_t *__restrict__ b
         return;
     }
     const int64_t ng = hdr->ngroups;
-    const int64_t x = blockIdx.x % 8, per = gridDim.x / 8, q = nblk / 8, rem = nblk % 8;
+    const int64_t x = blockIdx.x % kAqXcds, q = nblk / kAqXcds, rem = nblk % kAqXcds;
     const int64_t x0 = x * q + (x < rem ? x : rem), x1 = x0 + q + (x < rem ? 1 : 0);
-    // this workgroup's m-th block: run j0 + (m / kAqRun) per, block m % kAqRun of it
-    const int64_t j0 = blockIdx.x / 8;
-    auto block_of = [&](int64_t m) { return x0 + (j0 + (m / kAqRun) * per) * kAqRun + m % kAqRun; };
-    int64_t m = 0;
-    int64_t blk = block_of(0);
+    uint32_t *const ticket = tickets + x * kAqTicketStride;
+    if (t == 0) s_next = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    int64_t blk = x0 + (int64_t)s_next;
+    __syncthreads();  // every thread has read s_next before it holds the next ticket
     if (blk >= x1) return;
 
     int32_t count;
@@ -411,6 +422,10 @@ __global__ __launch_bounds__(256, 4) void k_apply_quant(uint16_t *__restrict__ b
     LOOKUP(c_, e, sf0, sf1);
 
     for (;;) {
+        // the next block's ticket: taken now, published in LDS just before the
+        // first barrier (its round trip overlaps the block's loads)
+        uint32_t next_ticket = 0;
+        if (t == 0) next_ticket = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int32_t col = c_bc * 128 + seg * 8;
         const bool col_ok = col < c_cols;
         const int32_t len = c_cols - c_bc * 128 < 128 ? c_cols - c_bc * 128 : 128;
@@ -448,10 +463,11 @@ __global__ __launch_bounds__(256, 4) void k_apply_quant(uint16_t *__restrict__ b
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) img[(rg + 16 * i) * 16 + seg] = u32x4{v[i].x, v[i].y, v[i].z, v[i].w};
+        if (t == 0) s_next = next_ticket;
         __syncthreads();
 
         // the next block and its entry range (the current one again at the end)
-        const int64_t nb = block_of(m + 1);
+        const int64_t nb = x0 + (int64_t)s_next;
         const bool more = nb < x1;
         AQ_LOCATE(n_, more ? nb : blk);
         int32_t ne, nsf0, nsf1;
@@ -490,9 +506,8 @@ __global__ __launch_bounds__(256, 4) void k_apply_quant(uint16_t *__restrict__ b
                              c_scales + (int64_t)c_br * c_nbc + c_bc);
         }
         if (!more) break;
-        __syncthreads();  // the image (and the maxima) read before the next block is stored
+        __syncthreads();  // the image (and the maxima) read, s_next read, before the next block starts
         blk = nb;
-        ++m;
 #define AQ_NEXT(T, f) c_##f = n_##f;
         AQ_FIELDS(AQ_NEXT)
 #undef AQ_NEXT
@@ -656,19 +671,31 @@ extern "C" int pulse_build_apply_quant_plan(const void *groups, int32_t ngroups,
     return 0;
 }
 
+// Workspace of the receiver's pass: the segment index (one int32 per 128
+// elements and the closing one), then the per-XCD block counters on lines of
+// their own.
+static int64_t aq_ticket_offset(int64_t n) { return (((n + 127) / 128 + 1) * 4 + 255) / 256 * 256; }
+
+extern "C" size_t pulse_apply_quant_ws_bytes(int64_t n) {
+    return (size_t)(aq_ticket_offset(n) + kAqXcds * kAqTicketStride * 4);
+}
+
 extern "C" int pulse_launch_apply_quant(uint16_t *b, int64_t n, const int32_t *idx, const uint16_t *val,
                                         const int64_t *d_count, int64_t max_count, const void *plan, int64_t nblocks,
-                                        uint32_t *d_status, int32_t *seg_first, hipStream_t stream) {
+                                        uint32_t *d_status, void *ws, hipStream_t stream) {
+    int32_t *seg_first = static_cast<int32_t *>(ws);
+    uint32_t *tickets = reinterpret_cast<uint32_t *>(static_cast<char *>(ws) + aq_ticket_offset(n));
     int64_t blocks = (max_count + 1 + 256 * kSegPer - 1) / (256 * kSegPer);
     if (blocks > 256 * 8) blocks = 256 * 8;
     k_patch_segments<<<dim3((unsigned)blocks), dim3(256), 0, stream>>>(idx, d_count, max_count, n, seg_first,
-                                                                       d_status);
+                                                                       d_status, tickets);
     if (hipGetLastError() != hipSuccess) return -5;
     if (nblocks < 1) return 0;
-    int64_t per = ((nblocks + 7) / 8 + kAqRun - 1) / kAqRun;  // workgroups per XCD: one run each at most
-    if (per > kAqMaxGroups / 8) per = kAqMaxGroups / 8;
-    k_apply_quant<<<dim3((unsigned)(8 * per)), dim3(256), 0, stream>>>(b, n, idx, val, d_count, max_count, seg_first,
-                                                                       static_cast<const uint8_t *>(plan), nblocks,
-                                                                       d_status);
+    // as many workgroups as the GPU holds at once (4 a CU), no more than blocks
+    int64_t per = (nblocks + kAqXcds - 1) / kAqXcds;
+    if (per > kAqMaxGroups / kAqXcds) per = kAqMaxGroups / kAqXcds;
+    k_apply_quant<<<dim3((unsigned)(kAqXcds * per)), dim3(256), 0, stream>>>(
+        b, n, idx, val, d_count, max_count, seg_first, static_cast<const uint8_t *>(plan), nblocks, d_status,
+        tickets);
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }

@@ -68,8 +68,10 @@ def test_workspace_sizes(lib):
     # fused sender pass: header + two status words per mask block
     assert ws(9, 32768 * 3 + 1, 65536) == 256 + 2 * 4 * 8
     assert ws(9, 1000, 1000) == 0
-    # receiver's pass: one int32 segment start per 128 elements, plus the closing one
-    assert ws(10, 128 * 5, 0) == 32 and ws(10, 128 * 5 + 1, 0) == 32 and ws(10, 128 * 8, 0) == 48
+    # receiver's pass: one int32 segment start per 128 elements plus the closing one (rounded to
+    # 256 bytes), then 8 block counters 128 bytes apart
+    assert ws(10, 128 * 5, 0) == 256 + 1024 and ws(10, 128 * 63, 0) == 256 + 1024
+    assert ws(10, 128 * 64, 0) == 512 + 1024
 
 
 V = ctypes.c_void_p
