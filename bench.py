@@ -591,6 +591,8 @@ def main():
             d_lr = int(cnt.sum().item()) / n
             c_lr = int(ctotal.sum().item()) / n
             sms = {k: round(sum(a.elapsed_time(b) for a, b in ev[k]) / ks, 3) for k in stages}
+            if parse_ev["lz4_decode"]:
+                sms["decode_parse"] = round(sum(a.elapsed_time(b) for a, b in parse_ev["lz4_decode"]) / ks, 3)
             sweep.append({"lr": lr, "changed_fraction": round(d_lr, 6), "lz4_bytes_per_param": round(c_lr, 5),
                           "ms_per_step": round(ms_lr, 3), "GBps_weights_step": round(2 * n / (ms_lr / 1e3) / 1e9, 1),
                           "stage_ms": sms, "steps": ks})

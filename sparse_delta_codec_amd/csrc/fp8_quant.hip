@@ -372,6 +372,7 @@ __global__ __launch_bounds__(256, 4) void k_apply_quant(uint16_t *__restrict__ b
     static_assert(FQ_GSRC == 4, "four sources a group");
     __shared__ u32x4 img[128 * 16];  // the block, 256 bytes a row
     __shared__ uint32_t s_next;      // the ticket of the workgroup's next block
+    __shared__ uint2 dirty[128 * 16 / 8];  // a byte per 16-byte piece: 1 once an entry landed in it
     const AQPlanHeader *hdr = reinterpret_cast<const AQPlanHeader *>(plan);
     const int t = threadIdx.x;
     if (hdr->n != n || hdr->nblocks != nblk) {  // a plan made for another view
@@ -463,6 +464,7 @@ __global__ __launch_bounds__(256, 4) void k_apply_quant(uint16_t *__restrict__ b
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) img[(rg + 16 * i) * 16 + seg] = u32x4{v[i].x, v[i].y, v[i].z, v[i].w};
+        dirty[t] = uint2{0u, 0u};
         if (t == 0) s_next = next_ticket;
         __syncthreads();
 
@@ -474,29 +476,43 @@ __global__ __launch_bounds__(256, 4) void k_apply_quant(uint16_t *__restrict__ b
         LOOKUP(n_, ne, nsf0, nsf1);
 
         uint16_t *img16 = reinterpret_cast<uint16_t *>(img);
+        uint8_t *dirty8 = reinterpret_cast<uint8_t *>(dirty);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int r = erow0 + 4 * j;  // block row
             const int32_t er = __shfl(e, 8 * j + 2 * (lane >> 4));
             const int32_t rel = ii[j] - er;
-            if (ii[j] >= 0 && rel >= 0 && rel < len) img16[r * 128 + rel] = vv[j];
+            if (ii[j] >= 0 && rel >= 0 && rel < len) {
+                img16[r * 128 + rel] = vv[j];
+                dirty8[r * 16 + (rel >> 3)] = 1;
+            }
         }
         // rows with more than 16 entries: the two lanes of the row take the
         // rest in turn
         for (int32_t k = k0 + 16 + (t & 1); k < k1; k += 2) {
             const int32_t rel = idx[k] - e;
-            if (rel >= 0 && rel < len) img16[rl * 128 + rel] = val[k];
+            if (rel >= 0 && rel < len) {
+                img16[rl * 128 + rel] = val[k];
+                dirty8[rl * 16 + (rel >> 3)] = 1;
+            }
         }
         __syncthreads();
 
-        // the patched block: written back whole (a block row is two full
-        // lines) and quantised
+        // the patched block: the 64-byte lines that received an entry are
+        // written back (the others hold the view's own bytes), and the whole
+        // block is quantised
         uint4 u[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const u32x4 w = img[(rg + 16 * i) * 16 + seg];
             u[i] = make_uint4(w.x, w.y, w.z, w.w);
-            if (ok[i])
+            // a 64-byte line of the row (four 16-byte pieces, four neighbouring
+            // lanes) is written whole when an entry landed in any of its
+            // pieces, else not at all: no partially written lines
+            uint32_t dl = dirty8[(rg + 16 * i) * 16 + seg];
+            dl |= dpp_mov<0xB1, 0xf, 0xf>(0u, dl);  // quad_perm [1,0,3,2]
+            dl |= dpp_mov<0x4E, 0xf, 0xf>(0u, dl);  // quad_perm [2,3,0,1]
+            if (ok[i] && dl)
                 __builtin_nontemporal_store(w, reinterpret_cast<u32x4 *>(b + ELEM(c_, c_br * 128 + rg + 16 * i, col)));
         }
         if (c_quant) {
