@@ -197,6 +197,57 @@ def views_equal(a, b, chunk=1 << 30):
     return True
 
 
+def independent_check(pulse, specs, offs, chunks, W, b_old, b_recv, stage, idx, val, cnt, codes, scales, status,
+                      send_receive, decode):
+    """The last chunk (final norm + lm_head) once more, checked against values
+    computed on the host without the library: windows of the sender's new view
+    and of the receiver's patched view against torch's CPU cast of the
+    masters, the patch entries in those windows against numpy's flatnonzero
+    of the two casts, and the FP8 codes and scales of the lm_head's first
+    128-row band against numpy's float32 division and torch's E4M3
+    conversion; after the decode + XOR the receiver's view is the old view."""
+    import numpy as np
+    import torch
+
+    ci = len(chunks) - 1
+    s0, e0, tids = chunks[ci]
+    m = e0 - s0
+    send_receive(ci)
+    torch.cuda.synchronize()
+    if int(status.item()) != 0:
+        raise SystemExit(f"check: device status {int(status.item())}")
+    count = int(cnt[ci].item())
+    ii = idx[:count]
+    for o in (0, m // 2, m - 65536):
+        w = W[s0 + o: s0 + o + 65536].cpu()
+        ref = w.to(torch.bfloat16).view(torch.int16)
+        old = b_old[s0 + o: s0 + o + 65536].cpu()
+        if not (torch.equal(stage[o:o + 65536].cpu(), ref) and torch.equal(b_recv[s0 + o: s0 + o + 65536].cpu(), ref)):
+            raise SystemExit(f"check: new or patched view differs from torch's cast at chunk offset {o}")
+        pos = np.flatnonzero((ref != old).numpy()) + o
+        lo, hi = (int(x) for x in torch.searchsorted(ii, torch.tensor([o, o + 65536], dtype=torch.int32,
+                                                                       device=ii.device)).cpu())
+        if not (np.array_equal(ii[lo:hi].cpu().numpy(), pos) and
+                torch.equal(val[lo:hi].cpu(), ref[torch.from_numpy(pos - o)])):
+            raise SystemExit(f"check: patch entries differ from numpy's flatnonzero at chunk offset {o}")
+    head = [i for i in tids if specs[i].name == "lm_head"][0]
+    cols = specs[head].shape[1]
+    x = W[offs[head]: offs[head] + 128 * cols].cpu().to(torch.bfloat16).to(torch.float32).numpy().reshape(128, cols)
+    for bc in range(0, (cols + 127) // 128):
+        blk = x[:, bc * 128:(bc + 1) * 128]
+        amax = np.float32(np.abs(blk).max())
+        sc = np.float32(1.0) if amax == 0 else np.float32(amax / np.float32(448.0))
+        q = np.ascontiguousarray((blk / sc).astype(np.float32))
+        ref_c = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        got_c = codes[:128 * cols].view(128, cols)[:, bc * 128:(bc + 1) * 128].cpu().numpy()
+        if not (np.array_equal(got_c, ref_c) and np.float32(scales[bc].item()) == sc):
+            raise SystemExit(f"check: FP8 codes or scale of lm_head block (0, {bc}) differ from numpy + torch")
+    decode(ci)
+    torch.cuda.synchronize()
+    if int(status.item()) != 0 or not views_equal(b_recv[s0:e0], b_old[s0:e0]):
+        raise SystemExit("check: the decode + XOR did not return the receiver's view to the old view")
+
+
 def log(msg):
     """Progress on stderr (the JSON result is the only stdout line)."""
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -455,6 +506,12 @@ def main():
                 raise SystemExit(f"device status {st} after the first step (capacity or corrupt payload)")
             if not views_equal(b_recv, b_old):
                 raise SystemExit("receiver view did not return to v0 after patch apply + XOR decode")
+    independent_check(pulse, specs, offs, chunks, W, b_old, b_recv, stage, idx, val, cnt, codes, scales, status,
+                      lambda ci: (encode(False, ci, bufs[0]), receive(False, ci, bufs[0])),
+                      lambda ci: (side_stream.wait_stream(main_stream), main_stream.wait_event(
+                          parse_chunk(False, ci, bufs[0])), decode_apply(False, ci, bufs[0])) if sched != "serial"
+                      else pulse.lz4_decode_blocks(payload, coffs, csizes, b_recv[chunks[ci][0]:chunks[ci][1]], status,
+                                                   ws_de, mode=1))
     log(f"warm-up done ({max(args.warmup, 1)} steps, end-to-end check passed)")
     counts = cnt.cpu().numpy()
     totals = ctotal.cpu().numpy()

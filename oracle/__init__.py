@@ -29,9 +29,10 @@ _I32 = ctypes.c_int32
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB):
+        path = os.environ.get("SDC_ORACLE_LIB", _build.LIB)  # the sanitizer test loads its own build
+        if not os.path.exists(path):
             _build.build()
-        L = ctypes.CDLL(_build.LIB)
+        L = ctypes.CDLL(path)
         L.oracle_bf16_rne.argtypes = [ctypes.c_uint32]
         L.oracle_bf16_rne.restype = ctypes.c_uint16
         L.oracle_cast_bf16.argtypes = [_P, _P, _I64]

@@ -27,7 +27,7 @@ __all__ = [
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libpulse.so")
+_LIB_PATH = os.environ.get("SDC_PULSE_LIB") or os.path.join(_HERE, "libpulse.so")  # (a sanitizer build in tests)
 if not os.path.exists(_LIB_PATH):
     raise ImportError(
         f"{_LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "

@@ -27,9 +27,15 @@ FLAGS = [
 ]
 
 
-def _compile(src, verbose):
-    obj = os.path.join(OUT, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(SRC, src), "-o", obj]
+# host-side sanitizers (the sanitizer test): each flag behind -Xarch_host, so
+# only the host code of every source is instrumented
+HOST_SANITIZE = ["-g", "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fsanitize=address",
+                 "-Xarch_host", "-fsanitize=undefined", "-Xarch_host", "-fno-sanitize-recover=all"]
+
+
+def _compile(src, verbose, out=None, extra=()):
+    obj = os.path.join(out or OUT, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(SRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -37,6 +43,20 @@ def _compile(src, verbose):
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
     warn = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l and l.strip())
     return obj, warn
+
+
+def build_host_sanitized(out_dir: str) -> str:
+    """libpulse.so with its host code built with AddressSanitizer and
+    UndefinedBehaviorSanitizer, into out_dir (load it with clang's ASan runtime
+    preloaded).  The device code is built as usual."""
+    os.makedirs(out_dir, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        results = list(ex.map(lambda s: _compile(s, False, out_dir, HOST_SANITIZE), SOURCES))
+    lib = os.path.join(out_dir, "libpulse.so")
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+           "-Xarch_host", "-fsanitize=undefined", "-shared-libsan", "-o", lib, *[o for o, _ in results]]
+    subprocess.run(cmd, check=True, capture_output=True)
+    return lib
 
 
 def build(verbose: bool = False) -> str:

@@ -8,7 +8,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pulse.h")
-LIB = os.path.join(ROOT, "sparse_delta_codec_amd", "libpulse.so")
+LIB = os.environ.get("SDC_PULSE_LIB") or os.path.join(ROOT, "sparse_delta_codec_amd", "libpulse.so")
 
 EINVAL, EALIGN, ERANGE, EWORKSPACE = -1, -2, -3, -4
 

@@ -446,12 +446,36 @@ def gpu_decode(payload, offsets, sizes, dst, mode, block_bytes=65536, payload_by
 
 
 @pytest.mark.parametrize("mode", [0, 1])
-@pytest.mark.parametrize("density", [0.0, 0.01, 0.08, 1.0])
+@pytest.mark.parametrize("density", [0.0, 0.00005, 0.0005, 0.002, 0.01, 0.08, 1.0])
 def test_lz4_decode_canonical_payloads(mode, density):
     nbytes = 7 * 65536 + 999
     m = mask_bytes(nbytes, density, seed=int(density * 100) + mode)
     enc = oracle.lz4_encode_blocks(m, 65536)
     dst = np.random.default_rng(5).integers(0, 256, nbytes, dtype=np.uint8)
+    got, st = gpu_decode(enc["payload"], enc["offsets"], enc["sizes"], dst, mode)
+    ref, rst = oracle.lz4_decode_blocks(enc["payload"], enc["offsets"], enc["sizes"], dst, mode=mode)
+    assert st == rst == 0 and np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_lz4_decode_long_zero_runs_at_window_edges(mode):
+    """Canonical sequences of l non-zero-ended literal runs (l = 1 .. 12)
+    followed by zero runs whose match lengths need k bytes of 255 and a final
+    byte: every k from 0 to one past what fits in a 16-byte window after the
+    literals, and final bytes 0, 1 and 254 -- both sides of the decoder's
+    one-window path and its byte-by-byte path."""
+    rng = np.random.default_rng(77 + mode)
+    parts = []
+    for ll in range(1, 13):
+        for k in range(0, 14 - ll):
+            for f in (0, 1, 254):
+                L = 19 + 255 * k + f  # match length: 15 in the token, then k bytes 255 and f
+                lit = rng.integers(1, 256, ll - 1, dtype=np.uint8)
+                parts += [lit, np.zeros(L + 1, np.uint8)]  # the run's first zero is the last literal
+    parts.append(rng.integers(1, 256, 40, dtype=np.uint8))
+    m = np.concatenate(parts)
+    enc = oracle.lz4_encode_blocks(m, 65536)
+    dst = np.random.default_rng(6).integers(0, 256, m.size, dtype=np.uint8)
     got, st = gpu_decode(enc["payload"], enc["offsets"], enc["sizes"], dst, mode)
     ref, rst = oracle.lz4_decode_blocks(enc["payload"], enc["offsets"], enc["sizes"], dst, mode=mode)
     assert st == rst == 0 and np.array_equal(got, ref)
