@@ -396,6 +396,24 @@ __device__ __forceinline__ uint64_t lookback_wave(uint64_t *status, uint32_t til
     return lookback_resolve<MAX>(status, tile, tag, aggregate, failed);
 }
 
+// Bytes [o, o + 16) of the 32 bytes A (low) then B, for o in 1 .. 16.
+__device__ __forceinline__ u32x4 take16(const u32x4 &A, const u32x4 &B, int o) {
+    const uint32_t w[8] = {A.x, A.y, A.z, A.w, B.x, B.y, B.z, B.w};
+    const int wq = o >> 2, bs = o & 3;
+    if (o == 16) return B;
+    if (wq == 0)
+        return u32x4{__builtin_amdgcn_alignbyte(w[1], w[0], bs), __builtin_amdgcn_alignbyte(w[2], w[1], bs),
+                     __builtin_amdgcn_alignbyte(w[3], w[2], bs), __builtin_amdgcn_alignbyte(w[4], w[3], bs)};
+    if (wq == 1)
+        return u32x4{__builtin_amdgcn_alignbyte(w[2], w[1], bs), __builtin_amdgcn_alignbyte(w[3], w[2], bs),
+                     __builtin_amdgcn_alignbyte(w[4], w[3], bs), __builtin_amdgcn_alignbyte(w[5], w[4], bs)};
+    if (wq == 2)
+        return u32x4{__builtin_amdgcn_alignbyte(w[3], w[2], bs), __builtin_amdgcn_alignbyte(w[4], w[3], bs),
+                     __builtin_amdgcn_alignbyte(w[5], w[4], bs), __builtin_amdgcn_alignbyte(w[6], w[5], bs)};
+    return u32x4{__builtin_amdgcn_alignbyte(w[4], w[3], bs), __builtin_amdgcn_alignbyte(w[5], w[4], bs),
+                 __builtin_amdgcn_alignbyte(w[6], w[5], bs), __builtin_amdgcn_alignbyte(w[7], w[6], bs)};
+}
+
 __device__ __forceinline__ uint16_t bf16_rne(uint32_t x) {
     // nearest BF16, ties to even; NaN -> quiet NaN with sign and top payload
     if ((x & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((x >> 16) | 0x40u);

@@ -12,19 +12,27 @@
 //                   table (inside the payload, no block starting before the
 //                   end of an earlier one: a prefix max over blocks by
 //                   decoupled look-back), then walks each block's token chain
-//                   from a 512-byte LDS ring of its compressed bytes that the
+//                   from a 256-byte LDS ring of its compressed bytes that the
 //                   wave refills with coalesced loads when lanes run out.  A
 //                   block in the form the canonical encoder writes (every match
 //                   has offset 1 and follows >= 1 literal) is validated in full
-//                   and every 32nd sequence start (input, output position) is
+//                   and every 16th sequence start (input, output position) is
 //                   recorded as a checkpoint; any other block is handed to K3.
+//                   A block with a length chain longer than the ring (a run
+//                   of one byte over most of the block, or one literal run)
+//                   is walked again straight from global memory.
 //  K2 k_lz4_fast    one WORKGROUP per checkpointed block: stages its compressed
 //                   bytes in LDS, starts the loads of its dst range (XOR mode),
 //                   rebuilds the block in a zeroed LDS image with one thread
-//                   per 32-sequence segment (long literal runs and non-zero
-//                   fills are deferred and copied by the whole workgroup), then
+//                   per 16-sequence segment (long literal runs and non-zero
+//                   fills are deferred and copied a wave per run in 16-byte
+//                   pieces), then
 //                   XORs (or stores) the image with 16-byte accesses; chunks
-//                   whose mask bytes are all zero are not written back.
+//                   whose mask bytes are all zero are not written back.  A
+//                   block that is one literal run of its full length (the
+//                   shape incompressible data takes) skips the image: its
+//                   length bytes are checked in parallel and its literals
+//                   stream from the payload to dst with 16-byte accesses.
 //  K3 k_lz4_slow    every other block: serial, fully validating parse by one
 //                   thread over LDS-staged input, cooperative copies into a
 //                   64 KiB LDS image, then a coalesced XOR / store.
@@ -35,7 +43,8 @@ namespace pulse {
 
 constexpr uint32_t BI_BAD = 0x80000000u;
 constexpr uint32_t BI_SLOW = 0x40000000u;
-constexpr uint32_t BI_NSEQ = 0x3FFFFFFFu;
+constexpr uint32_t BI_LIT = 0x20000000u;  // one literal run the size of the block (length bytes checked by K2)
+constexpr uint32_t BI_NSEQ = 0x1FFFFFFFu;
 
 // Checkpoints: one per kCkEvery sequences.  A sequence that is not the last
 // one takes >= 3 compressed bytes (token, 2-byte offset), so a block of S
@@ -134,19 +143,43 @@ __device__ __forceinline__ void ring_refill(uint8_t *rings, const uint8_t *pay, 
     __syncthreads();  // one-wave workgroup: the refilled rings are visible to their owners
 }
 
+// Byte reader over a block's compressed bytes (block byte x at base + mis + x,
+// base 16-byte aligned, in LDS or global memory) that loads one aligned
+// 16-byte piece at a time and keeps the last one: a length chain or a short
+// literal run costs one load per 16 bytes, not one per byte.  Only pieces
+// holding a byte of the block are loaded (such a piece never leaves that
+// byte's page).
+struct Win16 {
+    const uint8_t *base;
+    uint32_t mis, cur;
+    u32x4 w;
+    __device__ __forceinline__ Win16(const uint8_t *b, uint32_t m) : base(b), mis(m), cur(0xFFFFFFFFu), w{0u, 0u, 0u, 0u} {}
+    __device__ __forceinline__ uint32_t operator[](uint32_t x) {
+        const uint32_t p = mis + x, k = p >> 4;
+        if (k != cur) {
+            w = *reinterpret_cast<const u32x4 *>(base + 16 * (size_t)k);
+            cur = k;
+        }
+        const uint32_t d = (p >> 2) & 3u;
+        const uint32_t word = d == 0 ? w.x : d == 1 ? w.y : d == 2 ? w.z : w.w;
+        return (word >> (8 * (p & 3u))) & 0xFFu;
+    }
+};
+
 // Lane state of the walk, one word (bit flags in a VGPR keep divergent joins
 // free of per-flag lane-mask bookkeeping).
-constexpr uint32_t F_DONE = 1u, F_BAD = 2u, F_SLOW = 4u, F_STALL = 8u, F_OFF = 16u;
+constexpr uint32_t F_DONE = 1u, F_BAD = 2u, F_SLOW = 4u, F_STALL = 8u, F_OFF = 16u, F_LIT = 32u, F_LONG = 64u;
 
 // Reads a length extension (bytes added while they are 255) starting at
 // block position q into n.  r0: ring index of the step's first byte; a chain
-// that leaves a ring refilled at that step cannot be read from the ring at all.
+// that leaves a ring refilled at that step cannot be read from the ring at all
+// (F_LONG: the block is walked again by k1_walk_long).
 __device__ __forceinline__ uint32_t read_ext(const uint8_t *ring, int32_t rb, uint32_t S, uint32_t len,
                                              uint32_t r0, uint32_t &q, uint32_t &n) {
     while (true) {
         if (q >= S) return F_BAD | F_DONE;
         const uint32_t rq = q - (uint32_t)rb;
-        if (rq >= (uint32_t)K1_RING) return r0 < 16 ? (F_SLOW | F_DONE) : F_STALL;
+        if (rq >= (uint32_t)K1_RING) return r0 < 16 ? (F_LONG | F_DONE) : F_STALL;
         const uint32_t x = ring[rq];
         ++q;
         n += x;
@@ -164,8 +197,10 @@ struct WalkResult {
 // the skipped literals), then the offset (with match-length bytes).  A step
 // whose bytes lie past the ring stalls the lane until the wave's next refill.
 // The block is handed to K3 (F_SLOW) at the first sequence not in canonical
-// form, or at a length chain longer than a whole ring (impossible within a
-// 64 KiB block without overflowing it; kept for safety).
+// form.  A length chain longer than the ring (a run of one byte over most of a
+// 64 KiB block, or a block that is one literal run) ends the ring walk with
+// F_LONG; such blocks are few and have few sequences, and k1_walk_long walks
+// them again from global memory.
 __device__ __forceinline__ WalkResult k1_walk(uint8_t *rings, const uint8_t *ring, bool active, const uint8_t *pay,
                                               int64_t pay_bytes, int64_t boff, uint32_t S, uint32_t len, uint2 *ck) {
     int32_t rb = -(1 << 30);  // empty ring: every position maps past it
@@ -275,6 +310,60 @@ __device__ __forceinline__ WalkResult k1_walk(uint8_t *rings, const uint8_t *rin
     return WalkResult{nseq, f};
 }
 
+
+// The walk of one block straight from global memory, for the lanes whose
+// block has a length chain longer than the ring: the same checks, flags and
+// checkpoints as the ring walk (a sequence that is not canonical: F_SLOW),
+// reading the block's bytes one aligned 16-byte piece at a time.  A block
+// with the first token and the size of a single literal run of its full
+// length is marked F_LIT without reading its chain (K2 checks it).
+__device__ __forceinline__ WalkResult k1_walk_long(const uint8_t *pay, int64_t boff, uint32_t S, uint32_t len,
+                                                   uint2 *ck) {
+    const uint8_t *blk = pay + boff;
+    const uint32_t mis = (uint32_t)(reinterpret_cast<uintptr_t>(blk) & 15);
+    Win16 src(blk - mis, mis);
+    if (src[0] == 0xF0u && len >= 15 && S == len + (len - 15) / 255 + 2) return WalkResult{1u, F_LIT | F_DONE};
+    uint32_t ip = 0, op = 0, nseq = 0;
+    const WalkResult bad{0u, F_BAD | F_DONE};
+    while (true) {
+        if (ip >= S) return bad;
+        const uint32_t tok = src[ip];
+        uint32_t q = ip + 1, ll = tok >> 4, x;
+        if (ll == 15) {
+            do {
+                if (q >= S) return bad;
+                x = src[q++];
+                ll += x;
+                if (ll > len) return bad;
+            } while (x == 255);
+        }
+        if (ll > S - q || ll > len - op) return bad;
+        if (nseq % kCkEvery == 0) ck[nseq / kCkEvery] = make_uint2(ip, op);
+        ++nseq;
+        ip = q + ll;
+        op += ll;
+        if (ip == S) return WalkResult{nseq, F_DONE | (op != len ? F_BAD : 0u)};
+        if (ll == 0) return WalkResult{nseq, F_SLOW | F_DONE};  // a match right after a match
+        if (S - ip < 2) return bad;
+        const uint32_t mo = src[ip] | (src[ip + 1] << 8);
+        if (mo == 0 || mo > op) return bad;
+        if (mo != 1) return WalkResult{nseq, F_SLOW | F_DONE};
+        q = ip + 2;
+        uint32_t ml = (tok & 15) + 4;
+        if ((tok & 15) == 15) {
+            do {
+                if (q >= S) return bad;
+                x = src[q++];
+                ml += x;
+                if (ml > len) return bad;
+            } while (x == 255);
+        }
+        if (ml > len - op) return bad;
+        op += ml;
+        ip = q;
+    }
+}
+
 __global__ __launch_bounds__(64) void k_lz4_parse(Lz4DecArgs a) {
     __shared__ __align__(16) uint8_t s_rings[kWave * K1_STRIDE + kWave * 16];  // rings, then spill slots
     __shared__ uint32_t s_tile, s_tag;
@@ -319,8 +408,13 @@ __global__ __launch_bounds__(64) void k_lz4_parse(Lz4DecArgs a) {
 
     const uint32_t len = live ? block_len(a, b) : 0;
     uint2 *ck = a.ckpt + (live ? ck_base(off, b) : 0);
-    const WalkResult w =
+    WalkResult w =
         k1_walk(s_rings, s_rings + lane * K1_STRIDE, !bad, a.payload, a.payload_bytes, (int64_t)off, (uint32_t)S, len, ck);
+    if (__ballot((w.flags & F_LONG) != 0)) {
+        if (w.flags & F_LONG) w = k1_walk_long(a.payload, (int64_t)off, (uint32_t)S, len, ck);
+    }
+    // a valid block of one sequence is one literal run: K2 copies it as such
+    if (w.nseq == 1 && !(w.flags & (F_BAD | F_SLOW))) w.flags |= F_LIT;
     const uint32_t nseq = w.nseq;
     const bool slow = (w.flags & F_SLOW) != 0;
     bad = bad || (w.flags & F_BAD) != 0;
@@ -333,7 +427,7 @@ __global__ __launch_bounds__(64) void k_lz4_parse(Lz4DecArgs a) {
             const uint32_t k = add_agent32(&a.hdr->aux, 1u);
             if (k < a.nblocks) a.slow_list[k] = (uint32_t)b;
         } else {
-            a.binfo[b] = nseq;
+            a.binfo[b] = nseq | ((w.flags & F_LIT) ? BI_LIT : 0u);
         }
     }
 }
@@ -360,11 +454,12 @@ __device__ __forceinline__ bool k2_defer(K2Queue &qu, uint32_t op, uint32_t n, u
     return true;
 }
 
-// One sequence of a validated canonical block, byte by byte: literal bytes
-// into the zeroed image, then the offset-1 fill when it repeats a non-zero
-// byte.  Returns false at the final sequence.
+// One sequence of a validated canonical block: literal bytes into the zeroed
+// image, then the offset-1 fill when it repeats a non-zero byte; runs longer
+// than K2_LONG are queued for the whole workgroup.  Returns false at the final
+// sequence.
 template <typename Src>
-__device__ __forceinline__ bool k2_seq_bytes(Src src, uint32_t S, uint32_t &ip, uint32_t &op, uint8_t *img,
+__device__ __forceinline__ bool k2_seq_bytes(Src &src, uint32_t S, uint32_t &ip, uint32_t &op, uint8_t *img,
                                              K2Queue &qu) {
     const uint32_t tok = src[ip];
     uint32_t q = ip + 1, ll = tok >> 4;
@@ -407,13 +502,14 @@ __device__ __forceinline__ bool k2_seq_bytes(Src src, uint32_t S, uint32_t &ip, 
     return true;
 }
 
-// Rebuild of one kCkEvery-sequence segment (starting at checkpoint c).
-template <typename Src>
-__device__ __forceinline__ void k2_segment(Src src, uint32_t S, uint32_t nseq, uint32_t s, uint2 c, uint8_t *img,
-                                           K2Queue &qu) {
+// Rebuild of one kCkEvery-sequence segment (starting at checkpoint c) from
+// global memory (block byte x at base + mis + x, base 16-byte aligned).
+__device__ __forceinline__ void k2_segment(const uint8_t *base, uint32_t mis, uint32_t S, uint32_t nseq, uint32_t s,
+                                           uint2 c, uint8_t *img, K2Queue &qu) {
     uint32_t ip = c.x, op = c.y;
     const uint32_t rest = nseq - s * kCkEvery;
     const uint32_t kend = rest < kCkEvery ? rest : kCkEvery;
+    const uint8_t *src = base + mis;
     for (uint32_t k = 0; k < kend; ++k)
         if (!k2_seq_bytes(src, S, ip, op, img, qu)) break;
 }
@@ -472,10 +568,11 @@ __device__ __forceinline__ void k2_segment_lds(const uint8_t *stage, uint32_t mi
 
 // Thread t rebuilds segments t, t + 256, ...; the first from the checkpoint c0
 // loaded early (no loop around it, so nothing waits for the dst loads).
-// STAGED: src is the LDS stage (the block's bytes at src + mis).
-template <bool STAGED, typename Src>
-__device__ __forceinline__ void k2_segments(Src src, uint32_t mis, uint32_t S, uint32_t nseq, const uint2 *ck,
-                                            uint2 c0, uint8_t *img, K2Queue &qu) {
+// The block's bytes are at src + mis (src 16-byte aligned): the LDS stage when
+// STAGED, else global memory.
+template <bool STAGED>
+__device__ __forceinline__ void k2_segments(const uint8_t *src, uint32_t mis, uint32_t S, uint32_t nseq,
+                                            const uint2 *ck, uint2 c0, uint8_t *img, K2Queue &qu) {
     const uint32_t nseg = (nseq + kCkEvery - 1) / kCkEvery;
     const uint32_t t = threadIdx.x;
     if constexpr (STAGED) {
@@ -483,20 +580,50 @@ __device__ __forceinline__ void k2_segments(Src src, uint32_t mis, uint32_t S, u
         for (uint32_t s = t + K2_THREADS; s < nseg; s += K2_THREADS)
             k2_segment_lds(src, mis, S, nseq, s, ck[s], img, qu);
     } else {
-        if (t < nseg) k2_segment(src, S, nseq, t, c0, img, qu);
-        for (uint32_t s = t + K2_THREADS; s < nseg; s += K2_THREADS) k2_segment(src, S, nseq, s, ck[s], img, qu);
+        if (t < nseg) k2_segment(src, mis, S, nseq, t, c0, img, qu);
+        for (uint32_t s = t + K2_THREADS; s < nseg; s += K2_THREADS) k2_segment(src, mis, S, nseq, s, ck[s], img, qu);
     }
 }
 
-template <typename Src>
-__device__ __forceinline__ void k2_deferred(Src src, uint8_t *img, const K2Queue &qu) {
+// The queued runs, one wave per run: a literal run is copied from the
+// compressed bytes (block byte 0 at src, LDS or global memory) and a fill
+// writes its byte, both as 16-byte image pieces (each from two aligned source
+// pieces); the pieces at the run's two ends, shared with its neighbours, go
+// byte by byte.  Each lane has up to four pieces in flight.
+__device__ __forceinline__ void k2_deferred(const uint8_t *src, uint8_t *img, const K2Queue &qu) {
+    constexpr int NWV = K2_THREADS / kWave, U = 4;
     const uint32_t nq = qu.count < (uint32_t)K2_QCAP ? qu.count : (uint32_t)K2_QCAP;
-    for (uint32_t e = 0; e < nq; ++e) {
+    const uint32_t ln = threadIdx.x & (kWave - 1);
+    for (uint32_t e = threadIdx.x / kWave; e < nq; e += NWV) {
         const uint32_t o = qu.op[e], n = qu.n[e], sv = qu.src[e];
-        if (sv & K2_FILL) {
-            for (uint32_t i = threadIdx.x; i < n; i += K2_THREADS) img[o + i] = (uint8_t)sv;
-        } else {
-            for (uint32_t i = threadIdx.x; i < n; i += K2_THREADS) img[o + i] = src[sv + i];
+        const uint32_t p0 = o >> 4, p1 = (o + n - 1) >> 4;  // image pieces the run touches
+        const bool fill = (sv & K2_FILL) != 0;
+        const uint8_t *g = src + (fill ? 0u : sv);           // source of image byte o
+        const uint32_t gm = (uint32_t)((reinterpret_cast<uintptr_t>(g) - o) & 15u);
+        const uint32_t fb = (sv & 0xFFu) * 0x01010101u;
+        for (uint32_t p = p0 + ln; p <= p1; p += U * kWave) {
+            u32x4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t pp = p + (uint32_t)(u * kWave);
+                v[u] = u32x4{fb, fb, fb, fb};
+                if (!fill && pp <= p1 && 16 * pp >= o && 16 * pp + 16 <= o + n) {
+                    const u32x4 *a4 = reinterpret_cast<const u32x4 *>(g + (16 * pp - o) - gm);
+                    v[u] = a4[0];
+                    if (gm) v[u] = take16(v[u], a4[1], (int)gm);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t pp = p + (uint32_t)(u * kWave);
+                if (pp > p1) continue;
+                if (16 * pp >= o && 16 * pp + 16 <= o + n) {
+                    *reinterpret_cast<u32x4 *>(img + 16 * pp) = v[u];
+                } else {
+                    const uint32_t lo = 16 * pp > o ? 16 * pp : o, hi = 16 * pp + 16 < o + n ? 16 * pp + 16 : o + n;
+                    for (uint32_t x = lo; x < hi; ++x) img[x] = fill ? (uint8_t)sv : (uint8_t)g[x - o];
+                }
+            }
         }
     }
 }
@@ -568,7 +695,7 @@ __device__ __forceinline__ void k2_block(const Lz4DecArgs &a, int64_t b, uint32_
         lds_barrier();
         k2_deferred(static_cast<const uint8_t *>(s_stage + mis), s_img, s_q);
     } else {
-        k2_segments<false>(in, 0u, S, nseq, ck, c0, s_img, s_q);
+        k2_segments<false>(in - mis, mis, S, nseq, ck, c0, s_img, s_q);
         lds_barrier();
         k2_deferred(in, s_img, s_q);
     }
@@ -597,6 +724,55 @@ __device__ __forceinline__ void k2_block(const Lz4DecArgs &a, int64_t b, uint32_
     }
 }
 
+// A block K1 found to be one literal run of its full length L (validated in
+// full, or, for a chain longer than K1's ring, only its token and its size
+// S = L + h checked): its h - 1 length bytes are checked here in parallel
+// (255s, then the remainder), and the literals go to dst with
+// 16-byte streams (XORed in, or stored), each dst piece from two aligned
+// pieces of the payload.  A block whose length bytes say otherwise may still
+// be a valid block of another shape: it is handed to K3, which decodes and
+// checks any block.
+template <bool XOR>
+__device__ __forceinline__ void k2_literal_block(const Lz4DecArgs &a, int64_t b, uint64_t off, uint32_t S,
+                                                 uint32_t *s_flag) {
+    const int t = threadIdx.x;
+    const uint32_t len = block_len(a, b);
+    const uint8_t *in = a.payload + off;
+    const uint32_t h = S - len;
+    if (t == 0) *s_flag = 0u;
+    __syncthreads();
+    for (uint32_t x = (uint32_t)t + 1; x < h; x += K2_THREADS) {
+        const uint32_t want = x < h - 1 ? 255u : len - 15 - 255 * (h - 2);
+        if (in[x] != want) *s_flag = 1u;
+    }
+    __syncthreads();
+    if (*s_flag) {
+        if (t == 0) {
+            const uint32_t k = add_agent32(&a.hdr->aux, 1u);
+            if (k < a.nblocks) a.slow_list[k] = (uint32_t)b;
+        }
+        return;
+    }
+    const uint8_t *src = in + h;
+    const uint32_t mis = (uint32_t)(reinterpret_cast<uintptr_t>(src) & 15);
+    const u32x4 *s4 = reinterpret_cast<const u32x4 *>(src - mis);
+    u32x4 *d4 = reinterpret_cast<u32x4 *>(a.dst + b * (int64_t)a.block_bytes);
+    const uint32_t nfull = len >> 4;
+    for (uint32_t c = t; c < nfull; c += K2_THREADS) {
+        // (the second piece holds the last bytes of dst piece c: it starts
+        // inside the block's data, so it never leaves the data's page)
+        u32x4 v = s4[c];
+        if (mis) v = take16(v, s4[c + 1], (int)mis);
+        if constexpr (XOR) v ^= __builtin_nontemporal_load(d4 + c);
+        __builtin_nontemporal_store(v, d4 + c);
+    }
+    if (t == 0) {  // ragged tail of the last block
+        uint8_t *d = reinterpret_cast<uint8_t *>(d4 + nfull);
+        const uint8_t *v = src + 16 * nfull;
+        for (uint32_t x = 0; x < (len & 15); ++x) d[x] = XOR ? (uint8_t)(d[x] ^ v[x]) : v[x];
+    }
+}
+
 // IMG: image bytes, >= block_bytes (one instantiation per supported size class);
 // XOR: mode 1.  Both are compile-time so that every load is issued on one path
 // and the waits for the stage loads leave the dst loads in flight.
@@ -610,6 +786,10 @@ __global__ __launch_bounds__(K2_THREADS) void k_lz4_fast(Lz4DecArgs a) {
     if (info & (BI_BAD | BI_SLOW)) return;
     const uint64_t off = a.offs[b];
     const uint32_t S = a.sizes[b];
+    if (info & BI_LIT) {
+        k2_literal_block<XOR>(a, b, off, S, &s_q.count);
+        return;
+    }
     const uint32_t mis = (uint32_t)(reinterpret_cast<uintptr_t>(a.payload + off) & 15);
     if (S + mis <= (uint32_t)K2_STAGE) k2_block<IMG, XOR, true>(a, b, info & BI_NSEQ, off, S, s_img, s_stage, s_q);
     else k2_block<IMG, XOR, false>(a, b, info & BI_NSEQ, off, S, s_img, s_stage, s_q);

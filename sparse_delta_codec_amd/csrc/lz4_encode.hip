@@ -184,6 +184,7 @@ __device__ __forceinline__ void emit_chunk(uint8_t *win, int32_t wb, const uint8
 
 constexpr int LZE_NW = LZE_THREADS / kWave;
 
+
 struct EncShared {
     uint8_t img[LZE_MAX_BLOCK];
     uint8_t win[LZE_WIN + 48];  // window byte x at win[16 + x]; guards around it
@@ -588,6 +589,63 @@ __device__ __forceinline__ void enc_rest(const Lz4EncArgs &a, const FusedArgs &f
     const int32_t ll_final = len - a_final;
     const int32_t comp = qsum + 1 + ext_bytes(ll_final) + ll_final;
 
+    // A block without a qualifying run (incompressible bytes, such as the
+    // value planes of a packed patch) is one literal sequence: its token and
+    // length bytes, then the block's bytes as they are.  Those go from the
+    // image straight to the payload with 16-byte stores (each output piece
+    // from two image pieces), instead of through the window byte by byte.
+    if (qsum == 0) {
+        if (wv == 0) {
+            lookback_publish(a.status, b, tag, (uint64_t)comp);
+            bool failed = false;
+            const uint64_t off = lookback_resolve(a.status, b, tag, (uint64_t)comp, &failed);
+            if (ln == 0) {
+                if (failed) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
+                sh.off = off;
+                a.comp_sizes[b] = (uint32_t)comp;
+                a.comp_offsets[b] = off;
+                if (b == a.nblocks - 1) *a.d_total = off + comp;
+                if ((int64_t)(off + comp) > a.cap) or_agent32(a.d_status, 1u /*PULSE_DS_CAPACITY*/);
+            }
+        }
+        __syncthreads();
+        const uint32_t off_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(sh.off >> 32));
+        const uint32_t off_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)sh.off);
+        const uint64_t off = ((uint64_t)off_hi << 32) | off_lo;
+        if ((int64_t)(off + comp) > a.cap) return;
+        uint8_t *const dst = a.payload + off;
+        const int32_t h = 1 + ext_bytes(len);  // token and length bytes
+        if (t < h) {
+            uint32_t v;
+            if (t == 0) v = (uint32_t)((len >= 15 ? 15 : len) << 4);
+            else if (t < h - 1) v = 255u;
+            else v = (uint32_t)(len - 15 - 255 * (h - 2));
+            dst[t] = (uint8_t)v;
+        }
+        // literal byte p goes to body + p; aligned piece u of the body's
+        // span covers literal bytes [16 u - shift, +16)
+        uint8_t *const body = dst + h;
+        const int32_t shift = (int32_t)((uintptr_t)body & 15);
+        uint8_t *const base = body - shift;
+        const int32_t npc = (shift + len + 15) >> 4;
+        auto piece = [&](int32_t k) {  // image piece k (bytes [16 k, +16))
+            return *reinterpret_cast<const u32x4 *>(s_img + img_addr<CHLOG>(k << 4));
+        };
+        for (int32_t u = t; u < npc; u += LZE_THREADS) {
+            const int32_t p0 = 16 * u - shift;
+            if (p0 >= 0 && p0 + 16 <= len) {
+                const u32x4 r = shift == 0 ? piece(u) : take16(piece(u - 1), piece(u), 16 - shift);
+                *reinterpret_cast<u32x4 *>(base + 16 * u) = r;
+            } else {
+                for (int32_t j = 0; j < 16; ++j) {
+                    const int32_t p = p0 + j;
+                    if (p >= 0 && p < len) base[16 * u + j] = s_img[img_addr<CHLOG>(p)];
+                }
+            }
+        }
+        return;
+    }
+
     // 4 + 5. place the block and emit it.  Wave 0 publishes the block's size;
     // every wave emits into the LDS window (relative to the block's start),
     // and only then does wave 0 wait for the predecessors' sizes, so the wait
@@ -646,24 +704,7 @@ __device__ __forceinline__ void enc_rest(const Lz4EncArgs &a, const FusedArgs &f
             if (q >= shift && q + 16 <= end) {
                 const u32x4 A = *reinterpret_cast<const u32x4 *>(s_win + q);
                 const u32x4 B = *reinterpret_cast<const u32x4 *>(s_win + q + 16);
-                const uint32_t wv8[8] = {A.x, A.y, A.z, A.w, B.x, B.y, B.z, B.w};
-                u32x4 r;
-                const int wq = o >> 2, bs = o & 3;
-                if (o == 16) {
-                    r = B;
-                } else if (wq == 0) {
-                    r = u32x4{__builtin_amdgcn_alignbyte(wv8[1], wv8[0], bs), __builtin_amdgcn_alignbyte(wv8[2], wv8[1], bs),
-                              __builtin_amdgcn_alignbyte(wv8[3], wv8[2], bs), __builtin_amdgcn_alignbyte(wv8[4], wv8[3], bs)};
-                } else if (wq == 1) {
-                    r = u32x4{__builtin_amdgcn_alignbyte(wv8[2], wv8[1], bs), __builtin_amdgcn_alignbyte(wv8[3], wv8[2], bs),
-                              __builtin_amdgcn_alignbyte(wv8[4], wv8[3], bs), __builtin_amdgcn_alignbyte(wv8[5], wv8[4], bs)};
-                } else if (wq == 2) {
-                    r = u32x4{__builtin_amdgcn_alignbyte(wv8[3], wv8[2], bs), __builtin_amdgcn_alignbyte(wv8[4], wv8[3], bs),
-                              __builtin_amdgcn_alignbyte(wv8[5], wv8[4], bs), __builtin_amdgcn_alignbyte(wv8[6], wv8[5], bs)};
-                } else {
-                    r = u32x4{__builtin_amdgcn_alignbyte(wv8[4], wv8[3], bs), __builtin_amdgcn_alignbyte(wv8[5], wv8[4], bs),
-                              __builtin_amdgcn_alignbyte(wv8[6], wv8[5], bs), __builtin_amdgcn_alignbyte(wv8[7], wv8[6], bs)};
-                }
+                const u32x4 r = take16(A, B, o);
                 *reinterpret_cast<u32x4 *>(base + q) = r;
             } else {
                 for (int32_t x = (q > shift ? q : shift); x < q + 16 && x < end; ++x) base[x] = s_win[16 + x - shift];

@@ -538,6 +538,135 @@ def test_lz4_decode_corrupt_blocks_leave_dst():
             assert np.array_equal(got, ref)
 
 
+def ext_len(n):
+    """LZ4 length bytes after a nibble of 15 for a length n >= 15 (else 0)."""
+    return 0 if n < 15 else (n - 15) // 255 + 1
+
+
+def literal_mix(block_bytes, nlit, tail, seed):
+    """Blocks alternating between incompressible bytes (no two equal
+    neighbours, so no run qualifies: each is one literal run) and a
+    compressible block (random bytes, then zeros) whose encoding is chosen so
+    that a literal block and a compressible one together take an odd number of
+    payload bytes: the literal blocks then start at every alignment mod 16.
+    The last block is `tail` bytes of incompressible data."""
+    rng = np.random.default_rng(seed)
+
+    def lit(v):
+        return (np.cumsum(rng.integers(1, 256, v, dtype=np.int64)) % 256).astype(np.uint8)  # neighbours differ
+
+    lit_size = 1 + ext_len(block_bytes) + block_bytes
+    for p in range(20, 60):
+        cmp = np.zeros(block_bytes, np.uint8)
+        cmp[:p] = rng.integers(1, 256, p, dtype=np.uint8)
+        if (lit_size + int(oracle.lz4_encode_blocks(cmp, block_bytes)["total"])) % 2 == 1:
+            break
+    out = []
+    for _ in range(nlit):
+        out += [lit(block_bytes), cmp]
+    out.append(lit(tail))
+    return np.concatenate(out)
+
+
+@pytest.mark.parametrize("block_bytes", [65536, 16384])
+def test_lz4_literal_only_blocks(block_bytes):
+    """Incompressible blocks (one literal run each: token, length bytes up to
+    a 258-byte header for 64 KiB, then the bytes) at every payload alignment
+    and with ragged tails on both sides of every length-byte boundary: the
+    encoder's payload equals the oracle's byte for byte, and both decode modes
+    equal the oracle's."""
+    for tail in (15, 16, 31, 269, 270, 271, 524, 525, 4097, block_bytes):
+        m = literal_mix(block_bytes, 16, tail, seed=tail)
+        ref = oracle.lz4_encode_blocks(m, block_bytes)
+        lit_blocks = [b for b in range(0, ref["sizes"].size, 2)]
+        lens = [min(block_bytes, m.size - b * block_bytes) for b in lit_blocks]
+        assert all(int(ref["sizes"][b]) == 1 + ext_len(n) + n for b, n in zip(lit_blocks, lens))
+        shifts = {(int(ref["offsets"][b]) + 1 + ext_len(n)) % 16 for b, n in zip(lit_blocks, lens)}
+        assert len(shifts) == 16
+        got = gpu_encode(m, block_bytes)
+        assert got["status"] == 0 and got["total"] == ref["total"]
+        assert np.array_equal(got["sizes"], ref["sizes"]) and np.array_equal(got["offsets"], ref["offsets"])
+        assert np.array_equal(got["payload"], ref["payload"][:ref["total"]])
+        dst = np.random.default_rng(tail + 1).integers(0, 256, m.size, dtype=np.uint8)
+        for mode in (0, 1):
+            d, st = gpu_decode(ref["payload"], ref["offsets"], ref["sizes"], dst, mode, block_bytes=block_bytes)
+            r, rst = oracle.lz4_decode_blocks(ref["payload"], ref["offsets"], ref["sizes"], dst,
+                                              block_bytes=block_bytes, mode=mode)
+            assert st == rst == 0 and np.array_equal(d, r)
+            assert np.array_equal(r, m if mode == 0 else dst ^ m)
+
+
+def length_bytes(n):
+    return [255] * ((n - 15) // 255) + [(n - 15) % 255]
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_lz4_decode_literal_shaped_blocks_of_other_forms(mode):
+    """Blocks with the first token (0xF0) and the size of a single literal run
+    of their full length that are something else: (a) a valid block of two
+    sequences (25515 literals, a 4-byte match at offset 1, 40017 literals),
+    whose length bytes disagree with a single run, decodes like the oracle;
+    (b) a single run with one length byte changed is corrupt and leaves its
+    dst range as it was; the blocks around them decode as usual."""
+    rng = np.random.default_rng(900 + mode)
+    l1, l2 = 25515, 40017
+    a1, a2 = rng.integers(1, 256, l1, dtype=np.uint8), rng.integers(1, 256, l2, dtype=np.uint8)
+    two = np.concatenate([np.array([0xF0] + length_bytes(l1), np.uint8), a1, np.array([1, 0, 0xF0] + length_bytes(l2), np.uint8), a2])
+    assert two.size == 65536 + 1 + ext_len(65536)
+    plain_two = np.concatenate([a1, np.full(4, a1[-1], np.uint8), a2])
+    lit = rng.integers(1, 256, 65536, dtype=np.uint8)
+    one = np.concatenate([np.array([0xF0] + length_bytes(65536), np.uint8), lit])
+    for k, (blk, valid) in enumerate([(two, True), (one, False), (one, False)]):
+        bad = blk.copy()
+        if not valid:
+            bad[1 + (100 if k == 1 else ext_len(65536) - 1)] ^= 1   # a middle 255, then the last length byte
+        comps = [oracle.lz4_encode_blocks(mask_bytes(65536, 0.05, seed=k), 65536)["payload"], bad,
+                 oracle.lz4_encode_blocks(mask_bytes(65536, 1.0, seed=k), 65536)["payload"]]
+        sizes = np.array([c.size for c in comps], np.uint32)
+        offs = np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(np.uint64)
+        payload = np.concatenate(comps)
+        dst = np.full(3 * 65536, 0x5A, np.uint8)
+        got, st = gpu_decode(payload, offs, sizes, dst, mode)
+        ref, rst = oracle.lz4_decode_blocks(payload, offs, sizes, dst, mode=mode)
+        assert st == rst == (0 if valid else pulse.PULSE_DS_CORRUPT)
+        assert np.array_equal(got, ref)
+        if valid:
+            assert np.array_equal(ref[65536:131072], plain_two if mode == 0 else dst[65536:131072] ^ plain_two)
+        else:
+            assert np.all(ref[65536:131072] == 0x5A)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_lz4_decode_length_chains_across_the_ring(mode):
+    """Length chains longer than the parse's 256-byte ring of compressed
+    bytes, at many ring phases: all-zero blocks (a 257-byte match-length
+    chain), p literals then zeros (p = 1 .. 40: a chain of about 255 bytes
+    after each offset position), and 65040 .. 65530 literals then zeros (a
+    literal-length chain of 256 or 257 bytes).  The encoder's payload equals
+    the oracle's, and both decode modes equal the oracle's."""
+    rng = np.random.default_rng(40 + mode)
+    blocks = [np.zeros(65536, np.uint8)]
+    for p in range(1, 41):
+        b = np.zeros(65536, np.uint8)
+        b[:p] = rng.integers(1, 256, p, dtype=np.uint8)
+        blocks.append(b)
+    for L in (65040, 65041, 65100, 65295, 65296, 65300, 65530):
+        b = np.zeros(65536, np.uint8)
+        b[:L] = rng.integers(1, 256, L, dtype=np.uint8)
+        blocks.append(b)
+    blocks.append(np.zeros(65536 - 7, np.uint8))
+    m = np.concatenate(blocks)
+    enc = oracle.lz4_encode_blocks(m, 65536)
+    got = gpu_encode(m)
+    assert got["status"] == 0 and got["total"] == enc["total"]
+    assert np.array_equal(got["payload"], enc["payload"][:enc["total"]])
+    dst = rng.integers(0, 256, m.size, dtype=np.uint8)
+    d, st = gpu_decode(enc["payload"], enc["offsets"], enc["sizes"], dst, mode)
+    r, rst = oracle.lz4_decode_blocks(enc["payload"], enc["offsets"], enc["sizes"], dst, mode=mode)
+    assert st == rst == 0 and np.array_equal(d, r)
+    assert np.array_equal(r, m if mode == 0 else dst ^ m)
+
+
 def test_lz4_decode_in_two_calls_on_two_streams():
     """parse on one stream, apply on another after an event, several payloads in
     a row on one workspace (canonical, general and corrupt blocks): the same
