@@ -91,10 +91,14 @@ __device__ __forceinline__ uint32_t win_byte(uint64_t lo, uint64_t hi, uint32_t 
 // take twice the refills of 512 but leave the other kernel twice the room,
 // and the step is faster for it.
 constexpr int K1_RING = 256;
+// The K1_LOOK bytes after the ring are loaded with it: a sequence that starts
+// in the ring is read whole from one window (no step near the ring's end has
+// to go byte by byte), and a lane stalls only once its position leaves the ring.
+constexpr int K1_LOOK = 32;
 // Rings sit K1_STRIDE bytes apart: lanes refilled together read at nearly the
 // same ring offsets, and with a power-of-two stride those reads would all fall
 // in one LDS bank; 16 more bytes per ring move each lane four banks along.
-constexpr int K1_STRIDE = K1_RING + 16;
+constexpr int K1_STRIDE = K1_RING + K1_LOOK + 16;
 constexpr int K1_PIECES = K1_RING / 16;        // 16-byte pieces per ring
 constexpr int K1_RPI = kWave / K1_PIECES;      // rings filled by one load instruction
 constexpr int K1_BATCH = 8;                    // loads in flight per lane
@@ -120,6 +124,15 @@ __device__ __forceinline__ void ring_refill(uint8_t *rings, const uint8_t *pay, 
     const uint64_t nmask = __ballot(need);
     const int lane = lane_id();
     const int k = lane % K1_PIECES, r = lane / K1_PIECES;
+    // the lane's own lookahead pieces, in flight with the batches below
+    u32x4 la[K1_LOOK / 16];
+    bool lok[K1_LOOK / 16];
+#pragma unroll
+    for (int u = 0; u < K1_LOOK / 16; ++u) {
+        const int64_t o = rbo + K1_RING + 16 * u;
+        lok[u] = need && o < pay_bytes;
+        la[u] = *reinterpret_cast<const u32x4 *>(pay + (lok[u] ? o : -mis));
+    }
 #pragma unroll
     for (int g = 0; g < kWave; g += K1_RPB) {
         if (((nmask >> g) & ((1ull << K1_RPB) - 1)) == 0) continue;
@@ -139,6 +152,11 @@ __device__ __forceinline__ void ring_refill(uint8_t *rings, const uint8_t *pay, 
             uint8_t *to = ok[u] ? rings + j * K1_STRIDE + 16 * k : rings + kWave * K1_STRIDE + 16 * lane;
             *reinterpret_cast<u32x4 *>(to) = v[u];
         }
+    }
+#pragma unroll
+    for (int u = 0; u < K1_LOOK / 16; ++u) {
+        uint8_t *to = lok[u] ? rings + lane * K1_STRIDE + K1_RING + 16 * u : rings + kWave * K1_STRIDE + 16 * lane;
+        *reinterpret_cast<u32x4 *>(to) = la[u];
     }
     __syncthreads();  // one-wave workgroup: the refilled rings are visible to their owners
 }
@@ -179,7 +197,7 @@ __device__ __forceinline__ uint32_t read_ext(const uint8_t *ring, int32_t rb, ui
     while (true) {
         if (q >= S) return F_BAD | F_DONE;
         const uint32_t rq = q - (uint32_t)rb;
-        if (rq >= (uint32_t)K1_RING) return r0 < 16 ? (F_LONG | F_DONE) : F_STALL;
+        if (rq >= (uint32_t)(K1_RING + K1_LOOK)) return r0 < 16 ? (F_LONG | F_DONE) : F_STALL;
         const uint32_t x = ring[rq];
         ++q;
         n += x;
@@ -217,9 +235,12 @@ __device__ __forceinline__ WalkResult k1_walk(uint8_t *rings, const uint8_t *rin
                     // fast step: a whole canonical sequence (1 to 12 literals,
                     // offset 1, at most one match-length byte, inside the
                     // block and the output) from one 16-byte window of the
-                    // ring; everything the general step would check holds
+                    // ring and its lookahead; everything the general step
+                    // would check holds.  A lane past the ring stalls here.
                     const uint32_t r = ip - (uint32_t)rb;
-                    if (ip < S && r + 20 <= (uint32_t)K1_RING) {
+                    if (ip < S && r >= (uint32_t)K1_RING) {
+                        f |= F_STALL;
+                    } else if (ip < S) {
                         const uint32_t *d = reinterpret_cast<const uint32_t *>(ring + (r & ~3u));
                         const uint32_t d0 = d[0], d1 = d[1], d2 = d[2], d3 = d[3], d4 = d[4];
                         const uint32_t sh = r & 3u;
@@ -246,7 +267,7 @@ __device__ __forceinline__ WalkResult k1_walk(uint8_t *rings, const uint8_t *rin
                         }
                     }
                 }
-                if (!took && !(f & F_OFF)) {
+                if (!took && !(f & (F_OFF | F_STALL))) {
                     const uint32_t r = ip - (uint32_t)rb;
                     if (ip >= S) {
                         f |= F_BAD | F_DONE;
@@ -274,7 +295,7 @@ __device__ __forceinline__ WalkResult k1_walk(uint8_t *rings, const uint8_t *rin
                     const uint32_t r = ip - (uint32_t)rb;
                     if (S - ip < 2) {
                         f |= F_BAD | F_DONE;
-                    } else if (r >= (uint32_t)(K1_RING - 2)) {
+                    } else if (r >= (uint32_t)(K1_RING + K1_LOOK - 2)) {
                         f |= F_STALL;
                     } else {
                         const uint32_t mo = (uint32_t)ring[r] | ((uint32_t)ring[r + 1] << 8);
