@@ -194,10 +194,25 @@ constexpr uint32_t F_DONE = 1u, F_BAD = 2u, F_SLOW = 4u, F_STALL = 8u, F_OFF = 1
 // (F_LONG: the block is walked again by k1_walk_long).
 __device__ __forceinline__ uint32_t read_ext(const uint8_t *ring, int32_t rb, uint32_t S, uint32_t len,
                                              uint32_t r0, uint32_t &q, uint32_t &n) {
+    bool first = true;
     while (true) {
         if (q >= S) return F_BAD | F_DONE;
-        const uint32_t rq = q - (uint32_t)rb;
+        uint32_t rq = q - (uint32_t)rb;
         if (rq >= (uint32_t)(K1_RING + K1_LOOK)) return r0 < 16 ? (F_LONG | F_DONE) : F_STALL;
+        if (!first) {
+            // inside a chain of 255s: four bytes per LDS round trip while
+            // they are all 255 (and inside the block and the ring)
+            while (q + 4 <= S && rq + 4 <= (uint32_t)(K1_RING + K1_LOOK) &&
+                   (ring[rq] & ring[rq + 1] & ring[rq + 2] & ring[rq + 3]) == 255u) {
+                q += 4;
+                rq += 4;
+                n += 4 * 255;
+                if (n > len) return F_BAD | F_DONE;
+            }
+            if (q >= S) return F_BAD | F_DONE;
+            if (rq >= (uint32_t)(K1_RING + K1_LOOK)) return r0 < 16 ? (F_LONG | F_DONE) : F_STALL;
+        }
+        first = false;
         const uint32_t x = ring[rq];
         ++q;
         n += x;
@@ -475,22 +490,35 @@ __device__ __forceinline__ bool k2_defer(K2Queue &qu, uint32_t op, uint32_t n, u
     return true;
 }
 
+// The sum of a validated length chain starting at src[q] (bytes added while
+// they are 255); q moves past it.  GROUP (the LDS stage): past a first byte of
+// 255, four bytes are tested per round trip while they are all 255 (the
+// global-memory variant keeps the plain loop, which its hot path runs faster).
+template <bool GROUP, typename Src>
+__device__ __forceinline__ uint32_t k2_chain(Src &src, uint32_t S, uint32_t &q) {
+    uint32_t x = src[q++], n = x;
+    if (x != 255) return n;
+    while (GROUP && q + 4 <= S && (src[q] & src[q + 1] & src[q + 2] & src[q + 3]) == 255u) {
+        q += 4;
+        n += 4 * 255;
+    }
+    do {
+        x = src[q++];
+        n += x;
+    } while (x == 255);
+    return n;
+}
+
 // One sequence of a validated canonical block: literal bytes into the zeroed
 // image, then the offset-1 fill when it repeats a non-zero byte; runs longer
 // than K2_LONG are queued for the whole workgroup.  Returns false at the final
 // sequence.
-template <typename Src>
+template <bool GROUP, typename Src>
 __device__ __forceinline__ bool k2_seq_bytes(Src &src, uint32_t S, uint32_t &ip, uint32_t &op, uint8_t *img,
                                              K2Queue &qu) {
     const uint32_t tok = src[ip];
     uint32_t q = ip + 1, ll = tok >> 4;
-    if (ll == 15) {
-        uint32_t x;
-        do {
-            x = src[q++];
-            ll += x;
-        } while (x == 255);
-    }
+    if (ll == 15) ll += k2_chain<GROUP>(src, S, q);
     uint32_t last = 0;
     if (ll > K2_LONG) {
         last = src[q + ll - 1];
@@ -507,13 +535,7 @@ __device__ __forceinline__ bool k2_seq_bytes(Src &src, uint32_t S, uint32_t &ip,
     if (q >= S) return false;  // the final sequence
     q += 2;                    // offset 1
     uint32_t ml = (tok & 15) + 4;
-    if ((tok & 15) == 15) {
-        uint32_t x;
-        do {
-            x = src[q++];
-            ml += x;
-        } while (x == 255);
-    }
+    if ((tok & 15) == 15) ml += k2_chain<GROUP>(src, S, q);
     if (last) {
         if (ml <= K2_LONG || !k2_defer(qu, op, ml, K2_FILL | last))
             for (uint32_t i = 0; i < ml; ++i) img[op + i] = (uint8_t)last;
@@ -532,7 +554,7 @@ __device__ __forceinline__ void k2_segment(const uint8_t *base, uint32_t mis, ui
     const uint32_t kend = rest < kCkEvery ? rest : kCkEvery;
     const uint8_t *src = base + mis;
     for (uint32_t k = 0; k < kend; ++k)
-        if (!k2_seq_bytes(src, S, ip, op, img, qu)) break;
+        if (!k2_seq_bytes<false>(src, S, ip, op, img, qu)) break;
 }
 
 // The same from the LDS stage (the block's bytes start at stage + mis).  The
@@ -581,7 +603,7 @@ __device__ __forceinline__ void k2_segment_lds(const uint8_t *stage, uint32_t mi
             const uint32_t ext = mc == 15 ? 1u : 0u;
             op += ll + mc + 4 + (ext ? x : 0u);
             ip += 3 + ll + ext;
-        } else if (!k2_seq_bytes(src, S, ip, op, img, qu)) {
+        } else if (!k2_seq_bytes<true>(src, S, ip, op, img, qu)) {
             break;
         }
     }
