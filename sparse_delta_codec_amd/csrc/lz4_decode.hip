@@ -194,25 +194,10 @@ constexpr uint32_t F_DONE = 1u, F_BAD = 2u, F_SLOW = 4u, F_STALL = 8u, F_OFF = 1
 // (F_LONG: the block is walked again by k1_walk_long).
 __device__ __forceinline__ uint32_t read_ext(const uint8_t *ring, int32_t rb, uint32_t S, uint32_t len,
                                              uint32_t r0, uint32_t &q, uint32_t &n) {
-    bool first = true;
     while (true) {
         if (q >= S) return F_BAD | F_DONE;
-        uint32_t rq = q - (uint32_t)rb;
+        const uint32_t rq = q - (uint32_t)rb;
         if (rq >= (uint32_t)(K1_RING + K1_LOOK)) return r0 < 16 ? (F_LONG | F_DONE) : F_STALL;
-        if (!first) {
-            // inside a chain of 255s: four bytes per LDS round trip while
-            // they are all 255 (and inside the block and the ring)
-            while (q + 4 <= S && rq + 4 <= (uint32_t)(K1_RING + K1_LOOK) &&
-                   (ring[rq] & ring[rq + 1] & ring[rq + 2] & ring[rq + 3]) == 255u) {
-                q += 4;
-                rq += 4;
-                n += 4 * 255;
-                if (n > len) return F_BAD | F_DONE;
-            }
-            if (q >= S) return F_BAD | F_DONE;
-            if (rq >= (uint32_t)(K1_RING + K1_LOOK)) return r0 < 16 ? (F_LONG | F_DONE) : F_STALL;
-        }
-        first = false;
         const uint32_t x = ring[rq];
         ++q;
         n += x;
@@ -491,12 +476,18 @@ __device__ __forceinline__ bool k2_defer(K2Queue &qu, uint32_t op, uint32_t n, u
 }
 
 // The sum of a validated length chain starting at src[q] (bytes added while
-// they are 255); q moves past it.  GROUP (the LDS stage): past a first byte of
-// 255, four bytes are tested per round trip while they are all 255 (the
-// global-memory variant keeps the plain loop, which its hot path runs faster).
+// they are 255); q moves past it.  GROUP (the LDS stage): past eight bytes of
+// 255, four bytes are tested per round trip while they are all 255 (shorter
+// chains, the common ones, and the global-memory variant keep the byte loop,
+// which their hot paths run faster).
 template <bool GROUP, typename Src>
 __device__ __forceinline__ uint32_t k2_chain(Src &src, uint32_t S, uint32_t &q) {
-    uint32_t x = src[q++], n = x;
+    uint32_t x, n = 0, k = 0;
+    do {
+        x = src[q++];
+        n += x;
+        ++k;
+    } while (x == 255 && k < 8);
     if (x != 255) return n;
     while (GROUP && q + 4 <= S && (src[q] & src[q + 1] & src[q + 2] & src[q + 3]) == 255u) {
         q += 4;
