@@ -46,13 +46,24 @@ constexpr uint32_t BI_SLOW = 0x40000000u;
 constexpr uint32_t BI_LIT = 0x20000000u;  // one literal run the size of the block (length bytes checked by K2)
 constexpr uint32_t BI_NSEQ = 0x1FFFFFFFu;
 
-// Checkpoints: one per kCkEvery sequences.  A sequence that is not the last
-// one takes >= 3 compressed bytes (token, 2-byte offset), so a block of S
-// bytes holds at most floor(S / (3 kCkEvery)) + 1 checkpoints; block b's
-// checkpoints start at off_b / (3 kCkEvery) + 2 b, which keeps the blocks'
-// regions disjoint.
-constexpr uint32_t kCkEvery = 16;
+// Checkpoints: one per 2^L sequences, L = ck_log(S) in 0 .. 4 chosen from the
+// block's compressed size S.  A sequence that is not the last one takes >= 3
+// compressed bytes (token, 2-byte offset), so a block holds at most
+// floor(S / (3 * 2^L)) + 1 checkpoints: L is the smallest value that keeps
+// this at or under kCkSeg + 1 (one segment per K2 thread), up to 16
+// sequences a checkpoint for large blocks.  A sparse mask's small blocks thus
+// get short segments: their few sequences are rebuilt by many threads instead
+// of a few walking long ones.  Block b's checkpoints start at
+// off_b / kCkBytes + (kCkSeg + 2) b, which keeps the blocks' regions disjoint
+// (room for floor(S / kCkBytes) + kCkSeg + 2 entries).
+constexpr uint32_t kCkEvery = 16;             // the largest interval
 constexpr uint64_t kCkBytes = 3 * kCkEvery;
+constexpr uint32_t kCkSeg = 256;
+__device__ __forceinline__ uint32_t ck_log(uint32_t S) {
+    uint32_t L = 0;
+    while (L < 4 && S > ((3u * kCkSeg) << L)) ++L;
+    return L;
+}
 
 struct Lz4DecArgs {
     const uint8_t *payload;
@@ -73,7 +84,9 @@ struct Lz4DecArgs {
     uint32_t k1_tiles;
 };
 
-__device__ __forceinline__ int64_t ck_base(uint64_t off, int64_t b) { return (int64_t)(off / kCkBytes) + 2 * b; }
+__device__ __forceinline__ int64_t ck_base(uint64_t off, int64_t b) {
+    return (int64_t)(off / kCkBytes) + (int64_t)(kCkSeg + 2) * b;
+}
 
 __device__ __forceinline__ uint32_t block_len(const Lz4DecArgs &a, int64_t b) {
     const int64_t rest = a.nbytes - b * (int64_t)a.block_bytes;
@@ -220,9 +233,11 @@ struct WalkResult {
 // F_LONG; such blocks are few and have few sequences, and k1_walk_long walks
 // them again from global memory.
 __device__ __forceinline__ WalkResult k1_walk(uint8_t *rings, const uint8_t *ring, bool active, const uint8_t *pay,
-                                              int64_t pay_bytes, int64_t boff, uint32_t S, uint32_t len, uint2 *ck) {
+                                              int64_t pay_bytes, int64_t boff, uint32_t S, uint32_t len, uint2 *ck,
+                                              uint32_t ckl) {
     int32_t rb = -(1 << 30);  // empty ring: every position maps past it
     uint32_t ip = 0, op = 0, tok = 0, nseq = 0;
+    const uint32_t ckm = (1u << ckl) - 1u;
     uint32_t f = active ? 0u : F_DONE;
     while (__ballot(!(f & F_DONE))) {
         f &= ~F_STALL;
@@ -259,7 +274,7 @@ __device__ __forceinline__ WalkResult k1_walk(uint8_t *rings, const uint8_t *rin
                                               (uint32_t)((mc != 15) | (x != 255)) & (uint32_t)(seq_in <= S - ip) &
                                               (uint32_t)(ll + ml <= len - op);
                         if (fast) {
-                            if (nseq % kCkEvery == 0) ck[nseq / kCkEvery] = make_uint2(ip, op);
+                            if ((nseq & ckm) == 0) ck[nseq >> ckl] = make_uint2(ip, op);
                             ++nseq;
                             ip += seq_in;
                             op += ll + ml;
@@ -281,7 +296,7 @@ __device__ __forceinline__ WalkResult k1_walk(uint8_t *rings, const uint8_t *rin
                         if (e) {
                             f |= e;
                         } else {
-                            if (nseq % kCkEvery == 0) ck[nseq / kCkEvery] = make_uint2(ip, op);
+                            if ((nseq & ckm) == 0) ck[nseq >> ckl] = make_uint2(ip, op);
                             ++nseq;
                             ip = q + ll;
                             op += ll;
@@ -339,7 +354,7 @@ __device__ __forceinline__ WalkResult k1_walk(uint8_t *rings, const uint8_t *rin
 // with the first token and the size of a single literal run of its full
 // length is marked F_LIT without reading its chain (K2 checks it).
 __device__ __forceinline__ WalkResult k1_walk_long(const uint8_t *pay, int64_t boff, uint32_t S, uint32_t len,
-                                                   uint2 *ck) {
+                                                   uint2 *ck, uint32_t ckl) {
     const uint8_t *blk = pay + boff;
     const uint32_t mis = (uint32_t)(reinterpret_cast<uintptr_t>(blk) & 15);
     Win16 src(blk - mis, mis);
@@ -359,7 +374,7 @@ __device__ __forceinline__ WalkResult k1_walk_long(const uint8_t *pay, int64_t b
             } while (x == 255);
         }
         if (ll > S - q || ll > len - op) return bad;
-        if (nseq % kCkEvery == 0) ck[nseq / kCkEvery] = make_uint2(ip, op);
+        if ((nseq & ((1u << ckl) - 1u)) == 0) ck[nseq >> ckl] = make_uint2(ip, op);
         ++nseq;
         ip = q + ll;
         op += ll;
@@ -430,9 +445,10 @@ __global__ __launch_bounds__(64) void k_lz4_parse(Lz4DecArgs a) {
     const uint32_t len = live ? block_len(a, b) : 0;
     uint2 *ck = a.ckpt + (live ? ck_base(off, b) : 0);
     WalkResult w =
-        k1_walk(s_rings, s_rings + lane * K1_STRIDE, !bad, a.payload, a.payload_bytes, (int64_t)off, (uint32_t)S, len, ck);
+        k1_walk(s_rings, s_rings + lane * K1_STRIDE, !bad, a.payload, a.payload_bytes, (int64_t)off, (uint32_t)S, len, ck,
+                ck_log((uint32_t)S));
     if (__ballot((w.flags & F_LONG) != 0)) {
-        if (w.flags & F_LONG) w = k1_walk_long(a.payload, (int64_t)off, (uint32_t)S, len, ck);
+        if (w.flags & F_LONG) w = k1_walk_long(a.payload, (int64_t)off, (uint32_t)S, len, ck, ck_log((uint32_t)S));
     }
     // a valid block of one sequence is one literal run: K2 copies it as such
     if (w.nseq == 1 && !(w.flags & (F_BAD | F_SLOW))) w.flags |= F_LIT;
@@ -536,13 +552,13 @@ __device__ __forceinline__ bool k2_seq_bytes(Src &src, uint32_t S, uint32_t &ip,
     return true;
 }
 
-// Rebuild of one kCkEvery-sequence segment (starting at checkpoint c) from
+// Rebuild of one segment of 2^ckl sequences (starting at checkpoint c) from
 // global memory (block byte x at base + mis + x, base 16-byte aligned).
 __device__ __forceinline__ void k2_segment(const uint8_t *base, uint32_t mis, uint32_t S, uint32_t nseq, uint32_t s,
-                                           uint2 c, uint8_t *img, K2Queue &qu) {
+                                           uint32_t ckl, uint2 c, uint8_t *img, K2Queue &qu) {
     uint32_t ip = c.x, op = c.y;
-    const uint32_t rest = nseq - s * kCkEvery;
-    const uint32_t kend = rest < kCkEvery ? rest : kCkEvery;
+    const uint32_t rest = nseq - (s << ckl);
+    const uint32_t kend = rest < (1u << ckl) ? rest : (1u << ckl);
     const uint8_t *src = base + mis;
     for (uint32_t k = 0; k < kend; ++k)
         if (!k2_seq_bytes<false>(src, S, ip, op, img, qu)) break;
@@ -556,10 +572,10 @@ __device__ __forceinline__ void k2_segment(const uint8_t *base, uint32_t mis, ui
 // non-zero literal bytes are written (the image is zeroed).  Any other
 // sequence goes byte by byte, and the next one is tried on the fast path again.
 __device__ __forceinline__ void k2_segment_lds(const uint8_t *stage, uint32_t mis, uint32_t S, uint32_t nseq,
-                                               uint32_t s, uint2 c, uint8_t *img, K2Queue &qu) {
+                                               uint32_t s, uint32_t ckl, uint2 c, uint8_t *img, K2Queue &qu) {
     uint32_t ip = c.x, op = c.y;
-    const uint32_t rest = nseq - s * kCkEvery;
-    const uint32_t kend = rest < kCkEvery ? rest : kCkEvery;
+    const uint32_t rest = nseq - (s << ckl);
+    const uint32_t kend = rest < (1u << ckl) ? rest : (1u << ckl);
     const uint8_t *src = stage + mis;
     for (uint32_t k = 0; k < kend; ++k) {
         const uint32_t P = mis + ip;
@@ -606,16 +622,17 @@ __device__ __forceinline__ void k2_segment_lds(const uint8_t *stage, uint32_t mi
 // STAGED, else global memory.
 template <bool STAGED>
 __device__ __forceinline__ void k2_segments(const uint8_t *src, uint32_t mis, uint32_t S, uint32_t nseq,
-                                            const uint2 *ck, uint2 c0, uint8_t *img, K2Queue &qu) {
-    const uint32_t nseg = (nseq + kCkEvery - 1) / kCkEvery;
+                                            uint32_t ckl, const uint2 *ck, uint2 c0, uint8_t *img, K2Queue &qu) {
+    const uint32_t nseg = (nseq + (1u << ckl) - 1) >> ckl;
     const uint32_t t = threadIdx.x;
     if constexpr (STAGED) {
-        if (t < nseg) k2_segment_lds(src, mis, S, nseq, t, c0, img, qu);
+        if (t < nseg) k2_segment_lds(src, mis, S, nseq, t, ckl, c0, img, qu);
         for (uint32_t s = t + K2_THREADS; s < nseg; s += K2_THREADS)
-            k2_segment_lds(src, mis, S, nseq, s, ck[s], img, qu);
+            k2_segment_lds(src, mis, S, nseq, s, ckl, ck[s], img, qu);
     } else {
-        if (t < nseg) k2_segment(src, mis, S, nseq, t, c0, img, qu);
-        for (uint32_t s = t + K2_THREADS; s < nseg; s += K2_THREADS) k2_segment(src, mis, S, nseq, s, ck[s], img, qu);
+        if (t < nseg) k2_segment(src, mis, S, nseq, t, ckl, c0, img, qu);
+        for (uint32_t s = t + K2_THREADS; s < nseg; s += K2_THREADS)
+            k2_segment(src, mis, S, nseq, s, ckl, ck[s], img, qu);
     }
 }
 
@@ -694,7 +711,8 @@ __device__ __forceinline__ void k2_block(const Lz4DecArgs &a, int64_t b, uint32_
         }
     }
     const uint2 *ck = a.ckpt + ck_base(off, b);
-    const uint32_t nseg = (nseq + kCkEvery - 1) / kCkEvery;
+    const uint32_t ckl = ck_log(S);
+    const uint32_t nseg = (nseq + (1u << ckl) - 1) >> ckl;
     const uint2 c0 = ck[(uint32_t)t < nseg ? t : 0];
     sched_fence();
     u32x4 dv[CPT];
@@ -725,11 +743,11 @@ __device__ __forceinline__ void k2_block(const Lz4DecArgs &a, int64_t b, uint32_
     lds_barrier();
 
     if constexpr (STAGED) {
-        k2_segments<true>(static_cast<const uint8_t *>(s_stage), mis, S, nseq, ck, c0, s_img, s_q);
+        k2_segments<true>(static_cast<const uint8_t *>(s_stage), mis, S, nseq, ckl, ck, c0, s_img, s_q);
         lds_barrier();
         k2_deferred(static_cast<const uint8_t *>(s_stage + mis), s_img, s_q);
     } else {
-        k2_segments<false>(in - mis, mis, S, nseq, ck, c0, s_img, s_q);
+        k2_segments<false>(in - mis, mis, S, nseq, ckl, ck, c0, s_img, s_q);
         lds_barrier();
         k2_deferred(in, s_img, s_q);
     }
@@ -980,7 +998,7 @@ DecLayout dec_layout(size_t ws) {
     return L;
 }
 size_t ck_needed(int64_t nblocks, int64_t payload_bytes) {
-    return (size_t)payload_bytes / kCkBytes + 2 * (size_t)nblocks + 2;
+    return (size_t)payload_bytes / kCkBytes + (size_t)(kCkSeg + 2) * (size_t)nblocks + 2;
 }
 bool dec_fits(size_t ws, int64_t nblocks, int64_t payload_bytes) {
     const DecLayout L = dec_layout(ws);
