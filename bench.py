@@ -713,6 +713,27 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def line_count(idx, count, base_elems, esz, line=64):
+    """Distinct `line`-byte lines that the first `count` of an ascending index
+    list land in (element size esz, the indexed view starting base_elems
+    elements into a 256-byte aligned allocation)."""
+    import torch
+
+    if count <= 0:
+        return 0
+    l = torch.div(idx[:count].to(torch.int64) + base_elems, line // esz, rounding_mode="floor")
+    return int((l[1:] != l[:-1]).sum().item()) + 1
+
+
+def line_floor(ms, lines, stream_bytes):
+    """A scatter's memory-side floor: every 64-byte line it touches is read
+    and written whole (a partially written line costs the memory side a read
+    of it), plus the entry stream it reads."""
+    b = 2 * 64 * lines + stream_bytes
+    return {"touched_lines": lines, "line_floor_GB": round(b / 1e9, 3),
+            "line_floor_GBps": round(b / (ms / 1e3) / 1e9, 1) if ms > 0 else None}
+
+
 def _leg(ms, launches, alg_bytes, **extra):
     secs = ms / 1e3
     out = {"ms": round(ms, 3), "launches": launches, "alg_GB": round(alg_bytes / 1e9, 3),
@@ -795,12 +816,14 @@ def tensor_list_leg(pulse, specs, offs, W, b_old, changed, dev):
     if int(st.item()) != 0:
         raise SystemExit(f"tensor-list leg: device status {int(st.item())} after the apply")
     n = sum(s.numel for s in specs)
+    lines = sum(line_count(idx[so[i]:], so[i + 1] - so[i], offs[i], 2) for i in range(nt))
     log(f"tensor-list leg: one launch {times['list']:.2f} ms, {nt} launches {times['per_tensor']:.2f} ms")
     a_cd = n * 6 + 6 * changed  # read masters (4) + old view (2), write the patch
     return {"cast_diff_list": _leg(times["list"], 1, a_cd, tensors=nt, tiles=table.ntiles,
                                    checked="equal, tensor by tensor, to one pulse_cast_diff per tensor"),
             "cast_diff_per_tensor": _leg(times["per_tensor"], nt, a_cd),
-            "apply_list": _leg(t_apply, 1, 8 * changed, checked="every view equals the cast of its masters")}
+            "apply_list": _leg(t_apply, 1, 8 * changed, checked="every view equals the cast of its masters",
+                               **line_floor(t_apply, lines, 6 * changed))}
 
 
 def patch_stream_leg(pulse, chunks, W, b_old, stage, idx, val, cnt, status, ws_cd, dev, with_oracle):
@@ -904,6 +927,7 @@ def fp8_view_leg(pulse, specs, chunks, offs, qplans, W, b_old, stage, dev, with_
     st = torch.zeros(1, dtype=torch.int32, device=dev)
     ws = pulse.workspace(pulse.PULSE_OP_FP8_DELTA, max_q, 0, dev)
     t_delta = t_apply = 0.0
+    lines = 0
     nq_tot = ns_tot = 0
     ok = True
     sample = None
@@ -930,6 +954,7 @@ def fp8_view_leg(pulse, specs, chunks, offs, qplans, W, b_old, stage, dev, with_
         torch.cuda.synchronize()
         t_delta += ev[0].elapsed_time(ev[1])
         t_apply += ev[1].elapsed_time(ev[2])
+        lines += line_count(ci, int(cc[k].item()), 0, 1) + line_count(si, int(sc[k].item()), 0, 4)
         ok = ok and views_equal(co[:qo], cn[:qo]) and views_equal(so[:so_o].view(torch.int32),
                                                                      sn[:so_o].view(torch.int32))
         nq_tot, ns_tot = nq_tot + qo, ns_tot + so_o
@@ -944,7 +969,8 @@ def fp8_view_leg(pulse, specs, chunks, offs, qplans, W, b_old, stage, dev, with_
     out = {"fp8_view_delta": _leg(t_delta, len(chunks), a_delta, changed_codes_fraction=round(dq, 6),
                                   changed_scales=nscales, codes=nq_tot,
                                   checked="apply(quant(old), delta) == quant(new) on every chunk"),
-           "fp8_view_apply": _leg(t_apply, len(chunks), a_apply)}
+           "fp8_view_apply": _leg(t_apply, len(chunks), a_apply,
+                                  **line_floor(t_apply, lines, 5 * ncodes + 8 * nscales))}
     if sample is not None:  # the CPU baseline of this leg
         import numpy as np
 
@@ -1003,6 +1029,7 @@ def loco_leg(pulse, dev, with_oracle):
         chk = 1 << 22
         host_in = (theta[:chk].cpu().numpy(), delta[:chk].cpu().numpy(), resid[:chk].cpu().numpy())
         t_gate = t_acc = 0.0
+        acc_lines = 0
         first = None
         for k, (s0, e0, _) in enumerate(chunks):
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
@@ -1014,6 +1041,7 @@ def loco_leg(pulse, dev, with_oracle):
             torch.cuda.synchronize()
             t_gate += ev[0].elapsed_time(ev[1])
             t_acc += ev[1].elapsed_time(ev[2])
+            acc_lines += line_count(idx, int(cnt[k].item()), s0, 4)
             if k == 0:
                 m0 = int(cnt[0].item())
                 first = (idx[:min(m0, chk)].cpu().numpy(), val[:min(m0, chk)].cpu().numpy(),
@@ -1043,7 +1071,7 @@ def loco_leg(pulse, dev, with_oracle):
     out["loco_gate"] = _leg(t_gate, len(chunks), a_gate, sent_fraction=round(dg, 6), params=n,
                             workload="Qwen2.5-7B-shaped FP32 checkpoint, round 2 of H=8 local steps at lr 3e-6",
                             checked="first 2^22 elements: sent = visible, values and buffer exact")
-    out["loco_accumulate"] = _leg(t_acc, len(chunks), a_acc)
+    out["loco_accumulate"] = _leg(t_acc, len(chunks), a_acc, **line_floor(t_acc, acc_lines, 8 * sent))
     if with_oracle:  # the CPU baseline of this leg
         import oracle
 
@@ -1082,6 +1110,7 @@ def encode_apply_leg(pulse, chunks, W, b_old, b_recv, stage, idx, val, status, w
     cnt = torch.zeros(len(chunks), dtype=torch.int64, device=dev)
     cap = idx.numel()
     te = ta = 0.0
+    lines = 0
     for r in range(reps + 1):
         ev = []
         for ci, (s0, e0, _) in enumerate(chunks):
@@ -1090,6 +1119,8 @@ def encode_apply_leg(pulse, chunks, W, b_old, b_recv, stage, idx, val, status, w
             e[0].record()
             pulse.pulse_cast_diff(W[s0:e0], b_old[s0:e0], stage[:m], None, idx, val, cnt[ci:ci + 1], status, ws_cd)
             e[1].record()
+            if r == 0:  # (the checked pass, untimed) the receiver view's lines this chunk's patch lands in
+                lines += line_count(idx, int(cnt[ci].item()), s0, 2)
             pulse.pulse_apply_patch(b_recv[s0:e0], idx, val, cnt[ci:ci + 1], status, max_count=cap)
             e[2].record()
             ev.append(e)
@@ -1109,6 +1140,7 @@ def encode_apply_leg(pulse, chunks, W, b_old, b_recv, stage, idx, val, status, w
     a_enc, a_app = n * (8 + 6 * d), n * 8 * d
     secs = (me + ma) / 1e3
     return {"ms": round(me + ma, 3), "encode_ms": round(me, 3), "apply_ms": round(ma, 3),
+            "apply_line_floor": line_floor(ma, lines, 6 * int(cnt.sum().item())),
             "GBps_weights": round(2 * n / secs / 1e9, 1), "alg_GB": round((a_enc + a_app) / 1e9, 3),
             "GBps": round((a_enc + a_app) / secs / 1e9, 1), "frac_hbm": round((a_enc + a_app) / secs / PEAK_HBM, 4),
             "encode_frac_hbm": round(a_enc / (me / 1e3) / PEAK_HBM, 4),
