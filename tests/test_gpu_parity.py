@@ -667,6 +667,59 @@ def test_lz4_decode_length_chains_across_the_ring(mode):
     assert np.array_equal(r, m if mode == 0 else dst ^ m)
 
 
+def canonical_seq(lit, ml):
+    """One canonical sequence: one literal byte, offset 1, a match of ml >= 4
+    (the literal repeated): its bytes and the bytes it decodes to."""
+    mc = min(ml - 4, 15)
+    ext = length_bytes(ml - 4) if ml - 4 >= 15 else []
+    return [0x10 | mc, lit, 1, 0] + ext, [lit] * (ml + 1)
+
+
+def canonical_block(rng, nseq, ml, lf):
+    """nseq canonical sequences (match length ml each, non-zero literals), then
+    a final run of lf >= 5 literals."""
+    comp, plain = [], []
+    for lit in rng.integers(1, 256, nseq):
+        c, p = canonical_seq(int(lit), ml)
+        comp += c
+        plain += p
+    tail = [int(x) for x in rng.integers(1, 256, lf)]
+    comp += [min(lf, 15) << 4] + (length_bytes(lf) if lf >= 15 else []) + tail
+    plain += tail
+    return np.array(comp, np.uint8), np.array(plain, np.uint8)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_lz4_decode_checkpoint_intervals(mode):
+    """The decode's checkpoint interval is chosen per block from its
+    compressed size S (1 sequence up to S = 768, doubling at 768, 1536, 3072
+    and 6144 bytes, 16 above).  Blocks of the densest canonical sequences (4
+    bytes each) at sizes on both sides of every threshold, after a 64 KiB
+    block of 13,106 such sequences (820 segments: K2's threads take several
+    each) and a staged block of 5-byte sequences: both modes equal the
+    oracle's decode and the plain bytes."""
+    rng = np.random.default_rng(60 + mode)
+    a = canonical_block(rng, 13106, 4, 6)                      # 64 KiB out, S = 52,431
+    b = canonical_block(rng, 1074, 60, 65536 - 1074 * 61)      # 64 KiB out, S = 5,37x
+    assert a[1].size == 65536 and b[1].size == 65536 and a[0].size == 52431 and b[0].size < 6144
+    for target in (6, 200, 767, 768, 769, 1535, 1536, 1537, 3071, 3072, 3073, 6143, 6144, 6145, 13001):
+        lf = 5 + (target - 1 - 5) % 4                          # S = 4 k + 1 + lf
+        k = (target - 1 - lf) // 4
+        c, p = canonical_block(rng, k, 4, lf)
+        assert c.size == target
+        comps, plains = [a[0], b[0], c], [a[1], b[1], p]
+        sizes = np.array([x.size for x in comps], np.uint32)
+        offs = np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(np.uint64)
+        payload = np.concatenate(comps)
+        plain = np.concatenate(plains)
+        dst = rng.integers(0, 256, plain.size, dtype=np.uint8)
+        got, st = gpu_decode(payload, offs, sizes, dst, mode)
+        ref, rst = oracle.lz4_decode_blocks(payload, offs, sizes, dst, mode=mode)
+        assert st == rst == 0, target
+        assert np.array_equal(ref, plain if mode == 0 else dst ^ plain), target
+        assert np.array_equal(got, ref), target
+
+
 def test_lz4_decode_in_two_calls_on_two_streams():
     """parse on one stream, apply on another after an event, several payloads in
     a row on one workspace (canonical, general and corrupt blocks): the same
