@@ -12,7 +12,8 @@
 //    adding it to the shared checkpoint changes that entry's BF16 view; the
 //    rest stays in the buffer for the next round.
 //
-// One 256-thread workgroup per 16384-element tile; the tile is a ticket taken
+// One 256-thread workgroup per tile of R rounds of 16384 elements (R = 4 for
+// the one-byte codes, whose rounds are short, else 1); the tile is a ticket taken
 // with one atomic when the workgroup starts, so a tile only ever waits for
 // tiles whose workgroups are already running, whatever the device's residency
 // (no co-residency assumption).  Pass 1 streams the tile with 16-byte loads
@@ -31,10 +32,11 @@ namespace pulse {
 
 enum DcMode { DC_U8 = 0, DC_U32 = 1, DC_GATE = 2 };
 
+// K elements per lane and group, G groups, R rounds of DC_TILE elements a tile
 template <int M> struct DcShape;
-template <> struct DcShape<DC_U8> { static constexpr int K = 16, G = 4; };
-template <> struct DcShape<DC_U32> { static constexpr int K = 4, G = 16; };
-template <> struct DcShape<DC_GATE> { static constexpr int K = 4, G = 16; };
+template <> struct DcShape<DC_U8> { static constexpr int K = 16, G = 4, R = 4; };
+template <> struct DcShape<DC_U32> { static constexpr int K = 4, G = 16, R = 1; };
+template <> struct DcShape<DC_GATE> { static constexpr int K = 4, G = 16, R = 1; };
 
 struct DcArgs {
     const void *x0;  // U8 / U32: old view; GATE: checkpoint theta (float32)
@@ -53,7 +55,9 @@ struct DcArgs {
 
 constexpr int DC_THREADS = 256;
 constexpr int DC_WAVE_ELEMS = 4096;
-constexpr int DC_TILE = (DC_THREADS / kWave) * DC_WAVE_ELEMS;  // 16384
+constexpr int DC_TILE = (DC_THREADS / kWave) * DC_WAVE_ELEMS;  // 16384, one round
+template <int M>
+constexpr int64_t dc_tile_elems() { return (int64_t)DC_TILE * DcShape<M>::R; }
 // entries staged per wave before a coalesced flush: at least one group's worth
 // (64 lanes x K elements), which is what one group can add at once
 template <int M>
@@ -190,7 +194,7 @@ __device__ __forceinline__ uint64_t dc_pass1(const DcArgs &a, int64_t wbase, int
 
 template <int M>
 struct DcShared {
-    uint32_t wtot[DC_THREADS / kWave];
+    uint32_t wtot[DcShape<M>::R][DC_THREADS / kWave];
     uint64_t prefix;
     int32_t sbi[DC_THREADS / kWave][dc_sb<M>()];
     typename std::conditional<M == DC_U8, uint8_t, uint32_t>::type sbv[DC_THREADS / kWave][dc_sb<M>()];
@@ -217,28 +221,31 @@ __device__ __forceinline__ void dc_flush(const DcArgs &a, const int32_t *sbi, co
 
 template <int M, bool FULL>
 __device__ __forceinline__ void dc_tile(const DcArgs &a, uint32_t tile, uint32_t tag, DcShared<M> &sh) {
-    constexpr int K = DcShape<M>::K, G = DcShape<M>::G;
+    constexpr int K = DcShape<M>::K, G = DcShape<M>::G, R = DcShape<M>::R;
     const int w = wave_id(), l = lane_id();
-    const int64_t wbase = (int64_t)tile * DC_TILE + (int64_t)w * DC_WAVE_ELEMS;
-    uint32_t v[M == DC_U8 ? 16 : 64];
-    uint64_t flags = dc_pass1<M, FULL>(a, wbase, l, v);
-    {
+    // round r of the tile: elements [tile * R + r) * DC_TILE, +DC_TILE), wave w
+    // owning DC_WAVE_ELEMS of them; entries go out in element order
+    int64_t wbase[R];
+    uint32_t v[R][M == DC_U8 ? 16 : 64];
+    uint64_t flags[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        wbase[r] = ((int64_t)tile * R + r) * DC_TILE + (int64_t)w * DC_WAVE_ELEMS;
+        flags[r] = dc_pass1<M, FULL>(a, wbase[r], l, v[r]);
         // materialise the flags as one 64-bit word (otherwise the compiler keeps
         // each compare result live on its own until pass 2)
-        uint32_t lo = (uint32_t)flags, hi = (uint32_t)(flags >> 32);
+        uint32_t lo = (uint32_t)flags[r], hi = (uint32_t)(flags[r] >> 32);
         asm volatile("" : "+v"(lo), "+v"(hi));
-        flags = ((uint64_t)hi << 32) | lo;
+        flags[r] = ((uint64_t)hi << 32) | lo;
+        const uint32_t wtot = wave_reduce_sum((uint32_t)__builtin_popcountll(flags[r]));
+        if (l == 0) sh.wtot[r][w] = wtot;
     }
-
-    const uint32_t wtot = wave_reduce_sum((uint32_t)__builtin_popcountll(flags));
-    if (l == 0) sh.wtot[w] = wtot;
     __syncthreads();
-    uint32_t tile_count = 0, wpre = 0;
+    uint32_t tile_count = 0;
 #pragma unroll
-    for (int i = 0; i < DC_THREADS / kWave; ++i) {
-        if (i < w) wpre += sh.wtot[i];
-        tile_count += sh.wtot[i];
-    }
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int i = 0; i < DC_THREADS / kWave; ++i) tile_count += sh.wtot[r][i];
     if (w == 0) {
         bool failed = false;
         const uint64_t pre = lookback_wave(a.status, tile, tag, tile_count, &failed);
@@ -250,56 +257,67 @@ __device__ __forceinline__ void dc_tile(const DcArgs &a, uint32_t tile, uint32_t
         }
     }
     __syncthreads();
-    int64_t run = (int64_t)sh.prefix + wpre;
     int32_t *sbi = sh.sbi[w];
     auto *sbv = sh.sbv[w];
-    uint32_t nb = 0;
-    if (tile_count != 0 || M == DC_GATE) {
+    uint32_t before = 0;  // entries of the earlier rounds and of the lower waves of this one
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const uint32_t f = (uint32_t)(flags >> (g * K)) & ((1u << K) - 1u);
-            uint64_t m[K];
-            uint32_t gtot = 0;
+    for (int r = 0; r < R; ++r) {
+        uint32_t rpre = 0, rtot = 0;
 #pragma unroll
-            for (int k = 0; k < K; ++k) {
-                m[k] = __ballot((f >> k) & 1u);
-                gtot += __builtin_popcountll(m[k]);
-            }
-            uint32_t sent = 0;  // GATE: bit k set when element k went into the patch
-            if (gtot != 0) {
-                if (nb + gtot > (uint32_t)dc_sb<M>()) dc_flush<M>(a, sbi, sbv, nb, run);
-                uint32_t r = nb;
+        for (int i = 0; i < DC_THREADS / kWave; ++i) {
+            if (i < w) rpre += sh.wtot[r][i];
+            rtot += sh.wtot[r][i];
+        }
+        int64_t run = (int64_t)sh.prefix + before + rpre;
+        before += rtot;
+        uint32_t nb = 0;
+        if (rtot != 0 || M == DC_GATE) {
 #pragma unroll
-                for (int k = 0; k < K; ++k) r += lanes_below_dc(m[k]);
-                const int32_t e0 = (int32_t)(wbase + g * 64 * K + K * l);
+            for (int g = 0; g < G; ++g) {
+                const uint32_t f = (uint32_t)(flags[r] >> (g * K)) & ((1u << K) - 1u);
+                uint64_t m[K];
+                uint32_t gtot = 0;
 #pragma unroll
                 for (int k = 0; k < K; ++k) {
-                    if (f & (1u << k)) {
-                        sbi[r] = e0 + k;
-                        if constexpr (M == DC_U8) sbv[r] = (uint8_t)(v[4 * g + (k >> 2)] >> (8 * (k & 3)));
-                        else sbv[r] = v[4 * g + k];
-                        if (run + r < a.cap) sent |= 1u << k;
-                        ++r;
+                    m[k] = __ballot((f >> k) & 1u);
+                    gtot += __builtin_popcountll(m[k]);
+                }
+                uint32_t sent = 0;  // GATE: bit k set when element k went into the patch
+                if (gtot != 0) {
+                    if (nb + gtot > (uint32_t)dc_sb<M>()) dc_flush<M>(a, sbi, sbv, nb, run);
+                    uint32_t q = nb;
+#pragma unroll
+                    for (int k = 0; k < K; ++k) q += lanes_below_dc(m[k]);
+                    const int32_t e0 = (int32_t)(wbase[r] + g * 64 * K + K * l);
+#pragma unroll
+                    for (int k = 0; k < K; ++k) {
+                        if (f & (1u << k)) {
+                            sbi[q] = e0 + k;
+                            if constexpr (M == DC_U8) sbv[q] = (uint8_t)(v[r][4 * g + (k >> 2)] >> (8 * (k & 3)));
+                            else sbv[q] = v[r][4 * g + k];
+                            if (run + q < a.cap) sent |= 1u << k;
+                            ++q;
+                        }
+                    }
+                    nb += gtot;
+                }
+                if constexpr (M == DC_GATE) {
+                    // the buffer keeps everything that was not sent
+                    uint32_t *pr = reinterpret_cast<uint32_t *>(a.resid) + wbase[r] + g * 64 * K + K * l;
+                    u32x4 o;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) o[k] = (sent >> k) & 1u ? 0u : v[r][4 * g + k];
+                    if constexpr (FULL) {
+                        *reinterpret_cast<u32x4 *>(pr) = o;
+                    } else {
+#pragma unroll
+                        for (int k = 0; k < 4; ++k)
+                            if (wbase[r] + g * 64 * K + K * l + k < a.n) pr[k] = o[k];
                     }
                 }
-                nb += gtot;
             }
-            if constexpr (M == DC_GATE) {
-                // the buffer keeps everything that was not sent
-                uint32_t *pr = reinterpret_cast<uint32_t *>(a.resid) + wbase + g * 64 * K + K * l;
-                u32x4 o;
-#pragma unroll
-                for (int k = 0; k < 4; ++k) o[k] = (sent >> k) & 1u ? 0u : v[4 * g + k];
-                if constexpr (FULL) {
-                    *reinterpret_cast<u32x4 *>(pr) = o;
-                } else {
-#pragma unroll
-                    for (int k = 0; k < 4; ++k)
-                        if (wbase + g * 64 * K + K * l + k < a.n) pr[k] = o[k];
-                }
-            }
+            if (nb) dc_flush<M>(a, sbi, sbv, nb, run);
         }
-        if (nb) dc_flush<M>(a, sbi, sbv, nb, run);
     }
     __syncthreads();  // sh is reused by the next tile
 }
@@ -320,7 +338,7 @@ __global__ __launch_bounds__(DC_THREADS) void k_delta_compact(DcArgs a) {
         if (threadIdx.x == 0) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
         return;
     }
-    if (tile < (uint32_t)(a.n / DC_TILE)) dc_tile<M, true>(a, tile, tag, sh);
+    if (tile < (uint32_t)(a.n / dc_tile_elems<M>())) dc_tile<M, true>(a, tile, tag, sh);
     else dc_tile<M, false>(a, tile, tag, sh);
 }
 
@@ -387,7 +405,7 @@ int launch_delta_compact(const void *x0, const void *x1, float *resid, int64_t n
     a.n = n;
     a.hdr = reinterpret_cast<WsHeader *>(ws);
     a.status = reinterpret_cast<uint64_t *>(static_cast<char *>(ws) + sizeof(WsHeader));
-    const int64_t ntiles = (n + DC_TILE - 1) / DC_TILE;
+    const int64_t ntiles = (n + dc_tile_elems<M>() - 1) / dc_tile_elems<M>();
     a.ntiles = (uint32_t)ntiles;
     k_delta_compact<M><<<dim3((unsigned)ntiles), dim3(DC_THREADS), 0, stream>>>(a);
     return hipGetLastError() == hipSuccess ? 0 : -5;

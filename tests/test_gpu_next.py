@@ -14,6 +14,8 @@ if torch.cuda.is_available():
     from tests.gpu_util import dev, host, zeros  # noqa: E402
 
 SIZES = [1, 15, 16, 17, 1000, 16383, 16384, 16385, 3 * 16384 + 5, 100_007]
+# the codes' tiles are 65536 bytes (four rounds of 16384): both sides of a tile, partial rounds
+CODE_SIZES = SIZES + [65535, 65536, 65537, 3 * 65536 + 16389, 262_147]
 
 
 def u32(a):
@@ -46,7 +48,7 @@ def same_delta(g, r):
     assert g["status"] == r["status"]
 
 
-@pytest.mark.parametrize("n", SIZES)
+@pytest.mark.parametrize("n", CODE_SIZES)
 @pytest.mark.parametrize("p", [0.0, 0.01, 0.5, 1.0])
 def test_fp8_view_delta_matches_oracle(n, p):
     rng = np.random.default_rng(n * 7 + int(p * 100))
