@@ -53,17 +53,26 @@ constexpr uint32_t BI_NSEQ = 0x1FFFFFFFu;
 // this at or under kCkSeg + 1 (one segment per K2 thread), up to 16
 // sequences a checkpoint for large blocks.  A sparse mask's small blocks thus
 // get short segments: their few sequences are rebuilt by many threads instead
-// of a few walking long ones.  Block b's checkpoints start at
-// off_b / kCkBytes + (kCkSeg + 2) b, which keeps the blocks' regions disjoint
-// (room for floor(S / kCkBytes) + kCkSeg + 2 entries).
+// of a few walking long ones.  A block with L = 4 that compresses to more
+// than half its length (ck_direct: long literal runs of nearly incompressible
+// bytes) and holds at most kCkDirect sequences also gets one checkpoint per
+// sequence, in the kCkDirect slots after its 16-sequence ones (from
+// ck_direct_slot(S)): it is rebuilt one sequence per thread.  Block b's
+// checkpoints start at off_b / kCkBytes + (kCkSeg + 2) b, which keeps the
+// blocks' regions disjoint (room for floor(S / kCkBytes) + kCkSeg + 2 entries).
 constexpr uint32_t kCkEvery = 16;             // the largest interval
 constexpr uint64_t kCkBytes = 3 * kCkEvery;
 constexpr uint32_t kCkSeg = 256;
+constexpr uint32_t kCkDirect = 128;
 __device__ __forceinline__ uint32_t ck_log(uint32_t S) {
     uint32_t L = 0;
     while (L < 4 && S > ((3u * kCkSeg) << L)) ++L;
     return L;
 }
+__device__ __forceinline__ bool ck_direct(uint32_t S, uint32_t len, uint32_t nseq) {
+    return ck_log(S) == 4 && 2 * S > len && nseq <= kCkDirect;
+}
+__device__ __forceinline__ uint32_t ck_direct_slot(uint32_t S) { return S / (uint32_t)kCkBytes + 2; }
 
 struct Lz4DecArgs {
     const uint8_t *payload;
@@ -400,6 +409,39 @@ __device__ __forceinline__ WalkResult k1_walk_long(const uint8_t *pay, int64_t b
     }
 }
 
+// The direct checkpoints of a validated block (see ck_direct): its sequence
+// starts walked again from global memory, one aligned 16-byte piece at a time.
+__device__ __forceinline__ void k1_direct_ck(const uint8_t *pay, int64_t boff, uint32_t nseq, uint2 *dck) {
+    const uint8_t *blk = pay + boff;
+    const uint32_t mis = (uint32_t)(reinterpret_cast<uintptr_t>(blk) & 15);
+    Win16 src(blk - mis, mis);
+    uint32_t ip = 0, op = 0;
+    for (uint32_t k = 0; k < nseq; ++k) {
+        dck[k] = make_uint2(ip, op);
+        const uint32_t tok = src[ip];
+        uint32_t q = ip + 1, ll = tok >> 4, x;
+        if (ll == 15) {
+            do {
+                x = src[q++];
+                ll += x;
+            } while (x == 255);
+        }
+        q += ll;
+        op += ll;
+        if (k + 1 == nseq) break;  // the final sequence has no match
+        q += 2;
+        uint32_t ml = (tok & 15) + 4;
+        if ((tok & 15) == 15) {
+            do {
+                x = src[q++];
+                ml += x;
+            } while (x == 255);
+        }
+        op += ml;
+        ip = q;
+    }
+}
+
 __global__ __launch_bounds__(64) void k_lz4_parse(Lz4DecArgs a) {
     __shared__ __align__(16) uint8_t s_rings[kWave * K1_STRIDE + kWave * 16];  // rings, then spill slots
     __shared__ uint32_t s_tile, s_tag;
@@ -452,6 +494,11 @@ __global__ __launch_bounds__(64) void k_lz4_parse(Lz4DecArgs a) {
     }
     // a valid block of one sequence is one literal run: K2 copies it as such
     if (w.nseq == 1 && !(w.flags & (F_BAD | F_SLOW))) w.flags |= F_LIT;
+    // a large, literal-heavy block of few sequences: one checkpoint per sequence
+    const bool direct = !bad && !(w.flags & (F_BAD | F_SLOW | F_LIT)) && ck_direct((uint32_t)S, len, w.nseq);
+    if (__ballot(direct)) {
+        if (direct) k1_direct_ck(a.payload, (int64_t)off, w.nseq, ck + ck_direct_slot((uint32_t)S));
+    }
     const uint32_t nseq = w.nseq;
     const bool slow = (w.flags & F_SLOW) != 0;
     bad = bad || (w.flags & F_BAD) != 0;
@@ -711,7 +758,11 @@ __device__ __forceinline__ void k2_block(const Lz4DecArgs &a, int64_t b, uint32_
         }
     }
     const uint2 *ck = a.ckpt + ck_base(off, b);
-    const uint32_t ckl = ck_log(S);
+    uint32_t ckl = ck_log(S);
+    if (ck_direct(S, len, nseq)) {  // one checkpoint per sequence
+        ck += ck_direct_slot(S);
+        ckl = 0;
+    }
     const uint32_t nseg = (nseq + (1u << ckl) - 1) >> ckl;
     const uint2 c0 = ck[(uint32_t)t < nseg ? t : 0];
     sched_fence();

@@ -720,6 +720,57 @@ def test_lz4_decode_checkpoint_intervals(mode):
         assert np.array_equal(got, ref), target
 
 
+def literal_run_block(rng, nseq, total, ml):
+    """A canonical block of nseq sequences, each a run of non-zero literals and
+    an offset-1 match of ml, then a final literal run, decoding to `total`
+    bytes: its bytes and its plain bytes."""
+    ll = (total - 16) // nseq - ml
+    assert ll >= 1 and ml >= 4
+    comp, plain = [], []
+    for _ in range(nseq):
+        lits = [int(x) for x in rng.integers(1, 256, ll)]
+        mc = min(ml - 4, 15)
+        comp += [(min(ll, 15) << 4) | mc] + (length_bytes(ll) if ll >= 15 else []) + lits + [1, 0]
+        comp += length_bytes(ml - 4) if ml - 4 >= 15 else []
+        plain += lits + [lits[-1]] * ml
+    lf = total - len(plain)
+    tail = [int(x) for x in rng.integers(1, 256, lf)]
+    comp += [min(lf, 15) << 4] + (length_bytes(lf) if lf >= 15 else []) + tail
+    plain += tail
+    return np.array(comp, np.uint8), np.array(plain, np.uint8)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_lz4_decode_large_blocks_of_few_sequences(mode):
+    """Blocks over 6 KiB compressed hold 16-sequence checkpoints; those that
+    compress to more than half their length (long literal runs) also keep one
+    per sequence for their first 128, and are rebuilt one sequence per thread
+    when they have no more.  Blocks of 2 to 300 sequences of both kinds --
+    64 KiB blocks from global memory, a short last block from the LDS stage --
+    after a dense block: both modes equal the oracle's decode and the plain
+    bytes."""
+    rng = np.random.default_rng(70 + mode)
+    dense = canonical_block(rng, 13106, 4, 6)
+    for nseq in (2, 16, 17, 127, 128, 129, 300):
+        lit_heavy = literal_run_block(rng, nseq, 65536, 8)          # S > 32 KiB
+        match_heavy = literal_run_block(rng, nseq, 65536, (65536 - 16) // nseq - max(48, 7000 // nseq + 1))
+        last = literal_run_block(rng, nseq, 13000, 8)               # S in (6 KiB, 14 KiB]: staged
+        assert lit_heavy[0].size > 32768 and 6144 < match_heavy[0].size < 32768, nseq
+        assert 6500 < last[0].size <= 14336 and last[0].size > 6144, nseq
+        blocks = [lit_heavy, dense, match_heavy, last]
+        comps, plains = [x[0] for x in blocks], [x[1] for x in blocks]
+        sizes = np.array([x.size for x in comps], np.uint32)
+        offs = np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(np.uint64)
+        payload = np.concatenate(comps)
+        plain = np.concatenate(plains)
+        dst = rng.integers(0, 256, plain.size, dtype=np.uint8)
+        got, st = gpu_decode(payload, offs, sizes, dst, mode)
+        ref, rst = oracle.lz4_decode_blocks(payload, offs, sizes, dst, mode=mode)
+        assert st == rst == 0, nseq
+        assert np.array_equal(ref, plain if mode == 0 else dst ^ plain), nseq
+        assert np.array_equal(got, ref), nseq
+
+
 def test_lz4_decode_in_two_calls_on_two_streams():
     """parse on one stream, apply on another after an event, several payloads in
     a row on one workspace (canonical, general and corrupt blocks): the same
