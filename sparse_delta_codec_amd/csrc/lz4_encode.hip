@@ -30,8 +30,10 @@
 //     of its own chunk into a 14 KiB LDS window, relative to the block's
 //     start, while wave 0 waits for the predecessors' sizes; the window is
 //     then copied out with 16-byte stores.  Every block of a sparse mask fits
-//     one window; a larger encoding (incompressible bytes) takes several
-//     window passes, each thread emitting only in the passes its bytes reach.
+//     one window; a larger encoding takes several window passes, each thread
+//     emitting only in the passes its bytes reach.  A block with no
+//     qualifying run at all (incompressible bytes) is one literal sequence and
+//     skips the window: its bytes go from the image straight to the payload.
 //
 // The fused sender pass (pulse_cast_diff_lz4) runs the same block encoder on a
 // mask it makes itself: step 1 becomes the FP32 -> BF16 cast of the block's
