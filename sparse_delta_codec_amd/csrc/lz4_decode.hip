@@ -184,22 +184,26 @@ __device__ __forceinline__ void ring_refill(uint8_t *rings, const uint8_t *pay, 
 }
 
 // Byte reader over a block's compressed bytes (block byte x at base + mis + x,
-// base 16-byte aligned, in LDS or global memory) that loads one aligned
-// 16-byte piece at a time and keeps the last one: a length chain or a short
-// literal run costs one load per 16 bytes, not one per byte.  Only pieces
+// base 16-byte aligned, in LDS or global memory) that holds two consecutive
+// aligned 16-byte pieces and loads the next two together when a byte past
+// them is read: a length chain, or the offset, match bytes and next token
+// after a skipped literal run, costs one round trip per 32 bytes.  Only pieces
 // holding a byte of the block are loaded (such a piece never leaves that
 // byte's page).
-struct Win16 {
+struct Win32 {
     const uint8_t *base;
-    uint32_t mis, cur;
-    u32x4 w;
-    __device__ __forceinline__ Win16(const uint8_t *b, uint32_t m) : base(b), mis(m), cur(0xFFFFFFFFu), w{0u, 0u, 0u, 0u} {}
+    uint32_t mis, end, cur;  // end: pieces holding a byte of the block
+    u32x4 w0, w1;
+    __device__ __forceinline__ Win32(const uint8_t *b, uint32_t m, uint32_t S)
+        : base(b), mis(m), end((m + S + 15) >> 4), cur(0xFFFFFFFEu), w0{0u, 0u, 0u, 0u}, w1{0u, 0u, 0u, 0u} {}
     __device__ __forceinline__ uint32_t operator[](uint32_t x) {
         const uint32_t p = mis + x, k = p >> 4;
-        if (k != cur) {
-            w = *reinterpret_cast<const u32x4 *>(base + 16 * (size_t)k);
+        if (k - cur > 1u) {
+            w0 = *reinterpret_cast<const u32x4 *>(base + 16 * (size_t)k);
+            if (k + 1 < end) w1 = *reinterpret_cast<const u32x4 *>(base + 16 * (size_t)k + 16);
             cur = k;
         }
+        const u32x4 w = k == cur ? w0 : w1;
         const uint32_t d = (p >> 2) & 3u;
         const uint32_t word = d == 0 ? w.x : d == 1 ? w.y : d == 2 ? w.z : w.w;
         return (word >> (8 * (p & 3u))) & 0xFFu;
@@ -208,14 +212,21 @@ struct Win16 {
 
 // Lane state of the walk, one word (bit flags in a VGPR keep divergent joins
 // free of per-flag lane-mask bookkeeping).
-constexpr uint32_t F_DONE = 1u, F_BAD = 2u, F_SLOW = 4u, F_STALL = 8u, F_OFF = 16u, F_LIT = 32u, F_LONG = 64u;
+constexpr uint32_t F_DONE = 1u, F_BAD = 2u, F_SLOW = 4u, F_STALL = 8u, F_OFF = 16u, F_LIT = 32u, F_LONG = 64u,
+                   F_DCK = 128u;
+// A literal run longer than this (a length chain of more than eight bytes)
+// ends the ring walk with F_LONG: such runs belong to almost incompressible
+// blocks of few sequences, where each run would cost the ring walk a refill.
+constexpr uint32_t K1_LIT_MAX = 15 + 8 * 255;
+constexpr int32_t K1_NO_RING = -(1 << 30);  // ring start before the first refill
 
 // Reads a length extension (bytes added while they are 255) starting at
 // block position q into n.  r0: ring index of the step's first byte; a chain
 // that leaves a ring refilled at that step cannot be read from the ring at all
-// (F_LONG: the block is walked again by k1_walk_long).
+// (F_LONG: the block is walked again by k1_walk_long), nor can a length above
+// cap (<= len) that is not above len.
 __device__ __forceinline__ uint32_t read_ext(const uint8_t *ring, int32_t rb, uint32_t S, uint32_t len,
-                                             uint32_t r0, uint32_t &q, uint32_t &n) {
+                                             uint32_t cap, uint32_t r0, uint32_t &q, uint32_t &n) {
     while (true) {
         if (q >= S) return F_BAD | F_DONE;
         const uint32_t rq = q - (uint32_t)rb;
@@ -223,7 +234,7 @@ __device__ __forceinline__ uint32_t read_ext(const uint8_t *ring, int32_t rb, ui
         const uint32_t x = ring[rq];
         ++q;
         n += x;
-        if (n > len) return F_BAD | F_DONE;
+        if (n > cap) return n > len ? (F_BAD | F_DONE) : (F_LONG | F_DONE);
         if (x != 255) return 0;
     }
 }
@@ -238,13 +249,13 @@ struct WalkResult {
 // whose bytes lie past the ring stalls the lane until the wave's next refill.
 // The block is handed to K3 (F_SLOW) at the first sequence not in canonical
 // form.  A length chain longer than the ring (a run of one byte over most of a
-// 64 KiB block, or a block that is one literal run) ends the ring walk with
-// F_LONG; such blocks are few and have few sequences, and k1_walk_long walks
-// them again from global memory.
+// 64 KiB block), or a literal run longer than K1_LIT_MAX, ends the ring walk
+// with F_LONG; such blocks are few and have few sequences, and k1_walk_long
+// walks them again from global memory.
 __device__ __forceinline__ WalkResult k1_walk(uint8_t *rings, const uint8_t *ring, bool active, const uint8_t *pay,
                                               int64_t pay_bytes, int64_t boff, uint32_t S, uint32_t len, uint2 *ck,
                                               uint32_t ckl) {
-    int32_t rb = -(1 << 30);  // empty ring: every position maps past it
+    int32_t rb = K1_NO_RING;  // empty ring: every position maps past it
     uint32_t ip = 0, op = 0, tok = 0, nseq = 0;
     const uint32_t ckm = (1u << ckl) - 1u;
     uint32_t f = active ? 0u : F_DONE;
@@ -300,7 +311,7 @@ __device__ __forceinline__ WalkResult k1_walk(uint8_t *rings, const uint8_t *rin
                     } else {
                         tok = ring[r];
                         uint32_t q = ip + 1, ll = tok >> 4, e = 0;
-                        if (ll == 15) e = read_ext(ring, rb, S, len, r, q, ll);
+                        if (ll == 15) e = read_ext(ring, rb, S, len, len < K1_LIT_MAX ? len : K1_LIT_MAX, r, q, ll);
                         if (!e && (ll > S - q || ll > len - op)) e = F_BAD | F_DONE;
                         if (e) {
                             f |= e;
@@ -331,7 +342,7 @@ __device__ __forceinline__ WalkResult k1_walk(uint8_t *rings, const uint8_t *rin
                                 ml += x0;
                                 if (ml > len) e = F_BAD | F_DONE;
                             } else {
-                                e = read_ext(ring, rb, S, len, r, q, ml);
+                                e = read_ext(ring, rb, S, len, len, r, q, ml);
                             }
                         }
                         if (!e) {
@@ -357,17 +368,17 @@ __device__ __forceinline__ WalkResult k1_walk(uint8_t *rings, const uint8_t *rin
 
 
 // The walk of one block straight from global memory, for the lanes whose
-// block has a length chain longer than the ring: the same checks, flags and
-// checkpoints as the ring walk (a sequence that is not canonical: F_SLOW),
-// reading the block's bytes one aligned 16-byte piece at a time.  A block
-// with the first token and the size of a single literal run of its full
-// length is marked F_LIT without reading its chain (K2 checks it).
+// block has a length chain longer than the ring or a literal run longer than
+// K1_LIT_MAX: the same checks, flags and checkpoints as the ring walk (a
+// sequence that is not canonical: F_SLOW), reading the block's bytes 32 at a
+// time.  dck (or null): the block's direct checkpoint slots, filled for its
+// first kCkDirect sequences; a valid block of at most kCkDirect sequences then
+// has them all (F_DCK).
 __device__ __forceinline__ WalkResult k1_walk_long(const uint8_t *pay, int64_t boff, uint32_t S, uint32_t len,
-                                                   uint2 *ck, uint32_t ckl) {
+                                                   uint2 *ck, uint32_t ckl, uint2 *dck) {
     const uint8_t *blk = pay + boff;
     const uint32_t mis = (uint32_t)(reinterpret_cast<uintptr_t>(blk) & 15);
-    Win16 src(blk - mis, mis);
-    if (src[0] == 0xF0u && len >= 15 && S == len + (len - 15) / 255 + 2) return WalkResult{1u, F_LIT | F_DONE};
+    Win32 src(blk - mis, mis, S);
     uint32_t ip = 0, op = 0, nseq = 0;
     const WalkResult bad{0u, F_BAD | F_DONE};
     while (true) {
@@ -384,10 +395,14 @@ __device__ __forceinline__ WalkResult k1_walk_long(const uint8_t *pay, int64_t b
         }
         if (ll > S - q || ll > len - op) return bad;
         if ((nseq & ((1u << ckl) - 1u)) == 0) ck[nseq >> ckl] = make_uint2(ip, op);
+        if (dck && nseq < kCkDirect) dck[nseq] = make_uint2(ip, op);
         ++nseq;
         ip = q + ll;
         op += ll;
-        if (ip == S) return WalkResult{nseq, F_DONE | (op != len ? F_BAD : 0u)};
+        if (ip == S) {
+            if (op != len) return bad;
+            return WalkResult{nseq, F_DONE | (dck && nseq <= kCkDirect ? F_DCK : 0u)};
+        }
         if (ll == 0) return WalkResult{nseq, F_SLOW | F_DONE};  // a match right after a match
         if (S - ip < 2) return bad;
         const uint32_t mo = src[ip] | (src[ip + 1] << 8);
@@ -410,11 +425,12 @@ __device__ __forceinline__ WalkResult k1_walk_long(const uint8_t *pay, int64_t b
 }
 
 // The direct checkpoints of a validated block (see ck_direct): its sequence
-// starts walked again from global memory, one aligned 16-byte piece at a time.
-__device__ __forceinline__ void k1_direct_ck(const uint8_t *pay, int64_t boff, uint32_t nseq, uint2 *dck) {
+// starts walked again from global memory, 32 bytes at a time.
+__device__ __forceinline__ void k1_direct_ck(const uint8_t *pay, int64_t boff, uint32_t S, uint32_t nseq,
+                                             uint2 *dck) {
     const uint8_t *blk = pay + boff;
     const uint32_t mis = (uint32_t)(reinterpret_cast<uintptr_t>(blk) & 15);
-    Win16 src(blk - mis, mis);
+    Win32 src(blk - mis, mis, S);
     uint32_t ip = 0, op = 0;
     for (uint32_t k = 0; k < nseq; ++k) {
         dck[k] = make_uint2(ip, op);
@@ -490,14 +506,20 @@ __global__ __launch_bounds__(64) void k_lz4_parse(Lz4DecArgs a) {
         k1_walk(s_rings, s_rings + lane * K1_STRIDE, !bad, a.payload, a.payload_bytes, (int64_t)off, (uint32_t)S, len, ck,
                 ck_log((uint32_t)S));
     if (__ballot((w.flags & F_LONG) != 0)) {
-        if (w.flags & F_LONG) w = k1_walk_long(a.payload, (int64_t)off, (uint32_t)S, len, ck, ck_log((uint32_t)S));
+        if (w.flags & F_LONG) {
+            const bool dsz = ck_direct((uint32_t)S, len, 0);  // the size test of ck_direct
+            w = k1_walk_long(a.payload, (int64_t)off, (uint32_t)S, len, ck, ck_log((uint32_t)S),
+                             dsz ? ck + ck_direct_slot((uint32_t)S) : nullptr);
+        }
     }
     // a valid block of one sequence is one literal run: K2 copies it as such
     if (w.nseq == 1 && !(w.flags & (F_BAD | F_SLOW))) w.flags |= F_LIT;
     // a large, literal-heavy block of few sequences: one checkpoint per sequence
-    const bool direct = !bad && !(w.flags & (F_BAD | F_SLOW | F_LIT)) && ck_direct((uint32_t)S, len, w.nseq);
+    // (written here unless the walk from global memory wrote them)
+    const bool direct =
+        !bad && !(w.flags & (F_BAD | F_SLOW | F_LIT | F_DCK)) && ck_direct((uint32_t)S, len, w.nseq);
     if (__ballot(direct)) {
-        if (direct) k1_direct_ck(a.payload, (int64_t)off, w.nseq, ck + ck_direct_slot((uint32_t)S));
+        if (direct) k1_direct_ck(a.payload, (int64_t)off, (uint32_t)S, w.nseq, ck + ck_direct_slot((uint32_t)S));
     }
     const uint32_t nseq = w.nseq;
     const bool slow = (w.flags & F_SLOW) != 0;

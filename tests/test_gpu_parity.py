@@ -771,6 +771,63 @@ def test_lz4_decode_large_blocks_of_few_sequences(mode):
         assert np.array_equal(got, ref), nseq
 
 
+def sequence_block(rng, seqs, total):
+    """A canonical block of the sequences (literal count, match length) given,
+    each with non-zero literals and an offset-1 match, then a final literal
+    run that brings the plain bytes to `total`: its bytes and plain bytes."""
+    comp, plain = [], []
+    for ll, ml in seqs:
+        lits = [int(x) for x in rng.integers(1, 256, ll)]
+        comp += [(min(ll, 15) << 4) | min(ml - 4, 15)] + (length_bytes(ll) if ll >= 15 else []) + lits + [1, 0]
+        comp += length_bytes(ml - 4) if ml - 4 >= 15 else []
+        plain += lits + [lits[-1]] * ml
+    lf = total - len(plain)
+    assert lf >= 5
+    tail = [int(x) for x in rng.integers(1, 256, lf)]
+    comp += [min(lf, 15) << 4] + (length_bytes(lf) if lf >= 15 else []) + tail
+    plain += tail
+    return np.array(comp, np.uint8), np.array(plain, np.uint8)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_lz4_decode_literal_runs_past_the_ring_walk(mode):
+    """The parse hands a block with a literal run longer than 2055 bytes (a
+    length chain of nine bytes or more) to its walk from global memory, which
+    also writes the per-sequence checkpoints of a large literal-heavy block.
+    Runs of 2055 to 3000 bytes, first, in the middle and last; blocks of more
+    and of fewer than 128 sequences, over and under 32 KiB compressed; a short
+    last block from the LDS stage, one with fewer than 6 KiB compressed: both
+    modes equal the oracle's decode and the plain bytes."""
+    rng = np.random.default_rng(95 + mode)
+    B = 65536
+    blocks = [
+        sequence_block(rng, [(2056, 4)] + [(200, 4)] * 150, B),           # 152 sequences, S > 64 KiB
+        sequence_block(rng, [(1, 4)] * 100 + [(2100, 4)] + [(1, 300)] * 100, B),
+        sequence_block(rng, [(2055, 4)] + [(1, 500)] * 100, B),          # the ring walk keeps it
+        sequence_block(rng, [(1, 4)] * 3 + [(2240 + 7 * k, 4) for k in range(12)], B),
+        sequence_block(rng, [(3000, 8)] * 10, B),                         # 11 sequences, S > 32 KiB
+        sequence_block(rng, [(1, 8)] * 40 + [(2056, 4)] + [(1, 1000)] * 60, B),  # S < 6 KiB, a long last run
+        canonical_block(rng, 13106, 4, 6),
+    ]
+    assert blocks[0][0].size > B and blocks[4][0].size > 32768 and blocks[5][0].size < 6144
+    for last in ([(2500, 8)] * 4, [(2200, 4)] + [(1, 4)] * 50):
+        tot = sum(a * 1 + b for a, b in last) + 6
+        blk = sequence_block(rng, last, tot)
+        comps = [x[0] for x in blocks] + [blk[0]]
+        plains = [x[1] for x in blocks] + [blk[1]]
+        assert all(p.size == B for p in plains[:-1])
+        sizes = np.array([x.size for x in comps], np.uint32)
+        offs = np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(np.uint64)
+        payload = np.concatenate(comps)
+        plain = np.concatenate(plains)
+        dst = rng.integers(0, 256, plain.size, dtype=np.uint8)
+        got, st = gpu_decode(payload, offs, sizes, dst, mode)
+        ref, rst = oracle.lz4_decode_blocks(payload, offs, sizes, dst, mode=mode)
+        assert st == rst == 0, last[0]
+        assert np.array_equal(ref, plain if mode == 0 else dst ^ plain), last[0]
+        assert np.array_equal(got, ref), last[0]
+
+
 def test_lz4_decode_in_two_calls_on_two_streams():
     """parse on one stream, apply on another after an event, several payloads in
     a row on one workspace (canonical, general and corrupt blocks): the same
