@@ -193,22 +193,59 @@ __device__ __forceinline__ void ring_refill(uint8_t *rings, const uint8_t *pay, 
 struct Win32 {
     const uint8_t *base;
     uint32_t mis, end, cur;  // end: pieces holding a byte of the block
-    u32x4 w0, w1;
+    uint64_t q0, q1, q2, q3; // block bytes from piece cur on, eight per word
     __device__ __forceinline__ Win32(const uint8_t *b, uint32_t m, uint32_t S)
-        : base(b), mis(m), end((m + S + 15) >> 4), cur(0xFFFFFFFEu), w0{0u, 0u, 0u, 0u}, w1{0u, 0u, 0u, 0u} {}
-    __device__ __forceinline__ uint32_t operator[](uint32_t x) {
+        : base(b), mis(m), end((m + S + 15) >> 4), cur(0xFFFFFFFEu), q0(0), q1(0), q2(0), q3(0) {}
+    // position of block byte x in the window, loading the window if needed
+    __device__ __forceinline__ uint32_t at(uint32_t x) {
         const uint32_t p = mis + x, k = p >> 4;
         if (k - cur > 1u) {
-            w0 = *reinterpret_cast<const u32x4 *>(base + 16 * (size_t)k);
-            if (k + 1 < end) w1 = *reinterpret_cast<const u32x4 *>(base + 16 * (size_t)k + 16);
+            const u32x4 a = *reinterpret_cast<const u32x4 *>(base + 16 * (size_t)k);
+            u32x4 b = {0u, 0u, 0u, 0u};  // (not read when the block ends in piece k)
+            if (k + 1 < end) b = *reinterpret_cast<const u32x4 *>(base + 16 * (size_t)k + 16);
+            q0 = ((uint64_t)a.y << 32) | a.x;
+            q1 = ((uint64_t)a.w << 32) | a.z;
+            q2 = ((uint64_t)b.y << 32) | b.x;
+            q3 = ((uint64_t)b.w << 32) | b.z;
             cur = k;
         }
-        const u32x4 w = k == cur ? w0 : w1;
-        const uint32_t d = (p >> 2) & 3u;
-        const uint32_t word = d == 0 ? w.x : d == 1 ? w.y : d == 2 ? w.z : w.w;
-        return (word >> (8 * (p & 3u))) & 0xFFu;
+        return p - 16 * cur;
+    }
+    // the eight bytes of the window word holding window byte o (branch-free)
+    __device__ __forceinline__ uint64_t word(uint32_t o) const {
+        const uint64_t lo = (o & 16u) ? q2 : q0, hi = (o & 16u) ? q3 : q1;
+        return (o & 8u) ? hi : lo;
+    }
+    __device__ __forceinline__ uint32_t operator[](uint32_t x) {
+        const uint32_t o = at(x);
+        return (uint32_t)(word(o) >> (8 * (o & 7u))) & 0xFFu;
+    }
+    // block bytes x .. x + 7 are all 255 and start a window word (x + 8 <= S)
+    __device__ __forceinline__ bool ff8(uint32_t x) {
+        if ((mis + x) & 7u) return false;
+        return word(at(x)) == ~0ull;
     }
 };
+
+// Adds to n the length bytes starting at block byte q (bytes added while they
+// are 255, eight at a time where they fill a window word); q moves past them.
+// False when they run past the block (S bytes) or n passes len.
+__device__ __forceinline__ bool win_chain(Win32 &src, uint32_t S, uint32_t len, uint32_t &q, uint32_t &n) {
+    uint32_t x;
+    do {
+        if (q >= S) return false;
+        if (S - q >= 8 && src.ff8(q)) {
+            n += 8 * 255;
+            q += 8;
+            x = 255;
+        } else {
+            x = src[q++];
+            n += x;
+        }
+        if (n > len) return false;
+    } while (x == 255);
+    return true;
+}
 
 // Lane state of the walk, one word (bit flags in a VGPR keep divergent joins
 // free of per-flag lane-mask bookkeeping).
@@ -384,15 +421,8 @@ __device__ __forceinline__ WalkResult k1_walk_long(const uint8_t *pay, int64_t b
     while (true) {
         if (ip >= S) return bad;
         const uint32_t tok = src[ip];
-        uint32_t q = ip + 1, ll = tok >> 4, x;
-        if (ll == 15) {
-            do {
-                if (q >= S) return bad;
-                x = src[q++];
-                ll += x;
-                if (ll > len) return bad;
-            } while (x == 255);
-        }
+        uint32_t q = ip + 1, ll = tok >> 4;
+        if (ll == 15 && !win_chain(src, S, len, q, ll)) return bad;
         if (ll > S - q || ll > len - op) return bad;
         if ((nseq & ((1u << ckl) - 1u)) == 0) ck[nseq >> ckl] = make_uint2(ip, op);
         if (dck && nseq < kCkDirect) dck[nseq] = make_uint2(ip, op);
@@ -410,14 +440,7 @@ __device__ __forceinline__ WalkResult k1_walk_long(const uint8_t *pay, int64_t b
         if (mo != 1) return WalkResult{nseq, F_SLOW | F_DONE};
         q = ip + 2;
         uint32_t ml = (tok & 15) + 4;
-        if ((tok & 15) == 15) {
-            do {
-                if (q >= S) return bad;
-                x = src[q++];
-                ml += x;
-                if (ml > len) return bad;
-            } while (x == 255);
-        }
+        if ((tok & 15) == 15 && !win_chain(src, S, len, q, ml)) return bad;
         if (ml > len - op) return bad;
         op += ml;
         ip = q;
@@ -435,24 +458,14 @@ __device__ __forceinline__ void k1_direct_ck(const uint8_t *pay, int64_t boff, u
     for (uint32_t k = 0; k < nseq; ++k) {
         dck[k] = make_uint2(ip, op);
         const uint32_t tok = src[ip];
-        uint32_t q = ip + 1, ll = tok >> 4, x;
-        if (ll == 15) {
-            do {
-                x = src[q++];
-                ll += x;
-            } while (x == 255);
-        }
+        uint32_t q = ip + 1, ll = tok >> 4;
+        if (ll == 15) win_chain(src, S, ~0u, q, ll);  // (validated: it ends inside the block)
         q += ll;
         op += ll;
         if (k + 1 == nseq) break;  // the final sequence has no match
         q += 2;
         uint32_t ml = (tok & 15) + 4;
-        if ((tok & 15) == 15) {
-            do {
-                x = src[q++];
-                ml += x;
-            } while (x == 255);
-        }
+        if ((tok & 15) == 15) win_chain(src, S, ~0u, q, ml);
         op += ml;
         ip = q;
     }
