@@ -761,6 +761,77 @@ __device__ __forceinline__ void k2_deferred(const uint8_t *src, uint8_t *img, co
     }
 }
 
+// byte r (0 .. 31) of the 32 bytes A (low) then B, branch-free
+__device__ __forceinline__ uint32_t byte32(const u32x4 &A, const u32x4 &B, uint32_t r) {
+    const uint64_t a0 = ((uint64_t)A.y << 32) | A.x, a1 = ((uint64_t)A.w << 32) | A.z;
+    const uint64_t b0 = ((uint64_t)B.y << 32) | B.x, b1 = ((uint64_t)B.w << 32) | B.z;
+    const uint64_t lo = (r & 16u) ? b0 : a0, hi = (r & 16u) ? b1 : a1;
+    return (uint32_t)(((r & 8u) ? hi : lo) >> (8 * (r & 7u))) & 0xFFu;
+}
+
+// The queued runs of a block read from global memory (block byte 0 at src),
+// one wave per run, as k2_deferred does from the LDS stage, but with every
+// load of a lane's pieces issued before any is used: for each of its image
+// pieces a lane loads the one or two aligned 16-byte pieces holding the
+// source of the piece's bytes in the run (a lane past the run reloads the
+// run's first), so a round of four pieces per lane costs one memory round
+// trip.  Whole pieces are shifted into place (the shift is the same for all of
+// a run's pieces) and stored with 16-byte writes; a run's two end pieces,
+// shared with its neighbours, are written byte by byte from the registers.
+__device__ __forceinline__ void k2_deferred_global(const uint8_t *src, uint8_t *img, const K2Queue &qu) {
+    constexpr int NWV = K2_THREADS / kWave, U = 4;
+    const uint32_t nq = qu.count < (uint32_t)K2_QCAP ? qu.count : (uint32_t)K2_QCAP;
+    const uint32_t ln = threadIdx.x & (kWave - 1);
+    for (uint32_t e = threadIdx.x / kWave; e < nq; e += NWV) {
+        // the run, the same in every lane of the wave
+        const uint32_t o = (uint32_t)__builtin_amdgcn_readfirstlane((int)qu.op[e]);
+        const uint32_t n = (uint32_t)__builtin_amdgcn_readfirstlane((int)qu.n[e]);
+        const uint32_t sv = (uint32_t)__builtin_amdgcn_readfirstlane((int)qu.src[e]);
+        const uint32_t p0 = o >> 4, p1 = (o + n - 1) >> 4;  // image pieces the run touches
+        if (sv & K2_FILL) {
+            const uint32_t fb = (sv & 0xFFu) * 0x01010101u;
+            for (uint32_t pp = p0 + ln; pp <= p1; pp += kWave) {
+                if (16 * pp >= o && 16 * pp + 16 <= o + n) {
+                    *reinterpret_cast<u32x4 *>(img + 16 * pp) = u32x4{fb, fb, fb, fb};
+                } else {
+                    const uint32_t lo = 16 * pp > o ? 16 * pp : o, hi = 16 * pp + 16 < o + n ? 16 * pp + 16 : o + n;
+                    for (uint32_t x = lo; x < hi; ++x) img[x] = (uint8_t)sv;
+                }
+            }
+            continue;
+        }
+        const uint8_t *g = src + sv;  // source of image byte o
+        const uint8_t *glast = g + (n - 1);
+        const uint32_t gm = (uint32_t)((reinterpret_cast<uintptr_t>(g) - o) & 15u);  // shift of every whole piece
+        for (uint32_t p = p0 + ln; p <= p1; p += U * kWave) {
+            u32x4 A[U], B[U];
+            const uint8_t *base[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t pp = p + (uint32_t)(u * kWave);
+                const uint32_t lo = pp <= p1 && 16 * pp > o ? 16 * pp : o;
+                const uint8_t *s0 = g + (lo - o);
+                base[u] = s0 - (reinterpret_cast<uintptr_t>(s0) & 15u);
+                const uint8_t *bb = base[u] + 16 <= glast ? base[u] + 16 : base[u];
+                A[u] = *reinterpret_cast<const u32x4 *>(base[u]);
+                B[u] = *reinterpret_cast<const u32x4 *>(bb);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const uint32_t pp = p + (uint32_t)(u * kWave);
+                if (pp > p1) continue;
+                if (16 * pp >= o && 16 * pp + 16 <= o + n) {
+                    *reinterpret_cast<u32x4 *>(img + 16 * pp) = gm ? take16(A[u], B[u], (int)gm) : A[u];
+                } else {
+                    const uint32_t lo = 16 * pp > o ? 16 * pp : o, hi = 16 * pp + 16 < o + n ? 16 * pp + 16 : o + n;
+                    for (uint32_t x = lo; x < hi; ++x)
+                        img[x] = (uint8_t)byte32(A[u], B[u], (uint32_t)((g + (x - o)) - base[u]));
+                }
+            }
+        }
+    }
+}
+
 // One block of K2.  STAGED: the compressed bytes fit the LDS stage (else they
 // are read from global memory); the two variants share no code path, so the
 // waits of the staged one never count the other's byte loads.
@@ -835,7 +906,7 @@ __device__ __forceinline__ void k2_block(const Lz4DecArgs &a, int64_t b, uint32_
     } else {
         k2_segments<false>(in - mis, mis, S, nseq, ckl, ck, c0, s_img, s_q);
         lds_barrier();
-        k2_deferred(in, s_img, s_q);
+        k2_deferred_global(in, s_img, s_q);
     }
     lds_barrier();
 
