@@ -963,17 +963,33 @@ __device__ __forceinline__ void k2_literal_block(const Lz4DecArgs &a, int64_t b,
         return;
     }
     const uint8_t *src = in + h;
-    const uint32_t mis = (uint32_t)(reinterpret_cast<uintptr_t>(src) & 15);
+    const uint32_t mis = (uint32_t)__builtin_amdgcn_readfirstlane((int)(reinterpret_cast<uintptr_t>(src) & 15));
     const u32x4 *s4 = reinterpret_cast<const u32x4 *>(src - mis);
     u32x4 *d4 = reinterpret_cast<u32x4 *>(a.dst + b * (int64_t)a.block_bytes);
     const uint32_t nfull = len >> 4;
-    for (uint32_t c = t; c < nfull; c += K2_THREADS) {
-        // (the second piece holds the last bytes of dst piece c: it starts
-        // inside the block's data, so it never leaves the data's page)
-        u32x4 v = s4[c];
-        if (mis) v = take16(v, s4[c + 1], (int)mis);
-        if constexpr (XOR) v ^= __builtin_nontemporal_load(d4 + c);
-        __builtin_nontemporal_store(v, d4 + c);
+    // four dst pieces per thread and round, every load of a round issued
+    // before any is used (a piece past the block reloads the round's first)
+    constexpr int U = 4;
+    for (uint32_t c0 = t; c0 < nfull; c0 += U * K2_THREADS) {
+        u32x4 A[U], B[U], D[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t c = c0 + (uint32_t)(u * K2_THREADS), cc = c < nfull ? c : c0;
+            // (the second piece holds the last bytes of dst piece cc when
+            // mis > 0: it starts inside the block's data, so it never leaves
+            // the data's page)
+            A[u] = s4[cc];
+            B[u] = s4[mis ? cc + 1 : cc];
+            if constexpr (XOR) D[u] = __builtin_nontemporal_load(d4 + cc);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t c = c0 + (uint32_t)(u * K2_THREADS);
+            if (c >= nfull) break;
+            u32x4 v = mis ? take16(A[u], B[u], (int)mis) : A[u];
+            if constexpr (XOR) v ^= D[u];
+            __builtin_nontemporal_store(v, d4 + c);
+        }
     }
     if (t == 0) {  // ragged tail of the last block
         uint8_t *d = reinterpret_cast<uint8_t *>(d4 + nfull);
