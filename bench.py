@@ -50,6 +50,8 @@ SCHEDULES = {
     "ahead": "parse of chunk c on a second stream beside the encode of chunk c + 1; the receiver's pass and "
              "the decode apply of chunk c on the main stream after it",
     "side": "parse on a second stream beside the receiver's pass of the same chunk, apply on the main stream",
+    "behind": "main stream: receiver's pass of chunk c, encode of chunk c + 1, decode apply of chunk c; the parse "
+              "of chunk c + 1 on a second stream beside that decode apply",
     "pipeline": "encode and parse of chunk c on a second stream while the main stream receives and decodes "
                 "chunk c - 1",
     "serial": "one lz4_decode_blocks call per chunk, main stream",
@@ -77,9 +79,11 @@ def parse():
     p.add_argument("--receiver", choices=["fused", "separate"], default="fused",
                    help="fused: pulse_apply_quant (patch apply + FP8 quantisation in one read of the view); "
                         "separate: pulse_apply_patch, then fp8_block_quant_groups")
-    p.add_argument("--schedule", choices=["ahead", "side", "pipeline", "serial"], default="side",
+    p.add_argument("--schedule", choices=["ahead", "side", "behind", "pipeline", "serial"], default="side",
                    help="ahead: the decode parse of chunk c on a second stream beside the encode of chunk c + 1; "
                         "side: beside the receiver's pass of chunk c; "
+                        "behind: beside the decode apply of chunk c - 1, which the main stream runs after the "
+                        "encode of chunk c; "
                         "pipeline: encode and parse of chunk c on the second stream while the main stream "
                         "receives chunk c - 1; serial: one lz4_decode_blocks call per chunk, one stream")
     p.add_argument("--cpu-sample-frac", type=float, default=1.0,
@@ -358,7 +362,7 @@ def main():
     # buffer sets: what a chunk's sender output and parse live in until the
     # receiver is done with them (two when a chunk's encode overlaps another's)
     bufs = [(idx, val, payload, csizes, coffs, ws_de, tiles)]
-    if sched in ("ahead", "pipeline"):
+    if sched in ("ahead", "behind", "pipeline"):
         bufs.append((torch.empty_like(idx), torch.empty_like(val), torch.empty_like(payload),
                      torch.empty_like(csizes), torch.empty_like(coffs),
                      pulse.workspace(pulse.PULSE_OP_LZ4_DECODE, nbmax, pcap, dev), torch.zeros_like(tiles)))
@@ -464,6 +468,28 @@ def main():
                 receive(record, ci, bufs[0])
                 main_stream.wait_event(parsed)
                 decode_apply(record, ci, bufs[0])
+        elif sched == "behind":
+            # the main stream runs receive(c), encode(c + 1), decode_apply(c):
+            # the parse of chunk c + 1 (after its encode) runs beside the
+            # decode apply of chunk c, whose kernel leaves most of each CU's
+            # LDS and registers free, and no longer beside a receiver's pass.
+            # Buffer sets alternate: chunk c + 1's encode writes the set that
+            # chunk c - 1's decode apply (earlier on the main stream) used.
+            encode(record, 0, bufs[0])
+            side_stream.wait_stream(main_stream)
+            parsed = parse_chunk(record, 0, bufs[0])
+            for ci in range(N):
+                B = bufs[ci % 2]
+                receive(record, ci, B)
+                nxt = None
+                if ci + 1 < N:
+                    Bn = bufs[(ci + 1) % 2]
+                    encode(record, ci + 1, Bn)
+                    side_stream.wait_stream(main_stream)
+                    nxt = parse_chunk(record, ci + 1, Bn)
+                main_stream.wait_event(parsed)
+                decode_apply(record, ci, B)
+                parsed = nxt
         elif sched == "ahead":
             # the parse of chunk c starts with the encode of chunk c + 1 (the
             # event before that encode also follows chunk c - 1's decode, the

@@ -256,6 +256,11 @@ constexpr uint32_t F_DONE = 1u, F_BAD = 2u, F_SLOW = 4u, F_STALL = 8u, F_OFF = 1
 // blocks of few sequences, where each run would cost the ring walk a refill.
 constexpr uint32_t K1_LIT_MAX = 15 + 8 * 255;
 constexpr int32_t K1_NO_RING = -(1 << 30);  // ring start before the first refill
+// Sequences the walk's fast step takes per iteration, and the last ring offset
+// at which a later one of them may start (its 20-byte window then ends inside
+// the ring and its lookahead).
+constexpr int K1_SEQ = 4;
+constexpr int K1_SEQ_MAX = K1_RING + K1_LOOK - 20;
 
 // Reads a length extension (bytes added while they are 255) starting at
 // block position q into n.  r0: ring index of the step's first byte; a chain
@@ -274,6 +279,24 @@ __device__ __forceinline__ uint32_t read_ext(const uint8_t *ring, int32_t rb, ui
         if (n > cap) return n > len ? (F_BAD | F_DONE) : (F_LONG | F_DONE);
         if (x != 255) return 0;
     }
+}
+
+// One canonical sequence from the 16-byte window w0..w3 (little endian):
+// 1 to 12 literals, offset 1, at most one match-length byte, at most `room`
+// compressed bytes and `out` decoded bytes.  True with its compressed size,
+// literal and match lengths when the window holds such a sequence.
+__device__ __forceinline__ bool k1_fast_seq(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, uint32_t room,
+                                            uint32_t out, uint32_t &seq_in, uint32_t &ll, uint32_t &ml) {
+    const uint64_t lo = ((uint64_t)w1 << 32) | w0, hi = ((uint64_t)w3 << 32) | w2;
+    ll = (w0 >> 4) & 15u;
+    const uint32_t mc = w0 & 15u;
+    const uint32_t lc = ll <= 12 ? ll : 12u;
+    const uint32_t mo = win_byte(lo, hi, lc + 1) | (win_byte(lo, hi, lc + 2) << 8);
+    const uint32_t x = win_byte(lo, hi, lc + 3);
+    const uint32_t ext = mc == 15 ? 1u : 0u;
+    seq_in = 3 + ll + ext;
+    ml = mc + 4 + (ext ? x : 0u);
+    return (ll - 1u < 12u) & (mo == 1) & ((mc != 15) | (x != 255)) & (seq_in <= room) & (ll + ml <= out);
 }
 
 struct WalkResult {
@@ -301,44 +324,48 @@ __device__ __forceinline__ WalkResult k1_walk(uint8_t *rings, const uint8_t *rin
         while (true) {
             const bool run = !(f & (F_DONE | F_STALL));
             if (!__ballot(run)) break;
-            if (run) {
-                bool took = false;
-                if (!(f & F_OFF)) {
-                    // fast step: a whole canonical sequence (1 to 12 literals,
-                    // offset 1, at most one match-length byte, inside the
-                    // block and the output) from one 16-byte window of the
-                    // ring and its lookahead; everything the general step
-                    // would check holds.  A lane past the ring stalls here.
-                    const uint32_t r = ip - (uint32_t)rb;
-                    if (ip < S && r >= (uint32_t)K1_RING) {
-                        f |= F_STALL;
-                    } else if (ip < S) {
-                        const uint32_t *d = reinterpret_cast<const uint32_t *>(ring + (r & ~3u));
-                        const uint32_t d0 = d[0], d1 = d[1], d2 = d[2], d3 = d[3], d4 = d[4];
-                        const uint32_t sh = r & 3u;
-                        const uint32_t w0 = __builtin_amdgcn_alignbyte(d1, d0, sh);
-                        const uint32_t w1 = __builtin_amdgcn_alignbyte(d2, d1, sh);
-                        const uint32_t w2 = __builtin_amdgcn_alignbyte(d3, d2, sh);
-                        const uint32_t w3 = __builtin_amdgcn_alignbyte(d4, d3, sh);
-                        const uint64_t lo = ((uint64_t)w1 << 32) | w0, hi = ((uint64_t)w3 << 32) | w2;
-                        const uint32_t ll = (w0 >> 4) & 15u, mc = w0 & 15u;
-                        const uint32_t lc = ll <= 12 ? ll : 12u;
-                        const uint32_t mo = win_byte(lo, hi, lc + 1) | (win_byte(lo, hi, lc + 2) << 8);
-                        const uint32_t x = win_byte(lo, hi, lc + 3);
-                        const uint32_t ext = mc == 15 ? 1u : 0u;
-                        const uint32_t seq_in = 3 + ll + ext, ml = mc + 4 + (ext ? x : 0u);
-                        const uint32_t fast = (uint32_t)(ll - 1u < 12u) & (uint32_t)(mo == 1) &
-                                              (uint32_t)((mc != 15) | (x != 255)) & (uint32_t)(seq_in <= S - ip) &
-                                              (uint32_t)(ll + ml <= len - op);
-                        if (fast) {
-                            if ((nseq & ckm) == 0) ck[nseq >> ckl] = make_uint2(ip, op);
-                            ++nseq;
-                            ip += seq_in;
-                            op += ll + ml;
-                            took = true;
-                        }
-                    }
+            // fast step, without branches: up to K1_SEQ whole canonical
+            // sequences (each 1 to 12 literals, offset 1, at most one
+            // match-length byte, inside the block and the output), each read
+            // from a 20-byte window of the ring and its lookahead; everything
+            // the general step would check holds.  The first starts in the
+            // ring (a lane past the ring stalls here), each later one at most
+            // K1_SEQ_MAX bytes into it, so every window ends inside the ring
+            // and its lookahead.  A lane that cannot take one (or is not
+            // running) reads the ring's first bytes and takes none.
+            bool took;
+            {
+                const uint32_t r = ip - (uint32_t)rb;
+                const bool tryf = run && !(f & F_OFF) && ip < S;
+                const bool st = tryf && r >= (uint32_t)K1_RING;
+                f |= st ? F_STALL : 0u;
+                bool go = tryf && !st;
+                uint32_t rj = go ? r : 0u;
+                took = false;
+#pragma unroll
+                for (int j = 0; j < K1_SEQ; ++j) {
+                    const uint32_t *d = reinterpret_cast<const uint32_t *>(ring + (rj & ~3u));
+                    const uint32_t d0 = d[0], d1 = d[1], d2 = d[2], d3 = d[3], d4 = d[4];
+                    const uint32_t sh = rj & 3u;
+                    uint32_t seq_in, ll, ml;
+                    const bool fj = k1_fast_seq(__builtin_amdgcn_alignbyte(d1, d0, sh),
+                                                __builtin_amdgcn_alignbyte(d2, d1, sh),
+                                                __builtin_amdgcn_alignbyte(d3, d2, sh),
+                                                __builtin_amdgcn_alignbyte(d4, d3, sh), S - ip, len - op, seq_in,
+                                                ll, ml) &&
+                                    go;
+                    if (fj && (nseq & ckm) == 0) ck[nseq >> ckl] = make_uint2(ip, op);
+                    nseq += fj ? 1u : 0u;
+                    ip += fj ? seq_in : 0u;
+                    op += fj ? ll + ml : 0u;
+                    if (j == 0) took = fj;
+                    // the next window (seq_in <= 16 when fj holds)
+                    const uint32_t rn = rj + (seq_in <= 16u ? seq_in : 16u);
+                    go = fj && rn <= (uint32_t)K1_SEQ_MAX;
+                    rj = go ? rn : 0u;
                 }
+            }
+            if (run) {
                 if (!took && !(f & (F_OFF | F_STALL))) {
                     const uint32_t r = ip - (uint32_t)rb;
                     if (ip >= S) {
