@@ -281,21 +281,23 @@ __device__ __forceinline__ uint32_t read_ext(const uint8_t *ring, int32_t rb, ui
     }
 }
 
-// One canonical sequence from the 16-byte window w0..w3 (little endian):
-// 1 to 12 literals, offset 1, at most one match-length byte, at most `room`
-// compressed bytes and `out` decoded bytes.  True with its compressed size,
-// literal and match lengths when the window holds such a sequence.
-__device__ __forceinline__ bool k1_fast_seq(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, uint32_t room,
-                                            uint32_t out, uint32_t &seq_in, uint32_t &ll, uint32_t &ml) {
-    const uint64_t lo = ((uint64_t)w1 << 32) | w0, hi = ((uint64_t)w3 << 32) | w2;
-    ll = (w0 >> 4) & 15u;
-    const uint32_t mc = w0 & 15u;
-    const uint32_t lc = ll <= 12 ? ll : 12u;
-    const uint32_t mo = win_byte(lo, hi, lc + 1) | (win_byte(lo, hi, lc + 2) << 8);
-    const uint32_t x = win_byte(lo, hi, lc + 3);
-    const uint32_t ext = mc == 15 ? 1u : 0u;
-    seq_in = 3 + ll + ext;
-    ml = mc + 4 + (ext ? x : 0u);
+// The checks of one canonical sequence whose token (literal length ll, match
+// code mc, compressed size seq_in) starts the 16-byte window w0..w3 (little
+// endian): 1 to 12 literals, offset 1, at most one match-length byte, at most
+// `room` compressed bytes and `out` decoded bytes.  True, with the match
+// length, when the window holds such a sequence.
+__device__ __forceinline__ bool k1_fast_check(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, uint32_t ll,
+                                              uint32_t mc, uint32_t seq_in, uint32_t room, uint32_t out,
+                                              uint32_t &ml) {
+    // the offset and the first match-length byte: window bytes lc + 1 .. lc + 3
+    // (lc <= 12), taken by one byte-align from the dword pair holding them
+    const uint32_t p = (ll <= 12 ? ll : 12u) + 1u, k = p >> 2;
+    const uint32_t a0 = (k & 1u) ? w1 : w0, a1 = (k & 1u) ? w3 : w2;
+    const uint32_t b0 = (k & 1u) ? w2 : w1;
+    const uint32_t lo = (k & 2u) ? a1 : a0, hi = (k & 2u) ? w3 : b0;
+    const uint32_t v = __builtin_amdgcn_alignbyte(hi, lo, p & 3u);
+    const uint32_t mo = v & 0xFFFFu, x = (v >> 16) & 0xFFu;
+    ml = mc + 4 + (mc == 15 ? x : 0u);
     return (ll - 1u < 12u) & (mo == 1) & ((mc != 15) | (x != 255)) & (seq_in <= room) & (ll + ml <= out);
 }
 
@@ -342,27 +344,34 @@ __device__ __forceinline__ WalkResult k1_walk(uint8_t *rings, const uint8_t *rin
                 bool go = tryf && !st;
                 uint32_t rj = go ? r : 0u;
                 took = false;
+                const uint32_t *d = reinterpret_cast<const uint32_t *>(ring + (rj & ~3u));
+                uint32_t d0 = d[0], d1 = d[1], d2 = d[2], d3 = d[3], d4 = d[4];
 #pragma unroll
                 for (int j = 0; j < K1_SEQ; ++j) {
-                    const uint32_t *d = reinterpret_cast<const uint32_t *>(ring + (rj & ~3u));
-                    const uint32_t d0 = d[0], d1 = d[1], d2 = d[2], d3 = d[3], d4 = d[4];
                     const uint32_t sh = rj & 3u;
-                    uint32_t seq_in, ll, ml;
-                    const bool fj = k1_fast_seq(__builtin_amdgcn_alignbyte(d1, d0, sh),
-                                                __builtin_amdgcn_alignbyte(d2, d1, sh),
-                                                __builtin_amdgcn_alignbyte(d3, d2, sh),
-                                                __builtin_amdgcn_alignbyte(d4, d3, sh), S - ip, len - op, seq_in,
-                                                ll, ml) &&
-                                    go;
+                    const uint32_t w0 = __builtin_amdgcn_alignbyte(d1, d0, sh),
+                                   w1 = __builtin_amdgcn_alignbyte(d2, d1, sh),
+                                   w2 = __builtin_amdgcn_alignbyte(d3, d2, sh),
+                                   w3 = __builtin_amdgcn_alignbyte(d4, d3, sh);
+                    // the next sequence's position depends on the token alone:
+                    // its window is read before this sequence is checked
+                    const uint32_t ll = (w0 >> 4) & 15u, mc = w0 & 15u;
+                    const uint32_t seq_in = 3u + ll + (mc == 15u ? 1u : 0u);
+                    const uint32_t rn = rj + (seq_in <= 16u ? seq_in : 16u);
+                    const uint32_t rjn = rn <= (uint32_t)K1_SEQ_MAX ? rn : 0u;
+                    if (j + 1 < K1_SEQ) {
+                        const uint32_t *dn = reinterpret_cast<const uint32_t *>(ring + (rjn & ~3u));
+                        d0 = dn[0], d1 = dn[1], d2 = dn[2], d3 = dn[3], d4 = dn[4];
+                    }
+                    uint32_t ml;
+                    const bool fj = k1_fast_check(w0, w1, w2, w3, ll, mc, seq_in, S - ip, len - op, ml) && go;
                     if (fj && (nseq & ckm) == 0) ck[nseq >> ckl] = make_uint2(ip, op);
                     nseq += fj ? 1u : 0u;
                     ip += fj ? seq_in : 0u;
                     op += fj ? ll + ml : 0u;
                     if (j == 0) took = fj;
-                    // the next window (seq_in <= 16 when fj holds)
-                    const uint32_t rn = rj + (seq_in <= 16u ? seq_in : 16u);
                     go = fj && rn <= (uint32_t)K1_SEQ_MAX;
-                    rj = go ? rn : 0u;
+                    rj = rjn;
                 }
             }
             if (run) {
