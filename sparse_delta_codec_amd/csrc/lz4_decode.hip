@@ -364,8 +364,9 @@ __device__ __forceinline__ WalkResult k1_walk(uint8_t *rings, const uint8_t *rin
                         d0 = dn[0], d1 = dn[1], d2 = dn[2], d3 = dn[3], d4 = dn[4];
                     }
                     uint32_t ml;
-                    const bool fj = k1_fast_check(w0, w1, w2, w3, ll, mc, seq_in, S - ip, len - op, ml) && go;
-                    if (fj && (nseq & ckm) == 0) ck[nseq >> ckl] = make_uint2(ip, op);
+                    const bool fj = k1_fast_check(w0, w1, w2, w3, ll, mc, seq_in, S - ip, len - op, ml) & go;
+                    const bool ckw = fj & ((nseq & ckm) == 0);  // one condition: one masked store
+                    if (ckw) ck[nseq >> ckl] = make_uint2(ip, op);
                     nseq += fj ? 1u : 0u;
                     ip += fj ? seq_in : 0u;
                     op += fj ? ll + ml : 0u;
