@@ -481,6 +481,34 @@ def test_lz4_decode_long_zero_runs_at_window_edges(mode):
     assert st == rst == 0 and np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("shift", [0, 1, 2, 3, 7, 13])
+def test_lz4_decode_dense_short_sequences(mode, shift):
+    """Canonical blocks made of the shortest sequences (literal runs of 1 .. 13
+    bytes, zero runs of 5 .. 22 bytes, so 4 .. 17-byte sequences, a few with
+    one match-length byte and a few with a literal run too long for the
+    decoder's fast step), shifted by `shift` leading bytes: the parse takes
+    several such sequences per step at every offset of its ring, and its
+    per-step window limit and ring refills fall between and inside them."""
+    rng = np.random.default_rng(1000 + 10 * shift + mode)
+    parts = [rng.integers(1, 256, shift, dtype=np.uint8)]
+    total = shift
+    while total < 5 * 65536 + 4321:
+        ll = int(rng.choice([1, 1, 1, 2, 2, 3, 4, 5, 8, 12, 13]))
+        run = int(rng.choice([5, 5, 5, 6, 7, 9, 12, 19, 20, 22]))
+        lit = rng.integers(1, 256, ll - 1, dtype=np.uint8)
+        parts += [lit, np.zeros(run + 1, np.uint8)]  # the run's first zero is the last literal
+        total += ll + run
+    m = np.concatenate(parts)[: 5 * 65536 + 4321]
+    enc = oracle.lz4_encode_blocks(m, 65536)
+    assert enc["sizes"].max() > 20000  # dense blocks: thousands of sequences each
+    dst = np.random.default_rng(9 + shift).integers(0, 256, m.size, dtype=np.uint8)
+    got, st = gpu_decode(enc["payload"], enc["offsets"], enc["sizes"], dst, mode)
+    ref, rst = oracle.lz4_decode_blocks(enc["payload"], enc["offsets"], enc["sizes"], dst, mode=mode)
+    assert st == rst == 0 and np.array_equal(got, ref)
+    assert np.array_equal(ref, m if mode == 0 else dst ^ m)
+
+
 def random_payload(rng, nblocks, last, block_bytes=65536, **kw):
     comps, plains = [], []
     for b in range(nblocks):
