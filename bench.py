@@ -265,8 +265,8 @@ def src_hash(path):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the codec is single-device here, "
-              "see DESIGN.md for how it would shard", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): it measures one device's share of the "
+              "path; sharded, each GPU would encode and receive its own shard's patch and LZ4 blocks", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
