@@ -257,6 +257,26 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def run_env(torch):
+    """The software and the device the numbers were taken on: HIP and torch
+    versions, device name, architecture, compute units, and the clocks
+    rocm-smi reports (when it answers within a few seconds)."""
+    props = torch.cuda.get_device_properties(0)
+    env = {"hip": getattr(torch.version, "hip", None), "torch": torch.__version__, "device": props.name,
+           "arch": getattr(props, "gcnArchName", None), "compute_units": props.multi_processor_count,
+           "hbm_GiB": round(props.total_memory / 2 ** 30, 1)}
+    try:
+        import subprocess
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=15)
+        cards = json.loads(r.stdout) if r.returncode == 0 and r.stdout.strip().startswith("{") else {}
+        for card, vals in cards.items():
+            env["clocks"] = {k: v for k, v in vals.items() if "sclk" in k.lower() or "mclk" in k.lower()}
+            break
+    except Exception:
+        pass
+    return env
+
+
 def src_hash(path):
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -551,11 +571,18 @@ def main():
         ev[k].clear()
     parse_ev["lz4_decode"].clear()
     torch.cuda.synchronize()
+    # step boundaries as events on the main stream (the side stream joins it
+    # within every step), for the per-step median and minimum
+    step_marks = [torch.cuda.Event(enable_timing=True)]
     t0 = time.perf_counter()
+    step_marks[0].record(main_stream)
     for _ in range(args.steps):
         run_step(True)
+        step_marks.append(torch.cuda.Event(enable_timing=True))
+        step_marks[-1].record(main_stream)
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t0
+    step_each = [a.elapsed_time(b) for a, b in zip(step_marks[:-1], step_marks[1:])]
     if int(status.item()) != 0:
         raise SystemExit(f"device status {int(status.item())} during the timed steps")
     if not views_equal(b_recv, b_old):
@@ -631,7 +658,10 @@ def main():
             "stream": "second stream",
             "note": "lz4_decode above is the apply; the one-call decode is both"},
         "roofline": roofline,
+        "step_ms_median": round(float(np.median(step_each)), 3),
+        "step_ms_min": round(float(np.min(step_each)), 3),
         "setup_s": round(t_setup, 1),
+        "env": run_env(torch),
     }
 
     # ---- the metric's own quantity: patch-path encode + apply (pulse_cast_diff,
