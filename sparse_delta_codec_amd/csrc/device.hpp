@@ -266,7 +266,8 @@ struct WsHeader {
     uint64_t pad1[7];
     uint32_t aux;     // per-op counter (decode: slow-block count)
     uint32_t aux2;    // per-op counter (decode: slow-kernel blocks finished)
-    uint32_t pad2[14];
+    uint32_t aux3;    // per-op counter (decode: blocks for the wave walk)
+    uint32_t pad2[13];
 };
 static_assert(sizeof(WsHeader) == 256, "header is 256 bytes");
 

@@ -7,7 +7,7 @@
 // LZ4 block format; any valid block is accepted, not only the canonical parse.
 //
 // A block's token chain is serial, while applying it is a dense stream (a
-// sparse mask still changes nearly every cache line of dst).  Three kernels:
+// sparse mask still changes nearly every cache line of dst).  Four kernels:
 //  K1 k_lz4_parse   one LANE per block, 64 blocks per wave.  Checks the block
 //                   table (inside the payload, no block starting before the
 //                   end of an earlier one: a prefix max over blocks by
@@ -19,8 +19,11 @@
 //                   and every 16th sequence start (input, output position) is
 //                   recorded as a checkpoint; any other block is handed to K3.
 //                   A block with a length chain longer than the ring (a run
-//                   of one byte over most of the block, or one literal run)
-//                   is walked again straight from global memory.
+//                   of one byte over most of the block), a literal run
+//                   longer than 2,055 bytes, or a compressed size over 3/4 of
+//                   its length is listed for K1L.
+//  K1L k_lz4_long   one WAVE per listed block: the same walk and checks
+//                   straight from global memory, a KiB per coalesced load.
 //  K2 k_lz4_fast    one WORKGROUP per checkpointed block: stages its compressed
 //                   bytes in LDS, starts the loads of its dst range (XOR mode),
 //                   rebuilds the block in a zeroed LDS image with one thread
@@ -89,6 +92,7 @@ struct Lz4DecArgs {
     uint64_t *status;    // look-back words of K1 (one per K1 workgroup)
     uint32_t *binfo;     // per block: BI_BAD | BI_SLOW | number of sequences
     uint32_t *slow_list; // blocks for K3
+    uint32_t *long_list; // blocks for K1L
     uint2 *ckpt;         // checkpoints (input position, output position)
     uint32_t k1_tiles;
 };
@@ -227,10 +231,46 @@ struct Win32 {
     }
 };
 
+// Byte reader for a walk that a whole wave does together (every lane holds the
+// same position): lane l holds the aligned 16-byte piece cur + l, so the wave
+// holds 1 KiB of the block (byte x at base + mis + x, base 16-byte aligned),
+// loaded with one coalesced access whenever a byte past it is read: a jump
+// over a literal run costs one round trip, a length chain one per KiB.  A byte
+// is taken from the lane holding it by readlane, so the walk's state stays in
+// scalar registers.  Only pieces holding a byte of the block are loaded.
+struct WinWave {
+    const uint8_t *base;
+    uint32_t mis, end, cur;  // end: pieces holding a byte of the block
+    u32x4 v;                 // piece cur + lane
+    __device__ __forceinline__ WinWave(const uint8_t *b, uint32_t m, uint32_t S)
+        : base(b), mis(m), end((m + S + 15) >> 4), cur(0xFFFFFFC0u), v{0u, 0u, 0u, 0u} {}
+    // the block's aligned dword holding block byte x (x < S)
+    __device__ __forceinline__ uint32_t dword_at(uint32_t x) {
+        const uint32_t p = mis + x, k = p >> 4;
+        if (k - cur >= (uint32_t)kWave) {
+            const uint32_t c = k + (uint32_t)lane_id();
+            v = c < end ? *reinterpret_cast<const u32x4 *>(base + 16 * (size_t)c) : u32x4{0u, 0u, 0u, 0u};
+            cur = k;
+        }
+        const uint32_t r = p - 16 * cur, w = (r >> 2) & 3u;
+        const uint32_t d = w == 0 ? v.x : (w == 1 ? v.y : (w == 2 ? v.z : v.w));
+        return (uint32_t)__builtin_amdgcn_readlane((int)d, (int)(r >> 4));
+    }
+    __device__ __forceinline__ uint32_t operator[](uint32_t x) {
+        return (dword_at(x) >> (8 * ((mis + x) & 3u))) & 0xFFu;
+    }
+    // block bytes x .. x + 7 are all 255 and start an aligned dword pair (x + 8 <= S)
+    __device__ __forceinline__ bool ff8(uint32_t x) {
+        if ((mis + x) & 7u) return false;
+        return (dword_at(x) & dword_at(x + 4)) == ~0u;
+    }
+};
+
 // Adds to n the length bytes starting at block byte q (bytes added while they
-// are 255, eight at a time where they fill a window word); q moves past them.
+// are 255, eight at a time where they fill an aligned word); q moves past them.
 // False when they run past the block (S bytes) or n passes len.
-__device__ __forceinline__ bool win_chain(Win32 &src, uint32_t S, uint32_t len, uint32_t &q, uint32_t &n) {
+template <class Win>
+__device__ __forceinline__ bool win_chain(Win &src, uint32_t S, uint32_t len, uint32_t &q, uint32_t &n) {
     uint32_t x;
     do {
         if (q >= S) return false;
@@ -441,18 +481,18 @@ __device__ __forceinline__ WalkResult k1_walk(uint8_t *rings, const uint8_t *rin
 }
 
 
-// The walk of one block straight from global memory, for the lanes whose
-// block has a length chain longer than the ring or a literal run longer than
-// K1_LIT_MAX: the same checks, flags and checkpoints as the ring walk (a
-// sequence that is not canonical: F_SLOW), reading the block's bytes 32 at a
+// The walk of one block straight from global memory, for the blocks with a
+// length chain longer than the ring or a literal run longer than K1_LIT_MAX:
+// the same checks, flags and checkpoints as the ring walk (a sequence that is
+// not canonical: F_SLOW), by a whole wave (K1L) reading the block a KiB at a
 // time.  dck (or null): the block's direct checkpoint slots, filled for its
 // first kCkDirect sequences; a valid block of at most kCkDirect sequences then
-// has them all (F_DCK).
+// has them all (F_DCK).  Only the lanes with `wr` store checkpoints.
 __device__ __forceinline__ WalkResult k1_walk_long(const uint8_t *pay, int64_t boff, uint32_t S, uint32_t len,
-                                                   uint2 *ck, uint32_t ckl, uint2 *dck) {
+                                                   uint2 *ck, uint32_t ckl, uint2 *dck, bool wr) {
     const uint8_t *blk = pay + boff;
     const uint32_t mis = (uint32_t)(reinterpret_cast<uintptr_t>(blk) & 15);
-    Win32 src(blk - mis, mis, S);
+    WinWave src(blk - mis, mis, S);
     uint32_t ip = 0, op = 0, nseq = 0;
     const WalkResult bad{0u, F_BAD | F_DONE};
     while (true) {
@@ -461,8 +501,8 @@ __device__ __forceinline__ WalkResult k1_walk_long(const uint8_t *pay, int64_t b
         uint32_t q = ip + 1, ll = tok >> 4;
         if (ll == 15 && !win_chain(src, S, len, q, ll)) return bad;
         if (ll > S - q || ll > len - op) return bad;
-        if ((nseq & ((1u << ckl) - 1u)) == 0) ck[nseq >> ckl] = make_uint2(ip, op);
-        if (dck && nseq < kCkDirect) dck[nseq] = make_uint2(ip, op);
+        if (wr && (nseq & ((1u << ckl) - 1u)) == 0) ck[nseq >> ckl] = make_uint2(ip, op);
+        if (wr && dck && nseq < kCkDirect) dck[nseq] = make_uint2(ip, op);
         ++nseq;
         ip = q + ll;
         op += ll;
@@ -552,29 +592,32 @@ __global__ __launch_bounds__(64) void k_lz4_parse(Lz4DecArgs a) {
 
     const uint32_t len = live ? block_len(a, b) : 0;
     uint2 *ck = a.ckpt + (live ? ck_base(off, b) : 0);
-    WalkResult w =
-        k1_walk(s_rings, s_rings + lane * K1_STRIDE, !bad, a.payload, a.payload_bytes, (int64_t)off, (uint32_t)S, len, ck,
-                ck_log((uint32_t)S));
-    if (__ballot((w.flags & F_LONG) != 0)) {
-        if (w.flags & F_LONG) {
-            const bool dsz = ck_direct((uint32_t)S, len, 0);  // the size test of ck_direct
-            w = k1_walk_long(a.payload, (int64_t)off, (uint32_t)S, len, ck, ck_log((uint32_t)S),
-                             dsz ? ck + ck_direct_slot((uint32_t)S) : nullptr);
-        }
+    // a block that compresses to more than 3/4 of its length (nearly
+    // incompressible bytes: few, long literal runs, each a ring refill) is not
+    // walked here
+    const bool dense = live && !bad && 4 * S > 3 * (uint64_t)len;
+    WalkResult w = k1_walk(s_rings, s_rings + lane * K1_STRIDE, !bad && !dense, a.payload, a.payload_bytes,
+                           (int64_t)off, (uint32_t)S, len, ck, ck_log((uint32_t)S));
+    // such a block, and one the ring cannot walk, is listed for K1L, which
+    // walks it with a whole wave and writes its block info
+    const bool lng = dense || (live && !bad && (w.flags & F_LONG) != 0);
+    if (lng) {
+        const uint32_t k = add_agent32(&a.hdr->aux3, 1u);
+        if (k < a.nblocks) a.long_list[k] = (uint32_t)b;
     }
     // a valid block of one sequence is one literal run: K2 copies it as such
     if (w.nseq == 1 && !(w.flags & (F_BAD | F_SLOW))) w.flags |= F_LIT;
     // a large, literal-heavy block of few sequences: one checkpoint per sequence
     // (written here unless the walk from global memory wrote them)
-    const bool direct =
-        !bad && !(w.flags & (F_BAD | F_SLOW | F_LIT | F_DCK)) && ck_direct((uint32_t)S, len, w.nseq);
+    const bool direct = !bad && !lng && !(w.flags & (F_BAD | F_SLOW | F_LIT | F_DCK)) &&
+                        ck_direct((uint32_t)S, len, w.nseq);
     if (__ballot(direct)) {
         if (direct) k1_direct_ck(a.payload, (int64_t)off, (uint32_t)S, w.nseq, ck + ck_direct_slot((uint32_t)S));
     }
     const uint32_t nseq = w.nseq;
     const bool slow = (w.flags & F_SLOW) != 0;
     bad = bad || (w.flags & F_BAD) != 0;
-    if (live) {
+    if (live && !lng) {
         if (bad) {
             a.binfo[b] = BI_BAD;
             or_agent32(a.d_status, 4u /*PULSE_DS_CORRUPT*/);
@@ -584,6 +627,51 @@ __global__ __launch_bounds__(64) void k_lz4_parse(Lz4DecArgs a) {
             if (k < a.nblocks) a.slow_list[k] = (uint32_t)b;
         } else {
             a.binfo[b] = nseq | ((w.flags & F_LIT) ? BI_LIT : 0u);
+        }
+    }
+}
+
+// ---- K1L ---------------------------------------------------------------------
+// The blocks K1 listed (compressed to more than 3/4 of their length, a literal
+// run longer than K1_LIT_MAX, or a length chain longer than the ring: the
+// nearly incompressible blocks of few, long sequences), one wave per block:
+// the wave walks the block from global memory a KiB at a time, so each jump
+// over a literal run is one coalesced round trip, and the blocks are walked
+// side by side on many SIMDs instead of in one lane each.  Then the block's
+// info, as K1 writes it for the others.  Four waves per workgroup, each on
+// its own blocks.
+constexpr int K1L_THREADS = 256;
+constexpr int K1L_GROUPS = 2048;
+
+__global__ __launch_bounds__(K1L_THREADS) void k_lz4_long(Lz4DecArgs a) {
+    constexpr uint32_t NW = K1L_THREADS / kWave;
+    uint32_t count = ld_agent32(&a.hdr->aux3);
+    if (count > a.nblocks) count = (uint32_t)a.nblocks;
+    const bool lead = lane_id() == 0;
+    const uint32_t wv = threadIdx.x / kWave;
+    for (uint32_t i = blockIdx.x * NW + wv; i < count; i += gridDim.x * NW) {
+        const uint32_t bu = a.long_list[i];
+        if (bu >= a.nblocks) continue;  // (a workspace whose last parse had no apply)
+        const int64_t b = bu;
+        const uint64_t off = a.offs[b];
+        const uint32_t S = a.sizes[b];
+        const uint32_t len = block_len(a, b);
+        uint2 *ck = a.ckpt + ck_base(off, b);
+        const bool dsz = ck_direct(S, len, 0);  // the size test of ck_direct
+        WalkResult w = k1_walk_long(a.payload, (int64_t)off, S, len, ck, ck_log(S),
+                                    dsz ? ck + ck_direct_slot(S) : nullptr, lead);
+        if (w.nseq == 1 && !(w.flags & (F_BAD | F_SLOW))) w.flags |= F_LIT;
+        if (lead) {
+            if (w.flags & F_BAD) {
+                a.binfo[b] = BI_BAD;
+                or_agent32(a.d_status, 4u /*PULSE_DS_CORRUPT*/);
+            } else if (w.flags & F_SLOW) {
+                a.binfo[b] = BI_SLOW;
+                const uint32_t k = add_agent32(&a.hdr->aux, 1u);
+                if (k < a.nblocks) a.slow_list[k] = (uint32_t)b;
+            } else {
+                a.binfo[b] = w.nseq | ((w.flags & F_LIT) ? BI_LIT : 0u);
+            }
         }
     }
 }
@@ -1177,6 +1265,7 @@ __global__ __launch_bounds__(K3_THREADS) void k_lz4_slow(Lz4DecArgs a) {
         if (d == gridDim.x - 1) {
             st_agent32(&a.hdr->aux, 0u);
             st_agent32(&a.hdr->aux2, 0u);
+            st_agent32(&a.hdr->aux3, 0u);
         }
     }
 }
@@ -1189,10 +1278,10 @@ namespace {
 // The regions of a decode workspace are a function of its size alone, so the
 // look-back status words of one call never overlap the per-block data another
 // call of a different size left behind (a stale word must never carry a
-// matching epoch tag).  Status: 1 word per KiB; block info and slow list:
-// ws/8 bytes each; checkpoints: the rest.
+// matching epoch tag).  Status: 1 word per KiB; block info, slow list and
+// long list: ws/8 bytes each; checkpoints: the rest.
 struct DecLayout {
-    size_t status, binfo, slow, ckpt;
+    size_t status, binfo, slow, longl, ckpt;
     size_t status_words, blocks, ck_entries;
 };
 size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1203,7 +1292,8 @@ DecLayout dec_layout(size_t ws) {
     L.binfo = al256(L.status + 8 * L.status_words);
     L.blocks = ws >> 5;
     L.slow = al256(L.binfo + 4 * L.blocks);
-    L.ckpt = al256(L.slow + 4 * L.blocks);
+    L.longl = al256(L.slow + 4 * L.blocks);
+    L.ckpt = al256(L.longl + 4 * L.blocks);
     L.ck_entries = ws > L.ckpt ? (ws - L.ckpt) / sizeof(uint2) : 0;
     return L;
 }
@@ -1256,13 +1346,14 @@ Lz4DecArgs dec_args(const uint8_t *payload, int64_t payload_bytes, const uint64_
     a.status = reinterpret_cast<uint64_t *>(w + L.status);
     a.binfo = reinterpret_cast<uint32_t *>(w + L.binfo);
     a.slow_list = reinterpret_cast<uint32_t *>(w + L.slow);
+    a.long_list = reinterpret_cast<uint32_t *>(w + L.longl);
     a.ckpt = reinterpret_cast<uint2 *>(w + L.ckpt);
     a.k1_tiles = (uint32_t)((nblocks + 63) / 64);
     return a;
 }
 }  // namespace
 
-// K1 alone: validates the block table and parses every block into the
+// K1 and K1L: validate the block table and parse every block into the
 // workspace (per-block info, checkpoints, the list of blocks for K3).
 extern "C" int pulse_launch_lz4_decode_parse(const uint8_t *payload, int64_t payload_bytes, const uint64_t *offs,
                                              const uint32_t *sizes, int64_t nblocks, int32_t block_bytes,
@@ -1271,6 +1362,8 @@ extern "C" int pulse_launch_lz4_decode_parse(const uint8_t *payload, int64_t pay
     const Lz4DecArgs a = dec_args(payload, payload_bytes, offs, sizes, nblocks, block_bytes, nbytes, nullptr, 0,
                                   d_status, ws, ws_bytes);
     k_lz4_parse<<<dim3(a.k1_tiles), dim3(64), 0, stream>>>(a);
+    const int64_t nw = K1L_THREADS / kWave, gl = (nblocks + nw - 1) / nw < K1L_GROUPS ? (nblocks + nw - 1) / nw : K1L_GROUPS;
+    if (gl > 0) k_lz4_long<<<dim3((unsigned)gl), dim3(K1L_THREADS), 0, stream>>>(a);
     return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 

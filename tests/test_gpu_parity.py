@@ -856,9 +856,69 @@ def test_lz4_decode_literal_runs_past_the_ring_walk(mode):
         assert np.array_equal(got, ref), last[0]
 
 
+def raw_block(rng, seqs, total=None, final=None):
+    """LZ4 block bytes from (literal count, match offset, match length)
+    triples, any offsets; then a final literal run of `final` bytes, or of the
+    bytes that bring the plain length to `total`."""
+    comp, n = [], 0
+    for ll, off, ml in seqs:
+        comp += [(min(ll, 15) << 4) | min(ml - 4, 15)] + (length_bytes(ll) if ll >= 15 else [])
+        comp += [int(x) for x in rng.integers(1, 256, ll)] + [off & 255, off >> 8]
+        comp += length_bytes(ml - 4) if ml - 4 >= 15 else []
+        n += ll + ml
+    lf = total - n if final is None else final
+    comp += [min(lf, 15) << 4] + (length_bytes(lf) if lf >= 15 else []) + [int(x) for x in rng.integers(1, 256, lf)]
+    return np.array(comp, np.uint8)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_lz4_decode_long_blocks_of_other_forms(mode):
+    """Blocks that start with a literal run longer than 2055 bytes (so the
+    parse lists them for its wave-per-block walk from global memory), then go
+    on in forms other than the canonical one: valid ones (a match of offset
+    2, a match right after a match, a long run of offset 1 matches) decode like
+    the oracle through the serial kernel or the fast path; corrupt ones (an
+    offset of 0 or past the output, a literal run or a match past the block,
+    a length chain that runs off the block, a block that decodes short) are
+    reported and leave their dst range as it was, while the blocks around
+    them decode as usual."""
+    rng = np.random.default_rng(300 + mode)
+    B = 65536
+    L = 2100
+    valid = [
+        raw_block(rng, [(L, 1, 4)] * 6, B),                                # canonical
+        raw_block(rng, [(L, 1, 4), (300, 2, 9), (L, 1, 4)], B),            # offset 2
+        raw_block(rng, [(L, 1, 4), (0, 1, 7), (L, 1, 20)], B),             # a match right after a match
+        raw_block(rng, [(L, 1, 40000)], B),                                # a long offset-1 run
+        raw_block(rng, [(3000 + 17 * k, 1, 4 + k) for k in range(12)], B),
+    ]
+    bad = [
+        raw_block(rng, [(L, 1, 4), (20, 0, 4)], B),                        # offset 0
+        raw_block(rng, [(L, 1, 4), (20, 4000, 4)], B),                     # offset past the output
+        raw_block(rng, [(L, 1, 4)], None, 3000)[:L + 3000],                # final run past the block
+        raw_block(rng, [(L, 1, 70000)], None, 5),                          # match past the block length
+        np.concatenate([raw_block(rng, [(L, 1, 4)], None, 5)[:-6], np.array([0x0F, 1, 0] + [255] * 40, np.uint8)]),
+        raw_block(rng, [(L, 1, 4)] * 3, B - 100),                          # decodes 100 bytes short
+    ]
+    for blocks, want in ((valid, 0), (valid[:2] + bad[:1] + valid[2:4] + bad[1:] + valid[4:], pulse.PULSE_DS_CORRUPT)):
+        sizes = np.array([x.size for x in blocks], np.uint32)
+        offs = np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(np.uint64)
+        payload = np.concatenate(blocks)
+        dst = rng.integers(0, 256, B * len(blocks), dtype=np.uint8)
+        got, st = gpu_decode(payload, offs, sizes, dst, mode)
+        ref, rst = oracle.lz4_decode_blocks(payload, offs, sizes, dst, mode=mode)
+        assert st == rst == want
+        assert np.array_equal(got, ref)
+        if want:  # each corrupt block's range is untouched, each valid one changed
+            for k, blk in enumerate(blocks):
+                same = np.array_equal(got[k * B:(k + 1) * B], dst[k * B:(k + 1) * B])
+                assert same == any(blk is x for x in bad), k
+
+
 def test_lz4_decode_in_two_calls_on_two_streams():
     """parse on one stream, apply on another after an event, several payloads in
-    a row on one workspace (canonical, general and corrupt blocks): the same
+    a row on one workspace (canonical, general and corrupt blocks, and blocks
+    of long literal runs that the parse walks a wave per block): the same
     bytes and status as the one-call decode and the oracle, every time."""
     rng = np.random.default_rng(91)
     cases = []
@@ -871,6 +931,12 @@ def test_lz4_decode_in_two_calls_on_two_streams():
     bad[int(enc["offsets"][2])] ^= 0xFF
     cases.append((bad, enc["offsets"], enc["sizes"], m.size))
     cases.append((enc["payload"], enc["offsets"], enc["sizes"], m.size))
+    # blocks of long literal runs, walked a wave per block: valid, corrupt, valid
+    longb = [raw_block(rng, [(2100, 1, 4)] * 6, 65536), raw_block(rng, [(2100, 1, 4), (20, 0, 4)], 65536),
+             raw_block(rng, [(2100, 1, 40000)], 65536)]
+    lsz = np.array([x.size for x in longb], np.uint32)
+    cases.append((np.concatenate(longb), np.concatenate([[0], np.cumsum(lsz)[:-1]]).astype(np.uint64), lsz,
+                  3 * 65536))
     nbmax = max(len(c[1]) for c in cases)
     pbmax = max(c[0].size for c in cases)
     ws = pulse.workspace(pulse.PULSE_OP_LZ4_DECODE, nbmax, pbmax)
