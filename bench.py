@@ -259,22 +259,13 @@ def log(msg):
 
 def run_env(torch):
     """The software and the device the numbers were taken on: HIP and torch
-    versions, device name, architecture, compute units, and the clocks
-    rocm-smi reports (when it answers within a few seconds)."""
+    versions, device name, architecture, compute units and memory.  (No
+    helper program is started: a child of a process that holds the GPU must
+    not replace itself with another program.)"""
     props = torch.cuda.get_device_properties(0)
-    env = {"hip": getattr(torch.version, "hip", None), "torch": torch.__version__, "device": props.name,
-           "arch": getattr(props, "gcnArchName", None), "compute_units": props.multi_processor_count,
-           "hbm_GiB": round(props.total_memory / 2 ** 30, 1)}
-    try:
-        import subprocess
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=15)
-        cards = json.loads(r.stdout) if r.returncode == 0 and r.stdout.strip().startswith("{") else {}
-        for card, vals in cards.items():
-            env["clocks"] = {k: v for k, v in vals.items() if "sclk" in k.lower() or "mclk" in k.lower()}
-            break
-    except Exception:
-        pass
-    return env
+    return {"hip": getattr(torch.version, "hip", None), "torch": torch.__version__, "device": props.name,
+            "arch": getattr(props, "gcnArchName", None), "compute_units": props.multi_processor_count,
+            "hbm_GiB": round(props.total_memory / 2 ** 30, 1)}
 
 
 def src_hash(path):
