@@ -915,6 +915,35 @@ def test_lz4_decode_long_blocks_of_other_forms(mode):
                 assert same == any(blk is x for x in bad), k
 
 
+def test_lz4_decode_more_long_blocks_than_walk_waves():
+    """More blocks for the parse's wave-per-block walk than that kernel has
+    waves (2,048 workgroups of four): 8,450 incompressible 16 KiB blocks (each
+    one literal run), with a compressible block every 97th and a ragged last
+    block, so that waves take several list entries in turn.  The encoding
+    equals the oracle's byte for byte, and both decode modes equal the
+    oracle's decode."""
+    rng = np.random.default_rng(77)
+    B = 16384
+    nblk = 8450
+    m = (np.cumsum(rng.integers(1, 256, nblk * B - 777, dtype=np.int64)) % 256).astype(np.uint8)  # neighbours differ
+    for k in range(0, nblk - 1, 97):
+        m[k * B + 40:(k + 1) * B] = 0  # a compressible block now and then
+    ref = oracle.lz4_encode_blocks(m, B)
+    assert ref["status"] == 0
+    dense = int(np.sum(4 * ref["sizes"].astype(np.int64) > 3 * B))
+    assert dense > 4 * 2048
+    got = gpu_encode(m, B)
+    assert got["status"] == 0 and got["total"] == ref["total"]
+    assert np.array_equal(got["sizes"], ref["sizes"]) and np.array_equal(got["payload"], ref["payload"][:ref["total"]])
+    dst = rng.integers(0, 256, m.size, dtype=np.uint8)
+    for mode in (0, 1):
+        d, st = gpu_decode(ref["payload"], ref["offsets"], ref["sizes"], dst, mode, block_bytes=B)
+        r, rst = oracle.lz4_decode_blocks(ref["payload"], ref["offsets"], ref["sizes"], dst, block_bytes=B, mode=mode)
+        assert st == rst == 0
+        assert np.array_equal(d, r)
+        assert np.array_equal(r, m if mode == 0 else dst ^ m)
+
+
 def test_lz4_decode_in_two_calls_on_two_streams():
     """parse on one stream, apply on another after an event, several payloads in
     a row on one workspace (canonical, general and corrupt blocks, and blocks
