@@ -22,7 +22,7 @@ except ImportError:
     pulse = None
 
 from tests.gpu_util import dev, host, u16, zeros  # noqa: E402
-from tests import lz4_spec  # noqa: E402
+from tests import lz4_spec, lz4_system  # noqa: E402
 
 TILE = 16384  # elements per compaction tile
 SIZES = [1, 2, 63, 64, 65, 4095, 4097, TILE - 1, TILE, TILE + 1, 3 * TILE + 7, (1 << 20) + 7]
@@ -942,6 +942,27 @@ def test_lz4_decode_more_long_blocks_than_walk_waves():
         assert st == rst == 0
         assert np.array_equal(d, r)
         assert np.array_equal(r, m if mode == 0 else dst ^ m)
+
+
+@pytest.mark.skipif(not lz4_system.available(), reason="liblz4 is not installed")
+@pytest.mark.parametrize("mode", [0, 1])
+def test_lz4_decode_library_blocks(mode):
+    """Blocks written by the system's LZ4 library (its own parse: matches at
+    any offset, so most go to the serial kernel; random bytes become one
+    literal run, walked a wave per block): both decode modes give back the
+    bytes the library compressed, like the oracle's decode."""
+    rng = np.random.default_rng(500 + mode)
+    cases = [mask_bytes(5 * 65536 + 321, d, seed=int(d * 1e4) + mode) for d in (0.0, 0.0005, 0.01, 0.08, 0.5)]
+    cases.append(np.repeat(rng.integers(0, 256, 9000, dtype=np.uint8), rng.integers(1, 60, 9000))[:3 * 65536])
+    cases.append((np.cumsum(rng.integers(1, 256, 2 * 65536 + 77, dtype=np.int64)) % 256).astype(np.uint8))
+    for k, data in enumerate(cases):
+        payload, offs, sizes = lz4_system.compress_blocks(data, 65536, 1 + 7 * (k % 2))
+        dst = rng.integers(0, 256, data.size, dtype=np.uint8)
+        got, st = gpu_decode(payload, offs, sizes, dst, mode)
+        ref, rst = oracle.lz4_decode_blocks(payload, offs, sizes, dst, mode=mode)
+        assert st == rst == 0, k
+        assert np.array_equal(ref, data if mode == 0 else dst ^ data), k
+        assert np.array_equal(got, ref), k
 
 
 def test_lz4_decode_in_two_calls_on_two_streams():
