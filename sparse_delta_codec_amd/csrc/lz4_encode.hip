@@ -196,6 +196,7 @@ struct EncShared {
     uint64_t off;
     uint32_t pw[LZE_NW];  // fused pass: changed elements of each wave
     uint64_t poff;        // fused pass: the block's first patch entry
+    uint32_t comp;        // plain encoder: the size of a block left to enc_gather
 };
 
 // ---- fused sender pass: cast + diff + compaction feeding the block encoder ----
@@ -374,11 +375,259 @@ __device__ __forceinline__ void enc_load(const Lz4EncArgs &a, uint32_t b, uint8_
     }
 }
 
+// ---- large blocks of few sequences: emission by output piece ---------------
+// A block whose encoding is larger than the window (nearly incompressible
+// bytes with a few runs, such as the sign-and-exponent plane of a packed
+// patch) would take several window passes, each copying its literals byte by
+// byte.  With fewer than LZE_GCAP sequences the plain encoder places it (its
+// size and offset, in enc_rest) and then writes it by output piece
+// (enc_gather): the sequences go into a table in the window (output start, run
+// start i, match end j), and each thread builds whole aligned 16-byte pieces
+// of the payload: a piece inside one literal run is 16 image bytes (from two
+// image pieces), any other piece is put together byte by byte from its
+// sequences' token, length bytes, literals and offset.
+constexpr int LZE_GCAP = (LZE_WIN + 48) / 8;
+
+struct GatherTab {
+    const uint2 *tab;  // entry k < nseq: (output start, i | j << 16); entry nseq: (output start, 0)
+    int32_t nseq, len;
+    // the last entry whose output starts at or before o
+    __device__ __forceinline__ int32_t find(int32_t o) const {
+        int32_t lo = 0, hi = nseq;
+        while (lo < hi) {
+            const int32_t mid = (lo + hi + 1) >> 1;
+            if ((int32_t)tab[mid].x <= o) lo = mid;
+            else hi = mid - 1;
+        }
+        return lo;
+    }
+    // entry k: output start O, literal run [la, i) of the input, match [i, j),
+    // token and literal-length bytes h
+    __device__ __forceinline__ void get(int32_t k, int32_t &O, int32_t &la, int32_t &i, int32_t &j,
+                                       int32_t &h) const {
+        O = (int32_t)tab[k].x;
+        la = k == 0 ? 0 : (int32_t)(tab[k - 1].y >> 16);
+        const bool fin = k == nseq;
+        i = fin ? len : (int32_t)(tab[k].y & 0xFFFFu);
+        j = fin ? len : (int32_t)(tab[k].y >> 16);
+        h = 1 + ext_bytes(i - la);
+    }
+};
+
+// Output byte o of entry k (o inside the entry's bytes)
+template <int CHLOG>
+__device__ __forceinline__ uint32_t gather_byte(const GatherTab &g, const uint8_t *s_img, int32_t k, int32_t o) {
+    int32_t O, la, i, j, h;
+    g.get(k, O, la, i, j, h);
+    const int32_t ll = i - la, ml = j - i, rel = o - O;
+    if (rel == 0) return (uint32_t)(((ll >= 15 ? 15 : ll) << 4) | (k == g.nseq ? 0 : (ml - 4 >= 15 ? 15 : ml - 4)));
+    if (rel < h) return rel < h - 1 ? 255u : (uint32_t)(ll - 15 - 255 * (h - 2));
+    if (rel < h + ll) return s_img[img_addr<CHLOG>(la + rel - h)];
+    const int32_t e = rel - h - ll;  // the offset bytes, then the match length bytes
+    if (e < 2) return e == 0 ? 1u : 0u;
+    const int32_t em = ext_bytes(ml - 4);
+    return e - 2 < em - 1 ? 255u : (uint32_t)(ml - 4 - 15 - 255 * (em - 1));
+}
+
+// Writes block b, placed by enc_rest (sh.off, sh.comp), by output piece.  The
+// run analysis of enc_rest's steps 2 and 3 is made again here from the image
+// (still whole: nothing was emitted), so that none of enc_rest's state has to
+// outlive it.
+template <int CHLOG>
+__device__ __forceinline__ void enc_gather(const Lz4EncArgs &a, uint32_t b, EncShared &sh, int t) {
+    constexpr int32_t CH = 1 << CHLOG;
+    const uint8_t *const s_img = sh.img;
+    const int wv = __builtin_amdgcn_readfirstlane(t / kWave), ln = t % kWave;
+    const int64_t blk_base = (int64_t)b * a.block_bytes;
+    const int32_t len = (int32_t)((a.nbytes - blk_base) < a.block_bytes ? (a.nbytes - blk_base) : a.block_bytes);
+    const uint32_t off_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(sh.off >> 32));
+    const uint32_t off_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)sh.off);
+    const uint64_t off = ((uint64_t)off_hi << 32) | off_lo;
+    const int32_t comp = __builtin_amdgcn_readfirstlane((int)sh.comp);
+    if ((int64_t)(off + comp) > a.cap) return;
+
+    // the run boundaries of this thread's chunk (as in enc_rest, step 2)
+    const int32_t cs = t * CH;
+    const int32_t cl = len - cs < 0 ? 0 : (len - cs < CH ? len - cs : CH);
+    constexpr int NW = (CH + 31) / 32;
+    uint32_t mw[NW];
+#pragma unroll
+    for (int i = 0; i < NW; ++i) mw[i] = 0;
+    if (cl > 0) {
+        uint32_t prev = (t > 0) ? ((uint32_t)s_img[img_addr<CHLOG>(cs - 1)] << 24) : 0u;
+#pragma unroll
+        for (int32_t q = 0; q < CH; q += 16) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(s_img + img_addr<CHLOG>(cs + q));
+            const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int k = 0; k < 4; k += 2) {
+                uint32_t h[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const uint32_t x = d[k + e] ^ __builtin_amdgcn_alignbyte(d[k + e], prev, 3);
+                    prev = d[k + e];
+                    h[e] = (((x & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | x) & 0x80808080u;
+                }
+                const uint32_t byte8 = (((h[0] >> 4) | h[1]) * 0x00204081u) >> 24;
+                const int p0 = q + 4 * k;
+                mw[p0 >> 5] |= byte8 << (p0 & 31);
+            }
+        }
+        if (t == 0) mw[0] |= 1u;
+        if (cl < CH) {
+#pragma unroll
+            for (int i = 0; i < NW; ++i) {
+                const int32_t lo = 32 * i;
+                mw[i] &= cl <= lo ? 0u : (cl - lo >= 32 ? ~0u : ((1u << (cl - lo)) - 1u));
+            }
+        }
+    }
+    uint64_t m = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) m |= (uint64_t)mw[i] << (32 * i);
+    int32_t next_after;
+    {
+        const int32_t first_b = m ? cs + __builtin_ctzll(m) : len;
+        const int32_t inc = wave_incl_min_rev(first_b);
+        const int32_t exc = dpp_mov<dppc::kWaveShl1, 0xf, 0xf>(len, inc);
+        if (ln == 0) sh.scan[0][wv] = inc;
+        __syncthreads();
+        int32_t above = len;
+#pragma unroll
+        for (int w = 0; w < LZE_NW; ++w) {
+            const int32_t x = sh.scan[0][w];
+            if (w > wv) above = x < above ? x : above;
+        }
+        next_after = exc < above ? exc : above;
+    }
+    // the qualifying runs (step 3): this thread's last match end, then the
+    // previous one (exclusive maximum) as the start of its first literal run
+    uint64_t hi = 0;
+    {
+        const int32_t d = next_after - (cs + CH);
+        if (next_after < len && d >= 0 && d < 4) hi = 1ull << d;
+    }
+    const uint64_t Q = cl > 0 ? qualifying_starts<CH>(m, hi, cs, len) : 0ull;
+    int32_t last_qj = 0;
+    for (uint64_t q = Q; q;) {
+        const int u = 63 - __builtin_clzll(q);  // the last qualifying run
+        const int32_t e = run_end(m, u, cs, next_after);
+        last_qj = e < len - 5 ? e : len - 5;
+        break;
+    }
+    int32_t carry_j;
+    {
+        const int32_t inc_j = wave_incl_max(last_qj);
+        const int32_t exc_j = dpp_mov<dppc::kWaveShr1, 0xf, 0xf>(0, inc_j);
+        if (ln == kWave - 1) sh.scan[1][wv] = inc_j;
+        __syncthreads();
+        int32_t below = 0;
+#pragma unroll
+        for (int w = 0; w < LZE_NW; ++w) {
+            const int32_t xj = sh.scan[1][w];
+            if (w < wv) below = xj > below ? xj : below;
+        }
+        carry_j = exc_j > below ? exc_j : below;
+    }
+    // this thread's sequence bytes and count, and their exclusive sums
+    int32_t tot = 0;
+    {
+        int32_t la = carry_j;
+        for (uint64_t q = Q; q;) {
+            const int u = __builtin_ctzll(q);
+            q &= q - 1;
+            const int32_t e = run_end(m, u, cs, next_after);
+            const int32_t i = cs + u + 1, j = e < len - 5 ? e : len - 5;
+            tot += seq_bytes(i - la, j - i);
+            la = j;
+        }
+    }
+    int32_t pos0, rank0, nseq, qsum;
+    {
+        const uint32_t v = (uint32_t)tot | ((uint32_t)__builtin_popcountll(Q) << 18);
+        const uint32_t inc = wave_incl_sum(v);
+        if (ln == kWave - 1) sh.scan[3][wv] = (int32_t)inc;
+        __syncthreads();
+        uint32_t below = 0, all = 0;
+#pragma unroll
+        for (int w = 0; w < LZE_NW; ++w) {
+            const uint32_t x = (uint32_t)sh.scan[3][w];
+            if (w < wv) below += x;
+            all += x;
+        }
+        const uint32_t ex = below + inc - v;
+        pos0 = (int32_t)(ex & 0x3FFFFu);
+        rank0 = (int32_t)(ex >> 18);
+        qsum = __builtin_amdgcn_readfirstlane((int)(all & 0x3FFFFu));
+        nseq = __builtin_amdgcn_readfirstlane((int)(all >> 18));
+    }
+    // the table (enc_rest placed the block only with nseq < LZE_GCAP)
+    uint2 *const tab = reinterpret_cast<uint2 *>(sh.win);
+    {
+        int32_t r = rank0, pos = pos0, la = carry_j;
+        for (uint64_t q = Q; q;) {
+            const int u = __builtin_ctzll(q);
+            q &= q - 1;
+            const int32_t e = run_end(m, u, cs, next_after);
+            const int32_t i = cs + u + 1, j = e < len - 5 ? e : len - 5;
+            if (r < LZE_GCAP - 1) tab[r] = make_uint2((uint32_t)pos, (uint32_t)i | ((uint32_t)j << 16));
+            ++r;
+            pos += seq_bytes(i - la, j - i);
+            la = j;
+        }
+        if (t == 0 && nseq < LZE_GCAP) tab[nseq] = make_uint2((uint32_t)qsum, 0u);
+    }
+    __syncthreads();
+    if (nseq >= LZE_GCAP) return;  // (never: enc_rest counted the same runs)
+    const GatherTab g{tab, nseq, len};
+    uint8_t *const dst = a.payload + off;
+    // aligned payload piece u holds output bytes [16 u - shift, +16)
+    const int32_t shift = (int32_t)((uintptr_t)dst & 15);
+    uint8_t *const base = dst - shift;
+    const int32_t npc = (shift + comp + 15) >> 4;
+    for (int32_t u = t; u < npc; u += LZE_THREADS) {
+        const int32_t o0 = 16 * u - shift;
+        int32_t k = g.find(o0 > 0 ? o0 : 0);
+        int32_t O, la, i, j, h;
+        g.get(k, O, la, i, j, h);
+        if (o0 >= O + h && o0 + 16 <= O + h + (i - la)) {  // inside one literal run
+            const int32_t p = la + (o0 - O - h), q = p >> 4, r = p & 15;
+            const u32x4 A = *reinterpret_cast<const u32x4 *>(s_img + img_addr<CHLOG>(q << 4));
+            if (r) {
+                const u32x4 B = *reinterpret_cast<const u32x4 *>(s_img + img_addr<CHLOG>((q + 1) << 4));
+                *reinterpret_cast<u32x4 *>(base + 16 * u) = take16(A, B, r);
+            } else {
+                *reinterpret_cast<u32x4 *>(base + 16 * u) = A;
+            }
+        } else if (o0 >= 0 && o0 + 16 <= comp) {
+            uint64_t lo = 0, hi8 = 0;  // (no indexed array: it would live in scratch)
+            for (int32_t x = 0; x < 16; ++x) {
+                while (k < nseq && (int32_t)tab[k + 1].x <= o0 + x) ++k;
+                const uint64_t v = gather_byte<CHLOG>(g, s_img, k, o0 + x);
+                if (x < 8) lo |= v << (8 * x);
+                else hi8 |= v << (8 * (x - 8));
+            }
+            *reinterpret_cast<u32x4 *>(base + 16 * u) =
+                u32x4{(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi8, (uint32_t)(hi8 >> 32)};
+        } else {  // the block's first or last piece, shared with its neighbours
+            for (int32_t x = 0; x < 16; ++x) {
+                const int32_t o = o0 + x;
+                if (o < 0 || o >= comp) continue;
+                while (k < nseq && (int32_t)tab[k + 1].x <= o) ++k;
+                base[16 * u + x] = (uint8_t)gather_byte<CHLOG>(g, s_img, k, o);
+            }
+        }
+    }
+}
+
 // Steps 2-5 of block b, by the whole workgroup, once the image is complete
 // (and, for the fused pass, the patch counts of the waves are in sh.pw and
-// their entries staged).  Ends with the block's output written.
+// their entries staged).  Ends with the block's output written, or, for the
+// plain encoder, returns true with the block placed (sh.off, sh.comp) but not
+// written: a block larger than the window with few sequences, which
+// enc_gather then writes by output piece.
 template <int CHLOG, bool PATCH = false>
-__device__ __forceinline__ void enc_rest(const Lz4EncArgs &a, const FusedArgs &f, uint32_t b, uint32_t tag,
+__device__ __forceinline__ bool enc_rest(const Lz4EncArgs &a, const FusedArgs &f, uint32_t b, uint32_t tag,
                                          EncShared &sh, int t) {
     constexpr int32_t CH = 1 << CHLOG;
     uint8_t *const s_img = sh.img;
@@ -596,7 +845,23 @@ __device__ __forceinline__ void enc_rest(const Lz4EncArgs &a, const FusedArgs &f
     // length bytes, then the block's bytes as they are.  Those go from the
     // image straight to the payload with 16-byte stores (each output piece
     // from two image pieces), instead of through the window byte by byte.
-    if (qsum == 0) {
+    // a block larger than the window: its sequences are counted (slot set 0
+    // of the scans is free again), and with fewer than LZE_GCAP it is left to
+    // enc_gather once placed
+    [[maybe_unused]] bool defer = false;  // (uniform)
+    if constexpr (!PATCH) {
+        if (qsum != 0 && comp > LZE_WIN) {
+            const int32_t c = __builtin_popcountll(Q);
+            const int32_t ci = wave_incl_sum(c);
+            if (ln == kWave - 1) sh.scan[0][wv] = ci;
+            __syncthreads();
+            int32_t nseq = 0;
+#pragma unroll
+            for (int w = 0; w < LZE_NW; ++w) nseq += sh.scan[0][w];
+            defer = __builtin_amdgcn_readfirstlane(nseq) < LZE_GCAP;
+        }
+    }
+    if (qsum == 0 || defer) {
         if (wv == 0) {
             lookback_publish(a.status, b, tag, (uint64_t)comp);
             bool failed = false;
@@ -604,6 +869,7 @@ __device__ __forceinline__ void enc_rest(const Lz4EncArgs &a, const FusedArgs &f
             if (ln == 0) {
                 if (failed) or_agent32(a.d_status, 8u /*PULSE_DS_WORKSPACE*/);
                 sh.off = off;
+                sh.comp = (uint32_t)comp;
                 a.comp_sizes[b] = (uint32_t)comp;
                 a.comp_offsets[b] = off;
                 if (b == a.nblocks - 1) *a.d_total = off + comp;
@@ -611,10 +877,11 @@ __device__ __forceinline__ void enc_rest(const Lz4EncArgs &a, const FusedArgs &f
             }
         }
         __syncthreads();
+        if (defer) return true;
         const uint32_t off_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(sh.off >> 32));
         const uint32_t off_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)sh.off);
         const uint64_t off = ((uint64_t)off_hi << 32) | off_lo;
-        if ((int64_t)(off + comp) > a.cap) return;
+        if ((int64_t)(off + comp) > a.cap) return false;
         uint8_t *const dst = a.payload + off;
         const int32_t h = 1 + ext_bytes(len);  // token and length bytes
         if (t < h) {
@@ -645,7 +912,7 @@ __device__ __forceinline__ void enc_rest(const Lz4EncArgs &a, const FusedArgs &f
                 }
             }
         }
-        return;
+        return false;
     }
 
     // 4 + 5. place the block and emit it.  Wave 0 publishes the block's size;
@@ -691,7 +958,7 @@ __device__ __forceinline__ void enc_rest(const Lz4EncArgs &a, const FusedArgs &f
         const uint32_t off_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(sh.off >> 32));
         const uint32_t off_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)sh.off);
         const uint64_t off = ((uint64_t)off_hi << 32) | off_lo;
-        if ((int64_t)(off + comp) > a.cap) return;
+        if ((int64_t)(off + comp) > a.cap) return false;
         const int32_t n = comp - wb < LZE_WIN ? comp - wb : LZE_WIN;
         uint8_t *dst = a.payload + off + wb;
         // copy the pass out with 16-byte stores to aligned addresses (bytes
@@ -714,6 +981,7 @@ __device__ __forceinline__ void enc_rest(const Lz4EncArgs &a, const FusedArgs &f
         }
         if (wb + LZE_WIN < comp) __syncthreads();  // the next pass rewrites the window
     }
+    return false;
 }
 
 template <int CHLOG>
@@ -734,7 +1002,7 @@ __global__ __launch_bounds__(LZE_THREADS, 8) void k_lz4_encode(Lz4EncArgs a) {
     }
     enc_load<CHLOG>(a, b, sh.img);
     __syncthreads();
-    enc_rest<CHLOG>(a, FusedArgs{}, b, tag, sh, threadIdx.x);
+    if (enc_rest<CHLOG>(a, FusedArgs{}, b, tag, sh, threadIdx.x)) enc_gather<CHLOG>(a, b, sh, threadIdx.x);
 }
 
 // The fused pass: one 1024-thread workgroup per 64 KiB mask block (32768
@@ -778,7 +1046,9 @@ __global__ __launch_bounds__(LZE_THREADS, 8) void k_cast_diff_lz4(Lz4EncArgs a, 
     sched_fence();  // keeps the later steps' code out of step 1
     if (PATCH && (t % kWave) == 0) sh.pw[t / kWave] = nw;
     __syncthreads();
-    enc_rest<CHLOG, PATCH>(a, f, b, tag, sh, t);
+    if (enc_rest<CHLOG, PATCH>(a, f, b, tag, sh, t)) {
+        if constexpr (!PATCH) enc_gather<CHLOG>(a, b, sh, t);
+    }
 }
 
 }  // namespace pulse

@@ -381,6 +381,39 @@ def gpu_encode(src, block_bytes=65536, src_xor=None, cap=None):
                 offsets=host(offs, np.uint64)[:nb], total=t, status=int(host(st)[0]))
 
 
+def runs_block(rng, nruns, size=65536):
+    """`size` bytes holding `nruns` runs of exactly five zeros, evenly spread
+    between non-zero literals with no two equal neighbours (each run is one
+    sequence of the canonical parse), then literals to the end."""
+    gap = (size - 64) // nruns - 5
+    r = rng.integers(1, 254, size, dtype=np.int64)
+    lit = (np.cumsum(r) % 255 + 1).astype(np.uint8)  # 1 .. 255, neighbours differ
+    out = lit.copy()
+    for k in range(nruns):
+        s0 = k * (gap + 5) + gap
+        out[s0:s0 + 5] = 0
+    return out
+
+
+def test_lz4_encode_large_blocks_around_the_table_size():
+    """Blocks whose encoding is larger than the encoder's 14 KiB window, with
+    1 to 1,799 sequences: up to 1,797 (the sequence table's size less one)
+    they are written by output piece, from 1,798 on in window passes; ragged
+    last block, payload offsets at many alignments.  The payload equals the
+    oracle's byte for byte."""
+    rng = np.random.default_rng(41)
+    counts = [1, 2, 3, 17, 250, 1000, 1796, 1797, 1798, 1799]
+    blocks = [runs_block(rng, n) for n in counts] + [runs_block(rng, 300, 40000)]
+    m = np.concatenate(blocks)
+    ref = oracle.lz4_encode_blocks(m, 65536)
+    assert ref["status"] == 0 and int(ref["sizes"].min()) > 14336
+    assert len({int(o) % 16 for o in ref["offsets"]}) > 4
+    got = gpu_encode(m)
+    assert got["status"] == 0 and got["total"] == ref["total"]
+    assert np.array_equal(got["sizes"], ref["sizes"]) and np.array_equal(got["offsets"], ref["offsets"])
+    assert np.array_equal(got["payload"], ref["payload"][:ref["total"]])
+
+
 @pytest.mark.parametrize("nbytes", [1, 12, 13, 100, 65536, 65537, 3 * 65536 + 1234, 1 << 22])
 @pytest.mark.parametrize("density", [0.0, 0.01, 0.08, 0.5, 1.0])
 def test_lz4_encode_matches_oracle(nbytes, density):
