@@ -395,23 +395,31 @@ def runs_block(rng, nruns, size=65536):
     return out
 
 
-def test_lz4_encode_large_blocks_around_the_table_size():
+@pytest.mark.parametrize("block_bytes,counts", [
+    (65536, [1, 2, 3, 17, 250, 1000, 1796, 1797, 1798, 1799]),
+    (32768, [1, 3, 100, 1000, 1796, 1797, 1798, 1799]),
+    (16384, [1, 3, 50, 300, 600, 900]),
+])
+def test_lz4_encode_large_blocks_around_the_table_size(block_bytes, counts):
     """Blocks whose encoding is larger than the encoder's 14 KiB window, with
     1 to 1,799 sequences: up to 1,797 (the sequence table's size less one)
-    they are written by output piece, from 1,798 on in window passes; ragged
-    last block, payload offsets at many alignments.  The payload equals the
-    oracle's byte for byte."""
-    rng = np.random.default_rng(41)
-    counts = [1, 2, 3, 17, 250, 1000, 1796, 1797, 1798, 1799]
-    blocks = [runs_block(rng, n) for n in counts] + [runs_block(rng, 300, 40000)]
+    they are written by output piece, from 1,798 on in window passes; every
+    block size class, a ragged last block, payload offsets at many
+    alignments.  The payload equals the oracle's byte for byte."""
+    rng = np.random.default_rng(41 + block_bytes)
+    blocks = [runs_block(rng, n, block_bytes) for n in counts]
+    blocks.append(runs_block(rng, 20 if block_bytes < 65536 else 300, block_bytes - 1000))
     m = np.concatenate(blocks)
-    ref = oracle.lz4_encode_blocks(m, 65536)
+    ref = oracle.lz4_encode_blocks(m, block_bytes)
     assert ref["status"] == 0 and int(ref["sizes"].min()) > 14336
-    assert len({int(o) % 16 for o in ref["offsets"]}) > 4
-    got = gpu_encode(m)
+    assert len({int(o) % 16 for o in ref["offsets"]}) > 3
+    got = gpu_encode(m, block_bytes)
     assert got["status"] == 0 and got["total"] == ref["total"]
     assert np.array_equal(got["sizes"], ref["sizes"]) and np.array_equal(got["offsets"], ref["offsets"])
     assert np.array_equal(got["payload"], ref["payload"][:ref["total"]])
+    dst = rng.integers(0, 256, m.size, dtype=np.uint8)
+    d, st = gpu_decode(ref["payload"], ref["offsets"], ref["sizes"], dst, 1, block_bytes=block_bytes)
+    assert st == 0 and np.array_equal(d, dst ^ m)
 
 
 @pytest.mark.parametrize("nbytes", [1, 12, 13, 100, 65536, 65537, 3 * 65536 + 1234, 1 << 22])
